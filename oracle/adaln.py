@@ -1,0 +1,249 @@
+"""Forward and backward of the AdaLN final modulation, written out plainly.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Source of every step (page titles and sections; the pages print no code):
+
+  RL-Kernel pull request 538, "What":
+      scale, shift = (SiLU(temb) @ W^T + b).chunk(2)      3072 -> 6144, scale first
+      out = LayerNorm(x, eps=1e-6, no affine) * (1 + scale) + shift
+      d_scale, d_shift are token sums accumulated in FP32; the CPU reference
+      sums tokens sequentially with Neumaier compensation.
+  miles_diffusion pull request 108 ("Fused-norm rounding points"; later text
+  "Patches"): LayerNorm computes and returns fp32, (1 + scale) is rounded once
+  to bf16, the modulation is fp32, one bf16 rounding at the next consumer.
+  RL-Kernel pull request 538, review thread (automated review of the reference
+  projection): the SiLU derivative is sigmoid * (1 + z * (1 - sigmoid)); its
+  worked value at z = 1 is about 0.9277.  The same thread asks that every
+  reduction of the reference be compensated (input gradient and bias gradient
+  included), which this oracle does: every sum below is an NSum.
+
+Readings where the pages leave a step open (all listed in the design doc):
+  * SiLU is evaluated in float64 and rounded to float32, then to bf16 (its
+    output is the bf16 input of the projection matmul).
+  * The projection accumulates in fp32, adds the bias in fp32, then rounds
+    once to bf16 (emb is a bf16 tensor: scale | shift).
+  * LayerNorm: biased variance (divide by D), eps = float32(1e-6) inside the
+    square root, two passes (mean, then the mean of squared deviations),
+    correctly rounded sqrt and division.
+  * The modulation is (n * m) + shift as two fp32 operations (no fused
+    multiply-add), m = bf16(1 + scale); the output is rounded once to bf16.
+  * Backward: the upstream gradient g is bf16.  gy = g * m (exact);
+    alpha = sum(gy)/D, beta = sum(gy * n)/D; dx = bf16(rstd*((gy-alpha)-n*beta)).
+    The gradient passes straight through the bf16 rounding of (1 + scale):
+    d_scale = sum_s g * n, d_shift = sum_s g, both kept in fp32.
+  * Projection backward from the fp32 d_emb: da = sum_j d_emb_j * W_jk (fp32
+    products), dtemb = bf16(da * silu'(z)), dW = bf16(sum_b d_emb_bj * a_bk),
+    db = bf16(sum_b d_emb_bj).
+
+Arithmetic modes:
+  "fp32"  the oracle proper: every operation an IEEE float32 operation, every
+          reduction a sequential Neumaier sum in float32.
+  "fp64"  the fp64 twin (arbiter): the same steps in float64, rounded only at
+          the storage points -- a, emb, m, out, dx, dtemb, dW, db to bf16 (one
+          rounding each) and the LayerNorm output n, d_scale, d_shift to fp32.
+  "exact" float64 with no rounding at all; used for finite-difference checks.
+
+Parity pins live in tests/test_oracle_pins.py; nothing here is unpinned.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .fpmath import (bits_to_f32, bf16_round, f32_to_bf16_bits, f64_to_bf16_bits,
+                     nsum_stream)
+
+EPS = 1e-6
+
+
+class Arith:
+    """The arithmetic of one mode: working dtype, storage roundings, sums."""
+
+    def __init__(self, mode: str):
+        if mode not in ("fp32", "fp64", "exact"):
+            raise ValueError(mode)
+        self.mode = mode
+        self.dt = np.float32 if mode == "fp32" else np.float64
+
+    def c(self, v):
+        """Cast to the working dtype (exact for every value fed in)."""
+        return np.asarray(v, dtype=self.dt)
+
+    def bf16(self, v):
+        """Storage rounding to bfloat16 (identity in exact mode)."""
+        if self.mode == "exact":
+            return np.asarray(v, dtype=np.float64)
+        return bf16_round(np.asarray(v, dtype=self.dt))
+
+    def f32(self, v):
+        """Storage rounding to float32 (identity in fp32 and exact modes)."""
+        if self.mode == "fp64":
+            return np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
+        return np.asarray(v, dtype=self.dt)
+
+    def sum(self, terms, shape, want_abs=False):
+        return nsum_stream(terms, shape, self.dt, want_abs)
+
+
+def _silu64(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def _dsilu64(z):
+    s = 1.0 / (1.0 + np.exp(-z))
+    return s * (1.0 + z * (1.0 - s))
+
+
+def _val(inp: dict, key: str) -> np.ndarray:
+    """Input values: ``inp[key + '_val']`` (float64, exact mode) or the bf16 bits."""
+    if key + "_val" in inp:
+        return np.asarray(inp[key + "_val"], dtype=np.float64)
+    return bits_to_f32(inp[key])
+
+
+def silu_act(temb, ar: Arith):
+    """a = bf16(SiLU(temb)); SiLU in float64, rounded to float32 in fp32 mode."""
+    z = np.asarray(temb).astype(np.float64)
+    v = _silu64(z)
+    if ar.mode == "fp32":
+        v = v.astype(np.float32)
+    return ar.bf16(v)
+
+
+def dsilu(temb, ar: Arith):
+    """silu'(z) = sigma * (1 + z * (1 - sigma)) in float64 (float32 result in fp32 mode)."""
+    z = np.asarray(temb).astype(np.float64)
+    v = _dsilu64(z)
+    return ar.c(v.astype(np.float32)) if ar.mode == "fp32" else v
+
+
+def projection(a, W, bias, ar: Arith, want_abs=False):
+    """emb[b, j] = bf16(sum_k a[b,k] * W[j,k] + bias[j])  (scale = emb[:, :D])."""
+    WT = np.ascontiguousarray(ar.c(W).T)                             # [K, N]
+    bias = ar.c(bias)
+    a = ar.c(a)
+    B, K = a.shape
+    N = WT.shape[1]
+    terms = (a[:, k:k + 1] * WT[k][None, :] for k in range(K))
+    r = ar.sum(terms, (B, N), want_abs)
+    acc, A = (r if want_abs else (r, None))
+    emb = ar.bf16(acc + bias)
+    return (emb, A) if want_abs else emb
+
+
+def forward(inp: dict, mode: str = "fp32", eps: float = EPS, want_abs: bool = False):
+    """Forward pass.  ``inp`` holds bf16 bit arrays x, temb, W, bias.
+
+    Returns a dict: a, emb, m, mean, rstd, n, out (values in the mode's dtype;
+    bf16 quantities hold bf16-representable values) and, for bf16 outputs,
+    ``*_bits`` uint16 arrays.
+    """
+    ar = Arith(mode)
+    x = ar.c(_val(inp, "x"))
+    B, S, D = x.shape
+    a = silu_act(_val(inp, "temb"), ar)
+    pr = projection(a, _val(inp, "W"), _val(inp, "bias"), ar, want_abs)
+    emb, A_emb = pr if want_abs else (pr, None)
+    scale, shift = emb[:, :D], emb[:, D:]
+    one = ar.c(1.0)
+    m = ar.bf16(one + scale)
+
+    R = B * S
+    xT = np.ascontiguousarray(x.reshape(R, D).T)                     # [D, R]
+    Dt = ar.c(D)
+    mean = ar.sum(iter(xT), (R,)) / Dt
+    dT = xT - mean[None, :]
+    var = ar.sum((dT[d] * dT[d] for d in range(D)), (R,)) / Dt
+    eps_t = ar.c(np.float32(eps))
+    rstd = ar.c(1.0) / np.sqrt(var + eps_t)
+    n = ar.f32((x.reshape(R, D) - mean[:, None]) * rstd[:, None]).reshape(B, S, D)
+    out = ar.bf16(n * m[:, None, :] + shift[:, None, :])
+    res = dict(a=a, emb=emb, m=m, mean=mean.reshape(B, S), rstd=rstd.reshape(B, S),
+               n=n, out=out, var=var.reshape(B, S))
+    if mode != "exact":
+        res["out_bits"] = _bits(out)
+        res["emb_bits"] = _bits(emb)
+        res["a_bits"] = _bits(a)
+    if want_abs:
+        res["A_emb"] = A_emb
+    return res
+
+
+def backward(inp: dict, fwd: dict, mode: str = "fp32", want_abs: bool = False,
+             g=None):
+    """Backward pass from the upstream gradient ``inp['g']`` (bf16 bits).
+
+    Returns dx, d_scale, d_shift, d_emb (= d_scale | d_shift), da, dtemb, dW, db
+    and, for bf16 outputs, ``*_bits``.  With ``want_abs`` also the error scales
+    A (sum of |terms|, float64) of d_emb, alpha/beta, da, dW and db.
+    """
+    ar = Arith(mode)
+    g = ar.c(_val(inp, "g") if g is None else g)
+    B, S, D = g.shape
+    R = B * S
+    m, n, rstd = fwd["m"], fwd["n"], fwd["rstd"]
+    gy = g * m[:, None, :]                                            # exact in fp32
+    gyT = np.ascontiguousarray(gy.reshape(R, D).T)
+    nT = np.ascontiguousarray(n.reshape(R, D).T)
+    Dt = ar.c(D)
+    alpha = ar.sum(iter(gyT), (R,)) / Dt
+    beta = ar.sum((gyT[d] * nT[d] for d in range(D)), (R,)) / Dt
+    rs = rstd.reshape(R)[:, None]
+    dx = ar.bf16(rs * ((gy.reshape(R, D) - alpha[:, None]) - n.reshape(R, D) * beta[:, None]))
+    dx = dx.reshape(B, S, D)
+
+    # token sums over s, per sample
+    r1 = ar.sum((g[:, s, :] for s in range(S)), (B, D), want_abs)
+    r2 = ar.sum((g[:, s, :] * n[:, s, :] for s in range(S)), (B, D), want_abs)
+    d_shift, A_shift = r1 if want_abs else (r1, None)
+    d_scale, A_scale = r2 if want_abs else (r2, None)
+    d_shift = ar.f32(d_shift)
+    d_scale = ar.f32(d_scale)
+    d_emb = np.concatenate([d_scale, d_shift], axis=1)                 # [B, 2D]
+
+    W = ar.c(_val(inp, "W"))                                           # [N, K]
+    N, K = W.shape
+    r3 = ar.sum((d_emb[:, j:j + 1] * W[j][None, :] for j in range(N)), (B, K), want_abs)
+    da, A_da = r3 if want_abs else (r3, None)
+    ds = dsilu(_val(inp, "temb"), ar)
+    dtemb = ar.bf16(da * ds)
+
+    a = fwd["a"]
+    r4 = ar.sum((d_emb[b][:, None] * a[b][None, :] for b in range(B)), (N, K), want_abs)
+    dW_acc, A_dW = r4 if want_abs else (r4, None)
+    dW = ar.bf16(dW_acc)
+    r5 = ar.sum((d_emb[b] for b in range(B)), (N,), want_abs)
+    db_acc, A_db = r5 if want_abs else (r5, None)
+    db = ar.bf16(db_acc)
+
+    res = dict(dx=dx, d_scale=d_scale, d_shift=d_shift, d_emb=d_emb, da=da,
+               dtemb=dtemb, dW=dW, db=db, dW_acc=dW_acc, db_acc=db_acc,
+               alpha=alpha.reshape(B, S), beta=beta.reshape(B, S))
+    if mode != "exact":
+        for k in ("dx", "dtemb", "dW", "db"):
+            res[k + "_bits"] = _bits(res[k])
+    if want_abs:
+        res["A_d_emb"] = np.concatenate([A_scale, A_shift], axis=1)
+        res.update(A_da=A_da, A_dW=A_dW, A_db=A_db)
+    return res
+
+
+def _bits(v):
+    v = np.asarray(v)
+    if v.dtype == np.float64:
+        return f64_to_bf16_bits(v)
+    return f32_to_bf16_bits(v)
+
+
+def sgld_forward_out(inp: dict, fwd: dict):
+    """The rollout-side semantics the miles_diffusion pull request 108 summary
+    names as wrong: the LayerNorm output is rounded to bf16 and the modulation
+    runs in bf16 eager ops (each op rounds to bf16).  Used only as a negative
+    control: it must differ from ``forward``'s output."""
+    n16 = bf16_round(np.asarray(fwd["n"], dtype=np.float32))
+    m = np.asarray(fwd["m"], dtype=np.float32)
+    D = m.shape[1]
+    shift = np.asarray(fwd["emb"], dtype=np.float32)[:, D:]
+    prod = bf16_round(n16 * m[:, None, :])
+    return bf16_round(prod + shift[:, None, :])
