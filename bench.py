@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""Throughput of the batch-invariant AdaLN final modulation, forward + backward.
+
+One step is the whole hot path over one batch of synthetic input, through the
+C ABI: adaln_proj_fwd -> adaln_norm_mod_fwd -> adaln_norm_mod_bwd_tiles ->
+token_tree_fold -> adaln_proj_bwd.  Default workload: one 1024x1024 image
+stream, B = 1, S = 4096 tokens, D = 3072, bf16 storage, 1% outlier rows x20.
+
+Inputs are resident in HBM before the timed region.  The step rotates over
+several independent copies of every buffer (parameters included), so no step
+finds the previous step's data in the 256 MB MALL; reuse inside one step (x
+read by the forward and the backward, W by both projections) is left as is.
+
+Prints ONE JSON line.  `roofline` covers the dominant kernel (dx + level-0 token
+tiles of the norm backward), timed with HIP events on the stream it runs on;
+`cpu_baseline` is the NumPy oracle timed on this host on the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+D = 3072
+N = 2 * D
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 << 20
+METRIC = "fwd+bwd tokens/sec + achieved HBM GB/s at S=4096 D=3072 bf16 (batch-invariant)"
+
+
+def algorithmic_bytes(B: int, S: int) -> int:
+    """Bytes the method must move per step (no partials, no re-reads):
+    x read twice, out, g, dx (10 B per element); mean/rstd written and read;
+    W read twice, dW written; b read, db written; per-sample vectors."""
+    return 10 * B * S * D + 16 * B * S + 6 * N * D + 4 * N + 98304 * B
+
+
+def dominant_kernel_bytes(B: int, S: int) -> int:
+    """norm backward, level-0 stage: g and x read, dx written, mean/rstd read,
+    scale read (per sample)."""
+    return 6 * B * S * D + 8 * B * S + 2 * D * B
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="img1024_b1_s4096")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="after the steps, run a plain 512 MiB device copy (PMC byte-counter calibration)")
+    return ap.parse_args()
+
+
+def cpu_baseline(inp: dict, reps: int = 2) -> dict:
+    """The oracle (NumPy, single-threaded element-wise loops) on the same batch."""
+    from oracle import adaln
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        f = adaln.forward(inp)
+        adaln.backward(inp, f)
+    dt = (time.perf_counter() - t0) / reps
+    tokens = inp["B"] * inp["S"]
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole workload batch (B={inp['B']}, S={inp['S']}), fwd+bwd, "
+                      f"{reps} passes, {dt:.2f} s per pass"}
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the batch-invariant path has no multi-GPU "
+              "mode in this build (see DESIGN.md for how it would shard).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from invariant_silu_amd import lib
+    from synthetic_inputs import WORKLOADS, make_workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    L = lib.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if L.adaln_selftest() != 0:
+        print("strict-math self-test failed", file=sys.stderr)
+        return 3
+
+    w = WORKLOADS[args.workload]
+    B, S = w["B"], w["S"]
+    inp = make_workload(args.workload, seed=0)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    base = {k: to_dev(inp[k]) for k in ("x", "temb", "W", "bias", "g")}
+    ws_pf = lib.workspace_bytes(lib.OP_PROJ_FWD, B, S, D)
+    ws_nb = lib.workspace_bytes(lib.OP_NORM_MOD_BWD, B, S, D)
+    ws_pb = lib.workspace_bytes(lib.OP_PROJ_BWD, B, S, D)
+    T0 = math.ceil(S / 32)
+
+    def new_set():
+        s = {k: v.clone() for k, v in base.items()}
+        s.update(
+            emb=torch.empty((B, N), dtype=torch.bfloat16, device=dev),
+            out=torch.empty((B, S, D), dtype=torch.bfloat16, device=dev),
+            mean=torch.empty((B, S), dtype=torch.float32, device=dev),
+            rstd=torch.empty((B, S), dtype=torch.float32, device=dev),
+            dx=torch.empty((B, S, D), dtype=torch.bfloat16, device=dev),
+            d_emb=torch.empty((B, N), dtype=torch.float32, device=dev),
+            dW=torch.empty((N, D), dtype=torch.bfloat16, device=dev),
+            db=torch.empty((N,), dtype=torch.bfloat16, device=dev),
+            dtemb=torch.empty((B, D), dtype=torch.bfloat16, device=dev),
+            ws_pf=torch.empty(ws_pf, dtype=torch.uint8, device=dev),
+            ws_nb=torch.empty(ws_nb, dtype=torch.uint8, device=dev),
+            ws_pb=torch.empty(ws_pb, dtype=torch.uint8, device=dev),
+        )
+        return s
+
+    per_set = algorithmic_bytes(B, S)
+    nsets = max(2, math.ceil(3 * MALL_BYTES / per_set))
+    sets = [new_set() for _ in range(nsets)]
+    stream = torch.cuda.current_stream(dev)
+    st = stream.cuda_stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+
+    def step(s, evpair=None):
+        p = lambda k: s[k].data_ptr()   # noqa: E731
+        lib.check("adaln_proj_fwd", L.adaln_proj_fwd(p("temb"), p("W"), p("bias"), p("emb"), p("ws_pf"),
+                                                     ws_pf, B, D, N, st))
+        lib.check("adaln_norm_mod_fwd", L.adaln_norm_mod_fwd(p("x"), p("emb"), p("out"), p("mean"),
+                                                             p("rstd"), B, S, D, 1e-6, st))
+        if evpair is not None:
+            evpair[0].record(stream)
+        lib.check("adaln_norm_mod_bwd_tiles",
+                  L.adaln_norm_mod_bwd_tiles(p("g"), p("x"), p("mean"), p("rstd"), p("emb"), p("dx"),
+                                             p("ws_nb"), ws_nb, B, S, D, st))
+        if evpair is not None:
+            evpair[1].record(stream)
+        lib.check("token_tree_fold", L.token_tree_fold(p("ws_nb"), p("d_emb"), B, T0, N, st))
+        lib.check("adaln_proj_bwd", L.adaln_proj_bwd(p("d_emb"), p("temb"), p("W"), p("dW"), p("db"),
+                                                     p("dtemb"), p("ws_pb"), ws_pb, B, D, N, st))
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % nsets], ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    tokens_per_s = B * S / (ms_per_step / 1e3)
+    step_bytes = algorithmic_bytes(B, S)
+    k_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    k_mean_ms = sum(k_ms) / len(k_ms)
+    k_bytes = dominant_kernel_bytes(B, S)
+    achieved = k_bytes / (k_mean_ms / 1e3) / 1e9
+
+    if args.copy_calib:
+        n = 512 << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "S": S, "D": D, "N": N,
+                   "storage": "bf16", "accumulate": "fp64", "outlier_rows": w["outlier_frac"],
+                   "buffer_sets": nsets, "step_algorithmic_bytes": step_bytes,
+                   "step_gbps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
+                   "step_frac_of_peak": round(step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "roofline": {"bound": "hbm", "kernel": "norm_mod_bwd_kernel (dx + level-0 token tiles)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": k_bytes, "avg_launch_ms": round(k_mean_ms, 5),
+                     "median_launch_ms": round(k_ms[len(k_ms) // 2], 5)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

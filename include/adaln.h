@@ -1,0 +1,163 @@
+/*
+ * adaln.h -- C ABI of the batch-invariant AdaLN final modulation for MI355X (gfx950).
+ *
+ * The operation is Qwen-Image's final image-stream modulation `norm_out`
+ * (RL-Kernel pull request 538, section "What"):
+ *
+ *     scale, shift = (SiLU(temb) @ W^T + b).chunk(2)        3072 -> 6144, scale first
+ *     out          = LayerNorm(x, eps, no affine) * (1 + scale) + shift
+ *
+ * at the autocast rounding points of miles_diffusion pull request 108
+ * ("Fused-norm rounding points"): fp32 LayerNorm, (1 + scale) rounded once to
+ * bf16, fp32 modulation, one bf16 rounding of the output.  The backward gives
+ * dx, d_scale / d_shift as fp32 token sums over a fixed 32-token compensated
+ * tree whose shape depends only on S (pull request 538, review thread on
+ * token_sum.cu), and dW, db, dtemb through the projection.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - bf16 tensors are passed as `adaln_bf16` (uint16_t bit patterns); fp32 as
+ *   float; the only fp64 data lives in workspaces.
+ * - Every pointer is a DEVICE pointer on the current HIP device and must be
+ *   16-byte aligned.  Tensors are dense, row-major and contiguous.
+ * - The caller owns every buffer, workspaces included.  Apart from
+ *   adaln_selftest the library allocates no device memory, keeps no per-call
+ *   state and never synchronizes: the work is enqueued on `stream` (a
+ *   hipStream_t; NULL means the null stream).
+ * - Outputs are always written in full (never aliases or views of an input)
+ *   and must not overlap any input, any other output or the workspace.
+ * - Fixed widths: D = K = 3072 and N = 2 * D = 6144.  B >= 1, S >= 1.
+ * - Every check runs before anything is enqueued; a non-zero status means
+ *   nothing was launched (except ADALN_ERR_LAUNCH).
+ * - Determinism: identical inputs give identical bytes; every per-sample /
+ *   per-row output (emb, out, mean, rstd, dx, d_emb, dtemb) has the same bytes
+ *   for any batch size B and any position of the sample in the batch.  dW and
+ *   db are batch sums in ascending sample order; trailing all-zero gradient
+ *   samples leave them byte-identical.
+ * - Unsupported devices (anything but gfx950) fail closed with
+ *   ADALN_ERR_DEVICE (pull request 538: other platforms fail closed).
+ */
+#ifndef ADALN_H
+#define ADALN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t adaln_bf16;
+
+#define ADALN_ABI_VERSION 1
+
+enum adaln_status {
+  ADALN_OK = 0,
+  ADALN_ERR_NULL = -1,       /* a required pointer is NULL                        */
+  ADALN_ERR_SHAPE = -2,      /* B, S, H out of range or D/K/N not 3072/3072/6144  */
+  ADALN_ERR_ALIGN = -3,      /* a pointer is not 16-byte aligned                  */
+  ADALN_ERR_DEVICE = -4,     /* current device is not gfx950 / no HIP device       */
+  ADALN_ERR_WORKSPACE = -5,  /* ws_bytes < adaln_workspace_bytes(...)             */
+  ADALN_ERR_OVERLAP = -6,    /* an output overlaps an input, output or workspace  */
+  ADALN_ERR_LAUNCH = -7      /* a kernel launch failed (hipGetLastError)          */
+};
+
+enum adaln_op {
+  ADALN_OP_PROJ_FWD = 1,
+  ADALN_OP_NORM_MOD_BWD = 2,
+  ADALN_OP_PROJ_BWD = 3,
+  ADALN_OP_TOKEN_TREE_SUM = 4
+};
+
+/* Workspace bytes an entry point needs (0 for an unknown op or bad sizes).
+ *   PROJ_FWD:       H = K (3072), S ignored.  B*K*2 bytes (the SiLU activations).
+ *   NORM_MOD_BWD:   H = D (3072).  2 * B * ceil(S/32) * 2D * 4 bytes (level-0 pairs).
+ *   PROJ_BWD:       H = K (3072), S ignored.  B*K*2 (activations) + 32*B*K*8 (fp64 partials).
+ *   TOKEN_TREE_SUM: 2 * B * ceil(S/32) * H * 4 bytes.
+ * Each region is padded to 256 bytes. */
+size_t adaln_workspace_bytes(int op, int64_t B, int64_t S, int64_t H);
+
+/* Projection forward (pull request 538, "What": SiLU(temb) @ W^T + b, chunk(2)).
+ *   temb [B, K] bf16 (in), W [N, K] bf16 (in, row-major), bias [N] bf16 (in),
+ *   emb  [B, N] bf16 (out) = (scale | shift).
+ *   emb = bf16(fp32(sum_k a_k W_jk) + bias_j), a = bf16(fp32(SiLU(temb))),
+ *   SiLU evaluated in float64; the sum accumulates exact products in fp64 in a
+ *   fixed order independent of B. */
+int adaln_proj_fwd(const adaln_bf16* temb, const adaln_bf16* W, const adaln_bf16* bias,
+                   adaln_bf16* emb, void* ws, size_t ws_bytes, int64_t B, int64_t K, int64_t N,
+                   void* stream);
+
+/* LayerNorm + modulation forward (pull request 538, "What"; rounding points of
+ * miles_diffusion pull request 108).
+ *   x [B, S, D] bf16 (in), emb [B, 2D] bf16 (in, from adaln_proj_fwd),
+ *   out [B, S, D] bf16 (out), mean [B, S] fp32 (out), rstd [B, S] fp32 (out).
+ *   mean = fp32(sum x)/D, var = fp32(sum (x-mean)^2)/D (biased), rstd =
+ *   1/sqrt(var + eps) correctly rounded, n = (x - mean) * rstd,
+ *   out = bf16((n * bf16(1 + scale)) + shift).  Pass eps = 1e-6f. */
+int adaln_norm_mod_fwd(const adaln_bf16* x, const adaln_bf16* emb, adaln_bf16* out, float* mean,
+                       float* rstd, int64_t B, int64_t S, int64_t D, float eps, void* stream);
+
+/* LayerNorm + modulation backward with the token-sum tree (pull request 538,
+ * "What" and the token_sum.cu review fix).
+ *   gout [B, S, D] bf16 (in, upstream gradient), x [B, S, D] bf16 (in),
+ *   mean, rstd [B, S] fp32 (in, from adaln_norm_mod_fwd), emb [B, 2D] bf16 (in),
+ *   dx [B, S, D] bf16 (out), d_emb [B, 2D] fp32 (out) = (d_scale | d_shift).
+ *   gy = g * m, dx = bf16(rstd * ((gy - mean(gy)) - n * mean(gy * n)));
+ *   d_scale = tree_S(g * n), d_shift = tree_S(g), kept in fp32 (the gradient
+ *   passes straight through the bf16 rounding of 1 + scale). */
+int adaln_norm_mod_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float* mean,
+                       const float* rstd, const adaln_bf16* emb, adaln_bf16* dx, float* d_emb,
+                       void* ws, size_t ws_bytes, int64_t B, int64_t S, int64_t D, void* stream);
+
+/* The two stages of adaln_norm_mod_bwd, exported separately (the tree fold
+ * can then be timed, overlapped or reused on its own).
+ *
+ * adaln_norm_mod_bwd_tiles: dx as above, plus the level-0 pairs of the token
+ *   tree: `part` holds two fp32 arrays, sums then corrections, each
+ *   [B, ceil(S/32), 2D] and padded to 256 bytes; part_bytes must be at least
+ *   adaln_workspace_bytes(ADALN_OP_NORM_MOD_BWD, B, S, D).
+ * token_tree_fold: the levels >= 1 of the tree from such pairs: `part` as
+ *   written by adaln_norm_mod_bwd_tiles (H = 2D) or by the level 0 of
+ *   token_tree_sum (any H), T0 = ceil(S/32) tiles per sample; out [B, H] fp32. */
+int adaln_norm_mod_bwd_tiles(const adaln_bf16* gout, const adaln_bf16* x, const float* mean,
+                             const float* rstd, const adaln_bf16* emb, adaln_bf16* dx, void* part,
+                             size_t part_bytes, int64_t B, int64_t S, int64_t D, void* stream);
+int token_tree_fold(const void* part, float* out, int64_t B, int64_t T0, int64_t H, void* stream);
+
+/* Projection backward (pull request 538, "What": projection backward; review
+ * thread: silu'(z) = sigmoid(z) * (1 + z * (1 - sigmoid(z)))).
+ *   d_emb [B, N] fp32 (in), temb [B, K] bf16 (in), W [N, K] bf16 (in),
+ *   dW [N, K] bf16 (out), db [N] bf16 (out), dtemb [B, K] bf16 (out).
+ *   dW = bf16(fp32(sum_b d_emb_bj * a_bk)), db = bf16(fp32(sum_b d_emb_bj)),
+ *   dtemb = bf16(fp32(sum_j d_emb_bj * W_jk) * silu'(temb)); fp32 products,
+ *   fp64 accumulation in orders that do not depend on B. */
+int adaln_proj_bwd(const float* d_emb, const adaln_bf16* temb, const adaln_bf16* W,
+                   adaln_bf16* dW, adaln_bf16* db, adaln_bf16* dtemb, void* ws, size_t ws_bytes,
+                   int64_t B, int64_t K, int64_t N, void* stream);
+
+/* Token-sum tree (pull request 538: fixed 32-way tree that depends only on S;
+ * review thread: 32-token Neumaier tiles folded level by level, one final add).
+ *   x [B, S, H] fp32 (in), out [B, H] fp32 (out).  Any H >= 1.  S = 1 still
+ *   computes (out is a fresh buffer, never a view of x). */
+int token_tree_sum(const float* x, float* out, void* ws, size_t ws_bytes, int64_t B, int64_t S,
+                   int64_t H, void* stream);
+
+/* Device check plus strict-math probe (correctly rounded sqrt and divide, no
+ * contraction into fused multiply-add, bf16 round-to-nearest-even), run
+ * synchronously on the current device.  It is the one entry point that
+ * allocates: 80 KB of device memory for the probe, freed before it returns.
+ * The verdict is cached per device, both ways.  Returns ADALN_OK,
+ * ADALN_ERR_DEVICE, or a positive count of failed probe values. */
+int adaln_selftest(void);
+
+/* Static description of a status code. */
+const char* adaln_strerror(int status);
+
+/* ADALN_ABI_VERSION of the loaded library. */
+int adaln_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ADALN_H */

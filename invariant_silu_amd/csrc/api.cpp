@@ -1,0 +1,349 @@
+// C-ABI layer: argument validation, device check, workspace carving and
+// kernel sequencing.  Every check runs before anything is enqueued
+// (RL-Kernel pull request 538, automated review: capability checks before
+// allocation; width-correct 16-byte load guards; outputs never alias inputs;
+// probe verdicts cached both ways).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "../../include/adaln.h"
+#include "launch.hpp"
+
+namespace {
+
+using adaln::kProjBwdParts;
+
+constexpr int64_t kD = 3072;
+constexpr int64_t kN = 6144;
+constexpr int64_t kTile = 32;
+constexpr int64_t kMaxB = 65535;
+constexpr int64_t kMaxS = kTile * 65535;
+constexpr int kMaxDevices = 64;
+
+std::atomic<int> g_arch_verdict[kMaxDevices];    // 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_probe_verdict[kMaxDevices];   // 0 unknown, 1 pass, 2 fail
+std::atomic<int> g_probe_failures[kMaxDevices];
+
+inline size_t pad256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  const void* p;
+  size_t n;
+};
+inline bool overlaps(const Range& a, const Range& b) {
+  if (a.n == 0 || b.n == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+// every output against every input, every other output and the workspace
+int check_overlap(const std::vector<Range>& outs, const std::vector<Range>& ins) {
+  for (size_t i = 0; i < outs.size(); ++i) {
+    for (const Range& r : ins)
+      if (overlaps(outs[i], r)) return ADALN_ERR_OVERLAP;
+    for (size_t j = i + 1; j < outs.size(); ++j)
+      if (overlaps(outs[i], outs[j])) return ADALN_ERR_OVERLAP;
+  }
+  return ADALN_OK;
+}
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return ADALN_ERR_DEVICE;
+  }
+  int v = g_arch_verdict[dev].load(std::memory_order_acquire);
+  if (v == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      v = 2;
+    } else {
+      v = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    }
+    g_arch_verdict[dev].store(v, std::memory_order_release);
+  }
+  return v == 1 ? ADALN_OK : ADALN_ERR_DEVICE;
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline int launched(hipError_t e) { return e == hipSuccess ? ADALN_OK : ADALN_ERR_LAUNCH; }
+
+size_t ws_proj_fwd(int64_t B) { return pad256(static_cast<size_t>(B * kD * 2)); }
+size_t ws_norm_bwd(int64_t B, int64_t S) {
+  return 2 * pad256(static_cast<size_t>(B * ceil_div(S, kTile) * kN * 4));
+}
+size_t ws_proj_bwd(int64_t B) {
+  return pad256(static_cast<size_t>(B * kD * 2)) +
+         pad256(static_cast<size_t>(kProjBwdParts) * static_cast<size_t>(B * kD * 8));
+}
+size_t ws_tree(int64_t B, int64_t S, int64_t H) {
+  return 2 * pad256(static_cast<size_t>(B * ceil_div(S, kTile) * H * 4));
+}
+bool batch_ok(int64_t B) { return B >= 1 && B <= kMaxB; }
+bool seq_ok(int64_t S) { return S >= 1 && S <= kMaxS; }
+
+// host reference values for the strict-math probe
+uint32_t host_bf16(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+float from_bits(uint32_t u) {
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+uint32_t to_bits(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  return u;
+}
+
+int run_probe() {
+  constexpr int n = 4096;
+  std::vector<float> in(n);
+  // an fma would give 2^-24 here; two roundings give exactly 0
+  in[0] = 1.0f + 0x1p-12f;
+  in[1] = 1.0f + 0x1p-12f;
+  in[2] = -(1.0f + 0x1p-11f);
+  uint64_t st = 0x9e3779b97f4a7c15ull;
+  for (int i = 3; i < n; ++i) {
+    st = st * 6364136223846793005ull + 1442695040888963407ull;
+    const uint32_t r = static_cast<uint32_t>(st >> 32);
+    if (i % 4 == 0) {
+      // bf16 ties and near-ties
+      const uint32_t u = (0x3f800000u + ((r & 0xffu) << 16)) | 0x8000u | (r & 0x10000u ? 1u : 0u);
+      in[i] = from_bits(i % 8 == 0 ? (u & ~1u) : u);
+    } else {
+      const uint32_t mant = r & 0x7fffffu;
+      const uint32_t ex = 64u + ((r >> 23) & 127u);   // 2^-63 .. 2^63
+      in[i] = from_bits((ex << 23) | mant | ((r >> 31) << 31));
+    }
+  }
+  float *d_in = nullptr, *d_out = nullptr;
+  uint32_t* d_bits = nullptr;
+  int fails = -1;
+  if (hipMalloc(&d_in, n * 4) == hipSuccess && hipMalloc(&d_out, n * 16) == hipSuccess &&
+      hipMalloc(&d_bits, n * 4) == hipSuccess &&
+      hipMemcpy(d_in, in.data(), n * 4, hipMemcpyHostToDevice) == hipSuccess &&
+      adaln::launch_selftest_probe(d_in, d_out, d_bits, n, nullptr) == hipSuccess &&
+      hipDeviceSynchronize() == hipSuccess) {
+    std::vector<float> out(4 * n);
+    std::vector<uint32_t> bits(n);
+    if (hipMemcpy(out.data(), d_out, n * 16, hipMemcpyDeviceToHost) == hipSuccess &&
+        hipMemcpy(bits.data(), d_bits, n * 4, hipMemcpyDeviceToHost) == hipSuccess) {
+      fails = 0;
+      for (int i = 0; i < n; ++i) {
+        const float v = in[i], w = in[(i + 1) % n], c = in[(i + 2) % n];
+        volatile float prod = v * w;   // keep the host from contracting
+        const float want[4] = {std::sqrt(std::fabs(v)), 1.0f / v, prod + c,
+                               static_cast<float>(static_cast<double>(v) / static_cast<double>(w))};
+        for (int k = 0; k < 4; ++k)
+          if (to_bits(out[4 * i + k]) != to_bits(want[k])) ++fails;
+        if (bits[i] != host_bf16(v)) ++fails;
+      }
+      if (to_bits(out[2]) != 0u) ++fails;   // the fma detector must read +0
+    }
+  }
+  (void)hipGetLastError();
+  if (d_in) (void)hipFree(d_in);
+  if (d_out) (void)hipFree(d_out);
+  if (d_bits) (void)hipFree(d_bits);
+  return fails;
+}
+
+}  // namespace
+
+extern "C" {
+
+int adaln_abi_version(void) { return ADALN_ABI_VERSION; }
+
+const char* adaln_strerror(int status) {
+  switch (status) {
+    case ADALN_OK: return "ok";
+    case ADALN_ERR_NULL: return "a required pointer is NULL";
+    case ADALN_ERR_SHAPE: return "bad shape (need B, S >= 1 within limits and D = K = 3072, N = 6144)";
+    case ADALN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case ADALN_ERR_DEVICE: return "unsupported or missing device (gfx950 required)";
+    case ADALN_ERR_WORKSPACE: return "workspace too small";
+    case ADALN_ERR_OVERLAP: return "an output overlaps an input, another output or the workspace";
+    case ADALN_ERR_LAUNCH: return "kernel launch failed";
+    default: return status > 0 ? "strict-math probe mismatches" : "unknown status";
+  }
+}
+
+size_t adaln_workspace_bytes(int op, int64_t B, int64_t S, int64_t H) {
+  if (!batch_ok(B)) return 0;
+  switch (op) {
+    case ADALN_OP_PROJ_FWD: return H == kD ? ws_proj_fwd(B) : 0;
+    case ADALN_OP_NORM_MOD_BWD: return (H == kD && seq_ok(S)) ? ws_norm_bwd(B, S) : 0;
+    case ADALN_OP_PROJ_BWD: return H == kD ? ws_proj_bwd(B) : 0;
+    case ADALN_OP_TOKEN_TREE_SUM:
+      return (seq_ok(S) && H >= 1 && H <= (int64_t{1} << 24)) ? ws_tree(B, S, H) : 0;
+    default: return 0;
+  }
+}
+
+int adaln_proj_fwd(const adaln_bf16* temb, const adaln_bf16* W, const adaln_bf16* bias,
+                   adaln_bf16* emb, void* ws, size_t ws_bytes, int64_t B, int64_t K, int64_t N,
+                   void* stream) {
+  if (!temb || !W || !bias || !emb || !ws) return ADALN_ERR_NULL;
+  if (!batch_ok(B) || K != kD || N != kN) return ADALN_ERR_SHAPE;
+  if (!aligned16(temb) || !aligned16(W) || !aligned16(bias) || !aligned16(emb) || !aligned16(ws))
+    return ADALN_ERR_ALIGN;
+  if (ws_bytes < ws_proj_fwd(B)) return ADALN_ERR_WORKSPACE;
+  const size_t wsn = ws_proj_fwd(B);
+  if (int rc = check_overlap({{emb, static_cast<size_t>(B * kN * 2)}, {ws, wsn}},
+                             {{temb, static_cast<size_t>(B * kD * 2)}, {W, static_cast<size_t>(kN * kD * 2)},
+                              {bias, static_cast<size_t>(kN * 2)}}))
+    return rc;
+  if (int rc = check_device()) return rc;
+  (void)hipGetLastError();
+  uint16_t* a = static_cast<uint16_t*>(ws);
+  const hipStream_t s = as_stream(stream);
+  if (int rc = launched(adaln::launch_silu(temb, a, B * kD, s))) return rc;
+  return launched(adaln::launch_proj_fwd(a, W, bias, emb, B, s));
+}
+
+int adaln_norm_mod_fwd(const adaln_bf16* x, const adaln_bf16* emb, adaln_bf16* out, float* mean,
+                       float* rstd, int64_t B, int64_t S, int64_t D, float eps, void* stream) {
+  if (!x || !emb || !out || !mean || !rstd) return ADALN_ERR_NULL;
+  if (!batch_ok(B) || !seq_ok(S) || D != kD) return ADALN_ERR_SHAPE;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return ADALN_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(emb) || !aligned16(out) || !aligned16(mean) || !aligned16(rstd))
+    return ADALN_ERR_ALIGN;
+  const size_t rows = static_cast<size_t>(B * S);
+  if (int rc = check_overlap({{out, rows * kD * 2}, {mean, rows * 4}, {rstd, rows * 4}},
+                             {{x, rows * kD * 2}, {emb, static_cast<size_t>(B * kN * 2)}}))
+    return rc;
+  if (int rc = check_device()) return rc;
+  (void)hipGetLastError();
+  return launched(adaln::launch_norm_mod_fwd(x, emb, out, mean, rstd, B, S, eps, as_stream(stream)));
+}
+
+int adaln_norm_mod_bwd_tiles(const adaln_bf16* gout, const adaln_bf16* x, const float* mean,
+                             const float* rstd, const adaln_bf16* emb, adaln_bf16* dx, void* part,
+                             size_t part_bytes, int64_t B, int64_t S, int64_t D, void* stream) {
+  if (!gout || !x || !mean || !rstd || !emb || !dx || !part) return ADALN_ERR_NULL;
+  if (!batch_ok(B) || !seq_ok(S) || D != kD) return ADALN_ERR_SHAPE;
+  if (!aligned16(gout) || !aligned16(x) || !aligned16(mean) || !aligned16(rstd) ||
+      !aligned16(emb) || !aligned16(dx) || !aligned16(part))
+    return ADALN_ERR_ALIGN;
+  const size_t need = ws_norm_bwd(B, S);
+  if (part_bytes < need) return ADALN_ERR_WORKSPACE;
+  const size_t rows = static_cast<size_t>(B * S);
+  if (int rc = check_overlap({{dx, rows * kD * 2}, {part, need}},
+                             {{gout, rows * kD * 2}, {x, rows * kD * 2}, {mean, rows * 4},
+                              {rstd, rows * 4}, {emb, static_cast<size_t>(B * kN * 2)}}))
+    return rc;
+  if (int rc = check_device()) return rc;
+  (void)hipGetLastError();
+  const int64_t T0 = ceil_div(S, kTile);
+  float* part_s = static_cast<float*>(part);
+  float* part_c = reinterpret_cast<float*>(static_cast<char*>(part) + need / 2);
+  return launched(adaln::launch_norm_mod_bwd_level0(gout, x, mean, rstd, emb, dx, part_s, part_c, B,
+                                                    S, adaln::choose_norm_bwd_split(B, T0),
+                                                    as_stream(stream)));
+}
+
+int token_tree_fold(const void* part, float* out, int64_t B, int64_t T0, int64_t H, void* stream) {
+  if (!part || !out) return ADALN_ERR_NULL;
+  if (!batch_ok(B) || T0 < 1 || T0 > kMaxS / kTile || H < 1 || H > (int64_t{1} << 24))
+    return ADALN_ERR_SHAPE;
+  if (!aligned16(part) || !aligned16(out)) return ADALN_ERR_ALIGN;
+  const size_t half = pad256(static_cast<size_t>(B * T0 * H * 4));
+  if (int rc = check_overlap({{out, static_cast<size_t>(B * H * 4)}}, {{part, 2 * half}})) return rc;
+  if (int rc = check_device()) return rc;
+  (void)hipGetLastError();
+  const float* part_s = static_cast<const float*>(part);
+  const float* part_c = reinterpret_cast<const float*>(static_cast<const char*>(part) + half);
+  return launched(adaln::launch_tree_fold(part_s, part_c, out, B, T0, H, as_stream(stream)));
+}
+
+int adaln_norm_mod_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float* mean,
+                       const float* rstd, const adaln_bf16* emb, adaln_bf16* dx, float* d_emb,
+                       void* ws, size_t ws_bytes, int64_t B, int64_t S, int64_t D, void* stream) {
+  if (!gout || !x || !mean || !rstd || !emb || !dx || !d_emb || !ws) return ADALN_ERR_NULL;
+  if (!batch_ok(B) || !seq_ok(S) || D != kD) return ADALN_ERR_SHAPE;
+  if (!aligned16(d_emb)) return ADALN_ERR_ALIGN;
+  const size_t need = ws_norm_bwd(B, S);
+  const size_t rows = static_cast<size_t>(B * S);
+  if (int rc = check_overlap({{d_emb, static_cast<size_t>(B * kN * 4)}},
+                             {{gout, rows * kD * 2}, {x, rows * kD * 2}, {mean, rows * 4}, {rstd, rows * 4},
+                              {emb, static_cast<size_t>(B * kN * 2)}, {dx, rows * kD * 2},
+                              {ws, ws_bytes < need ? ws_bytes : need}}))
+    return rc;
+  if (int rc = adaln_norm_mod_bwd_tiles(gout, x, mean, rstd, emb, dx, ws, ws_bytes, B, S, D, stream))
+    return rc;
+  return token_tree_fold(ws, d_emb, B, ceil_div(S, kTile), kN, stream);
+}
+
+int adaln_proj_bwd(const float* d_emb, const adaln_bf16* temb, const adaln_bf16* W,
+                   adaln_bf16* dW, adaln_bf16* db, adaln_bf16* dtemb, void* ws, size_t ws_bytes,
+                   int64_t B, int64_t K, int64_t N, void* stream) {
+  if (!d_emb || !temb || !W || !dW || !db || !dtemb || !ws) return ADALN_ERR_NULL;
+  if (!batch_ok(B) || K != kD || N != kN) return ADALN_ERR_SHAPE;
+  if (!aligned16(d_emb) || !aligned16(temb) || !aligned16(W) || !aligned16(dW) || !aligned16(db) ||
+      !aligned16(dtemb) || !aligned16(ws))
+    return ADALN_ERR_ALIGN;
+  const size_t need = ws_proj_bwd(B);
+  if (ws_bytes < need) return ADALN_ERR_WORKSPACE;
+  if (int rc = check_overlap({{dW, static_cast<size_t>(kN * kD * 2)}, {db, static_cast<size_t>(kN * 2)},
+                              {dtemb, static_cast<size_t>(B * kD * 2)}, {ws, need}},
+                             {{d_emb, static_cast<size_t>(B * kN * 4)}, {temb, static_cast<size_t>(B * kD * 2)},
+                              {W, static_cast<size_t>(kN * kD * 2)}}))
+    return rc;
+  if (int rc = check_device()) return rc;
+  (void)hipGetLastError();
+  uint16_t* a = static_cast<uint16_t*>(ws);
+  double* part = reinterpret_cast<double*>(static_cast<char*>(ws) + pad256(static_cast<size_t>(B * kD * 2)));
+  const hipStream_t s = as_stream(stream);
+  if (int rc = launched(adaln::launch_silu(temb, a, B * kD, s))) return rc;
+  if (int rc = launched(adaln::launch_proj_bwd_dw(d_emb, a, dW, db, B, s))) return rc;
+  if (int rc = launched(adaln::launch_proj_bwd_da(d_emb, W, part, B, s))) return rc;
+  return launched(adaln::launch_proj_bwd_dtemb(part, temb, dtemb, B, s));
+}
+
+int token_tree_sum(const float* x, float* out, void* ws, size_t ws_bytes, int64_t B, int64_t S,
+                   int64_t H, void* stream) {
+  if (!x || !out || !ws) return ADALN_ERR_NULL;
+  if (!batch_ok(B) || !seq_ok(S) || H < 1 || H > (int64_t{1} << 24)) return ADALN_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(out) || !aligned16(ws)) return ADALN_ERR_ALIGN;
+  const size_t need = ws_tree(B, S, H);
+  if (ws_bytes < need) return ADALN_ERR_WORKSPACE;
+  if (int rc = check_overlap({{out, static_cast<size_t>(B * H * 4)}, {ws, need}},
+                             {{x, static_cast<size_t>(B * S * H * 4)}}))
+    return rc;
+  if (int rc = check_device()) return rc;
+  (void)hipGetLastError();
+  const int64_t T0 = ceil_div(S, kTile);
+  float* part_s = static_cast<float*>(ws);
+  float* part_c = reinterpret_cast<float*>(static_cast<char*>(ws) + need / 2);
+  const hipStream_t s = as_stream(stream);
+  if (int rc = launched(adaln::launch_token_level0(x, part_s, part_c, B, S, H, s))) return rc;
+  return launched(adaln::launch_tree_fold(part_s, part_c, out, B, T0, H, s));
+}
+
+int adaln_selftest(void) {
+  if (int rc = check_device()) return rc;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ADALN_ERR_DEVICE;
+  int v = g_probe_verdict[dev].load(std::memory_order_acquire);
+  if (v == 0) {
+    const int fails = run_probe();
+    g_probe_failures[dev].store(fails < 0 ? 1 : fails, std::memory_order_relaxed);
+    v = fails == 0 ? 1 : 2;
+    g_probe_verdict[dev].store(v, std::memory_order_release);
+  }
+  return v == 1 ? ADALN_OK : g_probe_failures[dev].load(std::memory_order_relaxed);
+}
+
+}  // extern "C"

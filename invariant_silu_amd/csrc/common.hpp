@@ -1,0 +1,98 @@
+// Shared device helpers for the AdaLN final-modulation kernels (gfx950).
+//
+// Numerics follow the autocast rounding points described in miles_diffusion
+// pull request 108 ("Fused-norm rounding points"): fp32 LayerNorm, (1 + scale)
+// rounded once to bf16, fp32 modulation, one bf16 rounding of the output.
+// Everything is built with -ffp-contract=off: every float operation below is
+// one IEEE operation, and a fused multiply-add appears only where it is
+// written out.  bf16 stores use the hardware round-to-nearest-even conversion.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace adaln {
+
+constexpr int kD = 3072;            // hidden width D (= conditioning width K)
+constexpr int kN = 2 * kD;          // projection width N: (scale | shift)
+constexpr int kChunks = kD / 8;     // 16-byte chunks (8 bf16) per row: 384
+constexpr int kTile = 32;           // tokens per level-0 tile of the token tree
+constexpr int kMaxFoldLevels = 5;   // S <= 32^6 tokens
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round-to-nearest-even float -> bf16 (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  bf16x2_t r = __builtin_convertvector(v, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return static_cast<uint16_t>(pack_bf16x2(f, 0.0f) & 0xffffu);
+}
+// bf16 value of an fp32 number, as fp32 (round to nearest even).
+__device__ __forceinline__ float round_bf16(float f) { return bf_lo(f32_to_bf16(f)); }
+
+__device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
+  f[0] = bf_lo(v.x); f[1] = bf_hi(v.x);
+  f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
+  f[4] = bf_lo(v.z); f[5] = bf_hi(v.z);
+  f[6] = bf_lo(v.w); f[7] = bf_hi(v.w);
+}
+__device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
+  uint4 r;
+  r.x = pack_bf16x2(f[0], f[1]);
+  r.y = pack_bf16x2(f[2], f[3]);
+  r.z = pack_bf16x2(f[4], f[5]);
+  r.w = pack_bf16x2(f[6], f[7]);
+  return r;
+}
+
+__device__ __forceinline__ uint4 ld16(const uint16_t* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ void st16(uint16_t* p, const uint4& v) {
+  *reinterpret_cast<uint4*>(p) = v;
+}
+
+// Sum over the 64 lanes of a wave as a pairwise tree over lane index
+// (xor 1, 2, 4, ..., 32).  IEEE addition commutes, so every lane ends with
+// the same bits; the tree depends only on which value sits in which lane.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// SiLU and its derivative, evaluated in float64 and rounded once to float32
+// (RL-Kernel pull request 538, review thread: silu'(z) = s (1 + z (1 - s))).
+__device__ __forceinline__ float silu_f32(float z) {
+  const double zd = z;
+  return static_cast<float>(zd / (1.0 + exp(-zd)));
+}
+__device__ __forceinline__ float dsilu_f32(float z) {
+  const double zd = z;
+  const double s = 1.0 / (1.0 + exp(-zd));
+  return static_cast<float>(s * (1.0 + zd * (1.0 - s)));
+}
+
+// One Neumaier step: t = s + x; c += exact rounding error of that add.
+// The branch-free form picks the larger-magnitude operand for Fast2Sum, so
+// c gets the same exact error term as the textbook |s| >= |x| branch.
+__device__ __forceinline__ void neumaier_add(float& s, float& c, float x) {
+  const float t = s + x;
+  const bool big = __builtin_fabsf(s) >= __builtin_fabsf(x);
+  const float hi = big ? s : x;
+  const float lo = big ? x : s;
+  c = c + ((hi - t) + lo);
+  s = t;
+}
+
+}  // namespace adaln

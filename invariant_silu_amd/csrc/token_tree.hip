@@ -1,0 +1,165 @@
+// Fixed token-sum tree (RL-Kernel pull request 538: "What" -- fixed 32-way
+// trees whose shape depends only on S -- and the review-thread fix of
+// token_sum.cu -- 32-token tiles summed in ascending order with Neumaier
+// compensation, sums and corrections folded level by level, one final add).
+//
+// Level 0 turns every 32-token tile of every sample into a pair (s, c).
+// Level k >= 1 turns every run of 32 consecutive level-(k-1) nodes into one
+// node: for each child in ascending order, one Neumaier step on the child's s,
+// then the child's c is added to the node's c.  The root's s + c is the sum.
+// Tiles restart at token 0 of each sample, so a sample's sum is the same bytes
+// whatever the batch size or the sample's position in the batch.
+//
+// token_level0_kernel: one thread per (sample, tile, column), for the
+//   stand-alone token_tree_sum (the norm backward computes its own level 0).
+// tree_fold_kernel: one block per (sample, 64 columns); 4 waves compute the
+//   level-1 nodes (4 at a time, one per wave); one wave then streams them
+//   through levels 2.. with per-level running nodes kept in registers, which
+//   is the same arithmetic as building each level in turn.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace adaln {
+
+namespace {
+
+constexpr int kFoldCols = 64;
+constexpr int kFoldLanes = 4;
+
+__global__ __launch_bounds__(256) void token_level0_kernel(const float* __restrict__ x,
+                                                           float* __restrict__ part_s,
+                                                           float* __restrict__ part_c,
+                                                           int64_t S, int64_t H, int64_t T0) {
+  const int64_t col = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t tile = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  if (col >= H) return;
+  const int64_t s0 = tile * kTile;
+  const int n = static_cast<int>((S - s0) < kTile ? (S - s0) : kTile);
+  const float* xp = x + (b * S + s0) * H + col;
+  float s = 0.0f, c = 0.0f;
+  for (int i = 0; i < n; ++i) neumaier_add(s, c, xp[static_cast<int64_t>(i) * H]);
+  part_s[(b * T0 + tile) * H + col] = s;
+  part_c[(b * T0 + tile) * H + col] = c;
+}
+
+__global__ __launch_bounds__(kFoldCols * kFoldLanes) void tree_fold_kernel(
+    const float* __restrict__ part_s, const float* __restrict__ part_c, float* __restrict__ out,
+    int64_t T0, int64_t H, int levels) {
+  __shared__ float lds_s[kFoldLanes][kFoldCols];
+  __shared__ float lds_c[kFoldLanes][kFoldCols];
+  const int q = threadIdx.x / kFoldCols;           // node lane (= wave)
+  const int cl = threadIdx.x % kFoldCols;
+  const int64_t col = static_cast<int64_t>(blockIdx.x) * kFoldCols + cl;
+  const bool ok = col < H;
+  const int64_t b = blockIdx.y;
+  const float* ps = part_s + b * T0 * H + col;
+  const float* pc = part_c + b * T0 * H + col;
+
+  if (levels == 0) {                                // one tile: s + c
+    if (q == 0 && ok) out[b * H + col] = ps[0] + pc[0];
+    return;
+  }
+  const int64_t T1 = (T0 + kTile - 1) / kTile;
+
+  // running nodes of levels 2 .. levels (index 0 = level 2)
+  float rs[kMaxFoldLevels - 1], rc[kMaxFoldLevels - 1];
+  int rn[kMaxFoldLevels - 1];
+#pragma unroll
+  for (int l = 0; l < kMaxFoldLevels - 1; ++l) { rs[l] = 0.0f; rc[l] = 0.0f; rn[l] = 0; }
+  const int top = levels - 2;                       // index of the root level (levels >= 2)
+
+  // push a finished node into level (2 + start); cascades up through full nodes
+  auto push = [&](int start, float s, float c) {
+    bool active = true;
+#pragma unroll
+    for (int l = 0; l < kMaxFoldLevels - 1; ++l) {
+      if (active && l >= start) {
+        neumaier_add(rs[l], rc[l], s);
+        rc[l] = rc[l] + c;
+        rn[l] += 1;
+        if (l == top || rn[l] < kTile) {
+          active = false;
+        } else {
+          s = rs[l]; c = rc[l];
+          rs[l] = 0.0f; rc[l] = 0.0f; rn[l] = 0;
+        }
+      }
+    }
+  };
+
+  float root_s = 0.0f, root_c = 0.0f;
+  for (int64_t n0 = 0; n0 < T1; n0 += kFoldLanes) {
+    const int64_t node = n0 + q;
+    float s = 0.0f, c = 0.0f;
+    if (ok && node < T1) {
+      const int64_t t0 = node * kTile;
+      const int cnt = static_cast<int>((T0 - t0) < kTile ? (T0 - t0) : kTile);
+      float vs[kTile], vc[kTile];
+#pragma unroll
+      for (int i = 0; i < kTile; ++i) {
+        vs[i] = i < cnt ? ps[(t0 + i) * H] : 0.0f;
+        vc[i] = i < cnt ? pc[(t0 + i) * H] : 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < kTile; ++i) {
+        if (i < cnt) {
+          neumaier_add(s, c, vs[i]);
+          c = c + vc[i];
+        }
+      }
+    }
+    __syncthreads();
+    lds_s[q][cl] = s;
+    lds_c[q][cl] = c;
+    __syncthreads();
+    if (q == 0) {
+      const int nn = static_cast<int>((T1 - n0) < kFoldLanes ? (T1 - n0) : kFoldLanes);
+      for (int k = 0; k < nn; ++k) {
+        if (levels == 1) { root_s = lds_s[k][cl]; root_c = lds_c[k][cl]; }
+        else push(0, lds_s[k][cl], lds_c[k][cl]);
+      }
+    }
+  }
+  if (q != 0 || !ok) return;
+  if (levels >= 2) {
+    // flush partial nodes bottom-up
+#pragma unroll
+    for (int l = 0; l < kMaxFoldLevels - 2; ++l) {
+      if (l < top && rn[l] > 0) {
+        const float s = rs[l], c = rc[l];
+        rs[l] = 0.0f; rc[l] = 0.0f; rn[l] = 0;
+        push(l + 1, s, c);
+      }
+    }
+#pragma unroll
+    for (int l = 0; l < kMaxFoldLevels - 1; ++l)
+      if (l == top) { root_s = rs[l]; root_c = rc[l]; }
+  }
+  out[b * H + col] = root_s + root_c;
+}
+
+}  // namespace
+
+hipError_t launch_token_level0(const float* x, float* part_s, float* part_c, int64_t B, int64_t S,
+                               int64_t H, hipStream_t s) {
+  const int64_t T0 = (S + kTile - 1) / kTile;
+  hipLaunchKernelGGL(token_level0_kernel,
+                     dim3(static_cast<unsigned>((H + 255) / 256), static_cast<unsigned>(T0),
+                          static_cast<unsigned>(B)),
+                     dim3(256), 0, s, x, part_s, part_c, S, H, T0);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_fold(const float* part_s, const float* part_c, float* out, int64_t B,
+                            int64_t T0, int64_t H, hipStream_t s) {
+  int levels = 0;
+  for (int64_t n = T0; n > 1; n = (n + kTile - 1) / kTile) ++levels;
+  if (levels > kMaxFoldLevels) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(tree_fold_kernel,
+                     dim3(static_cast<unsigned>((H + kFoldCols - 1) / kFoldCols), static_cast<unsigned>(B)),
+                     dim3(kFoldCols * kFoldLanes), 0, s, part_s, part_c, out, T0, H, levels);
+  return hipGetLastError();
+}
+
+}  // namespace adaln

@@ -1,0 +1,152 @@
+"""PyTorch-facing wrappers of the C ABI (include/adaln.h).
+
+PyTorch supplies device memory and the current HIP stream; every computation
+runs in the library's kernels.  Tensors are made contiguous, and any tensor
+whose data pointer is not 16-byte aligned is copied to an aligned buffer
+(``.contiguous()`` alone does not realign a view with a storage offset --
+RL-Kernel pull request 538, review thread on misaligned views).
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import lib as _lib
+
+D = 3072
+N = 2 * D
+EPS = 1e-6
+
+
+def aligned(t: torch.Tensor) -> torch.Tensor:
+    """Contiguous tensor whose data pointer is 16-byte aligned (copies if needed)."""
+    t = t.contiguous()
+    if t.data_ptr() % 16 != 0:
+        out = torch.empty(t.shape, dtype=t.dtype, device=t.device)
+        out.copy_(t)
+        t = out
+    return t
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _check(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (the HIP library has no CPU path)")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _ws(op: int, B: int, S: int, H: int, device) -> torch.Tensor:
+    n = _lib.workspace_bytes(op, B, S, H)
+    if n == 0:
+        raise ValueError(f"unsupported sizes for op {op}: B={B} S={S} H={H}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def proj_fwd(temb: torch.Tensor, W: torch.Tensor, bias: torch.Tensor) -> torch.Tensor:
+    """emb [B, 6144] bf16 = bf16(SiLU(temb) W^T + b) = (scale | shift)."""
+    for t, n in ((temb, "temb"), (W, "W"), (bias, "bias")):
+        _check(t, torch.bfloat16, n)
+    temb, W, bias = aligned(temb), aligned(W), aligned(bias)
+    B = temb.shape[0]
+    emb = torch.empty((B, N), dtype=torch.bfloat16, device=temb.device)
+    ws = _ws(_lib.OP_PROJ_FWD, B, 1, D, temb.device)
+    _lib.call("adaln_proj_fwd", temb.data_ptr(), W.data_ptr(), bias.data_ptr(), emb.data_ptr(),
+              ws.data_ptr(), ws.numel(), B, temb.shape[1], W.shape[0], _stream(temb.device))
+    return emb
+
+
+def norm_mod_fwd(x: torch.Tensor, emb: torch.Tensor, eps: float = EPS):
+    """(out bf16 [B,S,D], mean fp32 [B,S], rstd fp32 [B,S])."""
+    _check(x, torch.bfloat16, "x")
+    _check(emb, torch.bfloat16, "emb")
+    x, emb = aligned(x), aligned(emb)
+    B, S, Dx = x.shape
+    out = torch.empty_like(x)
+    mean = torch.empty((B, S), dtype=torch.float32, device=x.device)
+    rstd = torch.empty((B, S), dtype=torch.float32, device=x.device)
+    _lib.call("adaln_norm_mod_fwd", x.data_ptr(), emb.data_ptr(), out.data_ptr(), mean.data_ptr(),
+              rstd.data_ptr(), B, S, Dx, float(eps), _stream(x.device))
+    return out, mean, rstd
+
+
+def norm_mod_bwd(g: torch.Tensor, x: torch.Tensor, mean: torch.Tensor, rstd: torch.Tensor,
+                 emb: torch.Tensor):
+    """(dx bf16 [B,S,D], d_emb fp32 [B, 2D] = (d_scale | d_shift))."""
+    _check(g, torch.bfloat16, "g")
+    _check(x, torch.bfloat16, "x")
+    _check(mean, torch.float32, "mean")
+    _check(rstd, torch.float32, "rstd")
+    _check(emb, torch.bfloat16, "emb")
+    g, x, mean, rstd, emb = (aligned(t) for t in (g, x, mean, rstd, emb))
+    B, S, Dx = x.shape
+    dx = torch.empty_like(x)
+    d_emb = torch.empty((B, N), dtype=torch.float32, device=x.device)
+    ws = _ws(_lib.OP_NORM_MOD_BWD, B, S, Dx, x.device)
+    _lib.call("adaln_norm_mod_bwd", g.data_ptr(), x.data_ptr(), mean.data_ptr(), rstd.data_ptr(),
+              emb.data_ptr(), dx.data_ptr(), d_emb.data_ptr(), ws.data_ptr(), ws.numel(), B, S, Dx,
+              _stream(x.device))
+    return dx, d_emb
+
+
+def proj_bwd(d_emb: torch.Tensor, temb: torch.Tensor, W: torch.Tensor):
+    """(dW bf16 [6144, 3072], db bf16 [6144], dtemb bf16 [B, 3072])."""
+    _check(d_emb, torch.float32, "d_emb")
+    _check(temb, torch.bfloat16, "temb")
+    _check(W, torch.bfloat16, "W")
+    d_emb, temb, W = aligned(d_emb), aligned(temb), aligned(W)
+    B = temb.shape[0]
+    dW = torch.empty_like(W)
+    db = torch.empty((W.shape[0],), dtype=torch.bfloat16, device=W.device)
+    dtemb = torch.empty_like(temb)
+    ws = _ws(_lib.OP_PROJ_BWD, B, 1, D, W.device)
+    _lib.call("adaln_proj_bwd", d_emb.data_ptr(), temb.data_ptr(), W.data_ptr(), dW.data_ptr(),
+              db.data_ptr(), dtemb.data_ptr(), ws.data_ptr(), ws.numel(), B, temb.shape[1],
+              W.shape[0], _stream(W.device))
+    return dW, db, dtemb
+
+
+def token_tree_sum(x: torch.Tensor) -> torch.Tensor:
+    """Compensated 32-token tree sum over dim 1 of an fp32 [B, S, H] tensor."""
+    _check(x, torch.float32, "x")
+    x = aligned(x)
+    B, S, H = x.shape
+    out = torch.empty((B, H), dtype=torch.float32, device=x.device)
+    ws = _ws(_lib.OP_TOKEN_TREE_SUM, B, S, H, x.device)
+    _lib.call("token_tree_sum", x.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel(), B, S, H,
+              _stream(x.device))
+    return out
+
+
+def selftest() -> int:
+    return int(_lib.load().adaln_selftest())
+
+
+class AdaLNFinal(torch.autograd.Function):
+    """out = LayerNorm(x) * (1 + scale) + shift with (scale, shift) = (SiLU(temb) W^T + b).chunk(2).
+
+    Inputs: x [B, S, 3072] bf16, temb [B, 3072] bf16, W [6144, 3072] bf16,
+    b [6144] bf16.  Saves x, temb, W, emb, mean and rstd (8 bytes per row of
+    LayerNorm state, not the normalized activations)."""
+
+    @staticmethod
+    def forward(ctx, x, temb, W, b, eps=EPS):
+        emb = proj_fwd(temb, W, b)
+        out, mean, rstd = norm_mod_fwd(x, emb, eps)
+        ctx.save_for_backward(x, temb, W, emb, mean, rstd)
+        return out
+
+    @staticmethod
+    def backward(ctx, g):
+        x, temb, W, emb, mean, rstd = ctx.saved_tensors
+        g = g.to(torch.bfloat16)
+        dx, d_emb = norm_mod_bwd(g, x, mean, rstd, emb)
+        dW, db, dtemb = proj_bwd(d_emb, temb, W)
+        return dx, dtemb, dW, db, None
+
+
+def adaln_final(x, temb, W, b, eps=EPS):
+    return AdaLNFinal.apply(x, temb, W, b, eps)

@@ -132,6 +132,24 @@ def projection(a, W, bias, ar: Arith, want_abs=False):
     return (emb, A) if want_abs else emb
 
 
+def _ln_stats(x2, ar: Arith, eps: float = EPS):
+    """Per-row mean, biased variance and rstd of x2 [R, D] (two passes)."""
+    R, D = x2.shape
+    xT = np.ascontiguousarray(x2.T)                                   # [D, R]
+    Dt = ar.c(D)
+    mean = ar.sum(iter(xT), (R,)) / Dt
+    dT = xT - mean[None, :]
+    var = ar.sum((dT[d] * dT[d] for d in range(D)), (R,)) / Dt
+    eps_t = ar.c(np.float32(eps))
+    rstd = ar.c(1.0) / np.sqrt(var + eps_t)
+    return mean, var, rstd
+
+
+def _normalize(x2, mean, rstd, ar: Arith):
+    """n = (x - mean) * rstd, stored as the fp32 LayerNorm output."""
+    return ar.f32((x2 - mean[:, None]) * rstd[:, None])
+
+
 def forward(inp: dict, mode: str = "fp32", eps: float = EPS, want_abs: bool = False):
     """Forward pass.  ``inp`` holds bf16 bit arrays x, temb, W, bias.
 
@@ -149,15 +167,8 @@ def forward(inp: dict, mode: str = "fp32", eps: float = EPS, want_abs: bool = Fa
     one = ar.c(1.0)
     m = ar.bf16(one + scale)
 
-    R = B * S
-    xT = np.ascontiguousarray(x.reshape(R, D).T)                     # [D, R]
-    Dt = ar.c(D)
-    mean = ar.sum(iter(xT), (R,)) / Dt
-    dT = xT - mean[None, :]
-    var = ar.sum((dT[d] * dT[d] for d in range(D)), (R,)) / Dt
-    eps_t = ar.c(np.float32(eps))
-    rstd = ar.c(1.0) / np.sqrt(var + eps_t)
-    n = ar.f32((x.reshape(R, D) - mean[:, None]) * rstd[:, None]).reshape(B, S, D)
+    mean, var, rstd = _ln_stats(x.reshape(B * S, D), ar, eps)
+    n = _normalize(x.reshape(B * S, D), mean, rstd, ar).reshape(B, S, D)
     out = ar.bf16(n * m[:, None, :] + shift[:, None, :])
     res = dict(a=a, emb=emb, m=m, mean=mean.reshape(B, S), rstd=rstd.reshape(B, S),
                n=n, out=out, var=var.reshape(B, S))
@@ -247,3 +258,44 @@ def sgld_forward_out(inp: dict, fwd: dict):
     shift = np.asarray(fwd["emb"], dtype=np.float32)[:, D:]
     prod = bf16_round(n16 * m[:, None, :])
     return bf16_round(prod + shift[:, None, :])
+
+
+# ------------------------------------------------------- sampled evaluation --
+# For batches too large to run whole, the same steps evaluated for a subset of
+# outputs.  Every value goes through the functions above.
+
+def ln_stats(inp: dict, mode: str = "fp32", eps: float = EPS):
+    """mean, rstd [B, S] of every row (the saved LayerNorm state)."""
+    ar = Arith(mode)
+    x = ar.c(_val(inp, "x"))
+    B, S, D = x.shape
+    mean, _, rstd = _ln_stats(x.reshape(B * S, D), ar, eps)
+    return mean.reshape(B, S), rstd.reshape(B, S)
+
+
+def d_emb_columns(inp: dict, cols, mode: str = "fp32", eps: float = EPS, stats=None):
+    """d_emb[:, cols] (d_scale for cols < D, d_shift for cols >= D), every sample."""
+    ar = Arith(mode)
+    x = ar.c(_val(inp, "x"))
+    g = ar.c(_val(inp, "g"))
+    B, S, D = x.shape
+    mean, rstd = stats if stats is not None else ln_stats(inp, mode, eps)
+    cols = np.asarray(cols)
+    dcol = np.where(cols < D, cols, cols - D)
+    xs = x[:, :, dcol]                                                # [B, S, C]
+    gs = g[:, :, dcol]
+    n = _normalize(xs.reshape(B * S, -1), mean.reshape(-1), rstd.reshape(-1), ar).reshape(xs.shape)
+    terms = np.where((cols < D)[None, None, :], gs * n, gs)
+    out = ar.sum((terms[:, s, :] for s in range(S)), (B, len(cols)))
+    return ar.f32(out)
+
+
+def param_grads_rows(inp: dict, rows, mode: str = "fp32", eps: float = EPS, stats=None):
+    """dW[rows, :] and db[rows] (bf16 bits) over the whole batch."""
+    ar = Arith(mode)
+    a = silu_act(_val(inp, "temb"), ar)                               # [B, K]
+    de = d_emb_columns(inp, rows, mode, eps, stats)                   # [B, R]
+    B = a.shape[0]
+    dW = ar.bf16(ar.sum((de[b][:, None] * a[b][None, :] for b in range(B)), (len(rows), a.shape[1])))
+    db = ar.bf16(ar.sum((de[b] for b in range(B)), (len(rows),)))
+    return _bits(dW), _bits(db), de

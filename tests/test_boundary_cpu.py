@@ -1,0 +1,87 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function the
+header declares, the binding declares the same names, workspace sizes follow
+the documented formulas, and argument validation answers before any device
+work (no kernel runs here: there is no GPU in this environment)."""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from invariant_silu_amd import lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "adaln.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(lib.LIB_PATH):
+        pytest.skip("libadaln.so not built (run __graft_entry__.build())")
+    return lib.load()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for fn in ("adaln_proj_fwd", "adaln_proj_bwd", "adaln_norm_mod_fwd", "adaln_norm_mod_bwd",
+               "token_tree_sum"):
+        assert fn in names
+    assert names == set(lib.EXPORTS), names ^ set(lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared():
+        assert hasattr(L, name), name
+        assert isinstance(getattr(L, name), ctypes._CFuncPtr)
+
+
+def test_abi_version_and_strerror(L):
+    assert L.adaln_abi_version() == 1
+    for code in range(-7, 1):
+        assert len(lib.strerror(code)) >= 2
+
+
+def test_workspace_sizes(L):
+    pad = lambda n: (n + 255) // 256 * 256   # noqa: E731
+    for B, S in [(1, 31), (2, 1024), (1, 4096), (64, 1024), (3, 6889)]:
+        T0 = math.ceil(S / 32)
+        assert lib.workspace_bytes(lib.OP_NORM_MOD_BWD, B, S, 3072) == 2 * pad(B * T0 * 6144 * 4)
+        assert lib.workspace_bytes(lib.OP_TOKEN_TREE_SUM, B, S, 100) == 2 * pad(B * T0 * 100 * 4)
+        assert lib.workspace_bytes(lib.OP_PROJ_FWD, B, S, 3072) == pad(B * 3072 * 2)
+        assert lib.workspace_bytes(lib.OP_PROJ_BWD, B, S, 3072) == pad(B * 3072 * 2) + pad(32 * B * 3072 * 8)
+    assert lib.workspace_bytes(lib.OP_NORM_MOD_BWD, 1, 10, 1024) == 0
+    assert lib.workspace_bytes(99, 1, 10, 3072) == 0
+    assert lib.workspace_bytes(lib.OP_PROJ_FWD, 0, 1, 3072) == 0
+
+
+def test_validation_before_device_work(L):
+    """NULL pointers and bad shapes are reported without touching a device."""
+    assert L.adaln_proj_fwd(None, None, None, None, None, 0, 1, 3072, 6144, None) == lib.ERR_NULL
+    p = 4096   # a fake, aligned, non-null address: shape checks come first
+    assert L.adaln_proj_fwd(p, p, p, p, p, 1 << 20, 1, 1024, 6144, None) == lib.ERR_SHAPE
+    assert L.adaln_norm_mod_fwd(p, p, p, p, p, 1, 0, 3072, 1e-6, None) == lib.ERR_SHAPE
+    assert L.token_tree_sum(p, p, p, 1 << 20, 1, 1, 0, None) == lib.ERR_SHAPE
+    assert L.adaln_norm_mod_fwd(p + 2, p, p, p, p, 1, 1, 3072, 1e-6, None) == lib.ERR_ALIGN
+    # overlapping output and input is caught before the device check
+    assert L.adaln_norm_mod_fwd(p, p + (1 << 20), p, p + (2 << 20), p + (3 << 20), 1, 4, 3072, 1e-6,
+                                None) == lib.ERR_OVERLAP
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    saved = lib._lib
+    lib._lib = None
+    try:
+        with pytest.raises(ImportError):
+            lib.load(str(tmp_path / "missing.so"))
+    finally:
+        lib._lib = saved

@@ -461,3 +461,17 @@ def test_teeth_dropped_beta_term_caught(monkeypatch):
     monkeypatch.setattr(adaln, "backward", bwd)
     ok, worst = _fd_check(_fd_inputs())
     assert not ok
+
+
+def test_sampled_evaluation_matches_full_oracle():
+    """The sampled helpers (used where the full oracle would be too slow) give
+    the same bytes as the full backward on a small batch."""
+    inp = _small_inputs(3, 40, seed=19)
+    f = adaln.forward(inp)
+    b = adaln.backward(inp, f)
+    mean, rstd = adaln.ln_stats(inp)
+    assert mean.tobytes() == f["mean"].tobytes() and rstd.tobytes() == f["rstd"].tobytes()
+    cols = np.array([0, 5, 3071, 3072, 4000, 6143])
+    assert adaln.d_emb_columns(inp, cols).tobytes() == b["d_emb"][:, cols].tobytes()
+    dW, db, _ = adaln.param_grads_rows(inp, cols)
+    assert np.array_equal(dW, b["dW_bits"][cols]) and np.array_equal(db, b["db_bits"][cols])
