@@ -49,6 +49,23 @@ def dominant_kernel_bytes(B: int, S: int) -> int:
     return 6 * B * S * D + 8 * B * S + 2 * D * B
 
 
+def pmc_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed PMC record,
+    or None when the kernel's sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    try:
+        rec = json.load(open(path))
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            h.update(open(os.path.join(ROOT, src), "rb").read())
+        if h.hexdigest() != rec["sha256"]:
+            return None
+        return int(rec["fetch_bytes"] + rec["write_bytes"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,7 +216,7 @@ def main() -> int:
                    "step_frac_of_peak": round(step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)},
         "roofline": {"bound": "hbm", "kernel": "norm_mod_bwd_kernel (dx + level-0 token tiles)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": pmc_traffic(),
                      "bytes_per_launch": k_bytes, "avg_launch_ms": round(k_mean_ms, 5),
                      "median_launch_ms": round(k_ms[len(k_ms) // 2], 5)},
     }
