@@ -2,8 +2,8 @@
 """Throughput of the batch-invariant AdaLN final modulation, forward + backward.
 
 One step is the whole hot path over one batch of synthetic input, through the
-C ABI: adaln_proj_fwd -> adaln_norm_mod_fwd -> adaln_norm_mod_bwd_tiles ->
-token_tree_fold -> adaln_proj_bwd.  Default workload: one 1024x1024 image
+C ABI: adaln_proj_fwd -> adaln_norm_mod_fwd -> adaln_norm_mod_bwd_dx ->
+adaln_norm_mod_bwd_tiles -> token_tree_fold -> adaln_proj_bwd.  Default workload: one 1024x1024 image
 stream, B = 1, S = 4096 tokens, D = 3072, bf16 storage, 1% outlier rows x20.
 
 Inputs are resident in HBM before the timed region.  The step rotates over
@@ -11,8 +11,9 @@ several independent copies of every buffer (parameters included), so no step
 finds the previous step's data in the 256 MB MALL; reuse inside one step (x
 read by the forward and the backward, W by both projections) is left as is.
 
-Prints ONE JSON line.  `roofline` covers the dominant kernel (dx + level-0 token
-tiles of the norm backward), timed with HIP events on the stream it runs on;
+Prints ONE JSON line.  `roofline` covers the dominant kernel (the row pass of the
+norm backward: g, x in, dx out), timed in every timed step with HIP events that
+its own dispatch carries on the stream it runs on (adaln_timing_begin/end);
 `cpu_baseline` is the NumPy oracle timed on this host on the same workload.
 """
 
@@ -44,7 +45,7 @@ def algorithmic_bytes(B: int, S: int) -> int:
 
 
 def dominant_kernel_bytes(B: int, S: int) -> int:
-    """norm backward, level-0 stage: g and x read, dx written, mean/rstd read,
+    """norm backward, row pass: g and x read, dx written, mean/rstd read,
     scale read (per sample)."""
     return 6 * B * S * D + 8 * B * S + 2 * D * B
 
@@ -78,7 +79,7 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(inp: dict, reps: int = 2) -> dict:
+def cpu_baseline(inp: dict, reps: int = 8) -> dict:
     """The oracle (NumPy, single-threaded element-wise loops) on the same batch."""
     from oracle import adaln
     t0 = time.perf_counter()
@@ -123,7 +124,6 @@ def main() -> int:
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
     base = {k: to_dev(inp[k]) for k in ("x", "temb", "W", "bias", "g")}
-    ws_pf = lib.workspace_bytes(lib.OP_PROJ_FWD, B, S, D)
     ws_nb = lib.workspace_bytes(lib.OP_NORM_MOD_BWD, B, S, D)
     ws_pb = lib.workspace_bytes(lib.OP_PROJ_BWD, B, S, D)
     T0 = math.ceil(S / 32)
@@ -140,7 +140,6 @@ def main() -> int:
             dW=torch.empty((N, D), dtype=torch.bfloat16, device=dev),
             db=torch.empty((N,), dtype=torch.bfloat16, device=dev),
             dtemb=torch.empty((B, D), dtype=torch.bfloat16, device=dev),
-            ws_pf=torch.empty(ws_pf, dtype=torch.uint8, device=dev),
             ws_nb=torch.empty(ws_nb, dtype=torch.uint8, device=dev),
             ws_pb=torch.empty(ws_pb, dtype=torch.uint8, device=dev),
         )
@@ -151,22 +150,17 @@ def main() -> int:
     sets = [new_set() for _ in range(nsets)]
     stream = torch.cuda.current_stream(dev)
     st = stream.cuda_stream
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-
-    def step(s, evpair=None):
+    def step(s):
         p = lambda k: s[k].data_ptr()   # noqa: E731
-        lib.check("adaln_proj_fwd", L.adaln_proj_fwd(p("temb"), p("W"), p("bias"), p("emb"), p("ws_pf"),
-                                                     ws_pf, B, D, N, st))
+        lib.check("adaln_proj_fwd", L.adaln_proj_fwd(p("temb"), p("W"), p("bias"), p("emb"), B, D, N, st))
         lib.check("adaln_norm_mod_fwd", L.adaln_norm_mod_fwd(p("x"), p("emb"), p("out"), p("mean"),
                                                              p("rstd"), B, S, D, 1e-6, st))
-        if evpair is not None:
-            evpair[0].record(stream)
+        lib.check("adaln_norm_mod_bwd_dx",
+                  L.adaln_norm_mod_bwd_dx(p("g"), p("x"), p("mean"), p("rstd"), p("emb"), p("dx"),
+                                          B, S, D, st))
         lib.check("adaln_norm_mod_bwd_tiles",
-                  L.adaln_norm_mod_bwd_tiles(p("g"), p("x"), p("mean"), p("rstd"), p("emb"), p("dx"),
-                                             p("ws_nb"), ws_nb, B, S, D, st))
-        if evpair is not None:
-            evpair[1].record(stream)
+                  L.adaln_norm_mod_bwd_tiles(p("g"), p("x"), p("mean"), p("rstd"), p("ws_nb"), ws_nb,
+                                             B, S, D, st))
         lib.check("token_tree_fold", L.token_tree_fold(p("ws_nb"), p("d_emb"), B, T0, N, st))
         lib.check("adaln_proj_bwd", L.adaln_proj_bwd(p("d_emb"), p("temb"), p("W"), p("dW"), p("db"),
                                                      p("dtemb"), p("ws_pb"), ws_pb, B, D, N, st))
@@ -174,16 +168,20 @@ def main() -> int:
     for i in range(args.warmup):
         step(sets[i % nsets])
     torch.cuda.synchronize()
+    lib.check("adaln_timing_begin", L.adaln_timing_begin(args.steps))
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(sets[i % nsets], ev[i])
+        step(sets[i % nsets])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    import ctypes
+    ms_buf = (ctypes.c_float * args.steps)()
+    n_timed = L.adaln_timing_end(ms_buf, args.steps)
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     tokens_per_s = B * S / (ms_per_step / 1e3)
     step_bytes = algorithmic_bytes(B, S)
-    k_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    k_ms = sorted(ms_buf[i] for i in range(n_timed))
     k_mean_ms = sum(k_ms) / len(k_ms)
     k_bytes = dominant_kernel_bytes(B, S)
     achieved = k_bytes / (k_mean_ms / 1e3) / 1e9
@@ -214,7 +212,7 @@ def main() -> int:
                    "buffer_sets": nsets, "step_algorithmic_bytes": step_bytes,
                    "step_gbps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
                    "step_frac_of_peak": round(step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)},
-        "roofline": {"bound": "hbm", "kernel": "norm_mod_bwd_kernel (dx + level-0 token tiles)",
+        "roofline": {"bound": "hbm", "kernel": "norm_mod_bwd_dx_kernel",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": pmc_traffic(),
                      "bytes_per_launch": k_bytes, "avg_launch_ms": round(k_mean_ms, 5),

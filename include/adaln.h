@@ -63,16 +63,15 @@ enum adaln_status {
 };
 
 enum adaln_op {
-  ADALN_OP_PROJ_FWD = 1,
   ADALN_OP_NORM_MOD_BWD = 2,
   ADALN_OP_PROJ_BWD = 3,
   ADALN_OP_TOKEN_TREE_SUM = 4
 };
 
 /* Workspace bytes an entry point needs (0 for an unknown op or bad sizes).
- *   PROJ_FWD:       H = K (3072), S ignored.  B*K*2 bytes (the SiLU activations).
  *   NORM_MOD_BWD:   H = D (3072).  2 * B * ceil(S/32) * 2D * 4 bytes (level-0 pairs).
- *   PROJ_BWD:       H = K (3072), S ignored.  B*K*2 (activations) + 32*B*K*8 (fp64 partials).
+ *   PROJ_BWD:       H = K (3072), S ignored.  B*K*2 (SiLU activations, used when
+ *                   B > 4) + 32*B*K*8 (fp64 partials of dtemb).
  *   TOKEN_TREE_SUM: 2 * B * ceil(S/32) * H * 4 bytes.
  * Each region is padded to 256 bytes. */
 size_t adaln_workspace_bytes(int op, int64_t B, int64_t S, int64_t H);
@@ -84,8 +83,7 @@ size_t adaln_workspace_bytes(int op, int64_t B, int64_t S, int64_t H);
  *   SiLU evaluated in float64; the sum accumulates exact products in fp64 in a
  *   fixed order independent of B. */
 int adaln_proj_fwd(const adaln_bf16* temb, const adaln_bf16* W, const adaln_bf16* bias,
-                   adaln_bf16* emb, void* ws, size_t ws_bytes, int64_t B, int64_t K, int64_t N,
-                   void* stream);
+                   adaln_bf16* emb, int64_t B, int64_t K, int64_t N, void* stream);
 
 /* LayerNorm + modulation forward (pull request 538, "What"; rounding points of
  * miles_diffusion pull request 108).
@@ -109,19 +107,24 @@ int adaln_norm_mod_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float*
                        const float* rstd, const adaln_bf16* emb, adaln_bf16* dx, float* d_emb,
                        void* ws, size_t ws_bytes, int64_t B, int64_t S, int64_t D, void* stream);
 
-/* The two stages of adaln_norm_mod_bwd, exported separately (the tree fold
- * can then be timed, overlapped or reused on its own).
+/* The three stages of adaln_norm_mod_bwd, exported separately (each can then be
+ * timed, overlapped or reused on its own).
  *
- * adaln_norm_mod_bwd_tiles: dx as above, plus the level-0 pairs of the token
- *   tree: `part` holds two fp32 arrays, sums then corrections, each
- *   [B, ceil(S/32), 2D] and padded to 256 bytes; part_bytes must be at least
- *   adaln_workspace_bytes(ADALN_OP_NORM_MOD_BWD, B, S, D).
- * token_tree_fold: the levels >= 1 of the tree from such pairs: `part` as
- *   written by adaln_norm_mod_bwd_tiles (H = 2D) or by the level 0 of
- *   token_tree_sum (any H), T0 = ceil(S/32) tiles per sample; out [B, H] fp32. */
+ * adaln_norm_mod_bwd_dx: dx only (arguments as in adaln_norm_mod_bwd).
+ * adaln_norm_mod_bwd_tiles: level 0 of the token tree: `part` receives two fp32
+ *   arrays, sums then corrections, each [B, ceil(S/32), 2D] (columns [0, D) of
+ *   g * n for d_scale, [D, 2D) of g for d_shift) and each padded to 256 bytes;
+ *   part_bytes must be at least adaln_workspace_bytes(ADALN_OP_NORM_MOD_BWD, B, S, D).
+ * token_tree_fold: levels >= 1 of the tree from such pairs: `part` as written by
+ *   adaln_norm_mod_bwd_tiles (H = 2D) or by level 0 of token_tree_sum (any H),
+ *   T0 = ceil(S/32) tiles per sample, corrections at byte offset
+ *   pad256(B * T0 * H * 4); out [B, H] fp32. */
+int adaln_norm_mod_bwd_dx(const adaln_bf16* gout, const adaln_bf16* x, const float* mean,
+                          const float* rstd, const adaln_bf16* emb, adaln_bf16* dx, int64_t B,
+                          int64_t S, int64_t D, void* stream);
 int adaln_norm_mod_bwd_tiles(const adaln_bf16* gout, const adaln_bf16* x, const float* mean,
-                             const float* rstd, const adaln_bf16* emb, adaln_bf16* dx, void* part,
-                             size_t part_bytes, int64_t B, int64_t S, int64_t D, void* stream);
+                             const float* rstd, void* part, size_t part_bytes, int64_t B, int64_t S,
+                             int64_t D, void* stream);
 int token_tree_fold(const void* part, float* out, int64_t B, int64_t T0, int64_t H, void* stream);
 
 /* Projection backward (pull request 538, "What": projection backward; review
@@ -149,6 +152,16 @@ int token_tree_sum(const float* x, float* out, void* ws, size_t ws_bytes, int64_
  * The verdict is cached per device, both ways.  Returns ADALN_OK,
  * ADALN_ERR_DEVICE, or a positive count of failed probe values. */
 int adaln_selftest(void);
+
+/* Benchmarking aid: per-launch durations of the norm backward's row pass
+ * (adaln_norm_mod_bwd_dx, alone or inside adaln_norm_mod_bwd), timed with HIP
+ * events carried by the kernel dispatch itself (no extra packets in the stream).
+ * adaln_timing_begin(n) creates n event pairs; the next n launches on any stream
+ * record into them.  adaln_timing_end(ms, n) waits for the recorded launches,
+ * writes up to n durations in milliseconds, frees the events and returns the
+ * number written.  Events are host-side HIP objects; no device memory. */
+int adaln_timing_begin(int n);
+int adaln_timing_end(float* ms, int n);
 
 /* Static description of a status code. */
 const char* adaln_strerror(int status);

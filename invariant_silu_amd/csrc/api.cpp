@@ -8,6 +8,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/adaln.h"
@@ -27,6 +28,35 @@ constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_verdict[kMaxDevices];    // 0 unknown, 1 gfx950, 2 other
 std::atomic<int> g_probe_verdict[kMaxDevices];   // 0 unknown, 1 pass, 2 fail
 std::atomic<int> g_probe_failures[kMaxDevices];
+
+// Dispatch-attached timing of the norm backward's row pass (a benchmarking
+// aid): while armed, each launch records into the next free event pair.
+struct Timing {
+  std::mutex mu;
+  std::vector<hipEvent_t> start, stop;
+  size_t next = 0;
+};
+Timing g_timing;
+
+void timing_events(hipEvent_t* a, hipEvent_t* b) {
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  if (g_timing.next < g_timing.start.size()) {
+    *a = g_timing.start[g_timing.next];
+    *b = g_timing.stop[g_timing.next];
+    ++g_timing.next;
+  } else {
+    *a = nullptr;
+    *b = nullptr;
+  }
+}
+
+void timing_free_locked() {
+  for (hipEvent_t e : g_timing.start) (void)hipEventDestroy(e);
+  for (hipEvent_t e : g_timing.stop) (void)hipEventDestroy(e);
+  g_timing.start.clear();
+  g_timing.stop.clear();
+  g_timing.next = 0;
+}
 
 inline size_t pad256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -75,7 +105,6 @@ int check_device() {
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 inline int launched(hipError_t e) { return e == hipSuccess ? ADALN_OK : ADALN_ERR_LAUNCH; }
 
-size_t ws_proj_fwd(int64_t B) { return pad256(static_cast<size_t>(B * kD * 2)); }
 size_t ws_norm_bwd(int64_t B, int64_t S) {
   return 2 * pad256(static_cast<size_t>(B * ceil_div(S, kTile) * kN * 4));
 }
@@ -183,7 +212,6 @@ const char* adaln_strerror(int status) {
 size_t adaln_workspace_bytes(int op, int64_t B, int64_t S, int64_t H) {
   if (!batch_ok(B)) return 0;
   switch (op) {
-    case ADALN_OP_PROJ_FWD: return H == kD ? ws_proj_fwd(B) : 0;
     case ADALN_OP_NORM_MOD_BWD: return (H == kD && seq_ok(S)) ? ws_norm_bwd(B, S) : 0;
     case ADALN_OP_PROJ_BWD: return H == kD ? ws_proj_bwd(B) : 0;
     case ADALN_OP_TOKEN_TREE_SUM:
@@ -193,24 +221,17 @@ size_t adaln_workspace_bytes(int op, int64_t B, int64_t S, int64_t H) {
 }
 
 int adaln_proj_fwd(const adaln_bf16* temb, const adaln_bf16* W, const adaln_bf16* bias,
-                   adaln_bf16* emb, void* ws, size_t ws_bytes, int64_t B, int64_t K, int64_t N,
-                   void* stream) {
-  if (!temb || !W || !bias || !emb || !ws) return ADALN_ERR_NULL;
+                   adaln_bf16* emb, int64_t B, int64_t K, int64_t N, void* stream) {
+  if (!temb || !W || !bias || !emb) return ADALN_ERR_NULL;
   if (!batch_ok(B) || K != kD || N != kN) return ADALN_ERR_SHAPE;
-  if (!aligned16(temb) || !aligned16(W) || !aligned16(bias) || !aligned16(emb) || !aligned16(ws))
-    return ADALN_ERR_ALIGN;
-  if (ws_bytes < ws_proj_fwd(B)) return ADALN_ERR_WORKSPACE;
-  const size_t wsn = ws_proj_fwd(B);
-  if (int rc = check_overlap({{emb, static_cast<size_t>(B * kN * 2)}, {ws, wsn}},
+  if (!aligned16(temb) || !aligned16(W) || !aligned16(bias) || !aligned16(emb)) return ADALN_ERR_ALIGN;
+  if (int rc = check_overlap({{emb, static_cast<size_t>(B * kN * 2)}},
                              {{temb, static_cast<size_t>(B * kD * 2)}, {W, static_cast<size_t>(kN * kD * 2)},
                               {bias, static_cast<size_t>(kN * 2)}}))
     return rc;
   if (int rc = check_device()) return rc;
   (void)hipGetLastError();
-  uint16_t* a = static_cast<uint16_t*>(ws);
-  const hipStream_t s = as_stream(stream);
-  if (int rc = launched(adaln::launch_silu(temb, a, B * kD, s))) return rc;
-  return launched(adaln::launch_proj_fwd(a, W, bias, emb, B, s));
+  return launched(adaln::launch_proj_fwd(temb, W, bias, emb, B, as_stream(stream)));
 }
 
 int adaln_norm_mod_fwd(const adaln_bf16* x, const adaln_bf16* emb, adaln_bf16* out, float* mean,
@@ -229,29 +250,45 @@ int adaln_norm_mod_fwd(const adaln_bf16* x, const adaln_bf16* emb, adaln_bf16* o
   return launched(adaln::launch_norm_mod_fwd(x, emb, out, mean, rstd, B, S, eps, as_stream(stream)));
 }
 
-int adaln_norm_mod_bwd_tiles(const adaln_bf16* gout, const adaln_bf16* x, const float* mean,
-                             const float* rstd, const adaln_bf16* emb, adaln_bf16* dx, void* part,
-                             size_t part_bytes, int64_t B, int64_t S, int64_t D, void* stream) {
-  if (!gout || !x || !mean || !rstd || !emb || !dx || !part) return ADALN_ERR_NULL;
+int adaln_norm_mod_bwd_dx(const adaln_bf16* gout, const adaln_bf16* x, const float* mean,
+                          const float* rstd, const adaln_bf16* emb, adaln_bf16* dx, int64_t B,
+                          int64_t S, int64_t D, void* stream) {
+  if (!gout || !x || !mean || !rstd || !emb || !dx) return ADALN_ERR_NULL;
   if (!batch_ok(B) || !seq_ok(S) || D != kD) return ADALN_ERR_SHAPE;
   if (!aligned16(gout) || !aligned16(x) || !aligned16(mean) || !aligned16(rstd) ||
-      !aligned16(emb) || !aligned16(dx) || !aligned16(part))
+      !aligned16(emb) || !aligned16(dx))
     return ADALN_ERR_ALIGN;
-  const size_t need = ws_norm_bwd(B, S);
-  if (part_bytes < need) return ADALN_ERR_WORKSPACE;
   const size_t rows = static_cast<size_t>(B * S);
-  if (int rc = check_overlap({{dx, rows * kD * 2}, {part, need}},
+  if (int rc = check_overlap({{dx, rows * kD * 2}},
                              {{gout, rows * kD * 2}, {x, rows * kD * 2}, {mean, rows * 4},
                               {rstd, rows * 4}, {emb, static_cast<size_t>(B * kN * 2)}}))
     return rc;
   if (int rc = check_device()) return rc;
   (void)hipGetLastError();
-  const int64_t T0 = ceil_div(S, kTile);
+  hipEvent_t e0, e1;
+  timing_events(&e0, &e1);
+  return launched(adaln::launch_norm_mod_bwd_dx(gout, x, mean, rstd, emb, dx, B, S, as_stream(stream), e0, e1));
+}
+
+int adaln_norm_mod_bwd_tiles(const adaln_bf16* gout, const adaln_bf16* x, const float* mean,
+                             const float* rstd, void* part, size_t part_bytes, int64_t B, int64_t S,
+                             int64_t D, void* stream) {
+  if (!gout || !x || !mean || !rstd || !part) return ADALN_ERR_NULL;
+  if (!batch_ok(B) || !seq_ok(S) || D != kD) return ADALN_ERR_SHAPE;
+  if (!aligned16(gout) || !aligned16(x) || !aligned16(mean) || !aligned16(rstd) || !aligned16(part))
+    return ADALN_ERR_ALIGN;
+  const size_t need = ws_norm_bwd(B, S);
+  if (part_bytes < need) return ADALN_ERR_WORKSPACE;
+  const size_t rows = static_cast<size_t>(B * S);
+  if (int rc = check_overlap({{part, need}}, {{gout, rows * kD * 2}, {x, rows * kD * 2},
+                                              {mean, rows * 4}, {rstd, rows * 4}}))
+    return rc;
+  if (int rc = check_device()) return rc;
+  (void)hipGetLastError();
   float* part_s = static_cast<float*>(part);
   float* part_c = reinterpret_cast<float*>(static_cast<char*>(part) + need / 2);
-  return launched(adaln::launch_norm_mod_bwd_level0(gout, x, mean, rstd, emb, dx, part_s, part_c, B,
-                                                    S, adaln::choose_norm_bwd_split(B, T0),
-                                                    as_stream(stream)));
+  return launched(adaln::launch_norm_mod_bwd_tiles(gout, x, mean, rstd, part_s, part_c, B, S,
+                                                   as_stream(stream)));
 }
 
 int token_tree_fold(const void* part, float* out, int64_t B, int64_t T0, int64_t H, void* stream) {
@@ -273,16 +310,18 @@ int adaln_norm_mod_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float*
                        void* ws, size_t ws_bytes, int64_t B, int64_t S, int64_t D, void* stream) {
   if (!gout || !x || !mean || !rstd || !emb || !dx || !d_emb || !ws) return ADALN_ERR_NULL;
   if (!batch_ok(B) || !seq_ok(S) || D != kD) return ADALN_ERR_SHAPE;
-  if (!aligned16(d_emb)) return ADALN_ERR_ALIGN;
+  if (!aligned16(gout) || !aligned16(x) || !aligned16(mean) || !aligned16(rstd) ||
+      !aligned16(emb) || !aligned16(dx) || !aligned16(d_emb) || !aligned16(ws))
+    return ADALN_ERR_ALIGN;
   const size_t need = ws_norm_bwd(B, S);
+  if (ws_bytes < need) return ADALN_ERR_WORKSPACE;
   const size_t rows = static_cast<size_t>(B * S);
-  if (int rc = check_overlap({{d_emb, static_cast<size_t>(B * kN * 4)}},
-                             {{gout, rows * kD * 2}, {x, rows * kD * 2}, {mean, rows * 4}, {rstd, rows * 4},
-                              {emb, static_cast<size_t>(B * kN * 2)}, {dx, rows * kD * 2},
-                              {ws, ws_bytes < need ? ws_bytes : need}}))
+  if (int rc = check_overlap({{dx, rows * kD * 2}, {d_emb, static_cast<size_t>(B * kN * 4)}, {ws, need}},
+                             {{gout, rows * kD * 2}, {x, rows * kD * 2}, {mean, rows * 4},
+                              {rstd, rows * 4}, {emb, static_cast<size_t>(B * kN * 2)}}))
     return rc;
-  if (int rc = adaln_norm_mod_bwd_tiles(gout, x, mean, rstd, emb, dx, ws, ws_bytes, B, S, D, stream))
-    return rc;
+  if (int rc = adaln_norm_mod_bwd_dx(gout, x, mean, rstd, emb, dx, B, S, D, stream)) return rc;
+  if (int rc = adaln_norm_mod_bwd_tiles(gout, x, mean, rstd, ws, ws_bytes, B, S, D, stream)) return rc;
   return token_tree_fold(ws, d_emb, B, ceil_div(S, kTile), kN, stream);
 }
 
@@ -306,10 +345,14 @@ int adaln_proj_bwd(const float* d_emb, const adaln_bf16* temb, const adaln_bf16*
   uint16_t* a = static_cast<uint16_t*>(ws);
   double* part = reinterpret_cast<double*>(static_cast<char*>(ws) + pad256(static_cast<size_t>(B * kD * 2)));
   const hipStream_t s = as_stream(stream);
-  if (int rc = launched(adaln::launch_silu(temb, a, B * kD, s))) return rc;
-  if (int rc = launched(adaln::launch_proj_bwd_dw(d_emb, a, dW, db, B, s))) return rc;
-  if (int rc = launched(adaln::launch_proj_bwd_da(d_emb, W, part, B, s))) return rc;
-  return launched(adaln::launch_proj_bwd_dtemb(part, temb, dtemb, B, s));
+  if (B <= adaln::proj_bwd_fused_max_batch()) {
+    if (int rc = launched(adaln::launch_proj_bwd_fused(d_emb, temb, W, dW, part, B, s))) return rc;
+  } else {
+    if (int rc = launched(adaln::launch_silu(temb, a, B * kD, s))) return rc;
+    if (int rc = launched(adaln::launch_proj_bwd_dw(d_emb, a, dW, B, s))) return rc;
+    if (int rc = launched(adaln::launch_proj_bwd_da(d_emb, W, part, B, s))) return rc;
+  }
+  return launched(adaln::launch_proj_bwd_final(part, d_emb, temb, dtemb, db, B, s));
 }
 
 int token_tree_sum(const float* x, float* out, void* ws, size_t ws_bytes, int64_t B, int64_t S,
@@ -330,6 +373,41 @@ int token_tree_sum(const float* x, float* out, void* ws, size_t ws_bytes, int64_
   const hipStream_t s = as_stream(stream);
   if (int rc = launched(adaln::launch_token_level0(x, part_s, part_c, B, S, H, s))) return rc;
   return launched(adaln::launch_tree_fold(part_s, part_c, out, B, T0, H, s));
+}
+
+int adaln_timing_begin(int n) {
+  if (n < 1 || n > (1 << 20)) return ADALN_ERR_SHAPE;
+  if (int rc = check_device()) return rc;
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  timing_free_locked();
+  for (int i = 0; i < n; ++i) {
+    hipEvent_t a = nullptr, b = nullptr;
+    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+      if (a) (void)hipEventDestroy(a);
+      if (b) (void)hipEventDestroy(b);
+      timing_free_locked();
+      (void)hipGetLastError();
+      return ADALN_ERR_LAUNCH;
+    }
+    g_timing.start.push_back(a);
+    g_timing.stop.push_back(b);
+  }
+  return ADALN_OK;
+}
+
+int adaln_timing_end(float* ms, int n) {
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  const int used = static_cast<int>(g_timing.next);
+  int k = 0;
+  for (; ms && k < used && k < n; ++k) {
+    if (hipEventSynchronize(g_timing.stop[k]) != hipSuccess ||
+        hipEventElapsedTime(&ms[k], g_timing.start[k], g_timing.stop[k]) != hipSuccess) {
+      (void)hipGetLastError();
+      break;
+    }
+  }
+  timing_free_locked();
+  return k;
 }
 
 int adaln_selftest(void) {

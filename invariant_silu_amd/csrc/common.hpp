@@ -77,10 +77,32 @@ __device__ __forceinline__ float silu_f32(float z) {
   const double zd = z;
   return static_cast<float>(zd / (1.0 + exp(-zd)));
 }
+// Out-of-line copy for the rare fallback path of silu_bf16 (keeps the
+// registers of the float64 exp out of the callers' hot loops).
+__device__ __noinline__ float silu_f32_slow(float z) { return silu_f32(z); }
 __device__ __forceinline__ float dsilu_f32(float z) {
   const double zd = z;
   const double s = 1.0 / (1.0 + exp(-zd));
   return static_cast<float>(s * (1.0 + zd * (1.0 - s)));
+}
+
+// bf16(fl32(SiLU_f64(z))) computed mostly in fp32.  expf is accurate to about
+// 1 ulp and the add and the correctly rounded divide add half an ulp each, so
+// the fp32 value lies within 3 ulp of the float64 result.  bf16 rounding can
+// only differ between the two if a rounding tie (low 16 bits 0x8000) lies in
+// that window; whenever the fp32 value is within 8 ulp of a tie or is not
+// finite, and whenever |z| >= 64 (where expf(-z) approaches overflow and the
+// result approaches the denormal range), the float64 path decides.  Checked
+// exhaustively over all finite bf16 inputs against the float64 definition.
+__device__ __forceinline__ uint16_t silu_bf16(float z) {
+  const float y = z / (1.0f + expf(-z));
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t lo = u & 0xffffu;
+  const bool near_tie = (lo > 0x8000u - 8u) && (lo < 0x8000u + 8u);
+  const bool finite = (u & 0x7f800000u) != 0x7f800000u;
+  const bool wide = __builtin_fabsf(z) >= 64.0f;
+  const float v = (near_tie || !finite || wide) ? silu_f32_slow(z) : y;
+  return f32_to_bf16(v);
 }
 
 // One Neumaier step: t = s + x; c += exact rounding error of that add.

@@ -7,9 +7,10 @@
 //   out  = bf16((n_d * m_d) + shift_d),  m = bf16(1 + scale)
 // One wave per row: lane l holds the 16-byte chunks l, l+64, ..., l+320 of the
 // row; row sums are fp64 lane partials reduced by wave_sum_f64 (fixed lane
-// tree, no LDS, no atomics).  A block of 4 waves handles kRowsPerBlock rows of
-// ONE sample, so (1 + scale) and shift for that sample are staged once in LDS.
-// mu and rstd are written for the backward pass (8 bytes per row).
+// tree, no LDS, no atomics).  A block of 4 waves handles 4 rows of ONE sample;
+// the row loads are issued first and (1 + scale) and shift for that sample are
+// staged in LDS while they are in flight.  mu and rstd are written for the
+// backward pass (8 bytes per row).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -19,8 +20,7 @@ namespace {
 
 constexpr int kNfWaves = 4;
 constexpr int kNfThreads = 64 * kNfWaves;
-constexpr int kNfRowsPerWave = 2;
-constexpr int kNfRowsPerBlock = kNfWaves * kNfRowsPerWave;
+constexpr int kNfRowsPerBlock = kNfWaves;
 constexpr int kLaneChunks = kChunks / 64;   // 6
 
 __global__ __launch_bounds__(kNfThreads) void norm_mod_fwd_kernel(
@@ -29,87 +29,70 @@ __global__ __launch_bounds__(kNfThreads) void norm_mod_fwd_kernel(
   __shared__ float4 m_lds[kD / 4];
   __shared__ float4 sh_lds[kD / 4];
   const int64_t b = blockIdx.y;
-  const uint16_t* scale = emb + b * kN;
-  const uint16_t* shift = scale + kD;
-  for (int c = threadIdx.x; c < kD / 4; c += kNfThreads) {
-    float4 m, sh;
-    m.x = round_bf16(1.0f + bf16_to_f32(scale[4 * c + 0]));
-    m.y = round_bf16(1.0f + bf16_to_f32(scale[4 * c + 1]));
-    m.z = round_bf16(1.0f + bf16_to_f32(scale[4 * c + 2]));
-    m.w = round_bf16(1.0f + bf16_to_f32(scale[4 * c + 3]));
-    sh.x = bf16_to_f32(shift[4 * c + 0]);
-    sh.y = bf16_to_f32(shift[4 * c + 1]);
-    sh.z = bf16_to_f32(shift[4 * c + 2]);
-    sh.w = bf16_to_f32(shift[4 * c + 3]);
-    m_lds[c] = m;
-    sh_lds[c] = sh;
-  }
-  __syncthreads();
-
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int64_t s_base = static_cast<int64_t>(blockIdx.x) * kNfRowsPerBlock + wave;
+  const int64_t s = static_cast<int64_t>(blockIdx.x) * kNfRowsPerBlock + wave;
+  const bool valid = s < S;
+  const int64_t row = b * S + (valid ? s : 0);
 
-  uint4 xv[kNfRowsPerWave][kLaneChunks];
-  bool valid[kNfRowsPerWave];
+  uint4 xv[kLaneChunks];
 #pragma unroll
-  for (int r = 0; r < kNfRowsPerWave; ++r) {
-    const int64_t s = s_base + r * kNfWaves;
-    valid[r] = s < S;
-    const uint16_t* xr = x + (b * S + (valid[r] ? s : 0)) * kD;
-#pragma unroll
-    for (int i = 0; i < kLaneChunks; ++i)
-      xv[r][i] = valid[r] ? ld16(xr + (lane + 64 * i) * 8) : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < kLaneChunks; ++i) xv[i] = ld16(x + row * kD + (lane + 64 * i) * 8);
+
+  const uint2* scale = reinterpret_cast<const uint2*>(emb + b * kN);
+  const uint2* shift = reinterpret_cast<const uint2*>(emb + b * kN + kD);
+  for (int c = threadIdx.x; c < kD / 4; c += kNfThreads) {
+    const uint2 sc = scale[c], sh = shift[c];
+    m_lds[c] = make_float4(round_bf16(1.0f + bf_lo(sc.x)), round_bf16(1.0f + bf_hi(sc.x)),
+                           round_bf16(1.0f + bf_lo(sc.y)), round_bf16(1.0f + bf_hi(sc.y)));
+    sh_lds[c] = make_float4(bf_lo(sh.x), bf_hi(sh.x), bf_lo(sh.y), bf_hi(sh.y));
   }
+  __syncthreads();
+  if (!valid) return;   // whole wave
 
+  double acc = 0.0;
 #pragma unroll
-  for (int r = 0; r < kNfRowsPerWave; ++r) {
-    if (!valid[r]) continue;            // uniform across the wave
-    const int64_t row = b * S + s_base + r * kNfWaves;
-    double acc = 0.0;
+  for (int i = 0; i < kLaneChunks; ++i) {
+    float v[8];
+    unpack8(xv[i], v);
 #pragma unroll
-    for (int i = 0; i < kLaneChunks; ++i) {
-      float v[8];
-      unpack8(xv[r][i], v);
+    for (int e = 0; e < 8; ++e) acc += static_cast<double>(v[e]);
+  }
+  const float mu = static_cast<float>(wave_sum_f64(acc)) / static_cast<float>(kD);
+  double acc2 = 0.0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc += static_cast<double>(v[e]);
+  for (int i = 0; i < kLaneChunks; ++i) {
+    float v[8];
+    unpack8(xv[i], v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float d = v[e] - mu;
+      acc2 += static_cast<double>(d * d);
     }
-    const float mu = static_cast<float>(wave_sum_f64(acc)) / static_cast<float>(kD);
-    double acc2 = 0.0;
+  }
+  const float var = static_cast<float>(wave_sum_f64(acc2)) / static_cast<float>(kD);
+  const float rs = 1.0f / __builtin_sqrtf(var + eps);
+  uint16_t* orow = out + row * kD;
 #pragma unroll
-    for (int i = 0; i < kLaneChunks; ++i) {
-      float v[8];
-      unpack8(xv[r][i], v);
+  for (int i = 0; i < kLaneChunks; ++i) {
+    const int c = lane + 64 * i;
+    float v[8];
+    unpack8(xv[i], v);
+    const float4 m0 = m_lds[2 * c], m1 = m_lds[2 * c + 1];
+    const float4 h0 = sh_lds[2 * c], h1 = sh_lds[2 * c + 1];
+    const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+    const float hh[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+    float o[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float d = v[e] - mu;
-        acc2 += static_cast<double>(d * d);
-      }
+    for (int e = 0; e < 8; ++e) {
+      const float n = (v[e] - mu) * rs;
+      o[e] = n * mm[e] + hh[e];
     }
-    const float var = static_cast<float>(wave_sum_f64(acc2)) / static_cast<float>(kD);
-    const float rs = 1.0f / __builtin_sqrtf(var + eps);
-    uint16_t* orow = out + row * kD;
-#pragma unroll
-    for (int i = 0; i < kLaneChunks; ++i) {
-      const int c = lane + 64 * i;
-      float v[8];
-      unpack8(xv[r][i], v);
-      const float4 m0 = m_lds[2 * c], m1 = m_lds[2 * c + 1];
-      const float4 h0 = sh_lds[2 * c], h1 = sh_lds[2 * c + 1];
-      const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-      const float hh[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-      float o[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float n = (v[e] - mu) * rs;
-        o[e] = n * mm[e] + hh[e];
-      }
-      st16(orow + c * 8, pack8(o));
-    }
-    if (lane == 0) {
-      mean[row] = mu;
-      rstd[row] = rs;
-    }
+    st16(orow + c * 8, pack8(o));
+  }
+  if (lane == 0) {
+    mean[row] = mu;
+    rstd[row] = rs;
   }
 }
 

@@ -9,9 +9,16 @@
 //   dW, db  : samples in ascending order (trailing zero samples change nothing);
 //   da      : 32 fixed parts of 192 rows; in a part, 8 row slots each walk
 //             every 8th row in order, slots combined as a pairwise tree; the
-//             32 part sums are added in order by the dtemb kernel.
+//             32 part sums are added in order by the final kernel.
 // None of these orders depends on the batch size, so dtemb of a sample is the
 // same bytes alone or in any batch.
+//
+// B <= 4: proj_bwd_fused_kernel does dW and the da partials in one pass over
+//   the same (192-row, 256-column) tiles: W streams in, dW streams out, and
+//   each thread computes a = bf16(SiLU(temb)) for its own 8 columns.
+// B > 4:  silu_kernel (a into the workspace), proj_bwd_dw_kernel, then
+//   proj_bwd_da_kernel in batch chunks of 4 (same arithmetic per element).
+// proj_bwd_final_kernel: dtemb from the 32 partials, and db.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -19,7 +26,97 @@ namespace adaln {
 
 namespace {
 
-// ---- dW / db: a write stream over dW (37.75 MB), 4 rows per block ----------
+constexpr int kTileCols = 256;                       // columns per block (32 threads x 8)
+constexpr int kColThreads = kTileCols / 8;           // 32
+constexpr int kSlots = 8;                            // row slots per block
+constexpr int kBlockThreads = kColThreads * kSlots;  // 256
+constexpr int kRowsPerPart = kN / kProjBwdParts;     // 192
+constexpr int kSteps = kRowsPerPart / kSlots;        // 24 rows per thread
+constexpr int kBatchChunk = 4;
+
+static_assert(kN % kProjBwdParts == 0 && kRowsPerPart % kSlots == 0, "part layout");
+static_assert(kD % kTileCols == 0, "column blocks");
+
+// slots combined as ((s0+s1)+(s2+s3)) + ((s4+s5)+(s6+s7))
+__device__ __forceinline__ double slot_tree(const double (*red)[kBatchChunk][kTileCols], int b, int c) {
+  return ((red[0][b][c] + red[1][b][c]) + (red[2][b][c] + red[3][b][c])) +
+         ((red[4][b][c] + red[5][b][c]) + (red[6][b][c] + red[7][b][c]));
+}
+
+__global__ __launch_bounds__(kBlockThreads) void proj_bwd_fused_kernel(
+    const float* __restrict__ d_emb, const uint16_t* __restrict__ temb,
+    const uint16_t* __restrict__ W, uint16_t* __restrict__ dW, double* __restrict__ part, int B) {
+  __shared__ double red[kSlots][kBatchChunk][kTileCols];   // 64 KB
+  __shared__ float de_lds[kBatchChunk][kRowsPerPart];
+  const int p = blockIdx.x;
+  const int kb = blockIdx.y;
+  const int ct = threadIdx.x % kColThreads;
+  const int slot = threadIdx.x / kColThreads;
+  const int col = kb * kTileCols + ct * 8;
+  const int jbase = p * kRowsPerPart;
+
+  uint4 wv[kSteps];
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i)
+    wv[i] = ld16(W + static_cast<int64_t>(jbase + slot + kSlots * i) * kD + col);
+
+  for (int idx = threadIdx.x; idx < B * kRowsPerPart; idx += kBlockThreads)
+    de_lds[idx / kRowsPerPart][idx % kRowsPerPart] =
+        d_emb[static_cast<int64_t>(idx / kRowsPerPart) * kN + jbase + idx % kRowsPerPart];
+  float av[kBatchChunk][8];
+#pragma unroll
+  for (int b = 0; b < kBatchChunk; ++b) {
+    if (b < B) {
+      float z[8];
+      unpack8(ld16(temb + static_cast<int64_t>(b) * kD + col), z);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) av[b][e] = bf16_to_f32(silu_bf16(z[e]));
+    }
+  }
+  __syncthreads();
+
+  double acc[kBatchChunk][8];
+#pragma unroll
+  for (int b = 0; b < kBatchChunk; ++b)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[b][e] = 0.0;
+
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    const int jl = slot + kSlots * i;
+    float d[kBatchChunk];
+#pragma unroll
+    for (int b = 0; b < kBatchChunk; ++b) d[b] = b < B ? de_lds[b][jl] : 0.0f;
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      double s = 0.0;
+#pragma unroll
+      for (int b = 0; b < kBatchChunk; ++b)
+        if (b < B) s += static_cast<double>(d[b] * av[b][e]);
+      o[e] = static_cast<float>(s);
+    }
+    st16(dW + static_cast<int64_t>(jbase + jl) * kD + col, pack8(o));
+    float w[8];
+    unpack8(wv[i], w);
+#pragma unroll
+    for (int b = 0; b < kBatchChunk; ++b)
+      if (b < B)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[b][e] += static_cast<double>(d[b] * w[e]);
+  }
+#pragma unroll
+  for (int b = 0; b < kBatchChunk; ++b)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[slot][b][ct * 8 + e] = acc[b][e];
+  __syncthreads();
+  for (int o = threadIdx.x; o < B * kTileCols; o += kBlockThreads) {
+    const int b = o / kTileCols, c = o % kTileCols;
+    part[(static_cast<int64_t>(p) * B + b) * kD + kb * kTileCols + c] = slot_tree(red, b, c);
+  }
+}
+
+// ---- B > 4 ------------------------------------------------------------------
 constexpr int kDwRows = 4;
 constexpr int kDwThreads = kChunks;     // 384: one 16-byte chunk of a row each
 constexpr int kDwBatch = 8;
@@ -27,7 +124,6 @@ constexpr int kDwBatch = 8;
 __global__ __launch_bounds__(kDwThreads) void proj_bwd_dw_kernel(const float* __restrict__ d_emb,
                                                                  const uint16_t* __restrict__ a,
                                                                  uint16_t* __restrict__ dW,
-                                                                 uint16_t* __restrict__ db,
                                                                  int64_t B) {
   const int t = threadIdx.x;
   const int j0 = blockIdx.x * kDwRows;
@@ -41,9 +137,8 @@ __global__ __launch_bounds__(kDwThreads) void proj_bwd_dw_kernel(const float* __
     const int nb = static_cast<int>((B - b0) < kDwBatch ? (B - b0) : kDwBatch);
     float av[kDwBatch][8];
 #pragma unroll
-    for (int bb = 0; bb < kDwBatch; ++bb) {
+    for (int bb = 0; bb < kDwBatch; ++bb)
       if (bb < nb) unpack8(ld16(a + (b0 + bb) * kD + t * 8), av[bb]);
-    }
 #pragma unroll
     for (int bb = 0; bb < kDwBatch; ++bb) {
       if (bb < nb) {
@@ -63,114 +158,111 @@ __global__ __launch_bounds__(kDwThreads) void proj_bwd_dw_kernel(const float* __
     for (int e = 0; e < 8; ++e) o[e] = static_cast<float>(acc[r][e]);
     st16(dW + static_cast<int64_t>(j0 + r) * kD + t * 8, pack8(o));
   }
-  if (t < kDwRows) {
-    double s = 0.0;
-    for (int64_t b = 0; b < B; ++b) s += static_cast<double>(d_emb[b * kN + j0 + t]);
-    db[j0 + t] = f32_to_bf16(static_cast<float>(s));
-  }
 }
 
-// ---- da partials: a read stream over W (37.75 MB) ---------------------------
-constexpr int kDaCols = 256;                        // columns per block (32 threads x 8)
-constexpr int kDaColThreads = kDaCols / 8;          // 32
-constexpr int kDaSlots = 8;                         // row slots per block
-constexpr int kDaThreads = kDaColThreads * kDaSlots;   // 256
-constexpr int kDaRowsPerPart = kN / kProjBwdParts;  // 192
-constexpr int kDaBatch = 4;                         // samples per block
-
-__global__ __launch_bounds__(kDaThreads) void proj_bwd_da_kernel(const float* __restrict__ d_emb,
-                                                                 const uint16_t* __restrict__ W,
-                                                                 double* __restrict__ part,
-                                                                 int64_t B) {
-  __shared__ double red[kDaSlots][kDaBatch][kDaCols];   // 64 KB
+__global__ __launch_bounds__(kBlockThreads) void proj_bwd_da_kernel(const float* __restrict__ d_emb,
+                                                                    const uint16_t* __restrict__ W,
+                                                                    double* __restrict__ part,
+                                                                    int64_t B) {
+  __shared__ double red[kSlots][kBatchChunk][kTileCols];   // 64 KB
   const int p = blockIdx.x;
   const int kb = blockIdx.y;
-  const int64_t b0 = static_cast<int64_t>(blockIdx.z) * kDaBatch;
-  const int nb = static_cast<int>((B - b0) < kDaBatch ? (B - b0) : kDaBatch);
-  const int ct = threadIdx.x % kDaColThreads;
-  const int slot = threadIdx.x / kDaColThreads;
-  const int col = kb * kDaCols + ct * 8;
-  const int jbase = p * kDaRowsPerPart;
+  const int64_t b0 = static_cast<int64_t>(blockIdx.z) * kBatchChunk;
+  const int nb = static_cast<int>((B - b0) < kBatchChunk ? (B - b0) : kBatchChunk);
+  const int ct = threadIdx.x % kColThreads;
+  const int slot = threadIdx.x / kColThreads;
+  const int col = kb * kTileCols + ct * 8;
+  const int jbase = p * kRowsPerPart;
 
-  double acc[kDaBatch][8];
+  uint4 wv[kSteps];
 #pragma unroll
-  for (int bb = 0; bb < kDaBatch; ++bb)
+  for (int i = 0; i < kSteps; ++i)
+    wv[i] = ld16(W + static_cast<int64_t>(jbase + slot + kSlots * i) * kD + col);
+  double acc[kBatchChunk][8];
+#pragma unroll
+  for (int bb = 0; bb < kBatchChunk; ++bb)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[bb][e] = 0.0;
-
-  constexpr int kSteps = kDaRowsPerPart / kDaSlots;   // 24
-  uint4 wcur = ld16(W + static_cast<int64_t>(jbase + slot) * kD + col);
-  for (int i = 0; i < kSteps; ++i) {
-    const int j = jbase + slot + kDaSlots * i;
-    uint4 wnext = wcur;
-    if (i + 1 < kSteps) wnext = ld16(W + static_cast<int64_t>(j + kDaSlots) * kD + col);
-    float wv[8];
-    unpack8(wcur, wv);
 #pragma unroll
-    for (int bb = 0; bb < kDaBatch; ++bb) {
+  for (int i = 0; i < kSteps; ++i) {
+    const int j = jbase + slot + kSlots * i;
+    float w[8];
+    unpack8(wv[i], w);
+#pragma unroll
+    for (int bb = 0; bb < kBatchChunk; ++bb) {
       if (bb < nb) {
         const float d = d_emb[(b0 + bb) * kN + j];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[bb][e] += static_cast<double>(d * wv[e]);
+        for (int e = 0; e < 8; ++e) acc[bb][e] += static_cast<double>(d * w[e]);
       }
     }
-    wcur = wnext;
   }
 #pragma unroll
-  for (int bb = 0; bb < kDaBatch; ++bb)
+  for (int bb = 0; bb < kBatchChunk; ++bb)
 #pragma unroll
     for (int e = 0; e < 8; ++e) red[slot][bb][ct * 8 + e] = acc[bb][e];
   __syncthreads();
-  for (int o = threadIdx.x; o < kDaBatch * kDaCols; o += kDaThreads) {
-    const int bb = o / kDaCols;
-    const int c = o % kDaCols;
-    if (bb < nb) {
-      const double v = ((red[0][bb][c] + red[1][bb][c]) + (red[2][bb][c] + red[3][bb][c])) +
-                       ((red[4][bb][c] + red[5][bb][c]) + (red[6][bb][c] + red[7][bb][c]));
-      part[(static_cast<int64_t>(p) * B + b0 + bb) * kD + kb * kDaCols + c] = v;
-    }
+  for (int o = threadIdx.x; o < kBatchChunk * kTileCols; o += kBlockThreads) {
+    const int bb = o / kTileCols, c = o % kTileCols;
+    if (bb < nb)
+      part[(static_cast<int64_t>(p) * B + b0 + bb) * kD + kb * kTileCols + c] = slot_tree(red, bb, c);
   }
 }
 
-// ---- dtemb: sum the 32 parts in order, apply silu' ---------------------------
-__global__ __launch_bounds__(256) void proj_bwd_dtemb_kernel(const double* __restrict__ part,
+// ---- dtemb and db -------------------------------------------------------------
+__global__ __launch_bounds__(256) void proj_bwd_final_kernel(const double* __restrict__ part,
+                                                             const float* __restrict__ d_emb,
                                                              const uint16_t* __restrict__ temb,
                                                              uint16_t* __restrict__ dtemb,
-                                                             int64_t B) {
+                                                             uint16_t* __restrict__ db, int64_t B) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= B * kD) return;
-  double s = 0.0;
-#pragma unroll 8
-  for (int p = 0; p < kProjBwdParts; ++p) s += part[static_cast<int64_t>(p) * B * kD + i];
-  const float da = static_cast<float>(s);
-  dtemb[i] = f32_to_bf16(da * dsilu_f32(bf16_to_f32(temb[i])));
+  if (i < B * kD) {
+    double v[kProjBwdParts];
+#pragma unroll
+    for (int p = 0; p < kProjBwdParts; ++p) v[p] = part[static_cast<int64_t>(p) * B * kD + i];
+    double s = 0.0;
+#pragma unroll
+    for (int p = 0; p < kProjBwdParts; ++p) s += v[p];
+    dtemb[i] = f32_to_bf16(static_cast<float>(s) * dsilu_f32(bf16_to_f32(temb[i])));
+  }
+  if (i < kN) {
+    double s = 0.0;
+    for (int64_t b = 0; b < B; ++b) s += static_cast<double>(d_emb[b * kN + i]);
+    db[i] = f32_to_bf16(static_cast<float>(s));
+  }
 }
 
 }  // namespace
 
-hipError_t launch_proj_bwd_dw(const float* d_emb, const uint16_t* a, uint16_t* dW, uint16_t* db,
-                              int64_t B, hipStream_t s) {
-  hipLaunchKernelGGL(proj_bwd_dw_kernel, dim3(kN / kDwRows), dim3(kDwThreads), 0, s, d_emb, a, dW,
-                     db, B);
+int proj_bwd_fused_max_batch() { return kBatchChunk; }
+
+hipError_t launch_proj_bwd_fused(const float* d_emb, const uint16_t* temb, const uint16_t* W,
+                                 uint16_t* dW, double* part, int64_t B, hipStream_t s) {
+  if (B > kBatchChunk) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(proj_bwd_fused_kernel, dim3(kProjBwdParts, kD / kTileCols), dim3(kBlockThreads),
+                     0, s, d_emb, temb, W, dW, part, static_cast<int>(B));
+  return hipGetLastError();
+}
+
+hipError_t launch_proj_bwd_dw(const float* d_emb, const uint16_t* a, uint16_t* dW, int64_t B,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(proj_bwd_dw_kernel, dim3(kN / kDwRows), dim3(kDwThreads), 0, s, d_emb, a, dW, B);
   return hipGetLastError();
 }
 
 hipError_t launch_proj_bwd_da(const float* d_emb, const uint16_t* W, double* part, int64_t B,
                               hipStream_t s) {
-  static_assert(kN % kProjBwdParts == 0 && kDaRowsPerPart % kDaSlots == 0, "part layout");
-  static_assert(kD % kDaCols == 0, "column blocks");
-  const int64_t bz = (B + kDaBatch - 1) / kDaBatch;
-  hipLaunchKernelGGL(proj_bwd_da_kernel,
-                     dim3(kProjBwdParts, kD / kDaCols, static_cast<unsigned>(bz)), dim3(kDaThreads), 0,
-                     s, d_emb, W, part, B);
+  const int64_t bz = (B + kBatchChunk - 1) / kBatchChunk;
+  hipLaunchKernelGGL(proj_bwd_da_kernel, dim3(kProjBwdParts, kD / kTileCols, static_cast<unsigned>(bz)),
+                     dim3(kBlockThreads), 0, s, d_emb, W, part, B);
   return hipGetLastError();
 }
 
-hipError_t launch_proj_bwd_dtemb(const double* part, const uint16_t* temb, uint16_t* dtemb,
-                                 int64_t B, hipStream_t s) {
-  const int64_t n = B * kD;
-  hipLaunchKernelGGL(proj_bwd_dtemb_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
-                     0, s, part, temb, dtemb, B);
+hipError_t launch_proj_bwd_final(const double* part, const float* d_emb, const uint16_t* temb,
+                                 uint16_t* dtemb, uint16_t* db, int64_t B, hipStream_t s) {
+  const int64_t n = B * kD > kN ? B * kD : kN;
+  hipLaunchKernelGGL(proj_bwd_final_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+                     s, part, d_emb, temb, dtemb, db, B);
   return hipGetLastError();
 }
 

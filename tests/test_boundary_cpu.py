@@ -57,18 +57,18 @@ def test_workspace_sizes(L):
         T0 = math.ceil(S / 32)
         assert lib.workspace_bytes(lib.OP_NORM_MOD_BWD, B, S, 3072) == 2 * pad(B * T0 * 6144 * 4)
         assert lib.workspace_bytes(lib.OP_TOKEN_TREE_SUM, B, S, 100) == 2 * pad(B * T0 * 100 * 4)
-        assert lib.workspace_bytes(lib.OP_PROJ_FWD, B, S, 3072) == pad(B * 3072 * 2)
         assert lib.workspace_bytes(lib.OP_PROJ_BWD, B, S, 3072) == pad(B * 3072 * 2) + pad(32 * B * 3072 * 8)
     assert lib.workspace_bytes(lib.OP_NORM_MOD_BWD, 1, 10, 1024) == 0
     assert lib.workspace_bytes(99, 1, 10, 3072) == 0
-    assert lib.workspace_bytes(lib.OP_PROJ_FWD, 0, 1, 3072) == 0
+    assert lib.workspace_bytes(lib.OP_PROJ_BWD, 0, 1, 3072) == 0
+    assert lib.workspace_bytes(1, 1, 1, 3072) == 0
 
 
 def test_validation_before_device_work(L):
     """NULL pointers and bad shapes are reported without touching a device."""
-    assert L.adaln_proj_fwd(None, None, None, None, None, 0, 1, 3072, 6144, None) == lib.ERR_NULL
+    assert L.adaln_proj_fwd(None, None, None, None, 1, 3072, 6144, None) == lib.ERR_NULL
     p = 4096   # a fake, aligned, non-null address: shape checks come first
-    assert L.adaln_proj_fwd(p, p, p, p, p, 1 << 20, 1, 1024, 6144, None) == lib.ERR_SHAPE
+    assert L.adaln_proj_fwd(p, p, p, p, 1, 1024, 6144, None) == lib.ERR_SHAPE
     assert L.adaln_norm_mod_fwd(p, p, p, p, p, 1, 0, 3072, 1e-6, None) == lib.ERR_SHAPE
     assert L.token_tree_sum(p, p, p, 1 << 20, 1, 1, 0, None) == lib.ERR_SHAPE
     assert L.adaln_norm_mod_fwd(p + 2, p, p, p, p, 1, 1, 3072, 1e-6, None) == lib.ERR_ALIGN
