@@ -153,14 +153,18 @@ int token_tree_sum(const float* x, float* out, void* ws, size_t ws_bytes, int64_
  * ADALN_ERR_DEVICE, or a positive count of failed probe values. */
 int adaln_selftest(void);
 
-/* Benchmarking aid: per-launch durations of the norm backward's row pass
- * (adaln_norm_mod_bwd_dx, alone or inside adaln_norm_mod_bwd), timed with HIP
- * events carried by the kernel dispatch itself (no extra packets in the stream).
- * adaln_timing_begin(n) creates n event pairs; the next n launches on any stream
- * record into them.  adaln_timing_end(ms, n) waits for the recorded launches,
- * writes up to n durations in milliseconds, frees the events and returns the
- * number written.  Events are host-side HIP objects; no device memory. */
-int adaln_timing_begin(int n);
+/* Benchmarking aid: per-launch durations of the norm backward's main kernel
+ * (the fused dx + level-0 kernel of adaln_norm_mod_bwd, or the dx kernel of
+ * adaln_norm_mod_bwd_dx), timed with HIP events carried by the kernel
+ * dispatch itself (no extra packets in the stream).
+ * A timed dispatch leaves the stream idle for a few microseconds around it, so
+ * timing can be sampled: adaln_timing_begin(n, stride) creates n event pairs;
+ * launches number 0, stride, 2*stride, ... (counted from this call, on any
+ * stream) record into them until n are used.  adaln_timing_end(ms, n) waits
+ * for the recorded launches, writes up to n durations in milliseconds, frees
+ * the events and returns the number written.  Events are host-side HIP
+ * objects; no device memory. */
+int adaln_timing_begin(int n, int stride);
 int adaln_timing_end(float* ms, int n);
 
 /* Static description of a status code. */

@@ -34,13 +34,17 @@ std::atomic<int> g_probe_failures[kMaxDevices];
 struct Timing {
   std::mutex mu;
   std::vector<hipEvent_t> start, stop;
-  size_t next = 0;
+  size_t next = 0;     // next free event pair
+  int64_t seen = 0;    // launches since adaln_timing_begin
+  int64_t stride = 1;  // record every stride-th launch
 };
 Timing g_timing;
 
 void timing_events(hipEvent_t* a, hipEvent_t* b) {
   std::lock_guard<std::mutex> lock(g_timing.mu);
-  if (g_timing.next < g_timing.start.size()) {
+  const bool pick = g_timing.next < g_timing.start.size() && g_timing.seen % g_timing.stride == 0;
+  if (!g_timing.start.empty()) ++g_timing.seen;
+  if (pick) {
     *a = g_timing.start[g_timing.next];
     *b = g_timing.stop[g_timing.next];
     ++g_timing.next;
@@ -56,6 +60,8 @@ void timing_free_locked() {
   g_timing.start.clear();
   g_timing.stop.clear();
   g_timing.next = 0;
+  g_timing.seen = 0;
+  g_timing.stride = 1;
 }
 
 inline size_t pad256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
@@ -320,8 +326,15 @@ int adaln_norm_mod_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float*
                              {{gout, rows * kD * 2}, {x, rows * kD * 2}, {mean, rows * 4},
                               {rstd, rows * 4}, {emb, static_cast<size_t>(B * kN * 2)}}))
     return rc;
-  if (int rc = adaln_norm_mod_bwd_dx(gout, x, mean, rstd, emb, dx, B, S, D, stream)) return rc;
-  if (int rc = adaln_norm_mod_bwd_tiles(gout, x, mean, rstd, ws, ws_bytes, B, S, D, stream)) return rc;
+  if (int rc = check_device()) return rc;
+  (void)hipGetLastError();
+  float* part_s = static_cast<float*>(ws);
+  float* part_c = reinterpret_cast<float*>(static_cast<char*>(ws) + need / 2);
+  hipEvent_t e0, e1;
+  timing_events(&e0, &e1);
+  if (int rc = launched(adaln::launch_norm_mod_bwd(gout, x, mean, rstd, emb, dx, part_s, part_c, B, S,
+                                                   as_stream(stream), e0, e1)))
+    return rc;
   return token_tree_fold(ws, d_emb, B, ceil_div(S, kTile), kN, stream);
 }
 
@@ -375,11 +388,12 @@ int token_tree_sum(const float* x, float* out, void* ws, size_t ws_bytes, int64_
   return launched(adaln::launch_tree_fold(part_s, part_c, out, B, T0, H, s));
 }
 
-int adaln_timing_begin(int n) {
-  if (n < 1 || n > (1 << 20)) return ADALN_ERR_SHAPE;
+int adaln_timing_begin(int n, int stride) {
+  if (n < 1 || n > (1 << 20) || stride < 1) return ADALN_ERR_SHAPE;
   if (int rc = check_device()) return rc;
   std::lock_guard<std::mutex> lock(g_timing.mu);
   timing_free_locked();
+  g_timing.stride = stride;
   for (int i = 0; i < n; ++i) {
     hipEvent_t a = nullptr, b = nullptr;
     if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {

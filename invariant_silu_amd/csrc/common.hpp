@@ -61,6 +61,13 @@ __device__ __forceinline__ uint4 ld16(const uint16_t* p) {
 __device__ __forceinline__ void st16(uint16_t* p, const uint4& v) {
   *reinterpret_cast<uint4*>(p) = v;
 }
+// Streaming (nontemporal) 16-byte store for outputs nothing in the step reads
+// back soon.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st16_nt(uint16_t* p, const uint4& v) {
+  u32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+}
 
 // Sum over the 64 lanes of a wave as a pairwise tree over lane index
 // (xor 1, 2, 4, ..., 32).  IEEE addition commutes, so every lane ends with
@@ -77,9 +84,7 @@ __device__ __forceinline__ float silu_f32(float z) {
   const double zd = z;
   return static_cast<float>(zd / (1.0 + exp(-zd)));
 }
-// Out-of-line copy for the rare fallback path of silu_bf16 (keeps the
-// registers of the float64 exp out of the callers' hot loops).
-__device__ __noinline__ float silu_f32_slow(float z) { return silu_f32(z); }
+
 __device__ __forceinline__ float dsilu_f32(float z) {
   const double zd = z;
   const double s = 1.0 / (1.0 + exp(-zd));
@@ -90,19 +95,37 @@ __device__ __forceinline__ float dsilu_f32(float z) {
 // 1 ulp and the add and the correctly rounded divide add half an ulp each, so
 // the fp32 value lies within 3 ulp of the float64 result.  bf16 rounding can
 // only differ between the two if a rounding tie (low 16 bits 0x8000) lies in
-// that window; whenever the fp32 value is within 8 ulp of a tie or is not
-// finite, and whenever |z| >= 64 (where expf(-z) approaches overflow and the
-// result approaches the denormal range), the float64 path decides.  Checked
+// that window.  silu_bf16_fast returns the bf16 bits of the fp32 value and
+// reports whether the float64 path must decide instead: within 8 ulp of a
+// tie, a non-finite value, or |z| >= 64 (where expf(-z) approaches overflow
+// and the result approaches the denormal range).  Callers redo the flagged
+// elements with silu_bf16_exact in a separate, rarely taken loop.  Checked
 // exhaustively over all finite bf16 inputs against the float64 definition.
-__device__ __forceinline__ uint16_t silu_bf16(float z) {
+__device__ __forceinline__ uint32_t silu_bf16_fast(float z, bool& redo) {
   const float y = z / (1.0f + expf(-z));
   const uint32_t u = __float_as_uint(y);
   const uint32_t lo = u & 0xffffu;
   const bool near_tie = (lo > 0x8000u - 8u) && (lo < 0x8000u + 8u);
   const bool finite = (u & 0x7f800000u) != 0x7f800000u;
-  const bool wide = __builtin_fabsf(z) >= 64.0f;
-  const float v = (near_tie || !finite || wide) ? silu_f32_slow(z) : y;
-  return f32_to_bf16(v);
+  redo = near_tie || !finite || __builtin_fabsf(z) >= 64.0f;
+  return f32_to_bf16(y);
+}
+__device__ __forceinline__ uint16_t silu_bf16_exact(float z) { return f32_to_bf16(silu_f32(z)); }
+
+// SiLU of 8 consecutive bf16 inputs (one 16-byte chunk) -> 8 bf16 outputs.
+// Bit i of the returned mask is set when element i needs silu_bf16_exact.
+__device__ __forceinline__ uint4 silu8_fast(const uint4& in, uint32_t& redo_mask) {
+  float z[8];
+  unpack8(in, z);
+  uint32_t o[8];
+  redo_mask = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    bool r;
+    o[e] = silu_bf16_fast(z[e], r);
+    redo_mask |= static_cast<uint32_t>(r) << e;
+  }
+  return make_uint4(o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16), o[6] | (o[7] << 16));
 }
 
 // One Neumaier step: t = s + x; c += exact rounding error of that add.

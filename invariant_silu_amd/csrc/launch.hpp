@@ -17,6 +17,10 @@ hipError_t launch_proj_fwd(const uint16_t* temb, const uint16_t* W, const uint16
 hipError_t launch_norm_mod_fwd(const uint16_t* x, const uint16_t* emb, uint16_t* out,
                                float* mean, float* rstd, int64_t B, int64_t S, float eps,
                                hipStream_t s);
+hipError_t launch_norm_mod_bwd(const uint16_t* g, const uint16_t* x, const float* mean,
+                               const float* rstd, const uint16_t* emb, uint16_t* dx, float* part_s,
+                               float* part_c, int64_t B, int64_t S, hipStream_t s,
+                               hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 hipError_t launch_norm_mod_bwd_dx(const uint16_t* g, const uint16_t* x, const float* mean,
                                   const float* rstd, const uint16_t* emb, uint16_t* dx, int64_t B,
                                   int64_t S, hipStream_t s, hipEvent_t ev_start = nullptr,

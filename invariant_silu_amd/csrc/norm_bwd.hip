@@ -1,22 +1,27 @@
 // LayerNorm + modulation, backward (RL-Kernel pull request 538, "What"; token
-// sums per the review-thread fix of token_sum.cu).  Two kernels, one per kind
-// of parallelism, both reading g and x:
+// sums per the review-thread fix of token_sum.cu).  One launch, two kinds of
+// block, both reading the g and x rows of one 32-token tile:
 //
-// norm_mod_bwd_dx_kernel -- rows.  One wave per row r = (b, s):
+// row blocks (8 per tile, one wave per row r = (b, s)):
 //   n     = (x - mean) * rstd                (recomputed exactly as the forward)
 //   gy    = g * m,  m = bf16(1 + scale)      (exact: bf16 x bf16)
 //   alpha = fl32(sum_d gy) / D,  beta = fl32(sum_d gy * n) / D
 //   dx    = bf16(rstd * ((gy - alpha) - n * beta))
 //   Row sums: fp64 lane partials (chunks in order, columns in order), then the
-//   fixed lane tree of wave_sum_f64.  HBM-bound stream: g, x in, dx out.
+//   fixed lane tree of wave_sum_f64.  HBM-bound: g, x in, dx out.
 //
-// norm_mod_bwd_tiles_kernel -- columns.  One thread per (sample, 32-token tile,
-//   2 adjacent columns): the level-0 Neumaier pairs (s, c) of g (-> d_shift)
-//   and of g * n (-> d_scale), tokens in ascending order.  The 32-step
-//   recurrence of a column stays in one thread; g and x are read again (the
-//   row kernel has just streamed them, so they are usually still in the MALL).
+// column blocks (6 per tile, one thread per 2 adjacent columns): the level-0
+//   Neumaier pairs (s, c) of g (-> d_shift) and of g * n (-> d_scale), tokens
+//   in ascending order; the 32-step recurrence of a column stays in one
+//   thread.  ALU-bound.
 //
-// Neither kernel's arithmetic depends on the batch size or the grid.
+// The 14 blocks of a tile get block ids congruent mod 8, so they are
+// dispatched one after the other on the same XCD: the row blocks stream the
+// tile from HBM while the column blocks of the same tile find it in that
+// XCD's L2, and the ALU-bound and HBM-bound halves overlap.
+//
+// No arithmetic depends on the batch size or the grid.  Each half can also be
+// launched alone (adaln_norm_mod_bwd_dx / adaln_norm_mod_bwd_tiles).
 #include <hip/hip_ext.h>
 
 #include "common.hpp"
@@ -26,23 +31,31 @@ namespace adaln {
 
 namespace {
 
-constexpr int kDxWaves = 4;
-constexpr int kDxThreads = 64 * kDxWaves;
-constexpr int kLaneChunks = kChunks / 64;   // 6
+constexpr int kThreads = 256;
+constexpr int kLaneChunks = kChunks / 64;          // 6
+constexpr int kRowBlocks = kTile / 4;              // 8 row blocks of 4 rows per tile
+constexpr int kColPairs = kThreads;                // 256 column pairs per column block
+constexpr int kColBlockCols = 2 * kColPairs;       // 512 columns
+constexpr int kColBlocks = kD / kColBlockCols;     // 6
+constexpr int kBlocksPerTile = kRowBlocks + kColBlocks;   // 14
 
-__global__ __launch_bounds__(kDxThreads) void norm_mod_bwd_dx_kernel(
-    const uint16_t* __restrict__ g, const uint16_t* __restrict__ x,
-    const float* __restrict__ mean, const float* __restrict__ rstd,
-    const uint16_t* __restrict__ emb, uint16_t* __restrict__ dx, int64_t S) {
-  __shared__ float4 m_lds[kD / 4];
-  const int64_t b = blockIdx.y;
+enum Role { kBoth = 0, kRowsOnly = 1, kColsOnly = 2 };
+
+__device__ __forceinline__ void row_pass(const uint16_t* __restrict__ g, const uint16_t* __restrict__ x,
+                                         const float* __restrict__ mean, const float* __restrict__ rstd,
+                                         const uint16_t* __restrict__ emb, uint16_t* __restrict__ dx,
+                                         int64_t b, int64_t s, int64_t S, float4* m_lds) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int64_t s = static_cast<int64_t>(blockIdx.x) * kDxWaves + wave;
   const bool valid = s < S;
   const int64_t row = b * S + (valid ? s : 0);
 
-  // issue the row's loads before staging m, so the two latencies overlap
+  // small loads first: the memory counter drains in issue order, so staging
+  // m needs only these, while the row loads below stay in flight
+  const uint2* scale = reinterpret_cast<const uint2*>(emb + b * kN);
+  uint2 sc[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) sc[k] = scale[threadIdx.x + kThreads * k];
   uint4 gv[kLaneChunks], xv[kLaneChunks];
 #pragma unroll
   for (int i = 0; i < kLaneChunks; ++i) {
@@ -51,14 +64,13 @@ __global__ __launch_bounds__(kDxThreads) void norm_mod_bwd_dx_kernel(
   }
   const float mu = mean[row];
   const float rs = rstd[row];
-
-  const uint2* scale = reinterpret_cast<const uint2*>(emb + b * kN);
-  for (int c = threadIdx.x; c < kD / 4; c += kDxThreads) {
-    const uint2 w = scale[c];
-    m_lds[c] = make_float4(round_bf16(1.0f + bf_lo(w.x)), round_bf16(1.0f + bf_hi(w.x)),
-                           round_bf16(1.0f + bf_lo(w.y)), round_bf16(1.0f + bf_hi(w.y)));
-  }
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+    m_lds[threadIdx.x + kThreads * k] =
+        make_float4(round_bf16(1.0f + bf_lo(sc[k].x)), round_bf16(1.0f + bf_hi(sc[k].x)),
+                    round_bf16(1.0f + bf_lo(sc[k].y)), round_bf16(1.0f + bf_hi(sc[k].y)));
   __syncthreads();
+  (void)wave;
   if (!valid) return;   // whole wave
 
   double q1 = 0.0, q2 = 0.0;
@@ -80,6 +92,13 @@ __global__ __launch_bounds__(kDxThreads) void norm_mod_bwd_dx_kernel(
   }
   const float alpha = static_cast<float>(wave_sum_f64(q1)) / static_cast<float>(kD);
   const float beta = static_cast<float>(wave_sum_f64(q2)) / static_cast<float>(kD);
+  // keep the packed rows packed across the reduction (recompute below rather
+  // than hold 96 unpacked values in registers)
+#pragma unroll
+  for (int i = 0; i < kLaneChunks; ++i) {
+    asm volatile("" : "+v"(gv[i].x), "+v"(gv[i].y), "+v"(gv[i].z), "+v"(gv[i].w));
+    asm volatile("" : "+v"(xv[i].x), "+v"(xv[i].y), "+v"(xv[i].z), "+v"(xv[i].w));
+  }
 
   uint16_t* drow = dx + row * kD;
 #pragma unroll
@@ -96,24 +115,24 @@ __global__ __launch_bounds__(kDxThreads) void norm_mod_bwd_dx_kernel(
       const float gy = gf[e] * mm[e];
       d[e] = rs * ((gy - alpha) - n * beta);
     }
-    st16(drow + c * 8, pack8(d));
+    st16_nt(drow + c * 8, pack8(d));
   }
 }
 
-constexpr int kTlThreads = 256;
-constexpr int kTlCols = 2 * kTlThreads;     // 512 columns per block
-
-__global__ __launch_bounds__(kTlThreads) void norm_mod_bwd_tiles_kernel(
-    const uint16_t* __restrict__ g, const uint16_t* __restrict__ x,
-    const float* __restrict__ mean, const float* __restrict__ rstd,
-    float* __restrict__ part_s, float* __restrict__ part_c, int64_t S, int64_t T0) {
-  __shared__ float mu_s[kTile], rs_s[kTile];
-  const int col = blockIdx.x * kTlCols + 2 * threadIdx.x;
-  const int64_t tile = blockIdx.y;
-  const int64_t b = blockIdx.z;
+__device__ __forceinline__ void col_pass(const uint16_t* __restrict__ g, const uint16_t* __restrict__ x,
+                                         const float* __restrict__ mean, const float* __restrict__ rstd,
+                                         float* __restrict__ part_s, float* __restrict__ part_c,
+                                         int64_t b, int64_t tile, int cb, int64_t S, int64_t T0,
+                                         float* mu_s, float* rs_s) {
+  const int col = cb * kColBlockCols + 2 * threadIdx.x;
   const int rows = static_cast<int>((S - tile * kTile) < kTile ? (S - tile * kTile) : kTile);
   const int64_t row0 = b * S + tile * kTile;
 
+  float mu_l = 0.0f, rs_l = 0.0f;
+  if (threadIdx.x < rows) {
+    mu_l = mean[row0 + threadIdx.x];
+    rs_l = rstd[row0 + threadIdx.x];
+  }
   uint32_t gw[kTile], xw[kTile];
 #pragma unroll
   for (int r = 0; r < kTile; ++r) {
@@ -124,8 +143,8 @@ __global__ __launch_bounds__(kTlThreads) void norm_mod_bwd_tiles_kernel(
     }
   }
   if (threadIdx.x < rows) {
-    mu_s[threadIdx.x] = mean[row0 + threadIdx.x];
-    rs_s[threadIdx.x] = rstd[row0 + threadIdx.x];
+    mu_s[threadIdx.x] = mu_l;
+    rs_s[threadIdx.x] = rs_l;
   }
   __syncthreads();
 
@@ -152,32 +171,74 @@ __global__ __launch_bounds__(kTlThreads) void norm_mod_bwd_tiles_kernel(
   *reinterpret_cast<float2*>(part_c + base + kD) = make_float2(cg0, cg1);
 }
 
+// grid: 1-D, ceil(B*T0 / 8) * 8 * blocks_per_tile blocks (blocks_per_tile = 14,
+// 8 or 6 for kBoth / kRowsOnly / kColsOnly).  Block L runs on XCD L % 8; on
+// that XCD its index j = L / 8 selects tile (j / bpt) * 8 + L % 8 and role j % bpt.
+template <int kRole>
+__global__ __launch_bounds__(kThreads) void norm_mod_bwd_kernel(
+    const uint16_t* __restrict__ g, const uint16_t* __restrict__ x,
+    const float* __restrict__ mean, const float* __restrict__ rstd,
+    const uint16_t* __restrict__ emb, uint16_t* __restrict__ dx,
+    float* __restrict__ part_s, float* __restrict__ part_c, int64_t B, int64_t S, int64_t T0) {
+  constexpr int bpt = kRole == kBoth ? kBlocksPerTile : (kRole == kRowsOnly ? kRowBlocks : kColBlocks);
+  __shared__ float4 m_lds[kD / 4];   // row blocks: m = bf16(1 + scale); column blocks: mean/rstd
+  const int64_t L = blockIdx.x;
+  const int64_t j = L >> 3;
+  const int64_t G = (j / bpt) * 8 + (L & 7);
+  const int role = static_cast<int>(j % bpt);
+  if (G >= B * T0) return;
+  const int64_t b = G / T0;
+  const int64_t tile = G % T0;
+  if (kRole != kColsOnly && role < kRowBlocks) {
+    const int64_t s = tile * kTile + role * 4 + (threadIdx.x >> 6);
+    row_pass(g, x, mean, rstd, emb, dx, b, s, S, m_lds);
+  } else {
+    const int cb = kRole == kColsOnly ? role : role - kRowBlocks;
+    float* f = reinterpret_cast<float*>(m_lds);
+    col_pass(g, x, mean, rstd, part_s, part_c, b, tile, cb, S, T0, f, f + kTile);
+  }
+}
+
+template <int kRole>
+hipError_t launch_role(const uint16_t* g, const uint16_t* x, const float* mean, const float* rstd,
+                       const uint16_t* emb, uint16_t* dx, float* part_s, float* part_c, int64_t B,
+                       int64_t S, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  constexpr int bpt = kRole == kBoth ? kBlocksPerTile : (kRole == kRowsOnly ? kRowBlocks : kColBlocks);
+  const int64_t T0 = (S + kTile - 1) / kTile;
+  const int64_t groups = (B * T0 + 7) / 8;
+  const dim3 grid(static_cast<unsigned>(groups * 8 * bpt));
+  if (e0 != nullptr && e1 != nullptr) {
+    // events carried by the dispatch itself: no extra barrier in the stream
+    hipExtLaunchKernelGGL(norm_mod_bwd_kernel<kRole>, grid, dim3(kThreads), 0, s, e0, e1, 0, g, x, mean,
+                          rstd, emb, dx, part_s, part_c, B, S, T0);
+  } else {
+    hipLaunchKernelGGL(norm_mod_bwd_kernel<kRole>, grid, dim3(kThreads), 0, s, g, x, mean, rstd, emb, dx,
+                       part_s, part_c, B, S, T0);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_norm_mod_bwd(const uint16_t* g, const uint16_t* x, const float* mean,
+                               const float* rstd, const uint16_t* emb, uint16_t* dx, float* part_s,
+                               float* part_c, int64_t B, int64_t S, hipStream_t s, hipEvent_t e0,
+                               hipEvent_t e1) {
+  static_assert(kD % kColBlockCols == 0, "column blocks must tile D");
+  return launch_role<kBoth>(g, x, mean, rstd, emb, dx, part_s, part_c, B, S, s, e0, e1);
+}
 
 hipError_t launch_norm_mod_bwd_dx(const uint16_t* g, const uint16_t* x, const float* mean,
                                   const float* rstd, const uint16_t* emb, uint16_t* dx, int64_t B,
-                                  int64_t S, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
-  const int64_t gx = (S + kDxWaves - 1) / kDxWaves;
-  const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(B));
-  if (ev_start != nullptr && ev_stop != nullptr) {
-    // events carried by the dispatch itself: no extra barrier in the stream
-    hipExtLaunchKernelGGL(norm_mod_bwd_dx_kernel, grid, dim3(kDxThreads), 0, s, ev_start, ev_stop, 0,
-                          g, x, mean, rstd, emb, dx, S);
-  } else {
-    hipLaunchKernelGGL(norm_mod_bwd_dx_kernel, grid, dim3(kDxThreads), 0, s, g, x, mean, rstd, emb, dx, S);
-  }
-  return hipGetLastError();
+                                  int64_t S, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  return launch_role<kRowsOnly>(g, x, mean, rstd, emb, dx, nullptr, nullptr, B, S, s, e0, e1);
 }
 
 hipError_t launch_norm_mod_bwd_tiles(const uint16_t* g, const uint16_t* x, const float* mean,
                                      const float* rstd, float* part_s, float* part_c, int64_t B,
                                      int64_t S, hipStream_t s) {
-  static_assert(kD % kTlCols == 0, "column blocks must tile D");
-  const int64_t T0 = (S + kTile - 1) / kTile;
-  hipLaunchKernelGGL(norm_mod_bwd_tiles_kernel,
-                     dim3(kD / kTlCols, static_cast<unsigned>(T0), static_cast<unsigned>(B)),
-                     dim3(kTlThreads), 0, s, g, x, mean, rstd, part_s, part_c, S, T0);
-  return hipGetLastError();
+  return launch_role<kColsOnly>(g, x, mean, rstd, nullptr, nullptr, part_s, part_c, B, S, s, nullptr,
+                                nullptr);
 }
 
 }  // namespace adaln

@@ -13,9 +13,9 @@
 // None of these orders depends on the batch size, so dtemb of a sample is the
 // same bytes alone or in any batch.
 //
-// B <= 4: proj_bwd_fused_kernel does dW and the da partials in one pass over
-//   the same (192-row, 256-column) tiles: W streams in, dW streams out, and
-//   each thread computes a = bf16(SiLU(temb)) for its own 8 columns.
+// B <= 4: proj_bwd_small_kernel, one grid with a dW-writing and a W-reading
+//   half over the same (192-row, 256-column) tiles; the dW half computes
+//   a = bf16(SiLU(temb)) per thread for its own 8 columns.
 // B > 4:  silu_kernel (a into the workspace), proj_bwd_dw_kernel, then
 //   proj_bwd_da_kernel in batch chunks of 4 (same arithmetic per element).
 // proj_bwd_final_kernel: dtemb from the 32 partials, and db.
@@ -37,82 +37,124 @@ constexpr int kBatchChunk = 4;
 static_assert(kN % kProjBwdParts == 0 && kRowsPerPart % kSlots == 0, "part layout");
 static_assert(kD % kTileCols == 0, "column blocks");
 
-// slots combined as ((s0+s1)+(s2+s3)) + ((s4+s5)+(s6+s7))
+// slots combined as ((s0+s1)+(s2+s3)) + ((s4+s5)+(s6+s7)) (the same tree in
+// every kernel that forms da partials)
 __device__ __forceinline__ double slot_tree(const double (*red)[kBatchChunk][kTileCols], int b, int c) {
   return ((red[0][b][c] + red[1][b][c]) + (red[2][b][c] + red[3][b][c])) +
          ((red[4][b][c] + red[5][b][c]) + (red[6][b][c] + red[7][b][c]));
 }
 
-__global__ __launch_bounds__(kBlockThreads) void proj_bwd_fused_kernel(
+// Small batches (B <= 4, a template parameter): one grid, two kinds of block
+// over the same (192-row part, 256-column block) tiles.  blockIdx.z = 0 writes
+// dW (a write stream; each thread computes a = bf16(SiLU(temb)) for its 8
+// columns), blockIdx.z = 1 reads W and forms the fp64 da partials (a read
+// stream).  The two streams run side by side.
+template <int NB>
+__global__ __launch_bounds__(kBlockThreads) void proj_bwd_small_kernel(
     const float* __restrict__ d_emb, const uint16_t* __restrict__ temb,
-    const uint16_t* __restrict__ W, uint16_t* __restrict__ dW, double* __restrict__ part, int B) {
-  __shared__ double red[kSlots][kBatchChunk][kTileCols];   // 64 KB
-  __shared__ float de_lds[kBatchChunk][kRowsPerPart];
+    const uint16_t* __restrict__ W, uint16_t* __restrict__ dW, double* __restrict__ part) {
+  __shared__ double red[kSlots][NB][kTileCols];
+  __shared__ float de_lds[NB][kRowsPerPart];
   const int p = blockIdx.x;
   const int kb = blockIdx.y;
+  const bool write_dw = blockIdx.z == 0;
   const int ct = threadIdx.x % kColThreads;
   const int slot = threadIdx.x / kColThreads;
   const int col = kb * kTileCols + ct * 8;
   const int jbase = p * kRowsPerPart;
+  constexpr int kDeLoads = (NB * kRowsPerPart + kBlockThreads - 1) / kBlockThreads;
+
+  // small loads first (the memory counter drains in issue order)
+  float de_r[kDeLoads];
+#pragma unroll
+  for (int k = 0; k < kDeLoads; ++k) {
+    const int idx = threadIdx.x + kBlockThreads * k;
+    if (idx < NB * kRowsPerPart)
+      de_r[k] = d_emb[static_cast<int64_t>(idx / kRowsPerPart) * kN + jbase + idx % kRowsPerPart];
+  }
+  if (write_dw) {
+    uint4 tz[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) tz[b] = ld16(temb + static_cast<int64_t>(b) * kD + col);
+#pragma unroll
+    for (int k = 0; k < kDeLoads; ++k) {
+      const int idx = threadIdx.x + kBlockThreads * k;
+      if (idx < NB * kRowsPerPart) de_lds[idx / kRowsPerPart][idx % kRowsPerPart] = de_r[k];
+    }
+    float av[NB][8];
+    uint32_t redo = 0;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      uint32_t m;
+      unpack8(silu8_fast(tz[b], m), av[b]);
+      redo |= m << (8 * b);
+    }
+    while (redo != 0) {   // rarely taken: elements the fast SiLU cannot decide
+      const int bit = __builtin_ctz(redo);
+      redo &= redo - 1;
+      const int b = bit / 8, e = bit % 8;
+      const float v = bf16_to_f32(silu_bf16_exact(bf16_to_f32(temb[static_cast<int64_t>(b) * kD + col + e])));
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+        for (int ee = 0; ee < 8; ++ee)
+          if (bb == b && ee == e) av[bb][ee] = v;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int i = 0; i < kSteps; ++i) {
+      const int jl = slot + kSlots * i;
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        double s = 0.0;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) s += static_cast<double>(de_lds[b][jl] * av[b][e]);
+        o[e] = static_cast<float>(s);
+      }
+      st16_nt(dW + static_cast<int64_t>(jbase + jl) * kD + col, pack8(o));
+    }
+    return;
+  }
 
   uint4 wv[kSteps];
 #pragma unroll
   for (int i = 0; i < kSteps; ++i)
     wv[i] = ld16(W + static_cast<int64_t>(jbase + slot + kSlots * i) * kD + col);
-
-  for (int idx = threadIdx.x; idx < B * kRowsPerPart; idx += kBlockThreads)
-    de_lds[idx / kRowsPerPart][idx % kRowsPerPart] =
-        d_emb[static_cast<int64_t>(idx / kRowsPerPart) * kN + jbase + idx % kRowsPerPart];
-  float av[kBatchChunk][8];
 #pragma unroll
-  for (int b = 0; b < kBatchChunk; ++b) {
-    if (b < B) {
-      float z[8];
-      unpack8(ld16(temb + static_cast<int64_t>(b) * kD + col), z);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) av[b][e] = bf16_to_f32(silu_bf16(z[e]));
-    }
+  for (int k = 0; k < kDeLoads; ++k) {
+    const int idx = threadIdx.x + kBlockThreads * k;
+    if (idx < NB * kRowsPerPart) de_lds[idx / kRowsPerPart][idx % kRowsPerPart] = de_r[k];
   }
   __syncthreads();
-
-  double acc[kBatchChunk][8];
+  double acc[NB][8];
 #pragma unroll
-  for (int b = 0; b < kBatchChunk; ++b)
+  for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[b][e] = 0.0;
-
 #pragma unroll
   for (int i = 0; i < kSteps; ++i) {
     const int jl = slot + kSlots * i;
-    float d[kBatchChunk];
-#pragma unroll
-    for (int b = 0; b < kBatchChunk; ++b) d[b] = b < B ? de_lds[b][jl] : 0.0f;
-    float o[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      double s = 0.0;
-#pragma unroll
-      for (int b = 0; b < kBatchChunk; ++b)
-        if (b < B) s += static_cast<double>(d[b] * av[b][e]);
-      o[e] = static_cast<float>(s);
-    }
-    st16(dW + static_cast<int64_t>(jbase + jl) * kD + col, pack8(o));
     float w[8];
     unpack8(wv[i], w);
 #pragma unroll
-    for (int b = 0; b < kBatchChunk; ++b)
-      if (b < B)
+    for (int b = 0; b < NB; ++b) {
+      const float d = de_lds[b][jl];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[b][e] += static_cast<double>(d[b] * w[e]);
+      for (int e = 0; e < 8; ++e) acc[b][e] += static_cast<double>(d * w[e]);
+    }
   }
 #pragma unroll
-  for (int b = 0; b < kBatchChunk; ++b)
+  for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int e = 0; e < 8; ++e) red[slot][b][ct * 8 + e] = acc[b][e];
   __syncthreads();
-  for (int o = threadIdx.x; o < B * kTileCols; o += kBlockThreads) {
-    const int b = o / kTileCols, c = o % kTileCols;
-    part[(static_cast<int64_t>(p) * B + b) * kD + kb * kTileCols + c] = slot_tree(red, b, c);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int c = threadIdx.x;
+    const double v = ((red[0][b][c] + red[1][b][c]) + (red[2][b][c] + red[3][b][c])) +
+                     ((red[4][b][c] + red[5][b][c]) + (red[6][b][c] + red[7][b][c]));
+    part[(static_cast<int64_t>(p) * NB + b) * kD + kb * kTileCols + c] = v;
   }
 }
 
@@ -238,9 +280,14 @@ int proj_bwd_fused_max_batch() { return kBatchChunk; }
 
 hipError_t launch_proj_bwd_fused(const float* d_emb, const uint16_t* temb, const uint16_t* W,
                                  uint16_t* dW, double* part, int64_t B, hipStream_t s) {
-  if (B > kBatchChunk) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(proj_bwd_fused_kernel, dim3(kProjBwdParts, kD / kTileCols), dim3(kBlockThreads),
-                     0, s, d_emb, temb, W, dW, part, static_cast<int>(B));
+  const dim3 grid(kProjBwdParts, kD / kTileCols, 2), block(kBlockThreads);
+  switch (B) {
+    case 1: hipLaunchKernelGGL(proj_bwd_small_kernel<1>, grid, block, 0, s, d_emb, temb, W, dW, part); break;
+    case 2: hipLaunchKernelGGL(proj_bwd_small_kernel<2>, grid, block, 0, s, d_emb, temb, W, dW, part); break;
+    case 3: hipLaunchKernelGGL(proj_bwd_small_kernel<3>, grid, block, 0, s, d_emb, temb, W, dW, part); break;
+    case 4: hipLaunchKernelGGL(proj_bwd_small_kernel<4>, grid, block, 0, s, d_emb, temb, W, dW, part); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

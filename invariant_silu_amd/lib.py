@@ -38,7 +38,7 @@ _SIGS = {
     "token_tree_fold": ([_P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "adaln_workspace_bytes": ([ctypes.c_int, _I64, _I64, _I64], _SZ),
     "adaln_selftest": ([], ctypes.c_int),
-    "adaln_timing_begin": ([ctypes.c_int], ctypes.c_int),
+    "adaln_timing_begin": ([ctypes.c_int, ctypes.c_int], ctypes.c_int),
     "adaln_timing_end": ([ctypes.POINTER(ctypes.c_float), ctypes.c_int], ctypes.c_int),
     "adaln_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "adaln_abi_version": ([], ctypes.c_int),
