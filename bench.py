@@ -2,7 +2,9 @@
 """Throughput of the batch-invariant AdaLN final modulation, forward + backward.
 
 One step is the whole hot path over one batch of synthetic input, through the
-C ABI: adaln_proj_fwd -> adaln_norm_mod_fwd -> adaln_norm_mod_bwd -> adaln_proj_bwd.  Default workload: one 1024x1024 image
+C ABI: adaln_fwd (projection and LayerNorm statistics side by side, then the
+modulation) and adaln_bwd (level-0 token tiles, tree fold, then dx, dW and the
+W stream of the projection backward side by side, then dtemb and db).  Default workload: one 1024x1024 image
 stream, B = 1, S = 4096 tokens, D = 3072, bf16 storage, 1% outlier rows x20.
 
 Inputs are resident in HBM before the timed region.  The step rotates over
@@ -10,8 +12,8 @@ several independent copies of every buffer (parameters included), so no step
 finds the previous step's data in the 256 MB MALL; reuse inside one step (x
 read by the forward and the backward, W by both projections) is left as is.
 
-Prints ONE JSON line.  `roofline` covers the dominant kernel (the norm backward:
-g, x in, dx out, with the level-0 token tiles formed from the same reads),
+Prints ONE JSON line.  `roofline` covers the dominant kernel (the backward's
+main launch: W in, dW out, dx out),
 timed on every 8th timed step with HIP events that
 its own dispatch carries on the stream it runs on (adaln_timing_begin/end: a
 timed dispatch leaves the stream idle for a few us, so timing is sampled);
@@ -47,9 +49,11 @@ def algorithmic_bytes(B: int, S: int) -> int:
 
 
 def dominant_kernel_bytes(B: int, S: int) -> int:
-    """norm backward kernel: g and x read, dx written, mean/rstd read, scale
-    read (per sample).  Its level-0 tile pairs are implementation overhead."""
-    return 6 * B * S * D + 8 * B * S + 2 * D * B
+    """The backward's main launch (B <= 4): W read, dW written, dx written,
+    mean/rstd read; per sample scale, temb and d_emb read.  Its second read of
+    g and x (first read by the level-0 kernel) and its fp64 dtemb partials are
+    implementation overhead, not algorithmic bytes."""
+    return 2 * 2 * N * D + 2 * B * S * D + 8 * B * S + B * (2 * D + 2 * D + 4 * N)
 
 
 def pmc_traffic():
@@ -126,9 +130,7 @@ def main() -> int:
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
     base = {k: to_dev(inp[k]) for k in ("x", "temb", "W", "bias", "g")}
-    ws_nb = lib.workspace_bytes(lib.OP_NORM_MOD_BWD, B, S, D)
-    ws_pb = lib.workspace_bytes(lib.OP_PROJ_BWD, B, S, D)
-    T0 = math.ceil(S / 32)
+    ws_bw = lib.workspace_bytes(lib.OP_BWD, B, S, D)
 
     def new_set():
         s = {k: v.clone() for k, v in base.items()}
@@ -142,8 +144,7 @@ def main() -> int:
             dW=torch.empty((N, D), dtype=torch.bfloat16, device=dev),
             db=torch.empty((N,), dtype=torch.bfloat16, device=dev),
             dtemb=torch.empty((B, D), dtype=torch.bfloat16, device=dev),
-            ws_nb=torch.empty(ws_nb, dtype=torch.uint8, device=dev),
-            ws_pb=torch.empty(ws_pb, dtype=torch.uint8, device=dev),
+            ws_bw=torch.empty(ws_bw, dtype=torch.uint8, device=dev),
         )
         return s
 
@@ -154,14 +155,11 @@ def main() -> int:
     st = stream.cuda_stream
     def step(s):
         p = lambda k: s[k].data_ptr()   # noqa: E731
-        lib.check("adaln_proj_fwd", L.adaln_proj_fwd(p("temb"), p("W"), p("bias"), p("emb"), B, D, N, st))
-        lib.check("adaln_norm_mod_fwd", L.adaln_norm_mod_fwd(p("x"), p("emb"), p("out"), p("mean"),
-                                                             p("rstd"), B, S, D, 1e-6, st))
-        lib.check("adaln_norm_mod_bwd",
-                  L.adaln_norm_mod_bwd(p("g"), p("x"), p("mean"), p("rstd"), p("emb"), p("dx"), p("d_emb"),
-                                       p("ws_nb"), ws_nb, B, S, D, st))
-        lib.check("adaln_proj_bwd", L.adaln_proj_bwd(p("d_emb"), p("temb"), p("W"), p("dW"), p("db"),
-                                                     p("dtemb"), p("ws_pb"), ws_pb, B, D, N, st))
+        lib.check("adaln_fwd", L.adaln_fwd(p("temb"), p("W"), p("bias"), p("x"), p("emb"), p("out"), p("mean"),
+                                           p("rstd"), B, S, D, 1e-6, st))
+        lib.check("adaln_bwd", L.adaln_bwd(p("g"), p("x"), p("mean"), p("rstd"), p("emb"), p("temb"), p("W"),
+                                           p("dx"), p("d_emb"), p("dW"), p("db"), p("dtemb"), p("ws_bw"),
+                                           ws_bw, B, S, D, st))
 
     for i in range(args.warmup):
         step(sets[i % nsets])
@@ -173,6 +171,7 @@ def main() -> int:
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(sets[i % nsets])
+    t_enq = time.perf_counter()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     import ctypes
@@ -211,9 +210,10 @@ def main() -> int:
         "config": {"workload": args.workload, "B": B, "S": S, "D": D, "N": N,
                    "storage": "bf16", "accumulate": "fp64", "outlier_rows": w["outlier_frac"],
                    "buffer_sets": nsets, "step_algorithmic_bytes": step_bytes,
+                   "host_enqueue_ms_per_step": round((t_enq - t0) * 1e3 / args.steps, 5),
                    "step_gbps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
                    "step_frac_of_peak": round(step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)},
-        "roofline": {"bound": "hbm", "kernel": "norm_mod_bwd_kernel",
+        "roofline": {"bound": "hbm", "kernel": "bwd_stage2_kernel (dx rows, dW, W stream)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": pmc_traffic(),
                      "bytes_per_launch": k_bytes, "avg_launch_ms": round(k_mean_ms, 5),

@@ -65,7 +65,8 @@ enum adaln_status {
 enum adaln_op {
   ADALN_OP_NORM_MOD_BWD = 2,
   ADALN_OP_PROJ_BWD = 3,
-  ADALN_OP_TOKEN_TREE_SUM = 4
+  ADALN_OP_TOKEN_TREE_SUM = 4,
+  ADALN_OP_BWD = 5
 };
 
 /* Workspace bytes an entry point needs (0 for an unknown op or bad sizes).
@@ -73,6 +74,7 @@ enum adaln_op {
  *   PROJ_BWD:       H = K (3072), S ignored.  B*K*2 (SiLU activations, used when
  *                   B > 4) + 32*B*K*8 (fp64 partials of dtemb).
  *   TOKEN_TREE_SUM: 2 * B * ceil(S/32) * H * 4 bytes.
+ *   BWD:            H = D (3072).  NORM_MOD_BWD + PROJ_BWD, in that order.
  * Each region is padded to 256 bytes. */
 size_t adaln_workspace_bytes(int op, int64_t B, int64_t S, int64_t H);
 
@@ -153,10 +155,29 @@ int token_tree_sum(const float* x, float* out, void* ws, size_t ws_bytes, int64_
  * ADALN_ERR_DEVICE, or a positive count of failed probe values. */
 int adaln_selftest(void);
 
-/* Benchmarking aid: per-launch durations of the norm backward's main kernel
- * (the fused dx + level-0 kernel of adaln_norm_mod_bwd, or the dx kernel of
- * adaln_norm_mod_bwd_dx), timed with HIP events carried by the kernel
- * dispatch itself (no extra packets in the stream).
+/* One-call forward: adaln_proj_fwd then adaln_norm_mod_fwd, same results bit
+ * for bit, scheduled so that the projection's pass over W and the LayerNorm
+ * statistics pass over x run side by side (one launch), then the modulation.
+ *   temb, W, bias, x in; emb, out, mean, rstd out (layouts as above). */
+int adaln_fwd(const adaln_bf16* temb, const adaln_bf16* W, const adaln_bf16* bias, const adaln_bf16* x,
+              adaln_bf16* emb, adaln_bf16* out, float* mean, float* rstd, int64_t B, int64_t S,
+              int64_t D, float eps, void* stream);
+
+/* One-call backward: adaln_norm_mod_bwd then adaln_proj_bwd, same results bit
+ * for bit.  For B <= 4 the level-0 token tiles run first, then the tree fold,
+ * then one launch in which the dx rows, the dW stream and the W stream of the
+ * projection backward run side by side.  ws: adaln_workspace_bytes(ADALN_OP_BWD,
+ * B, S, D) bytes. */
+int adaln_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float* mean, const float* rstd,
+              const adaln_bf16* emb, const adaln_bf16* temb, const adaln_bf16* W, adaln_bf16* dx,
+              float* d_emb, adaln_bf16* dW, adaln_bf16* db, adaln_bf16* dtemb, void* ws, size_t ws_bytes,
+              int64_t B, int64_t S, int64_t D, void* stream);
+
+/* Benchmarking aid: per-launch durations of the main kernel of the backward
+ * (adaln_bwd: its last big launch -- dx, dW and W streams for B <= 4, the
+ * fused dx + level-0 kernel otherwise; adaln_norm_mod_bwd: the fused dx +
+ * level-0 kernel; adaln_norm_mod_bwd_dx: the dx kernel), timed with HIP
+ * events carried by the kernel dispatch itself (no extra packets).
  * A timed dispatch leaves the stream idle for a few microseconds around it, so
  * timing can be sampled: adaln_timing_begin(n, stride) creates n event pairs;
  * launches number 0, stride, 2*stride, ... (counted from this call, on any

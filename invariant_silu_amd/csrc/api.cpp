@@ -220,6 +220,7 @@ size_t adaln_workspace_bytes(int op, int64_t B, int64_t S, int64_t H) {
   switch (op) {
     case ADALN_OP_NORM_MOD_BWD: return (H == kD && seq_ok(S)) ? ws_norm_bwd(B, S) : 0;
     case ADALN_OP_PROJ_BWD: return H == kD ? ws_proj_bwd(B) : 0;
+    case ADALN_OP_BWD: return (H == kD && seq_ok(S)) ? ws_norm_bwd(B, S) + ws_proj_bwd(B) : 0;
     case ADALN_OP_TOKEN_TREE_SUM:
       return (seq_ok(S) && H >= 1 && H <= (int64_t{1} << 24)) ? ws_tree(B, S, H) : 0;
     default: return 0;
@@ -422,6 +423,79 @@ int adaln_timing_end(float* ms, int n) {
   }
   timing_free_locked();
   return k;
+}
+
+int adaln_fwd(const adaln_bf16* temb, const adaln_bf16* W, const adaln_bf16* bias, const adaln_bf16* x,
+              adaln_bf16* emb, adaln_bf16* out, float* mean, float* rstd, int64_t B, int64_t S,
+              int64_t D, float eps, void* stream) {
+  if (!temb || !W || !bias || !x || !emb || !out || !mean || !rstd) return ADALN_ERR_NULL;
+  if (!batch_ok(B) || !seq_ok(S) || D != kD) return ADALN_ERR_SHAPE;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return ADALN_ERR_SHAPE;
+  if (!aligned16(temb) || !aligned16(W) || !aligned16(bias) || !aligned16(x) || !aligned16(emb) ||
+      !aligned16(out) || !aligned16(mean) || !aligned16(rstd))
+    return ADALN_ERR_ALIGN;
+  const size_t rows = static_cast<size_t>(B * S);
+  if (int rc = check_overlap({{emb, static_cast<size_t>(B * kN * 2)}, {out, rows * kD * 2}, {mean, rows * 4},
+                              {rstd, rows * 4}},
+                             {{temb, static_cast<size_t>(B * kD * 2)}, {W, static_cast<size_t>(kN * kD * 2)},
+                              {bias, static_cast<size_t>(kN * 2)}, {x, rows * kD * 2}}))
+    return rc;
+  if (int rc = check_device()) return rc;
+  (void)hipGetLastError();
+  return launched(adaln::launch_fwd(temb, W, bias, x, emb, out, mean, rstd, B, S, eps, as_stream(stream)));
+}
+
+int adaln_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float* mean, const float* rstd,
+              const adaln_bf16* emb, const adaln_bf16* temb, const adaln_bf16* W, adaln_bf16* dx,
+              float* d_emb, adaln_bf16* dW, adaln_bf16* db, adaln_bf16* dtemb, void* ws, size_t ws_bytes,
+              int64_t B, int64_t S, int64_t D, void* stream) {
+  if (!gout || !x || !mean || !rstd || !emb || !temb || !W || !dx || !d_emb || !dW || !db || !dtemb || !ws)
+    return ADALN_ERR_NULL;
+  if (!batch_ok(B) || !seq_ok(S) || D != kD) return ADALN_ERR_SHAPE;
+  if (!aligned16(gout) || !aligned16(x) || !aligned16(mean) || !aligned16(rstd) || !aligned16(emb) ||
+      !aligned16(temb) || !aligned16(W) || !aligned16(dx) || !aligned16(d_emb) || !aligned16(dW) ||
+      !aligned16(db) || !aligned16(dtemb) || !aligned16(ws))
+    return ADALN_ERR_ALIGN;
+  const size_t n_norm = ws_norm_bwd(B, S);
+  const size_t need = n_norm + ws_proj_bwd(B);
+  if (ws_bytes < need) return ADALN_ERR_WORKSPACE;
+  const size_t rows = static_cast<size_t>(B * S);
+  if (int rc = check_overlap(
+          {{dx, rows * kD * 2}, {d_emb, static_cast<size_t>(B * kN * 4)}, {dW, static_cast<size_t>(kN * kD * 2)},
+           {db, static_cast<size_t>(kN * 2)}, {dtemb, static_cast<size_t>(B * kD * 2)}, {ws, need}},
+          {{gout, rows * kD * 2}, {x, rows * kD * 2}, {mean, rows * 4}, {rstd, rows * 4},
+           {emb, static_cast<size_t>(B * kN * 2)}, {temb, static_cast<size_t>(B * kD * 2)},
+           {W, static_cast<size_t>(kN * kD * 2)}}))
+    return rc;
+  if (int rc = check_device()) return rc;
+  (void)hipGetLastError();
+  const hipStream_t s = as_stream(stream);
+  const int64_t T0 = ceil_div(S, kTile);
+  float* part_s = static_cast<float*>(ws);
+  float* part_c = reinterpret_cast<float*>(static_cast<char*>(ws) + n_norm / 2);
+  char* pws = static_cast<char*>(ws) + n_norm;
+  uint16_t* a = reinterpret_cast<uint16_t*>(pws);
+  double* part = reinterpret_cast<double*>(pws + pad256(static_cast<size_t>(B * kD * 2)));
+  hipEvent_t e0, e1;
+  timing_events(&e0, &e1);
+  if (B <= adaln::proj_bwd_fused_max_batch()) {
+    // level-0 tiles; fold; then dx, dW and the da partials side by side
+    if (int rc = launched(adaln::launch_norm_mod_bwd_tiles(gout, x, mean, rstd, part_s, part_c, B, S, s)))
+      return rc;
+    if (int rc = launched(adaln::launch_tree_fold(part_s, part_c, d_emb, B, T0, kN, s))) return rc;
+    if (int rc = launched(adaln::launch_bwd_stage2(d_emb, temb, W, dW, part, gout, x, mean, rstd, emb, dx,
+                                                   B, S, s, e0, e1)))
+      return rc;
+  } else {
+    if (int rc = launched(adaln::launch_norm_mod_bwd(gout, x, mean, rstd, emb, dx, part_s, part_c, B, S, s,
+                                                     e0, e1)))
+      return rc;
+    if (int rc = launched(adaln::launch_tree_fold(part_s, part_c, d_emb, B, T0, kN, s))) return rc;
+    if (int rc = launched(adaln::launch_silu(temb, a, B * kD, s))) return rc;
+    if (int rc = launched(adaln::launch_proj_bwd_dw(d_emb, a, dW, B, s))) return rc;
+    if (int rc = launched(adaln::launch_proj_bwd_da(d_emb, W, part, B, s))) return rc;
+  }
+  return launched(adaln::launch_proj_bwd_final(part, d_emb, temb, dtemb, db, B, s));
 }
 
 int adaln_selftest(void) {

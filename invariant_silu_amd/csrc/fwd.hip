@@ -1,0 +1,367 @@
+// Forward of the AdaLN final modulation (RL-Kernel pull request 538, "What";
+// rounding points of miles_diffusion pull request 108):
+//
+//   emb  = bf16(fl32(SiLU(temb) W^T) + b)          (scale | shift), 3072 -> 6144
+//   mu   = fl32(sum_d x_d) / D,  var = fl32(sum_d (x_d - mu)^2) / D
+//   rstd = 1 / sqrt(var + eps),  n = (x - mu) * rstd
+//   out  = bf16((n * m) + shift),  m = bf16(1 + scale)
+//
+// Device pieces shared by every kernel below, so the standalone entry points
+// and the overlapped stage kernels compute identical bits:
+//
+// proj_block<NB>: 8 rows of W (4 waves x 2 rows) held in registers; lane l
+//   holds the 16-byte chunks l, l+64, ..., l+320 of a row, loaded chunk-major.
+//   The temb loads are issued first; their SiLU (silu8_fast, with the rare
+//   near-tie elements redone by silu_bf16_exact: identical bits to the float64
+//   definition) goes to LDS while W is in flight.  bf16 x bf16 products are
+//   exact in fp32 and are accumulated in fp64: chunk-major within the lane,
+//   then the fixed lane tree of wave_sum_f64; one rounding to fp32, the bias
+//   added in fp32, one rounding to bf16.  NB samples per pass, one
+//   accumulator each: emb of a sample does not depend on NB, B or the grid.
+// row_stats: one wave per row, the lane's 48 values summed in fp64 in order,
+//   then wave_sum_f64; (x - mu) and its square in fp32; correctly rounded
+//   sqrt and divide.
+// modulate: two fp32 operations per element, one bf16 rounding.
+//
+// Kernels: proj_fwd_kernel (adaln_proj_fwd), norm_mod_fwd_kernel (statistics
+// and modulation, adaln_norm_mod_fwd), and for the one-call forward adaln_fwd:
+// fwd_stage1_kernel (projection blocks and statistics blocks side by side in
+// one grid: two independent HBM streams, W and x) then norm_modulate_kernel.
+#include <type_traits>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace adaln {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kLaneChunks = kChunks / 64;                  // 6
+constexpr int kRows = 2;                                   // rows of W per wave
+constexpr int kProjRowsPerBlock = kWaves * kRows;          // 8
+constexpr int kProjBlocks = kN / kProjRowsPerBlock;        // 768
+static_assert(kN % kProjRowsPerBlock == 0, "rows per block must divide N");
+
+// ----------------------------------------------------------- projection ----
+template <int NB>
+struct ProjShared {
+  uint4 a[NB * kChunks];
+};
+
+template <int NB>
+__device__ __forceinline__ void proj_block(const uint16_t* __restrict__ temb,
+                                           const uint16_t* __restrict__ W,
+                                           const uint16_t* __restrict__ bias,
+                                           uint16_t* __restrict__ emb, int64_t B, int blk,
+                                           uint4* a_lds) {
+  constexpr int kStage = (NB * kChunks + kThreads - 1) / kThreads;
+  static_assert(kStage <= 8, "redo mask holds 8 chunks of 8 elements");
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int row0 = (blk * kWaves + wave) * kRows;
+
+  // SiLU of samples [b0, b0 + NB) into LDS; elements the fast path flags are
+  // redone from memory in a separate, rarely taken loop
+  auto stage = [&](const uint4 (&tz)[kStage], int64_t b0) __attribute__((always_inline)) {
+    uint64_t redo = 0;
+#pragma unroll
+    for (int k = 0; k < kStage; ++k) {
+      const int c = threadIdx.x + kThreads * k;
+      if (c < NB * kChunks) {
+        uint32_t m;
+        a_lds[c] = silu8_fast(tz[k], m);
+        redo |= static_cast<uint64_t>(m) << (8 * k);
+      }
+    }
+    while (redo != 0) {
+      const int bit = __builtin_ctzll(redo);
+      redo &= redo - 1;
+      const int c = threadIdx.x + kThreads * (bit / 8);
+      const int e = bit % 8;
+      reinterpret_cast<uint16_t*>(a_lds)[c * 8 + e] =
+          silu_bf16_exact(bf16_to_f32(temb[(b0 + c / kChunks) * kD + (c % kChunks) * 8 + e]));
+    }
+  };
+  auto load_temb = [&](uint4 (&tz)[kStage], int64_t b0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < kStage; ++k) {
+      const int c = threadIdx.x + kThreads * k;
+      if (c < NB * kChunks) tz[k] = ld16(temb + (b0 + c / kChunks) * kD + (c % kChunks) * 8);
+    }
+  };
+
+  // small loads first: the memory counter drains in issue order, so the
+  // first SiLU waits only for these while the W rows stay in flight
+  uint4 tz[kStage];
+  load_temb(tz, 0);
+  float bias_f[kRows];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) bias_f[r] = bf16_to_f32(bias[row0 + r]);
+  uint4 w[kLaneChunks][kRows];
+#pragma unroll
+  for (int i = 0; i < kLaneChunks; ++i)
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+      w[i][r] = ld16(W + static_cast<int64_t>(row0 + r) * kD + (lane + 64 * i) * 8);
+  stage(tz, 0);
+
+#pragma unroll 1
+  for (int64_t b0 = 0; b0 < B; b0 += NB) {
+    if (b0 > 0) {
+      __syncthreads();   // the previous pass is done reading a_lds
+      load_temb(tz, b0);
+      stage(tz, b0);
+      // the W registers are opaque here, so their unpacking is not hoisted
+      // out of this loop into extra registers
+#pragma unroll
+      for (int i = 0; i < kLaneChunks; ++i)
+#pragma unroll
+        for (int r = 0; r < kRows; ++r)
+          asm volatile("" : "+v"(w[i][r].x), "+v"(w[i][r].y), "+v"(w[i][r].z), "+v"(w[i][r].w));
+    }
+    __syncthreads();
+
+    double acc[kRows][NB];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) acc[r][bb] = 0.0;
+#pragma unroll
+    for (int i = 0; i < kLaneChunks; ++i) {
+      float av[NB][8];
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) unpack8(a_lds[bb * kChunks + lane + 64 * i], av[bb]);
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) {
+        float wv[8];
+        unpack8(w[i][r], wv);
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[r][bb] += static_cast<double>(av[bb][e] * wv[e]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        const double tot = wave_sum_f64(acc[r][bb]);
+        if (lane == r * NB + bb) {
+          const float v = static_cast<float>(tot) + bias_f[r];
+          emb[(b0 + bb) * kN + row0 + r] = f32_to_bf16(v);
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ LayerNorm ----
+__device__ __forceinline__ void load_row(const uint16_t* __restrict__ x, int64_t row, int lane,
+                                         uint4 (&xv)[kLaneChunks]) {
+#pragma unroll
+  for (int i = 0; i < kLaneChunks; ++i) xv[i] = ld16(x + row * kD + (lane + 64 * i) * 8);
+}
+
+__device__ __forceinline__ void row_stats(const uint4 (&xv)[kLaneChunks], float eps, float& mu,
+                                          float& rs) {
+  double acc = 0.0;
+#pragma unroll
+  for (int i = 0; i < kLaneChunks; ++i) {
+    float v[8];
+    unpack8(xv[i], v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += static_cast<double>(v[e]);
+  }
+  mu = static_cast<float>(wave_sum_f64(acc)) / static_cast<float>(kD);
+  double acc2 = 0.0;
+#pragma unroll
+  for (int i = 0; i < kLaneChunks; ++i) {
+    float v[8];
+    unpack8(xv[i], v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float d = v[e] - mu;
+      acc2 += static_cast<double>(d * d);
+    }
+  }
+  const float var = static_cast<float>(wave_sum_f64(acc2)) / static_cast<float>(kD);
+  rs = 1.0f / __builtin_sqrtf(var + eps);
+}
+
+// (1 + scale) and shift of sample b: loads (issue early), then LDS stores
+struct ModRegs {
+  uint2 sc[3], sh[3];
+};
+__device__ __forceinline__ void load_mod(const uint16_t* __restrict__ emb, int64_t b, ModRegs& r) {
+  const uint2* scale = reinterpret_cast<const uint2*>(emb + b * kN);
+  const uint2* shift = reinterpret_cast<const uint2*>(emb + b * kN + kD);
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    r.sc[k] = scale[threadIdx.x + kThreads * k];
+    r.sh[k] = shift[threadIdx.x + kThreads * k];
+  }
+}
+__device__ __forceinline__ void store_mod(const ModRegs& r, float4* m_lds, float4* sh_lds) {
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int c = threadIdx.x + kThreads * k;
+    m_lds[c] = make_float4(round_bf16(1.0f + bf_lo(r.sc[k].x)), round_bf16(1.0f + bf_hi(r.sc[k].x)),
+                           round_bf16(1.0f + bf_lo(r.sc[k].y)), round_bf16(1.0f + bf_hi(r.sc[k].y)));
+    sh_lds[c] = make_float4(bf_lo(r.sh[k].x), bf_hi(r.sh[k].x), bf_lo(r.sh[k].y), bf_hi(r.sh[k].y));
+  }
+}
+
+__device__ __forceinline__ void modulate(const uint4 (&xv)[kLaneChunks], float mu, float rs,
+                                         const float4* m_lds, const float4* sh_lds,
+                                         uint16_t* __restrict__ orow, int lane) {
+#pragma unroll
+  for (int i = 0; i < kLaneChunks; ++i) {
+    const int c = lane + 64 * i;
+    float v[8];
+    unpack8(xv[i], v);
+    const float4 m0 = m_lds[2 * c], m1 = m_lds[2 * c + 1];
+    const float4 h0 = sh_lds[2 * c], h1 = sh_lds[2 * c + 1];
+    const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+    const float hh[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float n = (v[e] - mu) * rs;
+      o[e] = n * mm[e] + hh[e];
+    }
+    st16_nt(orow + c * 8, pack8(o));
+  }
+}
+
+// ------------------------------------------------------------- kernels ----
+template <int NB>
+__global__ __launch_bounds__(kThreads) void proj_fwd_kernel(const uint16_t* __restrict__ temb,
+                                                            const uint16_t* __restrict__ W,
+                                                            const uint16_t* __restrict__ bias,
+                                                            uint16_t* __restrict__ emb, int64_t B) {
+  __shared__ ProjShared<NB> sh;
+  proj_block<NB>(temb, W, bias, emb, B, blockIdx.x, sh.a);
+}
+
+// 4 rows of one sample per block (one per wave): statistics and modulation
+__global__ __launch_bounds__(kThreads) void norm_mod_fwd_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ emb, uint16_t* __restrict__ out,
+    float* __restrict__ mean, float* __restrict__ rstd, int64_t S, float eps) {
+  __shared__ float4 m_lds[kD / 4];
+  __shared__ float4 sh_lds[kD / 4];
+  const int64_t b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int64_t s = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  const bool valid = s < S;
+  const int64_t row = b * S + (valid ? s : 0);
+  ModRegs mr;
+  load_mod(emb, b, mr);
+  uint4 xv[kLaneChunks];
+  load_row(x, row, lane, xv);
+  store_mod(mr, m_lds, sh_lds);
+  __syncthreads();
+  if (!valid) return;   // whole wave
+  float mu, rs;
+  row_stats(xv, eps, mu, rs);
+  modulate(xv, mu, rs, m_lds, sh_lds, out + row * kD, lane);
+  if (lane == 0) {
+    mean[row] = mu;
+    rstd[row] = rs;
+  }
+}
+
+// projection blocks [0, 768), then statistics blocks (4 rows each, rows of
+// all samples in order)
+template <int NB>
+__global__ __launch_bounds__(kThreads) void fwd_stage1_kernel(
+    const uint16_t* __restrict__ temb, const uint16_t* __restrict__ W,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ emb, const uint16_t* __restrict__ x,
+    float* __restrict__ mean, float* __restrict__ rstd, int64_t B, int64_t S, float eps) {
+  __shared__ ProjShared<NB> sh;
+  const int blk = blockIdx.x;
+  if (blk < kProjBlocks) {
+    proj_block<NB>(temb, W, bias, emb, B, blk, sh.a);
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  const int64_t r = static_cast<int64_t>(blk - kProjBlocks) * kWaves + (threadIdx.x >> 6);
+  if (r >= B * S) return;
+  uint4 xv[kLaneChunks];
+  load_row(x, r, lane, xv);
+  float mu, rs;
+  row_stats(xv, eps, mu, rs);
+  if (lane == 0) {
+    mean[r] = mu;
+    rstd[r] = rs;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void norm_modulate_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ emb, const float* __restrict__ mean,
+    const float* __restrict__ rstd, uint16_t* __restrict__ out, int64_t S) {
+  __shared__ float4 m_lds[kD / 4];
+  __shared__ float4 sh_lds[kD / 4];
+  const int64_t b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int64_t s = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  const bool valid = s < S;
+  const int64_t row = b * S + (valid ? s : 0);
+  ModRegs mr;
+  load_mod(emb, b, mr);
+  const float mu = mean[row];
+  const float rs = rstd[row];
+  uint4 xv[kLaneChunks];
+  load_row(x, row, lane, xv);
+  store_mod(mr, m_lds, sh_lds);
+  __syncthreads();
+  if (!valid) return;   // whole wave
+  modulate(xv, mu, rs, m_lds, sh_lds, out + row * kD, lane);
+}
+
+template <typename F>
+hipError_t by_batch(int64_t B, F&& f) {
+  if (B % 4 == 0) return f(std::integral_constant<int, 4>{});
+  if (B % 2 == 0) return f(std::integral_constant<int, 2>{});
+  return f(std::integral_constant<int, 1>{});
+}
+
+}  // namespace
+
+// NB = the largest of 4, 2, 1 that divides B, so every pass is a full one.
+hipError_t launch_proj_fwd(const uint16_t* temb, const uint16_t* W, const uint16_t* bias,
+                           uint16_t* emb, int64_t B, hipStream_t s) {
+  return by_batch(B, [&](auto nb) {
+    hipLaunchKernelGGL(proj_fwd_kernel<decltype(nb)::value>, dim3(kProjBlocks), dim3(kThreads), 0, s,
+                       temb, W, bias, emb, B);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_norm_mod_fwd(const uint16_t* x, const uint16_t* emb, uint16_t* out, float* mean,
+                               float* rstd, int64_t B, int64_t S, float eps, hipStream_t s) {
+  const int64_t gx = (S + kWaves - 1) / kWaves;
+  hipLaunchKernelGGL(norm_mod_fwd_kernel, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(B)),
+                     dim3(kThreads), 0, s, x, emb, out, mean, rstd, S, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const uint16_t* temb, const uint16_t* W, const uint16_t* bias,
+                      const uint16_t* x, uint16_t* emb, uint16_t* out, float* mean, float* rstd,
+                      int64_t B, int64_t S, float eps, hipStream_t s) {
+  const int64_t stat_blocks = (B * S + kWaves - 1) / kWaves;
+  hipError_t e = by_batch(B, [&](auto nb) {
+    hipLaunchKernelGGL(fwd_stage1_kernel<decltype(nb)::value>,
+                       dim3(static_cast<unsigned>(kProjBlocks + stat_blocks)), dim3(kThreads), 0, s,
+                       temb, W, bias, emb, x, mean, rstd, B, S, eps);
+    return hipGetLastError();
+  });
+  if (e != hipSuccess) return e;
+  const int64_t gx = (S + kWaves - 1) / kWaves;
+  hipLaunchKernelGGL(norm_modulate_kernel, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(B)),
+                     dim3(kThreads), 0, s, x, emb, mean, rstd, out, S);
+  return hipGetLastError();
+}
+
+}  // namespace adaln

@@ -12,6 +12,13 @@ namespace adaln {
 constexpr int kProjBwdParts = 32;
 
 hipError_t launch_silu(const uint16_t* temb, uint16_t* a, int64_t n, hipStream_t s);
+hipError_t launch_fwd(const uint16_t* temb, const uint16_t* W, const uint16_t* bias,
+                      const uint16_t* x, uint16_t* emb, uint16_t* out, float* mean, float* rstd,
+                      int64_t B, int64_t S, float eps, hipStream_t s);
+hipError_t launch_bwd_stage2(const float* d_emb, const uint16_t* temb, const uint16_t* W, uint16_t* dW,
+                             double* part, const uint16_t* g, const uint16_t* x, const float* mean,
+                             const float* rstd, const uint16_t* emb, uint16_t* dx, int64_t B, int64_t S,
+                             hipStream_t s, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 hipError_t launch_proj_fwd(const uint16_t* temb, const uint16_t* W, const uint16_t* bias,
                            uint16_t* emb, int64_t B, hipStream_t s);
 hipError_t launch_norm_mod_fwd(const uint16_t* x, const uint16_t* emb, uint16_t* out,

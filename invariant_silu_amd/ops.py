@@ -120,6 +120,44 @@ def token_tree_sum(x: torch.Tensor) -> torch.Tensor:
     return out
 
 
+def fwd(x: torch.Tensor, temb: torch.Tensor, W: torch.Tensor, bias: torch.Tensor, eps: float = EPS):
+    """One-call forward (adaln_fwd): (out, emb, mean, rstd), same bits as
+    proj_fwd followed by norm_mod_fwd."""
+    for t, n in ((x, "x"), (temb, "temb"), (W, "W"), (bias, "bias")):
+        _check(t, torch.bfloat16, n)
+    x, temb, W, bias = aligned(x), aligned(temb), aligned(W), aligned(bias)
+    B, S, Dx = x.shape
+    emb = torch.empty((B, N), dtype=torch.bfloat16, device=x.device)
+    out = torch.empty_like(x)
+    mean = torch.empty((B, S), dtype=torch.float32, device=x.device)
+    rstd = torch.empty((B, S), dtype=torch.float32, device=x.device)
+    _lib.call("adaln_fwd", temb.data_ptr(), W.data_ptr(), bias.data_ptr(), x.data_ptr(), emb.data_ptr(),
+              out.data_ptr(), mean.data_ptr(), rstd.data_ptr(), B, S, Dx, float(eps), _stream(x.device))
+    return out, emb, mean, rstd
+
+
+def bwd(g: torch.Tensor, x: torch.Tensor, mean: torch.Tensor, rstd: torch.Tensor, emb: torch.Tensor,
+        temb: torch.Tensor, W: torch.Tensor):
+    """One-call backward (adaln_bwd): (dx, d_emb, dW, db, dtemb), same bits as
+    norm_mod_bwd followed by proj_bwd."""
+    for t, n, dt in ((g, "g", torch.bfloat16), (x, "x", torch.bfloat16), (mean, "mean", torch.float32),
+                     (rstd, "rstd", torch.float32), (emb, "emb", torch.bfloat16),
+                     (temb, "temb", torch.bfloat16), (W, "W", torch.bfloat16)):
+        _check(t, dt, n)
+    g, x, mean, rstd, emb, temb, W = (aligned(t) for t in (g, x, mean, rstd, emb, temb, W))
+    B, S, Dx = x.shape
+    dx = torch.empty_like(x)
+    d_emb = torch.empty((B, N), dtype=torch.float32, device=x.device)
+    dW = torch.empty_like(W)
+    db = torch.empty((W.shape[0],), dtype=torch.bfloat16, device=W.device)
+    dtemb = torch.empty_like(temb)
+    ws = _ws(_lib.OP_BWD, B, S, Dx, x.device)
+    _lib.call("adaln_bwd", g.data_ptr(), x.data_ptr(), mean.data_ptr(), rstd.data_ptr(), emb.data_ptr(),
+              temb.data_ptr(), W.data_ptr(), dx.data_ptr(), d_emb.data_ptr(), dW.data_ptr(), db.data_ptr(),
+              dtemb.data_ptr(), ws.data_ptr(), ws.numel(), B, S, Dx, _stream(x.device))
+    return dx, d_emb, dW, db, dtemb
+
+
 def selftest() -> int:
     return int(_lib.load().adaln_selftest())
 
@@ -133,8 +171,7 @@ class AdaLNFinal(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, x, temb, W, b, eps=EPS):
-        emb = proj_fwd(temb, W, b)
-        out, mean, rstd = norm_mod_fwd(x, emb, eps)
+        out, emb, mean, rstd = fwd(x, temb, W, b, eps)
         ctx.save_for_backward(x, temb, W, emb, mean, rstd)
         return out
 
@@ -142,8 +179,7 @@ class AdaLNFinal(torch.autograd.Function):
     def backward(ctx, g):
         x, temb, W, emb, mean, rstd = ctx.saved_tensors
         g = g.to(torch.bfloat16)
-        dx, d_emb = norm_mod_bwd(g, x, mean, rstd, emb)
-        dW, db, dtemb = proj_bwd(d_emb, temb, W)
+        dx, d_emb, dW, db, dtemb = bwd(g, x, mean, rstd, emb, temb, W)
         return dx, dtemb, dW, db, None
 
 

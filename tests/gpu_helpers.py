@@ -39,6 +39,13 @@ def run_path_dev(d: dict, eps: float = 1e-6) -> dict:
     return dict(emb=emb, out=out, mean=mean, rstd=rstd, dx=dx, d_emb=d_emb, dW=dW, db=db, dtemb=dtemb)
 
 
+def run_onecall_dev(d: dict, eps: float = 1e-6) -> dict:
+    """The same step through the one-call entry points adaln_fwd / adaln_bwd."""
+    out, emb, mean, rstd = ops.fwd(d["x"], d["temb"], d["W"], d["bias"], eps)
+    dx, d_emb, dW, db, dtemb = ops.bwd(d["g"], d["x"], mean, rstd, emb, d["temb"], d["W"])
+    return dict(emb=emb, out=out, mean=mean, rstd=rstd, dx=dx, d_emb=d_emb, dW=dW, db=db, dtemb=dtemb)
+
+
 def to_host(r: dict) -> dict:
     torch.cuda.synchronize()
     h = {}

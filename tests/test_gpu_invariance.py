@@ -19,7 +19,7 @@ import pytest
 import torch
 
 from synthetic_inputs import make_inputs
-from tests.gpu_helpers import ROW_KEYS, dev_inputs, run_path_dev, same_bytes
+from tests.gpu_helpers import ROW_KEYS, dev_inputs, run_onecall_dev, run_path_dev, same_bytes
 
 pytestmark = pytest.mark.gpu
 
@@ -44,6 +44,8 @@ def test_b2_vs_b1(gpu_lib, S, seed):
     print(f"[invariance] B=2 vs B=1 S={S} seed={seed}", flush=True)
     d = dev_inputs(make_inputs(2, S, seed=seed))
     _assert_rows_equal(run_path_dev(d), _singletons(d, 2), label=f"S={S}")
+    # the one-call entry points, batch against singletons of the separate calls
+    _assert_rows_equal(run_onecall_dev(d), _singletons(d, 2), label=f"one-call S={S}")
 
 
 @pytest.mark.parametrize("S", [32, 33, 6032, 6889])

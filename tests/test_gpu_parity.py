@@ -18,7 +18,7 @@ from oracle import adaln, token_tree
 from oracle.fpmath import bits_to_f32
 from synthetic_inputs import make_inputs
 from tests.compare import bf16_gate, f32_gate
-from tests.gpu_helpers import run_path
+from tests.gpu_helpers import dev_inputs, run_onecall_dev, run_path, run_path_dev, same_bytes
 
 pytestmark = pytest.mark.gpu
 
@@ -120,3 +120,15 @@ def test_parity_large_batch_sampled(gpu_lib):
     rb = bf16_gate(gpu["db"][rows], db)
     print(f"  dW rows: {rw}\n  db rows: {rb}")
     assert rw["max_ulp"] <= 1 and rb["max_ulp"] <= 1
+
+
+@pytest.mark.parametrize("B,S", [(1, 31), (1, 4096), (2, 1024), (3, 97), (4, 33), (5, 40), (64, 64)])
+def test_onecall_path_matches_separate_calls(gpu_lib, B, S):
+    """adaln_fwd / adaln_bwd give the same bytes as the five separate entry
+    points (both branches of adaln_bwd: B <= 4 and B > 4)."""
+    print(f"[parity] one-call vs separate B={B} S={S}", flush=True)
+    d = dev_inputs(make_inputs(B, S, seed=B * 1000 + S, outlier_frac=0.01))
+    a = run_path_dev(d)
+    b = run_onecall_dev(d)
+    for k in a:
+        assert same_bytes(a[k], b[k]), k
