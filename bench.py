@@ -3,9 +3,10 @@
 
 One step is the whole hot path over one batch of synthetic input, through the
 C ABI: adaln_fwd (projection and LayerNorm statistics side by side, then the
-modulation) and adaln_bwd (level-0 token tiles, tree fold, then dx, dW and the
-W stream of the projection backward side by side, then dtemb and db).  Default workload: one 1024x1024 image
-stream, B = 1, S = 4096 tokens, D = 3072, bf16 storage, 1% outlier rows x20.
+modulation) and adaln_bwd (dx rows and level-0 token tiles in one launch, the
+tree fold, then the projection backward: dW and db, da and dtemb).  Default
+workload: one 1024x1024 image stream, B = 1, S = 4096 tokens, D = 3072, bf16
+storage, 1% outlier rows x20.
 
 Inputs are resident in HBM before the timed region.  The step rotates over
 several independent copies of every buffer (parameters included), so no step
@@ -13,8 +14,8 @@ finds the previous step's data in the 256 MB MALL; reuse inside one step (x
 read by the forward and the backward, W by both projections) is left as is.
 
 Prints ONE JSON line.  `roofline` covers the dominant kernel (the backward's
-main launch: W in, dW out, dx out),
-timed on every 8th timed step with HIP events that
+main launch: g and x in, dx out, level-0 token tiles out), timed on every 8th
+timed step with HIP events that
 its own dispatch carries on the stream it runs on (adaln_timing_begin/end: a
 timed dispatch leaves the stream idle for a few us, so timing is sampled);
 `cpu_baseline` is the NumPy oracle timed on this host on the same workload.
@@ -49,11 +50,11 @@ def algorithmic_bytes(B: int, S: int) -> int:
 
 
 def dominant_kernel_bytes(B: int, S: int) -> int:
-    """The backward's main launch (B <= 4): W read, dW written, dx written,
-    mean/rstd read; per sample scale, temb and d_emb read.  Its second read of
-    g and x (first read by the level-0 kernel) and its fp64 dtemb partials are
-    implementation overhead, not algorithmic bytes."""
-    return 2 * 2 * N * D + 2 * B * S * D + 8 * B * S + B * (2 * D + 2 * D + 4 * N)
+    """The backward's main launch: g and x read, dx written (6 B per element),
+    mean/rstd read, the scale half of emb read per sample.  Its level-0 token
+    tiles (fp32 pairs, 2 x 24 KB per 32-token tile) are implementation
+    overhead, not algorithmic bytes."""
+    return 6 * B * S * D + 8 * B * S + 2 * D * B
 
 
 def pmc_traffic():
@@ -213,7 +214,7 @@ def main() -> int:
                    "host_enqueue_ms_per_step": round((t_enq - t0) * 1e3 / args.steps, 5),
                    "step_gbps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
                    "step_frac_of_peak": round(step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)},
-        "roofline": {"bound": "hbm", "kernel": "bwd_stage2_kernel (dx rows, dW, W stream)",
+        "roofline": {"bound": "hbm", "kernel": "norm_mod_bwd_kernel<0> (dx rows + level-0 token tiles)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": pmc_traffic(),
                      "bytes_per_launch": k_bytes, "avg_launch_ms": round(k_mean_ms, 5),

@@ -70,10 +70,10 @@ enum adaln_op {
 };
 
 /* Workspace bytes an entry point needs (0 for an unknown op or bad sizes).
- *   NORM_MOD_BWD:   H = D (3072).  2 * B * ceil(S/32) * 2D * 4 bytes (level-0 pairs).
+ *   NORM_MOD_BWD:   H = D (3072).  B * ceil(S/32) * 2D * 8 bytes (level-0 pairs).
  *   PROJ_BWD:       H = K (3072), S ignored.  B*K*2 (SiLU activations, used when
- *                   B > 4) + 32*B*K*8 (fp64 partials of dtemb).
- *   TOKEN_TREE_SUM: 2 * B * ceil(S/32) * H * 4 bytes.
+ *                   B > 4).
+ *   TOKEN_TREE_SUM: B * ceil(S/32) * ceil(H/64) * 64 * 8 bytes (level-0 pairs).
  *   BWD:            H = D (3072).  NORM_MOD_BWD + PROJ_BWD, in that order.
  * Each region is padded to 256 bytes. */
 size_t adaln_workspace_bytes(int op, int64_t B, int64_t S, int64_t H);
@@ -113,14 +113,15 @@ int adaln_norm_mod_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float*
  * timed, overlapped or reused on its own).
  *
  * adaln_norm_mod_bwd_dx: dx only (arguments as in adaln_norm_mod_bwd).
- * adaln_norm_mod_bwd_tiles: level 0 of the token tree: `part` receives two fp32
- *   arrays, sums then corrections, each [B, ceil(S/32), 2D] (columns [0, D) of
- *   g * n for d_scale, [D, 2D) of g for d_shift) and each padded to 256 bytes;
- *   part_bytes must be at least adaln_workspace_bytes(ADALN_OP_NORM_MOD_BWD, B, S, D).
+ * adaln_norm_mod_bwd_tiles: level 0 of the token tree over H = 2D columns
+ *   (columns [0, D) of g * n for d_scale, [D, 2D) of g for d_shift).  `part`
+ *   receives fp32 [B, ceil(H/64), T0, 2, 64] with T0 = ceil(S/32): for sample b,
+ *   64-column group k and tile t, the 64 sums s of columns 64k .. 64k+63, then
+ *   their 64 corrections c; part_bytes must be at least
+ *   adaln_workspace_bytes(ADALN_OP_NORM_MOD_BWD, B, S, D).
  * token_tree_fold: levels >= 1 of the tree from such pairs: `part` as written by
- *   adaln_norm_mod_bwd_tiles (H = 2D) or by level 0 of token_tree_sum (any H),
- *   T0 = ceil(S/32) tiles per sample, corrections at byte offset
- *   pad256(B * T0 * H * 4); out [B, H] fp32. */
+ *   adaln_norm_mod_bwd_tiles (H = 2D) or by level 0 of token_tree_sum (any H, in
+ *   the same layout), T0 tiles per sample; out [B, H] fp32. */
 int adaln_norm_mod_bwd_dx(const adaln_bf16* gout, const adaln_bf16* x, const float* mean,
                           const float* rstd, const adaln_bf16* emb, adaln_bf16* dx, int64_t B,
                           int64_t S, int64_t D, void* stream);
@@ -163,20 +164,17 @@ int adaln_fwd(const adaln_bf16* temb, const adaln_bf16* W, const adaln_bf16* bia
               adaln_bf16* emb, adaln_bf16* out, float* mean, float* rstd, int64_t B, int64_t S,
               int64_t D, float eps, void* stream);
 
-/* One-call backward: adaln_norm_mod_bwd then adaln_proj_bwd, same results bit
- * for bit.  For B <= 4 the level-0 token tiles run first, then the tree fold,
- * then one launch in which the dx rows, the dW stream and the W stream of the
- * projection backward run side by side.  ws: adaln_workspace_bytes(ADALN_OP_BWD,
- * B, S, D) bytes. */
+/* One-call backward: adaln_norm_mod_bwd then adaln_proj_bwd (same launches,
+ * same results bit for bit) with one workspace and one validation pass.
+ * ws: adaln_workspace_bytes(ADALN_OP_BWD, B, S, D) bytes. */
 int adaln_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float* mean, const float* rstd,
               const adaln_bf16* emb, const adaln_bf16* temb, const adaln_bf16* W, adaln_bf16* dx,
               float* d_emb, adaln_bf16* dW, adaln_bf16* db, adaln_bf16* dtemb, void* ws, size_t ws_bytes,
               int64_t B, int64_t S, int64_t D, void* stream);
 
 /* Benchmarking aid: per-launch durations of the main kernel of the backward
- * (adaln_bwd: its last big launch -- dx, dW and W streams for B <= 4, the
- * fused dx + level-0 kernel otherwise; adaln_norm_mod_bwd: the fused dx +
- * level-0 kernel; adaln_norm_mod_bwd_dx: the dx kernel), timed with HIP
+ * (adaln_bwd and adaln_norm_mod_bwd: the fused dx + level-0 kernel;
+ * adaln_norm_mod_bwd_dx: the dx kernel), timed with HIP
  * events carried by the kernel dispatch itself (no extra packets).
  * A timed dispatch leaves the stream idle for a few microseconds around it, so
  * timing can be sampled: adaln_timing_begin(n, stride) creates n event pairs;

@@ -16,7 +16,6 @@
 
 namespace {
 
-using adaln::kProjBwdParts;
 
 constexpr int64_t kD = 3072;
 constexpr int64_t kN = 6144;
@@ -111,16 +110,15 @@ int check_device() {
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 inline int launched(hipError_t e) { return e == hipSuccess ? ADALN_OK : ADALN_ERR_LAUNCH; }
 
-size_t ws_norm_bwd(int64_t B, int64_t S) {
-  return 2 * pad256(static_cast<size_t>(B * ceil_div(S, kTile) * kN * 4));
+// level-0 pairs: per (sample, 64-column group, tile) 64 sums and 64 corrections
+size_t ws_pairs(int64_t B, int64_t S, int64_t H) {
+  return pad256(static_cast<size_t>(B * ceil_div(S, kTile) * ceil_div(H, 64) * 128 * 4));
 }
+size_t ws_norm_bwd(int64_t B, int64_t S) { return ws_pairs(B, S, kN); }
 size_t ws_proj_bwd(int64_t B) {
-  return pad256(static_cast<size_t>(B * kD * 2)) +
-         pad256(static_cast<size_t>(kProjBwdParts) * static_cast<size_t>(B * kD * 8));
+  return pad256(static_cast<size_t>(B * kD * 2));   // SiLU activations (B > 4)
 }
-size_t ws_tree(int64_t B, int64_t S, int64_t H) {
-  return 2 * pad256(static_cast<size_t>(B * ceil_div(S, kTile) * H * 4));
-}
+size_t ws_tree(int64_t B, int64_t S, int64_t H) { return ws_pairs(B, S, H); }
 bool batch_ok(int64_t B) { return B >= 1 && B <= kMaxB; }
 bool seq_ok(int64_t S) { return S >= 1 && S <= kMaxS; }
 
@@ -292,9 +290,7 @@ int adaln_norm_mod_bwd_tiles(const adaln_bf16* gout, const adaln_bf16* x, const 
     return rc;
   if (int rc = check_device()) return rc;
   (void)hipGetLastError();
-  float* part_s = static_cast<float*>(part);
-  float* part_c = reinterpret_cast<float*>(static_cast<char*>(part) + need / 2);
-  return launched(adaln::launch_norm_mod_bwd_tiles(gout, x, mean, rstd, part_s, part_c, B, S,
+  return launched(adaln::launch_norm_mod_bwd_tiles(gout, x, mean, rstd, static_cast<float*>(part), B, S,
                                                    as_stream(stream)));
 }
 
@@ -303,13 +299,11 @@ int token_tree_fold(const void* part, float* out, int64_t B, int64_t T0, int64_t
   if (!batch_ok(B) || T0 < 1 || T0 > kMaxS / kTile || H < 1 || H > (int64_t{1} << 24))
     return ADALN_ERR_SHAPE;
   if (!aligned16(part) || !aligned16(out)) return ADALN_ERR_ALIGN;
-  const size_t half = pad256(static_cast<size_t>(B * T0 * H * 4));
-  if (int rc = check_overlap({{out, static_cast<size_t>(B * H * 4)}}, {{part, 2 * half}})) return rc;
+  const size_t bytes = ws_pairs(B, T0 * kTile, H);
+  if (int rc = check_overlap({{out, static_cast<size_t>(B * H * 4)}}, {{part, bytes}})) return rc;
   if (int rc = check_device()) return rc;
   (void)hipGetLastError();
-  const float* part_s = static_cast<const float*>(part);
-  const float* part_c = reinterpret_cast<const float*>(static_cast<const char*>(part) + half);
-  return launched(adaln::launch_tree_fold(part_s, part_c, out, B, T0, H, as_stream(stream)));
+  return launched(adaln::launch_tree_fold(static_cast<const float*>(part), out, B, T0, H, as_stream(stream)));
 }
 
 int adaln_norm_mod_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float* mean,
@@ -329,11 +323,9 @@ int adaln_norm_mod_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float*
     return rc;
   if (int rc = check_device()) return rc;
   (void)hipGetLastError();
-  float* part_s = static_cast<float*>(ws);
-  float* part_c = reinterpret_cast<float*>(static_cast<char*>(ws) + need / 2);
   hipEvent_t e0, e1;
   timing_events(&e0, &e1);
-  if (int rc = launched(adaln::launch_norm_mod_bwd(gout, x, mean, rstd, emb, dx, part_s, part_c, B, S,
+  if (int rc = launched(adaln::launch_norm_mod_bwd(gout, x, mean, rstd, emb, dx, static_cast<float*>(ws), B, S,
                                                    as_stream(stream), e0, e1)))
     return rc;
   return token_tree_fold(ws, d_emb, B, ceil_div(S, kTile), kN, stream);
@@ -357,16 +349,12 @@ int adaln_proj_bwd(const float* d_emb, const adaln_bf16* temb, const adaln_bf16*
   if (int rc = check_device()) return rc;
   (void)hipGetLastError();
   uint16_t* a = static_cast<uint16_t*>(ws);
-  double* part = reinterpret_cast<double*>(static_cast<char*>(ws) + pad256(static_cast<size_t>(B * kD * 2)));
   const hipStream_t s = as_stream(stream);
-  if (B <= adaln::proj_bwd_fused_max_batch()) {
-    if (int rc = launched(adaln::launch_proj_bwd_fused(d_emb, temb, W, dW, part, B, s))) return rc;
-  } else {
-    if (int rc = launched(adaln::launch_silu(temb, a, B * kD, s))) return rc;
-    if (int rc = launched(adaln::launch_proj_bwd_dw(d_emb, a, dW, B, s))) return rc;
-    if (int rc = launched(adaln::launch_proj_bwd_da(d_emb, W, part, B, s))) return rc;
-  }
-  return launched(adaln::launch_proj_bwd_final(part, d_emb, temb, dtemb, db, B, s));
+  if (B <= adaln::proj_bwd_fused_max_batch())
+    return launched(adaln::launch_proj_bwd_fused(d_emb, temb, W, dW, db, dtemb, B, s));
+  if (int rc = launched(adaln::launch_silu(temb, a, B * kD, s))) return rc;
+  if (int rc = launched(adaln::launch_proj_bwd_dw(d_emb, a, dW, db, B, s))) return rc;
+  return launched(adaln::launch_proj_bwd_da(d_emb, W, temb, dtemb, B, s));
 }
 
 int token_tree_sum(const float* x, float* out, void* ws, size_t ws_bytes, int64_t B, int64_t S,
@@ -382,11 +370,10 @@ int token_tree_sum(const float* x, float* out, void* ws, size_t ws_bytes, int64_
   if (int rc = check_device()) return rc;
   (void)hipGetLastError();
   const int64_t T0 = ceil_div(S, kTile);
-  float* part_s = static_cast<float*>(ws);
-  float* part_c = reinterpret_cast<float*>(static_cast<char*>(ws) + need / 2);
+  float* part = static_cast<float*>(ws);
   const hipStream_t s = as_stream(stream);
-  if (int rc = launched(adaln::launch_token_level0(x, part_s, part_c, B, S, H, s))) return rc;
-  return launched(adaln::launch_tree_fold(part_s, part_c, out, B, T0, H, s));
+  if (int rc = launched(adaln::launch_token_level0(x, part, B, S, H, s))) return rc;
+  return launched(adaln::launch_tree_fold(part, out, B, T0, H, s));
 }
 
 int adaln_timing_begin(int n, int stride) {
@@ -471,31 +458,20 @@ int adaln_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float* mean, co
   (void)hipGetLastError();
   const hipStream_t s = as_stream(stream);
   const int64_t T0 = ceil_div(S, kTile);
-  float* part_s = static_cast<float*>(ws);
-  float* part_c = reinterpret_cast<float*>(static_cast<char*>(ws) + n_norm / 2);
-  char* pws = static_cast<char*>(ws) + n_norm;
-  uint16_t* a = reinterpret_cast<uint16_t*>(pws);
-  double* part = reinterpret_cast<double*>(pws + pad256(static_cast<size_t>(B * kD * 2)));
+  float* part = static_cast<float*>(ws);
+  uint16_t* a = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + n_norm);
   hipEvent_t e0, e1;
   timing_events(&e0, &e1);
-  if (B <= adaln::proj_bwd_fused_max_batch()) {
-    // level-0 tiles; fold; then dx, dW and the da partials side by side
-    if (int rc = launched(adaln::launch_norm_mod_bwd_tiles(gout, x, mean, rstd, part_s, part_c, B, S, s)))
-      return rc;
-    if (int rc = launched(adaln::launch_tree_fold(part_s, part_c, d_emb, B, T0, kN, s))) return rc;
-    if (int rc = launched(adaln::launch_bwd_stage2(d_emb, temb, W, dW, part, gout, x, mean, rstd, emb, dx,
-                                                   B, S, s, e0, e1)))
-      return rc;
-  } else {
-    if (int rc = launched(adaln::launch_norm_mod_bwd(gout, x, mean, rstd, emb, dx, part_s, part_c, B, S, s,
-                                                     e0, e1)))
-      return rc;
-    if (int rc = launched(adaln::launch_tree_fold(part_s, part_c, d_emb, B, T0, kN, s))) return rc;
-    if (int rc = launched(adaln::launch_silu(temb, a, B * kD, s))) return rc;
-    if (int rc = launched(adaln::launch_proj_bwd_dw(d_emb, a, dW, B, s))) return rc;
-    if (int rc = launched(adaln::launch_proj_bwd_da(d_emb, W, part, B, s))) return rc;
-  }
-  return launched(adaln::launch_proj_bwd_final(part, d_emb, temb, dtemb, db, B, s));
+  // dx rows and level-0 tiles in one launch (g and x read once), the fold,
+  // then the projection backward: adaln_norm_mod_bwd then adaln_proj_bwd
+  if (int rc = launched(adaln::launch_norm_mod_bwd(gout, x, mean, rstd, emb, dx, part, B, S, s, e0, e1)))
+    return rc;
+  if (int rc = launched(adaln::launch_tree_fold(part, d_emb, B, T0, kN, s))) return rc;
+  if (B <= adaln::proj_bwd_fused_max_batch())
+    return launched(adaln::launch_proj_bwd_fused(d_emb, temb, W, dW, db, dtemb, B, s));
+  if (int rc = launched(adaln::launch_silu(temb, a, B * kD, s))) return rc;
+  if (int rc = launched(adaln::launch_proj_bwd_dw(d_emb, a, dW, db, B, s))) return rc;
+  return launched(adaln::launch_proj_bwd_da(d_emb, W, temb, dtemb, B, s));
 }
 
 int adaln_selftest(void) {

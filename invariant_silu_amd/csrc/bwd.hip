@@ -18,21 +18,18 @@
 //   da[b,k]  = fl32(sum_j d_emb[b,j] * W[j,k])             (fp32 products)
 //   dtemb    = bf16(da * silu'(temb))
 // Sums accumulate fp32 products in fp64 in fixed orders: samples ascending
-// for dW and db; for da, 32 parts of 192 rows, in a part 8 row slots walking
-// every 8th row in order, slots as a pairwise tree, parts added in order.
+// for dW and db; for da, 128 row slots (slot t: rows t, t + 128, ... in
+// order) added as a pairwise tree.
 //
-// Device pieces are shared by every kernel, so the standalone entry points
-// and the overlapped stage kernel compute identical bits, and no order
-// depends on the batch size or the grid.
+// Device pieces are shared by every kernel, so every entry point computes
+// identical bits, and no order depends on the batch size or the grid.
 //
 // Kernels:
 //   norm_mod_bwd_kernel<role>  dx rows and/or level-0 tiles of a 32-token
 //                              tile, the 14 blocks of a tile on one XCD
-//   proj_bwd_small_kernel<NB>  B <= 4: dW-writing and W-reading blocks in one grid
+//   proj_bwd_small_kernel<NB>  B <= 4: da column blocks (-> dtemb) and dW
+//                              tiles (-> dW, db) in one grid
 //   silu/dW/da kernels         B > 4
-//   proj_bwd_final_kernel      dtemb from the partials, and db
-//   bwd_stage2_kernel<NB>      one-call backward, B <= 4: da-partial blocks,
-//                              dW blocks and dx row blocks side by side
 #include <hip/hip_ext.h>
 
 #include "common.hpp"
@@ -56,10 +53,11 @@ __device__ __forceinline__ void row_pass(const uint16_t* __restrict__ g, const u
                                          const float* __restrict__ mean, const float* __restrict__ rstd,
                                          const uint16_t* __restrict__ emb, uint16_t* __restrict__ dx,
                                          int64_t b, int64_t s, int64_t S, float4* m_lds) {
-  const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const bool valid = s < S;
-  const int64_t row = b * S + (valid ? s : 0);
+  // A wave past the end of the sample redoes row S - 1 and stores the same
+  // bytes as the wave that owns it: no branch follows the barrier, so the
+  // compiler keeps the row loads ahead of it.
+  const int64_t row = b * S + (s < S ? s : S - 1);
 
   // small loads first: the memory counter drains in issue order, so staging
   // m needs only these, while the row loads below stay in flight
@@ -67,22 +65,20 @@ __device__ __forceinline__ void row_pass(const uint16_t* __restrict__ g, const u
   uint2 sc[3];
 #pragma unroll
   for (int k = 0; k < 3; ++k) sc[k] = scale[threadIdx.x + kThreads * k];
+  const float mu = mean[row];
+  const float rs = rstd[row];
   uint4 gv[kLaneChunks], xv[kLaneChunks];
 #pragma unroll
   for (int i = 0; i < kLaneChunks; ++i) {
     gv[i] = ld16(g + row * kD + (lane + 64 * i) * 8);
     xv[i] = ld16(x + row * kD + (lane + 64 * i) * 8);
   }
-  const float mu = mean[row];
-  const float rs = rstd[row];
 #pragma unroll
   for (int k = 0; k < 3; ++k)
     m_lds[threadIdx.x + kThreads * k] =
         make_float4(round_bf16(1.0f + bf_lo(sc[k].x)), round_bf16(1.0f + bf_hi(sc[k].x)),
                     round_bf16(1.0f + bf_lo(sc[k].y)), round_bf16(1.0f + bf_hi(sc[k].y)));
   __syncthreads();
-  (void)wave;
-  if (!valid) return;   // whole wave
 
   double q1 = 0.0, q2 = 0.0;
 #pragma unroll
@@ -130,41 +126,45 @@ __device__ __forceinline__ void row_pass(const uint16_t* __restrict__ g, const u
   }
 }
 
-__device__ __forceinline__ void col_pass(const uint16_t* __restrict__ g, const uint16_t* __restrict__ x,
+// Level-0 pairs of one 32-token tile for 512 columns (2 per thread).  The
+// tile's statistics are the same for the whole block (scalar loads, no LDS,
+// no barrier).  A full tile takes the branch-free form: buffer loads (the
+// lane's column offset in a VGPR, the row's in an SGPR, no per-load address
+// arithmetic), and the memory counter lets the chains start on row 0 while
+// later rows are in flight.  Only the last, ragged tile of a sample takes the
+// guarded form.
+template <bool kFull>
+__device__ __forceinline__ void col_tile(const uint16_t* __restrict__ g, const uint16_t* __restrict__ x,
                                          const float* __restrict__ mean, const float* __restrict__ rstd,
-                                         float* __restrict__ part_s, float* __restrict__ part_c,
-                                         int64_t b, int64_t tile, int cb, int64_t S, int64_t T0,
-                                         float* mu_s, float* rs_s) {
+                                         float* __restrict__ part, int64_t b, int64_t tile, int cb,
+                                         int64_t S, int64_t T0, int rows) {
   const int col = cb * kColBlockCols + 2 * threadIdx.x;
-  const int rows = static_cast<int>((S - tile * kTile) < kTile ? (S - tile * kTile) : kTile);
   const int64_t row0 = b * S + tile * kTile;
-
-  float mu_l = 0.0f, rs_l = 0.0f;
-  if (threadIdx.x < rows) {
-    mu_l = mean[row0 + threadIdx.x];
-    rs_l = rstd[row0 + threadIdx.x];
-  }
   uint32_t gw[kTile], xw[kTile];
+  if (kFull) {
+    constexpr uint32_t kBytes = kTile * kD * 2;
+    const Buffer gt(g + row0 * kD, kBytes), xt(x + row0 * kD, kBytes);
 #pragma unroll
-  for (int r = 0; r < kTile; ++r) {
-    if (r < rows) {
-      const int64_t off = (row0 + r) * kD + col;
-      gw[r] = *reinterpret_cast<const uint32_t*>(g + off);
-      xw[r] = *reinterpret_cast<const uint32_t*>(x + off);
+    for (int r = 0; r < kTile; ++r) {
+      gw[r] = gt.u32(col * 2, r * kD * 2);
+      xw[r] = xt.u32(col * 2, r * kD * 2);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < kTile; ++r) {
+      if (r < rows) {
+        const int64_t off = (row0 + r) * kD + col;
+        gw[r] = *reinterpret_cast<const uint32_t*>(g + off);
+        xw[r] = *reinterpret_cast<const uint32_t*>(x + off);
+      }
     }
   }
-  if (threadIdx.x < rows) {
-    mu_s[threadIdx.x] = mu_l;
-    rs_s[threadIdx.x] = rs_l;
-  }
-  __syncthreads();
-
   float sg0 = 0.0f, cg0 = 0.0f, sg1 = 0.0f, cg1 = 0.0f;
   float sn0 = 0.0f, cn0 = 0.0f, sn1 = 0.0f, cn1 = 0.0f;
 #pragma unroll
   for (int r = 0; r < kTile; ++r) {
-    if (r < rows) {
-      const float mu = mu_s[r], rs = rs_s[r];
+    if (kFull || r < rows) {
+      const float mu = mean[row0 + r], rs = rstd[row0 + r];
       const float g0 = bf_lo(gw[r]), g1 = bf_hi(gw[r]);
       const float n0 = (bf_lo(xw[r]) - mu) * rs;
       const float n1 = (bf_hi(xw[r]) - mu) * rs;
@@ -175,11 +175,22 @@ __device__ __forceinline__ void col_pass(const uint16_t* __restrict__ g, const u
     }
   }
   // columns [0, D) of d_emb: d_scale (g * n); [D, 2D): d_shift (g)
-  const int64_t base = (b * T0 + tile) * kN + col;
-  *reinterpret_cast<float2*>(part_s + base) = make_float2(sn0, sn1);
-  *reinterpret_cast<float2*>(part_c + base) = make_float2(cn0, cn1);
-  *reinterpret_cast<float2*>(part_s + base + kD) = make_float2(sg0, sg1);
-  *reinterpret_cast<float2*>(part_c + base + kD) = make_float2(cg0, cg1);
+  constexpr int64_t kGroups = kN / kPairGroup;
+  const int64_t i_scale = pair_index(b, kGroups, T0, tile, col);
+  const int64_t i_shift = pair_index(b, kGroups, T0, tile, col + kD);
+  st8_nt(part + i_scale, sn0, sn1);
+  st8_nt(part + i_scale + kPairGroup, cn0, cn1);
+  st8_nt(part + i_shift, sg0, sg1);
+  st8_nt(part + i_shift + kPairGroup, cg0, cg1);
+}
+
+__device__ __forceinline__ void col_pass(const uint16_t* __restrict__ g, const uint16_t* __restrict__ x,
+                                         const float* __restrict__ mean, const float* __restrict__ rstd,
+                                         float* __restrict__ part, int64_t b, int64_t tile, int cb,
+                                         int64_t S, int64_t T0) {
+  const int64_t left = S - tile * kTile;
+  if (left >= kTile) col_tile<true>(g, x, mean, rstd, part, b, tile, cb, S, T0, kTile);
+  else col_tile<false>(g, x, mean, rstd, part, b, tile, cb, S, T0, static_cast<int>(left));
 }
 
 // grid: 1-D, ceil(B*T0 / 8) * 8 * blocks_per_tile blocks (blocks_per_tile = 14,
@@ -190,9 +201,9 @@ __global__ __launch_bounds__(kThreads) void norm_mod_bwd_kernel(
     const uint16_t* __restrict__ g, const uint16_t* __restrict__ x,
     const float* __restrict__ mean, const float* __restrict__ rstd,
     const uint16_t* __restrict__ emb, uint16_t* __restrict__ dx,
-    float* __restrict__ part_s, float* __restrict__ part_c, int64_t B, int64_t S, int64_t T0) {
+    float* __restrict__ part, int64_t B, int64_t S, int64_t T0) {
   constexpr int bpt = kRole == kBoth ? kBlocksPerTile : (kRole == kRowsOnly ? kRowBlocks : kColBlocks);
-  __shared__ float4 m_lds[kD / 4];   // row blocks: m = bf16(1 + scale); column blocks: mean/rstd
+  __shared__ float4 m_lds[kD / 4];   // row blocks: m = bf16(1 + scale)
   const int64_t L = blockIdx.x;
   const int64_t j = L >> 3;
   const int64_t G = (j / bpt) * 8 + (L & 7);
@@ -205,35 +216,149 @@ __global__ __launch_bounds__(kThreads) void norm_mod_bwd_kernel(
     row_pass(g, x, mean, rstd, emb, dx, b, s, S, m_lds);
   } else {
     const int cb = kRole == kColsOnly ? role : role - kRowBlocks;
-    float* f = reinterpret_cast<float*>(m_lds);
-    col_pass(g, x, mean, rstd, part_s, part_c, b, tile, cb, S, T0, f, f + kTile);
+    col_pass(g, x, mean, rstd, part, b, tile, cb, S, T0);
   }
 }
 
-constexpr int kTileCols = 256;                       // columns per block (32 threads x 8)
+// ---- projection backward ------------------------------------------------
+// dW tiles: part p of 32 (192 rows) x column block kb of 12 (256 columns),
+// a write stream; 8 row slots, a thread's 8 columns per row.
+constexpr int kDwParts = 32;
+constexpr int kTileCols = 256;                       // columns per dW tile (32 threads x 8)
 constexpr int kColThreads = kTileCols / 8;           // 32
-constexpr int kSlots = 8;                            // row slots per block
+constexpr int kSlots = 8;                            // row slots per dW tile
 constexpr int kBlockThreads = kColThreads * kSlots;  // 256
-constexpr int kRowsPerPart = kN / kProjBwdParts;     // 192
+constexpr int kRowsPerPart = kN / kDwParts;          // 192
 constexpr int kSteps = kRowsPerPart / kSlots;        // 24 rows per thread
+constexpr int kDwTiles = kDwParts * (kD / kTileCols);   // 384
 constexpr int kBatchChunk = 4;
 
-static_assert(kN % kProjBwdParts == 0 && kRowsPerPart % kSlots == 0, "part layout");
+static_assert(kN % kDwParts == 0 && kRowsPerPart % kSlots == 0, "part layout");
 static_assert(kD % kTileCols == 0, "column blocks");
+static_assert(kBlockThreads == kThreads, "one block size for every role");
 
-// slots combined as ((s0+s1)+(s2+s3)) + ((s4+s5)+(s6+s7)) (the same tree in
-// every kernel that forms da partials)
-__device__ __forceinline__ double slot_tree(const double (*red)[kBatchChunk][kTileCols], int b, int c) {
-  return ((red[0][b][c] + red[1][b][c]) + (red[2][b][c] + red[3][b][c])) +
-         ((red[4][b][c] + red[5][b][c]) + (red[6][b][c] + red[7][b][c]));
+// da blocks: 16 columns of W over all 6144 rows, so each block finishes the
+// sum and writes dtemb itself.  128 row slots, slot t walks rows t, t + 128,
+// ... in order (fp64 accumulation of fp32 products); the 128 slots are then
+// added as a pairwise tree.  The four 32-byte quarters of a 128-byte row
+// segment go to blocks L, L + 8, L + 16 and L + 24, which the dispatcher
+// places on the same XCD (one L2 serves all four).
+constexpr int kDaCols = 16;
+constexpr int kDaColThreads = kDaCols / 8;            // 2
+constexpr int kDaSlots = kThreads / kDaColThreads;    // 128
+constexpr int kDaBlocks = kD / kDaCols;               // 192
+constexpr int kDaSteps = kN / kDaSlots;               // 48 rows per thread
+constexpr int kDaShare = 128 / (kDaCols * 2);         // blocks sharing a 128-byte segment: 4
+
+static_assert(kDaBlocks % (8 * kDaShare) == 0, "da block to column mapping");
+
+__device__ __forceinline__ int da_first_col(int L) {
+  const int g = L / (8 * kDaShare), q = (L / 8) % kDaShare, xcd = L % 8;
+  return ((g * 8 + xcd) * kDaShare + q) * kDaCols;
+}
+
+// da and dtemb for samples b0 .. b0 + nb - 1 (nb <= NB) and the 32 columns of
+// block L.  red: LDS, kDaSlots * NB * kDaCols doubles.
+template <int NB>
+__device__ __forceinline__ void da_block(const float* __restrict__ d_emb, const uint16_t* __restrict__ W,
+                                         const uint16_t* __restrict__ temb, uint16_t* __restrict__ dtemb,
+                                         int L, int64_t b0, int nb, double* red) {
+  // rows per batch (two batches in flight), sized to keep registers <= ~128
+  constexpr int U = NB == 1 ? 8 : (NB == 2 ? 6 : (NB == 3 ? 6 : 4));
+  static_assert(kDaSteps % (2 * U) == 0, "batch pairs");
+  static_assert(kDaSteps % U == 0, "batches");
+  const int ct = threadIdx.x % kDaColThreads;
+  const int slot = threadIdx.x / kDaColThreads;
+  const int col0 = da_first_col(L);
+  const Buffer wb(W, static_cast<uint32_t>(kN) * kD * 2);
+  const Buffer eb(d_emb + b0 * kN, static_cast<uint32_t>(nb) * kN * 4);
+  const uint32_t w_lane = (static_cast<uint32_t>(slot) * kD + col0 + ct * 8) * 2;
+  const uint32_t e_lane = static_cast<uint32_t>(slot) * 4;
+  constexpr uint32_t kWStep = kDaSlots * kD * 2;   // bytes between a slot's rows
+  constexpr uint32_t kEStep = kDaSlots * 4;
+
+  auto load = [&](int i0, uint4 (&w)[U], float (&d)[U][NB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = wb.u128(w_lane, (i0 + u) * kWStep);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int bl = b < nb ? b : nb - 1;   // samples past nb: any in-range value, never stored
+        d[u][b] = eb.f32(e_lane, bl * kN * 4 + (i0 + u) * kEStep);
+      }
+  };
+  double acc[NB][8];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[b][e] = 0.0;
+  auto accumulate = [&](const uint4 (&w)[U], const float (&d)[U][NB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float wf[8];
+      unpack8(w[u], wf);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[b][e] += static_cast<double>(d[u][b] * wf[e]);
+    }
+  };
+
+  // two register batches: the next one is in flight while one is added
+  uint4 wa[U], wbt[U];
+  float da_[U][NB], db_[U][NB];
+  load(0, wa, da_);
+  // (scheduling barriers keep the compiler from hoisting a batch's loads
+  // above the adds of the batch whose registers they reuse)
+#pragma unroll 1
+  for (int i0 = 0; i0 < kDaSteps - 2 * U; i0 += 2 * U) {
+    load(i0 + U, wbt, db_);
+    __builtin_amdgcn_sched_barrier(0);
+    accumulate(wa, da_);
+    __builtin_amdgcn_sched_barrier(0);
+    load(i0 + 2 * U, wa, da_);
+    __builtin_amdgcn_sched_barrier(0);
+    accumulate(wbt, db_);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  load(kDaSteps - U, wbt, db_);
+  __builtin_amdgcn_sched_barrier(0);
+  accumulate(wa, da_);
+  accumulate(wbt, db_);
+
+  constexpr int kRow = NB * kDaCols;   // doubles per slot
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[slot * kRow + b * kDaCols + ct * 8 + e] = acc[b][e];
+  __syncthreads();
+  // pairwise tree over the slots: ((s0 + s1) + (s2 + s3)) + ...
+#pragma unroll
+  for (int w = 1; w < kDaSlots; w <<= 1) {
+    for (int i = threadIdx.x; i < (kDaSlots / (2 * w)) * kRow; i += kThreads) {
+      const int s = (i / kRow) * 2 * w, r = i % kRow;
+      red[s * kRow + r] += red[(s + w) * kRow + r];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x < kRow) {
+    const int b = threadIdx.x / kDaCols, c = threadIdx.x % kDaCols;
+    if (b < nb) {
+      const int64_t i = (b0 + b) * kD + col0 + c;
+      dtemb[i] = f32_to_bf16(static_cast<float>(red[threadIdx.x]) * dsilu_f32(bf16_to_f32(temb[i])));
+    }
+  }
 }
 
 // dW tile (192 rows x 256 columns of part p, column block kb): a write
-// stream; a = bf16(SiLU(temb)) per thread for its 8 columns.
+// stream; a = bf16(SiLU(temb)) per thread for its 8 columns.  Tiles of column
+// block 0 also write db for their rows: samples in order from +0.
 template <int NB>
 __device__ __forceinline__ void dw_tile(const float* __restrict__ d_emb,
                                         const uint16_t* __restrict__ temb, uint16_t* __restrict__ dW,
-                                        int p, int kb, float (*de_lds)[kRowsPerPart]) {
+                                        uint16_t* __restrict__ db, int p, int kb,
+                                        float (*de_lds)[kRowsPerPart]) {
   const int ct = threadIdx.x % kColThreads;
   const int slot = threadIdx.x / kColThreads;
   const int col = kb * kTileCols + ct * 8;
@@ -274,6 +399,12 @@ __device__ __forceinline__ void dw_tile(const float* __restrict__ d_emb,
         if (bb == b && ee == e) av[bb][ee] = v;
   }
   __syncthreads();
+  if (kb == 0 && threadIdx.x < kRowsPerPart) {
+    double s = 0.0;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) s += static_cast<double>(de_lds[b][threadIdx.x]);
+    db[jbase + threadIdx.x] = f32_to_bf16(static_cast<float>(s));
+  }
 #pragma unroll 4
   for (int i = 0; i < kSteps; ++i) {
     const int jl = slot + kSlots * i;
@@ -289,111 +420,29 @@ __device__ __forceinline__ void dw_tile(const float* __restrict__ d_emb,
   }
 }
 
-// da partial tile (same tiling): a read stream over W.
+// LDS of a projection-backward block, laid out per role.
 template <int NB>
-__device__ __forceinline__ void da_tile(const float* __restrict__ d_emb, const uint16_t* __restrict__ W,
-                                        double* __restrict__ part, int p, int kb,
-                                        float (*de_lds)[kRowsPerPart], double (*red)[NB][kTileCols]) {
-  const int ct = threadIdx.x % kColThreads;
-  const int slot = threadIdx.x / kColThreads;
-  const int col = kb * kTileCols + ct * 8;
-  const int jbase = p * kRowsPerPart;
-  constexpr int kDeLoads = (NB * kRowsPerPart + kBlockThreads - 1) / kBlockThreads;
-  float de_r[kDeLoads];
-#pragma unroll
-  for (int k = 0; k < kDeLoads; ++k) {
-    const int idx = threadIdx.x + kBlockThreads * k;
-    if (idx < NB * kRowsPerPart)
-      de_r[k] = d_emb[static_cast<int64_t>(idx / kRowsPerPart) * kN + jbase + idx % kRowsPerPart];
-  }
-  uint4 wv[kSteps];
-#pragma unroll
-  for (int i = 0; i < kSteps; ++i)
-    wv[i] = ld16(W + static_cast<int64_t>(jbase + slot + kSlots * i) * kD + col);
-#pragma unroll
-  for (int k = 0; k < kDeLoads; ++k) {
-    const int idx = threadIdx.x + kBlockThreads * k;
-    if (idx < NB * kRowsPerPart) de_lds[idx / kRowsPerPart][idx % kRowsPerPart] = de_r[k];
-  }
-  __syncthreads();
-  double acc[NB][8];
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[b][e] = 0.0;
-#pragma unroll
-  for (int i = 0; i < kSteps; ++i) {
-    const int jl = slot + kSlots * i;
-    float w[8];
-    unpack8(wv[i], w);
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const float d = de_lds[b][jl];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[b][e] += static_cast<double>(d * w[e]);
-    }
-  }
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) red[slot][b][ct * 8 + e] = acc[b][e];
-  __syncthreads();
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int c = threadIdx.x;
-    const double v = ((red[0][b][c] + red[1][b][c]) + (red[2][b][c] + red[3][b][c])) +
-                     ((red[4][b][c] + red[5][b][c]) + (red[6][b][c] + red[7][b][c]));
-    part[(static_cast<int64_t>(p) * NB + b) * kD + kb * kTileCols + c] = v;
-  }
-}
+struct ProjBwdShared {
+  static constexpr size_t kRed = sizeof(double) * kDaSlots * NB * kDaCols;
+  static constexpr size_t kDe = sizeof(float) * NB * kRowsPerPart;
+  static constexpr size_t kBytes = kRed > kDe ? kRed : kDe;
+};
 
-// Small batches (B <= 4, a template parameter): one grid, blockIdx.z = 0
-// writes dW, blockIdx.z = 1 reads W for the da partials; the two streams run
-// side by side.
+// Small batches (B <= 4, a template parameter): one grid, blocks [0, 192)
+// are the da column blocks (they read W and write dtemb), blocks [192, 576)
+// the dW tiles (they write dW and db); the two streams run side by side.
 template <int NB>
-__global__ __launch_bounds__(kBlockThreads) void proj_bwd_small_kernel(
-    const float* __restrict__ d_emb, const uint16_t* __restrict__ temb,
-    const uint16_t* __restrict__ W, uint16_t* __restrict__ dW, double* __restrict__ part) {
-  __shared__ double red[kSlots][NB][kTileCols];
-  __shared__ float de_lds[NB][kRowsPerPart];
-  if (blockIdx.z == 0) dw_tile<NB>(d_emb, temb, dW, blockIdx.x, blockIdx.y, de_lds);
-  else da_tile<NB>(d_emb, W, part, blockIdx.x, blockIdx.y, de_lds, red);
-}
-
-// One-call backward, second stage (B <= 4).  Blocks [0, 384): da partial
-// tiles; [384, 768): dW tiles; then dx row blocks (4 rows of one sample each,
-// samples in order).  W in, dW out and the dx stream (g and x again, just
-// read by the level-0 kernel, dx out) run side by side.
-constexpr int kProjTiles = kProjBwdParts * (kD / kTileCols);   // 384
-
-template <int NB>
-__global__ __launch_bounds__(kThreads) void bwd_stage2_kernel(
-    const float* __restrict__ d_emb, const uint16_t* __restrict__ temb,
-    const uint16_t* __restrict__ W, uint16_t* __restrict__ dW, double* __restrict__ part,
-    const uint16_t* __restrict__ g, const uint16_t* __restrict__ x, const float* __restrict__ mean,
-    const float* __restrict__ rstd, const uint16_t* __restrict__ emb, uint16_t* __restrict__ dx,
-    int64_t S) {
-  static_assert(kBlockThreads == kThreads, "one block size for every role");
-  // one LDS buffer, laid out per role
-  constexpr size_t kRed = sizeof(double) * kSlots * NB * kTileCols;
-  constexpr size_t kDe = sizeof(float) * NB * kRowsPerPart;
-  constexpr size_t kMod = sizeof(float4) * (kD / 4);
-  __shared__ __align__(16) unsigned char smem[(kRed + kDe) > kMod ? (kRed + kDe) : kMod];
-  auto* red = reinterpret_cast<double (*)[NB][kTileCols]>(smem);
-  auto* de_lds = reinterpret_cast<float (*)[kRowsPerPart]>(smem + kRed);
-  auto* m_lds = reinterpret_cast<float4*>(smem);
+__global__ __launch_bounds__(kThreads) void proj_bwd_small_kernel(
+    const float* __restrict__ d_emb, const uint16_t* __restrict__ temb, const uint16_t* __restrict__ W,
+    uint16_t* __restrict__ dW, uint16_t* __restrict__ db, uint16_t* __restrict__ dtemb) {
+  __shared__ __align__(16) unsigned char smem[ProjBwdShared<NB>::kBytes];
   const int blk = blockIdx.x;
-  if (blk < kProjTiles) {
-    da_tile<NB>(d_emb, W, part, blk % kProjBwdParts, blk / kProjBwdParts, de_lds, red);
-  } else if (blk < 2 * kProjTiles) {
-    const int t = blk - kProjTiles;
-    dw_tile<NB>(d_emb, temb, dW, t % kProjBwdParts, t / kProjBwdParts, de_lds);
+  if (blk < kDaBlocks) {
+    da_block<NB>(d_emb, W, temb, dtemb, blk, 0, NB, reinterpret_cast<double*>(smem));
   } else {
-    const int64_t groups = (S + 3) / 4;
-    const int64_t i = blk - 2 * kProjTiles;
-    const int64_t b = i / groups;
-    const int64_t s = (i % groups) * 4 + (threadIdx.x >> 6);
-    row_pass(g, x, mean, rstd, emb, dx, b, s, S, m_lds);
+    const int t = blk - kDaBlocks;
+    dw_tile<NB>(d_emb, temb, dW, db, t % kDwParts, t / kDwParts,
+                reinterpret_cast<float (*)[kRowsPerPart]>(smem));
   }
 }
 
@@ -413,10 +462,11 @@ constexpr int kDwRows = 4;
 constexpr int kDwThreads = kChunks;     // 384: one 16-byte chunk of a row each
 constexpr int kDwBatch = 8;
 
+// dW rows j0 .. j0 + 3 over all samples (in order, 8 at a time), and db.
 __global__ __launch_bounds__(kDwThreads) void proj_bwd_dw_kernel(const float* __restrict__ d_emb,
                                                                  const uint16_t* __restrict__ a,
                                                                  uint16_t* __restrict__ dW,
-                                                                 int64_t B) {
+                                                                 uint16_t* __restrict__ db, int64_t B) {
   const int t = threadIdx.x;
   const int j0 = blockIdx.x * kDwRows;
   double acc[kDwRows][8];
@@ -450,83 +500,27 @@ __global__ __launch_bounds__(kDwThreads) void proj_bwd_dw_kernel(const float* __
     for (int e = 0; e < 8; ++e) o[e] = static_cast<float>(acc[r][e]);
     st16(dW + static_cast<int64_t>(j0 + r) * kD + t * 8, pack8(o));
   }
+  if (t < kDwRows) {
+    double s = 0.0;
+    for (int64_t b = 0; b < B; ++b) s += static_cast<double>(d_emb[b * kN + j0 + t]);
+    db[j0 + t] = f32_to_bf16(static_cast<float>(s));
+  }
 }
 
-__global__ __launch_bounds__(kBlockThreads) void proj_bwd_da_kernel(const float* __restrict__ d_emb,
-                                                                    const uint16_t* __restrict__ W,
-                                                                    double* __restrict__ part,
-                                                                    int64_t B) {
-  __shared__ double red[kSlots][kBatchChunk][kTileCols];   // 64 KB
-  const int p = blockIdx.x;
-  const int kb = blockIdx.y;
-  const int64_t b0 = static_cast<int64_t>(blockIdx.z) * kBatchChunk;
+// da and dtemb, 4 samples per blockIdx.y
+__global__ __launch_bounds__(kThreads) void proj_bwd_da_kernel(const float* __restrict__ d_emb,
+                                                               const uint16_t* __restrict__ W,
+                                                               const uint16_t* __restrict__ temb,
+                                                               uint16_t* __restrict__ dtemb, int64_t B) {
+  __shared__ __align__(16) double red[kDaSlots * kBatchChunk * kDaCols];   // 64 KB
+  const int64_t b0 = static_cast<int64_t>(blockIdx.y) * kBatchChunk;
   const int nb = static_cast<int>((B - b0) < kBatchChunk ? (B - b0) : kBatchChunk);
-  const int ct = threadIdx.x % kColThreads;
-  const int slot = threadIdx.x / kColThreads;
-  const int col = kb * kTileCols + ct * 8;
-  const int jbase = p * kRowsPerPart;
-
-  uint4 wv[kSteps];
-#pragma unroll
-  for (int i = 0; i < kSteps; ++i)
-    wv[i] = ld16(W + static_cast<int64_t>(jbase + slot + kSlots * i) * kD + col);
-  double acc[kBatchChunk][8];
-#pragma unroll
-  for (int bb = 0; bb < kBatchChunk; ++bb)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[bb][e] = 0.0;
-#pragma unroll
-  for (int i = 0; i < kSteps; ++i) {
-    const int j = jbase + slot + kSlots * i;
-    float w[8];
-    unpack8(wv[i], w);
-#pragma unroll
-    for (int bb = 0; bb < kBatchChunk; ++bb) {
-      if (bb < nb) {
-        const float d = d_emb[(b0 + bb) * kN + j];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[bb][e] += static_cast<double>(d * w[e]);
-      }
-    }
-  }
-#pragma unroll
-  for (int bb = 0; bb < kBatchChunk; ++bb)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) red[slot][bb][ct * 8 + e] = acc[bb][e];
-  __syncthreads();
-  for (int o = threadIdx.x; o < kBatchChunk * kTileCols; o += kBlockThreads) {
-    const int bb = o / kTileCols, c = o % kTileCols;
-    if (bb < nb)
-      part[(static_cast<int64_t>(p) * B + b0 + bb) * kD + kb * kTileCols + c] = slot_tree(red, bb, c);
-  }
-}
-
-// ---- dtemb and db -------------------------------------------------------------
-__global__ __launch_bounds__(256) void proj_bwd_final_kernel(const double* __restrict__ part,
-                                                             const float* __restrict__ d_emb,
-                                                             const uint16_t* __restrict__ temb,
-                                                             uint16_t* __restrict__ dtemb,
-                                                             uint16_t* __restrict__ db, int64_t B) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i < B * kD) {
-    double v[kProjBwdParts];
-#pragma unroll
-    for (int p = 0; p < kProjBwdParts; ++p) v[p] = part[static_cast<int64_t>(p) * B * kD + i];
-    double s = 0.0;
-#pragma unroll
-    for (int p = 0; p < kProjBwdParts; ++p) s += v[p];
-    dtemb[i] = f32_to_bf16(static_cast<float>(s) * dsilu_f32(bf16_to_f32(temb[i])));
-  }
-  if (i < kN) {
-    double s = 0.0;
-    for (int64_t b = 0; b < B; ++b) s += static_cast<double>(d_emb[b * kN + i]);
-    db[i] = f32_to_bf16(static_cast<float>(s));
-  }
+  da_block<kBatchChunk>(d_emb, W, temb, dtemb, blockIdx.x, b0, nb, red);
 }
 
 template <int kRole>
 hipError_t launch_role(const uint16_t* g, const uint16_t* x, const float* mean, const float* rstd,
-                       const uint16_t* emb, uint16_t* dx, float* part_s, float* part_c, int64_t B,
+                       const uint16_t* emb, uint16_t* dx, float* part, int64_t B,
                        int64_t S, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   constexpr int bpt = kRole == kBoth ? kBlocksPerTile : (kRole == kRowsOnly ? kRowBlocks : kColBlocks);
   const int64_t T0 = (S + kTile - 1) / kTile;
@@ -535,10 +529,10 @@ hipError_t launch_role(const uint16_t* g, const uint16_t* x, const float* mean, 
   if (e0 != nullptr && e1 != nullptr) {
     // events carried by the dispatch itself: no extra barrier in the stream
     hipExtLaunchKernelGGL(norm_mod_bwd_kernel<kRole>, grid, dim3(kThreads), 0, s, e0, e1, 0, g, x, mean,
-                          rstd, emb, dx, part_s, part_c, B, S, T0);
+                          rstd, emb, dx, part, B, S, T0);
   } else {
     hipLaunchKernelGGL(norm_mod_bwd_kernel<kRole>, grid, dim3(kThreads), 0, s, g, x, mean, rstd, emb, dx,
-                       part_s, part_c, B, S, T0);
+                       part, B, S, T0);
   }
   return hipGetLastError();
 }
@@ -546,60 +540,52 @@ hipError_t launch_role(const uint16_t* g, const uint16_t* x, const float* mean, 
 }  // namespace
 
 hipError_t launch_norm_mod_bwd(const uint16_t* g, const uint16_t* x, const float* mean,
-                               const float* rstd, const uint16_t* emb, uint16_t* dx, float* part_s,
-                               float* part_c, int64_t B, int64_t S, hipStream_t s, hipEvent_t e0,
+                               const float* rstd, const uint16_t* emb, uint16_t* dx, float* part,
+                               int64_t B, int64_t S, hipStream_t s, hipEvent_t e0,
                                hipEvent_t e1) {
   static_assert(kD % kColBlockCols == 0, "column blocks must tile D");
-  return launch_role<kBoth>(g, x, mean, rstd, emb, dx, part_s, part_c, B, S, s, e0, e1);
+  return launch_role<kBoth>(g, x, mean, rstd, emb, dx, part, B, S, s, e0, e1);
 }
 
 hipError_t launch_norm_mod_bwd_dx(const uint16_t* g, const uint16_t* x, const float* mean,
                                   const float* rstd, const uint16_t* emb, uint16_t* dx, int64_t B,
                                   int64_t S, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  return launch_role<kRowsOnly>(g, x, mean, rstd, emb, dx, nullptr, nullptr, B, S, s, e0, e1);
+  return launch_role<kRowsOnly>(g, x, mean, rstd, emb, dx, nullptr, B, S, s, e0, e1);
 }
 
 hipError_t launch_norm_mod_bwd_tiles(const uint16_t* g, const uint16_t* x, const float* mean,
-                                     const float* rstd, float* part_s, float* part_c, int64_t B,
+                                     const float* rstd, float* part, int64_t B,
                                      int64_t S, hipStream_t s) {
-  return launch_role<kColsOnly>(g, x, mean, rstd, nullptr, nullptr, part_s, part_c, B, S, s, nullptr,
+  return launch_role<kColsOnly>(g, x, mean, rstd, nullptr, nullptr, part, B, S, s, nullptr,
                                 nullptr);
 }
 
 int proj_bwd_fused_max_batch() { return kBatchChunk; }
 
 hipError_t launch_proj_bwd_fused(const float* d_emb, const uint16_t* temb, const uint16_t* W,
-                                 uint16_t* dW, double* part, int64_t B, hipStream_t s) {
-  const dim3 grid(kProjBwdParts, kD / kTileCols, 2), block(kBlockThreads);
+                                 uint16_t* dW, uint16_t* db, uint16_t* dtemb, int64_t B, hipStream_t s) {
+  const dim3 grid(kDaBlocks + kDwTiles), block(kThreads);
   switch (B) {
-    case 1: hipLaunchKernelGGL(proj_bwd_small_kernel<1>, grid, block, 0, s, d_emb, temb, W, dW, part); break;
-    case 2: hipLaunchKernelGGL(proj_bwd_small_kernel<2>, grid, block, 0, s, d_emb, temb, W, dW, part); break;
-    case 3: hipLaunchKernelGGL(proj_bwd_small_kernel<3>, grid, block, 0, s, d_emb, temb, W, dW, part); break;
-    case 4: hipLaunchKernelGGL(proj_bwd_small_kernel<4>, grid, block, 0, s, d_emb, temb, W, dW, part); break;
+    case 1: hipLaunchKernelGGL(proj_bwd_small_kernel<1>, grid, block, 0, s, d_emb, temb, W, dW, db, dtemb); break;
+    case 2: hipLaunchKernelGGL(proj_bwd_small_kernel<2>, grid, block, 0, s, d_emb, temb, W, dW, db, dtemb); break;
+    case 3: hipLaunchKernelGGL(proj_bwd_small_kernel<3>, grid, block, 0, s, d_emb, temb, W, dW, db, dtemb); break;
+    case 4: hipLaunchKernelGGL(proj_bwd_small_kernel<4>, grid, block, 0, s, d_emb, temb, W, dW, db, dtemb); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_proj_bwd_dw(const float* d_emb, const uint16_t* a, uint16_t* dW, int64_t B,
+hipError_t launch_proj_bwd_dw(const float* d_emb, const uint16_t* a, uint16_t* dW, uint16_t* db, int64_t B,
                               hipStream_t s) {
-  hipLaunchKernelGGL(proj_bwd_dw_kernel, dim3(kN / kDwRows), dim3(kDwThreads), 0, s, d_emb, a, dW, B);
+  hipLaunchKernelGGL(proj_bwd_dw_kernel, dim3(kN / kDwRows), dim3(kDwThreads), 0, s, d_emb, a, dW, db, B);
   return hipGetLastError();
 }
 
-hipError_t launch_proj_bwd_da(const float* d_emb, const uint16_t* W, double* part, int64_t B,
-                              hipStream_t s) {
+hipError_t launch_proj_bwd_da(const float* d_emb, const uint16_t* W, const uint16_t* temb, uint16_t* dtemb,
+                              int64_t B, hipStream_t s) {
   const int64_t bz = (B + kBatchChunk - 1) / kBatchChunk;
-  hipLaunchKernelGGL(proj_bwd_da_kernel, dim3(kProjBwdParts, kD / kTileCols, static_cast<unsigned>(bz)),
-                     dim3(kBlockThreads), 0, s, d_emb, W, part, B);
-  return hipGetLastError();
-}
-
-hipError_t launch_proj_bwd_final(const double* part, const float* d_emb, const uint16_t* temb,
-                                 uint16_t* dtemb, uint16_t* db, int64_t B, hipStream_t s) {
-  const int64_t n = B * kD > kN ? B * kD : kN;
-  hipLaunchKernelGGL(proj_bwd_final_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
-                     s, part, d_emb, temb, dtemb, db, B);
+  hipLaunchKernelGGL(proj_bwd_da_kernel, dim3(kDaBlocks, static_cast<unsigned>(bz)), dim3(kThreads), 0, s,
+                     d_emb, W, temb, dtemb, B);
   return hipGetLastError();
 }
 
@@ -607,30 +593,6 @@ hipError_t launch_silu(const uint16_t* temb, uint16_t* a, int64_t n, hipStream_t
   const int64_t blocks = (n + 255) / 256;
   hipLaunchKernelGGL(silu_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, temb, a, n);
   return hipGetLastError();
-}
-
-hipError_t launch_bwd_stage2(const float* d_emb, const uint16_t* temb, const uint16_t* W, uint16_t* dW,
-                             double* part, const uint16_t* g, const uint16_t* x, const float* mean,
-                             const float* rstd, const uint16_t* emb, uint16_t* dx, int64_t B, int64_t S,
-                             hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  const int64_t blocks = 2 * kProjTiles + B * ((S + 3) / 4);
-  const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
-  auto go = [&](auto kern) {
-    if (e0 != nullptr && e1 != nullptr) {
-      hipExtLaunchKernelGGL(kern, grid, block, 0, s, e0, e1, 0, d_emb, temb, W, dW, part, g, x, mean, rstd,
-                            emb, dx, S);
-    } else {
-      hipLaunchKernelGGL(kern, grid, block, 0, s, d_emb, temb, W, dW, part, g, x, mean, rstd, emb, dx, S);
-    }
-    return hipGetLastError();
-  };
-  switch (B) {
-    case 1: return go(bwd_stage2_kernel<1>);
-    case 2: return go(bwd_stage2_kernel<2>);
-    case 3: return go(bwd_stage2_kernel<3>);
-    case 4: return go(bwd_stage2_kernel<4>);
-    default: return hipErrorInvalidValue;
-  }
 }
 
 }  // namespace adaln

@@ -69,6 +69,43 @@ __device__ __forceinline__ void st16_nt(uint16_t* p, const uint4& v) {
   __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
 }
 
+// A byte range read through a raw buffer resource.  The base is uniform; a
+// load takes a per-lane byte offset in a VGPR and a uniform one in an SGPR,
+// so a run of loads at fixed strides needs no per-load address arithmetic.
+// Callers keep every load inside [0, bytes): nothing relies on the range
+// check.  The third descriptor word is the gfx9-family raw-buffer format.
+struct Buffer {
+  __amdgpu_buffer_rsrc_t rsrc;
+  __device__ __forceinline__ Buffer(const void* base, uint32_t bytes)
+      : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                               0x00020000)) {}
+  __device__ __forceinline__ uint32_t u32(uint32_t lane_off, uint32_t uni_off) const {
+    return __builtin_amdgcn_raw_buffer_load_b32(rsrc, lane_off, uni_off, 0);
+  }
+  __device__ __forceinline__ float f32(uint32_t lane_off, uint32_t uni_off) const {
+    return __uint_as_float(u32(lane_off, uni_off));
+  }
+  __device__ __forceinline__ uint4 u128(uint32_t lane_off, uint32_t uni_off) const {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_off, uni_off, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  }
+};
+
+// Level-0 pairs of the token tree in memory: columns in groups of 64; per
+// (sample, group, tile) 64 sums s followed by their 64 corrections c, tiles
+// of a group consecutive.  The fold then reads each node's 32 children as one
+// contiguous 16 KB run.  pair_index gives the index of s; c is 64 later.
+constexpr int kPairGroup = 64;
+__device__ __forceinline__ int64_t pair_index(int64_t b, int64_t groups, int64_t T0, int64_t tile,
+                                              int64_t col) {
+  return ((b * groups + col / kPairGroup) * T0 + tile) * (2 * kPairGroup) + col % kPairGroup;
+}
+
+__device__ __forceinline__ void st8_nt(float* p, float a, float b) {
+  f32x2_t w = {a, b};
+  __builtin_nontemporal_store(w, reinterpret_cast<f32x2_t*>(p));
+}
+
 // Sum over the 64 lanes of a wave as a pairwise tree over lane index
 // (xor 1, 2, 4, ..., 32).  IEEE addition commutes, so every lane ends with
 // the same bits; the tree depends only on which value sits in which lane.

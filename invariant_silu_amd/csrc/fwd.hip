@@ -254,15 +254,15 @@ __global__ __launch_bounds__(kThreads) void norm_mod_fwd_kernel(
   const int64_t b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int64_t s = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-  const bool valid = s < S;
-  const int64_t row = b * S + (valid ? s : 0);
+  // a wave past the end redoes row S - 1 (same bytes as its owner): no branch
+  // after the barrier, so the row loads stay ahead of it
+  const int64_t row = b * S + (s < S ? s : S - 1);
   ModRegs mr;
   load_mod(emb, b, mr);
   uint4 xv[kLaneChunks];
   load_row(x, row, lane, xv);
   store_mod(mr, m_lds, sh_lds);
   __syncthreads();
-  if (!valid) return;   // whole wave
   float mu, rs;
   row_stats(xv, eps, mu, rs);
   modulate(xv, mu, rs, m_lds, sh_lds, out + row * kD, lane);
@@ -306,8 +306,7 @@ __global__ __launch_bounds__(kThreads) void norm_modulate_kernel(
   const int64_t b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int64_t s = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-  const bool valid = s < S;
-  const int64_t row = b * S + (valid ? s : 0);
+  const int64_t row = b * S + (s < S ? s : S - 1);   // as in norm_mod_fwd_kernel
   ModRegs mr;
   load_mod(emb, b, mr);
   const float mu = mean[row];
@@ -316,7 +315,6 @@ __global__ __launch_bounds__(kThreads) void norm_modulate_kernel(
   load_row(x, row, lane, xv);
   store_mod(mr, m_lds, sh_lds);
   __syncthreads();
-  if (!valid) return;   // whole wave
   modulate(xv, mu, rs, m_lds, sh_lds, out + row * kD, lane);
 }
 

@@ -7,47 +7,37 @@
 
 namespace adaln {
 
-// Number of fp64 da partials along the 6144 projection rows (fixed: the
-// summation order of dtemb depends on it, never on the batch size).
-constexpr int kProjBwdParts = 32;
-
 hipError_t launch_silu(const uint16_t* temb, uint16_t* a, int64_t n, hipStream_t s);
 hipError_t launch_fwd(const uint16_t* temb, const uint16_t* W, const uint16_t* bias,
                       const uint16_t* x, uint16_t* emb, uint16_t* out, float* mean, float* rstd,
                       int64_t B, int64_t S, float eps, hipStream_t s);
-hipError_t launch_bwd_stage2(const float* d_emb, const uint16_t* temb, const uint16_t* W, uint16_t* dW,
-                             double* part, const uint16_t* g, const uint16_t* x, const float* mean,
-                             const float* rstd, const uint16_t* emb, uint16_t* dx, int64_t B, int64_t S,
-                             hipStream_t s, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 hipError_t launch_proj_fwd(const uint16_t* temb, const uint16_t* W, const uint16_t* bias,
                            uint16_t* emb, int64_t B, hipStream_t s);
 hipError_t launch_norm_mod_fwd(const uint16_t* x, const uint16_t* emb, uint16_t* out,
                                float* mean, float* rstd, int64_t B, int64_t S, float eps,
                                hipStream_t s);
 hipError_t launch_norm_mod_bwd(const uint16_t* g, const uint16_t* x, const float* mean,
-                               const float* rstd, const uint16_t* emb, uint16_t* dx, float* part_s,
-                               float* part_c, int64_t B, int64_t S, hipStream_t s,
+                               const float* rstd, const uint16_t* emb, uint16_t* dx, float* part,
+                               int64_t B, int64_t S, hipStream_t s,
                                hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 hipError_t launch_norm_mod_bwd_dx(const uint16_t* g, const uint16_t* x, const float* mean,
                                   const float* rstd, const uint16_t* emb, uint16_t* dx, int64_t B,
                                   int64_t S, hipStream_t s, hipEvent_t ev_start = nullptr,
                                   hipEvent_t ev_stop = nullptr);
 hipError_t launch_norm_mod_bwd_tiles(const uint16_t* g, const uint16_t* x, const float* mean,
-                                     const float* rstd, float* part_s, float* part_c, int64_t B,
+                                     const float* rstd, float* part, int64_t B,
                                      int64_t S, hipStream_t s);
-hipError_t launch_token_level0(const float* x, float* part_s, float* part_c, int64_t B,
+hipError_t launch_token_level0(const float* x, float* part, int64_t B,
                                int64_t S, int64_t H, hipStream_t s);
-hipError_t launch_tree_fold(const float* part_s, const float* part_c, float* out, int64_t B,
+hipError_t launch_tree_fold(const float* part, float* out, int64_t B,
                             int64_t T0, int64_t H, hipStream_t s);
 int proj_bwd_fused_max_batch();
 hipError_t launch_proj_bwd_fused(const float* d_emb, const uint16_t* temb, const uint16_t* W,
-                                 uint16_t* dW, double* part, int64_t B, hipStream_t s);
-hipError_t launch_proj_bwd_dw(const float* d_emb, const uint16_t* a, uint16_t* dW, int64_t B,
-                              hipStream_t s);
-hipError_t launch_proj_bwd_da(const float* d_emb, const uint16_t* W, double* part, int64_t B,
-                              hipStream_t s);
-hipError_t launch_proj_bwd_final(const double* part, const float* d_emb, const uint16_t* temb,
-                                 uint16_t* dtemb, uint16_t* db, int64_t B, hipStream_t s);
+                                 uint16_t* dW, uint16_t* db, uint16_t* dtemb, int64_t B, hipStream_t s);
+hipError_t launch_proj_bwd_dw(const float* d_emb, const uint16_t* a, uint16_t* dW, uint16_t* db,
+                              int64_t B, hipStream_t s);
+hipError_t launch_proj_bwd_da(const float* d_emb, const uint16_t* W, const uint16_t* temb,
+                              uint16_t* dtemb, int64_t B, hipStream_t s);
 hipError_t launch_selftest_probe(const float* in, float* out, uint32_t* bits, int n,
                                  hipStream_t s);
 

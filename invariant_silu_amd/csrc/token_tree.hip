@@ -10,12 +10,15 @@
 // Tiles restart at token 0 of each sample, so a sample's sum is the same bytes
 // whatever the batch size or the sample's position in the batch.
 //
+// Level-0 pairs are stored in groups of 64 columns (pair_index): the 32
+// children of a level-1 node are one contiguous run per group.
+//
 // token_level0_kernel: one thread per (sample, tile, column), for the
 //   stand-alone token_tree_sum (the norm backward computes its own level 0).
-// tree_fold_kernel: one block per (sample, 64 columns); 4 waves compute the
-//   level-1 nodes (4 at a time, one per wave); one wave then streams them
-//   through levels 2.. with per-level running nodes kept in registers, which
-//   is the same arithmetic as building each level in turn.
+// tree_fold_kernel: one block per (sample, 64-column group); its 4 waves
+//   compute the level-1 nodes 4 at a time (one per wave); the first wave then
+//   streams them through levels 2.. with per-level running nodes kept in
+//   registers, which is the same arithmetic as building each level in turn.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -23,13 +26,12 @@ namespace adaln {
 
 namespace {
 
-constexpr int kFoldCols = 64;
+constexpr int kFoldCols = kPairGroup;
 constexpr int kFoldLanes = 4;
 
 __global__ __launch_bounds__(256) void token_level0_kernel(const float* __restrict__ x,
-                                                           float* __restrict__ part_s,
-                                                           float* __restrict__ part_c,
-                                                           int64_t S, int64_t H, int64_t T0) {
+                                                           float* __restrict__ part, int64_t S,
+                                                           int64_t H, int64_t T0) {
   const int64_t col = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t tile = blockIdx.y;
   const int64_t b = blockIdx.z;
@@ -39,25 +41,25 @@ __global__ __launch_bounds__(256) void token_level0_kernel(const float* __restri
   const float* xp = x + (b * S + s0) * H + col;
   float s = 0.0f, c = 0.0f;
   for (int i = 0; i < n; ++i) neumaier_add(s, c, xp[static_cast<int64_t>(i) * H]);
-  part_s[(b * T0 + tile) * H + col] = s;
-  part_c[(b * T0 + tile) * H + col] = c;
+  const int64_t i = pair_index(b, (H + kPairGroup - 1) / kPairGroup, T0, tile, col);
+  part[i] = s;
+  part[i + kPairGroup] = c;
 }
 
 __global__ __launch_bounds__(kFoldCols * kFoldLanes) void tree_fold_kernel(
-    const float* __restrict__ part_s, const float* __restrict__ part_c, float* __restrict__ out,
-    int64_t T0, int64_t H, int levels) {
+    const float* __restrict__ part, float* __restrict__ out, int64_t T0, int64_t H, int levels) {
   __shared__ float lds_s[kFoldLanes][kFoldCols];
   __shared__ float lds_c[kFoldLanes][kFoldCols];
-  const int q = threadIdx.x / kFoldCols;           // node lane (= wave)
+  const int q = threadIdx.x / kFoldCols;           // node lane
   const int cl = threadIdx.x % kFoldCols;
   const int64_t col = static_cast<int64_t>(blockIdx.x) * kFoldCols + cl;
   const bool ok = col < H;
   const int64_t b = blockIdx.y;
-  const float* ps = part_s + b * T0 * H + col;
-  const float* pc = part_c + b * T0 * H + col;
+  // this column's tile t: s at ps[t * 128], c at ps[t * 128 + 64]
+  const float* ps = part + pair_index(b, gridDim.x, T0, 0, col);
 
   if (levels == 0) {                                // one tile: s + c
-    if (q == 0 && ok) out[b * H + col] = ps[0] + pc[0];
+    if (q == 0 && ok) out[b * H + col] = ps[0] + ps[kPairGroup];
     return;
   }
   const int64_t T1 = (T0 + kTile - 1) / kTile;
@@ -95,11 +97,14 @@ __global__ __launch_bounds__(kFoldCols * kFoldLanes) void tree_fold_kernel(
     if (ok && node < T1) {
       const int64_t t0 = node * kTile;
       const int cnt = static_cast<int>((T0 - t0) < kTile ? (T0 - t0) : kTile);
+      // loads of a short last node repeat its last child (always in
+      // bounds, never used), so every load is unconditional
       float vs[kTile], vc[kTile];
 #pragma unroll
       for (int i = 0; i < kTile; ++i) {
-        vs[i] = i < cnt ? ps[(t0 + i) * H] : 0.0f;
-        vc[i] = i < cnt ? pc[(t0 + i) * H] : 0.0f;
+        const int64_t t = t0 + (i < cnt ? i : cnt - 1);
+        vs[i] = ps[t * 2 * kPairGroup];
+        vc[i] = ps[t * 2 * kPairGroup + kPairGroup];
       }
 #pragma unroll
       for (int i = 0; i < kTile; ++i) {
@@ -141,24 +146,24 @@ __global__ __launch_bounds__(kFoldCols * kFoldLanes) void tree_fold_kernel(
 
 }  // namespace
 
-hipError_t launch_token_level0(const float* x, float* part_s, float* part_c, int64_t B, int64_t S,
-                               int64_t H, hipStream_t s) {
+hipError_t launch_token_level0(const float* x, float* part, int64_t B, int64_t S, int64_t H,
+                               hipStream_t s) {
   const int64_t T0 = (S + kTile - 1) / kTile;
   hipLaunchKernelGGL(token_level0_kernel,
                      dim3(static_cast<unsigned>((H + 255) / 256), static_cast<unsigned>(T0),
                           static_cast<unsigned>(B)),
-                     dim3(256), 0, s, x, part_s, part_c, S, H, T0);
+                     dim3(256), 0, s, x, part, S, H, T0);
   return hipGetLastError();
 }
 
-hipError_t launch_tree_fold(const float* part_s, const float* part_c, float* out, int64_t B,
-                            int64_t T0, int64_t H, hipStream_t s) {
+hipError_t launch_tree_fold(const float* part, float* out, int64_t B, int64_t T0, int64_t H,
+                            hipStream_t s) {
   int levels = 0;
   for (int64_t n = T0; n > 1; n = (n + kTile - 1) / kTile) ++levels;
   if (levels > kMaxFoldLevels) return hipErrorInvalidValue;
   hipLaunchKernelGGL(tree_fold_kernel,
                      dim3(static_cast<unsigned>((H + kFoldCols - 1) / kFoldCols), static_cast<unsigned>(B)),
-                     dim3(kFoldCols * kFoldLanes), 0, s, part_s, part_c, out, T0, H, levels);
+                     dim3(kFoldCols * kFoldLanes), 0, s, part, out, T0, H, levels);
   return hipGetLastError();
 }
 

@@ -55,9 +55,9 @@ def test_workspace_sizes(L):
     pad = lambda n: (n + 255) // 256 * 256   # noqa: E731
     for B, S in [(1, 31), (2, 1024), (1, 4096), (64, 1024), (3, 6889)]:
         T0 = math.ceil(S / 32)
-        assert lib.workspace_bytes(lib.OP_NORM_MOD_BWD, B, S, 3072) == 2 * pad(B * T0 * 6144 * 4)
-        assert lib.workspace_bytes(lib.OP_TOKEN_TREE_SUM, B, S, 100) == 2 * pad(B * T0 * 100 * 4)
-        assert lib.workspace_bytes(lib.OP_PROJ_BWD, B, S, 3072) == pad(B * 3072 * 2) + pad(32 * B * 3072 * 8)
+        assert lib.workspace_bytes(lib.OP_NORM_MOD_BWD, B, S, 3072) == pad(B * T0 * 6144 * 8)
+        assert lib.workspace_bytes(lib.OP_TOKEN_TREE_SUM, B, S, 100) == pad(B * T0 * 128 * 8)
+        assert lib.workspace_bytes(lib.OP_PROJ_BWD, B, S, 3072) == pad(B * 3072 * 2)
     assert lib.workspace_bytes(lib.OP_NORM_MOD_BWD, 1, 10, 1024) == 0
     assert lib.workspace_bytes(99, 1, 10, 3072) == 0
     assert lib.workspace_bytes(lib.OP_PROJ_BWD, 0, 1, 3072) == 0
