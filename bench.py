@@ -187,6 +187,23 @@ def main() -> int:
     k_bytes = dominant_kernel_bytes(B, S)
     achieved = k_bytes / (k_mean_ms / 1e3) / 1e9
 
+    # achievable-bandwidth ceiling in the same run: a plain device copy moving
+    # the step's algorithmic bytes (half read, half written), rotating over
+    # three buffer pairs so that, like the step, it is not served from MALL
+    cn = (step_bytes // 2 + 255) // 256 * 256
+    pairs = [(torch.empty(cn, dtype=torch.uint8, device=dev).fill_(1),
+              torch.empty(cn, dtype=torch.uint8, device=dev)) for _ in range(3)]
+    for i in range(3):
+        pairs[i][1].copy_(pairs[i][0])
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(30):
+        pairs[i % 3][1].copy_(pairs[i % 3][0])
+    ev1.record()
+    ev1.synchronize()
+    copy_gbps = 2 * cn * 30 / (ev0.elapsed_time(ev1) / 1e3) / 1e9
+    del pairs
+
     if args.copy_calib:
         n = 512 << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -213,7 +230,9 @@ def main() -> int:
                    "buffer_sets": nsets, "step_algorithmic_bytes": step_bytes,
                    "host_enqueue_ms_per_step": round((t_enq - t0) * 1e3 / args.steps, 5),
                    "step_gbps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
-                   "step_frac_of_peak": round(step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)},
+                   "step_frac_of_peak": round(step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+                   "copy_ceiling_gbps": round(copy_gbps, 1),
+                   "step_frac_of_copy_ceiling": round(step_bytes / (ms_per_step / 1e3) / 1e9 / copy_gbps, 4)},
         "roofline": {"bound": "hbm", "kernel": "norm_mod_bwd_kernel<0> (dx rows + level-0 token tiles)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": pmc_traffic(),

@@ -92,25 +92,32 @@ __global__ __launch_bounds__(kFoldCols * kFoldLanes) void tree_fold_kernel(
 
   float root_s = 0.0f, root_c = 0.0f;
   for (int64_t n0 = 0; n0 < T1; n0 += kFoldLanes) {
-    const int64_t node = n0 + q;
+    const int64_t node = n0 + q;                    // q is the wave: uniform per wave
     float s = 0.0f, c = 0.0f;
-    if (ok && node < T1) {
+    if (node < T1) {
       const int64_t t0 = node * kTile;
       const int cnt = static_cast<int>((T0 - t0) < kTile ? (T0 - t0) : kTile);
-      // loads of a short last node repeat its last child (always in
-      // bounds, never used), so every load is unconditional
-      float vs[kTile], vc[kTile];
+      if (cnt == kTile) {
+        // a full node: its 32 children are one contiguous 16 KB run; buffer
+        // loads with the lane's column in a VGPR and the child in an SGPR
+        // (lanes past H read the group's unused slots, never stored)
+        const Buffer run(part + pair_index(b, gridDim.x, T0, t0, static_cast<int64_t>(blockIdx.x) * kFoldCols),
+                         kTile * 2 * kPairGroup * 4);
+        float vs[kTile], vc[kTile];
 #pragma unroll
-      for (int i = 0; i < kTile; ++i) {
-        const int64_t t = t0 + (i < cnt ? i : cnt - 1);
-        vs[i] = ps[t * 2 * kPairGroup];
-        vc[i] = ps[t * 2 * kPairGroup + kPairGroup];
-      }
+        for (int i = 0; i < kTile; ++i) {
+          vs[i] = run.f32(cl * 4, i * 2 * kPairGroup * 4);
+          vc[i] = run.f32(cl * 4, i * 2 * kPairGroup * 4 + kPairGroup * 4);
+        }
 #pragma unroll
-      for (int i = 0; i < kTile; ++i) {
-        if (i < cnt) {
+        for (int i = 0; i < kTile; ++i) {
           neumaier_add(s, c, vs[i]);
           c = c + vc[i];
+        }
+      } else {
+        for (int i = 0; i < cnt; ++i) {
+          neumaier_add(s, c, ps[(t0 + i) * 2 * kPairGroup]);
+          c = c + ps[(t0 + i) * 2 * kPairGroup + kPairGroup];
         }
       }
     }
