@@ -9,7 +9,7 @@
 // Device pieces shared by every kernel below, so the standalone entry points
 // and the overlapped stage kernels compute identical bits:
 //
-// proj_block<NB>: 8 rows of W (4 waves x 2 rows) held in registers; lane l
+// proj_block<NB, kOnePass>: 8 rows of W (4 waves x 2 rows) held in registers; lane l
 //   holds the 16-byte chunks l, l+64, ..., l+320 of a row, loaded chunk-major.
 //   The temb loads are issued first; their SiLU (silu8_fast, with the rare
 //   near-tie elements redone by silu_bf16_exact: identical bits to the float64
@@ -50,7 +50,9 @@ struct ProjShared {
   uint4 a[NB * kChunks];
 };
 
-template <int NB>
+// kOnePass: B == NB, a single pass over the samples (the loop bound is a
+// constant, so nothing is kept live for a later pass: ~60 fewer VGPRs).
+template <int NB, bool kOnePass>
 __device__ __forceinline__ void proj_block(const uint16_t* __restrict__ temb,
                                            const uint16_t* __restrict__ W,
                                            const uint16_t* __restrict__ bias,
@@ -108,7 +110,7 @@ __device__ __forceinline__ void proj_block(const uint16_t* __restrict__ temb,
   stage(tz, 0);
 
 #pragma unroll 1
-  for (int64_t b0 = 0; b0 < B; b0 += NB) {
+  for (int64_t b0 = 0; b0 < (kOnePass ? NB : B); b0 += NB) {
     if (b0 > 0) {
       __syncthreads();   // the previous pass is done reading a_lds
       load_temb(tz, b0);
@@ -236,13 +238,13 @@ __device__ __forceinline__ void modulate(const uint4 (&xv)[kLaneChunks], float m
 }
 
 // ------------------------------------------------------------- kernels ----
-template <int NB>
+template <int NB, bool kOnePass>
 __global__ __launch_bounds__(kThreads) void proj_fwd_kernel(const uint16_t* __restrict__ temb,
                                                             const uint16_t* __restrict__ W,
                                                             const uint16_t* __restrict__ bias,
                                                             uint16_t* __restrict__ emb, int64_t B) {
   __shared__ ProjShared<NB> sh;
-  proj_block<NB>(temb, W, bias, emb, B, blockIdx.x, sh.a);
+  proj_block<NB, kOnePass>(temb, W, bias, emb, B, blockIdx.x, sh.a);
 }
 
 // 4 rows of one sample per block (one per wave): statistics and modulation
@@ -273,8 +275,11 @@ __global__ __launch_bounds__(kThreads) void norm_mod_fwd_kernel(
 }
 
 // projection blocks [0, 768), then statistics blocks (4 rows each, rows of
-// all samples in order)
-template <int NB>
+// all samples in order).  The statistics run last on purpose: the block for
+// rows 4i..4i+3 runs on XCD i % 8, and (S a multiple of 4) so does the
+// modulation block for the same rows right after, which then finds x in that
+// XCD's L2 (3.1 MB of x per XCD at S = 4096 against a 4 MB L2).
+template <int NB, bool kOnePass>
 __global__ __launch_bounds__(kThreads) void fwd_stage1_kernel(
     const uint16_t* __restrict__ temb, const uint16_t* __restrict__ W,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ emb, const uint16_t* __restrict__ x,
@@ -282,11 +287,12 @@ __global__ __launch_bounds__(kThreads) void fwd_stage1_kernel(
   __shared__ ProjShared<NB> sh;
   const int blk = blockIdx.x;
   if (blk < kProjBlocks) {
-    proj_block<NB>(temb, W, bias, emb, B, blk, sh.a);
+    proj_block<NB, kOnePass>(temb, W, bias, emb, B, blk, sh.a);
     return;
   }
+  const int64_t idx = blk - kProjBlocks;
   const int lane = threadIdx.x & 63;
-  const int64_t r = static_cast<int64_t>(blk - kProjBlocks) * kWaves + (threadIdx.x >> 6);
+  const int64_t r = idx * kWaves + (threadIdx.x >> 6);
   if (r >= B * S) return;
   uint4 xv[kLaneChunks];
   load_row(x, r, lane, xv);
@@ -318,21 +324,24 @@ __global__ __launch_bounds__(kThreads) void norm_modulate_kernel(
   modulate(xv, mu, rs, m_lds, sh_lds, out + row * kD, lane);
 }
 
+// NB = the largest of 4, 2, 1 that divides B, so every pass is a full one;
+// B == NB takes the single-pass instance.
 template <typename F>
 hipError_t by_batch(int64_t B, F&& f) {
-  if (B % 4 == 0) return f(std::integral_constant<int, 4>{});
-  if (B % 2 == 0) return f(std::integral_constant<int, 2>{});
-  return f(std::integral_constant<int, 1>{});
+  using One = std::true_type;
+  using Many = std::false_type;
+  if (B % 4 == 0) return B == 4 ? f(std::integral_constant<int, 4>{}, One{}) : f(std::integral_constant<int, 4>{}, Many{});
+  if (B % 2 == 0) return B == 2 ? f(std::integral_constant<int, 2>{}, One{}) : f(std::integral_constant<int, 2>{}, Many{});
+  return B == 1 ? f(std::integral_constant<int, 1>{}, One{}) : f(std::integral_constant<int, 1>{}, Many{});
 }
 
 }  // namespace
 
-// NB = the largest of 4, 2, 1 that divides B, so every pass is a full one.
 hipError_t launch_proj_fwd(const uint16_t* temb, const uint16_t* W, const uint16_t* bias,
                            uint16_t* emb, int64_t B, hipStream_t s) {
-  return by_batch(B, [&](auto nb) {
-    hipLaunchKernelGGL(proj_fwd_kernel<decltype(nb)::value>, dim3(kProjBlocks), dim3(kThreads), 0, s,
-                       temb, W, bias, emb, B);
+  return by_batch(B, [&](auto nb, auto one) {
+    hipLaunchKernelGGL((proj_fwd_kernel<decltype(nb)::value, decltype(one)::value>), dim3(kProjBlocks),
+                       dim3(kThreads), 0, s, temb, W, bias, emb, B);
     return hipGetLastError();
   });
 }
@@ -349,8 +358,8 @@ hipError_t launch_fwd(const uint16_t* temb, const uint16_t* W, const uint16_t* b
                       const uint16_t* x, uint16_t* emb, uint16_t* out, float* mean, float* rstd,
                       int64_t B, int64_t S, float eps, hipStream_t s) {
   const int64_t stat_blocks = (B * S + kWaves - 1) / kWaves;
-  hipError_t e = by_batch(B, [&](auto nb) {
-    hipLaunchKernelGGL(fwd_stage1_kernel<decltype(nb)::value>,
+  hipError_t e = by_batch(B, [&](auto nb, auto one) {
+    hipLaunchKernelGGL((fwd_stage1_kernel<decltype(nb)::value, decltype(one)::value>),
                        dim3(static_cast<unsigned>(kProjBlocks + stat_blocks)), dim3(kThreads), 0, s,
                        temb, W, bias, emb, x, mean, rstd, B, S, eps);
     return hipGetLastError();
