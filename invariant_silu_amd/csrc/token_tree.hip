@@ -50,7 +50,9 @@ __global__ __launch_bounds__(kFoldCols * kFoldLanes) void tree_fold_kernel(
     const float* __restrict__ part, float* __restrict__ out, int64_t T0, int64_t H, int levels) {
   __shared__ float lds_s[kFoldLanes][kFoldCols];
   __shared__ float lds_c[kFoldLanes][kFoldCols];
-  const int q = threadIdx.x / kFoldCols;           // node lane
+  // node lane = wave index; readfirstlane tells the compiler it is uniform,
+  // so the buffer descriptors built from it live in SGPRs (no per-load loop)
+  const int q = __builtin_amdgcn_readfirstlane(threadIdx.x / kFoldCols);
   const int cl = threadIdx.x % kFoldCols;
   const int64_t col = static_cast<int64_t>(blockIdx.x) * kFoldCols + cl;
   const bool ok = col < H;
