@@ -458,53 +458,75 @@ __global__ __launch_bounds__(256) void silu_kernel(const uint16_t* __restrict__ 
 }
 
 // ---- B > 4 ------------------------------------------------------------------
-constexpr int kDwRows = 4;
-constexpr int kDwThreads = kChunks;     // 384: one 16-byte chunk of a row each
-constexpr int kDwBatch = 8;
+// dW tile of 32 rows x 256 columns per block; samples staged through LDS 64 at
+// a time (a: 32 KB, d_emb: 8 KB).  Thread (ct, rg) owns rows 4 rg .. 4 rg + 3
+// and columns 8 ct .. 8 ct + 7: 32 fp64 sums, samples in ascending order.
+// Blocks of column block 0 also sum db for their rows.
+constexpr int kDwBRows = 32;
+constexpr int kDwBCols = 256;
+constexpr int kDwBSamples = 64;
+constexpr int kDwBLoads = kDwBSamples * (kDwBCols / 8) / kThreads;   // 8 chunk loads per thread
+static_assert(kDwBSamples * kDwBRows / kThreads == kDwBLoads, "staging layout");
 
-// dW rows j0 .. j0 + 3 over all samples (in order, 8 at a time), and db.
-__global__ __launch_bounds__(kDwThreads) void proj_bwd_dw_kernel(const float* __restrict__ d_emb,
-                                                                 const uint16_t* __restrict__ a,
-                                                                 uint16_t* __restrict__ dW,
-                                                                 uint16_t* __restrict__ db, int64_t B) {
-  const int t = threadIdx.x;
-  const int j0 = blockIdx.x * kDwRows;
-  double acc[kDwRows][8];
+__global__ __launch_bounds__(kThreads) void proj_bwd_dw_kernel(const float* __restrict__ d_emb,
+                                                               const uint16_t* __restrict__ a,
+                                                               uint16_t* __restrict__ dW,
+                                                               uint16_t* __restrict__ db, int64_t B) {
+  __shared__ uint4 a_lds[kDwBSamples][kDwBCols / 8];   // 32 KB
+  __shared__ __align__(16) float d_lds[kDwBSamples][kDwBRows];   // 8 KB
+  const int ct = threadIdx.x % (kDwBCols / 8);
+  const int rg = threadIdx.x / (kDwBCols / 8);
+  const int j0 = blockIdx.x * kDwBRows;
+  const int k0 = blockIdx.y * kDwBCols;
+  double acc[4][8];
 #pragma unroll
-  for (int r = 0; r < kDwRows; ++r)
+  for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[r][e] = 0.0;
-
-  for (int64_t b0 = 0; b0 < B; b0 += kDwBatch) {
-    const int nb = static_cast<int>((B - b0) < kDwBatch ? (B - b0) : kDwBatch);
-    float av[kDwBatch][8];
+  double dbs = 0.0;
+  for (int64_t c0 = 0; c0 < B; c0 += kDwBSamples) {
+    const int nb = static_cast<int>((B - c0) < kDwBSamples ? (B - c0) : kDwBSamples);
+    // unconditional loads (slots past nb repeat sample nb - 1 and are unused)
+    uint4 av_r[kDwBLoads];
+    float d_r[kDwBLoads];
 #pragma unroll
-    for (int bb = 0; bb < kDwBatch; ++bb)
-      if (bb < nb) unpack8(ld16(a + (b0 + bb) * kD + t * 8), av[bb]);
+    for (int u = 0; u < kDwBLoads; ++u) {
+      const int idx = threadIdx.x + kThreads * u;
+      const int sa = idx / (kDwBCols / 8) < nb ? idx / (kDwBCols / 8) : nb - 1;
+      av_r[u] = ld16(a + (c0 + sa) * kD + k0 + (idx % (kDwBCols / 8)) * 8);
+      const int sd = idx / kDwBRows < nb ? idx / kDwBRows : nb - 1;
+      d_r[u] = d_emb[(c0 + sd) * kN + j0 + idx % kDwBRows];
+    }
+    __syncthreads();   // the previous chunk is consumed
 #pragma unroll
-    for (int bb = 0; bb < kDwBatch; ++bb) {
-      if (bb < nb) {
+    for (int u = 0; u < kDwBLoads; ++u) {
+      const int idx = threadIdx.x + kThreads * u;
+      a_lds[idx / (kDwBCols / 8)][idx % (kDwBCols / 8)] = av_r[u];
+      d_lds[idx / kDwBRows][idx % kDwBRows] = d_r[u];
+    }
+    __syncthreads();
+    if (blockIdx.y == 0 && threadIdx.x < kDwBRows)
+      for (int b = 0; b < nb; ++b) dbs += static_cast<double>(d_lds[b][threadIdx.x]);
+#pragma unroll 2
+    for (int b = 0; b < nb; ++b) {
+      float av[8];
+      unpack8(a_lds[b][ct], av);
+      const float4 d4 = *reinterpret_cast<const float4*>(&d_lds[b][rg * 4]);
+      const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-        for (int r = 0; r < kDwRows; ++r) {
-          const float d = d_emb[(b0 + bb) * kN + j0 + r];
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[r][e] += static_cast<double>(d * av[bb][e]);
-        }
-      }
+        for (int e = 0; e < 8; ++e) acc[r][e] += static_cast<double>(dd[r] * av[e]);
     }
   }
 #pragma unroll
-  for (int r = 0; r < kDwRows; ++r) {
+  for (int r = 0; r < 4; ++r) {
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = static_cast<float>(acc[r][e]);
-    st16(dW + static_cast<int64_t>(j0 + r) * kD + t * 8, pack8(o));
+    st16_nt(dW + static_cast<int64_t>(j0 + rg * 4 + r) * kD + k0 + ct * 8, pack8(o));
   }
-  if (t < kDwRows) {
-    double s = 0.0;
-    for (int64_t b = 0; b < B; ++b) s += static_cast<double>(d_emb[b * kN + j0 + t]);
-    db[j0 + t] = f32_to_bf16(static_cast<float>(s));
-  }
+  if (blockIdx.y == 0 && threadIdx.x < kDwBRows) db[j0 + threadIdx.x] = f32_to_bf16(static_cast<float>(dbs));
 }
 
 // da and dtemb, 4 samples per blockIdx.y
@@ -577,7 +599,8 @@ hipError_t launch_proj_bwd_fused(const float* d_emb, const uint16_t* temb, const
 
 hipError_t launch_proj_bwd_dw(const float* d_emb, const uint16_t* a, uint16_t* dW, uint16_t* db, int64_t B,
                               hipStream_t s) {
-  hipLaunchKernelGGL(proj_bwd_dw_kernel, dim3(kN / kDwRows), dim3(kDwThreads), 0, s, d_emb, a, dW, db, B);
+  hipLaunchKernelGGL(proj_bwd_dw_kernel, dim3(kN / kDwBRows, kD / kDwBCols), dim3(kThreads), 0, s, d_emb, a,
+                     dW, db, B);
   return hipGetLastError();
 }
 
