@@ -1,37 +1,20 @@
-// Backward of the AdaLN final modulation (RL-Kernel pull request 538, "What";
-// token sums per the review-thread fix of token_sum.cu; SiLU VJP per the
-// review thread).
-//
-// LayerNorm + modulation, per row r = (b, s), with m = bf16(1 + scale) and n
-// recomputed exactly as in the forward from the saved mean / rstd:
-//   gy    = g * m                            (exact: bf16 x bf16)
-//   alpha = fl32(sum_d gy) / D,  beta = fl32(sum_d gy * n) / D
-//   dx    = bf16(rstd * ((gy - alpha) - n * beta))
-//   (fp64 lane partials, chunks and columns in order, then wave_sum_f64)
-// and the level-0 pairs of the token tree, per (b, 32-token tile, column):
-// Neumaier (s, c) of g (-> d_shift) and of g * n (-> d_scale), tokens in
-// ascending order.  Levels >= 1 are folded by tree_fold_kernel.
-//
-// Projection, from the fp32 d_emb = (d_scale | d_shift):
+// Projection backward of the AdaLN final modulation (RL-Kernel pull request
+// 538, "What"; SiLU VJP per the review thread), from the fp32
+// d_emb = (d_scale | d_shift):
 //   dW[j,k]  = bf16(fl32(sum_b d_emb[b,j] * a[b,k]))      (fp32 products)
 //   db[j]    = bf16(fl32(sum_b d_emb[b,j]))
 //   da[b,k]  = fl32(sum_j d_emb[b,j] * W[j,k])             (fp32 products)
 //   dtemb    = bf16(da * silu'(temb))
 // Sums accumulate fp32 products in fp64 in fixed orders: samples ascending
 // for dW and db; for da, 128 row slots (slot t: rows t, t + 128, ... in
-// order) added as a pairwise tree.
-//
-// Device pieces are shared by every kernel, so every entry point computes
-// identical bits, and no order depends on the batch size or the grid.
+// order) added as a pairwise tree.  Device pieces are shared by every
+// kernel, so every entry point computes identical bits, and no order depends
+// on the batch size or the grid.
 //
 // Kernels:
-//   norm_mod_bwd_kernel<role>  dx rows and/or level-0 tiles of a 32-token
-//                              tile, the 14 blocks of a tile on one XCD
 //   proj_bwd_small_kernel<NB>  B <= 4: da column blocks (-> dtemb) and dW
 //                              tiles (-> dW, db) in one grid
-//   silu/dW/da kernels         B > 4
-#include <hip/hip_ext.h>
-
+//   silu_kernel, proj_bwd_dw_kernel, proj_bwd_da_kernel   B > 4
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -40,185 +23,6 @@ namespace adaln {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kLaneChunks = kChunks / 64;          // 6
-constexpr int kRowBlocks = kTile / 4;              // 8 row blocks of 4 rows per tile
-constexpr int kColPairs = kThreads;                // 256 column pairs per column block
-constexpr int kColBlockCols = 2 * kColPairs;       // 512 columns
-constexpr int kColBlocks = kD / kColBlockCols;     // 6
-constexpr int kBlocksPerTile = kRowBlocks + kColBlocks;   // 14
-
-enum Role { kBoth = 0, kRowsOnly = 1, kColsOnly = 2 };
-
-__device__ __forceinline__ void row_pass(const uint16_t* __restrict__ g, const uint16_t* __restrict__ x,
-                                         const float* __restrict__ mean, const float* __restrict__ rstd,
-                                         const uint16_t* __restrict__ emb, uint16_t* __restrict__ dx,
-                                         int64_t b, int64_t s, int64_t S, float4* m_lds) {
-  const int lane = threadIdx.x & 63;
-  // A wave past the end of the sample redoes row S - 1 and stores the same
-  // bytes as the wave that owns it: no branch follows the barrier, so the
-  // compiler keeps the row loads ahead of it.
-  const int64_t row = b * S + (s < S ? s : S - 1);
-
-  // small loads first: the memory counter drains in issue order, so staging
-  // m needs only these, while the row loads below stay in flight
-  const uint2* scale = reinterpret_cast<const uint2*>(emb + b * kN);
-  uint2 sc[3];
-#pragma unroll
-  for (int k = 0; k < 3; ++k) sc[k] = scale[threadIdx.x + kThreads * k];
-  const float mu = mean[row];
-  const float rs = rstd[row];
-  uint4 gv[kLaneChunks], xv[kLaneChunks];
-#pragma unroll
-  for (int i = 0; i < kLaneChunks; ++i) {
-    gv[i] = ld16(g + row * kD + (lane + 64 * i) * 8);
-    xv[i] = ld16(x + row * kD + (lane + 64 * i) * 8);
-  }
-#pragma unroll
-  for (int k = 0; k < 3; ++k)
-    m_lds[threadIdx.x + kThreads * k] =
-        make_float4(round_bf16(1.0f + bf_lo(sc[k].x)), round_bf16(1.0f + bf_hi(sc[k].x)),
-                    round_bf16(1.0f + bf_lo(sc[k].y)), round_bf16(1.0f + bf_hi(sc[k].y)));
-  __syncthreads();
-
-  double q1 = 0.0, q2 = 0.0;
-#pragma unroll
-  for (int i = 0; i < kLaneChunks; ++i) {
-    const int c = lane + 64 * i;
-    float gf[8], xf[8];
-    unpack8(gv[i], gf);
-    unpack8(xv[i], xf);
-    const float4 m0 = m_lds[2 * c], m1 = m_lds[2 * c + 1];
-    const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float n = (xf[e] - mu) * rs;
-      const float gy = gf[e] * mm[e];
-      q1 += static_cast<double>(gy);
-      q2 += static_cast<double>(gy * n);
-    }
-  }
-  const float alpha = static_cast<float>(wave_sum_f64(q1)) / static_cast<float>(kD);
-  const float beta = static_cast<float>(wave_sum_f64(q2)) / static_cast<float>(kD);
-  // keep the packed rows packed across the reduction (recompute below rather
-  // than hold 96 unpacked values in registers)
-#pragma unroll
-  for (int i = 0; i < kLaneChunks; ++i) {
-    asm volatile("" : "+v"(gv[i].x), "+v"(gv[i].y), "+v"(gv[i].z), "+v"(gv[i].w));
-    asm volatile("" : "+v"(xv[i].x), "+v"(xv[i].y), "+v"(xv[i].z), "+v"(xv[i].w));
-  }
-
-  uint16_t* drow = dx + row * kD;
-#pragma unroll
-  for (int i = 0; i < kLaneChunks; ++i) {
-    const int c = lane + 64 * i;
-    float gf[8], xf[8], d[8];
-    unpack8(gv[i], gf);
-    unpack8(xv[i], xf);
-    const float4 m0 = m_lds[2 * c], m1 = m_lds[2 * c + 1];
-    const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float n = (xf[e] - mu) * rs;
-      const float gy = gf[e] * mm[e];
-      d[e] = rs * ((gy - alpha) - n * beta);
-    }
-    st16_nt(drow + c * 8, pack8(d));
-  }
-}
-
-// Level-0 pairs of one 32-token tile for 512 columns (2 per thread).  The
-// tile's statistics are the same for the whole block (scalar loads, no LDS,
-// no barrier).  A full tile takes the branch-free form: buffer loads (the
-// lane's column offset in a VGPR, the row's in an SGPR, no per-load address
-// arithmetic), and the memory counter lets the chains start on row 0 while
-// later rows are in flight.  Only the last, ragged tile of a sample takes the
-// guarded form.
-template <bool kFull>
-__device__ __forceinline__ void col_tile(const uint16_t* __restrict__ g, const uint16_t* __restrict__ x,
-                                         const float* __restrict__ mean, const float* __restrict__ rstd,
-                                         float* __restrict__ part, int64_t b, int64_t tile, int cb,
-                                         int64_t S, int64_t T0, int rows) {
-  const int col = cb * kColBlockCols + 2 * threadIdx.x;
-  const int64_t row0 = b * S + tile * kTile;
-  uint32_t gw[kTile], xw[kTile];
-  if (kFull) {
-    constexpr uint32_t kBytes = kTile * kD * 2;
-    const Buffer gt(g + row0 * kD, kBytes), xt(x + row0 * kD, kBytes);
-#pragma unroll
-    for (int r = 0; r < kTile; ++r) {
-      gw[r] = gt.u32(col * 2, r * kD * 2);
-      xw[r] = xt.u32(col * 2, r * kD * 2);
-    }
-  } else {
-#pragma unroll
-    for (int r = 0; r < kTile; ++r) {
-      if (r < rows) {
-        const int64_t off = (row0 + r) * kD + col;
-        gw[r] = *reinterpret_cast<const uint32_t*>(g + off);
-        xw[r] = *reinterpret_cast<const uint32_t*>(x + off);
-      }
-    }
-  }
-  float sg0 = 0.0f, cg0 = 0.0f, sg1 = 0.0f, cg1 = 0.0f;
-  float sn0 = 0.0f, cn0 = 0.0f, sn1 = 0.0f, cn1 = 0.0f;
-#pragma unroll
-  for (int r = 0; r < kTile; ++r) {
-    if (kFull || r < rows) {
-      const float mu = mean[row0 + r], rs = rstd[row0 + r];
-      const float g0 = bf_lo(gw[r]), g1 = bf_hi(gw[r]);
-      const float n0 = (bf_lo(xw[r]) - mu) * rs;
-      const float n1 = (bf_hi(xw[r]) - mu) * rs;
-      neumaier_add(sg0, cg0, g0);
-      neumaier_add(sg1, cg1, g1);
-      neumaier_add(sn0, cn0, g0 * n0);
-      neumaier_add(sn1, cn1, g1 * n1);
-    }
-  }
-  // columns [0, D) of d_emb: d_scale (g * n); [D, 2D): d_shift (g)
-  constexpr int64_t kGroups = kN / kPairGroup;
-  const int64_t i_scale = pair_index(b, kGroups, T0, tile, col);
-  const int64_t i_shift = pair_index(b, kGroups, T0, tile, col + kD);
-  st8_nt(part + i_scale, sn0, sn1);
-  st8_nt(part + i_scale + kPairGroup, cn0, cn1);
-  st8_nt(part + i_shift, sg0, sg1);
-  st8_nt(part + i_shift + kPairGroup, cg0, cg1);
-}
-
-__device__ __forceinline__ void col_pass(const uint16_t* __restrict__ g, const uint16_t* __restrict__ x,
-                                         const float* __restrict__ mean, const float* __restrict__ rstd,
-                                         float* __restrict__ part, int64_t b, int64_t tile, int cb,
-                                         int64_t S, int64_t T0) {
-  const int64_t left = S - tile * kTile;
-  if (left >= kTile) col_tile<true>(g, x, mean, rstd, part, b, tile, cb, S, T0, kTile);
-  else col_tile<false>(g, x, mean, rstd, part, b, tile, cb, S, T0, static_cast<int>(left));
-}
-
-// grid: 1-D, ceil(B*T0 / 8) * 8 * blocks_per_tile blocks (blocks_per_tile = 14,
-// 8 or 6 for kBoth / kRowsOnly / kColsOnly).  Block L runs on XCD L % 8; on
-// that XCD its index j = L / 8 selects tile (j / bpt) * 8 + L % 8 and role j % bpt.
-template <int kRole>
-__global__ __launch_bounds__(kThreads) void norm_mod_bwd_kernel(
-    const uint16_t* __restrict__ g, const uint16_t* __restrict__ x,
-    const float* __restrict__ mean, const float* __restrict__ rstd,
-    const uint16_t* __restrict__ emb, uint16_t* __restrict__ dx,
-    float* __restrict__ part, int64_t B, int64_t S, int64_t T0) {
-  constexpr int bpt = kRole == kBoth ? kBlocksPerTile : (kRole == kRowsOnly ? kRowBlocks : kColBlocks);
-  __shared__ float4 m_lds[kD / 4];   // row blocks: m = bf16(1 + scale)
-  const int64_t L = blockIdx.x;
-  const int64_t j = L >> 3;
-  const int64_t G = (j / bpt) * 8 + (L & 7);
-  const int role = static_cast<int>(j % bpt);
-  if (G >= B * T0) return;
-  const int64_t b = G / T0;
-  const int64_t tile = G % T0;
-  if (kRole != kColsOnly && role < kRowBlocks) {
-    const int64_t s = tile * kTile + role * 4 + (threadIdx.x >> 6);
-    row_pass(g, x, mean, rstd, emb, dx, b, s, S, m_lds);
-  } else {
-    const int cb = kRole == kColsOnly ? role : role - kRowBlocks;
-    col_pass(g, x, mean, rstd, part, b, tile, cb, S, T0);
-  }
-}
 
 // ---- projection backward ------------------------------------------------
 // dW tiles: part p of 32 (192 rows) x column block kb of 12 (256 columns),
@@ -540,47 +344,8 @@ __global__ __launch_bounds__(kThreads) void proj_bwd_da_kernel(const float* __re
   da_block<kBatchChunk>(d_emb, W, temb, dtemb, blockIdx.x, b0, nb, red);
 }
 
-template <int kRole>
-hipError_t launch_role(const uint16_t* g, const uint16_t* x, const float* mean, const float* rstd,
-                       const uint16_t* emb, uint16_t* dx, float* part, int64_t B,
-                       int64_t S, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  constexpr int bpt = kRole == kBoth ? kBlocksPerTile : (kRole == kRowsOnly ? kRowBlocks : kColBlocks);
-  const int64_t T0 = (S + kTile - 1) / kTile;
-  const int64_t groups = (B * T0 + 7) / 8;
-  const dim3 grid(static_cast<unsigned>(groups * 8 * bpt));
-  if (e0 != nullptr && e1 != nullptr) {
-    // events carried by the dispatch itself: no extra barrier in the stream
-    hipExtLaunchKernelGGL(norm_mod_bwd_kernel<kRole>, grid, dim3(kThreads), 0, s, e0, e1, 0, g, x, mean,
-                          rstd, emb, dx, part, B, S, T0);
-  } else {
-    hipLaunchKernelGGL(norm_mod_bwd_kernel<kRole>, grid, dim3(kThreads), 0, s, g, x, mean, rstd, emb, dx,
-                       part, B, S, T0);
-  }
-  return hipGetLastError();
-}
 
 }  // namespace
-
-hipError_t launch_norm_mod_bwd(const uint16_t* g, const uint16_t* x, const float* mean,
-                               const float* rstd, const uint16_t* emb, uint16_t* dx, float* part,
-                               int64_t B, int64_t S, hipStream_t s, hipEvent_t e0,
-                               hipEvent_t e1) {
-  static_assert(kD % kColBlockCols == 0, "column blocks must tile D");
-  return launch_role<kBoth>(g, x, mean, rstd, emb, dx, part, B, S, s, e0, e1);
-}
-
-hipError_t launch_norm_mod_bwd_dx(const uint16_t* g, const uint16_t* x, const float* mean,
-                                  const float* rstd, const uint16_t* emb, uint16_t* dx, int64_t B,
-                                  int64_t S, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  return launch_role<kRowsOnly>(g, x, mean, rstd, emb, dx, nullptr, B, S, s, e0, e1);
-}
-
-hipError_t launch_norm_mod_bwd_tiles(const uint16_t* g, const uint16_t* x, const float* mean,
-                                     const float* rstd, float* part, int64_t B,
-                                     int64_t S, hipStream_t s) {
-  return launch_role<kColsOnly>(g, x, mean, rstd, nullptr, nullptr, part, B, S, s, nullptr,
-                                nullptr);
-}
 
 int proj_bwd_fused_max_batch() { return kBatchChunk; }
 
@@ -617,5 +382,6 @@ hipError_t launch_silu(const uint16_t* temb, uint16_t* a, int64_t n, hipStream_t
   hipLaunchKernelGGL(silu_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, temb, a, n);
   return hipGetLastError();
 }
+
 
 }  // namespace adaln
