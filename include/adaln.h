@@ -157,8 +157,11 @@ int token_tree_sum(const float* x, float* out, void* ws, size_t ws_bytes, int64_
 int adaln_selftest(void);
 
 /* One-call forward: adaln_proj_fwd then adaln_norm_mod_fwd, same results bit
- * for bit, scheduled so that the projection's pass over W and the LayerNorm
- * statistics pass over x run side by side (one launch), then the modulation.
+ * for bit.  B <= 4: the projection's pass over W and the LayerNorm statistics
+ * pass over x run side by side (one launch), then the modulation.  B > 4: the
+ * SiLU once (into the first B * 3072 elements of `out`, which the modulation
+ * overwrites afterwards), the projection, then statistics and modulation in
+ * one pass over x.
  *   temb, W, bias, x in; emb, out, mean, rstd out (layouts as above). */
 int adaln_fwd(const adaln_bf16* temb, const adaln_bf16* W, const adaln_bf16* bias, const adaln_bf16* x,
               adaln_bf16* emb, adaln_bf16* out, float* mean, float* rstd, int64_t B, int64_t S,

@@ -66,7 +66,10 @@ __device__ __forceinline__ void row_pass(const uint16_t* __restrict__ g, const u
                     round_bf16(1.0f + bf_lo(sc[k].y)), round_bf16(1.0f + bf_hi(sc[k].y)));
   __syncthreads();
 
+  // first pass: n and gy into registers (96 values; the second pass then
+  // needs four operations per element), the two row sums in fp64
   double q1 = 0.0, q2 = 0.0;
+  float nv[kLaneChunks][8], gyv[kLaneChunks][8];
 #pragma unroll
   for (int i = 0; i < kLaneChunks; ++i) {
     const int c = lane + 64 * i;
@@ -77,37 +80,21 @@ __device__ __forceinline__ void row_pass(const uint16_t* __restrict__ g, const u
     const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float n = (xf[e] - mu) * rs;
-      const float gy = gf[e] * mm[e];
-      q1 += static_cast<double>(gy);
-      q2 += static_cast<double>(gy * n);
+      nv[i][e] = (xf[e] - mu) * rs;
+      gyv[i][e] = gf[e] * mm[e];
+      q1 += static_cast<double>(gyv[i][e]);
+      q2 += static_cast<double>(gyv[i][e] * nv[i][e]);
     }
   }
   const float alpha = static_cast<float>(wave_sum_f64(q1)) / static_cast<float>(kD);
   const float beta = static_cast<float>(wave_sum_f64(q2)) / static_cast<float>(kD);
-  // keep the packed rows packed across the reduction (recompute below rather
-  // than hold 96 unpacked values in registers)
-#pragma unroll
-  for (int i = 0; i < kLaneChunks; ++i) {
-    asm volatile("" : "+v"(gv[i].x), "+v"(gv[i].y), "+v"(gv[i].z), "+v"(gv[i].w));
-    asm volatile("" : "+v"(xv[i].x), "+v"(xv[i].y), "+v"(xv[i].z), "+v"(xv[i].w));
-  }
-
   uint16_t* drow = dx + row * kD;
 #pragma unroll
   for (int i = 0; i < kLaneChunks; ++i) {
     const int c = lane + 64 * i;
-    float gf[8], xf[8], d[8];
-    unpack8(gv[i], gf);
-    unpack8(xv[i], xf);
-    const float4 m0 = m_lds[2 * c], m1 = m_lds[2 * c + 1];
-    const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+    float d[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float n = (xf[e] - mu) * rs;
-      const float gy = gf[e] * mm[e];
-      d[e] = rs * ((gy - alpha) - n * beta);
-    }
+    for (int e = 0; e < 8; ++e) d[e] = rs * ((gyv[i][e] - alpha) - nv[i][e] * beta);
     st16_nt(drow + c * 8, pack8(d));
   }
 }
