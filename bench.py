@@ -104,7 +104,7 @@ def main() -> int:
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the batch-invariant path has no multi-GPU "
-              "mode in this build (see DESIGN.md for how it would shard).", file=sys.stderr)
+              "mode; --gpus must be 1.", file=sys.stderr)
         return 2
 
     import numpy as np

@@ -18,7 +18,7 @@ Source of every step (page titles and sections; the pages print no code):
   reduction of the reference be compensated (input gradient and bias gradient
   included), which this oracle does: every sum below is an NSum.
 
-Readings where the pages leave a step open (all listed in the design doc):
+Readings where the pages leave a step open:
   * SiLU is evaluated in float64 and rounded to float32, then to bf16 (its
     output is the bf16 input of the projection matmul).
   * The projection accumulates in fp32, adds the bias in fp32, then rounds

@@ -15,7 +15,7 @@ recursively until one value remains).  Its review thread records two versions:
   of sum and correction gives the result.  The H100 results section reports
   6030 on the cancellation case.
 
-Reading of the fold (the pages do not spell it out; listed in the design doc): a
+Reading of the fold (the pages do not spell it out): a
 node visits its children in ascending order; for each child it takes one
 Neumaier step on the child's sum (s, c updated) and then adds the child's
 correction into c.  Tiles restart at token 0 of every sample.  Accumulators
