@@ -49,7 +49,7 @@ extern "C" {
 
 typedef uint16_t adaln_bf16;
 
-#define ADALN_ABI_VERSION 1
+#define ADALN_ABI_VERSION 2
 
 enum adaln_status {
   ADALN_OK = 0,
@@ -63,6 +63,7 @@ enum adaln_status {
 };
 
 enum adaln_op {
+  ADALN_OP_PROJ_FWD = 1,
   ADALN_OP_NORM_MOD_BWD = 2,
   ADALN_OP_PROJ_BWD = 3,
   ADALN_OP_TOKEN_TREE_SUM = 4,
@@ -70,6 +71,8 @@ enum adaln_op {
 };
 
 /* Workspace bytes an entry point needs (0 for an unknown op or bad sizes).
+ *   PROJ_FWD:       H = K (3072), S ignored.  B*K*2 (SiLU activations, used when
+ *                   B > 4).
  *   NORM_MOD_BWD:   H = D (3072).  B * ceil(S/32) * 2D * 8 bytes (level-0 pairs).
  *   PROJ_BWD:       H = K (3072), S ignored.  B*K*2 (SiLU activations, used when
  *                   B > 4).
@@ -82,10 +85,17 @@ size_t adaln_workspace_bytes(int op, int64_t B, int64_t S, int64_t H);
  *   temb [B, K] bf16 (in), W [N, K] bf16 (in, row-major), bias [N] bf16 (in),
  *   emb  [B, N] bf16 (out) = (scale | shift).
  *   emb = bf16(fp32(sum_k a_k W_jk) + bias_j), a = bf16(fp32(SiLU(temb))),
- *   SiLU evaluated in float64; the sum accumulates exact products in fp64 in a
- *   fixed order independent of B. */
+ *   SiLU evaluated in float64.  The sum is one fixed tree whatever B: 64 leaves
+ *   of 48 consecutive k, each accumulated from +0 by fp64 fused multiply-adds
+ *   (exact products, one rounding per add) in the order k = 48 l + 12 g + s
+ *   (s = 0..11 outer, g = 0..3 inner), the leaves then added pairwise in index
+ *   order.  B <= 4 runs it on the vector units, B > 4 on the fp64 matrix cores
+ *   (a chain of fused multiply-adds in k order): the same bits either way.
+ *   ws: adaln_workspace_bytes(ADALN_OP_PROJ_FWD, B, 1, K) bytes, 16-byte
+ *   aligned; holds a when B > 4. */
 int adaln_proj_fwd(const adaln_bf16* temb, const adaln_bf16* W, const adaln_bf16* bias,
-                   adaln_bf16* emb, int64_t B, int64_t K, int64_t N, void* stream);
+                   adaln_bf16* emb, void* ws, size_t ws_bytes, int64_t B, int64_t K, int64_t N,
+                   void* stream);
 
 /* LayerNorm + modulation forward (pull request 538, "What"; rounding points of
  * miles_diffusion pull request 108).
@@ -135,8 +145,14 @@ int token_tree_fold(const void* part, float* out, int64_t B, int64_t T0, int64_t
  *   d_emb [B, N] fp32 (in), temb [B, K] bf16 (in), W [N, K] bf16 (in),
  *   dW [N, K] bf16 (out), db [N] bf16 (out), dtemb [B, K] bf16 (out).
  *   dW = bf16(fp32(sum_b d_emb_bj * a_bk)), db = bf16(fp32(sum_b d_emb_bj)),
- *   dtemb = bf16(fp32(sum_j d_emb_bj * W_jk) * silu'(temb)); fp32 products,
- *   fp64 accumulation in orders that do not depend on B. */
+ *   dtemb = bf16(fp32(sum_j d_emb_bj * W_jk) * silu'(temb)).  Every product is
+ *   exact (an fp64 fused multiply-add) and the sums run in fp64 in orders that
+ *   do not depend on B: dW and db over samples ascending from +0; da as 128
+ *   leaves (leaf t: rows t, t + 128, ..., ascending, from +0) added pairwise in
+ *   leaf order.  B <= 4 runs on the vector units, B > 4 on the fp64 matrix
+ *   cores: the same bits either way.
+ *   ws: adaln_workspace_bytes(ADALN_OP_PROJ_BWD, B, 1, K) bytes (holds a when
+ *   B > 4). */
 int adaln_proj_bwd(const float* d_emb, const adaln_bf16* temb, const adaln_bf16* W,
                    adaln_bf16* dW, adaln_bf16* db, adaln_bf16* dtemb, void* ws, size_t ws_bytes,
                    int64_t B, int64_t K, int64_t N, void* stream);

@@ -3,7 +3,8 @@
 Flags: -O3, -ffp-contract=off (no implicit fused multiply-add: every float
 operation in the kernels is one IEEE operation), correctly rounded fp32
 division and square root, fp32 denormals kept (HIP's default for gfx950),
-packed fp32 vector instructions disabled on the device pass, code object v5.
+packed fp32 vector instructions disabled on the device pass, matrix-core
+accumulators in VGPRs, code object v5.
 """
 
 from __future__ import annotations
@@ -27,6 +28,10 @@ COMMON_FLAGS = [
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-mcode-object-version=5",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: a runtime loop over an MFMA
+    # chain otherwise copies every accumulator between VGPRs and AGPRs on
+    # each iteration
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     f"-I{os.path.join(ROOT, 'include')}",
 ]

@@ -115,6 +115,9 @@ size_t ws_pairs(int64_t B, int64_t S, int64_t H) {
   return pad256(static_cast<size_t>(B * ceil_div(S, kTile) * ceil_div(H, 64) * 128 * 4));
 }
 size_t ws_norm_bwd(int64_t B, int64_t S) { return ws_pairs(B, S, kN); }
+size_t ws_proj_fwd(int64_t B) {
+  return pad256(static_cast<size_t>(B * kD * 2));   // SiLU activations (B > 4)
+}
 size_t ws_proj_bwd(int64_t B) {
   return pad256(static_cast<size_t>(B * kD * 2));   // SiLU activations (B > 4)
 }
@@ -217,6 +220,7 @@ size_t adaln_workspace_bytes(int op, int64_t B, int64_t S, int64_t H) {
   if (!batch_ok(B)) return 0;
   switch (op) {
     case ADALN_OP_NORM_MOD_BWD: return (H == kD && seq_ok(S)) ? ws_norm_bwd(B, S) : 0;
+    case ADALN_OP_PROJ_FWD: return H == kD ? ws_proj_fwd(B) : 0;
     case ADALN_OP_PROJ_BWD: return H == kD ? ws_proj_bwd(B) : 0;
     case ADALN_OP_BWD: return (H == kD && seq_ok(S)) ? ws_norm_bwd(B, S) + ws_proj_bwd(B) : 0;
     case ADALN_OP_TOKEN_TREE_SUM:
@@ -226,17 +230,22 @@ size_t adaln_workspace_bytes(int op, int64_t B, int64_t S, int64_t H) {
 }
 
 int adaln_proj_fwd(const adaln_bf16* temb, const adaln_bf16* W, const adaln_bf16* bias,
-                   adaln_bf16* emb, int64_t B, int64_t K, int64_t N, void* stream) {
-  if (!temb || !W || !bias || !emb) return ADALN_ERR_NULL;
+                   adaln_bf16* emb, void* ws, size_t ws_bytes, int64_t B, int64_t K, int64_t N,
+                   void* stream) {
+  if (!temb || !W || !bias || !emb || !ws) return ADALN_ERR_NULL;
   if (!batch_ok(B) || K != kD || N != kN) return ADALN_ERR_SHAPE;
-  if (!aligned16(temb) || !aligned16(W) || !aligned16(bias) || !aligned16(emb)) return ADALN_ERR_ALIGN;
-  if (int rc = check_overlap({{emb, static_cast<size_t>(B * kN * 2)}},
+  if (!aligned16(temb) || !aligned16(W) || !aligned16(bias) || !aligned16(emb) || !aligned16(ws))
+    return ADALN_ERR_ALIGN;
+  const size_t need = ws_proj_fwd(B);
+  if (ws_bytes < need) return ADALN_ERR_WORKSPACE;
+  if (int rc = check_overlap({{emb, static_cast<size_t>(B * kN * 2)}, {ws, need}},
                              {{temb, static_cast<size_t>(B * kD * 2)}, {W, static_cast<size_t>(kN * kD * 2)},
                               {bias, static_cast<size_t>(kN * 2)}}))
     return rc;
   if (int rc = check_device()) return rc;
   (void)hipGetLastError();
-  return launched(adaln::launch_proj_fwd(temb, W, bias, emb, B, as_stream(stream)));
+  return launched(adaln::launch_proj_fwd(temb, W, bias, emb, static_cast<uint16_t*>(ws), B,
+                                         as_stream(stream)));
 }
 
 int adaln_norm_mod_fwd(const adaln_bf16* x, const adaln_bf16* emb, adaln_bf16* out, float* mean,

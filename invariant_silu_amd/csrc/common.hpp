@@ -165,15 +165,6 @@ __device__ __forceinline__ uint4 silu8_fast(const uint4& in, uint32_t& redo_mask
   return make_uint4(o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16), o[6] | (o[7] << 16));
 }
 
-// acc + a * w for bf16-valued a and w: the fp32 product of two bf16 values
-// is exact (16 significant bits; outside fp32's range it rounds as fp32
-// does), and the add rounds once in fp64.  Every projection-forward kernel
-// accumulates through this, in the same order, so emb does not depend on
-// which kernel (or batch size) produced it.
-__device__ __forceinline__ double mac_exact(float a, float w, double acc) {
-  return acc + static_cast<double>(a * w);
-}
-
 // One Neumaier step: t = s + x; c += exact rounding error of that add.
 // The branch-free form picks the larger-magnitude operand for Fast2Sum, so
 // c gets the same exact error term as the textbook |s| >= |x| branch.

@@ -6,36 +6,33 @@
 //   rstd = 1 / sqrt(var + eps),  n = (x - mu) * rstd
 //   out  = bf16((n * m) + shift),  m = bf16(1 + scale)
 //
-// Device pieces shared by every kernel below, so the standalone entry points
-// and the overlapped stage kernels compute identical bits:
+// The projection's sum for one (sample, row of W) has one fixed shape: a tree
+// of 64 leaves of 48 products each (described with the kernels below).
 //
-// proj_block<NB> (B = NB <= 4): 8 rows of W (4 waves x 2 rows) held in
-//   registers; lane l holds the 16-byte chunks l, l+64, ..., l+320 of a row,
-//   loaded chunk-major.  The temb loads are issued first; their SiLU
-//   (silu8_fast, with the rare near-tie elements redone by silu_bf16_exact:
-//   identical bits to the float64 definition) goes to LDS while W is in
-//   flight.  bf16 x bf16 products (exact in fp32) are accumulated in fp64
-//   (mac_exact): chunk-major within the lane, then the fixed lane tree of
-//   wave_sum_f64; one rounding to fp32, the bias added in fp32, one rounding
-//   to bf16.  One accumulator per sample: emb of a sample does not depend on
-//   B or the grid.
-// proj_wide_kernel (B > 4): the same rows, lanes, chunks and order for 8
-//   samples per block, so the same bits.
+// proj_block<NB> (B = NB <= 4): 8 rows of W per block (4 waves x 2 rows) in
+//   registers, lane l holding leaf l of each row.  The temb loads are issued
+//   first; their SiLU (silu8_fast, with the rare near-tie elements redone by
+//   silu_bf16_exact: identical bits to the float64 definition) goes to LDS
+//   while W is in flight.  Leaves accumulate in fp64 fused multiply-adds,
+//   then wave_sum_f64; one rounding to fp32, the bias added in fp32, one
+//   rounding to bf16.
+// proj_mfma_kernel (B > 4): the same leaves and tree on the fp64 matrix
+//   cores, from a = bf16(SiLU(temb)) computed once by silu_kernel.  emb of a
+//   sample has the same bits whatever B and whichever kernel produced it.
 // row_stats: one wave per row, the lane's 48 values summed in fp64 in order,
 //   then wave_sum_f64; (x - mu) and its square in fp32; correctly rounded
 //   sqrt and divide.
 // modulate: two fp32 operations per element, one bf16 rounding.
 //
-// Kernels: proj_fwd_kernel / proj_wide_kernel (adaln_proj_fwd),
+// Kernels: proj_fwd_kernel / proj_mfma_kernel (adaln_proj_fwd),
 // norm_mod_fwd_kernel (statistics and modulation, adaln_norm_mod_fwd), and
 // for the one-call forward adaln_fwd with B <= 4: fwd_stage1_kernel
 // (projection blocks and statistics blocks in one grid: two independent HBM
-// streams, W and x) then norm_modulate_kernel; with B > 4, proj_wide_kernel
-// then norm_mod_fwd_kernel.
-#include <type_traits>
-
+// streams, W and x) then norm_modulate_kernel; with B > 4, silu_kernel and
+// proj_mfma_kernel, then norm_mod_fwd_kernel.
 #include "common.hpp"
 #include "launch.hpp"
+#include "mfma.hpp"
 
 namespace adaln {
 
@@ -51,17 +48,39 @@ constexpr int kMaxNarrowBatch = 4;                         // proj_block up to h
 static_assert(kN % kProjRowsPerBlock == 0, "rows per block must divide N");
 
 // ----------------------------------------------------------- projection ----
+// The sum for one (sample, row of W) is a tree of 64 leaves.  Leaf l covers
+// k in [48 l, 48 l + 48), taken as 12 steps of 4: step s adds the elements
+// 48 l + 12 g + s for g = 0, 1, 2, 3 in that order, each an fp64 fused
+// multiply-add of bf16-valued operands (the product is exact, the add rounds
+// once), starting from +0.  The 64 leaves are then added pairwise in index
+// order (0+1, 2+3, ..., then pairs of pairs).  The VALU blocks below hold
+// leaf l in lane l and take the tree with wave_sum_f64; the matrix-core
+// kernel feeds the same four terms of a step to one v_mfma_f64_16x16x4f64
+// (a chain of four fused multiply-adds in k order) and builds the same tree
+// in registers.  Every path therefore produces the same bits.
+constexpr int kLeafK = kD / 64;                            // 48
+constexpr int kLeafSteps = kLeafK / 4;                     // 12
+
 template <int NB>
 struct ProjShared {
-  uint4 a[NB * kChunks];
+  // a of each sample, per leaf (lane) 24 dwords in step-pair order: position
+  // 4 t + g holds dword 6 g + t of the leaf (elements 12 g + 2t, 12 g + 2t + 1);
+  // 28 dwords per lane so 16 lanes' 16-byte reads hit distinct banks
+  uint32_t a[NB * 64 * 28];
 };
+constexpr int kLdsLane = 28;
+
+// byte offset in ProjShared::a of dword d (0..23, natural order) of leaf l
+__device__ __forceinline__ int a_lds_dword(int bb, int l, int d) {
+  return (bb * 64 + l) * kLdsLane + 4 * (d % 6) + d / 6;
+}
 
 // Projection blocks for B = NB <= 4 (one pass over the samples).
 template <int NB>
 __device__ __forceinline__ void proj_block(const uint16_t* __restrict__ temb,
                                            const uint16_t* __restrict__ W,
                                            const uint16_t* __restrict__ bias,
-                                           uint16_t* __restrict__ emb, int blk, uint4* a_lds) {
+                                           uint16_t* __restrict__ emb, int blk, uint32_t* a_lds) {
   constexpr int kStage = (NB * kChunks + kThreads - 1) / kThreads;
   static_assert(kStage <= 8, "redo mask holds 8 chunks of 8 elements");
   const int wave = threadIdx.x >> 6;
@@ -79,22 +98,30 @@ __device__ __forceinline__ void proj_block(const uint16_t* __restrict__ temb,
   float bias_f[kRows];
 #pragma unroll
   for (int r = 0; r < kRows; ++r) bias_f[r] = bf16_to_f32(bias[row0 + r]);
+  // lane l: the 48 elements of leaf l of each row (6 x 16 bytes)
   uint4 w[kLaneChunks][kRows];
 #pragma unroll
-  for (int i = 0; i < kLaneChunks; ++i)
+  for (int q = 0; q < kLaneChunks; ++q)
 #pragma unroll
     for (int r = 0; r < kRows; ++r)
-      w[i][r] = ld16(W + static_cast<int64_t>(row0 + r) * kD + (lane + 64 * i) * 8);
+      w[q][r] = ld16(W + static_cast<int64_t>(row0 + r) * kD + lane * kLeafK + 8 * q);
 
-  // SiLU of the NB samples into LDS; elements the fast path flags are redone
-  // from memory in a separate, rarely taken loop
+  // SiLU of the NB samples into LDS (chunk c of a sample is dwords 4 (c % 6)
+  // .. + 3 of leaf c / 6); elements the fast path flags are redone from
+  // memory in a separate, rarely taken loop
   uint64_t redo = 0;
 #pragma unroll
   for (int k = 0; k < kStage; ++k) {
     const int c = threadIdx.x + kThreads * k;
     if (c < NB * kChunks) {
       uint32_t m;
-      a_lds[c] = silu8_fast(tz[k], m);
+      const uint4 v = silu8_fast(tz[k], m);
+      const int bb = c / kChunks, cc = c % kChunks;
+      const int l = cc / 6, d0 = 4 * (cc % 6);
+      a_lds[a_lds_dword(bb, l, d0 + 0)] = v.x;
+      a_lds[a_lds_dword(bb, l, d0 + 1)] = v.y;
+      a_lds[a_lds_dword(bb, l, d0 + 2)] = v.z;
+      a_lds[a_lds_dword(bb, l, d0 + 3)] = v.w;
       redo |= static_cast<uint64_t>(m) << (8 * k);
     }
   }
@@ -103,8 +130,10 @@ __device__ __forceinline__ void proj_block(const uint16_t* __restrict__ temb,
     redo &= redo - 1;
     const int c = threadIdx.x + kThreads * (bit / 8);
     const int e = bit % 8;
-    reinterpret_cast<uint16_t*>(a_lds)[c * 8 + e] =
-        silu_bf16_exact(bf16_to_f32(temb[(c / kChunks) * kD + (c % kChunks) * 8 + e]));
+    const int bb = c / kChunks, cc = c % kChunks;
+    const uint16_t h =
+        silu_bf16_exact(bf16_to_f32(temb[bb * kD + cc * 8 + e]));
+    reinterpret_cast<uint16_t*>(a_lds)[2 * a_lds_dword(bb, cc / 6, 4 * (cc % 6) + e / 2) + (e & 1)] = h;
   }
   __syncthreads();
 
@@ -113,20 +142,36 @@ __device__ __forceinline__ void proj_block(const uint16_t* __restrict__ temb,
   for (int r = 0; r < kRows; ++r)
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) acc[r][bb] = 0.0;
+  const uint32_t(&wd)[kLaneChunks][kRows][4] = reinterpret_cast<const uint32_t(&)[kLaneChunks][kRows][4]>(w);
 #pragma unroll
-  for (int i = 0; i < kLaneChunks; ++i) {
-    float av[NB][8];
+  for (int t = 0; t < kLeafSteps / 2; ++t) {
+    // steps 2t and 2t + 1: dwords 6 g + t of the leaf, low then high halves
+    uint4 av[NB];
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb) unpack8(a_lds[bb * kChunks + lane + 64 * i], av[bb]);
+    for (int bb = 0; bb < NB; ++bb)
+      av[bb] = *reinterpret_cast<const uint4*>(a_lds + (bb * 64 + lane) * kLdsLane + 4 * t);
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-      float wv[8];
-      unpack8(w[i][r], wv);
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int bb = 0; bb < NB; ++bb)
+      for (int g = 0; g < 4; ++g) {
+        const int d = 6 * g + t;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[r][bb] = mac_exact(av[bb][e], wv[e], acc[r][bb]);
+        for (int r = 0; r < kRows; ++r) {
+          const double wv = bf_half64(wd[d / 4][r][d % 4], h);
+#pragma unroll
+          for (int bb = 0; bb < NB; ++bb) {
+            const uint32_t ad = g == 0 ? av[bb].x : g == 1 ? av[bb].y : g == 2 ? av[bb].z : av[bb].w;
+            acc[r][bb] = __builtin_fma(bf_half64(ad, h), wv, acc[r][bb]);
+          }
+        }
+      }
     }
+    // the accumulators are materialised here: each step pair's fp64
+    // conversions stay next to their uses instead of being kept for later
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) asm volatile("" : "+v"(acc[r][bb]));
   }
 #pragma unroll
   for (int r = 0; r < kRows; ++r) {
@@ -141,121 +186,123 @@ __device__ __forceinline__ void proj_block(const uint16_t* __restrict__ temb,
   }
 }
 
-// Projection for B > 4: the same 8 rows of W per block (same lanes, chunks
-// and order), kWideBT samples per blockIdx.y.  Per (sample, row) the lane's
-// partial sum and the wave tree are exactly those of proj_block, so emb has
-// the same bits whatever B.
-constexpr int kWideBT = 8;
-constexpr int kWideSB = 1;
+// ------------------------------------------------ projection, matrix cores --
+// B > 4.  Block: 16 rows of W (j0 ..) x 16 kTiles samples (b0 ..); its
+// kSplit waves split the 64 leaves: wave w takes leaves (64 / kSplit) w ..
+// for every (sample, row) of the block, one accumulator chain per sample
+// tile (the W operand is shared between them).  A lane (r = lane % 16,
+// g = lane / 16) feeds v_mfma_f64_16x16x4f64 with a[b0 + 16 t + r][48 l + 12 g
+// + s] and W[j0 + r][48 l + 12 g + s] at step s of leaf l: 24 contiguous bytes
+// of each per leaf, loaded two leaves ahead.  A wave adds its leaf results in
+// the leaf tree as they complete (in registers); the waves' subtrees meet in
+// LDS, pairwise in leaf order.  Rows past B load sample B - 1 and are never
+// stored.
+constexpr int kMfmaRows = 16;                               // rows of W per block
+constexpr int kLeafAhead = 2;                               // leaves in flight
 
-// kHaveA: `src` already holds a = bf16(SiLU(temb)) [B, 3072] (computed once
-// by silu_kernel); otherwise `src` is temb and every block computes the SiLU
-// of its samples (768-fold redundant, which the arithmetic-bound large-batch
-// case cannot hide).  a has the same bits either way.
-template <bool kHaveA>
-__global__ __launch_bounds__(kThreads) void proj_wide_kernel(const uint16_t* __restrict__ src,
-                                                             const uint16_t* __restrict__ W,
-                                                             const uint16_t* __restrict__ bias,
-                                                             uint16_t* __restrict__ emb, int64_t B) {
-  const uint16_t* __restrict__ temb = src;
-  constexpr int kStage = kWideBT * kChunks / kThreads;   // 12 chunks of 8 per thread
-  static_assert(kWideBT * kChunks % kThreads == 0, "staging layout");
-  __shared__ uint4 a_lds[kWideBT * kChunks];            // 48 KB
-  const int wave = threadIdx.x >> 6;
+template <int kTiles>
+struct LeafRaw {
+  uint32_t a[kTiles][6], w[6];   // 12 bf16 per operand (steps 0..11)
+};
+
+template <int kTiles, int kSplit>
+__global__ __launch_bounds__(64 * kSplit) void proj_mfma_kernel(const uint16_t* __restrict__ a,
+                                                                const uint16_t* __restrict__ W,
+                                                                const uint16_t* __restrict__ bias,
+                                                                uint16_t* __restrict__ emb, int64_t B) {
+  constexpr int kWaveLeaves = 64 / kSplit;
+  constexpr int kSamples = 16 * kTiles;
+  static_assert(kSplit == 1 || kSplit == 2 || kSplit == 4 || kSplit == 8, "leaf split");
+  __shared__ f64x4_t sub[kSplit > 1 ? kSplit - 1 : 1][kTiles][64];
+  // wave index through readfirstlane: the leaf offsets below stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
-  const int row0 = (static_cast<int>(blockIdx.x) * kWaves + wave) * kRows;
-  const int64_t b0 = static_cast<int64_t>(blockIdx.y) * kWideBT;
-  const int nb = static_cast<int>((B - b0) < kWideBT ? (B - b0) : kWideBT);
+  const int r = lane & 15, g = lane >> 4;
+  const int j0 = static_cast<int>(blockIdx.x) * kMfmaRows;
+  const int64_t bblk = static_cast<int64_t>(blockIdx.y) * kSamples;
+  const int rows_here = static_cast<int>((B - bblk) < kSamples ? (B - bblk) : kSamples);
 
-  uint4 tz[kStage];
+  const Buffer abuf(a + bblk * kD, static_cast<uint32_t>(rows_here) * kD * 2);
+  const Buffer wbuf(W + static_cast<int64_t>(j0) * kD, kMfmaRows * kD * 2);
+  uint32_t a_off[kTiles];
 #pragma unroll
-  for (int k = 0; k < kStage; ++k) {
-    const int c = threadIdx.x + kThreads * k;
-    if (c / kChunks < nb) tz[k] = ld16(temb + (b0 + c / kChunks) * kD + (c % kChunks) * 8);
+  for (int t = 0; t < kTiles; ++t) {
+    const int ra = (16 * t + r) < rows_here ? (16 * t + r) : rows_here - 1;
+    a_off[t] = static_cast<uint32_t>(ra) * kD * 2 + 24 * g;
   }
-  float bias_f[kRows];
-#pragma unroll
-  for (int r = 0; r < kRows; ++r) bias_f[r] = bf16_to_f32(bias[row0 + r]);
-  uint4 w[kLaneChunks][kRows];
-#pragma unroll
-  for (int i = 0; i < kLaneChunks; ++i)
-#pragma unroll
-    for (int r = 0; r < kRows; ++r)
-      w[i][r] = ld16(W + static_cast<int64_t>(row0 + r) * kD + (lane + 64 * i) * 8);
+  const uint32_t w_off = static_cast<uint32_t>(r) * kD * 2 + 24 * g;
+  const uint32_t leaf_base = static_cast<uint32_t>(wave * kWaveLeaves) * kLeafK * 2;
 
-  // SiLU into LDS one chunk at a time (a scheduling barrier per chunk keeps
-  // the temporaries of only one chunk live next to the W registers); the
-  // elements the fast path cannot decide are redone from memory afterwards
-  uint64_t redo[2] = {0, 0};
+  LeafRaw<kTiles> raw[kLeafAhead + 1];
+  auto load_leaf = [&](LeafRaw<kTiles>& d, int n) {
+    const uint32_t off = leaf_base + static_cast<uint32_t>(n) * kLeafK * 2;
 #pragma unroll
-  for (int k = 0; k < kStage; ++k) {
-    if (kHaveA) {
-      const int c = threadIdx.x + kThreads * k;
-      if (c / kChunks < nb) a_lds[c] = tz[k];
-      continue;
+    for (int q = 0; q < 3; ++q) {
+      const auto vw = __builtin_amdgcn_raw_buffer_load_b64(wbuf.rsrc, w_off, off + 8 * q, 0);
+      d.w[2 * q] = vw[0];
+      d.w[2 * q + 1] = vw[1];
     }
-    const int c = threadIdx.x + kThreads * k;
-    if (c / kChunks < nb) {
-      uint32_t m;
-      a_lds[c] = silu8_fast(tz[k], m);
-      redo[k / 8] |= static_cast<uint64_t>(m) << (8 * (k % 8));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    while (redo[h] != 0) {
-      const int bit = __builtin_ctzll(redo[h]);
-      redo[h] &= redo[h] - 1;
-      const int c = threadIdx.x + kThreads * (8 * h + bit / 8);
-      const int e = bit % 8;
-      reinterpret_cast<uint16_t*>(a_lds)[c * 8 + e] =
-          silu_bf16_exact(bf16_to_f32(temb[(b0 + c / kChunks) * kD + (c % kChunks) * 8 + e]));
-    }
-  }
-  __syncthreads();
-
-  // W unpacked to fp32 once (96 registers); then per group of samples the
-  // lane's partial per row, chunk-major as in proj_block, and the wave tree
-  float wf[kLaneChunks][kRows][8];
+    for (int t = 0; t < kTiles; ++t)
 #pragma unroll
-  for (int i = 0; i < kLaneChunks; ++i)
-#pragma unroll
-    for (int r = 0; r < kRows; ++r) unpack8(w[i][r], wf[i][r]);
-#pragma unroll 1
-  for (int s0 = 0; s0 < kWideBT; s0 += kWideSB) {
-    // kWideSB samples at a time: 2 * kWideSB independent fp64 chains per wave
-    // (one per sample and row) hide the add latency.  Slots past nb hold
-    // stale LDS data; their sums are never stored.
-    double acc[kWideSB][kRows];
-#pragma unroll
-    for (int q = 0; q < kWideSB; ++q)
-#pragma unroll
-      for (int r = 0; r < kRows; ++r) acc[q][r] = 0.0;
-#pragma unroll
-    for (int i = 0; i < kLaneChunks; ++i) {
-#pragma unroll
-      for (int q = 0; q < kWideSB; ++q) {
-        float av[8];
-        unpack8(a_lds[(s0 + q) * kChunks + lane + 64 * i], av);
-#pragma unroll
-        for (int r = 0; r < kRows; ++r)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[q][r] = mac_exact(av[e], wf[i][r][e], acc[q][r]);
+      for (int q = 0; q < 3; ++q) {
+        const auto va = __builtin_amdgcn_raw_buffer_load_b64(abuf.rsrc, a_off[t], off + 8 * q, 0);
+        d.a[t][2 * q] = va[0];
+        d.a[t][2 * q + 1] = va[1];
       }
+  };
+#pragma unroll
+  for (int n = 0; n < kLeafAhead; ++n) load_leaf(raw[n], n);
+
+  PairTree<ilog2(kWaveLeaves), f64x4_t> tree[kTiles];
+  static_for<0, kWaveLeaves>([&](auto nc) {
+    constexpr int n = decltype(nc)::value;
+    if constexpr (n + kLeafAhead < kWaveLeaves) load_leaf(raw[(n + kLeafAhead) % (kLeafAhead + 1)], n + kLeafAhead);
+    const LeafRaw<kTiles>& cur = raw[n % (kLeafAhead + 1)];
+    f64x4_t acc[kTiles];
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) acc[t] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int s = 0; s < kLeafSteps; ++s) {
+      const double wv = bf_half64(cur.w[s / 2], s & 1);
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t)
+        acc[t] = mfma_f64(bf_half64(cur.a[t][s / 2], s & 1), wv, acc[t]);
     }
 #pragma unroll
-    for (int q = 0; q < kWideSB; ++q) {
+    for (int t = 0; t < kTiles; ++t) tree[t].template push<n>(acc[t]);
+  });
+  constexpr int kTop = ilog2(kWaveLeaves);
+
+  // subtrees of the waves, pairwise in leaf order: ((w0 + w1) + (w2 + w3)) ...
+  f64x4_t tot[kTiles];
 #pragma unroll
-      for (int r = 0; r < kRows; ++r) {
-        const double tot = wave_sum_f64(acc[q][r]);
-        if (lane == r && s0 + q < nb) {
-          const float v = static_cast<float>(tot) + bias_f[r];
-          emb[(b0 + s0 + q) * kN + row0 + r] = f32_to_bf16(v);
-        }
-      }
+  for (int t = 0; t < kTiles; ++t) tot[t] = tree[t].node[kTop];
+  if constexpr (kSplit > 1) {
+    if (wave > 0)
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) sub[wave - 1][t][lane] = tot[t];
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+      f64x4_t v[kSplit];
+      v[0] = tot[t];
+#pragma unroll
+      for (int w = 1; w < kSplit; ++w) v[w] = sub[w - 1][t][lane];
+      tot[t] = pair_reduce(v);
     }
   }
+  // lane holds rows g + 4 v of each sample tile, column r (row j0 + r of W)
+  const float bias_f = bf16_to_f32(bias[j0 + r]);
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int sr = 16 * t + g + 4 * v;
+      if (sr < rows_here)
+        emb[(bblk + sr) * kN + j0 + r] = f32_to_bf16(static_cast<float>(tot[t][v]) + bias_f);
+    }
 }
 
 // ------------------------------------------------------------ LayerNorm ----
@@ -424,7 +471,7 @@ __global__ __launch_bounds__(kThreads) void norm_modulate_kernel(
   modulate(xv, mu, rs, m_lds, sh_lds, out + row * kD, lane);
 }
 
-// B <= 4: proj_block with NB = B; larger batches: proj_wide_kernel
+// B <= 4: proj_block with NB = B; larger batches: proj_mfma_kernel
 template <typename F>
 hipError_t by_batch(int64_t B, F&& f) {
   switch (B) {
@@ -436,29 +483,28 @@ hipError_t by_batch(int64_t B, F&& f) {
   }
 }
 
-hipError_t launch_wide(const uint16_t* temb, const uint16_t* W, const uint16_t* bias, uint16_t* emb,
-                       int64_t B, hipStream_t s) {
-  const int64_t by = (B + kWideBT - 1) / kWideBT;
-  hipLaunchKernelGGL(proj_wide_kernel<false>, dim3(kProjBlocks, static_cast<unsigned>(by)), dim3(kThreads), 0,
-                     s, temb, W, bias, emb, B);
+// a = bf16(SiLU(temb)) computed once into `a`, then the matrix-core
+// projection: one sample tile per wave up to 16 samples, two beyond
+constexpr int kMfmaSplit = 4;
+template <int kTiles>
+hipError_t launch_mfma_tiles(const uint16_t* a, const uint16_t* W, const uint16_t* bias, uint16_t* emb,
+                             int64_t B, hipStream_t s) {
+  const int64_t by = (B + 16 * kTiles - 1) / (16 * kTiles);
+  hipLaunchKernelGGL((proj_mfma_kernel<kTiles, kMfmaSplit>), dim3(kN / kMfmaRows, static_cast<unsigned>(by)),
+                     dim3(64 * kMfmaSplit), 0, s, a, W, bias, emb, B);
   return hipGetLastError();
 }
-
-// a = bf16(SiLU(temb)) computed once into `a`, then the projection from it
-hipError_t launch_wide_from_a(const uint16_t* temb, uint16_t* a, const uint16_t* W, const uint16_t* bias,
-                              uint16_t* emb, int64_t B, hipStream_t s) {
+hipError_t launch_mfma(const uint16_t* temb, uint16_t* a, const uint16_t* W, const uint16_t* bias,
+                       uint16_t* emb, int64_t B, hipStream_t s) {
   if (hipError_t e = launch_silu(temb, a, B * kD, s); e != hipSuccess) return e;
-  const int64_t by = (B + kWideBT - 1) / kWideBT;
-  hipLaunchKernelGGL(proj_wide_kernel<true>, dim3(kProjBlocks, static_cast<unsigned>(by)), dim3(kThreads), 0,
-                     s, a, W, bias, emb, B);
-  return hipGetLastError();
+  return B <= 16 ? launch_mfma_tiles<1>(a, W, bias, emb, B, s) : launch_mfma_tiles<2>(a, W, bias, emb, B, s);
 }
 
 }  // namespace
 
 hipError_t launch_proj_fwd(const uint16_t* temb, const uint16_t* W, const uint16_t* bias,
-                           uint16_t* emb, int64_t B, hipStream_t s) {
-  if (B > kMaxNarrowBatch) return launch_wide(temb, W, bias, emb, B, s);
+                           uint16_t* emb, uint16_t* a, int64_t B, hipStream_t s) {
+  if (B > kMaxNarrowBatch) return launch_mfma(temb, a, W, bias, emb, B, s);
   return by_batch(B, [&](auto nb) {
     hipLaunchKernelGGL(proj_fwd_kernel<decltype(nb)::value>, dim3(kProjBlocks), dim3(kThreads), 0, s, temb,
                        W, bias, emb);
@@ -478,10 +524,10 @@ hipError_t launch_fwd(const uint16_t* temb, const uint16_t* W, const uint16_t* b
                       const uint16_t* x, uint16_t* emb, uint16_t* out, float* mean, float* rstd,
                       int64_t B, int64_t S, float eps, hipStream_t s) {
   if (B > kMaxNarrowBatch) {
-    // the projection is arithmetic-bound here: SiLU once (into the first
-    // B * 3072 elements of `out`, which the modulation overwrites later),
-    // the projection, then statistics and modulation in one pass over x
-    if (hipError_t e = launch_wide_from_a(temb, out, W, bias, emb, B, s); e != hipSuccess) return e;
+    // SiLU once (into the first B * 3072 elements of `out`, which the
+    // modulation overwrites later), the matrix-core projection, then
+    // statistics and modulation in one pass over x
+    if (hipError_t e = launch_mfma(temb, out, W, bias, emb, B, s); e != hipSuccess) return e;
     return launch_norm_mod_fwd(x, emb, out, mean, rstd, B, S, eps, s);
   }
   const int64_t stat_blocks = (B * S + kWaves - 1) / kWaves;

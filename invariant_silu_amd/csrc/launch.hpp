@@ -12,7 +12,7 @@ hipError_t launch_fwd(const uint16_t* temb, const uint16_t* W, const uint16_t* b
                       const uint16_t* x, uint16_t* emb, uint16_t* out, float* mean, float* rstd,
                       int64_t B, int64_t S, float eps, hipStream_t s);
 hipError_t launch_proj_fwd(const uint16_t* temb, const uint16_t* W, const uint16_t* bias,
-                           uint16_t* emb, int64_t B, hipStream_t s);
+                           uint16_t* emb, uint16_t* a, int64_t B, hipStream_t s);
 hipError_t launch_norm_mod_fwd(const uint16_t* x, const uint16_t* emb, uint16_t* out,
                                float* mean, float* rstd, int64_t B, int64_t S, float eps,
                                hipStream_t s);

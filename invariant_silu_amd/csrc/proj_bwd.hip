@@ -1,22 +1,27 @@
 // Projection backward of the AdaLN final modulation (RL-Kernel pull request
 // 538, "What"; SiLU VJP per the review thread), from the fp32
 // d_emb = (d_scale | d_shift):
-//   dW[j,k]  = bf16(fl32(sum_b d_emb[b,j] * a[b,k]))      (fp32 products)
+//   dW[j,k]  = bf16(fl32(sum_b d_emb[b,j] * a[b,k]))
 //   db[j]    = bf16(fl32(sum_b d_emb[b,j]))
-//   da[b,k]  = fl32(sum_j d_emb[b,j] * W[j,k])             (fp32 products)
+//   da[b,k]  = fl32(sum_j d_emb[b,j] * W[j,k])
 //   dtemb    = bf16(da * silu'(temb))
-// Sums accumulate fp32 products in fp64 in fixed orders: samples ascending
-// for dW and db; for da, 128 row slots (slot t: rows t, t + 128, ... in
-// order) added as a pairwise tree.  Device pieces are shared by every
-// kernel, so every entry point computes identical bits, and no order depends
-// on the batch size or the grid.
+// Every product is exact (an fp64 fused multiply-add of the fp32 and bf16
+// operands) and the sums run in fp64 in fixed orders:
+//   dW: samples ascending from +0, one fused multiply-add each;
+//   db: samples ascending from +0 (plain adds);
+//   da: 128 leaves, leaf t over rows t, t + 128, ..., t + 128 * 47 in that
+//       order from +0; then the leaves added pairwise in index order.
+// The vector-unit kernels (B <= 4) and the matrix-core kernels (B > 4; a
+// v_mfma_f64_16x16x4f64 is that same chain of four fused multiply-adds) run
+// these orders exactly, so no result depends on the batch size or the grid.
 //
 // Kernels:
 //   proj_bwd_small_kernel<NB>  B <= 4: da column blocks (-> dtemb) and dW
 //                              tiles (-> dW, db) in one grid
-//   silu_kernel, proj_bwd_dw_kernel, proj_bwd_da_kernel   B > 4
+//   silu_kernel, dw_mfma_kernel, da_mfma_kernel   B > 4
 #include "common.hpp"
 #include "launch.hpp"
+#include "mfma.hpp"
 
 namespace adaln {
 
@@ -42,9 +47,8 @@ static_assert(kD % kTileCols == 0, "column blocks");
 static_assert(kBlockThreads == kThreads, "one block size for every role");
 
 // da blocks: 16 columns of W over all 6144 rows, so each block finishes the
-// sum and writes dtemb itself.  128 row slots, slot t walks rows t, t + 128,
-// ... in order (fp64 accumulation of fp32 products); the 128 slots are then
-// added as a pairwise tree.  The four 32-byte quarters of a 128-byte row
+// sum and writes dtemb itself.  128 row slots, slot t = leaf t: rows t,
+// t + 128, ... in order; the 128 slots are then added as a pairwise tree.  The four 32-byte quarters of a 128-byte row
 // segment go to blocks L, L + 8, L + 16 and L + 24, which the dispatcher
 // places on the same XCD (one L2 serves all four).
 constexpr int kDaCols = 16;
@@ -55,6 +59,7 @@ constexpr int kDaSteps = kN / kDaSlots;               // 48 rows per thread
 constexpr int kDaShare = 128 / (kDaCols * 2);         // blocks sharing a 128-byte segment: 4
 
 static_assert(kDaBlocks % (8 * kDaShare) == 0, "da block to column mapping");
+static_assert(kDaSteps == 48, "a slot is one leaf of 48 rows");
 
 __device__ __forceinline__ int da_first_col(int L) {
   const int g = L / (8 * kDaShare), q = (L / 8) % kDaShare, xcd = L % 8;
@@ -103,9 +108,11 @@ __device__ __forceinline__ void da_block(const float* __restrict__ d_emb, const 
       float wf[8];
       unpack8(w[u], wf);
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+      for (int b = 0; b < NB; ++b) {
+        const double dd = static_cast<double>(d[u][b]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[b][e] += static_cast<double>(d[u][b] * wf[e]);
+        for (int e = 0; e < 8; ++e) acc[b][e] = __builtin_fma(dd, static_cast<double>(wf[e]), acc[b][e]);
+      }
     }
   };
 
@@ -217,7 +224,8 @@ __device__ __forceinline__ void dw_tile(const float* __restrict__ d_emb,
     for (int e = 0; e < 8; ++e) {
       double s = 0.0;
 #pragma unroll
-      for (int b = 0; b < NB; ++b) s += static_cast<double>(de_lds[b][jl] * av[b][e]);
+      for (int b = 0; b < NB; ++b)
+        s = __builtin_fma(static_cast<double>(de_lds[b][jl]), static_cast<double>(av[b][e]), s);
       o[e] = static_cast<float>(s);
     }
     st16_nt(dW + static_cast<int64_t>(jbase + jl) * kD + col, pack8(o));
@@ -261,89 +269,203 @@ __global__ __launch_bounds__(256) void silu_kernel(const uint16_t* __restrict__ 
   }
 }
 
-// ---- B > 4 ------------------------------------------------------------------
-// dW tile of 32 rows x 256 columns per block; samples staged through LDS 64 at
-// a time (a: 32 KB, d_emb: 8 KB).  Thread (ct, rg) owns rows 4 rg .. 4 rg + 3
-// and columns 8 ct .. 8 ct + 7: 32 fp64 sums, samples in ascending order.
-// Blocks of column block 0 also sum db for their rows.
-constexpr int kDwBRows = 32;
-constexpr int kDwBCols = 256;
-constexpr int kDwBSamples = 64;
-constexpr int kDwBLoads = kDwBSamples * (kDwBCols / 8) / kThreads;   // 8 chunk loads per thread
-static_assert(kDwBSamples * kDwBRows / kThreads == kDwBLoads, "staging layout");
+// ---- B > 4: matrix cores ----------------------------------------------------
+// dW: a wave computes 64 rows x 16 kCT columns as 4 x kCT output tiles; tile
+// (m, n) holds rows j0 + 4 i + m and columns k0 + kCT c + n (i, c = 0 .. 15),
+// so a lane's operands per sample are 16 contiguous bytes of d_emb (4 rows)
+// and 2 kCT contiguous bytes of a (kCT columns).  Step s feeds samples
+// 4 s .. 4 s + 3 (slot g = sample 4 s + g): each sum is the chain over samples
+// in ascending order from +0, as in dw_tile.  Samples past B enter with
+// d_emb = 0, which leaves every sum unchanged (the chain never holds -0).
+// Waves of column block 0 also sum db for their 64 rows.
+constexpr int kDwMRows = 64;
+constexpr int kDwMWaves = 4;
 
-__global__ __launch_bounds__(kThreads) void proj_bwd_dw_kernel(const float* __restrict__ d_emb,
-                                                               const uint16_t* __restrict__ a,
-                                                               uint16_t* __restrict__ dW,
-                                                               uint16_t* __restrict__ db, int64_t B) {
-  __shared__ uint4 a_lds[kDwBSamples][kDwBCols / 8];   // 32 KB
-  __shared__ __align__(16) float d_lds[kDwBSamples][kDwBRows];   // 8 KB
-  const int ct = threadIdx.x % (kDwBCols / 8);
-  const int rg = threadIdx.x / (kDwBCols / 8);
-  const int j0 = blockIdx.x * kDwBRows;
-  const int k0 = blockIdx.y * kDwBCols;
-  double acc[4][8];
+template <int kCT>
+__global__ __launch_bounds__(64 * kDwMWaves) void dw_mfma_kernel(const float* __restrict__ d_emb,
+                                                                 const uint16_t* __restrict__ a,
+                                                                 uint16_t* __restrict__ dW,
+                                                                 uint16_t* __restrict__ db, int64_t B) {
+  constexpr int kCols = 16 * kCT;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int j0 = static_cast<int>(blockIdx.x) * kDwMRows;
+  const int k0 = (static_cast<int>(blockIdx.y) * kDwMWaves + wave) * kCols;
+  const int64_t steps = (B + 3) / 4;
+
+  f64x4_t acc[4][kCT];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[r][e] = 0.0;
-  double dbs = 0.0;
-  for (int64_t c0 = 0; c0 < B; c0 += kDwBSamples) {
-    const int nb = static_cast<int>((B - c0) < kDwBSamples ? (B - c0) : kDwBSamples);
-    // unconditional loads (slots past nb repeat sample nb - 1 and are unused)
-    uint4 av_r[kDwBLoads];
-    float d_r[kDwBLoads];
-#pragma unroll
-    for (int u = 0; u < kDwBLoads; ++u) {
-      const int idx = threadIdx.x + kThreads * u;
-      const int sa = idx / (kDwBCols / 8) < nb ? idx / (kDwBCols / 8) : nb - 1;
-      av_r[u] = ld16(a + (c0 + sa) * kD + k0 + (idx % (kDwBCols / 8)) * 8);
-      const int sd = idx / kDwBRows < nb ? idx / kDwBRows : nb - 1;
-      d_r[u] = d_emb[(c0 + sd) * kN + j0 + idx % kDwBRows];
+    for (int n = 0; n < kCT; ++n) acc[m][n] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+
+  const float* dp = d_emb + j0 + 4 * r;
+  const uint16_t* ap = a + k0 + kCT * r;
+  auto load = [&](int64_t st, float4& dv, uint32_t (&av)[(kCT + 1) / 2]) {
+    const int64_t b = 4 * st + g;
+    const int64_t bc = b < B ? b : B - 1;
+    dv = *reinterpret_cast<const float4*>(dp + bc * kN);
+    if constexpr (kCT == 4) {
+      const uint2 v = *reinterpret_cast<const uint2*>(ap + bc * kD);
+      av[0] = v.x;
+      av[1] = v.y;
+    } else {
+      av[0] = *reinterpret_cast<const uint32_t*>(ap + bc * kD);
     }
-    __syncthreads();   // the previous chunk is consumed
+    if (b >= B) dv = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  };
+  auto step = [&](const float4& dv, const uint32_t (&av)[(kCT + 1) / 2]) {
+    const double dd[4] = {static_cast<double>(dv.x), static_cast<double>(dv.y), static_cast<double>(dv.z),
+                          static_cast<double>(dv.w)};
+    double aa[kCT];
 #pragma unroll
-    for (int u = 0; u < kDwBLoads; ++u) {
-      const int idx = threadIdx.x + kThreads * u;
-      a_lds[idx / (kDwBCols / 8)][idx % (kDwBCols / 8)] = av_r[u];
-      d_lds[idx / kDwBRows][idx % kDwBRows] = d_r[u];
-    }
-    __syncthreads();
-    if (blockIdx.y == 0 && threadIdx.x < kDwBRows)
-      for (int b = 0; b < nb; ++b) dbs += static_cast<double>(d_lds[b][threadIdx.x]);
-#pragma unroll 2
-    for (int b = 0; b < nb; ++b) {
-      float av[8];
-      unpack8(a_lds[b][ct], av);
-      const float4 d4 = *reinterpret_cast<const float4*>(&d_lds[b][rg * 4]);
-      const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+    for (int n = 0; n < kCT; ++n) aa[n] = bf_half64(av[n / 2], n & 1);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[r][e] += static_cast<double>(dd[r] * av[e]);
-    }
+      for (int n = 0; n < kCT; ++n) acc[m][n] = mfma_f64(dd[m], aa[n], acc[m][n]);
+  };
+  float4 d0, d1;
+  uint32_t a0[(kCT + 1) / 2], a1[(kCT + 1) / 2];
+  load(0, d0, a0);
+  int64_t st = 0;
+  for (; st + 2 <= steps; st += 2) {
+    load(st + 1, d1, a1);
+    step(d0, a0);
+    load(st + 2 < steps ? st + 2 : st + 1, d0, a0);
+    step(d1, a1);
   }
+  if (st < steps) step(d0, a0);
+
+  // lane holds rows j0 + 4 (g + 4 v) + m, columns k0 + kCT r + n
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float o[8];
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = static_cast<float>(acc[r][e]);
-    st16_nt(dW + static_cast<int64_t>(j0 + rg * 4 + r) * kD + k0 + ct * 8, pack8(o));
+    for (int v = 0; v < 4; ++v) {
+      uint16_t* o = dW + static_cast<int64_t>(j0 + 4 * (g + 4 * v) + m) * kD + k0 + kCT * r;
+      if constexpr (kCT == 4) {
+        *reinterpret_cast<uint2*>(o) = make_uint2(
+            pack_bf16x2(static_cast<float>(acc[m][0][v]), static_cast<float>(acc[m][1][v])),
+            pack_bf16x2(static_cast<float>(acc[m][2][v]), static_cast<float>(acc[m][3][v])));
+      } else {
+        *reinterpret_cast<uint32_t*>(o) =
+            pack_bf16x2(static_cast<float>(acc[m][0][v]), static_cast<float>(acc[m][1][v]));
+      }
+    }
+  if (blockIdx.y == 0 && wave == 0) {
+    double sdb = 0.0;
+    for (int64_t b = 0; b < B; ++b) sdb += static_cast<double>(d_emb[b * kN + j0 + lane]);
+    db[j0 + lane] = f32_to_bf16(static_cast<float>(sdb));
   }
-  if (blockIdx.y == 0 && threadIdx.x < kDwBRows) db[j0 + threadIdx.x] = f32_to_bf16(static_cast<float>(dbs));
 }
 
-// da and dtemb, 4 samples per blockIdx.y
-__global__ __launch_bounds__(kThreads) void proj_bwd_da_kernel(const float* __restrict__ d_emb,
-                                                               const uint16_t* __restrict__ W,
-                                                               const uint16_t* __restrict__ temb,
-                                                               uint16_t* __restrict__ dtemb, int64_t B) {
-  __shared__ __align__(16) double red[kDaSlots * kBatchChunk * kDaCols];   // 64 KB
-  const int64_t b0 = static_cast<int64_t>(blockIdx.y) * kBatchChunk;
-  const int nb = static_cast<int>((B - b0) < kBatchChunk ? (B - b0) : kBatchChunk);
-  da_block<kBatchChunk>(d_emb, W, temb, dtemb, blockIdx.x, b0, nb, red);
-}
+// da and dtemb: block of 16 samples (b0 ..) x 32 columns (k0 ..), 8 waves;
+// wave w takes leaves 16 w .. 16 w + 15 in four groups of four consecutive
+// leaves t0 .. t0 + 3, run side by side (8 chains: 4 leaves x 2 column
+// tiles).  Step s of a leaf feeds rows t + 128 (4 s + g) at slot g, so a
+// leaf's 12 steps are its 48 rows in order.  Output tile n (0, 1) holds
+// columns k0 + 2 c + n.  Lane (r, g) loads d_emb[b0 + r][t0 + 128 (4 s + g)
+// .. + 3] (16 bytes: the four leaves) and W[t0 + l + 128 (4 s + g)][k0 + 2 r ..
+// + 1] for l = 0 .. 3.  Leaf results go into the wave's leaf tree in order;
+// the 8 subtrees meet in LDS, pairwise in leaf order.  Blocks x and x + 8
+// (same XCD) take the two halves of one 128-byte row segment of W.  Rows
+// past B load sample B - 1 and are never stored.
+constexpr int kLeafSteps = 12;   // 48 rows of a leaf, 4 per matrix-core step
+constexpr int kDaMWaves = 8;
+constexpr int kDaMLeaves = 128 / kDaMWaves;    // 16 per wave
+constexpr int kDaMGroup = 4;                   // leaves run side by side
+constexpr int kDaMCols = 32;
+constexpr int kDaMAhead = 2;                   // steps in flight
 
+struct DaStep {
+  uint4 d;          // d_emb of the group's 4 leaves
+  uint32_t w[4];    // W, 2 columns, per leaf
+};
+
+__global__ __launch_bounds__(64 * kDaMWaves) void da_mfma_kernel(const float* __restrict__ d_emb,
+                                                                 const uint16_t* __restrict__ W,
+                                                                 const uint16_t* __restrict__ temb,
+                                                                 uint16_t* __restrict__ dtemb, int64_t B) {
+  __shared__ f64x4_t sub[kDaMWaves - 1][2][64];   // 28 KB
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int x = blockIdx.x;
+  const int k0 = ((x / 16) * 8 + x % 8) * 64 + ((x / 8) % 2) * kDaMCols;
+  const int64_t b0 = static_cast<int64_t>(blockIdx.y) * 16;
+  const int rows_here = static_cast<int>((B - b0) < 16 ? (B - b0) : 16);
+  const int br = r < rows_here ? r : rows_here - 1;
+
+  const Buffer eb(d_emb + b0 * kN, static_cast<uint32_t>(rows_here) * kN * 4);
+  const Buffer wbuf(W, static_cast<uint32_t>(kN) * kD * 2);
+  const uint32_t e_off = (static_cast<uint32_t>(br) * kN + kDaSlots * g) * 4;
+  const uint32_t w_off = (static_cast<uint32_t>(kDaSlots * g) * kD + k0 + 2 * r) * 2;
+  const int leaf0 = wave * kDaMLeaves;
+
+  PairTree<ilog2(kDaMLeaves), f64x4_t> tree[2];
+  static_for<0, kDaMLeaves / kDaMGroup>([&](auto qc) {
+    constexpr int q = decltype(qc)::value;
+    const int t0 = leaf0 + kDaMGroup * q;
+    auto load = [&](DaStep& d, int st) {
+      const uint32_t row = static_cast<uint32_t>(t0 + kDaSlots * 4 * st);   // + 128 g in the lane offset
+      d.d = eb.u128(e_off, row * 4);
+#pragma unroll
+      for (int l = 0; l < kDaMGroup; ++l) d.w[l] = wbuf.u32(w_off, (row + l) * kD * 2);
+    };
+    DaStep buf[kDaMAhead + 1];
+#pragma unroll
+    for (int st = 0; st < kDaMAhead; ++st) load(buf[st], st);
+    f64x4_t acc[kDaMGroup][2];
+#pragma unroll
+    for (int l = 0; l < kDaMGroup; ++l) acc[l][0] = acc[l][1] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int st = 0; st < kLeafSteps; ++st) {
+      if (st + kDaMAhead < kLeafSteps) load(buf[(st + kDaMAhead) % (kDaMAhead + 1)], st + kDaMAhead);
+      const DaStep& cur = buf[st % (kDaMAhead + 1)];
+      const uint32_t dv[4] = {cur.d.x, cur.d.y, cur.d.z, cur.d.w};
+#pragma unroll
+      for (int l = 0; l < kDaMGroup; ++l) {
+        const double dd = static_cast<double>(__uint_as_float(dv[l]));
+        acc[l][0] = mfma_f64(dd, bf_lo64(cur.w[l]), acc[l][0]);
+        acc[l][1] = mfma_f64(dd, bf_hi64(cur.w[l]), acc[l][1]);
+      }
+    }
+    static_for<0, kDaMGroup>([&](auto lc) {
+      constexpr int l = decltype(lc)::value;
+      tree[0].template push<kDaMGroup * q + l>(acc[l][0]);
+      tree[1].template push<kDaMGroup * q + l>(acc[l][1]);
+    });
+  });
+  constexpr int kTop = ilog2(kDaMLeaves);
+  if (wave > 0) {
+    sub[wave - 1][0][lane] = tree[0].node[kTop];
+    sub[wave - 1][1][lane] = tree[1].node[kTop];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+  f64x4_t tot[2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    f64x4_t v[kDaMWaves];
+    v[0] = tree[n].node[kTop];
+#pragma unroll
+    for (int w = 1; w < kDaMWaves; ++w) v[w] = sub[w - 1][n][lane];
+    tot[n] = pair_reduce(v);
+  }
+  // lane holds samples b0 + g + 4 v, columns k0 + 2 r + n
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int sr = g + 4 * v;
+    if (sr < rows_here) {
+      const int64_t i = (b0 + sr) * kD + k0 + 2 * r;
+      const uint32_t z = *reinterpret_cast<const uint32_t*>(temb + i);
+      *reinterpret_cast<uint32_t*>(dtemb + i) =
+          pack_bf16x2(static_cast<float>(tot[0][v]) * dsilu_f32(bf_lo(z)),
+                      static_cast<float>(tot[1][v]) * dsilu_f32(bf_hi(z)));
+    }
+  }
+}
 
 }  // namespace
 
@@ -364,15 +486,16 @@ hipError_t launch_proj_bwd_fused(const float* d_emb, const uint16_t* temb, const
 
 hipError_t launch_proj_bwd_dw(const float* d_emb, const uint16_t* a, uint16_t* dW, uint16_t* db, int64_t B,
                               hipStream_t s) {
-  hipLaunchKernelGGL(proj_bwd_dw_kernel, dim3(kN / kDwBRows, kD / kDwBCols), dim3(kThreads), 0, s, d_emb, a,
-                     dW, db, B);
+  constexpr int kCT = 2;
+  hipLaunchKernelGGL(dw_mfma_kernel<kCT>, dim3(kN / kDwMRows, kD / (16 * kCT * kDwMWaves)),
+                     dim3(64 * kDwMWaves), 0, s, d_emb, a, dW, db, B);
   return hipGetLastError();
 }
 
 hipError_t launch_proj_bwd_da(const float* d_emb, const uint16_t* W, const uint16_t* temb, uint16_t* dtemb,
                               int64_t B, hipStream_t s) {
-  const int64_t bz = (B + kBatchChunk - 1) / kBatchChunk;
-  hipLaunchKernelGGL(proj_bwd_da_kernel, dim3(kDaBlocks, static_cast<unsigned>(bz)), dim3(kThreads), 0, s,
+  const int64_t by = (B + 15) / 16;
+  hipLaunchKernelGGL(da_mfma_kernel, dim3(kD / kDaMCols, static_cast<unsigned>(by)), dim3(64 * kDaMWaves), 0, s,
                      d_emb, W, temb, dtemb, B);
   return hipGetLastError();
 }

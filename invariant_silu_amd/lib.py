@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libadaln.so")
 
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DEVICE, ERR_WORKSPACE, ERR_OVERLAP, ERR_LAUNCH = range(-1, -8, -1)
-OP_NORM_MOD_BWD, OP_PROJ_BWD, OP_TOKEN_TREE_SUM, OP_BWD = 2, 3, 4, 5
+OP_PROJ_FWD, OP_NORM_MOD_BWD, OP_PROJ_BWD, OP_TOKEN_TREE_SUM, OP_BWD = 1, 2, 3, 4, 5
 
 EXPORTS = ("adaln_fwd", "adaln_bwd", "adaln_proj_fwd", "adaln_norm_mod_fwd", "adaln_norm_mod_bwd", "adaln_proj_bwd",
            "token_tree_sum", "adaln_norm_mod_bwd_dx", "adaln_norm_mod_bwd_tiles", "token_tree_fold",
@@ -28,7 +28,7 @@ _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _SZ = ctypes.c_size_t
 _SIGS = {
-    "adaln_proj_fwd": ([_P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "adaln_proj_fwd": ([_P, _P, _P, _P, _P, _SZ, _I64, _I64, _I64, _P], ctypes.c_int),
     "adaln_fwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_float, _P], ctypes.c_int),
     "adaln_bwd": ([_P] * 13 + [_SZ, _I64, _I64, _I64, _P], ctypes.c_int),
     "adaln_norm_mod_fwd": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_float, _P], ctypes.c_int),

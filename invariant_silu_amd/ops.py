@@ -53,8 +53,9 @@ def proj_fwd(temb: torch.Tensor, W: torch.Tensor, bias: torch.Tensor) -> torch.T
     temb, W, bias = aligned(temb), aligned(W), aligned(bias)
     B = temb.shape[0]
     emb = torch.empty((B, N), dtype=torch.bfloat16, device=temb.device)
+    ws = _ws(_lib.OP_PROJ_FWD, B, 1, temb.shape[1], temb.device)
     _lib.call("adaln_proj_fwd", temb.data_ptr(), W.data_ptr(), bias.data_ptr(), emb.data_ptr(),
-              B, temb.shape[1], W.shape[0], _stream(temb.device))
+              ws.data_ptr(), ws.numel(), B, temb.shape[1], W.shape[0], _stream(temb.device))
     return emb
 
 

@@ -32,9 +32,16 @@ Readings where the pages leave a step open:
     alpha = sum(gy)/D, beta = sum(gy * n)/D; dx = bf16(rstd*((gy-alpha)-n*beta)).
     The gradient passes straight through the bf16 rounding of (1 + scale):
     d_scale = sum_s g * n, d_shift = sum_s g, both kept in fp32.
-  * Projection backward from the fp32 d_emb: da = sum_j d_emb_j * W_jk (fp32
-    products), dtemb = bf16(da * silu'(z)), dW = bf16(sum_b d_emb_bj * a_bk),
+  * Projection backward from the fp32 d_emb: da = sum_j d_emb_j * W_jk,
+    dtemb = bf16(da * silu'(z)), dW = bf16(sum_b d_emb_bj * a_bk),
     db = bf16(sum_b d_emb_bj).
+  * Every product of the projection, forward and backward, is exact: the
+    pages give the projection as a fixed-order GPU kernel accumulating in
+    fp32, where a * b + acc is a fused multiply-add (one rounding), and say
+    nothing of rounding a product on its own.  In fp32 mode each product
+    enters the sum as two fp32 terms whose sum is the product (its fp32
+    rounding and the exact remainder); bf16 x bf16 products are exact in
+    fp32 anyway, so this changes only the backward's fp32 x bf16 products.
 
 Arithmetic modes:
   "fp32"  the oracle proper: every operation an IEEE float32 operation, every
@@ -85,6 +92,19 @@ class Arith:
     def sum(self, terms, shape, want_abs=False):
         return nsum_stream(terms, shape, self.dt, want_abs)
 
+    def prod(self, x, y):
+        """The terms of the exact products x * y (fp32 or bf16 operands).
+
+        float64 holds such a product exactly (at most 48 significant bits), so
+        the fp64 and exact modes yield it as one term.  In fp32 mode it is
+        yielded as hi = fp32(p) and lo = p - hi, both exact in fp32 (lo has
+        at most 24 significant bits) unless |p| is below about 2^-100."""
+        p = np.asarray(x, np.float64) * np.asarray(y, np.float64)
+        if self.mode != "fp32":
+            return (p,)
+        hi = p.astype(np.float32)
+        return (hi, (p - hi.astype(np.float64)).astype(np.float32))
+
 
 def _silu64(z):
     return z / (1.0 + np.exp(-z))
@@ -125,7 +145,7 @@ def projection(a, W, bias, ar: Arith, want_abs=False):
     a = ar.c(a)
     B, K = a.shape
     N = WT.shape[1]
-    terms = (a[:, k:k + 1] * WT[k][None, :] for k in range(K))
+    terms = (t for k in range(K) for t in ar.prod(a[:, k:k + 1], WT[k][None, :]))
     r = ar.sum(terms, (B, N), want_abs)
     acc, A = (r if want_abs else (r, None))
     emb = ar.bf16(acc + bias)
@@ -214,19 +234,9 @@ def backward(inp: dict, fwd: dict, mode: str = "fp32", want_abs: bool = False,
     d_emb = np.concatenate([d_scale, d_shift], axis=1)                 # [B, 2D]
 
     W = ar.c(_val(inp, "W"))                                           # [N, K]
-    N, K = W.shape
-    r3 = ar.sum((d_emb[:, j:j + 1] * W[j][None, :] for j in range(N)), (B, K), want_abs)
-    da, A_da = r3 if want_abs else (r3, None)
-    ds = dsilu(_val(inp, "temb"), ar)
-    dtemb = ar.bf16(da * ds)
-
-    a = fwd["a"]
-    r4 = ar.sum((d_emb[b][:, None] * a[b][None, :] for b in range(B)), (N, K), want_abs)
-    dW_acc, A_dW = r4 if want_abs else (r4, None)
-    dW = ar.bf16(dW_acc)
-    r5 = ar.sum((d_emb[b] for b in range(B)), (N,), want_abs)
-    db_acc, A_db = r5 if want_abs else (r5, None)
-    db = ar.bf16(db_acc)
+    pb = proj_backward(d_emb, fwd["a"], W, _val(inp, "temb"), ar, want_abs)
+    da, dtemb, dW_acc, dW, db_acc, db = (pb[k] for k in ("da", "dtemb", "dW_acc", "dW", "db_acc", "db"))
+    A_da, A_dW, A_db = pb.get("A_da"), pb.get("A_dW"), pb.get("A_db")
 
     res = dict(dx=dx, d_scale=d_scale, d_shift=d_shift, d_emb=d_emb, da=da,
                dtemb=dtemb, dW=dW, db=db, dW_acc=dW_acc, db_acc=db_acc,
@@ -236,6 +246,26 @@ def backward(inp: dict, fwd: dict, mode: str = "fp32", want_abs: bool = False,
             res[k + "_bits"] = _bits(res[k])
     if want_abs:
         res["A_d_emb"] = np.concatenate([A_scale, A_shift], axis=1)
+        res.update(A_da=A_da, A_dW=A_dW, A_db=A_db)
+    return res
+
+
+def proj_backward(d_emb, a, W, temb, ar: Arith, want_abs: bool = False) -> dict:
+    """Projection backward from d_emb [B, N] (fp32 values), a [B, K] (bf16
+    values), W [N, K] and temb [B, K]: da, dtemb = bf16(da * silu'(temb)),
+    dW = bf16(sum_b d_emb_b x a_b), db = bf16(sum_b d_emb_b), every product exact."""
+    d_emb, a, W = ar.c(d_emb), ar.c(a), ar.c(W)
+    B, N = d_emb.shape
+    K = W.shape[1]
+    r3 = ar.sum((t for j in range(N) for t in ar.prod(d_emb[:, j:j + 1], W[j][None, :])), (B, K), want_abs)
+    da, A_da = r3 if want_abs else (r3, None)
+    dtemb = ar.bf16(da * dsilu(temb, ar))
+    r4 = ar.sum((t for b in range(B) for t in ar.prod(d_emb[b][:, None], a[b][None, :])), (N, K), want_abs)
+    dW_acc, A_dW = r4 if want_abs else (r4, None)
+    r5 = ar.sum((d_emb[b] for b in range(B)), (N,), want_abs)
+    db_acc, A_db = r5 if want_abs else (r5, None)
+    res = dict(da=da, dtemb=dtemb, dW_acc=dW_acc, dW=ar.bf16(dW_acc), db_acc=db_acc, db=ar.bf16(db_acc))
+    if want_abs:
         res.update(A_da=A_da, A_dW=A_dW, A_db=A_db)
     return res
 
@@ -296,6 +326,7 @@ def param_grads_rows(inp: dict, rows, mode: str = "fp32", eps: float = EPS, stat
     a = silu_act(_val(inp, "temb"), ar)                               # [B, K]
     de = d_emb_columns(inp, rows, mode, eps, stats)                   # [B, R]
     B = a.shape[0]
-    dW = ar.bf16(ar.sum((de[b][:, None] * a[b][None, :] for b in range(B)), (len(rows), a.shape[1])))
+    dW = ar.bf16(ar.sum((t for b in range(B) for t in ar.prod(de[b][:, None], a[b][None, :])),
+                        (len(rows), a.shape[1])))
     db = ar.bf16(ar.sum((de[b] for b in range(B)), (len(rows),)))
     return _bits(dW), _bits(db), de

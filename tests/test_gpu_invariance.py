@@ -136,3 +136,30 @@ def test_param_grads_zero_padding(gpu_lib):
     r2 = run_path_dev({"x": d2["x"], "temb": d["temb"][:3], "W": d["W"], "bias": d["bias"], "g": d2["g"]})
     assert same_bytes(r2["d_emb"], base["d_emb"])
     assert same_bytes(r2["dW"], base["dW"]) and same_bytes(r2["db"], base["db"])
+
+
+def test_projection_paths_agree_on_extreme_inputs(gpu_lib):
+    """B <= 4 runs the projection on the vector units and B > 4 on the fp64
+    matrix cores; emb must be the same bytes either way.  The inputs reach where
+    an fp32 product of the operands would lose bits: SiLU of temb near -90 is a
+    bf16 subnormal (or zero), and W spans 2^-40 .. 2^20, so some products lie
+    far below fp32's normal range while others dominate the sums."""
+    print("[invariance] projection paths, extreme inputs, B=40 vs 1 and 4", flush=True)
+    from invariant_silu_amd import ops
+    from synthetic_inputs import f32_to_bf16_bits
+    from tests.gpu_helpers import to_dev
+    rng = np.random.default_rng(11)
+    B = 40
+    temb = rng.standard_normal((B, 3072), dtype=np.float32)
+    mask = rng.random((B, 3072)) < 0.2
+    temb[mask] = -rng.uniform(86.0, 98.0, int(mask.sum())).astype(np.float32)
+    W = rng.standard_normal((6144, 3072), dtype=np.float32)
+    W *= np.exp2(rng.integers(-40, 21, (6144, 3072))).astype(np.float32)
+    bias = rng.standard_normal(6144, dtype=np.float32)
+    t_d, W_d, b_d = (to_dev(f32_to_bf16_bits(v)) for v in (temb, W, bias))
+    emb = ops.proj_fwd(t_d, W_d, b_d)
+    assert torch.isfinite(emb.float()).all()
+    for b in range(B):
+        assert same_bytes(emb[b:b + 1], ops.proj_fwd(t_d[b:b + 1], W_d, b_d)), f"sample {b} (B=1)"
+    for lo in range(0, B, 4):
+        assert same_bytes(emb[lo:lo + 4], ops.proj_fwd(t_d[lo:lo + 4], W_d, b_d)), f"samples {lo}.. (B=4)"

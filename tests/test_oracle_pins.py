@@ -315,6 +315,63 @@ def test_projection_tiny_exact_rationals():
             assert bf16_ulp_diff(f32_to_bf16_bits(got[b, j]), want) == 0
 
 
+def _proj_bwd_cancelling_case(seed=21, B=3, N=12, K=10):
+    """Tiny projection-backward operands whose sums nearly cancel: sample 1
+    repeats sample 0 with a negated a and a d_emb a few fp32 ulps away, row 1
+    of W negates row 0 and d_emb column 1 sits a few ulps from column 0.  The
+    d_emb values carry full 24-bit significands, so a product rounded to fp32
+    on its own loses bits that the cancelling sum exposes."""
+    rng = np.random.default_rng(seed)
+    bf = lambda v: bits_to_f32(f32_to_bf16_bits(np.asarray(v, np.float32)))   # noqa: E731
+    a = bf(rng.standard_normal((B, K)))
+    a[1] = -a[0]
+    W = bf(rng.standard_normal((N, K)) * 0.3)
+    W[1] = -W[0]
+    d = (rng.standard_normal((B, N)) * (1 + rng.random((B, N)))).astype(np.float32)
+    steps = rng.integers(1, 9, (N,)).astype(np.int64)
+    d[1] = (d[0].view(np.int32) + steps.astype(np.int32)).view(np.float32)
+    d[:, 1] = (d[:, 0].view(np.int32) + np.int32(3)).view(np.float32)
+    temb = bf(rng.standard_normal((B, K)))
+    return d, a, W, temb
+
+
+def _exact_proj_bwd(d, a, W):
+    B, N = d.shape
+    K = a.shape[1]
+    F = lambda v: Fraction(float(v))   # noqa: E731
+    dW = np.empty((N, K), np.float32)
+    for j in range(N):
+        for k in range(K):
+            dW[j, k] = frac_to_f32(sum(F(d[b, j]) * F(a[b, k]) for b in range(B)))
+    da = np.empty((B, K), np.float32)
+    for b in range(B):
+        for k in range(K):
+            da[b, k] = frac_to_f32(sum(F(d[b, j]) * F(W[j, k]) for j in range(N)))
+    return dW, da
+
+
+def test_projection_backward_tiny_exact_rationals():
+    """P-15: da and dW against exact rational sums of exact products, rounded
+    once to fp32 (dW then to bf16), on operands that cancel."""
+    d, a, W, temb = _proj_bwd_cancelling_case()
+    r = adaln.proj_backward(d, a, W, temb, adaln.Arith("fp32"))
+    dW_ex, da_ex = _exact_proj_bwd(d, a, W)
+    assert np.array_equal(f32_to_bf16_bits(r["dW"]), f32_to_bf16_bits(dW_ex))
+    assert np.array_equal(r["dW_acc"].view(np.uint32), dW_ex.view(np.uint32))
+    assert np.array_equal(r["da"].view(np.uint32), da_ex.view(np.uint32))
+
+
+def test_teeth_rounded_products_caught(monkeypatch):
+    """Rounding each backward product to fp32 on its own fails P-15."""
+    monkeypatch.setattr(adaln.Arith, "prod",
+                        lambda self, x, y: ((np.asarray(x, self.dt) * np.asarray(y, self.dt)),))
+    d, a, W, temb = _proj_bwd_cancelling_case()
+    r = adaln.proj_backward(d, a, W, temb, adaln.Arith("fp32"))
+    dW_ex, da_ex = _exact_proj_bwd(d, a, W)
+    assert not (np.array_equal(r["dW_acc"].view(np.uint32), dW_ex.view(np.uint32))
+                and np.array_equal(r["da"].view(np.uint32), da_ex.view(np.uint32)))
+
+
 def test_silu_worked_value_and_special_cases():
     """P-9: the review thread's worked value silu'(1) = 0.9277; silu(0) = 0,
     silu'(0) = 1/2; silu(z) -> z for large z and -> 0 for very negative z."""
