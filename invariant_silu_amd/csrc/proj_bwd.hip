@@ -368,7 +368,8 @@ __global__ __launch_bounds__(64 * kDwMWaves) void dw_mfma_kernel(const float* __
 // columns k0 + 2 c + n.  Lane (r, g) loads d_emb[b0 + r][t0 + 128 (4 s + g)
 // .. + 3] (16 bytes: the four leaves) and W[t0 + l + 128 (4 s + g)][k0 + 2 r ..
 // + 1] for l = 0 .. 3.  Leaf results go into the wave's leaf tree in order;
-// the 8 subtrees meet in LDS, pairwise in leaf order.  Blocks x and x + 8
+// the 8 subtrees meet in LDS, pairwise in leaf order.  At most 128 VGPRs,
+// so two blocks fit a CU.  Blocks x and x + 8
 // (same XCD) take the two halves of one 128-byte row segment of W.  Rows
 // past B load sample B - 1 and are never stored.
 constexpr int kLeafSteps = 12;   // 48 rows of a leaf, 4 per matrix-core step
@@ -376,7 +377,7 @@ constexpr int kDaMWaves = 8;
 constexpr int kDaMLeaves = 128 / kDaMWaves;    // 16 per wave
 constexpr int kDaMGroup = 4;                   // leaves run side by side
 constexpr int kDaMCols = 32;
-constexpr int kDaMAhead = 2;                   // steps in flight
+constexpr int kDaMAhead = 1;                   // steps in flight
 
 struct DaStep {
   uint4 d;          // d_emb of the group's 4 leaves
