@@ -65,12 +65,19 @@ EPS = 1e-6
 
 
 class Arith:
-    """The arithmetic of one mode: working dtype, storage roundings, sums."""
+    """The arithmetic of one mode: working dtype, storage roundings, sums.
 
-    def __init__(self, mode: str):
+    ``io`` is the storage type of the operator's tensors: "bf16" (the
+    autocast rounding points) or "fp32" (the FP32 execution the pages also
+    measure: every stored tensor is fp32, so no bf16 rounding anywhere)."""
+
+    def __init__(self, mode: str, io: str = "bf16"):
         if mode not in ("fp32", "fp64", "exact"):
             raise ValueError(mode)
+        if io not in ("bf16", "fp32"):
+            raise ValueError(io)
         self.mode = mode
+        self.io = io
         self.dt = np.float32 if mode == "fp32" else np.float64
 
     def c(self, v):
@@ -88,6 +95,10 @@ class Arith:
         if self.mode == "fp64":
             return np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
         return np.asarray(v, dtype=self.dt)
+
+    def store(self, v):
+        """Rounding at a storage point: to bf16, or to fp32 for fp32 storage."""
+        return self.bf16(v) if self.io == "bf16" else self.f32(v)
 
     def sum(self, terms, shape, want_abs=False):
         return nsum_stream(terms, shape, self.dt, want_abs)
@@ -116,19 +127,28 @@ def _dsilu64(z):
 
 
 def _val(inp: dict, key: str) -> np.ndarray:
-    """Input values: ``inp[key + '_val']`` (float64, exact mode) or the bf16 bits."""
+    """Input values: ``inp[key + '_val']`` (float64, exact mode), fp32 values
+    (fp32 storage) or the bf16 bits."""
     if key + "_val" in inp:
         return np.asarray(inp[key + "_val"], dtype=np.float64)
-    return bits_to_f32(inp[key])
+    v = np.asarray(inp[key])
+    if v.dtype == np.float32:
+        return v
+    return bits_to_f32(v)
+
+
+def _io(inp: dict) -> str:
+    return inp.get("io", "bf16")
 
 
 def silu_act(temb, ar: Arith):
-    """a = bf16(SiLU(temb)); SiLU in float64, rounded to float32 in fp32 mode."""
+    """a = SiLU(temb) at its storage rounding (bf16, or fp32); SiLU in float64,
+    rounded to float32 in fp32 mode."""
     z = np.asarray(temb).astype(np.float64)
     v = _silu64(z)
     if ar.mode == "fp32":
         v = v.astype(np.float32)
-    return ar.bf16(v)
+    return ar.store(v)
 
 
 def dsilu(temb, ar: Arith):
@@ -148,7 +168,7 @@ def projection(a, W, bias, ar: Arith, want_abs=False):
     terms = (t for k in range(K) for t in ar.prod(a[:, k:k + 1], WT[k][None, :]))
     r = ar.sum(terms, (B, N), want_abs)
     acc, A = (r if want_abs else (r, None))
-    emb = ar.bf16(acc + bias)
+    emb = ar.store(acc + bias)
     return (emb, A) if want_abs else emb
 
 
@@ -171,13 +191,14 @@ def _normalize(x2, mean, rstd, ar: Arith):
 
 
 def forward(inp: dict, mode: str = "fp32", eps: float = EPS, want_abs: bool = False):
-    """Forward pass.  ``inp`` holds bf16 bit arrays x, temb, W, bias.
+    """Forward pass.  ``inp`` holds x, temb, W, bias as bf16 bit arrays, or as
+    fp32 arrays with ``inp['io'] == 'fp32'`` (fp32 storage).
 
     Returns a dict: a, emb, m, mean, rstd, n, out (values in the mode's dtype;
-    bf16 quantities hold bf16-representable values) and, for bf16 outputs,
+    bf16 quantities hold bf16-representable values) and, for bf16 storage,
     ``*_bits`` uint16 arrays.
     """
-    ar = Arith(mode)
+    ar = Arith(mode, _io(inp))
     x = ar.c(_val(inp, "x"))
     B, S, D = x.shape
     a = silu_act(_val(inp, "temb"), ar)
@@ -185,14 +206,14 @@ def forward(inp: dict, mode: str = "fp32", eps: float = EPS, want_abs: bool = Fa
     emb, A_emb = pr if want_abs else (pr, None)
     scale, shift = emb[:, :D], emb[:, D:]
     one = ar.c(1.0)
-    m = ar.bf16(one + scale)
+    m = ar.store(one + scale)
 
     mean, var, rstd = _ln_stats(x.reshape(B * S, D), ar, eps)
     n = _normalize(x.reshape(B * S, D), mean, rstd, ar).reshape(B, S, D)
-    out = ar.bf16(n * m[:, None, :] + shift[:, None, :])
+    out = ar.store(n * m[:, None, :] + shift[:, None, :])
     res = dict(a=a, emb=emb, m=m, mean=mean.reshape(B, S), rstd=rstd.reshape(B, S),
                n=n, out=out, var=var.reshape(B, S))
-    if mode != "exact":
+    if mode != "exact" and ar.io == "bf16":
         res["out_bits"] = _bits(out)
         res["emb_bits"] = _bits(emb)
         res["a_bits"] = _bits(a)
@@ -209,7 +230,7 @@ def backward(inp: dict, fwd: dict, mode: str = "fp32", want_abs: bool = False,
     and, for bf16 outputs, ``*_bits``.  With ``want_abs`` also the error scales
     A (sum of |terms|, float64) of d_emb, alpha/beta, da, dW and db.
     """
-    ar = Arith(mode)
+    ar = Arith(mode, _io(inp))
     g = ar.c(_val(inp, "g") if g is None else g)
     B, S, D = g.shape
     R = B * S
@@ -221,7 +242,7 @@ def backward(inp: dict, fwd: dict, mode: str = "fp32", want_abs: bool = False,
     alpha = ar.sum(iter(gyT), (R,)) / Dt
     beta = ar.sum((gyT[d] * nT[d] for d in range(D)), (R,)) / Dt
     rs = rstd.reshape(R)[:, None]
-    dx = ar.bf16(rs * ((gy.reshape(R, D) - alpha[:, None]) - n.reshape(R, D) * beta[:, None]))
+    dx = ar.store(rs * ((gy.reshape(R, D) - alpha[:, None]) - n.reshape(R, D) * beta[:, None]))
     dx = dx.reshape(B, S, D)
 
     # token sums over s, per sample
@@ -241,7 +262,7 @@ def backward(inp: dict, fwd: dict, mode: str = "fp32", want_abs: bool = False,
     res = dict(dx=dx, d_scale=d_scale, d_shift=d_shift, d_emb=d_emb, da=da,
                dtemb=dtemb, dW=dW, db=db, dW_acc=dW_acc, db_acc=db_acc,
                alpha=alpha.reshape(B, S), beta=beta.reshape(B, S))
-    if mode != "exact":
+    if mode != "exact" and ar.io == "bf16":
         for k in ("dx", "dtemb", "dW", "db"):
             res[k + "_bits"] = _bits(res[k])
     if want_abs:
@@ -259,12 +280,12 @@ def proj_backward(d_emb, a, W, temb, ar: Arith, want_abs: bool = False) -> dict:
     K = W.shape[1]
     r3 = ar.sum((t for j in range(N) for t in ar.prod(d_emb[:, j:j + 1], W[j][None, :])), (B, K), want_abs)
     da, A_da = r3 if want_abs else (r3, None)
-    dtemb = ar.bf16(da * dsilu(temb, ar))
+    dtemb = ar.store(da * dsilu(temb, ar))
     r4 = ar.sum((t for b in range(B) for t in ar.prod(d_emb[b][:, None], a[b][None, :])), (N, K), want_abs)
     dW_acc, A_dW = r4 if want_abs else (r4, None)
     r5 = ar.sum((d_emb[b] for b in range(B)), (N,), want_abs)
     db_acc, A_db = r5 if want_abs else (r5, None)
-    res = dict(da=da, dtemb=dtemb, dW_acc=dW_acc, dW=ar.bf16(dW_acc), db_acc=db_acc, db=ar.bf16(db_acc))
+    res = dict(da=da, dtemb=dtemb, dW_acc=dW_acc, dW=ar.store(dW_acc), db_acc=db_acc, db=ar.store(db_acc))
     if want_abs:
         res.update(A_da=A_da, A_dW=A_dW, A_db=A_db)
     return res
@@ -296,7 +317,7 @@ def sgld_forward_out(inp: dict, fwd: dict):
 
 def ln_stats(inp: dict, mode: str = "fp32", eps: float = EPS):
     """mean, rstd [B, S] of every row (the saved LayerNorm state)."""
-    ar = Arith(mode)
+    ar = Arith(mode, _io(inp))
     x = ar.c(_val(inp, "x"))
     B, S, D = x.shape
     mean, _, rstd = _ln_stats(x.reshape(B * S, D), ar, eps)
@@ -305,7 +326,7 @@ def ln_stats(inp: dict, mode: str = "fp32", eps: float = EPS):
 
 def d_emb_columns(inp: dict, cols, mode: str = "fp32", eps: float = EPS, stats=None):
     """d_emb[:, cols] (d_scale for cols < D, d_shift for cols >= D), every sample."""
-    ar = Arith(mode)
+    ar = Arith(mode, _io(inp))
     x = ar.c(_val(inp, "x"))
     g = ar.c(_val(inp, "g"))
     B, S, D = x.shape
@@ -321,12 +342,15 @@ def d_emb_columns(inp: dict, cols, mode: str = "fp32", eps: float = EPS, stats=N
 
 
 def param_grads_rows(inp: dict, rows, mode: str = "fp32", eps: float = EPS, stats=None):
-    """dW[rows, :] and db[rows] (bf16 bits) over the whole batch."""
-    ar = Arith(mode)
+    """dW[rows, :] and db[rows] over the whole batch (bf16 bits, or fp32
+    values for fp32 storage)."""
+    ar = Arith(mode, _io(inp))
     a = silu_act(_val(inp, "temb"), ar)                               # [B, K]
     de = d_emb_columns(inp, rows, mode, eps, stats)                   # [B, R]
     B = a.shape[0]
-    dW = ar.bf16(ar.sum((t for b in range(B) for t in ar.prod(de[b][:, None], a[b][None, :])),
-                        (len(rows), a.shape[1])))
-    db = ar.bf16(ar.sum((de[b] for b in range(B)), (len(rows),)))
+    dW = ar.store(ar.sum((t for b in range(B) for t in ar.prod(de[b][:, None], a[b][None, :])),
+                         (len(rows), a.shape[1])))
+    db = ar.store(ar.sum((de[b] for b in range(B)), (len(rows),)))
+    if ar.io == "fp32":
+        return dW, db, de
     return _bits(dW), _bits(db), de

@@ -58,12 +58,13 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def make_inputs(B: int, S: int, seed: int = 0, outlier_frac: float = 0.0,
-                D: int = HIDDEN) -> dict:
+                D: int = HIDDEN, io: str = "bf16") -> dict:
     """Draw one batch: x [B,S,D], temb [B,D], W [2D,D], bias [2D], g [B,S,D].
 
     ``outlier_frac`` of each sample's rows (rounded) are multiplied by 20 in
     float32 before the bfloat16 rounding; the row indices are drawn last, per
-    sample, without replacement.
+    sample, without replacement.  With ``io="fp32"`` the same draws are
+    returned as float32 arrays, not rounded to bfloat16 (fp32 storage).
     """
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((B, S, D), dtype=np.float32)
@@ -78,6 +79,9 @@ def make_inputs(B: int, S: int, seed: int = 0, outlier_frac: float = 0.0,
             rows = np.sort(rng.choice(S, size=k, replace=False))
             x[b, rows, :] *= np.float32(20.0)
             outliers.append(rows)
+    if io == "fp32":
+        return {"x": x, "temb": temb, "W": W, "bias": bias, "g": g, "outlier_rows": outliers,
+                "B": B, "S": S, "D": D, "seed": seed, "io": "fp32"}
     return {
         "x": f32_to_bf16_bits(x),
         "temb": f32_to_bf16_bits(temb),

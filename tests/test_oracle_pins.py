@@ -479,6 +479,86 @@ def test_twin_and_oracle_agree():
         assert (d > 1).mean() < 2e-3, k
 
 
+# ------------------------------------------------------------ fp32 storage --
+def _fp32_identity_case():
+    inp = _small_inputs(2, 40, seed=31, outlier_frac=0.05, io="fp32")
+    inp["W"] = np.concatenate([np.eye(D, dtype=np.float32), np.zeros((D, D), np.float32)])
+    inp["bias"] = np.zeros(2 * D, np.float32)
+    return inp
+
+
+def _fp32_storage_checks(inp):
+    """The facts P-16 checks, as booleans (the teeth test reuses them)."""
+    f = adaln.forward(inp)
+    ok = {}
+    # identity projection: emb = (a | 0) exactly, a kept in fp32 (most values
+    # are not bf16-representable)
+    ok["emb_identity"] = (np.array_equal(f["emb"][:, :D], f["a"]) and np.all(f["emb"][:, D:] == 0))
+    a_bf = bits_to_f32(f32_to_bf16_bits(f["a"]))
+    ok["a_fp32"] = (a_bf != f["a"]).mean() > 0.9
+    # W = 0, b = 0: out = LayerNorm(x) in fp32 against a float64 two-pass LayerNorm
+    w0 = dict(inp, W=np.zeros_like(inp["W"]), bias=np.zeros_like(inp["bias"]))
+    f0 = adaln.forward(w0)
+    tb = _textbook_ln(inp["x"])
+    ok["layernorm"] = bool(np.all(np.abs(f0["out"] - tb) <= 4e-7 * np.abs(tb) + 1e-7))
+    # scale = 2^-12: 1 + scale stays in fp32 (a bf16 rounding would give m = 1)
+    sh = np.random.default_rng(32).standard_normal(D).astype(np.float32)
+    w1 = dict(w0, bias=np.concatenate([np.full(D, 2.0 ** -12, np.float32), sh]))
+    f1 = adaln.forward(w1)
+    ok["m_fp32"] = bool(np.all(f1["m"] == np.float32(1 + 2.0 ** -12)))
+    # scale = -1: m = 0 and out = shift exactly
+    w2 = dict(w0, bias=np.concatenate([np.full(D, -1.0, np.float32), sh]))
+    f2 = adaln.forward(w2)
+    ok["out_shift"] = bool(np.all(f2["m"] == 0) and np.array_equal(f2["out"], np.broadcast_to(sh, f2["out"].shape)))
+    return ok
+
+
+def test_fp32_storage_closed_forms():
+    """P-16: fp32 storage.  W = [I; 0], b = 0 gives emb = (a | 0) exactly with a
+    kept in fp32; W = 0, b = 0 gives out = LayerNorm(x) against a float64
+    two-pass LayerNorm; 1 + scale is kept in fp32 (scale = 2^-12); scale = -1
+    gives out = shift exactly."""
+    ok = _fp32_storage_checks(_fp32_identity_case())
+    assert all(ok.values()), ok
+
+
+def test_fp32_storage_batch_sums_at_b1_s1():
+    """P-17: fp32 storage, one sample of one token: d_shift = g and d_scale =
+    g * n (one fp32 product), dW = d_emb * a (one fp32 product), db = d_emb,
+    bit for bit."""
+    inp = _small_inputs(1, 1, seed=33, io="fp32")
+    f = adaln.forward(inp)
+    b = adaln.backward(inp, f)
+    g = inp["g"][:, 0, :]
+    assert b["d_shift"].tobytes() == g.tobytes()
+    assert b["d_scale"].tobytes() == (g * f["n"][:, 0, :]).astype(np.float32).tobytes()
+    de, a = b["d_emb"][0], f["a"][0]
+    assert b["dW"].tobytes() == (de[:, None] * a[None, :]).astype(np.float32).tobytes()
+    assert b["db"].tobytes() == de.tobytes()
+
+
+def test_projection_backward_fp32_operands_exact_rationals():
+    """P-15b: da and dW with fp32 a and W (24-bit significands, products of up
+    to 48 bits) against exact rational sums rounded once to fp32."""
+    d, a, W, temb = _proj_bwd_cancelling_case(seed=34)
+    rng = np.random.default_rng(35)
+    a = (a * (1 + rng.random(a.shape) * 2.0 ** -9)).astype(np.float32)
+    a[1] = -a[0]
+    W = (W * (1 + rng.random(W.shape) * 2.0 ** -9)).astype(np.float32)
+    W[1] = -W[0]
+    r = adaln.proj_backward(d, a, W, temb, adaln.Arith("fp32", io="fp32"))
+    dW_ex, da_ex = _exact_proj_bwd(d, a, W)
+    assert np.array_equal(r["dW"].view(np.uint32), dW_ex.view(np.uint32))
+    assert np.array_equal(r["da"].view(np.uint32), da_ex.view(np.uint32))
+
+
+def test_teeth_bf16_rounding_in_fp32_storage_caught(monkeypatch):
+    """A bf16 storage rounding left in the fp32 storage mode fails P-16."""
+    monkeypatch.setattr(adaln.Arith, "store", lambda self, v: self.bf16(v))
+    ok = _fp32_storage_checks(_fp32_identity_case())
+    assert not all(ok.values())
+
+
 # ------------------------------------------------------------ planted mistakes --
 def test_teeth_swapped_chunks_caught(monkeypatch):
     orig = adaln.projection
