@@ -49,7 +49,7 @@ extern "C" {
 
 typedef uint16_t adaln_bf16;
 
-#define ADALN_ABI_VERSION 2
+#define ADALN_ABI_VERSION 3
 
 enum adaln_status {
   ADALN_OK = 0,
@@ -67,7 +67,8 @@ enum adaln_op {
   ADALN_OP_NORM_MOD_BWD = 2,
   ADALN_OP_PROJ_BWD = 3,
   ADALN_OP_TOKEN_TREE_SUM = 4,
-  ADALN_OP_BWD = 5
+  ADALN_OP_BWD = 5,
+  ADALN_OP_BWD_F32 = 6
 };
 
 /* Workspace bytes an entry point needs (0 for an unknown op or bad sizes).
@@ -78,6 +79,7 @@ enum adaln_op {
  *                   B > 4).
  *   TOKEN_TREE_SUM: B * ceil(S/32) * ceil(H/64) * 64 * 8 bytes (level-0 pairs).
  *   BWD:            H = D (3072).  NORM_MOD_BWD + PROJ_BWD, in that order.
+ *   BWD_F32:        H = D (3072).  NORM_MOD_BWD + B*K*4 (fp32 activations).
  * Each region is padded to 256 bytes. */
 size_t adaln_workspace_bytes(int op, int64_t B, int64_t S, int64_t H);
 
@@ -190,6 +192,23 @@ int adaln_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float* mean, co
               const adaln_bf16* emb, const adaln_bf16* temb, const adaln_bf16* W, adaln_bf16* dx,
               float* d_emb, adaln_bf16* dW, adaln_bf16* db, adaln_bf16* dtemb, void* ws, size_t ws_bytes,
               int64_t B, int64_t S, int64_t D, void* stream);
+
+/* FP32 storage (the FP32 execution RL-Kernel pull request 538 measures beside
+ * BF16): every tensor fp32, the same method without the bf16 rounding points --
+ * a = fp32(SiLU(temb)), emb = fp32(sum a W) + b, m = 1 + scale in fp32,
+ * out = (n * m) + shift, dx, dtemb, dW, db stored in fp32 -- and the same
+ * summation orders as with bf16 storage.  Layouts as above with fp32 elements;
+ * mean, rstd, d_emb as above.  The projection and dW run on the fp64 matrix
+ * cores for every B, da on the vector units for B <= 4 and the matrix cores
+ * beyond (the same order, the same bits).
+ * adaln_fwd_f32 uses the first B * 3072 elements of `out` as scratch before
+ * writing it.  adaln_bwd_f32: ws = adaln_workspace_bytes(ADALN_OP_BWD_F32,
+ * B, S, D) bytes. */
+int adaln_fwd_f32(const float* temb, const float* W, const float* bias, const float* x, float* emb, float* out,
+                  float* mean, float* rstd, int64_t B, int64_t S, int64_t D, float eps, void* stream);
+int adaln_bwd_f32(const float* gout, const float* x, const float* mean, const float* rstd, const float* emb,
+                  const float* temb, const float* W, float* dx, float* d_emb, float* dW, float* db, float* dtemb,
+                  void* ws, size_t ws_bytes, int64_t B, int64_t S, int64_t D, void* stream);
 
 /* Benchmarking aid: per-launch durations of the main kernel of the backward
  * (adaln_bwd and adaln_norm_mod_bwd: the fused dx + level-0 kernel;

@@ -122,6 +122,9 @@ size_t ws_proj_bwd(int64_t B) {
   return pad256(static_cast<size_t>(B * kD * 2));   // SiLU activations (B > 4)
 }
 size_t ws_tree(int64_t B, int64_t S, int64_t H) { return ws_pairs(B, S, H); }
+size_t ws_proj_bwd_f32(int64_t B) {
+  return pad256(static_cast<size_t>(B * kD * 4));   // SiLU activations (fp32 storage)
+}
 bool batch_ok(int64_t B) { return B >= 1 && B <= kMaxB; }
 bool seq_ok(int64_t S) { return S >= 1 && S <= kMaxS; }
 
@@ -223,6 +226,7 @@ size_t adaln_workspace_bytes(int op, int64_t B, int64_t S, int64_t H) {
     case ADALN_OP_PROJ_FWD: return H == kD ? ws_proj_fwd(B) : 0;
     case ADALN_OP_PROJ_BWD: return H == kD ? ws_proj_bwd(B) : 0;
     case ADALN_OP_BWD: return (H == kD && seq_ok(S)) ? ws_norm_bwd(B, S) + ws_proj_bwd(B) : 0;
+    case ADALN_OP_BWD_F32: return (H == kD && seq_ok(S)) ? ws_norm_bwd(B, S) + ws_proj_bwd_f32(B) : 0;
     case ADALN_OP_TOKEN_TREE_SUM:
       return (seq_ok(S) && H >= 1 && H <= (int64_t{1} << 24)) ? ws_tree(B, S, H) : 0;
     default: return 0;
@@ -481,6 +485,61 @@ int adaln_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float* mean, co
   if (int rc = launched(adaln::launch_silu(temb, a, B * kD, s))) return rc;
   if (int rc = launched(adaln::launch_proj_bwd_dw(d_emb, a, dW, db, B, s))) return rc;
   return launched(adaln::launch_proj_bwd_da(d_emb, W, temb, dtemb, B, s));
+}
+
+int adaln_fwd_f32(const float* temb, const float* W, const float* bias, const float* x, float* emb, float* out,
+                  float* mean, float* rstd, int64_t B, int64_t S, int64_t D, float eps, void* stream) {
+  if (!temb || !W || !bias || !x || !emb || !out || !mean || !rstd) return ADALN_ERR_NULL;
+  if (!batch_ok(B) || !seq_ok(S) || D != kD) return ADALN_ERR_SHAPE;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return ADALN_ERR_SHAPE;
+  if (!aligned16(temb) || !aligned16(W) || !aligned16(bias) || !aligned16(x) || !aligned16(emb) ||
+      !aligned16(out) || !aligned16(mean) || !aligned16(rstd))
+    return ADALN_ERR_ALIGN;
+  const size_t rows = static_cast<size_t>(B * S);
+  if (int rc = check_overlap({{emb, static_cast<size_t>(B * kN * 4)}, {out, rows * kD * 4}, {mean, rows * 4},
+                              {rstd, rows * 4}},
+                             {{temb, static_cast<size_t>(B * kD * 4)}, {W, static_cast<size_t>(kN * kD * 4)},
+                              {bias, static_cast<size_t>(kN * 4)}, {x, rows * kD * 4}}))
+    return rc;
+  if (int rc = check_device()) return rc;
+  (void)hipGetLastError();
+  const hipStream_t s = as_stream(stream);
+  // SiLU into the first B * 3072 elements of `out` (overwritten by the
+  // modulation afterwards), the projection, then statistics and modulation
+  if (int rc = launched(adaln::launch_proj_fwd_f32(temb, out, W, bias, emb, B, s))) return rc;
+  return launched(adaln::launch_norm_mod_fwd_f32(x, emb, out, mean, rstd, B, S, eps, s));
+}
+
+int adaln_bwd_f32(const float* gout, const float* x, const float* mean, const float* rstd, const float* emb,
+                  const float* temb, const float* W, float* dx, float* d_emb, float* dW, float* db, float* dtemb,
+                  void* ws, size_t ws_bytes, int64_t B, int64_t S, int64_t D, void* stream) {
+  if (!gout || !x || !mean || !rstd || !emb || !temb || !W || !dx || !d_emb || !dW || !db || !dtemb || !ws)
+    return ADALN_ERR_NULL;
+  if (!batch_ok(B) || !seq_ok(S) || D != kD) return ADALN_ERR_SHAPE;
+  if (!aligned16(gout) || !aligned16(x) || !aligned16(mean) || !aligned16(rstd) || !aligned16(emb) ||
+      !aligned16(temb) || !aligned16(W) || !aligned16(dx) || !aligned16(d_emb) || !aligned16(dW) ||
+      !aligned16(db) || !aligned16(dtemb) || !aligned16(ws))
+    return ADALN_ERR_ALIGN;
+  const size_t n_norm = ws_norm_bwd(B, S);
+  const size_t need = n_norm + ws_proj_bwd_f32(B);
+  if (ws_bytes < need) return ADALN_ERR_WORKSPACE;
+  const size_t rows = static_cast<size_t>(B * S);
+  if (int rc = check_overlap(
+          {{dx, rows * kD * 4}, {d_emb, static_cast<size_t>(B * kN * 4)}, {dW, static_cast<size_t>(kN * kD * 4)},
+           {db, static_cast<size_t>(kN * 4)}, {dtemb, static_cast<size_t>(B * kD * 4)}, {ws, need}},
+          {{gout, rows * kD * 4}, {x, rows * kD * 4}, {mean, rows * 4}, {rstd, rows * 4},
+           {emb, static_cast<size_t>(B * kN * 4)}, {temb, static_cast<size_t>(B * kD * 4)},
+           {W, static_cast<size_t>(kN * kD * 4)}}))
+    return rc;
+  if (int rc = check_device()) return rc;
+  (void)hipGetLastError();
+  const hipStream_t s = as_stream(stream);
+  const int64_t T0 = ceil_div(S, kTile);
+  float* part = static_cast<float*>(ws);
+  float* a = reinterpret_cast<float*>(static_cast<char*>(ws) + n_norm);
+  if (int rc = launched(adaln::launch_norm_mod_bwd_f32(gout, x, mean, rstd, emb, dx, part, B, S, s))) return rc;
+  if (int rc = launched(adaln::launch_tree_fold(part, d_emb, B, T0, kN, s))) return rc;
+  return launched(adaln::launch_proj_bwd_f32(d_emb, temb, W, a, dW, db, dtemb, B, s));
 }
 
 int adaln_selftest(void) {

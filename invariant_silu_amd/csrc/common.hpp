@@ -165,6 +165,21 @@ __device__ __forceinline__ uint4 silu8_fast(const uint4& in, uint32_t& redo_mask
   return make_uint4(o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16), o[6] | (o[7] << 16));
 }
 
+// Element access for the two storage types of the operator's tensors: bf16
+// (bit patterns in uint16_t; stores round to nearest even) and fp32.
+template <typename T>
+struct Storage;
+template <>
+struct Storage<uint16_t> {
+  __device__ __forceinline__ static float load1(uint16_t v) { return bf16_to_f32(v); }
+  __device__ __forceinline__ static uint16_t store1(float v) { return f32_to_bf16(v); }
+};
+template <>
+struct Storage<float> {
+  __device__ __forceinline__ static float load1(float v) { return v; }
+  __device__ __forceinline__ static float store1(float v) { return v; }
+};
+
 // One Neumaier step: t = s + x; c += exact rounding error of that add.
 // The branch-free form picks the larger-magnitude operand for Fast2Sum, so
 // c gets the same exact error term as the textbook |s| >= |x| branch.

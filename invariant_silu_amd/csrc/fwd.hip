@@ -200,18 +200,20 @@ __device__ __forceinline__ void proj_block(const uint16_t* __restrict__ temb,
 constexpr int kMfmaRows = 16;                               // rows of W per block
 constexpr int kLeafAhead = 2;                               // leaves in flight
 
-template <int kTiles>
+template <int kTiles, typename T>
 struct LeafRaw {
-  uint32_t a[kTiles][6], w[6];   // 12 bf16 per operand (steps 0..11)
+  RowRun<12, T> a[kTiles], w;   // 12 elements per operand (steps 0..11)
 };
 
-template <int kTiles, int kSplit>
-__global__ __launch_bounds__(64 * kSplit) void proj_mfma_kernel(const uint16_t* __restrict__ a,
-                                                                const uint16_t* __restrict__ W,
-                                                                const uint16_t* __restrict__ bias,
-                                                                uint16_t* __restrict__ emb, int64_t B) {
+// T: storage type of a, W, bias and emb (bf16 bit patterns or fp32)
+template <int kTiles, int kSplit, typename T>
+__global__ __launch_bounds__(64 * kSplit) void proj_mfma_kernel(const T* __restrict__ a,
+                                                                const T* __restrict__ W,
+                                                                const T* __restrict__ bias,
+                                                                T* __restrict__ emb, int64_t B) {
   constexpr int kWaveLeaves = 64 / kSplit;
   constexpr int kSamples = 16 * kTiles;
+  constexpr uint32_t kEl = sizeof(T);
   static_assert(kSplit == 1 || kSplit == 2 || kSplit == 4 || kSplit == 8, "leaf split");
   __shared__ f64x4_t sub[kSplit > 1 ? kSplit - 1 : 1][kTiles][64];
   // wave index through readfirstlane: the leaf offsets below stay scalar
@@ -222,34 +224,23 @@ __global__ __launch_bounds__(64 * kSplit) void proj_mfma_kernel(const uint16_t* 
   const int64_t bblk = static_cast<int64_t>(blockIdx.y) * kSamples;
   const int rows_here = static_cast<int>((B - bblk) < kSamples ? (B - bblk) : kSamples);
 
-  const Buffer abuf(a + bblk * kD, static_cast<uint32_t>(rows_here) * kD * 2);
-  const Buffer wbuf(W + static_cast<int64_t>(j0) * kD, kMfmaRows * kD * 2);
+  const Buffer abuf(a + bblk * kD, static_cast<uint32_t>(rows_here) * kD * kEl);
+  const Buffer wbuf(W + static_cast<int64_t>(j0) * kD, kMfmaRows * kD * kEl);
   uint32_t a_off[kTiles];
 #pragma unroll
   for (int t = 0; t < kTiles; ++t) {
     const int ra = (16 * t + r) < rows_here ? (16 * t + r) : rows_here - 1;
-    a_off[t] = static_cast<uint32_t>(ra) * kD * 2 + 24 * g;
+    a_off[t] = static_cast<uint32_t>(ra) * kD * kEl + 12 * g * kEl;
   }
-  const uint32_t w_off = static_cast<uint32_t>(r) * kD * 2 + 24 * g;
-  const uint32_t leaf_base = static_cast<uint32_t>(wave * kWaveLeaves) * kLeafK * 2;
+  const uint32_t w_off = static_cast<uint32_t>(r) * kD * kEl + 12 * g * kEl;
+  const uint32_t leaf_base = static_cast<uint32_t>(wave * kWaveLeaves) * kLeafK * kEl;
 
-  LeafRaw<kTiles> raw[kLeafAhead + 1];
-  auto load_leaf = [&](LeafRaw<kTiles>& d, int n) {
-    const uint32_t off = leaf_base + static_cast<uint32_t>(n) * kLeafK * 2;
+  LeafRaw<kTiles, T> raw[kLeafAhead + 1];
+  auto load_leaf = [&](LeafRaw<kTiles, T>& d, int n) {
+    const uint32_t off = leaf_base + static_cast<uint32_t>(n) * kLeafK * kEl;
+    d.w.load(wbuf, w_off, off);
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      const auto vw = __builtin_amdgcn_raw_buffer_load_b64(wbuf.rsrc, w_off, off + 8 * q, 0);
-      d.w[2 * q] = vw[0];
-      d.w[2 * q + 1] = vw[1];
-    }
-#pragma unroll
-    for (int t = 0; t < kTiles; ++t)
-#pragma unroll
-      for (int q = 0; q < 3; ++q) {
-        const auto va = __builtin_amdgcn_raw_buffer_load_b64(abuf.rsrc, a_off[t], off + 8 * q, 0);
-        d.a[t][2 * q] = va[0];
-        d.a[t][2 * q + 1] = va[1];
-      }
+    for (int t = 0; t < kTiles; ++t) d.a[t].load(abuf, a_off[t], off);
   };
 #pragma unroll
   for (int n = 0; n < kLeafAhead; ++n) load_leaf(raw[n], n);
@@ -258,16 +249,15 @@ __global__ __launch_bounds__(64 * kSplit) void proj_mfma_kernel(const uint16_t* 
   static_for<0, kWaveLeaves>([&](auto nc) {
     constexpr int n = decltype(nc)::value;
     if constexpr (n + kLeafAhead < kWaveLeaves) load_leaf(raw[(n + kLeafAhead) % (kLeafAhead + 1)], n + kLeafAhead);
-    const LeafRaw<kTiles>& cur = raw[n % (kLeafAhead + 1)];
+    const LeafRaw<kTiles, T>& cur = raw[n % (kLeafAhead + 1)];
     f64x4_t acc[kTiles];
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) acc[t] = f64x4_t{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int s = 0; s < kLeafSteps; ++s) {
-      const double wv = bf_half64(cur.w[s / 2], s & 1);
+      const double wv = cur.w.at(s);
 #pragma unroll
-      for (int t = 0; t < kTiles; ++t)
-        acc[t] = mfma_f64(bf_half64(cur.a[t][s / 2], s & 1), wv, acc[t]);
+      for (int t = 0; t < kTiles; ++t) acc[t] = mfma_f64(cur.a[t].at(s), wv, acc[t]);
     }
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) tree[t].template push<n>(acc[t]);
@@ -294,14 +284,14 @@ __global__ __launch_bounds__(64 * kSplit) void proj_mfma_kernel(const uint16_t* 
     }
   }
   // lane holds rows g + 4 v of each sample tile, column r (row j0 + r of W)
-  const float bias_f = bf16_to_f32(bias[j0 + r]);
+  const float bias_f = Storage<T>::load1(bias[j0 + r]);
 #pragma unroll
   for (int t = 0; t < kTiles; ++t)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int sr = 16 * t + g + 4 * v;
       if (sr < rows_here)
-        emb[(bblk + sr) * kN + j0 + r] = f32_to_bf16(static_cast<float>(tot[t][v]) + bias_f);
+        emb[(bblk + sr) * kN + j0 + r] = Storage<T>::store1(static_cast<float>(tot[t][v]) + bias_f);
     }
 }
 
@@ -483,21 +473,24 @@ hipError_t by_batch(int64_t B, F&& f) {
   }
 }
 
-// a = bf16(SiLU(temb)) computed once into `a`, then the matrix-core
-// projection: one sample tile per wave up to 16 samples, two beyond
+// a = SiLU(temb) computed once into `a`, then the matrix-core projection:
+// one sample tile per wave up to 16 samples, two beyond
 constexpr int kMfmaSplit = 4;
-template <int kTiles>
-hipError_t launch_mfma_tiles(const uint16_t* a, const uint16_t* W, const uint16_t* bias, uint16_t* emb,
-                             int64_t B, hipStream_t s) {
+template <int kTiles, typename T>
+hipError_t launch_mfma_tiles(const T* a, const T* W, const T* bias, T* emb, int64_t B, hipStream_t s) {
   const int64_t by = (B + 16 * kTiles - 1) / (16 * kTiles);
-  hipLaunchKernelGGL((proj_mfma_kernel<kTiles, kMfmaSplit>), dim3(kN / kMfmaRows, static_cast<unsigned>(by)),
+  hipLaunchKernelGGL((proj_mfma_kernel<kTiles, kMfmaSplit, T>), dim3(kN / kMfmaRows, static_cast<unsigned>(by)),
                      dim3(64 * kMfmaSplit), 0, s, a, W, bias, emb, B);
   return hipGetLastError();
+}
+template <typename T>
+hipError_t launch_mfma_from_a(const T* a, const T* W, const T* bias, T* emb, int64_t B, hipStream_t s) {
+  return B <= 16 ? launch_mfma_tiles<1, T>(a, W, bias, emb, B, s) : launch_mfma_tiles<2, T>(a, W, bias, emb, B, s);
 }
 hipError_t launch_mfma(const uint16_t* temb, uint16_t* a, const uint16_t* W, const uint16_t* bias,
                        uint16_t* emb, int64_t B, hipStream_t s) {
   if (hipError_t e = launch_silu(temb, a, B * kD, s); e != hipSuccess) return e;
-  return B <= 16 ? launch_mfma_tiles<1>(a, W, bias, emb, B, s) : launch_mfma_tiles<2>(a, W, bias, emb, B, s);
+  return launch_mfma_from_a(a, W, bias, emb, B, s);
 }
 
 }  // namespace
@@ -542,6 +535,12 @@ hipError_t launch_fwd(const uint16_t* temb, const uint16_t* W, const uint16_t* b
   hipLaunchKernelGGL(norm_modulate_kernel, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(B)),
                      dim3(kThreads), 0, s, x, emb, mean, rstd, out, S);
   return hipGetLastError();
+}
+
+hipError_t launch_proj_fwd_f32(const float* temb, float* a, const float* W, const float* bias, float* emb,
+                               int64_t B, hipStream_t s) {
+  if (hipError_t e = launch_silu_f32(temb, a, B * kD, s); e != hipSuccess) return e;
+  return launch_mfma_from_a(a, W, bias, emb, B, s);
 }
 
 }  // namespace adaln

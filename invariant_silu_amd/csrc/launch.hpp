@@ -38,6 +38,17 @@ hipError_t launch_proj_bwd_dw(const float* d_emb, const uint16_t* a, uint16_t* d
                               int64_t B, hipStream_t s);
 hipError_t launch_proj_bwd_da(const float* d_emb, const uint16_t* W, const uint16_t* temb,
                               uint16_t* dtemb, int64_t B, hipStream_t s);
+// fp32 storage
+hipError_t launch_silu_f32(const float* temb, float* a, int64_t n, hipStream_t s);
+hipError_t launch_proj_fwd_f32(const float* temb, float* a, const float* W, const float* bias, float* emb,
+                               int64_t B, hipStream_t s);
+hipError_t launch_norm_mod_fwd_f32(const float* x, const float* emb, float* out, float* mean, float* rstd,
+                                   int64_t B, int64_t S, float eps, hipStream_t s);
+hipError_t launch_norm_mod_bwd_f32(const float* g, const float* x, const float* mean, const float* rstd,
+                                   const float* emb, float* dx, float* part, int64_t B, int64_t S,
+                                   hipStream_t s);
+hipError_t launch_proj_bwd_f32(const float* d_emb, const float* temb, const float* W, float* a, float* dW,
+                               float* db, float* dtemb, int64_t B, hipStream_t s);
 hipError_t launch_selftest_probe(const float* in, float* out, uint32_t* bits, int n,
                                  hipStream_t s);
 

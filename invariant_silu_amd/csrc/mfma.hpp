@@ -23,6 +23,41 @@ __device__ __forceinline__ double bf_lo64(uint32_t w) { return static_cast<doubl
 __device__ __forceinline__ double bf_hi64(uint32_t w) { return static_cast<double>(bf_hi(w)); }
 __device__ __forceinline__ double bf_half64(uint32_t w, int h) { return h ? bf_hi64(w) : bf_lo64(w); }
 
+// n consecutive elements of one row held raw in registers (loaded with
+// buffer loads of 8 or 16 bytes); at(i) is element i widened exactly to fp64.
+template <int n, typename T>
+struct RowRun;
+template <int n>
+struct RowRun<n, uint16_t> {
+  static_assert(n % 4 == 0, "8-byte loads");
+  uint32_t v[n / 2];
+  __device__ __forceinline__ void load(const Buffer& b, uint32_t lane_off, uint32_t off) {
+#pragma unroll
+    for (int q = 0; q < n / 4; ++q) {
+      const auto t = __builtin_amdgcn_raw_buffer_load_b64(b.rsrc, lane_off, off + 8 * q, 0);
+      v[2 * q] = t[0];
+      v[2 * q + 1] = t[1];
+    }
+  }
+  __device__ __forceinline__ double at(int i) const { return bf_half64(v[i / 2], i & 1); }
+};
+template <int n>
+struct RowRun<n, float> {
+  static_assert(n % 4 == 0, "16-byte loads");
+  float v[n];
+  __device__ __forceinline__ void load(const Buffer& b, uint32_t lane_off, uint32_t off) {
+#pragma unroll
+    for (int q = 0; q < n / 4; ++q) {
+      const uint4 t = b.u128(lane_off, off + 16 * q);
+      v[4 * q] = __uint_as_float(t.x);
+      v[4 * q + 1] = __uint_as_float(t.y);
+      v[4 * q + 2] = __uint_as_float(t.z);
+      v[4 * q + 3] = __uint_as_float(t.w);
+    }
+  }
+  __device__ __forceinline__ double at(int i) const { return static_cast<double>(v[i]); }
+};
+
 // Pairwise tree over values pushed in index order (0 + 1, 2 + 3, then pairs of
 // pairs, ...); node[kLevels] is the root once 2^kLevels values are in.
 template <int kLevels, typename T>

@@ -61,34 +61,94 @@ constexpr int kDaShare = 128 / (kDaCols * 2);         // blocks sharing a 128-by
 static_assert(kDaBlocks % (8 * kDaShare) == 0, "da block to column mapping");
 static_assert(kDaSteps == 48, "a slot is one leaf of 48 rows");
 
+// 8 consecutive elements of one row: one 16-byte load (bf16) or two (fp32)
+template <typename T>
+struct Row8;
+template <>
+struct Row8<uint16_t> {
+  uint4 v;
+  __device__ __forceinline__ void load(const Buffer& b, uint32_t lane_off, uint32_t off) {
+    v = b.u128(lane_off, off);
+  }
+  __device__ __forceinline__ void unpack(float (&f)[8]) const { unpack8(v, f); }
+};
+template <>
+struct Row8<float> {
+  uint4 v[2];
+  __device__ __forceinline__ void load(const Buffer& b, uint32_t lane_off, uint32_t off) {
+    v[0] = b.u128(lane_off, off);
+    v[1] = b.u128(lane_off, off + 16);
+  }
+  __device__ __forceinline__ void unpack(float (&f)[8]) const {
+    const uint32_t u[8] = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = __uint_as_float(u[e]);
+  }
+};
+
+// 2 consecutive elements of one row
+template <typename T>
+struct Pair;
+template <>
+struct Pair<uint16_t> {
+  uint32_t v;
+  __device__ __forceinline__ void load(const Buffer& b, uint32_t lane_off, uint32_t off) { v = b.u32(lane_off, off); }
+  __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint32_t*>(p); }
+  __device__ __forceinline__ float lo() const { return bf_lo(v); }
+  __device__ __forceinline__ float hi() const { return bf_hi(v); }
+  __device__ __forceinline__ static void store(uint16_t* p, float a, float b) {
+    *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(a, b);
+  }
+};
+template <>
+struct Pair<float> {
+  uint32_t v[2];
+  __device__ __forceinline__ void load(const Buffer& b, uint32_t lane_off, uint32_t off) {
+    const auto t = __builtin_amdgcn_raw_buffer_load_b64(b.rsrc, lane_off, off, 0);
+    v[0] = t[0];
+    v[1] = t[1];
+  }
+  __device__ __forceinline__ void load(const float* p) {
+    const uint2 t = *reinterpret_cast<const uint2*>(p);
+    v[0] = t.x;
+    v[1] = t.y;
+  }
+  __device__ __forceinline__ float lo() const { return __uint_as_float(v[0]); }
+  __device__ __forceinline__ float hi() const { return __uint_as_float(v[1]); }
+  __device__ __forceinline__ static void store(float* p, float a, float b) {
+    *reinterpret_cast<float2*>(p) = make_float2(a, b);
+  }
+};
+
 __device__ __forceinline__ int da_first_col(int L) {
   const int g = L / (8 * kDaShare), q = (L / 8) % kDaShare, xcd = L % 8;
   return ((g * 8 + xcd) * kDaShare + q) * kDaCols;
 }
 
-// da and dtemb for samples b0 .. b0 + nb - 1 (nb <= NB) and the 32 columns of
-// block L.  red: LDS, kDaSlots * NB * kDaCols doubles.
-template <int NB>
-__device__ __forceinline__ void da_block(const float* __restrict__ d_emb, const uint16_t* __restrict__ W,
-                                         const uint16_t* __restrict__ temb, uint16_t* __restrict__ dtemb,
+// da and dtemb for samples b0 .. b0 + nb - 1 (nb <= NB) and the 16 columns of
+// block L; T is the storage type of W, temb and dtemb.  red: LDS,
+// kDaSlots * NB * kDaCols doubles.
+template <int NB, typename T>
+__device__ __forceinline__ void da_block(const float* __restrict__ d_emb, const T* __restrict__ W,
+                                         const T* __restrict__ temb, T* __restrict__ dtemb,
                                          int L, int64_t b0, int nb, double* red) {
   // rows per batch (two batches in flight), sized to keep registers <= ~128
-  constexpr int U = NB == 1 ? 8 : (NB == 2 ? 6 : (NB == 3 ? 6 : 4));
+  constexpr int U = sizeof(T) == 4 ? 4 : (NB == 1 ? 8 : (NB == 2 ? 6 : (NB == 3 ? 6 : 4)));
   static_assert(kDaSteps % (2 * U) == 0, "batch pairs");
   static_assert(kDaSteps % U == 0, "batches");
   const int ct = threadIdx.x % kDaColThreads;
   const int slot = threadIdx.x / kDaColThreads;
   const int col0 = da_first_col(L);
-  const Buffer wb(W, static_cast<uint32_t>(kN) * kD * 2);
+  const Buffer wb(W, static_cast<uint32_t>(kN) * kD * sizeof(T));
   const Buffer eb(d_emb + b0 * kN, static_cast<uint32_t>(nb) * kN * 4);
-  const uint32_t w_lane = (static_cast<uint32_t>(slot) * kD + col0 + ct * 8) * 2;
+  const uint32_t w_lane = (static_cast<uint32_t>(slot) * kD + col0 + ct * 8) * sizeof(T);
   const uint32_t e_lane = static_cast<uint32_t>(slot) * 4;
-  constexpr uint32_t kWStep = kDaSlots * kD * 2;   // bytes between a slot's rows
+  constexpr uint32_t kWStep = kDaSlots * kD * sizeof(T);   // bytes between a slot's rows
   constexpr uint32_t kEStep = kDaSlots * 4;
 
-  auto load = [&](int i0, uint4 (&w)[U], float (&d)[U][NB]) __attribute__((always_inline)) {
+  auto load = [&](int i0, Row8<T> (&w)[U], float (&d)[U][NB]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) w[u] = wb.u128(w_lane, (i0 + u) * kWStep);
+    for (int u = 0; u < U; ++u) w[u].load(wb, w_lane, (i0 + u) * kWStep);
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -102,11 +162,11 @@ __device__ __forceinline__ void da_block(const float* __restrict__ d_emb, const 
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[b][e] = 0.0;
-  auto accumulate = [&](const uint4 (&w)[U], const float (&d)[U][NB]) __attribute__((always_inline)) {
+  auto accumulate = [&](const Row8<T> (&w)[U], const float (&d)[U][NB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float wf[8];
-      unpack8(w[u], wf);
+      w[u].unpack(wf);
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const double dd = static_cast<double>(d[u][b]);
@@ -117,7 +177,7 @@ __device__ __forceinline__ void da_block(const float* __restrict__ d_emb, const 
   };
 
   // two register batches: the next one is in flight while one is added
-  uint4 wa[U], wbt[U];
+  Row8<T> wa[U], wbt[U];
   float da_[U][NB], db_[U][NB];
   load(0, wa, da_);
   // (scheduling barriers keep the compiler from hoisting a batch's loads
@@ -157,7 +217,7 @@ __device__ __forceinline__ void da_block(const float* __restrict__ d_emb, const 
     const int b = threadIdx.x / kDaCols, c = threadIdx.x % kDaCols;
     if (b < nb) {
       const int64_t i = (b0 + b) * kD + col0 + c;
-      dtemb[i] = f32_to_bf16(static_cast<float>(red[threadIdx.x]) * dsilu_f32(bf16_to_f32(temb[i])));
+      dtemb[i] = Storage<T>::store1(static_cast<float>(red[threadIdx.x]) * dsilu_f32(Storage<T>::load1(temb[i])));
     }
   }
 }
@@ -250,7 +310,7 @@ __global__ __launch_bounds__(kThreads) void proj_bwd_small_kernel(
   __shared__ __align__(16) unsigned char smem[ProjBwdShared<NB>::kBytes];
   const int blk = blockIdx.x;
   if (blk < kDaBlocks) {
-    da_block<NB>(d_emb, W, temb, dtemb, blk, 0, NB, reinterpret_cast<double*>(smem));
+    da_block<NB, uint16_t>(d_emb, W, temb, dtemb, blk, 0, NB, reinterpret_cast<double*>(smem));
   } else {
     const int t = blk - kDaBlocks;
     dw_tile<NB>(d_emb, temb, dW, db, t % kDwParts, t / kDwParts,
@@ -269,65 +329,57 @@ __global__ __launch_bounds__(256) void silu_kernel(const uint16_t* __restrict__ 
   }
 }
 
-// ---- B > 4: matrix cores ----------------------------------------------------
-// dW: a wave computes 64 rows x 16 kCT columns as 4 x kCT output tiles; tile
-// (m, n) holds rows j0 + 4 i + m and columns k0 + kCT c + n (i, c = 0 .. 15),
-// so a lane's operands per sample are 16 contiguous bytes of d_emb (4 rows)
-// and 2 kCT contiguous bytes of a (kCT columns).  Step s feeds samples
-// 4 s .. 4 s + 3 (slot g = sample 4 s + g): each sum is the chain over samples
-// in ascending order from +0, as in dw_tile.  Samples past B enter with
-// d_emb = 0, which leaves every sum unchanged (the chain never holds -0).
-// Waves of column block 0 also sum db for their 64 rows.
+// ---- matrix cores -------------------------------------------------------------
+// dW: a wave computes 64 rows x 32 columns as 4 x 2 output tiles; tile (m, n)
+// holds rows j0 + 4 i + m and columns k0 + 2 c + n (i, c = 0 .. 15), so a
+// lane's operands per sample are 16 contiguous bytes of d_emb (4 rows) and
+// two contiguous elements of a.  Step s feeds samples 4 s .. 4 s + 3 (slot g =
+// sample 4 s + g): each sum is the chain over samples in ascending order from
+// +0, as in dw_tile.  Samples past B enter with d_emb = 0, which leaves every
+// sum unchanged (the chain never holds -0).  Waves of column block 0 also sum
+// db for their 64 rows.  T: storage type of a, dW and db.
 constexpr int kDwMRows = 64;
+constexpr int kDwMCols = 32;
 constexpr int kDwMWaves = 4;
 
-template <int kCT>
+template <typename T>
 __global__ __launch_bounds__(64 * kDwMWaves) void dw_mfma_kernel(const float* __restrict__ d_emb,
-                                                                 const uint16_t* __restrict__ a,
-                                                                 uint16_t* __restrict__ dW,
-                                                                 uint16_t* __restrict__ db, int64_t B) {
-  constexpr int kCols = 16 * kCT;
+                                                                 const T* __restrict__ a,
+                                                                 T* __restrict__ dW,
+                                                                 T* __restrict__ db, int64_t B) {
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
   const int j0 = static_cast<int>(blockIdx.x) * kDwMRows;
-  const int k0 = (static_cast<int>(blockIdx.y) * kDwMWaves + wave) * kCols;
+  const int k0 = (static_cast<int>(blockIdx.y) * kDwMWaves + wave) * kDwMCols;
   const int64_t steps = (B + 3) / 4;
 
-  f64x4_t acc[4][kCT];
+  f64x4_t acc[4][2];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int n = 0; n < kCT; ++n) acc[m][n] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+    for (int n = 0; n < 2; ++n) acc[m][n] = f64x4_t{0.0, 0.0, 0.0, 0.0};
 
   const float* dp = d_emb + j0 + 4 * r;
-  const uint16_t* ap = a + k0 + kCT * r;
-  auto load = [&](int64_t st, float4& dv, uint32_t (&av)[(kCT + 1) / 2]) {
+  const T* ap = a + k0 + 2 * r;
+  auto load = [&](int64_t st, float4& dv, Pair<T>& av) {
     const int64_t b = 4 * st + g;
     const int64_t bc = b < B ? b : B - 1;
     dv = *reinterpret_cast<const float4*>(dp + bc * kN);
-    if constexpr (kCT == 4) {
-      const uint2 v = *reinterpret_cast<const uint2*>(ap + bc * kD);
-      av[0] = v.x;
-      av[1] = v.y;
-    } else {
-      av[0] = *reinterpret_cast<const uint32_t*>(ap + bc * kD);
-    }
+    av.load(ap + bc * kD);
     if (b >= B) dv = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   };
-  auto step = [&](const float4& dv, const uint32_t (&av)[(kCT + 1) / 2]) {
+  auto step = [&](const float4& dv, const Pair<T>& av) {
     const double dd[4] = {static_cast<double>(dv.x), static_cast<double>(dv.y), static_cast<double>(dv.z),
                           static_cast<double>(dv.w)};
-    double aa[kCT];
-#pragma unroll
-    for (int n = 0; n < kCT; ++n) aa[n] = bf_half64(av[n / 2], n & 1);
+    const double aa[2] = {static_cast<double>(av.lo()), static_cast<double>(av.hi())};
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int n = 0; n < kCT; ++n) acc[m][n] = mfma_f64(dd[m], aa[n], acc[m][n]);
+      for (int n = 0; n < 2; ++n) acc[m][n] = mfma_f64(dd[m], aa[n], acc[m][n]);
   };
   float4 d0, d1;
-  uint32_t a0[(kCT + 1) / 2], a1[(kCT + 1) / 2];
+  Pair<T> a0, a1;
   load(0, d0, a0);
   int64_t st = 0;
   for (; st + 2 <= steps; st += 2) {
@@ -338,25 +390,17 @@ __global__ __launch_bounds__(64 * kDwMWaves) void dw_mfma_kernel(const float* __
   }
   if (st < steps) step(d0, a0);
 
-  // lane holds rows j0 + 4 (g + 4 v) + m, columns k0 + kCT r + n
+  // lane holds rows j0 + 4 (g + 4 v) + m, columns k0 + 2 r + n
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      uint16_t* o = dW + static_cast<int64_t>(j0 + 4 * (g + 4 * v) + m) * kD + k0 + kCT * r;
-      if constexpr (kCT == 4) {
-        *reinterpret_cast<uint2*>(o) = make_uint2(
-            pack_bf16x2(static_cast<float>(acc[m][0][v]), static_cast<float>(acc[m][1][v])),
-            pack_bf16x2(static_cast<float>(acc[m][2][v]), static_cast<float>(acc[m][3][v])));
-      } else {
-        *reinterpret_cast<uint32_t*>(o) =
-            pack_bf16x2(static_cast<float>(acc[m][0][v]), static_cast<float>(acc[m][1][v]));
-      }
-    }
+    for (int v = 0; v < 4; ++v)
+      Pair<T>::store(dW + static_cast<int64_t>(j0 + 4 * (g + 4 * v) + m) * kD + k0 + 2 * r,
+                     static_cast<float>(acc[m][0][v]), static_cast<float>(acc[m][1][v]));
   if (blockIdx.y == 0 && wave == 0) {
     double sdb = 0.0;
     for (int64_t b = 0; b < B; ++b) sdb += static_cast<double>(d_emb[b * kN + j0 + lane]);
-    db[j0 + lane] = f32_to_bf16(static_cast<float>(sdb));
+    db[j0 + lane] = Storage<T>::store1(static_cast<float>(sdb));
   }
 }
 
@@ -379,15 +423,18 @@ constexpr int kDaMGroup = 4;                   // leaves run side by side
 constexpr int kDaMCols = 32;
 constexpr int kDaMAhead = 1;                   // steps in flight
 
+template <typename T>
 struct DaStep {
   uint4 d;          // d_emb of the group's 4 leaves
-  uint32_t w[4];    // W, 2 columns, per leaf
+  Pair<T> w[4];     // W, 2 columns, per leaf
 };
 
+// T: storage type of W, temb and dtemb
+template <typename T>
 __global__ __launch_bounds__(64 * kDaMWaves) void da_mfma_kernel(const float* __restrict__ d_emb,
-                                                                 const uint16_t* __restrict__ W,
-                                                                 const uint16_t* __restrict__ temb,
-                                                                 uint16_t* __restrict__ dtemb, int64_t B) {
+                                                                 const T* __restrict__ W,
+                                                                 const T* __restrict__ temb,
+                                                                 T* __restrict__ dtemb, int64_t B) {
   __shared__ f64x4_t sub[kDaMWaves - 1][2][64];   // 28 KB
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
@@ -399,22 +446,22 @@ __global__ __launch_bounds__(64 * kDaMWaves) void da_mfma_kernel(const float* __
   const int br = r < rows_here ? r : rows_here - 1;
 
   const Buffer eb(d_emb + b0 * kN, static_cast<uint32_t>(rows_here) * kN * 4);
-  const Buffer wbuf(W, static_cast<uint32_t>(kN) * kD * 2);
+  const Buffer wbuf(W, static_cast<uint32_t>(kN) * kD * sizeof(T));
   const uint32_t e_off = (static_cast<uint32_t>(br) * kN + kDaSlots * g) * 4;
-  const uint32_t w_off = (static_cast<uint32_t>(kDaSlots * g) * kD + k0 + 2 * r) * 2;
+  const uint32_t w_off = (static_cast<uint32_t>(kDaSlots * g) * kD + k0 + 2 * r) * sizeof(T);
   const int leaf0 = wave * kDaMLeaves;
 
   PairTree<ilog2(kDaMLeaves), f64x4_t> tree[2];
   static_for<0, kDaMLeaves / kDaMGroup>([&](auto qc) {
     constexpr int q = decltype(qc)::value;
     const int t0 = leaf0 + kDaMGroup * q;
-    auto load = [&](DaStep& d, int st) {
+    auto load = [&](DaStep<T>& d, int st) {
       const uint32_t row = static_cast<uint32_t>(t0 + kDaSlots * 4 * st);   // + 128 g in the lane offset
       d.d = eb.u128(e_off, row * 4);
 #pragma unroll
-      for (int l = 0; l < kDaMGroup; ++l) d.w[l] = wbuf.u32(w_off, (row + l) * kD * 2);
+      for (int l = 0; l < kDaMGroup; ++l) d.w[l].load(wbuf, w_off, (row + l) * kD * sizeof(T));
     };
-    DaStep buf[kDaMAhead + 1];
+    DaStep<T> buf[kDaMAhead + 1];
 #pragma unroll
     for (int st = 0; st < kDaMAhead; ++st) load(buf[st], st);
     f64x4_t acc[kDaMGroup][2];
@@ -423,13 +470,13 @@ __global__ __launch_bounds__(64 * kDaMWaves) void da_mfma_kernel(const float* __
 #pragma unroll
     for (int st = 0; st < kLeafSteps; ++st) {
       if (st + kDaMAhead < kLeafSteps) load(buf[(st + kDaMAhead) % (kDaMAhead + 1)], st + kDaMAhead);
-      const DaStep& cur = buf[st % (kDaMAhead + 1)];
+      const DaStep<T>& cur = buf[st % (kDaMAhead + 1)];
       const uint32_t dv[4] = {cur.d.x, cur.d.y, cur.d.z, cur.d.w};
 #pragma unroll
       for (int l = 0; l < kDaMGroup; ++l) {
         const double dd = static_cast<double>(__uint_as_float(dv[l]));
-        acc[l][0] = mfma_f64(dd, bf_lo64(cur.w[l]), acc[l][0]);
-        acc[l][1] = mfma_f64(dd, bf_hi64(cur.w[l]), acc[l][1]);
+        acc[l][0] = mfma_f64(dd, static_cast<double>(cur.w[l].lo()), acc[l][0]);
+        acc[l][1] = mfma_f64(dd, static_cast<double>(cur.w[l].hi()), acc[l][1]);
       }
     }
     static_for<0, kDaMGroup>([&](auto lc) {
@@ -460,12 +507,22 @@ __global__ __launch_bounds__(64 * kDaMWaves) void da_mfma_kernel(const float* __
     const int sr = g + 4 * v;
     if (sr < rows_here) {
       const int64_t i = (b0 + sr) * kD + k0 + 2 * r;
-      const uint32_t z = *reinterpret_cast<const uint32_t*>(temb + i);
-      *reinterpret_cast<uint32_t*>(dtemb + i) =
-          pack_bf16x2(static_cast<float>(tot[0][v]) * dsilu_f32(bf_lo(z)),
-                      static_cast<float>(tot[1][v]) * dsilu_f32(bf_hi(z)));
+      Pair<T> z;
+      z.load(temb + i);
+      Pair<T>::store(dtemb + i, static_cast<float>(tot[0][v]) * dsilu_f32(z.lo()),
+                     static_cast<float>(tot[1][v]) * dsilu_f32(z.hi()));
     }
   }
+}
+
+// da and dtemb for fp32 storage and B = NB <= 4 (the vector da blocks)
+template <int NB>
+__global__ __launch_bounds__(kThreads) void da_small_f32_kernel(const float* __restrict__ d_emb,
+                                                                const float* __restrict__ W,
+                                                                const float* __restrict__ temb,
+                                                                float* __restrict__ dtemb) {
+  __shared__ __align__(16) double red[kDaSlots * NB * kDaCols];
+  da_block<NB, float>(d_emb, W, temb, dtemb, blockIdx.x, 0, NB, red);
 }
 
 }  // namespace
@@ -487,8 +544,7 @@ hipError_t launch_proj_bwd_fused(const float* d_emb, const uint16_t* temb, const
 
 hipError_t launch_proj_bwd_dw(const float* d_emb, const uint16_t* a, uint16_t* dW, uint16_t* db, int64_t B,
                               hipStream_t s) {
-  constexpr int kCT = 2;
-  hipLaunchKernelGGL(dw_mfma_kernel<kCT>, dim3(kN / kDwMRows, kD / (16 * kCT * kDwMWaves)),
+  hipLaunchKernelGGL(dw_mfma_kernel<uint16_t>, dim3(kN / kDwMRows, kD / (kDwMCols * kDwMWaves)),
                      dim3(64 * kDwMWaves), 0, s, d_emb, a, dW, db, B);
   return hipGetLastError();
 }
@@ -496,8 +552,8 @@ hipError_t launch_proj_bwd_dw(const float* d_emb, const uint16_t* a, uint16_t* d
 hipError_t launch_proj_bwd_da(const float* d_emb, const uint16_t* W, const uint16_t* temb, uint16_t* dtemb,
                               int64_t B, hipStream_t s) {
   const int64_t by = (B + 15) / 16;
-  hipLaunchKernelGGL(da_mfma_kernel, dim3(kD / kDaMCols, static_cast<unsigned>(by)), dim3(64 * kDaMWaves), 0, s,
-                     d_emb, W, temb, dtemb, B);
+  hipLaunchKernelGGL(da_mfma_kernel<uint16_t>, dim3(kD / kDaMCols, static_cast<unsigned>(by)), dim3(64 * kDaMWaves),
+                     0, s, d_emb, W, temb, dtemb, B);
   return hipGetLastError();
 }
 
@@ -507,5 +563,28 @@ hipError_t launch_silu(const uint16_t* temb, uint16_t* a, int64_t n, hipStream_t
   return hipGetLastError();
 }
 
+
+// fp32 storage: a = SiLU(temb) into `a`, dW and db on the matrix cores for
+// every B, da and dtemb on the vector units for B <= 4 and the matrix cores
+// beyond (the same leaves and order either way)
+hipError_t launch_proj_bwd_f32(const float* d_emb, const float* temb, const float* W, float* a, float* dW,
+                               float* db, float* dtemb, int64_t B, hipStream_t s) {
+  if (hipError_t e = launch_silu_f32(temb, a, B * kD, s); e != hipSuccess) return e;
+  hipLaunchKernelGGL(dw_mfma_kernel<float>, dim3(kN / kDwMRows, kD / (kDwMCols * kDwMWaves)),
+                     dim3(64 * kDwMWaves), 0, s, d_emb, a, dW, db, B);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  switch (B) {
+    case 1: hipLaunchKernelGGL(da_small_f32_kernel<1>, dim3(kDaBlocks), dim3(kThreads), 0, s, d_emb, W, temb, dtemb); break;
+    case 2: hipLaunchKernelGGL(da_small_f32_kernel<2>, dim3(kDaBlocks), dim3(kThreads), 0, s, d_emb, W, temb, dtemb); break;
+    case 3: hipLaunchKernelGGL(da_small_f32_kernel<3>, dim3(kDaBlocks), dim3(kThreads), 0, s, d_emb, W, temb, dtemb); break;
+    case 4: hipLaunchKernelGGL(da_small_f32_kernel<4>, dim3(kDaBlocks), dim3(kThreads), 0, s, d_emb, W, temb, dtemb); break;
+    default: {
+      const int64_t by = (B + 15) / 16;
+      hipLaunchKernelGGL(da_mfma_kernel<float>, dim3(kD / kDaMCols, static_cast<unsigned>(by)),
+                         dim3(64 * kDaMWaves), 0, s, d_emb, W, temb, dtemb, B);
+    }
+  }
+  return hipGetLastError();
+}
 
 }  // namespace adaln

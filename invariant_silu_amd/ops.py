@@ -121,41 +121,54 @@ def token_tree_sum(x: torch.Tensor) -> torch.Tensor:
     return out
 
 
+_STORAGE = (torch.bfloat16, torch.float32)
+
+
 def fwd(x: torch.Tensor, temb: torch.Tensor, W: torch.Tensor, bias: torch.Tensor, eps: float = EPS):
-    """One-call forward (adaln_fwd): (out, emb, mean, rstd), same bits as
-    proj_fwd followed by norm_mod_fwd."""
+    """One-call forward (adaln_fwd, or adaln_fwd_f32 for fp32 tensors):
+    (out, emb, mean, rstd); with bf16 tensors the same bits as proj_fwd
+    followed by norm_mod_fwd."""
+    dt = x.dtype
+    if dt not in _STORAGE:
+        raise TypeError(f"x must be bfloat16 or float32, got {dt}")
     for t, n in ((x, "x"), (temb, "temb"), (W, "W"), (bias, "bias")):
-        _check(t, torch.bfloat16, n)
+        _check(t, dt, n)
     x, temb, W, bias = aligned(x), aligned(temb), aligned(W), aligned(bias)
     B, S, Dx = x.shape
-    emb = torch.empty((B, N), dtype=torch.bfloat16, device=x.device)
+    emb = torch.empty((B, N), dtype=dt, device=x.device)
     out = torch.empty_like(x)
     mean = torch.empty((B, S), dtype=torch.float32, device=x.device)
     rstd = torch.empty((B, S), dtype=torch.float32, device=x.device)
-    _lib.call("adaln_fwd", temb.data_ptr(), W.data_ptr(), bias.data_ptr(), x.data_ptr(), emb.data_ptr(),
-              out.data_ptr(), mean.data_ptr(), rstd.data_ptr(), B, S, Dx, float(eps), _stream(x.device))
+    _lib.call("adaln_fwd" if dt == torch.bfloat16 else "adaln_fwd_f32", temb.data_ptr(), W.data_ptr(),
+              bias.data_ptr(), x.data_ptr(), emb.data_ptr(), out.data_ptr(), mean.data_ptr(), rstd.data_ptr(),
+              B, S, Dx, float(eps), _stream(x.device))
     return out, emb, mean, rstd
 
 
 def bwd(g: torch.Tensor, x: torch.Tensor, mean: torch.Tensor, rstd: torch.Tensor, emb: torch.Tensor,
         temb: torch.Tensor, W: torch.Tensor):
-    """One-call backward (adaln_bwd): (dx, d_emb, dW, db, dtemb), same bits as
+    """One-call backward (adaln_bwd, or adaln_bwd_f32 for fp32 tensors):
+    (dx, d_emb, dW, db, dtemb); with bf16 tensors the same bits as
     norm_mod_bwd followed by proj_bwd."""
-    for t, n, dt in ((g, "g", torch.bfloat16), (x, "x", torch.bfloat16), (mean, "mean", torch.float32),
-                     (rstd, "rstd", torch.float32), (emb, "emb", torch.bfloat16),
-                     (temb, "temb", torch.bfloat16), (W, "W", torch.bfloat16)):
-        _check(t, dt, n)
+    dt = x.dtype
+    if dt not in _STORAGE:
+        raise TypeError(f"x must be bfloat16 or float32, got {dt}")
+    for t, n, tdt in ((g, "g", dt), (x, "x", dt), (mean, "mean", torch.float32),
+                      (rstd, "rstd", torch.float32), (emb, "emb", dt), (temb, "temb", dt), (W, "W", dt)):
+        _check(t, tdt, n)
     g, x, mean, rstd, emb, temb, W = (aligned(t) for t in (g, x, mean, rstd, emb, temb, W))
     B, S, Dx = x.shape
     dx = torch.empty_like(x)
     d_emb = torch.empty((B, N), dtype=torch.float32, device=x.device)
     dW = torch.empty_like(W)
-    db = torch.empty((W.shape[0],), dtype=torch.bfloat16, device=W.device)
+    db = torch.empty((W.shape[0],), dtype=dt, device=W.device)
     dtemb = torch.empty_like(temb)
-    ws = _ws(_lib.OP_BWD, B, S, Dx, x.device)
-    _lib.call("adaln_bwd", g.data_ptr(), x.data_ptr(), mean.data_ptr(), rstd.data_ptr(), emb.data_ptr(),
-              temb.data_ptr(), W.data_ptr(), dx.data_ptr(), d_emb.data_ptr(), dW.data_ptr(), db.data_ptr(),
-              dtemb.data_ptr(), ws.data_ptr(), ws.numel(), B, S, Dx, _stream(x.device))
+    f32 = dt == torch.float32
+    ws = _ws(_lib.OP_BWD_F32 if f32 else _lib.OP_BWD, B, S, Dx, x.device)
+    _lib.call("adaln_bwd_f32" if f32 else "adaln_bwd", g.data_ptr(), x.data_ptr(), mean.data_ptr(),
+              rstd.data_ptr(), emb.data_ptr(), temb.data_ptr(), W.data_ptr(), dx.data_ptr(), d_emb.data_ptr(),
+              dW.data_ptr(), db.data_ptr(), dtemb.data_ptr(), ws.data_ptr(), ws.numel(), B, S, Dx,
+              _stream(x.device))
     return dx, d_emb, dW, db, dtemb
 
 
@@ -166,9 +179,10 @@ def selftest() -> int:
 class AdaLNFinal(torch.autograd.Function):
     """out = LayerNorm(x) * (1 + scale) + shift with (scale, shift) = (SiLU(temb) W^T + b).chunk(2).
 
-    Inputs: x [B, S, 3072] bf16, temb [B, 3072] bf16, W [6144, 3072] bf16,
-    b [6144] bf16.  Saves x, temb, W, emb, mean and rstd (8 bytes per row of
-    LayerNorm state, not the normalized activations)."""
+    Inputs: x [B, S, 3072], temb [B, 3072], W [6144, 3072], b [6144], all bf16
+    (the autocast rounding points) or all fp32 (fp32 storage).  Saves x, temb,
+    W, emb, mean and rstd (8 bytes per row of LayerNorm state, not the
+    normalized activations)."""
 
     @staticmethod
     def forward(ctx, x, temb, W, b, eps=EPS):
@@ -179,7 +193,7 @@ class AdaLNFinal(torch.autograd.Function):
     @staticmethod
     def backward(ctx, g):
         x, temb, W, emb, mean, rstd = ctx.saved_tensors
-        g = g.to(torch.bfloat16)
+        g = g.to(x.dtype)
         dx, d_emb, dW, db, dtemb = bwd(g, x, mean, rstd, emb, temb, W)
         return dx, dtemb, dW, db, None
 

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_strerror(L):
-    assert L.adaln_abi_version() == 2
+    assert L.adaln_abi_version() == 3
     for code in range(-7, 1):
         assert len(lib.strerror(code)) >= 2
 
@@ -59,6 +59,7 @@ def test_workspace_sizes(L):
         assert lib.workspace_bytes(lib.OP_TOKEN_TREE_SUM, B, S, 100) == pad(B * T0 * 128 * 8)
         assert lib.workspace_bytes(lib.OP_PROJ_BWD, B, S, 3072) == pad(B * 3072 * 2)
         assert lib.workspace_bytes(lib.OP_PROJ_FWD, B, S, 3072) == pad(B * 3072 * 2)
+        assert lib.workspace_bytes(lib.OP_BWD_F32, B, S, 3072) == pad(B * T0 * 6144 * 8) + pad(B * 3072 * 4)
     assert lib.workspace_bytes(lib.OP_NORM_MOD_BWD, 1, 10, 1024) == 0
     assert lib.workspace_bytes(99, 1, 10, 3072) == 0
     assert lib.workspace_bytes(lib.OP_PROJ_BWD, 0, 1, 3072) == 0
@@ -70,6 +71,13 @@ def test_validation_before_device_work(L):
     assert L.adaln_proj_fwd(None, None, None, None, None, 0, 1, 3072, 6144, None) == lib.ERR_NULL
     p = 4096   # a fake, aligned, non-null address: shape checks come first
     assert L.adaln_proj_fwd(p, p, p, p, p, 1 << 20, 1, 1024, 6144, None) == lib.ERR_SHAPE
+    # fp32 storage entry points: the same checks, fp32 sizes
+    assert L.adaln_fwd_f32(None, p, p, p, p, p, p, p, 1, 4, 3072, 1e-6, None) == lib.ERR_NULL
+    assert L.adaln_fwd_f32(p, p, p, p, p, p, p, p, 1, 4, 1024, 1e-6, None) == lib.ERR_SHAPE
+    assert L.adaln_fwd_f32(p + 8, p, p, p, p, p, p, p, 1, 4, 3072, 1e-6, None) == lib.ERR_ALIGN
+    bufs = [p + (k << 28) for k in range(13)]
+    assert L.adaln_bwd_f32(*bufs, 16, 2, 64, 3072, None) == lib.ERR_WORKSPACE
+    assert L.adaln_bwd_f32(*bufs[:12], None, 1 << 20, 2, 64, 3072, None) == lib.ERR_NULL
     # a workspace smaller than adaln_workspace_bytes(PROJ_FWD) is refused
     assert L.adaln_proj_fwd(p, p + (1 << 20), p + (2 << 20), p + (3 << 20), p + (4 << 20), 16,
                             8, 3072, 6144, None) == lib.ERR_WORKSPACE
