@@ -6,7 +6,8 @@ C ABI: adaln_fwd (projection and LayerNorm statistics side by side, then the
 modulation) and adaln_bwd (dx rows and level-0 token tiles in one launch, the
 tree fold, then the projection backward: dW and db, da and dtemb).  Default
 workload: one 1024x1024 image stream, B = 1, S = 4096 tokens, D = 3072, bf16
-storage, 1% outlier rows x20.
+storage, 1% outlier rows x20.  --storage fp32 runs the fp32-storage entry
+points (adaln_fwd_f32 / adaln_bwd_f32) on the same draws, unrounded.
 
 Inputs are resident in HBM before the timed region.  The step rotates over
 several independent copies of every buffer (parameters included), so no step
@@ -42,19 +43,21 @@ SAMPLE = 8        # the dominant kernel is timed on every SAMPLE-th timed step
 METRIC = "fwd+bwd tokens/sec + achieved HBM GB/s at S=4096 D=3072 bf16 (batch-invariant)"
 
 
-def algorithmic_bytes(B: int, S: int) -> int:
-    """Bytes the method must move per step (no partials, no re-reads):
-    x read twice, out, g, dx (10 B per element); mean/rstd written and read;
-    W read twice, dW written; b read, db written; per-sample vectors."""
-    return 10 * B * S * D + 16 * B * S + 6 * N * D + 4 * N + 98304 * B
+def algorithmic_bytes(B: int, S: int, el: int = 2) -> int:
+    """Bytes the method must move per step (no partials, no re-reads), with
+    el-byte storage: x read twice, out, g, dx (5 el B per element); mean/rstd
+    written and read; W read twice, dW written; b read, db written; per-sample
+    vectors (temb twice, emb written and read, scale read, dtemb: 24 K
+    elements; d_emb written and read in fp32: 48 KB)."""
+    return 5 * el * B * S * D + 16 * B * S + 3 * el * N * D + 2 * el * N + (24576 * el + 49152) * B
 
 
-def dominant_kernel_bytes(B: int, S: int) -> int:
-    """The backward's main launch: g and x read, dx written (6 B per element),
-    mean/rstd read, the scale half of emb read per sample.  Its level-0 token
-    tiles (fp32 pairs, 2 x 24 KB per 32-token tile) are implementation
-    overhead, not algorithmic bytes."""
-    return 6 * B * S * D + 8 * B * S + 2 * D * B
+def dominant_kernel_bytes(B: int, S: int, el: int = 2) -> int:
+    """The backward's main launch: g and x read, dx written (3 el B per
+    element), mean/rstd read, the scale half of emb read per sample.  Its
+    level-0 token tiles (fp32 pairs, 2 x 24 KB per 32-token tile) are
+    implementation overhead, not algorithmic bytes."""
+    return 3 * el * B * S * D + 8 * B * S + el * D * B
 
 
 def pmc_traffic():
@@ -80,6 +83,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="img1024_b1_s4096")
+    ap.add_argument("--storage", choices=("bf16", "fp32"), default="bf16",
+                    help="tensor storage type (fp32: the fp32-storage entry points)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true",
                     help="after the steps, run a plain 512 MiB device copy (PMC byte-counter calibration)")
@@ -125,42 +130,50 @@ def main() -> int:
 
     w = WORKLOADS[args.workload]
     B, S = w["B"], w["S"]
-    inp = make_workload(args.workload, seed=0)
+    f32 = args.storage == "fp32"
+    el = 4 if f32 else 2
+    inp = make_workload(args.workload, seed=0, io=args.storage)
+    sdt = torch.float32 if f32 else torch.bfloat16
 
-    def to_dev(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+    def to_dev(a):
+        if f32:
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
     base = {k: to_dev(inp[k]) for k in ("x", "temb", "W", "bias", "g")}
-    ws_bw = lib.workspace_bytes(lib.OP_BWD, B, S, D)
+    ws_bw = lib.workspace_bytes(lib.OP_BWD_F32 if f32 else lib.OP_BWD, B, S, D)
 
     def new_set():
         s = {k: v.clone() for k, v in base.items()}
         s.update(
-            emb=torch.empty((B, N), dtype=torch.bfloat16, device=dev),
-            out=torch.empty((B, S, D), dtype=torch.bfloat16, device=dev),
+            emb=torch.empty((B, N), dtype=sdt, device=dev),
+            out=torch.empty((B, S, D), dtype=sdt, device=dev),
             mean=torch.empty((B, S), dtype=torch.float32, device=dev),
             rstd=torch.empty((B, S), dtype=torch.float32, device=dev),
-            dx=torch.empty((B, S, D), dtype=torch.bfloat16, device=dev),
+            dx=torch.empty((B, S, D), dtype=sdt, device=dev),
             d_emb=torch.empty((B, N), dtype=torch.float32, device=dev),
-            dW=torch.empty((N, D), dtype=torch.bfloat16, device=dev),
-            db=torch.empty((N,), dtype=torch.bfloat16, device=dev),
-            dtemb=torch.empty((B, D), dtype=torch.bfloat16, device=dev),
+            dW=torch.empty((N, D), dtype=sdt, device=dev),
+            db=torch.empty((N,), dtype=sdt, device=dev),
+            dtemb=torch.empty((B, D), dtype=sdt, device=dev),
             ws_bw=torch.empty(ws_bw, dtype=torch.uint8, device=dev),
         )
         return s
 
-    per_set = algorithmic_bytes(B, S)
+    per_set = algorithmic_bytes(B, S, el)
     nsets = max(2, math.ceil(3 * MALL_BYTES / per_set))
     sets = [new_set() for _ in range(nsets)]
     stream = torch.cuda.current_stream(dev)
     st = stream.cuda_stream
+    fwd_name, bwd_name = ("adaln_fwd_f32", "adaln_bwd_f32") if f32 else ("adaln_fwd", "adaln_bwd")
+    fwd_fn, bwd_fn = getattr(L, fwd_name), getattr(L, bwd_name)
+
     def step(s):
         p = lambda k: s[k].data_ptr()   # noqa: E731
-        lib.check("adaln_fwd", L.adaln_fwd(p("temb"), p("W"), p("bias"), p("x"), p("emb"), p("out"), p("mean"),
-                                           p("rstd"), B, S, D, 1e-6, st))
-        lib.check("adaln_bwd", L.adaln_bwd(p("g"), p("x"), p("mean"), p("rstd"), p("emb"), p("temb"), p("W"),
-                                           p("dx"), p("d_emb"), p("dW"), p("db"), p("dtemb"), p("ws_bw"),
-                                           ws_bw, B, S, D, st))
+        lib.check(fwd_name, fwd_fn(p("temb"), p("W"), p("bias"), p("x"), p("emb"), p("out"), p("mean"),
+                                   p("rstd"), B, S, D, 1e-6, st))
+        lib.check(bwd_name, bwd_fn(p("g"), p("x"), p("mean"), p("rstd"), p("emb"), p("temb"), p("W"),
+                                   p("dx"), p("d_emb"), p("dW"), p("db"), p("dtemb"), p("ws_bw"),
+                                   ws_bw, B, S, D, st))
 
     for i in range(args.warmup):
         step(sets[i % nsets])
@@ -181,10 +194,10 @@ def main() -> int:
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     tokens_per_s = B * S / (ms_per_step / 1e3)
-    step_bytes = algorithmic_bytes(B, S)
+    step_bytes = algorithmic_bytes(B, S, el)
     k_ms = sorted(ms_buf[i] for i in range(n_timed))
     k_mean_ms = sum(k_ms) / len(k_ms)
-    k_bytes = dominant_kernel_bytes(B, S)
+    k_bytes = dominant_kernel_bytes(B, S, el)
     achieved = k_bytes / (k_mean_ms / 1e3) / 1e9
 
     # achievable-bandwidth ceiling in the same run: a plain device copy moving
@@ -226,16 +239,18 @@ def main() -> int:
         "dtype": "fp32",
         "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "S": S, "D": D, "N": N,
-                   "storage": "bf16", "accumulate": "fp64", "outlier_rows": w["outlier_frac"],
+                   "storage": args.storage, "accumulate": "fp64", "outlier_rows": w["outlier_frac"],
                    "buffer_sets": nsets, "step_algorithmic_bytes": step_bytes,
                    "host_enqueue_ms_per_step": round((t_enq - t0) * 1e3 / args.steps, 5),
                    "step_gbps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
                    "step_frac_of_peak": round(step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
                    "copy_ceiling_gbps": round(copy_gbps, 1),
                    "step_frac_of_copy_ceiling": round(step_bytes / (ms_per_step / 1e3) / 1e9 / copy_gbps, 4)},
-        "roofline": {"bound": "hbm", "kernel": "norm_mod_bwd_kernel<0> (dx rows + level-0 token tiles)",
+        "roofline": {"bound": "hbm",
+                     "kernel": ("norm_mod_bwd_f32_kernel" if f32 else "norm_mod_bwd_kernel<0>")
+                     + " (dx rows + level-0 token tiles)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": pmc_traffic(),
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None if f32 else pmc_traffic(),
                      "bytes_per_launch": k_bytes, "avg_launch_ms": round(k_mean_ms, 5),
                      "timed_launches": n_timed, "timed_every": SAMPLE,
                      "median_launch_ms": round(k_ms[len(k_ms) // 2], 5)},

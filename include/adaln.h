@@ -211,7 +211,7 @@ int adaln_bwd_f32(const float* gout, const float* x, const float* mean, const fl
                   void* ws, size_t ws_bytes, int64_t B, int64_t S, int64_t D, void* stream);
 
 /* Benchmarking aid: per-launch durations of the main kernel of the backward
- * (adaln_bwd and adaln_norm_mod_bwd: the fused dx + level-0 kernel;
+ * (adaln_bwd, adaln_bwd_f32 and adaln_norm_mod_bwd: the fused dx + level-0 kernel;
  * adaln_norm_mod_bwd_dx: the dx kernel), timed with HIP
  * events carried by the kernel dispatch itself (no extra packets).
  * A timed dispatch leaves the stream idle for a few microseconds around it, so

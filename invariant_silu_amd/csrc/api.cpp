@@ -537,7 +537,10 @@ int adaln_bwd_f32(const float* gout, const float* x, const float* mean, const fl
   const int64_t T0 = ceil_div(S, kTile);
   float* part = static_cast<float*>(ws);
   float* a = reinterpret_cast<float*>(static_cast<char*>(ws) + n_norm);
-  if (int rc = launched(adaln::launch_norm_mod_bwd_f32(gout, x, mean, rstd, emb, dx, part, B, S, s))) return rc;
+  hipEvent_t e0, e1;
+  timing_events(&e0, &e1);
+  if (int rc = launched(adaln::launch_norm_mod_bwd_f32(gout, x, mean, rstd, emb, dx, part, B, S, s, e0, e1)))
+    return rc;
   if (int rc = launched(adaln::launch_tree_fold(part, d_emb, B, T0, kN, s))) return rc;
   return launched(adaln::launch_proj_bwd_f32(d_emb, temb, W, a, dW, db, dtemb, B, s));
 }

@@ -46,7 +46,7 @@ hipError_t launch_norm_mod_fwd_f32(const float* x, const float* emb, float* out,
                                    int64_t B, int64_t S, float eps, hipStream_t s);
 hipError_t launch_norm_mod_bwd_f32(const float* g, const float* x, const float* mean, const float* rstd,
                                    const float* emb, float* dx, float* part, int64_t B, int64_t S,
-                                   hipStream_t s);
+                                   hipStream_t s, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 hipError_t launch_proj_bwd_f32(const float* d_emb, const float* temb, const float* W, float* a, float* dW,
                                float* db, float* dtemb, int64_t B, hipStream_t s);
 hipError_t launch_selftest_probe(const float* in, float* out, uint32_t* bits, int n,

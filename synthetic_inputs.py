@@ -93,9 +93,9 @@ def make_inputs(B: int, S: int, seed: int = 0, outlier_frac: float = 0.0,
     }
 
 
-def make_workload(name: str, seed: int = 0) -> dict:
+def make_workload(name: str, seed: int = 0, io: str = "bf16") -> dict:
     w = WORKLOADS[name]
-    return make_inputs(w["B"], w["S"], seed=seed, outlier_frac=w["outlier_frac"])
+    return make_inputs(w["B"], w["S"], seed=seed, outlier_frac=w["outlier_frac"], io=io)
 
 
 def cancellation_tokens(S: int, pos_big: int, pos_neg: int, big: float = 2.0 ** 26) -> np.ndarray:
