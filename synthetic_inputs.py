@@ -93,6 +93,23 @@ def make_inputs(B: int, S: int, seed: int = 0, outlier_frac: float = 0.0,
     }
 
 
+def make_residual_inputs(B: int, S: int, seed: int = 0, D: int = HIDDEN) -> dict:
+    """One batch for the residual norm site: x, residual [B,S,D], mod [B,3D] =
+    (shift | scale | gate), upstream gradients g_out, g_h [B,S,D]; bf16 bits.
+
+    Draw order x, residual, mod, g_out, g_h; standard normals scaled by 1 (x,
+    residual, gradients) and 0.5 (mod), rounded to bfloat16."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B, S, D), dtype=np.float32)
+    residual = rng.standard_normal((B, S, D), dtype=np.float32)
+    mod = rng.standard_normal((B, 3 * D), dtype=np.float32) * np.float32(0.5)
+    g_out = rng.standard_normal((B, S, D), dtype=np.float32)
+    g_h = rng.standard_normal((B, S, D), dtype=np.float32)
+    return {"x": f32_to_bf16_bits(x), "residual": f32_to_bf16_bits(residual), "mod": f32_to_bf16_bits(mod),
+            "g_out": f32_to_bf16_bits(g_out), "g_h": f32_to_bf16_bits(g_h), "B": B, "S": S, "D": D,
+            "seed": seed}
+
+
 def make_workload(name: str, seed: int = 0, io: str = "bf16") -> dict:
     w = WORKLOADS[name]
     return make_inputs(w["B"], w["S"], seed=seed, outlier_frac=w["outlier_frac"], io=io)

@@ -17,9 +17,9 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from oracle import adaln, fpmath, token_tree
+from oracle import adaln, fpmath, residual, token_tree
 from oracle.fpmath import bf16_ulp_diff, bits_to_f32, f32_to_bf16_bits, nsum
-from synthetic_inputs import cancellation_tokens, make_inputs
+from synthetic_inputs import cancellation_tokens, make_inputs, make_residual_inputs
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 D = 3072
@@ -557,6 +557,99 @@ def test_teeth_bf16_rounding_in_fp32_storage_caught(monkeypatch):
     monkeypatch.setattr(adaln.Arith, "store", lambda self, v: self.bf16(v))
     ok = _fp32_storage_checks(_fp32_identity_case())
     assert not all(ok.values())
+
+
+# ---------------------------------------------------- residual norm site --
+def test_residual_update_closed_forms():
+    """P-18: gate = 0 gives h = residual; residual = 0 with gate = 1 gives h = x
+    (bit for bit: the product and the add are exact there)."""
+    inp = make_residual_inputs(2, 9, seed=51, D=D)
+    Dd = D
+    mod = bits_to_f32(inp["mod"]).copy()
+    mod[:, 2 * Dd:] = 0.0
+    f = residual.residual_forward(dict(inp, mod=f32_to_bf16_bits(mod)))
+    assert np.array_equal(f["h_bits"], inp["residual"])
+    mod[:, 2 * Dd:] = 1.0
+    f = residual.residual_forward(dict(inp, mod=f32_to_bf16_bits(mod), residual=np.zeros_like(inp["residual"])))
+    assert np.array_equal(f["h_bits"], inp["x"])
+
+
+def test_residual_site_reduces_to_norm_out():
+    """P-19: with one sample, the site's out, and with g_h = 0 its dh, d_scale and
+    d_shift, are those of the (separately pinned) norm_out operator applied to
+    h with emb = (scale | shift)."""
+    rinp = make_residual_inputs(1, 21, seed=52, D=D)
+    rinp["g_h"] = np.zeros_like(rinp["g_h"])
+    f = residual.residual_forward(rinp)
+    b = residual.residual_backward(rinp, f)
+    mod = rinp["mod"][0]
+    ninp = {"x": f["h_bits"], "temb": np.zeros((1, D), np.uint16), "W": np.zeros((2 * D, D), np.uint16),
+            "bias": np.concatenate([mod[D:2 * D], mod[:D]]), "g": rinp["g_out"]}
+    nf = adaln.forward(ninp)
+    nb = adaln.backward(ninp, nf)
+    assert np.array_equal(nf["emb_bits"][0], ninp["bias"])
+    assert np.array_equal(f["out_bits"], nf["out_bits"])
+    assert np.array_equal(b["dh_bits"], nb["dx_bits"])
+    assert b["d_scale"].tobytes() == nb["d_scale"].tobytes()
+    assert b["d_shift"].tobytes() == nb["d_shift"].tobytes()
+
+
+def test_residual_site_gradient_closed_forms():
+    """P-20: g_out = 0 gives dh = g_h and dx = bf16(g_h * gate) bit for bit, and
+    with one token d_gate = g_h * x (one exact product), d_scale = d_shift = 0."""
+    rinp = make_residual_inputs(2, 1, seed=53, D=D)
+    rinp["g_out"] = np.zeros_like(rinp["g_out"])
+    f = residual.residual_forward(rinp)
+    b = residual.residual_backward(rinp, f)
+    gh = bits_to_f32(rinp["g_h"])
+    gate = bits_to_f32(rinp["mod"])[:, 2 * D:]
+    assert np.array_equal(b["dh_bits"], rinp["g_h"])
+    assert np.array_equal(b["dx_bits"], f32_to_bf16_bits(gh * gate[:, None, :]))
+    xs = bits_to_f32(rinp["x"])
+    assert b["d_gate"].tobytes() == (gh[:, 0, :] * xs[:, 0, :]).astype(np.float32).tobytes()
+    assert np.all(b["d_scale"] == 0) and np.all(b["d_shift"] == 0)
+
+
+def _residual_fd(seed=54, B=2, S=3, Dd=8, drop_gh=False):
+    rng = np.random.default_rng(seed)
+    inp = {"x_val": rng.standard_normal((B, S, Dd)), "residual_val": rng.standard_normal((B, S, Dd)),
+           "mod_val": rng.standard_normal((B, 3 * Dd)) * 0.5, "g_out_val": rng.standard_normal((B, S, Dd)),
+           "g_h_val": rng.standard_normal((B, S, Dd))}
+    f = residual.residual_forward(inp, "exact")
+    if drop_gh:
+        inp_b = dict(inp, g_h_val=np.zeros_like(inp["g_h_val"]))
+    else:
+        inp_b = inp
+    b = residual.residual_backward(inp_b, f, "exact")
+    G, Gh = inp["g_out_val"], inp["g_h_val"]
+    grads = {"x_val": b["dx"], "residual_val": b["d_residual"], "mod_val": b["d_mod"]}
+    worst = 0.0
+    for key, ana in grads.items():
+        base = inp[key]
+        fd = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            hstep = 1e-6 * max(1.0, abs(base[idx]))
+            for sgn in (1, -1):
+                arr = base.copy()
+                arr[idx] += sgn * hstep
+                ff = residual.residual_forward(dict(inp, **{key: arr}), "exact")
+                L = float((ff["out"] * G).sum() + (ff["h"] * Gh).sum())
+                fd[idx] += sgn * L / (2 * hstep)
+        sc = max(np.abs(fd).max(), 1e-12)
+        worst = max(worst, float(np.abs(fd - ana).max() / sc))
+    return worst
+
+
+def test_residual_site_finite_differences():
+    """P-21: dx, d_residual and d_mod = (d_shift | d_scale | d_gate) against
+    central differences of L = sum(out * g_out) + sum(h * g_h), rounding points
+    disabled."""
+    assert _residual_fd() <= 1e-6
+
+
+def test_teeth_residual_gradient_dropped_caught():
+    """Leaving g_h out of dh fails P-21."""
+    assert _residual_fd(drop_gh=True) > 1e-3
 
 
 # ------------------------------------------------------------ planted mistakes --
