@@ -49,7 +49,7 @@ extern "C" {
 
 typedef uint16_t adaln_bf16;
 
-#define ADALN_ABI_VERSION 3
+#define ADALN_ABI_VERSION 4
 
 enum adaln_status {
   ADALN_OK = 0,
@@ -68,7 +68,8 @@ enum adaln_op {
   ADALN_OP_PROJ_BWD = 3,
   ADALN_OP_TOKEN_TREE_SUM = 4,
   ADALN_OP_BWD = 5,
-  ADALN_OP_BWD_F32 = 6
+  ADALN_OP_BWD_F32 = 6,
+  ADALN_OP_RESIDUAL_BWD = 7
 };
 
 /* Workspace bytes an entry point needs (0 for an unknown op or bad sizes).
@@ -80,6 +81,7 @@ enum adaln_op {
  *   TOKEN_TREE_SUM: B * ceil(S/32) * ceil(H/64) * 64 * 8 bytes (level-0 pairs).
  *   BWD:            H = D (3072).  NORM_MOD_BWD + PROJ_BWD, in that order.
  *   BWD_F32:        H = D (3072).  NORM_MOD_BWD + B*K*4 (fp32 activations).
+ *   RESIDUAL_BWD:   H = D (3072).  B * ceil(S/32) * 3D * 8 bytes (level-0 pairs).
  * Each region is padded to 256 bytes. */
 size_t adaln_workspace_bytes(int op, int64_t B, int64_t S, int64_t H);
 
@@ -209,6 +211,29 @@ int adaln_fwd_f32(const float* temb, const float* W, const float* bias, const fl
 int adaln_bwd_f32(const float* gout, const float* x, const float* mean, const float* rstd, const float* emb,
                   const float* temb, const float* W, float* dx, float* d_emb, float* dW, float* db, float* dtemb,
                   void* ws, size_t ws_bytes, int64_t B, int64_t S, int64_t D, void* stream);
+
+/* Residual norm site of a transformer block (ScaleResidualLayerNormScaleShift:
+ * miles_diffusion pull request 108 names it beside LayerNormScaleShift with the
+ * same autocast rounding points; its formula is the reading below).
+ *   x, residual [B, S, D] bf16 (in), mod [B, 3D] bf16 (in) = (shift | scale |
+ *   gate), h [B, S, D] bf16 (out), out [B, S, D] bf16 (out), mean, rstd [B, S]
+ *   fp32 (out):
+ *   h = bf16(residual + bf16(gate * x)),  out = bf16((n * bf16(1 + scale)) + shift),
+ *   n = LayerNorm(h) as in adaln_norm_mod_fwd.
+ * Backward, from g_out = dL/dout and g_h = dL/dh (bf16 [B, S, D], in):
+ *   dh = bf16(bf16(rstd * ((gy - alpha) - n * beta)) + g_h), gy = g_out * m;
+ *   d_residual = dh, dx = bf16(dh * gate) (bf16 [B, S, D], out);
+ *   d_mod [B, 3D] fp32 (out) = (sum_S g_out | sum_S g_out * n | sum_S dh * x),
+ *   each the 32-token Neumaier tree of token_tree_sum.
+ *   ws: adaln_workspace_bytes(ADALN_OP_RESIDUAL_BWD, B, S, D) bytes.
+ * Per-sample outputs are the same bytes whatever B. */
+int adaln_residual_fwd(const adaln_bf16* x, const adaln_bf16* residual, const adaln_bf16* mod, adaln_bf16* h,
+                       adaln_bf16* out, float* mean, float* rstd, int64_t B, int64_t S, int64_t D, float eps,
+                       void* stream);
+int adaln_residual_bwd(const adaln_bf16* g_out, const adaln_bf16* g_h, const adaln_bf16* x, const adaln_bf16* h,
+                       const float* mean, const float* rstd, const adaln_bf16* mod, adaln_bf16* d_residual,
+                       adaln_bf16* dx, float* d_mod, void* ws, size_t ws_bytes, int64_t B, int64_t S, int64_t D,
+                       void* stream);
 
 /* Benchmarking aid: per-launch durations of the main kernel of the backward
  * (adaln_bwd, adaln_bwd_f32 and adaln_norm_mod_bwd: the fused dx + level-0 kernel;

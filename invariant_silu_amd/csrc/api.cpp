@@ -227,6 +227,7 @@ size_t adaln_workspace_bytes(int op, int64_t B, int64_t S, int64_t H) {
     case ADALN_OP_PROJ_BWD: return H == kD ? ws_proj_bwd(B) : 0;
     case ADALN_OP_BWD: return (H == kD && seq_ok(S)) ? ws_norm_bwd(B, S) + ws_proj_bwd(B) : 0;
     case ADALN_OP_BWD_F32: return (H == kD && seq_ok(S)) ? ws_norm_bwd(B, S) + ws_proj_bwd_f32(B) : 0;
+    case ADALN_OP_RESIDUAL_BWD: return (H == kD && seq_ok(S)) ? ws_pairs(B, S, 3 * kD) : 0;
     case ADALN_OP_TOKEN_TREE_SUM:
       return (seq_ok(S) && H >= 1 && H <= (int64_t{1} << 24)) ? ws_tree(B, S, H) : 0;
     default: return 0;
@@ -543,6 +544,53 @@ int adaln_bwd_f32(const float* gout, const float* x, const float* mean, const fl
     return rc;
   if (int rc = launched(adaln::launch_tree_fold(part, d_emb, B, T0, kN, s))) return rc;
   return launched(adaln::launch_proj_bwd_f32(d_emb, temb, W, a, dW, db, dtemb, B, s));
+}
+
+int adaln_residual_fwd(const adaln_bf16* x, const adaln_bf16* residual, const adaln_bf16* mod, adaln_bf16* h,
+                       adaln_bf16* out, float* mean, float* rstd, int64_t B, int64_t S, int64_t D, float eps,
+                       void* stream) {
+  if (!x || !residual || !mod || !h || !out || !mean || !rstd) return ADALN_ERR_NULL;
+  if (!batch_ok(B) || !seq_ok(S) || D != kD) return ADALN_ERR_SHAPE;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return ADALN_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(residual) || !aligned16(mod) || !aligned16(h) || !aligned16(out) ||
+      !aligned16(mean) || !aligned16(rstd))
+    return ADALN_ERR_ALIGN;
+  const size_t rows = static_cast<size_t>(B * S);
+  if (int rc = check_overlap({{h, rows * kD * 2}, {out, rows * kD * 2}, {mean, rows * 4}, {rstd, rows * 4}},
+                             {{x, rows * kD * 2}, {residual, rows * kD * 2}, {mod, static_cast<size_t>(B * 3 * kD * 2)}}))
+    return rc;
+  if (int rc = check_device()) return rc;
+  (void)hipGetLastError();
+  return launched(adaln::launch_residual_fwd(x, residual, mod, h, out, mean, rstd, B, S, eps, as_stream(stream)));
+}
+
+int adaln_residual_bwd(const adaln_bf16* g_out, const adaln_bf16* g_h, const adaln_bf16* x, const adaln_bf16* h,
+                       const float* mean, const float* rstd, const adaln_bf16* mod, adaln_bf16* d_residual,
+                       adaln_bf16* dx, float* d_mod, void* ws, size_t ws_bytes, int64_t B, int64_t S, int64_t D,
+                       void* stream) {
+  if (!g_out || !g_h || !x || !h || !mean || !rstd || !mod || !d_residual || !dx || !d_mod || !ws)
+    return ADALN_ERR_NULL;
+  if (!batch_ok(B) || !seq_ok(S) || D != kD) return ADALN_ERR_SHAPE;
+  if (!aligned16(g_out) || !aligned16(g_h) || !aligned16(x) || !aligned16(h) || !aligned16(mean) ||
+      !aligned16(rstd) || !aligned16(mod) || !aligned16(d_residual) || !aligned16(dx) || !aligned16(d_mod) ||
+      !aligned16(ws))
+    return ADALN_ERR_ALIGN;
+  const size_t need = ws_pairs(B, S, 3 * kD);
+  if (ws_bytes < need) return ADALN_ERR_WORKSPACE;
+  const size_t rows = static_cast<size_t>(B * S);
+  if (int rc = check_overlap(
+          {{d_residual, rows * kD * 2}, {dx, rows * kD * 2}, {d_mod, static_cast<size_t>(B * 3 * kD * 4)},
+           {ws, need}},
+          {{g_out, rows * kD * 2}, {g_h, rows * kD * 2}, {x, rows * kD * 2}, {h, rows * kD * 2}, {mean, rows * 4},
+           {rstd, rows * 4}, {mod, static_cast<size_t>(B * 3 * kD * 2)}}))
+    return rc;
+  if (int rc = check_device()) return rc;
+  (void)hipGetLastError();
+  const hipStream_t s = as_stream(stream);
+  float* part = static_cast<float*>(ws);
+  if (int rc = launched(adaln::launch_residual_bwd(g_out, g_h, x, h, mean, rstd, mod, d_residual, dx, part, B, S, s)))
+    return rc;
+  return launched(adaln::launch_tree_fold(part, d_mod, B, ceil_div(S, kTile), 3 * kD, s));
 }
 
 int adaln_selftest(void) {

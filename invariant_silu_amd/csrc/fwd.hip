@@ -461,6 +461,74 @@ __global__ __launch_bounds__(kThreads) void norm_modulate_kernel(
   modulate(xv, mu, rs, m_lds, sh_lds, out + row * kD, lane);
 }
 
+// ------------------------------------------------- residual norm site ----
+// ScaleResidualLayerNormScaleShift at a block's norm site (reading of
+// miles_diffusion pull request 108, "Fused-norm rounding points"):
+//   h   = bf16(residual + bf16(gate * x))      eager bf16 multiply and add
+//   out = bf16((LayerNorm(h) * bf16(1 + scale)) + shift)
+// mod [B, 3D] = (shift | scale | gate).  One wave per row: the row's h is
+// formed in registers, stored, and goes through row_stats and modulate as the
+// final modulation's x does.
+__device__ __forceinline__ void load_mod3(const uint16_t* __restrict__ mod, int64_t b, ModRegs& r,
+                                          uint2 (&gt)[3]) {
+  const uint2* shift = reinterpret_cast<const uint2*>(mod + b * 3 * kD);
+  const uint2* scale = reinterpret_cast<const uint2*>(mod + b * 3 * kD + kD);
+  const uint2* gate = reinterpret_cast<const uint2*>(mod + b * 3 * kD + 2 * kD);
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    r.sc[k] = scale[threadIdx.x + kThreads * k];
+    r.sh[k] = shift[threadIdx.x + kThreads * k];
+    gt[k] = gate[threadIdx.x + kThreads * k];
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void residual_fwd_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ residual, const uint16_t* __restrict__ mod,
+    uint16_t* __restrict__ h, uint16_t* __restrict__ out, float* __restrict__ mean, float* __restrict__ rstd,
+    int64_t S, float eps) {
+  __shared__ float4 m_lds[kD / 4];
+  __shared__ float4 sh_lds[kD / 4];
+  __shared__ float4 gate_lds[kD / 4];
+  const int64_t b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int64_t s = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  // a wave past the end redoes row S - 1 (same bytes as its owner)
+  const int64_t row = b * S + (s < S ? s : S - 1);
+  ModRegs mr;
+  uint2 gt[3];
+  load_mod3(mod, b, mr, gt);
+  uint4 xv[kLaneChunks], rv[kLaneChunks];
+  load_row(x, row, lane, xv);
+  load_row(residual, row, lane, rv);
+  store_mod(mr, m_lds, sh_lds);
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+    gate_lds[threadIdx.x + kThreads * k] =
+        make_float4(bf_lo(gt[k].x), bf_hi(gt[k].x), bf_lo(gt[k].y), bf_hi(gt[k].y));
+  __syncthreads();
+  uint4 hv[kLaneChunks];
+#pragma unroll
+  for (int i = 0; i < kLaneChunks; ++i) {
+    const int c = lane + 64 * i;
+    float xf[8], rf[8], hf[8];
+    unpack8(xv[i], xf);
+    unpack8(rv[i], rf);
+    const float4 g0 = gate_lds[2 * c], g1 = gate_lds[2 * c + 1];
+    const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) hf[e] = rf[e] + round_bf16(gg[e] * xf[e]);
+    hv[i] = pack8(hf);
+    st16_nt(h + row * kD + c * 8, hv[i]);
+  }
+  float mu, rs;
+  row_stats(hv, eps, mu, rs);
+  modulate(hv, mu, rs, m_lds, sh_lds, out + row * kD, lane);
+  if (lane == 0) {
+    mean[row] = mu;
+    rstd[row] = rs;
+  }
+}
+
 // B <= 4: proj_block with NB = B; larger batches: proj_mfma_kernel
 template <typename F>
 hipError_t by_batch(int64_t B, F&& f) {
@@ -541,6 +609,15 @@ hipError_t launch_proj_fwd_f32(const float* temb, float* a, const float* W, cons
                                int64_t B, hipStream_t s) {
   if (hipError_t e = launch_silu_f32(temb, a, B * kD, s); e != hipSuccess) return e;
   return launch_mfma_from_a(a, W, bias, emb, B, s);
+}
+
+hipError_t launch_residual_fwd(const uint16_t* x, const uint16_t* residual, const uint16_t* mod, uint16_t* h,
+                               uint16_t* out, float* mean, float* rstd, int64_t B, int64_t S, float eps,
+                               hipStream_t s) {
+  const int64_t gx = (S + kWaves - 1) / kWaves;
+  hipLaunchKernelGGL(residual_fwd_kernel, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(B)), dim3(kThreads),
+                     0, s, x, residual, mod, h, out, mean, rstd, S, eps);
+  return hipGetLastError();
 }
 
 }  // namespace adaln

@@ -172,6 +172,43 @@ def bwd(g: torch.Tensor, x: torch.Tensor, mean: torch.Tensor, rstd: torch.Tensor
     return dx, d_emb, dW, db, dtemb
 
 
+def residual_fwd(x: torch.Tensor, residual: torch.Tensor, mod: torch.Tensor, eps: float = EPS):
+    """Residual norm site (adaln_residual_fwd): (out, h, mean, rstd) with
+    h = bf16(residual + bf16(gate * x)), out = bf16(LN(h) * bf16(1 + scale) + shift),
+    mod [B, 3 * 3072] = (shift | scale | gate); bf16 tensors."""
+    for t, n in ((x, "x"), (residual, "residual"), (mod, "mod")):
+        _check(t, torch.bfloat16, n)
+    x, residual, mod = aligned(x), aligned(residual), aligned(mod)
+    B, S, Dx = x.shape
+    h = torch.empty_like(x)
+    out = torch.empty_like(x)
+    mean = torch.empty((B, S), dtype=torch.float32, device=x.device)
+    rstd = torch.empty((B, S), dtype=torch.float32, device=x.device)
+    _lib.call("adaln_residual_fwd", x.data_ptr(), residual.data_ptr(), mod.data_ptr(), h.data_ptr(), out.data_ptr(),
+              mean.data_ptr(), rstd.data_ptr(), B, S, Dx, float(eps), _stream(x.device))
+    return out, h, mean, rstd
+
+
+def residual_bwd(g_out: torch.Tensor, g_h: torch.Tensor, x: torch.Tensor, h: torch.Tensor, mean: torch.Tensor,
+                 rstd: torch.Tensor, mod: torch.Tensor):
+    """Backward of the residual norm site (adaln_residual_bwd):
+    (d_residual bf16, dx bf16, d_mod fp32 [B, 3 * 3072] = (d_shift | d_scale | d_gate))."""
+    for t, n, dt in ((g_out, "g_out", torch.bfloat16), (g_h, "g_h", torch.bfloat16), (x, "x", torch.bfloat16),
+                     (h, "h", torch.bfloat16), (mean, "mean", torch.float32), (rstd, "rstd", torch.float32),
+                     (mod, "mod", torch.bfloat16)):
+        _check(t, dt, n)
+    g_out, g_h, x, h, mean, rstd, mod = (aligned(t) for t in (g_out, g_h, x, h, mean, rstd, mod))
+    B, S, Dx = x.shape
+    d_residual = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    d_mod = torch.empty((B, 3 * Dx), dtype=torch.float32, device=x.device)
+    ws = _ws(_lib.OP_RESIDUAL_BWD, B, S, Dx, x.device)
+    _lib.call("adaln_residual_bwd", g_out.data_ptr(), g_h.data_ptr(), x.data_ptr(), h.data_ptr(), mean.data_ptr(),
+              rstd.data_ptr(), mod.data_ptr(), d_residual.data_ptr(), dx.data_ptr(), d_mod.data_ptr(),
+              ws.data_ptr(), ws.numel(), B, S, Dx, _stream(x.device))
+    return d_residual, dx, d_mod
+
+
 def selftest() -> int:
     return int(_lib.load().adaln_selftest())
 

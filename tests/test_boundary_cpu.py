@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_strerror(L):
-    assert L.adaln_abi_version() == 3
+    assert L.adaln_abi_version() == 4
     for code in range(-7, 1):
         assert len(lib.strerror(code)) >= 2
 
@@ -60,6 +60,7 @@ def test_workspace_sizes(L):
         assert lib.workspace_bytes(lib.OP_PROJ_BWD, B, S, 3072) == pad(B * 3072 * 2)
         assert lib.workspace_bytes(lib.OP_PROJ_FWD, B, S, 3072) == pad(B * 3072 * 2)
         assert lib.workspace_bytes(lib.OP_BWD_F32, B, S, 3072) == pad(B * T0 * 6144 * 8) + pad(B * 3072 * 4)
+        assert lib.workspace_bytes(lib.OP_RESIDUAL_BWD, B, S, 3072) == pad(B * T0 * 9216 * 8)
     assert lib.workspace_bytes(lib.OP_NORM_MOD_BWD, 1, 10, 1024) == 0
     assert lib.workspace_bytes(99, 1, 10, 3072) == 0
     assert lib.workspace_bytes(lib.OP_PROJ_BWD, 0, 1, 3072) == 0
@@ -78,6 +79,11 @@ def test_validation_before_device_work(L):
     bufs = [p + (k << 28) for k in range(13)]
     assert L.adaln_bwd_f32(*bufs, 16, 2, 64, 3072, None) == lib.ERR_WORKSPACE
     assert L.adaln_bwd_f32(*bufs[:12], None, 1 << 20, 2, 64, 3072, None) == lib.ERR_NULL
+    # residual norm site
+    assert L.adaln_residual_fwd(None, p, p, p, p, p, p, 1, 4, 3072, 1e-6, None) == lib.ERR_NULL
+    assert L.adaln_residual_fwd(p, p, p, p, p, p, p, 1, 0, 3072, 1e-6, None) == lib.ERR_SHAPE
+    rb = [p + (k << 28) for k in range(11)]
+    assert L.adaln_residual_bwd(*rb, 16, 2, 64, 3072, None) == lib.ERR_WORKSPACE
     # a workspace smaller than adaln_workspace_bytes(PROJ_FWD) is refused
     assert L.adaln_proj_fwd(p, p + (1 << 20), p + (2 << 20), p + (3 << 20), p + (4 << 20), 16,
                             8, 3072, 6144, None) == lib.ERR_WORKSPACE
