@@ -8,6 +8,12 @@ tree fold, then the projection backward: dW and db, da and dtemb).  Default
 workload: one 1024x1024 image stream, B = 1, S = 4096 tokens, D = 3072, bf16
 storage, 1% outlier rows x20.  --storage fp32 runs the fp32-storage entry
 points (adaln_fwd_f32 / adaln_bwd_f32) on the same draws, unrounded.
+--site residual times a block's residual norm site instead (adaln_residual_fwd:
+h = residual + gate * x, LayerNorm of h, modulation; adaln_residual_bwd: dh and
+dx rows with the level-0 tiles of d_shift / d_scale, the d_gate tiles, the
+fold) at the same B and S, bf16 storage.  --site mod6 times a block's 6-way
+modulation projection (adaln_proj_fwd and adaln_proj_bwd at N = 18432) at the
+workload's B.
 
 Inputs are resident in HBM before the timed region.  The step rotates over
 several independent copies of every buffer (parameters included), so no step
@@ -41,6 +47,9 @@ HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 << 20
 SAMPLE = 8        # the dominant kernel is timed on every SAMPLE-th timed step
 METRIC = "fwd+bwd tokens/sec + achieved HBM GB/s at S=4096 D=3072 bf16 (batch-invariant)"
+METRIC_RESIDUAL = "residual norm site fwd+bwd tokens/sec at D=3072 bf16 (batch-invariant)"
+METRIC_MOD6 = "6-way modulation projection fwd+bwd samples/sec at 3072->18432 bf16 (batch-invariant)"
+N6 = 6 * D
 
 
 def algorithmic_bytes(B: int, S: int, el: int = 2) -> int:
@@ -58,6 +67,34 @@ def dominant_kernel_bytes(B: int, S: int, el: int = 2) -> int:
     level-0 token tiles (fp32 pairs, 2 x 24 KB per 32-token tile) are
     implementation overhead, not algorithmic bytes."""
     return 3 * el * B * S * D + 8 * B * S + el * D * B
+
+
+def residual_algorithmic_bytes(B: int, S: int) -> int:
+    """Residual norm site, bf16: the forward reads x and residual and writes h
+    and out; the backward reads g_out, g_h, x and h and writes d_residual and
+    dx (20 bytes per element in all); mean/rstd written and read (16 per row);
+    mod read twice (2 x 18 KB per sample), d_mod written in fp32 (36 KB)."""
+    return 20 * B * S * D + 16 * B * S + (2 * 2 * 3 * D + 4 * 3 * D) * B
+
+
+def residual_dominant_kernel_bytes(B: int, S: int) -> int:
+    """The residual backward's main launch: g_out, g_h, x and h read,
+    d_residual and dx written (12 bytes per element), mean/rstd read, scale and
+    gate read per sample.  Its level-0 tiles are implementation overhead."""
+    return 12 * B * S * D + 8 * B * S + 2 * 2 * D * B
+
+
+def mod6_algorithmic_bytes(B: int) -> int:
+    """6-way projection, bf16: W read by the forward and by the backward, dW
+    written; bias read, db written; per sample temb read twice, emb and dtemb
+    written, d_emb read in fp32."""
+    return 3 * 2 * N6 * D + 2 * 2 * N6 + (3 * 2 * D + 2 * N6 + 4 * N6) * B
+
+
+def mod6_dominant_kernel_bytes(B: int) -> int:
+    """The backward's one kernel at B <= 4: W read, dW and db written, d_emb,
+    temb read, dtemb written."""
+    return 2 * 2 * N6 * D + 2 * N6 + (4 * N6 + 2 * 2 * D) * B
 
 
 def pmc_traffic():
@@ -85,20 +122,29 @@ def parse():
     ap.add_argument("--workload", default="img1024_b1_s4096")
     ap.add_argument("--storage", choices=("bf16", "fp32"), default="bf16",
                     help="tensor storage type (fp32: the fp32-storage entry points)")
+    ap.add_argument("--site", choices=("final", "residual", "mod6"), default="final",
+                    help="final: the final modulation (norm_out); residual: a block's residual norm site; "
+                         "mod6: a block's 6-way modulation projection")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true",
                     help="after the steps, run a plain 512 MiB device copy (PMC byte-counter calibration)")
     return ap.parse_args()
 
 
-def cpu_baseline(inp: dict, reps: int = 8) -> dict:
+def cpu_baseline(inp: dict, reps: int = 8, site: str = "final") -> dict:
     """The oracle (NumPy, single-threaded element-wise loops) on the same batch."""
-    from oracle import adaln
+    from oracle import adaln, modulation, residual
+    fwd, bwd = {"final": (adaln.forward, adaln.backward),
+                "residual": (residual.residual_forward, residual.residual_backward),
+                "mod6": (modulation.mod6_forward, modulation.mod6_backward)}[site]
     t0 = time.perf_counter()
     for _ in range(reps):
-        f = adaln.forward(inp)
-        adaln.backward(inp, f)
+        f = fwd(inp)
+        bwd(inp, f)
     dt = (time.perf_counter() - t0) / reps
+    if site == "mod6":
+        return {"value": inp["B"] / dt, "unit": "samples/s", "cores": 1, "kind": "oracle",
+                "sample": f"the whole batch (B={inp['B']}), fwd+bwd, {reps} passes, {dt:.2f} s per pass"}
     tokens = inp["B"] * inp["S"]
     return {"value": tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"the whole workload batch (B={inp['B']}, S={inp['S']}), fwd+bwd, "
@@ -116,7 +162,7 @@ def main() -> int:
     import torch
 
     from invariant_silu_amd import lib
-    from synthetic_inputs import WORKLOADS, make_workload
+    from synthetic_inputs import WORKLOADS, make_mod6_inputs, make_residual_inputs, make_workload
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -130,9 +176,22 @@ def main() -> int:
 
     w = WORKLOADS[args.workload]
     B, S = w["B"], w["S"]
+    residual_site = args.site == "residual"
+    mod6_site = args.site == "mod6"
+    if args.site != "final" and args.storage != "bf16":
+        print(f"--site {args.site} runs with bf16 storage only", file=sys.stderr)
+        return 2
     f32 = args.storage == "fp32"
     el = 4 if f32 else 2
-    inp = make_workload(args.workload, seed=0, io=args.storage)
+    if residual_site:
+        inp = make_residual_inputs(B, S, seed=0)
+        keys = ("x", "residual", "mod", "g_out", "g_h")
+    elif mod6_site:
+        inp = make_mod6_inputs(B, seed=0)
+        keys = ("temb", "W", "bias")
+    else:
+        inp = make_workload(args.workload, seed=0, io=args.storage)
+        keys = ("x", "temb", "W", "bias", "g")
     sdt = torch.float32 if f32 else torch.bfloat16
 
     def to_dev(a):
@@ -140,35 +199,89 @@ def main() -> int:
             return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    base = {k: to_dev(inp[k]) for k in ("x", "temb", "W", "bias", "g")}
-    ws_bw = lib.workspace_bytes(lib.OP_BWD_F32 if f32 else lib.OP_BWD, B, S, D)
+    base = {k: to_dev(inp[k]) for k in keys}
+    if mod6_site:
+        base["d_emb"] = torch.from_numpy(np.ascontiguousarray(inp["d_emb"])).to(dev)
+    ws_fw = lib.workspace_bytes(lib.OP_PROJ_FWD, B, 1, D)
+    if residual_site:
+        ws_bw = lib.workspace_bytes(lib.OP_RESIDUAL_BWD, B, S, D)
+    elif mod6_site:
+        ws_bw = lib.workspace_bytes(lib.OP_PROJ_BWD, B, 1, D)
+    else:
+        ws_bw = lib.workspace_bytes(lib.OP_BWD_F32 if f32 else lib.OP_BWD, B, S, D)
 
     def new_set():
         s = {k: v.clone() for k, v in base.items()}
+        if mod6_site:
+            s.update(
+                emb=torch.empty((B, N6), dtype=sdt, device=dev),
+                dW=torch.empty((N6, D), dtype=sdt, device=dev),
+                db=torch.empty((N6,), dtype=sdt, device=dev),
+                dtemb=torch.empty((B, D), dtype=sdt, device=dev),
+                ws_fw=torch.empty(ws_fw, dtype=torch.uint8, device=dev),
+                ws_bw=torch.empty(ws_bw, dtype=torch.uint8, device=dev),
+            )
+            return s
         s.update(
-            emb=torch.empty((B, N), dtype=sdt, device=dev),
             out=torch.empty((B, S, D), dtype=sdt, device=dev),
             mean=torch.empty((B, S), dtype=torch.float32, device=dev),
             rstd=torch.empty((B, S), dtype=torch.float32, device=dev),
             dx=torch.empty((B, S, D), dtype=sdt, device=dev),
-            d_emb=torch.empty((B, N), dtype=torch.float32, device=dev),
-            dW=torch.empty((N, D), dtype=sdt, device=dev),
-            db=torch.empty((N,), dtype=sdt, device=dev),
-            dtemb=torch.empty((B, D), dtype=sdt, device=dev),
             ws_bw=torch.empty(ws_bw, dtype=torch.uint8, device=dev),
         )
+        if residual_site:
+            s.update(
+                h=torch.empty((B, S, D), dtype=sdt, device=dev),
+                d_residual=torch.empty((B, S, D), dtype=sdt, device=dev),
+                d_mod=torch.empty((B, 3 * D), dtype=torch.float32, device=dev),
+            )
+        else:
+            s.update(
+                emb=torch.empty((B, N), dtype=sdt, device=dev),
+                d_emb=torch.empty((B, N), dtype=torch.float32, device=dev),
+                dW=torch.empty((N, D), dtype=sdt, device=dev),
+                db=torch.empty((N,), dtype=sdt, device=dev),
+                dtemb=torch.empty((B, D), dtype=sdt, device=dev),
+            )
         return s
 
-    per_set = algorithmic_bytes(B, S, el)
-    nsets = max(2, math.ceil(3 * MALL_BYTES / per_set))
+    if mod6_site:
+        if B > 4:
+            print("--site mod6 times the B <= 4 backward kernel; use a workload with B <= 4", file=sys.stderr)
+            return 2
+        step_bytes = mod6_algorithmic_bytes(B)
+        k_bytes = mod6_dominant_kernel_bytes(B)
+        fwd_name, bwd_name = "adaln_proj_fwd", "adaln_proj_bwd"
+        k_name = f"proj_bwd_small_kernel<{B}, 18432> (dW tiles + da column blocks)"
+    elif residual_site:
+        step_bytes = residual_algorithmic_bytes(B, S)
+        k_bytes = residual_dominant_kernel_bytes(B, S)
+        fwd_name, bwd_name = "adaln_residual_fwd", "adaln_residual_bwd"
+        k_name = "residual_bwd_kernel (dh / dx rows + level-0 tiles of d_shift, d_scale)"
+    else:
+        step_bytes = algorithmic_bytes(B, S, el)
+        k_bytes = dominant_kernel_bytes(B, S, el)
+        fwd_name, bwd_name = ("adaln_fwd_f32", "adaln_bwd_f32") if f32 else ("adaln_fwd", "adaln_bwd")
+        k_name = ("norm_mod_bwd_f32_kernel" if f32 else "norm_mod_bwd_kernel<0>") + " (dx rows + level-0 token tiles)"
+    nsets = max(2, math.ceil(3 * MALL_BYTES / step_bytes))
     sets = [new_set() for _ in range(nsets)]
     stream = torch.cuda.current_stream(dev)
     st = stream.cuda_stream
-    fwd_name, bwd_name = ("adaln_fwd_f32", "adaln_bwd_f32") if f32 else ("adaln_fwd", "adaln_bwd")
     fwd_fn, bwd_fn = getattr(L, fwd_name), getattr(L, bwd_name)
 
     def step(s):
         p = lambda k: s[k].data_ptr()   # noqa: E731
+        if mod6_site:
+            lib.check(fwd_name, fwd_fn(p("temb"), p("W"), p("bias"), p("emb"), p("ws_fw"), ws_fw, B, D, N6, st))
+            lib.check(bwd_name, bwd_fn(p("d_emb"), p("temb"), p("W"), p("dW"), p("db"), p("dtemb"), p("ws_bw"),
+                                       ws_bw, B, D, N6, st))
+            return
+        if residual_site:
+            lib.check(fwd_name, fwd_fn(p("x"), p("residual"), p("mod"), p("h"), p("out"), p("mean"), p("rstd"),
+                                       B, S, D, 1e-6, st))
+            lib.check(bwd_name, bwd_fn(p("g_out"), p("g_h"), p("x"), p("h"), p("mean"), p("rstd"), p("mod"),
+                                       p("d_residual"), p("dx"), p("d_mod"), p("ws_bw"), ws_bw, B, S, D, st))
+            return
         lib.check(fwd_name, fwd_fn(p("temb"), p("W"), p("bias"), p("x"), p("emb"), p("out"), p("mean"),
                                    p("rstd"), B, S, D, 1e-6, st))
         lib.check(bwd_name, bwd_fn(p("g"), p("x"), p("mean"), p("rstd"), p("emb"), p("temb"), p("W"),
@@ -193,11 +306,9 @@ def main() -> int:
     n_timed = L.adaln_timing_end(ms_buf, n_sampled)
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    tokens_per_s = B * S / (ms_per_step / 1e3)
-    step_bytes = algorithmic_bytes(B, S, el)
+    tokens_per_s = (B if mod6_site else B * S) / (ms_per_step / 1e3)
     k_ms = sorted(ms_buf[i] for i in range(n_timed))
     k_mean_ms = sum(k_ms) / len(k_ms)
-    k_bytes = dominant_kernel_bytes(B, S, el)
     achieved = k_bytes / (k_mean_ms / 1e3) / 1e9
 
     # achievable-bandwidth ceiling in the same run: a plain device copy moving
@@ -226,9 +337,9 @@ def main() -> int:
         torch.cuda.synchronize()
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC_MOD6 if mod6_site else (METRIC_RESIDUAL if residual_site else METRIC),
         "value": round(tokens_per_s, 1),
-        "unit": "tokens/s",
+        "unit": "samples/s" if mod6_site else "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -238,8 +349,9 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "fp32",
         "data": "synthetic",
-        "config": {"workload": args.workload, "B": B, "S": S, "D": D, "N": N,
-                   "storage": args.storage, "accumulate": "fp64", "outlier_rows": w["outlier_frac"],
+        "config": {"workload": args.workload, "B": B, "S": None if mod6_site else S, "D": D,
+                   "N": N6 if mod6_site else N, "site": args.site, "storage": args.storage, "accumulate": "fp64",
+                   "outlier_rows": w["outlier_frac"] if args.site == "final" else 0.0,
                    "buffer_sets": nsets, "step_algorithmic_bytes": step_bytes,
                    "host_enqueue_ms_per_step": round((t_enq - t0) * 1e3 / args.steps, 5),
                    "step_gbps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
@@ -247,16 +359,15 @@ def main() -> int:
                    "copy_ceiling_gbps": round(copy_gbps, 1),
                    "step_frac_of_copy_ceiling": round(step_bytes / (ms_per_step / 1e3) / 1e9 / copy_gbps, 4)},
         "roofline": {"bound": "hbm",
-                     "kernel": ("norm_mod_bwd_f32_kernel" if f32 else "norm_mod_bwd_kernel<0>")
-                     + " (dx rows + level-0 token tiles)",
+                     "kernel": k_name,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None if f32 else pmc_traffic(),
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None if (f32 or args.site != "final") else pmc_traffic(),
                      "bytes_per_launch": k_bytes, "avg_launch_ms": round(k_mean_ms, 5),
                      "timed_launches": n_timed, "timed_every": SAMPLE,
                      "median_launch_ms": round(k_ms[len(k_ms) // 2], 5)},
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(inp)
+        result["cpu_baseline"] = cpu_baseline(inp, reps=1 if mod6_site else 8, site=args.site)
     print(json.dumps(result), flush=True)
     return 0
 

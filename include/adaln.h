@@ -87,7 +87,11 @@ size_t adaln_workspace_bytes(int op, int64_t B, int64_t S, int64_t H);
 
 /* Projection forward (pull request 538, "What": SiLU(temb) @ W^T + b, chunk(2)).
  *   temb [B, K] bf16 (in), W [N, K] bf16 (in, row-major), bias [N] bf16 (in),
- *   emb  [B, N] bf16 (out) = (scale | shift).
+ *   emb  [B, N] bf16 (out).  K = 3072; N = 6144, the final modulation, emb =
+ *   (scale | shift), or N = 18432, a block's 6-way modulation (pull request
+ *   537, named in 538's "What" and "Prior art & reuse decision": the six
+ *   chunks of temb.chunk(6)), emb = (shift1 | scale1 | gate1 | shift2 | scale2 |
+ *   gate2) for the block's two norm sites.  Any other N: ADALN_ERR_SHAPE.
  *   emb = bf16(fp32(sum_k a_k W_jk) + bias_j), a = bf16(fp32(SiLU(temb))),
  *   SiLU evaluated in float64.  The sum is one fixed tree whatever B: 64 leaves
  *   of 48 consecutive k, each accumulated from +0 by fp64 fused multiply-adds
@@ -147,13 +151,14 @@ int token_tree_fold(const void* part, float* out, int64_t B, int64_t T0, int64_t
 /* Projection backward (pull request 538, "What": projection backward; review
  * thread: silu'(z) = sigmoid(z) * (1 + z * (1 - sigmoid(z)))).
  *   d_emb [B, N] fp32 (in), temb [B, K] bf16 (in), W [N, K] bf16 (in),
- *   dW [N, K] bf16 (out), db [N] bf16 (out), dtemb [B, K] bf16 (out).
+ *   dW [N, K] bf16 (out), db [N] bf16 (out), dtemb [B, K] bf16 (out);
+ *   K = 3072, N = 6144 or 18432 as for adaln_proj_fwd.
  *   dW = bf16(fp32(sum_b d_emb_bj * a_bk)), db = bf16(fp32(sum_b d_emb_bj)),
  *   dtemb = bf16(fp32(sum_j d_emb_bj * W_jk) * silu'(temb)).  Every product is
  *   exact (an fp64 fused multiply-add) and the sums run in fp64 in orders that
  *   do not depend on B: dW and db over samples ascending from +0; da as 128
- *   leaves (leaf t: rows t, t + 128, ..., ascending, from +0) added pairwise in
- *   leaf order.  B <= 4 runs on the vector units, B > 4 on the fp64 matrix
+ *   leaves (leaf t: rows t, t + 128, ..., ascending, from +0; N / 128 rows
+ *   each) added pairwise in leaf order.  B <= 4 runs on the vector units, B > 4 on the fp64 matrix
  *   cores: the same bits either way.
  *   ws: adaln_workspace_bytes(ADALN_OP_PROJ_BWD, B, 1, K) bytes (holds a when
  *   B > 4). */
@@ -237,7 +242,8 @@ int adaln_residual_bwd(const adaln_bf16* g_out, const adaln_bf16* g_h, const ada
 
 /* Benchmarking aid: per-launch durations of the main kernel of the backward
  * (adaln_bwd, adaln_bwd_f32 and adaln_norm_mod_bwd: the fused dx + level-0 kernel;
- * adaln_norm_mod_bwd_dx: the dx kernel), timed with HIP
+ * adaln_norm_mod_bwd_dx: the dx kernel; adaln_residual_bwd: the dh / dx +
+ * level-0 kernel; adaln_proj_bwd with B <= 4: its one kernel), timed with HIP
  * events carried by the kernel dispatch itself (no extra packets).
  * A timed dispatch leaves the stream idle for a few microseconds around it, so
  * timing can be sampled: adaln_timing_begin(n, stride) creates n event pairs;

@@ -19,6 +19,7 @@ namespace {
 
 constexpr int64_t kD = 3072;
 constexpr int64_t kN = 6144;
+constexpr int64_t kN6 = 18432;   // a block's 6-way modulation projection
 constexpr int64_t kTile = 32;
 constexpr int64_t kMaxB = 65535;
 constexpr int64_t kMaxS = kTile * 65535;
@@ -127,6 +128,8 @@ size_t ws_proj_bwd_f32(int64_t B) {
 }
 bool batch_ok(int64_t B) { return B >= 1 && B <= kMaxB; }
 bool seq_ok(int64_t S) { return S >= 1 && S <= kMaxS; }
+// projection widths: the final modulation (2D) and a block's 6-way modulation (6D)
+bool proj_width_ok(int64_t N) { return N == kN || N == kN6; }
 
 // host reference values for the strict-math probe
 uint32_t host_bf16(float f) {
@@ -238,18 +241,18 @@ int adaln_proj_fwd(const adaln_bf16* temb, const adaln_bf16* W, const adaln_bf16
                    adaln_bf16* emb, void* ws, size_t ws_bytes, int64_t B, int64_t K, int64_t N,
                    void* stream) {
   if (!temb || !W || !bias || !emb || !ws) return ADALN_ERR_NULL;
-  if (!batch_ok(B) || K != kD || N != kN) return ADALN_ERR_SHAPE;
+  if (!batch_ok(B) || K != kD || !proj_width_ok(N)) return ADALN_ERR_SHAPE;
   if (!aligned16(temb) || !aligned16(W) || !aligned16(bias) || !aligned16(emb) || !aligned16(ws))
     return ADALN_ERR_ALIGN;
   const size_t need = ws_proj_fwd(B);
   if (ws_bytes < need) return ADALN_ERR_WORKSPACE;
-  if (int rc = check_overlap({{emb, static_cast<size_t>(B * kN * 2)}, {ws, need}},
-                             {{temb, static_cast<size_t>(B * kD * 2)}, {W, static_cast<size_t>(kN * kD * 2)},
-                              {bias, static_cast<size_t>(kN * 2)}}))
+  if (int rc = check_overlap({{emb, static_cast<size_t>(B * N * 2)}, {ws, need}},
+                             {{temb, static_cast<size_t>(B * kD * 2)}, {W, static_cast<size_t>(N * kD * 2)},
+                              {bias, static_cast<size_t>(N * 2)}}))
     return rc;
   if (int rc = check_device()) return rc;
   (void)hipGetLastError();
-  return launched(adaln::launch_proj_fwd(temb, W, bias, emb, static_cast<uint16_t*>(ws), B,
+  return launched(adaln::launch_proj_fwd(temb, W, bias, emb, static_cast<uint16_t*>(ws), B, N,
                                          as_stream(stream)));
 }
 
@@ -349,26 +352,29 @@ int adaln_proj_bwd(const float* d_emb, const adaln_bf16* temb, const adaln_bf16*
                    adaln_bf16* dW, adaln_bf16* db, adaln_bf16* dtemb, void* ws, size_t ws_bytes,
                    int64_t B, int64_t K, int64_t N, void* stream) {
   if (!d_emb || !temb || !W || !dW || !db || !dtemb || !ws) return ADALN_ERR_NULL;
-  if (!batch_ok(B) || K != kD || N != kN) return ADALN_ERR_SHAPE;
+  if (!batch_ok(B) || K != kD || !proj_width_ok(N)) return ADALN_ERR_SHAPE;
   if (!aligned16(d_emb) || !aligned16(temb) || !aligned16(W) || !aligned16(dW) || !aligned16(db) ||
       !aligned16(dtemb) || !aligned16(ws))
     return ADALN_ERR_ALIGN;
   const size_t need = ws_proj_bwd(B);
   if (ws_bytes < need) return ADALN_ERR_WORKSPACE;
-  if (int rc = check_overlap({{dW, static_cast<size_t>(kN * kD * 2)}, {db, static_cast<size_t>(kN * 2)},
+  if (int rc = check_overlap({{dW, static_cast<size_t>(N * kD * 2)}, {db, static_cast<size_t>(N * 2)},
                               {dtemb, static_cast<size_t>(B * kD * 2)}, {ws, need}},
-                             {{d_emb, static_cast<size_t>(B * kN * 4)}, {temb, static_cast<size_t>(B * kD * 2)},
-                              {W, static_cast<size_t>(kN * kD * 2)}}))
+                             {{d_emb, static_cast<size_t>(B * N * 4)}, {temb, static_cast<size_t>(B * kD * 2)},
+                              {W, static_cast<size_t>(N * kD * 2)}}))
     return rc;
   if (int rc = check_device()) return rc;
   (void)hipGetLastError();
   uint16_t* a = static_cast<uint16_t*>(ws);
   const hipStream_t s = as_stream(stream);
-  if (B <= adaln::proj_bwd_fused_max_batch())
-    return launched(adaln::launch_proj_bwd_fused(d_emb, temb, W, dW, db, dtemb, B, s));
+  if (B <= adaln::proj_bwd_fused_max_batch()) {
+    hipEvent_t e0, e1;
+    timing_events(&e0, &e1);
+    return launched(adaln::launch_proj_bwd_fused(d_emb, temb, W, dW, db, dtemb, B, N, s, e0, e1));
+  }
   if (int rc = launched(adaln::launch_silu(temb, a, B * kD, s))) return rc;
-  if (int rc = launched(adaln::launch_proj_bwd_dw(d_emb, a, dW, db, B, s))) return rc;
-  return launched(adaln::launch_proj_bwd_da(d_emb, W, temb, dtemb, B, s));
+  if (int rc = launched(adaln::launch_proj_bwd_dw(d_emb, a, dW, db, B, N, s))) return rc;
+  return launched(adaln::launch_proj_bwd_da(d_emb, W, temb, dtemb, B, N, s));
 }
 
 int token_tree_sum(const float* x, float* out, void* ws, size_t ws_bytes, int64_t B, int64_t S,
@@ -482,10 +488,10 @@ int adaln_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float* mean, co
     return rc;
   if (int rc = launched(adaln::launch_tree_fold(part, d_emb, B, T0, kN, s))) return rc;
   if (B <= adaln::proj_bwd_fused_max_batch())
-    return launched(adaln::launch_proj_bwd_fused(d_emb, temb, W, dW, db, dtemb, B, s));
+    return launched(adaln::launch_proj_bwd_fused(d_emb, temb, W, dW, db, dtemb, B, kN, s));
   if (int rc = launched(adaln::launch_silu(temb, a, B * kD, s))) return rc;
-  if (int rc = launched(adaln::launch_proj_bwd_dw(d_emb, a, dW, db, B, s))) return rc;
-  return launched(adaln::launch_proj_bwd_da(d_emb, W, temb, dtemb, B, s));
+  if (int rc = launched(adaln::launch_proj_bwd_dw(d_emb, a, dW, db, B, kN, s))) return rc;
+  return launched(adaln::launch_proj_bwd_da(d_emb, W, temb, dtemb, B, kN, s));
 }
 
 int adaln_fwd_f32(const float* temb, const float* W, const float* bias, const float* x, float* emb, float* out,
@@ -588,7 +594,10 @@ int adaln_residual_bwd(const adaln_bf16* g_out, const adaln_bf16* g_h, const ada
   (void)hipGetLastError();
   const hipStream_t s = as_stream(stream);
   float* part = static_cast<float*>(ws);
-  if (int rc = launched(adaln::launch_residual_bwd(g_out, g_h, x, h, mean, rstd, mod, d_residual, dx, part, B, S, s)))
+  hipEvent_t e0, e1;
+  timing_events(&e0, &e1);
+  if (int rc = launched(
+          adaln::launch_residual_bwd(g_out, g_h, x, h, mean, rstd, mod, d_residual, dx, part, B, S, s, e0, e1)))
     return rc;
   return launched(adaln::launch_tree_fold(part, d_mod, B, ceil_div(S, kTile), 3 * kD, s));
 }

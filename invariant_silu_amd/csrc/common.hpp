@@ -15,6 +15,7 @@ namespace adaln {
 
 constexpr int kD = 3072;            // hidden width D (= conditioning width K)
 constexpr int kN = 2 * kD;          // projection width N: (scale | shift)
+constexpr int kN6 = 6 * kD;         // a block's 6-way modulation projection: 2 x (shift | scale | gate)
 constexpr int kChunks = kD / 8;     // 16-byte chunks (8 bf16) per row: 384
 constexpr int kTile = 32;           // tokens per level-0 tile of the token tree
 constexpr int kMaxFoldLevels = 5;   // S <= 32^6 tokens

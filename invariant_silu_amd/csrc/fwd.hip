@@ -45,7 +45,7 @@ constexpr int kRows = 2;                                   // rows of W per wave
 constexpr int kProjRowsPerBlock = kWaves * kRows;          // 8
 constexpr int kProjBlocks = kN / kProjRowsPerBlock;        // 768
 constexpr int kMaxNarrowBatch = 4;                         // proj_block up to here
-static_assert(kN % kProjRowsPerBlock == 0, "rows per block must divide N");
+static_assert(kN % kProjRowsPerBlock == 0 && kN6 % kProjRowsPerBlock == 0, "rows per block must divide N");
 
 // ----------------------------------------------------------- projection ----
 // The sum for one (sample, row of W) is a tree of 64 leaves.  Leaf l covers
@@ -75,8 +75,8 @@ __device__ __forceinline__ int a_lds_dword(int bb, int l, int d) {
   return (bb * 64 + l) * kLdsLane + 4 * (d % 6) + d / 6;
 }
 
-// Projection blocks for B = NB <= 4 (one pass over the samples).
-template <int NB>
+// Projection blocks for B = NB <= 4 (one pass over the samples); N rows of W.
+template <int NB, int N = kN>
 __device__ __forceinline__ void proj_block(const uint16_t* __restrict__ temb,
                                            const uint16_t* __restrict__ W,
                                            const uint16_t* __restrict__ bias,
@@ -180,7 +180,7 @@ __device__ __forceinline__ void proj_block(const uint16_t* __restrict__ temb,
       const double tot = wave_sum_f64(acc[r][bb]);
       if (lane == r * NB + bb) {
         const float v = static_cast<float>(tot) + bias_f[r];
-        emb[bb * kN + row0 + r] = f32_to_bf16(v);
+        emb[bb * N + row0 + r] = f32_to_bf16(v);
       }
     }
   }
@@ -205,8 +205,8 @@ struct LeafRaw {
   RowRun<12, T> a[kTiles], w;   // 12 elements per operand (steps 0..11)
 };
 
-// T: storage type of a, W, bias and emb (bf16 bit patterns or fp32)
-template <int kTiles, int kSplit, typename T>
+// T: storage type of a, W, bias and emb (bf16 bit patterns or fp32); N rows of W
+template <int kTiles, int kSplit, typename T, int N = kN>
 __global__ __launch_bounds__(64 * kSplit) void proj_mfma_kernel(const T* __restrict__ a,
                                                                 const T* __restrict__ W,
                                                                 const T* __restrict__ bias,
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(64 * kSplit) void proj_mfma_kernel(const T* __restr
     for (int v = 0; v < 4; ++v) {
       const int sr = 16 * t + g + 4 * v;
       if (sr < rows_here)
-        emb[(bblk + sr) * kN + j0 + r] = Storage<T>::store1(static_cast<float>(tot[t][v]) + bias_f);
+        emb[(bblk + sr) * N + j0 + r] = Storage<T>::store1(static_cast<float>(tot[t][v]) + bias_f);
     }
 }
 
@@ -374,13 +374,13 @@ __device__ __forceinline__ void modulate(const uint4 (&xv)[kLaneChunks], float m
 }
 
 // ------------------------------------------------------------- kernels ----
-template <int NB>
+template <int NB, int N>
 __global__ __launch_bounds__(kThreads) void proj_fwd_kernel(const uint16_t* __restrict__ temb,
                                                             const uint16_t* __restrict__ W,
                                                             const uint16_t* __restrict__ bias,
                                                             uint16_t* __restrict__ emb) {
   __shared__ ProjShared<NB> sh;
-  proj_block<NB>(temb, W, bias, emb, blockIdx.x, sh.a);
+  proj_block<NB, N>(temb, W, bias, emb, blockIdx.x, sh.a);
 }
 
 // 4 rows of one sample per block (one per wave): statistics and modulation
@@ -544,33 +544,43 @@ hipError_t by_batch(int64_t B, F&& f) {
 // a = SiLU(temb) computed once into `a`, then the matrix-core projection:
 // one sample tile per wave up to 16 samples, two beyond
 constexpr int kMfmaSplit = 4;
-template <int kTiles, typename T>
+template <int kTiles, typename T, int N>
 hipError_t launch_mfma_tiles(const T* a, const T* W, const T* bias, T* emb, int64_t B, hipStream_t s) {
   const int64_t by = (B + 16 * kTiles - 1) / (16 * kTiles);
-  hipLaunchKernelGGL((proj_mfma_kernel<kTiles, kMfmaSplit, T>), dim3(kN / kMfmaRows, static_cast<unsigned>(by)),
+  hipLaunchKernelGGL((proj_mfma_kernel<kTiles, kMfmaSplit, T, N>), dim3(N / kMfmaRows, static_cast<unsigned>(by)),
                      dim3(64 * kMfmaSplit), 0, s, a, W, bias, emb, B);
   return hipGetLastError();
 }
-template <typename T>
+template <typename T, int N = kN>
 hipError_t launch_mfma_from_a(const T* a, const T* W, const T* bias, T* emb, int64_t B, hipStream_t s) {
-  return B <= 16 ? launch_mfma_tiles<1, T>(a, W, bias, emb, B, s) : launch_mfma_tiles<2, T>(a, W, bias, emb, B, s);
+  return B <= 16 ? launch_mfma_tiles<1, T, N>(a, W, bias, emb, B, s)
+                 : launch_mfma_tiles<2, T, N>(a, W, bias, emb, B, s);
 }
+template <int N = kN>
 hipError_t launch_mfma(const uint16_t* temb, uint16_t* a, const uint16_t* W, const uint16_t* bias,
                        uint16_t* emb, int64_t B, hipStream_t s) {
   if (hipError_t e = launch_silu(temb, a, B * kD, s); e != hipSuccess) return e;
-  return launch_mfma_from_a(a, W, bias, emb, B, s);
+  return launch_mfma_from_a<uint16_t, N>(a, W, bias, emb, B, s);
+}
+
+template <int N>
+hipError_t proj_fwd_rows(const uint16_t* temb, const uint16_t* W, const uint16_t* bias, uint16_t* emb,
+                         uint16_t* a, int64_t B, hipStream_t s) {
+  if (B > kMaxNarrowBatch) return launch_mfma<N>(temb, a, W, bias, emb, B, s);
+  return by_batch(B, [&](auto nb) {
+    hipLaunchKernelGGL((proj_fwd_kernel<decltype(nb)::value, N>), dim3(N / kProjRowsPerBlock), dim3(kThreads), 0,
+                       s, temb, W, bias, emb);
+    return hipGetLastError();
+  });
 }
 
 }  // namespace
 
 hipError_t launch_proj_fwd(const uint16_t* temb, const uint16_t* W, const uint16_t* bias,
-                           uint16_t* emb, uint16_t* a, int64_t B, hipStream_t s) {
-  if (B > kMaxNarrowBatch) return launch_mfma(temb, a, W, bias, emb, B, s);
-  return by_batch(B, [&](auto nb) {
-    hipLaunchKernelGGL(proj_fwd_kernel<decltype(nb)::value>, dim3(kProjBlocks), dim3(kThreads), 0, s, temb,
-                       W, bias, emb);
-    return hipGetLastError();
-  });
+                           uint16_t* emb, uint16_t* a, int64_t B, int64_t N, hipStream_t s) {
+  if (N == kN) return proj_fwd_rows<kN>(temb, W, bias, emb, a, B, s);
+  if (N == kN6) return proj_fwd_rows<kN6>(temb, W, bias, emb, a, B, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_norm_mod_fwd(const uint16_t* x, const uint16_t* emb, uint16_t* out, float* mean,

@@ -11,8 +11,9 @@ hipError_t launch_silu(const uint16_t* temb, uint16_t* a, int64_t n, hipStream_t
 hipError_t launch_fwd(const uint16_t* temb, const uint16_t* W, const uint16_t* bias,
                       const uint16_t* x, uint16_t* emb, uint16_t* out, float* mean, float* rstd,
                       int64_t B, int64_t S, float eps, hipStream_t s);
+// projections: N = kN (final modulation) or kN6 (a block's 6-way modulation)
 hipError_t launch_proj_fwd(const uint16_t* temb, const uint16_t* W, const uint16_t* bias,
-                           uint16_t* emb, uint16_t* a, int64_t B, hipStream_t s);
+                           uint16_t* emb, uint16_t* a, int64_t B, int64_t N, hipStream_t s);
 hipError_t launch_norm_mod_fwd(const uint16_t* x, const uint16_t* emb, uint16_t* out,
                                float* mean, float* rstd, int64_t B, int64_t S, float eps,
                                hipStream_t s);
@@ -33,18 +34,20 @@ hipError_t launch_tree_fold(const float* part, float* out, int64_t B,
                             int64_t T0, int64_t H, hipStream_t s);
 int proj_bwd_fused_max_batch();
 hipError_t launch_proj_bwd_fused(const float* d_emb, const uint16_t* temb, const uint16_t* W,
-                                 uint16_t* dW, uint16_t* db, uint16_t* dtemb, int64_t B, hipStream_t s);
+                                 uint16_t* dW, uint16_t* db, uint16_t* dtemb, int64_t B, int64_t N,
+                                 hipStream_t s, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 hipError_t launch_proj_bwd_dw(const float* d_emb, const uint16_t* a, uint16_t* dW, uint16_t* db,
-                              int64_t B, hipStream_t s);
+                              int64_t B, int64_t N, hipStream_t s);
 hipError_t launch_proj_bwd_da(const float* d_emb, const uint16_t* W, const uint16_t* temb,
-                              uint16_t* dtemb, int64_t B, hipStream_t s);
+                              uint16_t* dtemb, int64_t B, int64_t N, hipStream_t s);
 // residual norm site (mod = shift | scale | gate); part: pairs of 3D columns
 hipError_t launch_residual_fwd(const uint16_t* x, const uint16_t* residual, const uint16_t* mod, uint16_t* h,
                                uint16_t* out, float* mean, float* rstd, int64_t B, int64_t S, float eps,
                                hipStream_t s);
 hipError_t launch_residual_bwd(const uint16_t* g_out, const uint16_t* g_h, const uint16_t* x, const uint16_t* h,
                                const float* mean, const float* rstd, const uint16_t* mod, uint16_t* d_residual,
-                               uint16_t* dx, float* part, int64_t B, int64_t S, hipStream_t s);
+                               uint16_t* dx, float* part, int64_t B, int64_t S, hipStream_t s,
+                               hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 // fp32 storage
 hipError_t launch_silu_f32(const float* temb, float* a, int64_t n, hipStream_t s);
 hipError_t launch_proj_fwd_f32(const float* temb, float* a, const float* W, const float* bias, float* emb,

@@ -413,11 +413,18 @@ hipError_t launch_norm_mod_bwd_tiles(const uint16_t* g, const uint16_t* x, const
 
 hipError_t launch_residual_bwd(const uint16_t* g_out, const uint16_t* g_h, const uint16_t* x, const uint16_t* h,
                                const float* mean, const float* rstd, const uint16_t* mod, uint16_t* d_residual,
-                               uint16_t* dx, float* part, int64_t B, int64_t S, hipStream_t s) {
+                               uint16_t* dx, float* part, int64_t B, int64_t S, hipStream_t s, hipEvent_t e0,
+                               hipEvent_t e1) {
   const int64_t T0 = (S + kTile - 1) / kTile;
   const int64_t groups = (B * T0 + 7) / 8;
-  hipLaunchKernelGGL(residual_bwd_kernel, dim3(static_cast<unsigned>(groups * 8 * kBlocksPerTile)), dim3(kThreads),
-                     0, s, g_out, g_h, x, h, mean, rstd, mod, d_residual, dx, part, B, S, T0);
+  const dim3 grid(static_cast<unsigned>(groups * 8 * kBlocksPerTile));
+  if (e0 && e1) {
+    hipExtLaunchKernelGGL(residual_bwd_kernel, grid, dim3(kThreads), 0, s, e0, e1, 0, g_out, g_h, x, h, mean, rstd,
+                          mod, d_residual, dx, part, B, S, T0);
+  } else {
+    hipLaunchKernelGGL(residual_bwd_kernel, grid, dim3(kThreads), 0, s, g_out, g_h, x, h, mean, rstd, mod,
+                       d_residual, dx, part, B, S, T0);
+  }
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   hipLaunchKernelGGL(gate_tile_kernel, dim3(static_cast<unsigned>(B * T0 * kColBlocks)), dim3(kThreads), 0, s,
                      d_residual, x, part, S, T0);

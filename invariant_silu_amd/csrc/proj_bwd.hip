@@ -9,8 +9,10 @@
 // operands) and the sums run in fp64 in fixed orders:
 //   dW: samples ascending from +0, one fused multiply-add each;
 //   db: samples ascending from +0 (plain adds);
-//   da: 128 leaves, leaf t over rows t, t + 128, ..., t + 128 * 47 in that
-//       order from +0; then the leaves added pairwise in index order.
+//   da: 128 leaves, leaf t over rows t, t + 128, ..., t + 128 (N / 128 - 1)
+//       in that order from +0; then the leaves added pairwise in index order.
+// N is the projection width: 6144 for the final modulation, 18432 for a
+// block's 6-way modulation (a template parameter of every kernel here).
 // The vector-unit kernels (B <= 4) and the matrix-core kernels (B > 4; a
 // v_mfma_f64_16x16x4f64 is that same chain of four fused multiply-adds) run
 // these orders exactly, so no result depends on the batch size or the grid.
@@ -19,6 +21,8 @@
 //   proj_bwd_small_kernel<NB>  B <= 4: da column blocks (-> dtemb) and dW
 //                              tiles (-> dW, db) in one grid
 //   silu_kernel, dw_mfma_kernel, da_mfma_kernel   B > 4
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "mfma.hpp"
@@ -30,23 +34,25 @@ namespace {
 constexpr int kThreads = 256;
 
 // ---- projection backward ------------------------------------------------
-// dW tiles: part p of 32 (192 rows) x column block kb of 12 (256 columns),
-// a write stream; 8 row slots, a thread's 8 columns per row.
-constexpr int kDwParts = 32;
+// dW tiles: part p of N / 192 (192 rows) x column block kb of 12 (256
+// columns), a write stream; 8 row slots, a thread's 8 columns per row.
 constexpr int kTileCols = 256;                       // columns per dW tile (32 threads x 8)
 constexpr int kColThreads = kTileCols / 8;           // 32
 constexpr int kSlots = 8;                            // row slots per dW tile
 constexpr int kBlockThreads = kColThreads * kSlots;  // 256
-constexpr int kRowsPerPart = kN / kDwParts;          // 192
+constexpr int kRowsPerPart = 192;
 constexpr int kSteps = kRowsPerPart / kSlots;        // 24 rows per thread
-constexpr int kDwTiles = kDwParts * (kD / kTileCols);   // 384
+template <int N>
+constexpr int kDwParts = N / kRowsPerPart;           // 32 at N = 6144
+template <int N>
+constexpr int kDwTiles = kDwParts<N> * (kD / kTileCols);   // 384 at N = 6144
 constexpr int kBatchChunk = 4;
 
-static_assert(kN % kDwParts == 0 && kRowsPerPart % kSlots == 0, "part layout");
+static_assert(kN % kRowsPerPart == 0 && kN6 % kRowsPerPart == 0 && kRowsPerPart % kSlots == 0, "part layout");
 static_assert(kD % kTileCols == 0, "column blocks");
 static_assert(kBlockThreads == kThreads, "one block size for every role");
 
-// da blocks: 16 columns of W over all 6144 rows, so each block finishes the
+// da blocks: 16 columns of W over all N rows, so each block finishes the
 // sum and writes dtemb itself.  128 row slots, slot t = leaf t: rows t,
 // t + 128, ... in order; the 128 slots are then added as a pairwise tree.  The four 32-byte quarters of a 128-byte row
 // segment go to blocks L, L + 8, L + 16 and L + 24, which the dispatcher
@@ -55,11 +61,12 @@ constexpr int kDaCols = 16;
 constexpr int kDaColThreads = kDaCols / 8;            // 2
 constexpr int kDaSlots = kThreads / kDaColThreads;    // 128
 constexpr int kDaBlocks = kD / kDaCols;               // 192
-constexpr int kDaSteps = kN / kDaSlots;               // 48 rows per thread
+template <int N>
+constexpr int kDaSteps = N / kDaSlots;                // rows per thread: 48 at N = 6144
 constexpr int kDaShare = 128 / (kDaCols * 2);         // blocks sharing a 128-byte segment: 4
 
 static_assert(kDaBlocks % (8 * kDaShare) == 0, "da block to column mapping");
-static_assert(kDaSteps == 48, "a slot is one leaf of 48 rows");
+static_assert(kDaSteps<kN> == 48, "a slot is one leaf of 48 rows");
 
 // 8 consecutive elements of one row: one 16-byte load (bf16) or two (fp32)
 template <typename T>
@@ -128,19 +135,20 @@ __device__ __forceinline__ int da_first_col(int L) {
 // da and dtemb for samples b0 .. b0 + nb - 1 (nb <= NB) and the 16 columns of
 // block L; T is the storage type of W, temb and dtemb.  red: LDS,
 // kDaSlots * NB * kDaCols doubles.
-template <int NB, typename T>
+template <int NB, typename T, int N = kN>
 __device__ __forceinline__ void da_block(const float* __restrict__ d_emb, const T* __restrict__ W,
                                          const T* __restrict__ temb, T* __restrict__ dtemb,
                                          int L, int64_t b0, int nb, double* red) {
   // rows per batch (two batches in flight), sized to keep registers <= ~128
   constexpr int U = sizeof(T) == 4 ? 4 : (NB == 1 ? 8 : (NB == 2 ? 6 : (NB == 3 ? 6 : 4)));
-  static_assert(kDaSteps % (2 * U) == 0, "batch pairs");
-  static_assert(kDaSteps % U == 0, "batches");
+  constexpr int kLeafRows = kDaSteps<N>;
+  static_assert(kLeafRows % (2 * U) == 0, "batch pairs");
+  static_assert(kLeafRows % U == 0, "batches");
   const int ct = threadIdx.x % kDaColThreads;
   const int slot = threadIdx.x / kDaColThreads;
   const int col0 = da_first_col(L);
-  const Buffer wb(W, static_cast<uint32_t>(kN) * kD * sizeof(T));
-  const Buffer eb(d_emb + b0 * kN, static_cast<uint32_t>(nb) * kN * 4);
+  const Buffer wb(W, static_cast<uint32_t>(N) * kD * sizeof(T));
+  const Buffer eb(d_emb + b0 * N, static_cast<uint32_t>(nb) * N * 4);
   const uint32_t w_lane = (static_cast<uint32_t>(slot) * kD + col0 + ct * 8) * sizeof(T);
   const uint32_t e_lane = static_cast<uint32_t>(slot) * 4;
   constexpr uint32_t kWStep = kDaSlots * kD * sizeof(T);   // bytes between a slot's rows
@@ -154,7 +162,7 @@ __device__ __forceinline__ void da_block(const float* __restrict__ d_emb, const 
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int bl = b < nb ? b : nb - 1;   // samples past nb: any in-range value, never stored
-        d[u][b] = eb.f32(e_lane, bl * kN * 4 + (i0 + u) * kEStep);
+        d[u][b] = eb.f32(e_lane, bl * N * 4 + (i0 + u) * kEStep);
       }
   };
   double acc[NB][8];
@@ -183,7 +191,7 @@ __device__ __forceinline__ void da_block(const float* __restrict__ d_emb, const 
   // (scheduling barriers keep the compiler from hoisting a batch's loads
   // above the adds of the batch whose registers they reuse)
 #pragma unroll 1
-  for (int i0 = 0; i0 < kDaSteps - 2 * U; i0 += 2 * U) {
+  for (int i0 = 0; i0 < kLeafRows - 2 * U; i0 += 2 * U) {
     load(i0 + U, wbt, db_);
     __builtin_amdgcn_sched_barrier(0);
     accumulate(wa, da_);
@@ -193,7 +201,7 @@ __device__ __forceinline__ void da_block(const float* __restrict__ d_emb, const 
     accumulate(wbt, db_);
     __builtin_amdgcn_sched_barrier(0);
   }
-  load(kDaSteps - U, wbt, db_);
+  load(kLeafRows - U, wbt, db_);
   __builtin_amdgcn_sched_barrier(0);
   accumulate(wa, da_);
   accumulate(wbt, db_);
@@ -225,7 +233,7 @@ __device__ __forceinline__ void da_block(const float* __restrict__ d_emb, const 
 // dW tile (192 rows x 256 columns of part p, column block kb): a write
 // stream; a = bf16(SiLU(temb)) per thread for its 8 columns.  Tiles of column
 // block 0 also write db for their rows: samples in order from +0.
-template <int NB>
+template <int NB, int N = kN>
 __device__ __forceinline__ void dw_tile(const float* __restrict__ d_emb,
                                         const uint16_t* __restrict__ temb, uint16_t* __restrict__ dW,
                                         uint16_t* __restrict__ db, int p, int kb,
@@ -240,7 +248,7 @@ __device__ __forceinline__ void dw_tile(const float* __restrict__ d_emb,
   for (int k = 0; k < kDeLoads; ++k) {
     const int idx = threadIdx.x + kBlockThreads * k;
     if (idx < NB * kRowsPerPart)
-      de_r[k] = d_emb[static_cast<int64_t>(idx / kRowsPerPart) * kN + jbase + idx % kRowsPerPart];
+      de_r[k] = d_emb[static_cast<int64_t>(idx / kRowsPerPart) * N + jbase + idx % kRowsPerPart];
   }
   uint4 tz[NB];
 #pragma unroll
@@ -301,20 +309,21 @@ struct ProjBwdShared {
 };
 
 // Small batches (B <= 4, a template parameter): one grid, blocks [0, 192)
-// are the da column blocks (they read W and write dtemb), blocks [192, 576)
-// the dW tiles (they write dW and db); the two streams run side by side.
-template <int NB>
+// are the da column blocks (they read W and write dtemb), the rest the dW
+// tiles (they write dW and db): [192, 576) at N = 6144; the two streams run
+// side by side.
+template <int NB, int N = kN>
 __global__ __launch_bounds__(kThreads) void proj_bwd_small_kernel(
     const float* __restrict__ d_emb, const uint16_t* __restrict__ temb, const uint16_t* __restrict__ W,
     uint16_t* __restrict__ dW, uint16_t* __restrict__ db, uint16_t* __restrict__ dtemb) {
   __shared__ __align__(16) unsigned char smem[ProjBwdShared<NB>::kBytes];
   const int blk = blockIdx.x;
   if (blk < kDaBlocks) {
-    da_block<NB, uint16_t>(d_emb, W, temb, dtemb, blk, 0, NB, reinterpret_cast<double*>(smem));
+    da_block<NB, uint16_t, N>(d_emb, W, temb, dtemb, blk, 0, NB, reinterpret_cast<double*>(smem));
   } else {
     const int t = blk - kDaBlocks;
-    dw_tile<NB>(d_emb, temb, dW, db, t % kDwParts, t / kDwParts,
-                reinterpret_cast<float (*)[kRowsPerPart]>(smem));
+    dw_tile<NB, N>(d_emb, temb, dW, db, t % kDwParts<N>, t / kDwParts<N>,
+                   reinterpret_cast<float (*)[kRowsPerPart]>(smem));
   }
 }
 
@@ -337,12 +346,12 @@ __global__ __launch_bounds__(256) void silu_kernel(const uint16_t* __restrict__ 
 // sample 4 s + g): each sum is the chain over samples in ascending order from
 // +0, as in dw_tile.  Samples past B enter with d_emb = 0, which leaves every
 // sum unchanged (the chain never holds -0).  Waves of column block 0 also sum
-// db for their 64 rows.  T: storage type of a, dW and db.
+// db for their 64 rows.  T: storage type of a, dW and db; N rows.
 constexpr int kDwMRows = 64;
 constexpr int kDwMCols = 32;
 constexpr int kDwMWaves = 4;
 
-template <typename T>
+template <typename T, int N = kN>
 __global__ __launch_bounds__(64 * kDwMWaves) void dw_mfma_kernel(const float* __restrict__ d_emb,
                                                                  const T* __restrict__ a,
                                                                  T* __restrict__ dW,
@@ -365,7 +374,7 @@ __global__ __launch_bounds__(64 * kDwMWaves) void dw_mfma_kernel(const float* __
   auto load = [&](int64_t st, float4& dv, Pair<T>& av) {
     const int64_t b = 4 * st + g;
     const int64_t bc = b < B ? b : B - 1;
-    dv = *reinterpret_cast<const float4*>(dp + bc * kN);
+    dv = *reinterpret_cast<const float4*>(dp + bc * N);
     av.load(ap + bc * kD);
     if (b >= B) dv = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   };
@@ -399,7 +408,7 @@ __global__ __launch_bounds__(64 * kDwMWaves) void dw_mfma_kernel(const float* __
                      static_cast<float>(acc[m][0][v]), static_cast<float>(acc[m][1][v]));
   if (blockIdx.y == 0 && wave == 0) {
     double sdb = 0.0;
-    for (int64_t b = 0; b < B; ++b) sdb += static_cast<double>(d_emb[b * kN + j0 + lane]);
+    for (int64_t b = 0; b < B; ++b) sdb += static_cast<double>(d_emb[b * N + j0 + lane]);
     db[j0 + lane] = Storage<T>::store1(static_cast<float>(sdb));
   }
 }
@@ -408,7 +417,7 @@ __global__ __launch_bounds__(64 * kDwMWaves) void dw_mfma_kernel(const float* __
 // wave w takes leaves 16 w .. 16 w + 15 in four groups of four consecutive
 // leaves t0 .. t0 + 3, run side by side (8 chains: 4 leaves x 2 column
 // tiles).  Step s of a leaf feeds rows t + 128 (4 s + g) at slot g, so a
-// leaf's 12 steps are its 48 rows in order.  Output tile n (0, 1) holds
+// leaf's N / 512 steps (12 at N = 6144) are its rows in order.  Output tile n (0, 1) holds
 // columns k0 + 2 c + n.  Lane (r, g) loads d_emb[b0 + r][t0 + 128 (4 s + g)
 // .. + 3] (16 bytes: the four leaves) and W[t0 + l + 128 (4 s + g)][k0 + 2 r ..
 // + 1] for l = 0 .. 3.  Leaf results go into the wave's leaf tree in order;
@@ -416,7 +425,8 @@ __global__ __launch_bounds__(64 * kDwMWaves) void dw_mfma_kernel(const float* __
 // so two blocks fit a CU.  Blocks x and x + 8
 // (same XCD) take the two halves of one 128-byte row segment of W.  Rows
 // past B load sample B - 1 and are never stored.
-constexpr int kLeafSteps = 12;   // 48 rows of a leaf, 4 per matrix-core step
+template <int N>
+constexpr int kLeafSteps = N / (4 * kDaSlots);   // a leaf's rows, 4 per matrix-core step
 constexpr int kDaMWaves = 8;
 constexpr int kDaMLeaves = 128 / kDaMWaves;    // 16 per wave
 constexpr int kDaMGroup = 4;                   // leaves run side by side
@@ -429,8 +439,8 @@ struct DaStep {
   Pair<T> w[4];     // W, 2 columns, per leaf
 };
 
-// T: storage type of W, temb and dtemb
-template <typename T>
+// T: storage type of W, temb and dtemb; N rows of W
+template <typename T, int N = kN>
 __global__ __launch_bounds__(64 * kDaMWaves) void da_mfma_kernel(const float* __restrict__ d_emb,
                                                                  const T* __restrict__ W,
                                                                  const T* __restrict__ temb,
@@ -445,9 +455,9 @@ __global__ __launch_bounds__(64 * kDaMWaves) void da_mfma_kernel(const float* __
   const int rows_here = static_cast<int>((B - b0) < 16 ? (B - b0) : 16);
   const int br = r < rows_here ? r : rows_here - 1;
 
-  const Buffer eb(d_emb + b0 * kN, static_cast<uint32_t>(rows_here) * kN * 4);
-  const Buffer wbuf(W, static_cast<uint32_t>(kN) * kD * sizeof(T));
-  const uint32_t e_off = (static_cast<uint32_t>(br) * kN + kDaSlots * g) * 4;
+  const Buffer eb(d_emb + b0 * N, static_cast<uint32_t>(rows_here) * N * 4);
+  const Buffer wbuf(W, static_cast<uint32_t>(N) * kD * sizeof(T));
+  const uint32_t e_off = (static_cast<uint32_t>(br) * N + kDaSlots * g) * 4;
   const uint32_t w_off = (static_cast<uint32_t>(kDaSlots * g) * kD + k0 + 2 * r) * sizeof(T);
   const int leaf0 = wave * kDaMLeaves;
 
@@ -468,8 +478,8 @@ __global__ __launch_bounds__(64 * kDaMWaves) void da_mfma_kernel(const float* __
 #pragma unroll
     for (int l = 0; l < kDaMGroup; ++l) acc[l][0] = acc[l][1] = f64x4_t{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int st = 0; st < kLeafSteps; ++st) {
-      if (st + kDaMAhead < kLeafSteps) load(buf[(st + kDaMAhead) % (kDaMAhead + 1)], st + kDaMAhead);
+    for (int st = 0; st < kLeafSteps<N>; ++st) {
+      if (st + kDaMAhead < kLeafSteps<N>) load(buf[(st + kDaMAhead) % (kDaMAhead + 1)], st + kDaMAhead);
       const DaStep<T>& cur = buf[st % (kDaMAhead + 1)];
       const uint32_t dv[4] = {cur.d.x, cur.d.y, cur.d.z, cur.d.w};
 #pragma unroll
@@ -529,32 +539,72 @@ __global__ __launch_bounds__(kThreads) void da_small_f32_kernel(const float* __r
 
 int proj_bwd_fused_max_batch() { return kBatchChunk; }
 
-hipError_t launch_proj_bwd_fused(const float* d_emb, const uint16_t* temb, const uint16_t* W,
-                                 uint16_t* dW, uint16_t* db, uint16_t* dtemb, int64_t B, hipStream_t s) {
-  const dim3 grid(kDaBlocks + kDwTiles), block(kThreads);
+namespace {
+
+template <int NB, int N>
+void launch_small(const float* d_emb, const uint16_t* temb, const uint16_t* W, uint16_t* dW, uint16_t* db,
+                  uint16_t* dtemb, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  const dim3 grid(kDaBlocks + kDwTiles<N>), block(kThreads);
+  if (e0 && e1)
+    hipExtLaunchKernelGGL((proj_bwd_small_kernel<NB, N>), grid, block, 0, s, e0, e1, 0, d_emb, temb, W, dW, db,
+                          dtemb);
+  else
+    hipLaunchKernelGGL((proj_bwd_small_kernel<NB, N>), grid, block, 0, s, d_emb, temb, W, dW, db, dtemb);
+}
+
+template <int N>
+hipError_t proj_bwd_fused_rows(const float* d_emb, const uint16_t* temb, const uint16_t* W, uint16_t* dW,
+                               uint16_t* db, uint16_t* dtemb, int64_t B, hipStream_t s, hipEvent_t e0,
+                               hipEvent_t e1) {
   switch (B) {
-    case 1: hipLaunchKernelGGL(proj_bwd_small_kernel<1>, grid, block, 0, s, d_emb, temb, W, dW, db, dtemb); break;
-    case 2: hipLaunchKernelGGL(proj_bwd_small_kernel<2>, grid, block, 0, s, d_emb, temb, W, dW, db, dtemb); break;
-    case 3: hipLaunchKernelGGL(proj_bwd_small_kernel<3>, grid, block, 0, s, d_emb, temb, W, dW, db, dtemb); break;
-    case 4: hipLaunchKernelGGL(proj_bwd_small_kernel<4>, grid, block, 0, s, d_emb, temb, W, dW, db, dtemb); break;
+    case 1: launch_small<1, N>(d_emb, temb, W, dW, db, dtemb, s, e0, e1); break;
+    case 2: launch_small<2, N>(d_emb, temb, W, dW, db, dtemb, s, e0, e1); break;
+    case 3: launch_small<3, N>(d_emb, temb, W, dW, db, dtemb, s, e0, e1); break;
+    case 4: launch_small<4, N>(d_emb, temb, W, dW, db, dtemb, s, e0, e1); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_proj_bwd_dw(const float* d_emb, const uint16_t* a, uint16_t* dW, uint16_t* db, int64_t B,
-                              hipStream_t s) {
-  hipLaunchKernelGGL(dw_mfma_kernel<uint16_t>, dim3(kN / kDwMRows, kD / (kDwMCols * kDwMWaves)),
+template <int N>
+hipError_t proj_bwd_dw_rows(const float* d_emb, const uint16_t* a, uint16_t* dW, uint16_t* db, int64_t B,
+                            hipStream_t s) {
+  hipLaunchKernelGGL((dw_mfma_kernel<uint16_t, N>), dim3(N / kDwMRows, kD / (kDwMCols * kDwMWaves)),
                      dim3(64 * kDwMWaves), 0, s, d_emb, a, dW, db, B);
   return hipGetLastError();
 }
 
-hipError_t launch_proj_bwd_da(const float* d_emb, const uint16_t* W, const uint16_t* temb, uint16_t* dtemb,
-                              int64_t B, hipStream_t s) {
+template <int N>
+hipError_t proj_bwd_da_rows(const float* d_emb, const uint16_t* W, const uint16_t* temb, uint16_t* dtemb,
+                            int64_t B, hipStream_t s) {
   const int64_t by = (B + 15) / 16;
-  hipLaunchKernelGGL(da_mfma_kernel<uint16_t>, dim3(kD / kDaMCols, static_cast<unsigned>(by)), dim3(64 * kDaMWaves),
-                     0, s, d_emb, W, temb, dtemb, B);
+  hipLaunchKernelGGL((da_mfma_kernel<uint16_t, N>), dim3(kD / kDaMCols, static_cast<unsigned>(by)),
+                     dim3(64 * kDaMWaves), 0, s, d_emb, W, temb, dtemb, B);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_proj_bwd_fused(const float* d_emb, const uint16_t* temb, const uint16_t* W,
+                                 uint16_t* dW, uint16_t* db, uint16_t* dtemb, int64_t B, int64_t N, hipStream_t s,
+                                 hipEvent_t e0, hipEvent_t e1) {
+  if (N == kN) return proj_bwd_fused_rows<kN>(d_emb, temb, W, dW, db, dtemb, B, s, e0, e1);
+  if (N == kN6) return proj_bwd_fused_rows<kN6>(d_emb, temb, W, dW, db, dtemb, B, s, e0, e1);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_proj_bwd_dw(const float* d_emb, const uint16_t* a, uint16_t* dW, uint16_t* db, int64_t B,
+                              int64_t N, hipStream_t s) {
+  if (N == kN) return proj_bwd_dw_rows<kN>(d_emb, a, dW, db, B, s);
+  if (N == kN6) return proj_bwd_dw_rows<kN6>(d_emb, a, dW, db, B, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_proj_bwd_da(const float* d_emb, const uint16_t* W, const uint16_t* temb, uint16_t* dtemb,
+                              int64_t B, int64_t N, hipStream_t s) {
+  if (N == kN) return proj_bwd_da_rows<kN>(d_emb, W, temb, dtemb, B, s);
+  if (N == kN6) return proj_bwd_da_rows<kN6>(d_emb, W, temb, dtemb, B, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_silu(const uint16_t* temb, uint16_t* a, int64_t n, hipStream_t s) {

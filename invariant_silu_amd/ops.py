@@ -47,12 +47,14 @@ def _ws(op: int, B: int, S: int, H: int, device) -> torch.Tensor:
 
 
 def proj_fwd(temb: torch.Tensor, W: torch.Tensor, bias: torch.Tensor) -> torch.Tensor:
-    """emb [B, 6144] bf16 = bf16(SiLU(temb) W^T + b) = (scale | shift)."""
+    """emb [B, N] bf16 = bf16(SiLU(temb) W^T + b), N = W.shape[0]: 6144 for the
+    final modulation (scale | shift), 18432 for a block's 6-way modulation
+    (shift1 | scale1 | gate1 | shift2 | scale2 | gate2)."""
     for t, n in ((temb, "temb"), (W, "W"), (bias, "bias")):
         _check(t, torch.bfloat16, n)
     temb, W, bias = aligned(temb), aligned(W), aligned(bias)
     B = temb.shape[0]
-    emb = torch.empty((B, N), dtype=torch.bfloat16, device=temb.device)
+    emb = torch.empty((B, W.shape[0]), dtype=torch.bfloat16, device=temb.device)
     ws = _ws(_lib.OP_PROJ_FWD, B, 1, temb.shape[1], temb.device)
     _lib.call("adaln_proj_fwd", temb.data_ptr(), W.data_ptr(), bias.data_ptr(), emb.data_ptr(),
               ws.data_ptr(), ws.numel(), B, temb.shape[1], W.shape[0], _stream(temb.device))
@@ -93,7 +95,8 @@ def norm_mod_bwd(g: torch.Tensor, x: torch.Tensor, mean: torch.Tensor, rstd: tor
 
 
 def proj_bwd(d_emb: torch.Tensor, temb: torch.Tensor, W: torch.Tensor):
-    """(dW bf16 [6144, 3072], db bf16 [6144], dtemb bf16 [B, 3072])."""
+    """(dW bf16 [N, 3072], db bf16 [N], dtemb bf16 [B, 3072]); N = W.shape[0]
+    (6144 or 18432, as for proj_fwd)."""
     _check(d_emb, torch.float32, "d_emb")
     _check(temb, torch.bfloat16, "temb")
     _check(W, torch.bfloat16, "W")

@@ -87,6 +87,20 @@ def test_validation_before_device_work(L):
     # a workspace smaller than adaln_workspace_bytes(PROJ_FWD) is refused
     assert L.adaln_proj_fwd(p, p + (1 << 20), p + (2 << 20), p + (3 << 20), p + (4 << 20), 16,
                             8, 3072, 6144, None) == lib.ERR_WORKSPACE
+    # projection widths: 6144 (final modulation) and 18432 (a block's 6-way
+    # modulation) pass the shape check, others do not
+    for n in (3072, 12288, 18431, 24576):
+        assert L.adaln_proj_fwd(p, p, p, p, p, 1 << 20, 1, 3072, n, None) == lib.ERR_SHAPE
+        assert L.adaln_proj_bwd(p, p, p, p, p, p, p, 1 << 20, 1, 3072, n, None) == lib.ERR_SHAPE
+    assert L.adaln_proj_fwd(p, p + (1 << 20), p + (2 << 20), p + (3 << 20), p + (4 << 20), 16,
+                            8, 3072, 18432, None) == lib.ERR_WORKSPACE
+    pb = [p + (k << 28) for k in range(7)]
+    assert L.adaln_proj_bwd(*pb, 16, 8, 3072, 18432, None) == lib.ERR_WORKSPACE
+    # the overlap check spans N rows of W: emb 100 MB past W's start lies inside
+    # a 6-way W (113 MB) but not inside a final-modulation W (37.7 MB)
+    args = (p, p + (1 << 20), p + (200 << 20), p + (101 << 20), p + (300 << 20), 1 << 20, 1, 3072)
+    assert L.adaln_proj_fwd(*args, 18432, None) == lib.ERR_OVERLAP
+    assert L.adaln_proj_fwd(*args, 6144, None) != lib.ERR_OVERLAP
     assert L.adaln_norm_mod_fwd(p, p, p, p, p, 1, 0, 3072, 1e-6, None) == lib.ERR_SHAPE
     assert L.token_tree_sum(p, p, p, 1 << 20, 1, 1, 0, None) == lib.ERR_SHAPE
     assert L.adaln_norm_mod_fwd(p + 2, p, p, p, p, 1, 1, 3072, 1e-6, None) == lib.ERR_ALIGN

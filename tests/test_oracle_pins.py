@@ -17,9 +17,9 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from oracle import adaln, fpmath, residual, token_tree
+from oracle import adaln, fpmath, modulation, residual, token_tree
 from oracle.fpmath import bf16_ulp_diff, bits_to_f32, f32_to_bf16_bits, nsum
-from synthetic_inputs import cancellation_tokens, make_inputs, make_residual_inputs
+from synthetic_inputs import cancellation_tokens, make_inputs, make_mod6_inputs, make_residual_inputs
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 D = 3072
@@ -650,6 +650,83 @@ def test_residual_site_finite_differences():
 def test_teeth_residual_gradient_dropped_caught():
     """Leaving g_h out of dh fails P-21."""
     assert _residual_fd(drop_gh=True) > 1e-3
+
+
+# ------------------------------------------------ 6-way modulation projection --
+def test_mod6_projection_float64_and_chunks():
+    """P-22: the 6-way projection (W6 [6K, K]) against numpy's float64 matmul;
+    W6 = six scaled identities c_q I with b6 = 0 puts c_q * a in chunk q
+    exactly, and site_chunks(., 2) returns chunks 3, 4, 5 as shift, scale, gate."""
+    K = 64
+    inp = make_mod6_inputs(3, seed=40, K=K)
+    f = modulation.mod6_forward(inp)
+    a = f["a"].astype(np.float64)
+    W = bits_to_f32(inp["W"]).astype(np.float64)
+    bias = bits_to_f32(inp["bias"]).astype(np.float64)
+    d = bf16_ulp_diff(f["emb_bits"], fpmath.f64_to_bf16_bits(a @ W.T + bias))
+    assert d.max() <= 1 and (d == 0).mean() > 0.99
+    c = np.array([1.0, 2.0, -1.0, 0.5, 4.0, -2.0], np.float32)
+    inp["W"] = f32_to_bf16_bits(np.concatenate([ci * np.eye(K, dtype=np.float32) for ci in c]))
+    inp["bias"] = np.zeros_like(inp["bias"])
+    f2 = modulation.mod6_forward(inp)
+    av = f2["a"].astype(np.float32)
+    for q in range(6):
+        assert np.array_equal(f2["emb_bits"][:, q * K:(q + 1) * K], f32_to_bf16_bits(c[q] * av))
+    ch = modulation.site_chunks(bits_to_f32(f2["emb_bits"]), 2)
+    for name, q in (("shift", 3), ("scale", 4), ("gate", 5)):
+        assert np.array_equal(ch[name], c[q] * av)
+
+
+def _mod6_fd():
+    """Largest relative error of dW6, db6 and dtemb against central differences
+    of L = sum(emb6 * G), rounding points disabled (exact mode)."""
+    rng = np.random.default_rng(41)
+    B, K = 2, 4
+    inp = {"temb_val": rng.standard_normal((B, K)), "W_val": rng.standard_normal((6 * K, K)) * 0.4,
+           "bias_val": rng.standard_normal(6 * K) * 0.2}
+    G = rng.standard_normal((B, 6 * K))
+    f = modulation.mod6_forward(inp, "exact")
+    b = modulation.mod6_backward(dict(inp, d_emb=G.astype(np.float32)), f, "exact")
+    G = G.astype(np.float32).astype(np.float64)
+    worst = 0.0
+    for key, ana in (("W_val", b["dW"]), ("bias_val", b["db"]), ("temb_val", b["dtemb"])):
+        base = inp[key]
+        fd = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            h = 1e-6 * max(1.0, abs(base[idx]))
+            for sgn in (1, -1):
+                arr = base.copy()
+                arr[idx] += sgn * h
+                L = float((modulation.mod6_forward(dict(inp, **{key: arr}), "exact")["emb"] * G).sum())
+                fd[idx] += sgn * L / (2 * h)
+        worst = max(worst, float(np.abs(fd - ana).max() / max(np.abs(fd).max(), 1e-12)))
+    return worst
+
+
+def test_mod6_backward_closed_forms_and_finite_differences():
+    """P-23: one sample: dW6 = bf16(d_emb (x) a) (one fp32 product each), db6 =
+    bf16(d_emb); every gradient against central differences."""
+    inp = make_mod6_inputs(1, seed=42, K=32)
+    f = modulation.mod6_forward(inp)
+    b = modulation.mod6_backward(inp, f)
+    de, a = inp["d_emb"][0], f["a"][0].astype(np.float32)
+    assert np.array_equal(b["dW_bits"], f32_to_bf16_bits(de[:, None] * a[None, :]))
+    assert np.array_equal(b["db_bits"], f32_to_bf16_bits(de))
+    assert _mod6_fd() <= 1e-6
+
+
+def test_teeth_mod6_second_site_dropped_caught(monkeypatch):
+    """A backward that takes only the first site's half of d_emb (chunks 0..2)
+    fails P-23."""
+    orig = modulation.proj_backward
+
+    def first_half(d_emb, a, W, temb, ar, want_abs=False):
+        d = np.array(d_emb, copy=True)
+        d[:, d.shape[1] // 2:] = 0
+        return orig(d, a, W, temb, ar, want_abs)
+
+    monkeypatch.setattr(modulation, "proj_backward", first_half)
+    assert _mod6_fd() > 1e-3
 
 
 # ------------------------------------------------------------ planted mistakes --
