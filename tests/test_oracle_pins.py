@@ -17,7 +17,7 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from oracle import adaln, fpmath, modulation, residual, token_tree
+from oracle import adaln, fpmath, modulation, proj_out, residual, token_tree
 from oracle.fpmath import bf16_ulp_diff, bits_to_f32, f32_to_bf16_bits, nsum
 from synthetic_inputs import cancellation_tokens, make_inputs, make_mod6_inputs, make_residual_inputs
 
@@ -727,6 +727,83 @@ def test_teeth_mod6_second_site_dropped_caught(monkeypatch):
 
     monkeypatch.setattr(modulation, "proj_backward", first_half)
     assert _mod6_fd() > 1e-3
+
+
+# ----------------------------------------------------------------- proj_out --
+def _proj_out_inputs(T, seed, K=D, O=64):
+    rng = np.random.default_rng(seed)
+    return {"out": f32_to_bf16_bits(rng.standard_normal((T, K), dtype=np.float32)),
+            "W": f32_to_bf16_bits(rng.standard_normal((O, K), dtype=np.float32) * np.float32(0.02)),
+            "bias": f32_to_bf16_bits(rng.standard_normal(O, dtype=np.float32) * np.float32(0.01)),
+            "d_lat": f32_to_bf16_bits(rng.standard_normal((T, O), dtype=np.float32))}
+
+
+def test_proj_out_float64_and_identity():
+    """P-24: latent = bf16(out Wp^T + bp) against numpy's float64 matmul; Wp =
+    [I | 0] with bp = 0 gives latent = out[:, :64] exactly."""
+    inp = _proj_out_inputs(5, seed=60)
+    f = proj_out.proj_out_forward(inp)
+    x = bits_to_f32(inp["out"]).astype(np.float64)
+    W = bits_to_f32(inp["W"]).astype(np.float64)
+    b = bits_to_f32(inp["bias"]).astype(np.float64)
+    d = bf16_ulp_diff(f["latent_bits"], fpmath.f64_to_bf16_bits(x @ W.T + b))
+    assert d.max() <= 1 and (d == 0).mean() > 0.99
+    inp["W"] = f32_to_bf16_bits(np.eye(64, D, dtype=np.float32))
+    inp["bias"] = np.zeros_like(inp["bias"])
+    assert np.array_equal(proj_out.proj_out_forward(inp)["latent_bits"], inp["out"][:, :64])
+
+
+def _proj_out_fd():
+    """Largest relative error of d_out, dWp and dbp against central differences
+    of L = sum(latent * G), rounding points disabled (exact mode)."""
+    rng = np.random.default_rng(61)
+    T, K, O = 3, 5, 4
+    inp = {"out_val": rng.standard_normal((T, K)), "W_val": rng.standard_normal((O, K)) * 0.4,
+           "bias_val": rng.standard_normal(O) * 0.2, "d_lat_val": rng.standard_normal((T, O))}
+    b = proj_out.proj_out_backward(inp, "exact")
+    G = inp["d_lat_val"]
+    worst = 0.0
+    for key, ana in (("out_val", b["d_out"]), ("W_val", b["dW"]), ("bias_val", b["db"])):
+        base = inp[key]
+        fd = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            h = 1e-6 * max(1.0, abs(base[idx]))
+            for sgn in (1, -1):
+                arr = base.copy()
+                arr[idx] += sgn * h
+                L = float((proj_out.proj_out_forward(dict(inp, **{key: arr}), "exact")["latent"] * G).sum())
+                fd[idx] += sgn * L / (2 * h)
+        worst = max(worst, float(np.abs(fd - ana).max() / max(np.abs(fd).max(), 1e-12)))
+    return worst
+
+
+def test_proj_out_backward_closed_forms_and_finite_differences():
+    """P-25: one token: dWp = bf16(d_lat (x) out) (an exact product, one
+    rounding), dbp = d_lat; d_out of Wp = [I | 0] is d_lat in the first 64
+    columns and 0 elsewhere; every gradient against central differences."""
+    inp = _proj_out_inputs(1, seed=62)
+    b = proj_out.proj_out_backward(inp)
+    dl, x = bits_to_f32(inp["d_lat"])[0], bits_to_f32(inp["out"])[0]
+    assert np.array_equal(b["dW_bits"], f32_to_bf16_bits(dl[:, None] * x[None, :]))
+    assert np.array_equal(b["db_bits"], inp["d_lat"][0])
+    inp["W"] = f32_to_bf16_bits(np.eye(64, D, dtype=np.float32))
+    b = proj_out.proj_out_backward(inp)
+    assert np.array_equal(b["d_out_bits"][:, :64], inp["d_lat"])
+    assert np.all(bits_to_f32(b["d_out_bits"][:, 64:]) == 0)
+    assert _proj_out_fd() <= 1e-6
+
+
+def test_teeth_proj_out_token_mixup_caught(monkeypatch):
+    """A backward whose d_out rows land on the wrong tokens (a token index
+    mix-up, here reversed) fails P-25's finite differences."""
+    orig = proj_out.proj_out_backward
+
+    def wrong(inp, mode="fp32", want_abs=False):
+        r = orig(inp, mode, want_abs)
+        return dict(r, d_out=r["d_out"][::-1].copy())
+
+    monkeypatch.setattr(proj_out, "proj_out_backward", wrong)
+    assert _proj_out_fd() > 1e-3
 
 
 # ------------------------------------------------------------ planted mistakes --
