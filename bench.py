@@ -13,7 +13,9 @@ h = residual + gate * x, LayerNorm of h, modulation; adaln_residual_bwd: dh and
 dx rows with the level-0 tiles of d_shift / d_scale, the d_gate tiles, the
 fold) at the same B and S, bf16 storage.  --site mod6 times a block's 6-way
 modulation projection (adaln_proj_fwd and adaln_proj_bwd at N = 18432) at the
-workload's B.
+workload's B.  --site proj_out times the 3072 -> 64 projection after the final
+modulation (adaln_proj_out_fwd and adaln_proj_out_bwd) over the workload's B * S
+tokens.
 
 Inputs are resident in HBM before the timed region.  The step rotates over
 several independent copies of every buffer (parameters included), so no step
@@ -50,6 +52,8 @@ METRIC = "fwd+bwd tokens/sec + achieved HBM GB/s at S=4096 D=3072 bf16 (batch-in
 METRIC_RESIDUAL = "residual norm site fwd+bwd tokens/sec at D=3072 bf16 (batch-invariant)"
 METRIC_MOD6 = "6-way modulation projection fwd+bwd samples/sec at 3072->18432 bf16 (batch-invariant)"
 N6 = 6 * D
+PO = 64           # proj_out channels
+METRIC_PROJ_OUT = "proj_out fwd+bwd tokens/sec at 3072->64 bf16 (batch-invariant)"
 
 
 def algorithmic_bytes(B: int, S: int, el: int = 2) -> int:
@@ -97,6 +101,18 @@ def mod6_dominant_kernel_bytes(B: int) -> int:
     return 2 * 2 * N6 * D + 2 * N6 + (4 * N6 + 2 * 2 * D) * B
 
 
+def proj_out_algorithmic_bytes(T: int) -> int:
+    """proj_out, bf16: out read by the forward and by the backward, d_out written
+    (6 bytes per element of out); latent written, d_lat read; W read twice, dW
+    written; bias read, db written."""
+    return 6 * T * D + 4 * T * PO + 6 * PO * D + 4 * PO
+
+
+def proj_out_dominant_kernel_bytes(T: int) -> int:
+    """The d_out kernel: d_lat and W read, d_out written."""
+    return 2 * T * D + 2 * T * PO + 2 * PO * D
+
+
 def pmc_traffic():
     """HBM bytes per launch of the dominant kernel from the committed PMC record,
     or None when the kernel's sources changed since the counters were taken."""
@@ -122,9 +138,9 @@ def parse():
     ap.add_argument("--workload", default="img1024_b1_s4096")
     ap.add_argument("--storage", choices=("bf16", "fp32"), default="bf16",
                     help="tensor storage type (fp32: the fp32-storage entry points)")
-    ap.add_argument("--site", choices=("final", "residual", "mod6"), default="final",
+    ap.add_argument("--site", choices=("final", "residual", "mod6", "proj_out"), default="final",
                     help="final: the final modulation (norm_out); residual: a block's residual norm site; "
-                         "mod6: a block's 6-way modulation projection")
+                         "mod6: a block's 6-way modulation projection; proj_out: the 3072 -> 64 projection")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true",
                     help="after the steps, run a plain 512 MiB device copy (PMC byte-counter calibration)")
@@ -133,10 +149,11 @@ def parse():
 
 def cpu_baseline(inp: dict, reps: int = 8, site: str = "final") -> dict:
     """The oracle (NumPy, single-threaded element-wise loops) on the same batch."""
-    from oracle import adaln, modulation, residual
+    from oracle import adaln, modulation, proj_out, residual
     fwd, bwd = {"final": (adaln.forward, adaln.backward),
                 "residual": (residual.residual_forward, residual.residual_backward),
-                "mod6": (modulation.mod6_forward, modulation.mod6_backward)}[site]
+                "mod6": (modulation.mod6_forward, modulation.mod6_backward),
+                "proj_out": (proj_out.proj_out_forward, lambda i, f: proj_out.proj_out_backward(i))}[site]
     t0 = time.perf_counter()
     for _ in range(reps):
         f = fwd(inp)
@@ -145,6 +162,9 @@ def cpu_baseline(inp: dict, reps: int = 8, site: str = "final") -> dict:
     if site == "mod6":
         return {"value": inp["B"] / dt, "unit": "samples/s", "cores": 1, "kind": "oracle",
                 "sample": f"the whole batch (B={inp['B']}), fwd+bwd, {reps} passes, {dt:.2f} s per pass"}
+    if site == "proj_out":
+        return {"value": inp["T"] / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": f"{inp['T']} of the workload's tokens, fwd+bwd, {reps} passes, {dt:.2f} s per pass"}
     tokens = inp["B"] * inp["S"]
     return {"value": tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"the whole workload batch (B={inp['B']}, S={inp['S']}), fwd+bwd, "
@@ -162,7 +182,8 @@ def main() -> int:
     import torch
 
     from invariant_silu_amd import lib
-    from synthetic_inputs import WORKLOADS, make_mod6_inputs, make_residual_inputs, make_workload
+    from synthetic_inputs import (WORKLOADS, make_mod6_inputs, make_proj_out_inputs, make_residual_inputs,
+                                  make_workload)
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -178,6 +199,7 @@ def main() -> int:
     B, S = w["B"], w["S"]
     residual_site = args.site == "residual"
     mod6_site = args.site == "mod6"
+    po_site = args.site == "proj_out"
     if args.site != "final" and args.storage != "bf16":
         print(f"--site {args.site} runs with bf16 storage only", file=sys.stderr)
         return 2
@@ -189,6 +211,9 @@ def main() -> int:
     elif mod6_site:
         inp = make_mod6_inputs(B, seed=0)
         keys = ("temb", "W", "bias")
+    elif po_site:
+        inp = make_proj_out_inputs(B * S, seed=0)
+        keys = ("out", "W", "bias", "d_lat")
     else:
         inp = make_workload(args.workload, seed=0, io=args.storage)
         keys = ("x", "temb", "W", "bias", "g")
@@ -207,6 +232,8 @@ def main() -> int:
         ws_bw = lib.workspace_bytes(lib.OP_RESIDUAL_BWD, B, S, D)
     elif mod6_site:
         ws_bw = lib.workspace_bytes(lib.OP_PROJ_BWD, B, 1, D)
+    elif po_site:
+        ws_bw = lib.workspace_bytes(lib.OP_PROJ_OUT_BWD, B, S, D)
     else:
         ws_bw = lib.workspace_bytes(lib.OP_BWD_F32 if f32 else lib.OP_BWD, B, S, D)
 
@@ -219,6 +246,15 @@ def main() -> int:
                 db=torch.empty((N6,), dtype=sdt, device=dev),
                 dtemb=torch.empty((B, D), dtype=sdt, device=dev),
                 ws_fw=torch.empty(ws_fw, dtype=torch.uint8, device=dev),
+                ws_bw=torch.empty(ws_bw, dtype=torch.uint8, device=dev),
+            )
+            return s
+        if po_site:
+            s.update(
+                latent=torch.empty((B * S, PO), dtype=sdt, device=dev),
+                d_out=torch.empty((B * S, D), dtype=sdt, device=dev),
+                dW=torch.empty((PO, D), dtype=sdt, device=dev),
+                db=torch.empty((PO,), dtype=sdt, device=dev),
                 ws_bw=torch.empty(ws_bw, dtype=torch.uint8, device=dev),
             )
             return s
@@ -245,7 +281,12 @@ def main() -> int:
             )
         return s
 
-    if mod6_site:
+    if po_site:
+        step_bytes = proj_out_algorithmic_bytes(B * S)
+        k_bytes = proj_out_dominant_kernel_bytes(B * S)
+        fwd_name, bwd_name = "adaln_proj_out_fwd", "adaln_proj_out_bwd"
+        k_name = "proj_out_dx_kernel (d_out = d_lat Wp)"
+    elif mod6_site:
         if B > 4:
             print("--site mod6 times the B <= 4 backward kernel; use a workload with B <= 4", file=sys.stderr)
             return 2
@@ -271,6 +312,12 @@ def main() -> int:
 
     def step(s):
         p = lambda k: s[k].data_ptr()   # noqa: E731
+        if po_site:
+            T = B * S
+            lib.check(fwd_name, fwd_fn(p("out"), p("W"), p("bias"), p("latent"), T, D, PO, st))
+            lib.check(bwd_name, bwd_fn(p("d_lat"), p("out"), p("W"), p("d_out"), p("dW"), p("db"), p("ws_bw"), ws_bw,
+                                       T, D, PO, st))
+            return
         if mod6_site:
             lib.check(fwd_name, fwd_fn(p("temb"), p("W"), p("bias"), p("emb"), p("ws_fw"), ws_fw, B, D, N6, st))
             lib.check(bwd_name, bwd_fn(p("d_emb"), p("temb"), p("W"), p("dW"), p("db"), p("dtemb"), p("ws_bw"),
@@ -337,7 +384,8 @@ def main() -> int:
         torch.cuda.synchronize()
 
     result = {
-        "metric": METRIC_MOD6 if mod6_site else (METRIC_RESIDUAL if residual_site else METRIC),
+        "metric": {"final": METRIC, "residual": METRIC_RESIDUAL, "mod6": METRIC_MOD6,
+                   "proj_out": METRIC_PROJ_OUT}[args.site],
         "value": round(tokens_per_s, 1),
         "unit": "samples/s" if mod6_site else "tokens/s",
         "n_gpus": 1,
@@ -350,7 +398,8 @@ def main() -> int:
         "dtype": "fp32",
         "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "S": None if mod6_site else S, "D": D,
-                   "N": N6 if mod6_site else N, "site": args.site, "storage": args.storage, "accumulate": "fp64",
+                   "N": {"mod6": N6, "proj_out": PO}.get(args.site, N), "site": args.site,
+                   "storage": args.storage, "accumulate": "fp32" if po_site else "fp64",
                    "outlier_rows": w["outlier_frac"] if args.site == "final" else 0.0,
                    "buffer_sets": nsets, "step_algorithmic_bytes": step_bytes,
                    "host_enqueue_ms_per_step": round((t_enq - t0) * 1e3 / args.steps, 5),
@@ -367,7 +416,9 @@ def main() -> int:
                      "median_launch_ms": round(k_ms[len(k_ms) // 2], 5)},
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(inp, reps=1 if mod6_site else 8, site=args.site)
+        if po_site:   # a bounded sample: the oracle on 256 of the tokens
+            inp = make_proj_out_inputs(256, seed=0)
+        result["cpu_baseline"] = cpu_baseline(inp, reps=1 if (mod6_site or po_site) else 8, site=args.site)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -123,6 +123,15 @@ size_t ws_proj_bwd(int64_t B) {
   return pad256(static_cast<size_t>(B * kD * 2));   // SiLU activations (B > 4)
 }
 size_t ws_tree(int64_t B, int64_t S, int64_t H) { return ws_pairs(B, S, H); }
+constexpr int64_t kMaxTokens = int64_t{65535} * 512;   // proj_out: its dW launch has one grid row per 512 tokens
+constexpr int64_t kProjOutO = 64;
+bool tokens_ok(int64_t T) { return T >= 1 && T <= kMaxTokens; }
+size_t ws_proj_out_db_offset(int64_t T) {
+  return pad256(static_cast<size_t>(adaln::proj_out_chunks(T) * kProjOutO * kD * 4));
+}
+size_t ws_proj_out(int64_t T) {
+  return ws_proj_out_db_offset(T) + pad256(static_cast<size_t>(adaln::proj_out_chunks(T) * kProjOutO * 8));
+}
 size_t ws_proj_bwd_f32(int64_t B) {
   return pad256(static_cast<size_t>(B * kD * 4));   // SiLU activations (fp32 storage)
 }
@@ -231,6 +240,8 @@ size_t adaln_workspace_bytes(int op, int64_t B, int64_t S, int64_t H) {
     case ADALN_OP_BWD: return (H == kD && seq_ok(S)) ? ws_norm_bwd(B, S) + ws_proj_bwd(B) : 0;
     case ADALN_OP_BWD_F32: return (H == kD && seq_ok(S)) ? ws_norm_bwd(B, S) + ws_proj_bwd_f32(B) : 0;
     case ADALN_OP_RESIDUAL_BWD: return (H == kD && seq_ok(S)) ? ws_pairs(B, S, 3 * kD) : 0;
+    case ADALN_OP_PROJ_OUT_BWD:
+      return (H == kD && seq_ok(S) && tokens_ok(B * S)) ? ws_proj_out(B * S) : 0;
     case ADALN_OP_TOKEN_TREE_SUM:
       return (seq_ok(S) && H >= 1 && H <= (int64_t{1} << 24)) ? ws_tree(B, S, H) : 0;
     default: return 0;
@@ -600,6 +611,46 @@ int adaln_residual_bwd(const adaln_bf16* g_out, const adaln_bf16* g_h, const ada
           adaln::launch_residual_bwd(g_out, g_h, x, h, mean, rstd, mod, d_residual, dx, part, B, S, s, e0, e1)))
     return rc;
   return launched(adaln::launch_tree_fold(part, d_mod, B, ceil_div(S, kTile), 3 * kD, s));
+}
+
+int adaln_proj_out_fwd(const adaln_bf16* out, const adaln_bf16* W, const adaln_bf16* bias, adaln_bf16* latent,
+                       int64_t T, int64_t K, int64_t O, void* stream) {
+  if (!out || !W || !bias || !latent) return ADALN_ERR_NULL;
+  if (!tokens_ok(T) || K != kD || O != kProjOutO) return ADALN_ERR_SHAPE;
+  if (!aligned16(out) || !aligned16(W) || !aligned16(bias) || !aligned16(latent)) return ADALN_ERR_ALIGN;
+  if (int rc = check_overlap({{latent, static_cast<size_t>(T * kProjOutO * 2)}},
+                             {{out, static_cast<size_t>(T * kD * 2)}, {W, static_cast<size_t>(kProjOutO * kD * 2)},
+                              {bias, static_cast<size_t>(kProjOutO * 2)}}))
+    return rc;
+  if (int rc = check_device()) return rc;
+  (void)hipGetLastError();
+  return launched(adaln::launch_proj_out_fwd(out, W, bias, latent, T, as_stream(stream)));
+}
+
+int adaln_proj_out_bwd(const adaln_bf16* d_lat, const adaln_bf16* out, const adaln_bf16* W, adaln_bf16* d_out,
+                       adaln_bf16* dW, adaln_bf16* db, void* ws, size_t ws_bytes, int64_t T, int64_t K, int64_t O,
+                       void* stream) {
+  if (!d_lat || !out || !W || !d_out || !dW || !db || !ws) return ADALN_ERR_NULL;
+  if (!tokens_ok(T) || K != kD || O != kProjOutO) return ADALN_ERR_SHAPE;
+  if (!aligned16(d_lat) || !aligned16(out) || !aligned16(W) || !aligned16(d_out) || !aligned16(dW) ||
+      !aligned16(db) || !aligned16(ws))
+    return ADALN_ERR_ALIGN;
+  const size_t need = ws_proj_out(T);
+  if (ws_bytes < need) return ADALN_ERR_WORKSPACE;
+  if (int rc = check_overlap(
+          {{d_out, static_cast<size_t>(T * kD * 2)}, {dW, static_cast<size_t>(kProjOutO * kD * 2)},
+           {db, static_cast<size_t>(kProjOutO * 2)}, {ws, need}},
+          {{d_lat, static_cast<size_t>(T * kProjOutO * 2)}, {out, static_cast<size_t>(T * kD * 2)},
+           {W, static_cast<size_t>(kProjOutO * kD * 2)}}))
+    return rc;
+  if (int rc = check_device()) return rc;
+  (void)hipGetLastError();
+  float* part = static_cast<float*>(ws);
+  double* part_db = reinterpret_cast<double*>(static_cast<unsigned char*>(ws) + ws_proj_out_db_offset(T));
+  hipEvent_t e0, e1;
+  timing_events(&e0, &e1);
+  return launched(adaln::launch_proj_out_bwd(d_lat, out, W, d_out, dW, db, part, part_db, T, as_stream(stream), e0,
+                                             e1));
 }
 
 int adaln_selftest(void) {

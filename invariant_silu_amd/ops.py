@@ -212,6 +212,36 @@ def residual_bwd(g_out: torch.Tensor, g_h: torch.Tensor, x: torch.Tensor, h: tor
     return d_residual, dx, d_mod
 
 
+def proj_out_fwd(out: torch.Tensor, W: torch.Tensor, bias: torch.Tensor) -> torch.Tensor:
+    """proj_out (adaln_proj_out_fwd): latent [..., 64] bf16 = bf16(out W^T + b) per
+    token; out [..., 3072], W [64, 3072], bias [64], all bf16."""
+    for t, n in ((out, "out"), (W, "W"), (bias, "bias")):
+        _check(t, torch.bfloat16, n)
+    out, W, bias = aligned(out), aligned(W), aligned(bias)
+    T = out.numel() // out.shape[-1]
+    latent = torch.empty(out.shape[:-1] + (W.shape[0],), dtype=torch.bfloat16, device=out.device)
+    _lib.call("adaln_proj_out_fwd", out.data_ptr(), W.data_ptr(), bias.data_ptr(), latent.data_ptr(), T,
+              out.shape[-1], W.shape[0], _stream(out.device))
+    return latent
+
+
+def proj_out_bwd(d_lat: torch.Tensor, out: torch.Tensor, W: torch.Tensor):
+    """Backward of proj_out (adaln_proj_out_bwd): (d_out bf16 like out, dW bf16
+    [64, 3072], db bf16 [64])."""
+    for t, n in ((d_lat, "d_lat"), (out, "out"), (W, "W")):
+        _check(t, torch.bfloat16, n)
+    d_lat, out, W = aligned(d_lat), aligned(out), aligned(W)
+    T = out.numel() // out.shape[-1]
+    d_out = torch.empty_like(out)
+    dW = torch.empty_like(W)
+    db = torch.empty((W.shape[0],), dtype=torch.bfloat16, device=W.device)
+    B, S = (out.shape[0], out.shape[1]) if out.dim() == 3 else (1, T)   # the workspace depends on T = B * S
+    ws = _ws(_lib.OP_PROJ_OUT_BWD, B, S, out.shape[-1], out.device)
+    _lib.call("adaln_proj_out_bwd", d_lat.data_ptr(), out.data_ptr(), W.data_ptr(), d_out.data_ptr(), dW.data_ptr(),
+              db.data_ptr(), ws.data_ptr(), ws.numel(), T, out.shape[-1], W.shape[0], _stream(out.device))
+    return d_out, dW, db
+
+
 def selftest() -> int:
     return int(_lib.load().adaln_selftest())
 

@@ -59,22 +59,30 @@ def proj_out_forward(inp: dict, mode: str = "fp32", want_abs: bool = False) -> d
     return res
 
 
-def proj_out_backward(inp: dict, mode: str = "fp32", want_abs: bool = False) -> dict:
+def proj_out_backward(inp: dict, mode: str = "fp32", want_abs: bool = False,
+                      outputs=("d_out", "dW", "db")) -> dict:
     """``inp``: d_lat [T, O] (or [B, S, O]) bf16 bits, plus the forward's out and W.
-    Returns d_out [T, K], dW [O, K], db [O] (``*_bits``; A_* with ``want_abs``)."""
+    Returns the requested ``outputs`` among d_out [T, K], dW [O, K], db [O]
+    (``*_bits``; A_* with ``want_abs``)."""
     ar = Arith(mode)
     x = ar.c(_tokens(_val(inp, "out")))
     W = ar.c(_val(inp, "W"))
     d = ar.c(_tokens(_val(inp, "d_lat")))
     T, K = x.shape
     O = W.shape[0]
-    r1 = ar.sum((t for o in range(O) for t in ar.prod(d[:, o:o + 1], W[o][None, :])), (T, K), want_abs)
-    r2 = ar.sum((t for i in range(T) for t in ar.prod(d[i][:, None], x[i][None, :])), (O, K), want_abs)
-    r3 = ar.sum((d[i] for i in range(T)), (O,), want_abs)
-    (d_out, A1), (dW, A2), (db, A3) = (r if want_abs else (r, None) for r in (r1, r2, r3))
-    res = dict(d_out=ar.store(d_out), dW=ar.store(dW), db=ar.store(db))
-    if mode != "exact":
-        res.update({k + "_bits": _bits(res[k]) for k in ("d_out", "dW", "db")})
-    if want_abs:
-        res.update(A_d_out=A1, A_dW=A2, A_db=A3)
+    sums = {
+        "d_out": lambda: ar.sum((t for o in range(O) for t in ar.prod(d[:, o:o + 1], W[o][None, :])), (T, K),
+                                want_abs),
+        "dW": lambda: ar.sum((t for i in range(T) for t in ar.prod(d[i][:, None], x[i][None, :])), (O, K), want_abs),
+        "db": lambda: ar.sum((d[i] for i in range(T)), (O,), want_abs),
+    }
+    res = {}
+    for k in outputs:
+        r = sums[k]()
+        v, A = r if want_abs else (r, None)
+        res[k] = ar.store(v)
+        if mode != "exact":
+            res[k + "_bits"] = _bits(res[k])
+        if want_abs:
+            res["A_" + k] = A
     return res

@@ -127,6 +127,19 @@ def make_mod6_inputs(B: int, seed: int = 0, K: int = HIDDEN, d_sigma: float = 8.
             "d_emb": d_emb, "B": B, "K": K, "N": 6 * K, "seed": seed}
 
 
+def make_proj_out_inputs(T: int, seed: int = 0, K: int = HIDDEN, O: int = 64) -> dict:
+    """One batch for proj_out (K -> O per token): out [T, K], W [O, K], bias [O],
+    d_lat [T, O], all bf16 bits.  Draw order out, W, bias, d_lat; standard
+    normals scaled by 1 (out: a modulated LayerNorm output), 0.02, 0.01 and 1."""
+    rng = np.random.default_rng(seed)
+    out = rng.standard_normal((T, K), dtype=np.float32)
+    W = rng.standard_normal((O, K), dtype=np.float32) * np.float32(0.02)
+    bias = rng.standard_normal(O, dtype=np.float32) * np.float32(0.01)
+    d_lat = rng.standard_normal((T, O), dtype=np.float32)
+    return {"out": f32_to_bf16_bits(out), "W": f32_to_bf16_bits(W), "bias": f32_to_bf16_bits(bias),
+            "d_lat": f32_to_bf16_bits(d_lat), "T": T, "seed": seed}
+
+
 def make_workload(name: str, seed: int = 0, io: str = "bf16") -> dict:
     w = WORKLOADS[name]
     return make_inputs(w["B"], w["S"], seed=seed, outlier_frac=w["outlier_frac"], io=io)

@@ -1,0 +1,122 @@
+"""proj_out (3072 -> 64 per token) on the GPU through adaln_proj_out_fwd /
+adaln_proj_out_bwd: parity with oracle/proj_out.py, per-token invariance and
+zero-gradient padding of dWp, dbp.
+
+Gates (tests/compare.py, bf16_accum_gate): every bf16 output within 1 ulp of
+the fp32 oracle, else within 1 ulp of its fp64 twin, else within the fp32
+accumulation bound ulp(e) + kappa 2^-24 A of the exact sum e.  The matrix
+cores accumulate in fp32 (the reading: an fp32-accumulating GEMM whose order
+the pages do not fix), so where a sum cancels the result can sit several bf16
+ulps from the correctly rounded one; the oracle, compensated, lands on it.
+kappa counts the fp32 roundings along the longest path: latent 96 chained
+instructions, d_out 2, dWp 16 per chunk, each + 8 for the adds inside an
+instruction and the final rounding; dbp sums in fp64.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import proj_out as po
+from synthetic_inputs import make_proj_out_inputs
+from tests.compare import bf16_accum_gate
+from tests.gpu_helpers import bf16_bits, same_bytes, to_dev
+
+pytestmark = pytest.mark.gpu
+
+K, O = 3072, 64
+KAPPA = {"latent": 104, "d_out": 10, "dW": 26, "db": 2}
+
+
+KEYS = ("out", "W", "bias", "d_lat")
+
+
+def _inputs(T, seed):
+    inp = make_proj_out_inputs(T, seed)
+    return {k: inp[k] for k in KEYS}
+
+
+def _run(d):
+    from invariant_silu_amd import ops
+    latent = ops.proj_out_fwd(d["out"], d["W"], d["bias"])
+    d_out, dW, db = ops.proj_out_bwd(d["d_lat"], d["out"], d["W"])
+    return dict(latent=latent, d_out=d_out, dW=dW, db=db)
+
+
+@pytest.mark.parametrize("T", [1, 37, 600])
+def test_proj_out_parity(gpu_lib, T):
+    print(f"[proj_out] parity T={T}", flush=True)
+    inp = _inputs(T, seed=100 + T)
+    gpu = _run({k: to_dev(v) for k, v in inp.items()})
+    torch.cuda.synchronize()
+    f, f6, fe = (po.proj_out_forward(inp, m, want_abs=(m == "fp32")) for m in ("fp32", "fp64", "exact"))
+    b, b6, be = (po.proj_out_backward(inp, m, want_abs=(m == "fp32")) for m in ("fp32", "fp64", "exact"))
+    for k, o, t, e in (("latent", f, f6, fe), ("d_out", b, b6, be), ("dW", b, b6, be), ("db", b, b6, be)):
+        r = bf16_accum_gate(bf16_bits(gpu[k]), o[k + "_bits"], t[k + "_bits"], e[k], o["A_" + k], KAPPA[k])
+        print(f"  {k}: {r}")
+        assert r["n_fail"] == 0, k
+
+
+def test_proj_out_large_sampled(gpu_lib):
+    """T = 4096 (one 1024 x 1024 image stream): latent and d_out of sampled tokens
+    (each token on its own in the oracle), dWp and dbp in full."""
+    T = 4096
+    print(f"[proj_out] T={T} sampled", flush=True)
+    inp = _inputs(T, seed=111)
+    gpu = _run({k: to_dev(v) for k, v in inp.items()})
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 15, 16, 63, 64, 511, 512, 2047, 4031, 4094, 4095])
+    sub = dict(inp, out=inp["out"][rows], d_lat=inp["d_lat"][rows])
+    f, f6, fe = (po.proj_out_forward(sub, m, want_abs=(m == "fp32")) for m in ("fp32", "fp64", "exact"))
+    bs, bs6, bse = (po.proj_out_backward(sub, m, want_abs=(m == "fp32"), outputs=("d_out",))
+                    for m in ("fp32", "fp64", "exact"))
+    for k, got, o, t, e in (("latent", gpu["latent"][rows], f, f6, fe), ("d_out", gpu["d_out"][rows], bs, bs6, bse)):
+        r = bf16_accum_gate(bf16_bits(got), o[k + "_bits"], t[k + "_bits"], e[k], o["A_" + k], KAPPA[k])
+        print(f"  {k} (sampled): {r}")
+        assert r["n_fail"] == 0, k
+    b, b6, be = (po.proj_out_backward(inp, m, want_abs=(m == "fp32"), outputs=("dW", "db"))
+                 for m in ("fp32", "fp64", "exact"))
+    for k in ("dW", "db"):
+        r = bf16_accum_gate(bf16_bits(gpu[k]), b[k + "_bits"], b6[k + "_bits"], be[k], b["A_" + k], KAPPA[k])
+        print(f"  {k}: {r}")
+        assert r["n_fail"] == 0, k
+
+
+def test_proj_out_token_invariance(gpu_lib):
+    """latent and d_out of a token are the same bytes alone, in a ragged run and
+    at any offset of a long run."""
+    print("[proj_out] token invariance", flush=True)
+    d = {k: to_dev(v) for k, v in _inputs(1000, seed=120).items()}
+    full = _run(d)
+    for lo, hi in ((0, 1), (5, 6), (999, 1000), (17, 50), (300, 1000)):
+        part = _run(dict(d, out=d["out"][lo:hi].contiguous(), d_lat=d["d_lat"][lo:hi].contiguous()))
+        for k in ("latent", "d_out"):
+            assert same_bytes(full[k][lo:hi], part[k]), (lo, hi, k)
+
+
+def test_proj_out_param_grads_zero_padding(gpu_lib):
+    """dWp and dbp of 600 tokens equal those of 1100 tokens whose last 500 have
+    d_lat = 0, byte for byte (the last chunk grows, a zero chunk is added)."""
+    print("[proj_out] zero padding", flush=True)
+    d = {k: to_dev(v) for k, v in _inputs(1100, seed=121).items()}
+    base = _run(dict(d, out=d["out"][:600].contiguous(), d_lat=d["d_lat"][:600].contiguous()))
+    padded = dict(d, d_lat=d["d_lat"].clone())
+    padded["d_lat"][600:] = 0
+    r = _run(padded)
+    assert same_bytes(r["dW"], base["dW"]) and same_bytes(r["db"], base["db"])
+
+
+def test_proj_out_shapes_through_ops(gpu_lib):
+    """[B, S, 3072] tensors: the wrapper flattens tokens; rows equal the flat call."""
+    print("[proj_out] batched shapes", flush=True)
+    d = {k: to_dev(v) for k, v in _inputs(2 * 300, seed=122).items()}
+    from invariant_silu_amd import ops
+    x3 = d["out"].view(2, 300, K)
+    lat3 = ops.proj_out_fwd(x3, d["W"], d["bias"])
+    d3, dW3, db3 = ops.proj_out_bwd(d["d_lat"].view(2, 300, O), x3, d["W"])
+    flat = _run(d)
+    assert lat3.shape == (2, 300, O) and same_bytes(lat3.reshape(600, O), flat["latent"])
+    assert same_bytes(d3.reshape(600, K), flat["d_out"])
+    assert same_bytes(dW3, flat["dW"]) and same_bytes(db3, flat["db"])
