@@ -233,6 +233,7 @@ def main() -> int:
     elif mod6_site:
         ws_bw = lib.workspace_bytes(lib.OP_PROJ_BWD, B, 1, D)
     elif po_site:
+        ws_fw = lib.workspace_bytes(lib.OP_PROJ_OUT_FWD, B, S, D)
         ws_bw = lib.workspace_bytes(lib.OP_PROJ_OUT_BWD, B, S, D)
     else:
         ws_bw = lib.workspace_bytes(lib.OP_BWD_F32 if f32 else lib.OP_BWD, B, S, D)
@@ -255,6 +256,7 @@ def main() -> int:
                 d_out=torch.empty((B * S, D), dtype=sdt, device=dev),
                 dW=torch.empty((PO, D), dtype=sdt, device=dev),
                 db=torch.empty((PO,), dtype=sdt, device=dev),
+                ws_fw=torch.empty(ws_fw, dtype=torch.uint8, device=dev),
                 ws_bw=torch.empty(ws_bw, dtype=torch.uint8, device=dev),
             )
             return s
@@ -314,7 +316,7 @@ def main() -> int:
         p = lambda k: s[k].data_ptr()   # noqa: E731
         if po_site:
             T = B * S
-            lib.check(fwd_name, fwd_fn(p("out"), p("W"), p("bias"), p("latent"), T, D, PO, st))
+            lib.check(fwd_name, fwd_fn(p("out"), p("W"), p("bias"), p("latent"), p("ws_fw"), ws_fw, T, D, PO, st))
             lib.check(bwd_name, bwd_fn(p("d_lat"), p("out"), p("W"), p("d_out"), p("dW"), p("db"), p("ws_bw"), ws_bw,
                                        T, D, PO, st))
             return

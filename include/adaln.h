@@ -49,7 +49,7 @@ extern "C" {
 
 typedef uint16_t adaln_bf16;
 
-#define ADALN_ABI_VERSION 5
+#define ADALN_ABI_VERSION 6
 
 enum adaln_status {
   ADALN_OK = 0,
@@ -70,7 +70,8 @@ enum adaln_op {
   ADALN_OP_BWD = 5,
   ADALN_OP_BWD_F32 = 6,
   ADALN_OP_RESIDUAL_BWD = 7,
-  ADALN_OP_PROJ_OUT_BWD = 8
+  ADALN_OP_PROJ_OUT_BWD = 8,
+  ADALN_OP_PROJ_OUT_FWD = 9
 };
 
 /* Workspace bytes an entry point needs (0 for an unknown op or bad sizes).
@@ -86,6 +87,8 @@ enum adaln_op {
  *   PROJ_OUT_BWD:   H = K (3072), T = B * S tokens (T <= 65535 * 512).
  *                   C * 64 * K * 4 bytes (dWp partials) + C * 64 * 8 (dbp
  *                   partials), C = ceil(T / 512).
+ *   PROJ_OUT_FWD:   H = K (3072), T = B * S tokens.  4 * T * 64 * 4 bytes (the
+ *                   K quarters' partial sums).
  * Each region is padded to 256 bytes. */
 size_t adaln_workspace_bytes(int op, int64_t B, int64_t S, int64_t H);
 
@@ -251,20 +254,22 @@ int adaln_residual_bwd(const adaln_bf16* g_out, const adaln_bf16* g_h, const ada
  * on its own (T = B * S of the modulation, 1 <= T <= 65535 * 512), K = 3072,
  * O = 64.
  * adaln_proj_out_fwd: out [T, K] bf16 (in), W [O, K] bf16 (in), bias [O] bf16
- *   (in), latent [T, O] bf16 (out) = bf16(fp32(sum_k out_tk W_ok) + bias_o).
+ *   (in), latent [T, O] bf16 (out) = bf16(fp32(sum_k out_tk W_ok) + bias_o);
+ *   ws: adaln_workspace_bytes(ADALN_OP_PROJ_OUT_FWD, 1, T, K) bytes.
  * adaln_proj_out_bwd: d_lat [T, O] bf16 (in), out, W as above (in); d_out
  *   [T, K] bf16 (out) = bf16(sum_o d_lat_to W_ok), dW [O, K] bf16 (out) =
  *   bf16(sum_t d_lat_to out_tk), db [O] bf16 (out) = bf16(sum_t d_lat_to);
  *   ws: adaln_workspace_bytes(ADALN_OP_PROJ_OUT_BWD, 1, T, K) bytes.
  * Products run on the bf16 matrix cores (exact products, fp32 accumulation):
- * latent and d_out are one fixed chain per output, the same for a token
- * wherever it sits, so per-token outputs do not depend on T; dW and db sum
+ * latent is four fixed chains per output (one per quarter of K) added as
+ * ((q0 + q1) + (q2 + q3)) + bias, d_out one chain per output, the same for a
+ * token wherever it sits, so per-token outputs do not depend on T; dW and db sum
  * fixed 512-token chunks, then the chunks in ascending order in fp64, so
  * trailing tokens with d_lat = 0 leave them unchanged.  Results agree with the
  * exact sums to within the fp32 accumulation (within 1 bf16 ulp of the
  * correctly rounded result in all but near-tie cases). */
 int adaln_proj_out_fwd(const adaln_bf16* out, const adaln_bf16* W, const adaln_bf16* bias, adaln_bf16* latent,
-                       int64_t T, int64_t K, int64_t O, void* stream);
+                       void* ws, size_t ws_bytes, int64_t T, int64_t K, int64_t O, void* stream);
 int adaln_proj_out_bwd(const adaln_bf16* d_lat, const adaln_bf16* out, const adaln_bf16* W, adaln_bf16* d_out,
                        adaln_bf16* dW, adaln_bf16* db, void* ws, size_t ws_bytes, int64_t T, int64_t K, int64_t O,
                        void* stream);

@@ -129,6 +129,7 @@ bool tokens_ok(int64_t T) { return T >= 1 && T <= kMaxTokens; }
 size_t ws_proj_out_db_offset(int64_t T) {
   return pad256(static_cast<size_t>(adaln::proj_out_chunks(T) * kProjOutO * kD * 4));
 }
+size_t ws_proj_out_fwd(int64_t T) { return pad256(static_cast<size_t>(4 * T * kProjOutO * 4)); }
 size_t ws_proj_out(int64_t T) {
   return ws_proj_out_db_offset(T) + pad256(static_cast<size_t>(adaln::proj_out_chunks(T) * kProjOutO * 8));
 }
@@ -242,6 +243,8 @@ size_t adaln_workspace_bytes(int op, int64_t B, int64_t S, int64_t H) {
     case ADALN_OP_RESIDUAL_BWD: return (H == kD && seq_ok(S)) ? ws_pairs(B, S, 3 * kD) : 0;
     case ADALN_OP_PROJ_OUT_BWD:
       return (H == kD && seq_ok(S) && tokens_ok(B * S)) ? ws_proj_out(B * S) : 0;
+    case ADALN_OP_PROJ_OUT_FWD:
+      return (H == kD && seq_ok(S) && tokens_ok(B * S)) ? ws_proj_out_fwd(B * S) : 0;
     case ADALN_OP_TOKEN_TREE_SUM:
       return (seq_ok(S) && H >= 1 && H <= (int64_t{1} << 24)) ? ws_tree(B, S, H) : 0;
     default: return 0;
@@ -614,17 +617,20 @@ int adaln_residual_bwd(const adaln_bf16* g_out, const adaln_bf16* g_h, const ada
 }
 
 int adaln_proj_out_fwd(const adaln_bf16* out, const adaln_bf16* W, const adaln_bf16* bias, adaln_bf16* latent,
-                       int64_t T, int64_t K, int64_t O, void* stream) {
-  if (!out || !W || !bias || !latent) return ADALN_ERR_NULL;
+                       void* ws, size_t ws_bytes, int64_t T, int64_t K, int64_t O, void* stream) {
+  if (!out || !W || !bias || !latent || !ws) return ADALN_ERR_NULL;
   if (!tokens_ok(T) || K != kD || O != kProjOutO) return ADALN_ERR_SHAPE;
-  if (!aligned16(out) || !aligned16(W) || !aligned16(bias) || !aligned16(latent)) return ADALN_ERR_ALIGN;
-  if (int rc = check_overlap({{latent, static_cast<size_t>(T * kProjOutO * 2)}},
+  if (!aligned16(out) || !aligned16(W) || !aligned16(bias) || !aligned16(latent) || !aligned16(ws))
+    return ADALN_ERR_ALIGN;
+  const size_t need = ws_proj_out_fwd(T);
+  if (ws_bytes < need) return ADALN_ERR_WORKSPACE;
+  if (int rc = check_overlap({{latent, static_cast<size_t>(T * kProjOutO * 2)}, {ws, need}},
                              {{out, static_cast<size_t>(T * kD * 2)}, {W, static_cast<size_t>(kProjOutO * kD * 2)},
                               {bias, static_cast<size_t>(kProjOutO * 2)}}))
     return rc;
   if (int rc = check_device()) return rc;
   (void)hipGetLastError();
-  return launched(adaln::launch_proj_out_fwd(out, W, bias, latent, T, as_stream(stream)));
+  return launched(adaln::launch_proj_out_fwd(out, W, bias, latent, static_cast<float*>(ws), T, as_stream(stream)));
 }
 
 int adaln_proj_out_bwd(const adaln_bf16* d_lat, const adaln_bf16* out, const adaln_bf16* W, adaln_bf16* d_out,

@@ -48,11 +48,12 @@ hipError_t launch_residual_bwd(const uint16_t* g_out, const uint16_t* g_h, const
                                const float* mean, const float* rstd, const uint16_t* mod, uint16_t* d_residual,
                                uint16_t* dx, float* part, int64_t B, int64_t S, hipStream_t s,
                                hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
-// proj_out (3072 -> 64 per token); part: proj_out_chunks(T) x 64 x 3072 fp32,
+// proj_out (3072 -> 64 per token).  Forward part: 4 x T x 64 fp32 (the K
+// quarters' partial sums); backward part: proj_out_chunks(T) x 64 x 3072 fp32,
 // part_db: proj_out_chunks(T) x 64 fp64
 int64_t proj_out_chunks(int64_t T);
 hipError_t launch_proj_out_fwd(const uint16_t* out, const uint16_t* W, const uint16_t* bias, uint16_t* latent,
-                               int64_t T, hipStream_t s);
+                               float* part, int64_t T, hipStream_t s);
 hipError_t launch_proj_out_bwd(const uint16_t* d_lat, const uint16_t* out, const uint16_t* W, uint16_t* d_out,
                                uint16_t* dW, uint16_t* db, float* part, double* part_db, int64_t T, hipStream_t s,
                                hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);

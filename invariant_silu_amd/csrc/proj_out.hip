@@ -13,9 +13,9 @@
 // same instruction sequence wherever the token sits in a tile (the unit gives
 // every output position the same arithmetic), so per-token outputs do not
 // depend on the batch.  Sums:
-//   latent: two chains per output, k in [0, 1536) and [1536, 3072), each 48
-//           instructions of 32 (a lane's 8 operands: k = 64 s + 16 g + 8 h + e)
-//           from +0, then added (first half + second half) and the bias added;
+//   latent: four chains per output, one per quarter of K, each 24
+//           instructions of 32 consecutive k from +0; then ((q0 + q1) +
+//           (q2 + q3)) + bias in fp32 (a second launch) and one bf16 rounding;
 //   d_out:  one chain per output over o in 2 instructions of 32;
 //   dWp:    per fixed chunk of 512 tokens a chain over 16 instructions of 32
 //           tokens, from +0; the chunks added in fp64 in ascending order
@@ -40,9 +40,6 @@ __device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32
 }
 
 constexpr int kO = 64;                 // latent channels
-constexpr int kHalves = 2;             // forward: waves per output tile, each half of K
-constexpr int kSteps = kD / 64 / kHalves;   // 24 steps of 64 k (two instructions each) per wave
-constexpr int kAhead = 8;              // steps in flight
 constexpr int kChunk = 512;            // tokens per dWp partial
 constexpr int kRound = 64;             // tokens staged in LDS at a time
 constexpr int kLdsStride = 72;         // bf16 elements per transposed LDS row (64 + pad; 144 bytes)
@@ -62,82 +59,84 @@ __device__ __forceinline__ void interleave8(const uint4& r0, const uint4& r1, ui
 }
 
 // ---- forward ---------------------------------------------------------------
-// Block: kTT tiles of 16 tokens (t0 ..) x all 64 outputs, 8 waves: wave w owns
-// outputs 16 (w % 4) .. + 15 over the K half w / 4 (k0 = 1536 (w / 4)).  Lane
-// (r = lane % 16, g = lane / 16) feeds the A operand with out[t0 + 16 tt +
-// r][k0 + 64 s + 16 g + 8 h .. + 7] and the B operand with Wp[16 (w % 4) +
-// r][same k] for the two instructions h = 0, 1 of step s; eight steps of
-// loads are in flight (one wave per SIMD at T = 4096 hides the memory latency
-// only with many).  The second half's waves pass their sums through LDS.
-// Rows past T load row T - 1 and are never stored.
-template <int kTT>
-struct FwdStep {
-  uint4 w[2];
-  uint4 a[kTT][2];
-};
+// Partials: block = 64 tokens (t0 ..) x one quarter of K (kq: k in [768 kq,
+// 768 kq + 768)), 4 waves; wave w owns outputs 16 w .. + 15 and holds its B
+// operand, Wp[16 w + r][768 kq + 32 s + 8 g .. + 7] for the 24 steps s, in
+// registers.  The block stages its 64 x 768 slice of out in LDS once (rows
+// padded to 1552 bytes: 16 lanes reading 16 rows hit distinct banks); token
+// tile tt's A operand is out[t0 + 16 tt + r][same k].  Each partial is one
+// chain of 24 instructions from +0.  Tokens past T are staged as zeros and
+// never stored.  The quarters' partials go to part[kq][t][o].
+constexpr int kQuarters = 4;
+constexpr int kQK = kD / kQuarters;            // 768
+constexpr int kQSteps = kQK / 32;              // 24
+constexpr int kFwdTokens = 64;
+constexpr int kARow32 = (kQK * 2 + 16) / 4;    // 388 dwords per staged row
 
-template <int kTT>
-__global__ __launch_bounds__(512) void proj_out_fwd_kernel(const uint16_t* __restrict__ out,
-                                                           const uint16_t* __restrict__ W,
-                                                           const uint16_t* __restrict__ bias,
-                                                           uint16_t* __restrict__ latent, int64_t T) {
-  __shared__ f32x4_t half1[4][kTT][64];
+__global__ __launch_bounds__(256) void proj_out_fwd_part_kernel(const uint16_t* __restrict__ out,
+                                                                const uint16_t* __restrict__ W,
+                                                                float* __restrict__ part, int64_t T) {
+  __shared__ __align__(16) uint32_t as[kFwdTokens * kARow32];   // 97 KB
+  const int kq = blockIdx.y;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kFwdTokens;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  const int ot = wave % 4, kh = wave / 4;
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 16 * kTT;
-  const int k0 = kh * (kD / kHalves);
-  const uint16_t* wrow = W + static_cast<int64_t>(16 * ot + r) * kD + k0 + 16 * g;
-  const uint16_t* arow[kTT];
+  // stage: 64 rows x 96 chunks of 16 bytes, consecutive threads on consecutive chunks
+  const uint16_t* abase = out + kq * kQK;
+  constexpr int kChunksPerRow = kQK / 8;   // 96
+  constexpr int kIt = kFwdTokens * kChunksPerRow / 256;
+  uint4 av[kIt];
 #pragma unroll
-  for (int tt = 0; tt < kTT; ++tt) {
-    const int64_t t = t0 + 16 * tt + r;
-    arow[tt] = out + (t < T ? t : T - 1) * kD + k0 + 16 * g;
+  for (int it = 0; it < kIt; ++it) {
+    const int q = threadIdx.x + 256 * it;
+    const int row = q / kChunksPerRow, c = q % kChunksPerRow;
+    const int64_t t = t0 + row;
+    av[it] = t < T ? ld16(abase + t * kD + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
   }
-  FwdStep<kTT> buf[kAhead + 1];
-  auto load = [&](FwdStep<kTT>& d, int s) {
+  // all 24 loads stay in flight before the first LDS write (one block per CU:
+  // the slice's bytes in flight are what keeps HBM busy)
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) d.w[h] = ld16(wrow + 64 * s + 8 * h);
-#pragma unroll
-    for (int tt = 0; tt < kTT; ++tt)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) d.a[tt][h] = ld16(arow[tt] + 64 * s + 8 * h);
-  };
-#pragma unroll
-  for (int s = 0; s < kAhead; ++s) load(buf[s], s);
-  f32x4_t acc[kTT];
-#pragma unroll
-  for (int tt = 0; tt < kTT; ++tt) acc[tt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
-    if (s + kAhead < kSteps) load(buf[(s + kAhead) % (kAhead + 1)], s + kAhead);
-    // keeps the loads above issued here: the scheduler would otherwise sink
-    // them next to their use and leave only a few steps in flight
-    __builtin_amdgcn_sched_barrier(0);
-    const FwdStep<kTT>& cur = buf[s % (kAhead + 1)];
-#pragma unroll
-    for (int tt = 0; tt < kTT; ++tt) {
-      acc[tt] = mfma_bf16(cur.a[tt][0], cur.w[0], acc[tt]);
-      acc[tt] = mfma_bf16(cur.a[tt][1], cur.w[1], acc[tt]);
-    }
+  for (int it = 0; it < kIt; ++it) {
+    const int q = threadIdx.x + 256 * it;
+    const int row = q / kChunksPerRow, c = q % kChunksPerRow;
+    *reinterpret_cast<uint4*>(as + row * kARow32 + 4 * c) = av[it];
   }
-  if (kh == 1)
+  uint4 wv[kQSteps];
+  const uint16_t* wrow = W + static_cast<int64_t>(16 * wave + r) * kD + kq * kQK + 8 * g;
 #pragma unroll
-    for (int tt = 0; tt < kTT; ++tt) half1[ot][tt][lane] = acc[tt];
+  for (int st = 0; st < kQSteps; ++st) wv[st] = ld16(wrow + 32 * st);
   __syncthreads();
-  if (kh == 1) return;
-  // lane holds tokens t0 + 16 tt + 4 g + v, output 16 ot + r
-  const float bf = bf16_to_f32(bias[16 * ot + r]);
+  f32x4_t acc[kFwdTokens / 16];
 #pragma unroll
-  for (int tt = 0; tt < kTT; ++tt) {
-    const f32x4_t h1 = half1[ot][tt][lane];
+  for (int tt = 0; tt < kFwdTokens / 16; ++tt) {
+    acc[tt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    const uint32_t* arow = as + (16 * tt + r) * kARow32 + 4 * g;
+#pragma unroll
+    for (int st = 0; st < kQSteps; ++st)
+      acc[tt] = mfma_bf16(*reinterpret_cast<const uint4*>(arow + 16 * st), wv[st], acc[tt]);
+  }
+  // lane holds tokens t0 + 16 tt + 4 g + v, output 16 w + r
+  float* pq = part + static_cast<int64_t>(kq) * T * kO;
+#pragma unroll
+  for (int tt = 0; tt < kFwdTokens / 16; ++tt)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int64_t t = t0 + 16 * tt + 4 * g + v;
-      if (t < T) latent[t * kO + 16 * ot + r] = f32_to_bf16((acc[tt][v] + h1[v]) + bf);
+      if (t < T) pq[t * kO + 16 * wave + r] = acc[tt][v];
     }
-  }
+}
+
+// latent = bf16(((q0 + q1) + (q2 + q3)) + bias) per element, in fp32
+__global__ __launch_bounds__(256) void proj_out_fwd_combine_kernel(const float* __restrict__ part,
+                                                                   const uint16_t* __restrict__ bias,
+                                                                   uint16_t* __restrict__ latent, int64_t T) {
+  const int64_t n = T * kO;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  const float s = (part[i] + part[n + i]) + (part[2 * n + i] + part[3 * n + i]);
+  latent[i] = f32_to_bf16(s + bf16_to_f32(bias[i % kO]));
 }
 
 // ---- backward: d_out ---------------------------------------------------------
@@ -197,7 +196,7 @@ __global__ __launch_bounds__(256) void proj_out_dx_kernel(const uint16_t* __rest
       v.y = pack_bf16x2(acc[0][2], acc[0][3]);
       v.z = pack_bf16x2(acc[1][0], acc[1][1]);
       v.w = pack_bf16x2(acc[1][2], acc[1][3]);
-      *reinterpret_cast<uint4*>(orow + 32 * m) = v;
+      st16_nt(orow + 32 * m, v);
     }
   }
 }
@@ -296,10 +295,12 @@ __global__ __launch_bounds__(256) void proj_out_dw_combine_kernel(const float* _
 int64_t proj_out_chunks(int64_t T) { return (T + kChunk - 1) / kChunk; }
 
 hipError_t launch_proj_out_fwd(const uint16_t* out, const uint16_t* W, const uint16_t* bias, uint16_t* latent,
-                               int64_t T, hipStream_t s) {
-  const int64_t blocks = (T + 15) / 16;
-  hipLaunchKernelGGL(proj_out_fwd_kernel<1>, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, out, W, bias,
-                     latent, T);
+                               float* part, int64_t T, hipStream_t s) {
+  hipLaunchKernelGGL(proj_out_fwd_part_kernel, dim3(static_cast<unsigned>((T + kFwdTokens - 1) / kFwdTokens), kQuarters),
+                     dim3(256), 0, s, out, W, part, T);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  hipLaunchKernelGGL(proj_out_fwd_combine_kernel, dim3(static_cast<unsigned>((T * kO + 255) / 256)), dim3(256), 0, s,
+                     part, bias, latent, T);
   return hipGetLastError();
 }
 

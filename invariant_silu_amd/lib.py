@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libadaln.so")
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DEVICE, ERR_WORKSPACE, ERR_OVERLAP, ERR_LAUNCH = range(-1, -8, -1)
 (OP_PROJ_FWD, OP_NORM_MOD_BWD, OP_PROJ_BWD, OP_TOKEN_TREE_SUM, OP_BWD, OP_BWD_F32, OP_RESIDUAL_BWD,
- OP_PROJ_OUT_BWD) = range(1, 9)
+ OP_PROJ_OUT_BWD, OP_PROJ_OUT_FWD) = range(1, 10)
 
 EXPORTS = ("adaln_fwd", "adaln_bwd", "adaln_fwd_f32", "adaln_bwd_f32", "adaln_residual_fwd", "adaln_residual_bwd",
            "adaln_proj_out_fwd", "adaln_proj_out_bwd", "adaln_proj_fwd", "adaln_norm_mod_fwd", "adaln_norm_mod_bwd", "adaln_proj_bwd",
@@ -35,7 +35,7 @@ _SIGS = {
     "adaln_bwd": ([_P] * 13 + [_SZ, _I64, _I64, _I64, _P], ctypes.c_int),
     "adaln_residual_fwd": ([_P] * 7 + [_I64, _I64, _I64, ctypes.c_float, _P], ctypes.c_int),
     "adaln_residual_bwd": ([_P] * 11 + [_SZ, _I64, _I64, _I64, _P], ctypes.c_int),
-    "adaln_proj_out_fwd": ([_P] * 4 + [_I64, _I64, _I64, _P], ctypes.c_int),
+    "adaln_proj_out_fwd": ([_P] * 5 + [_SZ, _I64, _I64, _I64, _P], ctypes.c_int),
     "adaln_proj_out_bwd": ([_P] * 7 + [_SZ, _I64, _I64, _I64, _P], ctypes.c_int),
     "adaln_fwd_f32": ([_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_float, _P], ctypes.c_int),
     "adaln_bwd_f32": ([_P] * 13 + [_SZ, _I64, _I64, _I64, _P], ctypes.c_int),

@@ -220,8 +220,10 @@ def proj_out_fwd(out: torch.Tensor, W: torch.Tensor, bias: torch.Tensor) -> torc
     out, W, bias = aligned(out), aligned(W), aligned(bias)
     T = out.numel() // out.shape[-1]
     latent = torch.empty(out.shape[:-1] + (W.shape[0],), dtype=torch.bfloat16, device=out.device)
-    _lib.call("adaln_proj_out_fwd", out.data_ptr(), W.data_ptr(), bias.data_ptr(), latent.data_ptr(), T,
-              out.shape[-1], W.shape[0], _stream(out.device))
+    B, S = (out.shape[0], out.shape[1]) if out.dim() == 3 else (1, T)   # the workspace depends on T = B * S
+    ws = _ws(_lib.OP_PROJ_OUT_FWD, B, S, out.shape[-1], out.device)
+    _lib.call("adaln_proj_out_fwd", out.data_ptr(), W.data_ptr(), bias.data_ptr(), latent.data_ptr(), ws.data_ptr(),
+              ws.numel(), T, out.shape[-1], W.shape[0], _stream(out.device))
     return latent
 
 

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_strerror(L):
-    assert L.adaln_abi_version() == 5
+    assert L.adaln_abi_version() == 6
     for code in range(-7, 1):
         assert len(lib.strerror(code)) >= 2
 
@@ -63,6 +63,7 @@ def test_workspace_sizes(L):
         assert lib.workspace_bytes(lib.OP_RESIDUAL_BWD, B, S, 3072) == pad(B * T0 * 9216 * 8)
         C = math.ceil(B * S / 512)
         assert lib.workspace_bytes(lib.OP_PROJ_OUT_BWD, B, S, 3072) == pad(C * 64 * 3072 * 4) + pad(C * 64 * 8)
+        assert lib.workspace_bytes(lib.OP_PROJ_OUT_FWD, B, S, 3072) == pad(4 * B * S * 64 * 4)
     assert lib.workspace_bytes(lib.OP_NORM_MOD_BWD, 1, 10, 1024) == 0
     assert lib.workspace_bytes(99, 1, 10, 3072) == 0
     assert lib.workspace_bytes(lib.OP_PROJ_BWD, 0, 1, 3072) == 0
@@ -103,17 +104,19 @@ def test_validation_before_device_work(L):
     args = (p, p + (1 << 20), p + (200 << 20), p + (101 << 20), p + (300 << 20), 1 << 20, 1, 3072)
     assert L.adaln_proj_fwd(*args, 18432, None) == lib.ERR_OVERLAP
     assert L.adaln_proj_fwd(*args, 6144, None) != lib.ERR_OVERLAP
-    # proj_out: T tokens, K = 3072, O = 64; the workspace holds the dW partials
-    assert L.adaln_proj_out_fwd(None, p, p, p, 4, 3072, 64, None) == lib.ERR_NULL
+    # proj_out: T tokens, K = 3072, O = 64; the workspaces hold partial sums
+    assert L.adaln_proj_out_fwd(None, p, p, p, p, 1 << 20, 4, 3072, 64, None) == lib.ERR_NULL
     for T, K, O in ((0, 3072, 64), (65535 * 512 + 1, 3072, 64), (4, 3071, 64), (4, 3072, 32)):
-        assert L.adaln_proj_out_fwd(p, p, p, p, T, K, O, None) == lib.ERR_SHAPE
+        assert L.adaln_proj_out_fwd(p, p, p, p, p, 1 << 30, T, K, O, None) == lib.ERR_SHAPE
         assert L.adaln_proj_out_bwd(p, p, p, p, p, p, p, 1 << 30, T, K, O, None) == lib.ERR_SHAPE
-    assert L.adaln_proj_out_fwd(p + 4, p, p, p, 4, 3072, 64, None) == lib.ERR_ALIGN
+    assert L.adaln_proj_out_fwd(p + 4, p, p, p, p, 1 << 20, 4, 3072, 64, None) == lib.ERR_ALIGN
     po = [p + (k << 28) for k in range(7)]
+    assert L.adaln_proj_out_fwd(*po[:5], 4 * 1000 * 64 * 4 - 1, 1000, 3072, 64, None) == lib.ERR_WORKSPACE
     need = lib.workspace_bytes(lib.OP_PROJ_OUT_BWD, 1, 1000, 3072)
     assert L.adaln_proj_out_bwd(*po, need - 1, 1000, 3072, 64, None) == lib.ERR_WORKSPACE
     # latent overlapping out is caught before the device check
-    assert L.adaln_proj_out_fwd(p, p + (1 << 20), p + (2 << 20), p + 6144 * 3, 8, 3072, 64, None) == lib.ERR_OVERLAP
+    assert L.adaln_proj_out_fwd(p, p + (1 << 20), p + (2 << 20), p + 6144 * 3, p + (3 << 20), 1 << 20, 8, 3072, 64,
+                                None) == lib.ERR_OVERLAP
     assert L.adaln_norm_mod_fwd(p, p, p, p, p, 1, 0, 3072, 1e-6, None) == lib.ERR_SHAPE
     assert L.token_tree_sum(p, p, p, 1 << 20, 1, 1, 0, None) == lib.ERR_SHAPE
     assert L.adaln_norm_mod_fwd(p + 2, p, p, p, p, 1, 1, 3072, 1e-6, None) == lib.ERR_ALIGN
