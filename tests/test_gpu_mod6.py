@@ -95,3 +95,34 @@ def test_mod6_rows_equal_final_projection(gpu_lib):
         e6 = ops.proj_fwd(d["temb"], d["W"], d["bias"])
         e2 = ops.proj_fwd(d["temb"], d["W"][:2 * K].contiguous(), d["bias"][:2 * K].contiguous())
         assert same_bytes(e6[:, :2 * K], e2), B
+
+
+def test_mod6_large_batch_sampled(gpu_lib):
+    """B = 2048 (the pages' large conditioning batch): emb and dtemb of sampled
+    samples (each sample on its own in the oracle), dW and db on sampled rows of
+    W (a row's sums run over all 2048 samples)."""
+    B = 2048
+    print(f"[mod6] B={B} sampled", flush=True)
+    inp = make_mod6_inputs(B, seed=98)
+    gpu = _run(_dev(inp))
+    torch.cuda.synchronize()
+    samples = np.array([0, 1, 15, 16, 1023, 2032, 2047])
+    sub = dict(inp, temb=inp["temb"][samples], d_emb=inp["d_emb"][samples])
+    f, f6 = modulation.mod6_forward(sub), modulation.mod6_forward(sub, "fp64")
+    b, b6 = modulation.mod6_backward(sub, f), modulation.mod6_backward(sub, f6, "fp64")
+    for k, got, o, t in (("emb", gpu["emb"][samples], f, f6), ("dtemb", gpu["dtemb"][samples], b, b6)):
+        r = bf16_gate(bf16_bits(got), o[k + "_bits"], t[k + "_bits"])
+        print(f"  {k} (sampled samples): {r}")
+        assert r["n_fail"] == 0, k
+    rows = np.array([0, 1, 63, 64, 6143, 6144, 9000, 12287, 18367, 18431])
+    from oracle import adaln
+    W = adaln._val(inp, "W")
+    temb = adaln._val(inp, "temb")
+    ar, ar6 = adaln.Arith("fp32"), adaln.Arith("fp64")
+    # a row of dW and db depends on that row of d_emb and on a of every sample only
+    pr = adaln.proj_backward(inp["d_emb"][:, rows], adaln.silu_act(temb, ar), W[rows], temb, ar)
+    pr6 = adaln.proj_backward(inp["d_emb"][:, rows], adaln.silu_act(temb, ar6), W[rows], temb, ar6)
+    for k, got in (("dW", gpu["dW"][rows]), ("db", gpu["db"][rows])):
+        r = bf16_gate(bf16_bits(got), adaln._bits(pr[k]), adaln._bits(pr6[k]))
+        print(f"  {k} (sampled rows): {r}")
+        assert r["n_fail"] == 0, k

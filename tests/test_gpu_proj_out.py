@@ -46,7 +46,7 @@ def _run(d):
     return dict(latent=latent, d_out=d_out, dW=dW, db=db)
 
 
-@pytest.mark.parametrize("T", [1, 37, 600])
+@pytest.mark.parametrize("T", [1, 37, 511, 512, 513, 600])
 def test_proj_out_parity(gpu_lib, T):
     print(f"[proj_out] parity T={T}", flush=True)
     inp = _inputs(T, seed=100 + T)

@@ -82,3 +82,27 @@ def test_residual_zero_gradient_tokens(gpu_lib):
     r0 = _run({k: to_dev(a[k]) for k in KEYS})
     r1 = _run({k: to_dev(bigger[k]) for k in KEYS})
     assert same_bytes(r0["d_mod"], r1["d_mod"])
+
+
+def test_residual_bench_shape_full(gpu_lib):
+    """B = 1, S = 4096 (the bench's shape, its launch configuration): every
+    output against the oracle; d_shift against the CPU tree model bit for bit."""
+    print("[residual] B=1 S=4096 full", flush=True)
+    inp = make_residual_inputs(1, 4096, seed=0)
+    gpu = _run({k: to_dev(inp[k]) for k in KEYS})
+    torch.cuda.synchronize()
+    f = residual.residual_forward(inp)
+    b = residual.residual_backward(inp, f, want_abs=True)
+    f6 = residual.residual_forward(inp, "fp64")
+    b6 = residual.residual_backward(inp, f6, "fp64")
+    assert np.array_equal(bf16_bits(gpu["h"]), f["h_bits"])
+    for k, o, t in (("out", f["out_bits"], f6["out_bits"]), ("d_residual", b["dh_bits"], b6["dh_bits"]),
+                    ("dx", b["dx_bits"], b6["dx_bits"])):
+        r = bf16_gate(bf16_bits(gpu[k]), o, t)
+        print(f"  {k}: {r}")
+        assert r["n_fail"] == 0, k
+    r = f32_gate(gpu["d_mod"].cpu().numpy(), b["d_mod"], b["A_d_mod"])
+    print(f"  d_mod: {r}")
+    assert r["n_fail"] == 0
+    want = token_tree.tree_sum(bits_to_f32(inp["g_out"]))
+    assert gpu["d_mod"][:, :3072].cpu().numpy().tobytes() == want.tobytes()
