@@ -49,7 +49,7 @@ extern "C" {
 
 typedef uint16_t adaln_bf16;
 
-#define ADALN_ABI_VERSION 6
+#define ADALN_ABI_VERSION 7
 
 enum adaln_status {
   ADALN_OK = 0,
@@ -238,7 +238,9 @@ int adaln_bwd_f32(const float* gout, const float* x, const float* mean, const fl
  *   d_mod [B, 3D] fp32 (out) = (sum_S g_out | sum_S g_out * n | sum_S dh * x),
  *   each the 32-token Neumaier tree of token_tree_sum.
  *   ws: adaln_workspace_bytes(ADALN_OP_RESIDUAL_BWD, B, S, D) bytes.
- * Per-sample outputs are the same bytes whatever B. */
+ * Per-sample outputs are the same bytes whatever B.  These are adaln_site_fwd /
+ * adaln_site_bwd with the views mod, mod + D, mod + 2D (and d_mod likewise),
+ * row stride 3D. */
 int adaln_residual_fwd(const adaln_bf16* x, const adaln_bf16* residual, const adaln_bf16* mod, adaln_bf16* h,
                        adaln_bf16* out, float* mean, float* rstd, int64_t B, int64_t S, int64_t D, float eps,
                        void* stream);
@@ -246,6 +248,36 @@ int adaln_residual_bwd(const adaln_bf16* g_out, const adaln_bf16* g_h, const ada
                        const float* mean, const float* rstd, const adaln_bf16* mod, adaln_bf16* d_residual,
                        adaln_bf16* dx, float* d_mod, void* ws, size_t ws_bytes, int64_t B, int64_t S, int64_t D,
                        void* stream);
+
+/* A block's norm site with its modulation as views (pull request 108: the
+ * LayerNormScaleShift and ScaleResidualLayerNormScaleShift sites; pull request
+ * 538, "Prior art & reuse decision": scale / shift as views of the 6-way
+ * modulation temb.chunk(6)), so each site reads its chunks straight out of
+ * adaln_proj_fwd's N = 18432 output and writes its gradients into the 6-way
+ * d_emb.  shift, scale, gate: [B, D] bf16 views, row b at view + b * mod_ld;
+ * d_shift, d_scale, d_gate: [B, D] fp32 views, row stride dmod_ld.  Strides
+ * are elements, >= D and multiples of 8; every pointer 16-byte aligned.  Views
+ * of one tensor may interleave (their rows must not share bytes).
+ * adaln_site_fwd: residual == NULL: the plain site (LayerNormScaleShift), out =
+ *   bf16((LayerNorm(x) * bf16(1 + scale)) + shift), gate and h unused (may be
+ *   NULL); residual != NULL: adaln_residual_fwd's site, h written.
+ * adaln_site_bwd: g_h == NULL: the plain site's backward from g_out: dx =
+ *   bf16(rstd * ((gy - alpha) - n * beta)) with n from x, d_shift and d_scale;
+ *   h, gate, d_residual, d_gate unused (may be NULL).  g_h != NULL:
+ *   adaln_residual_bwd's outputs (h = the forward's h).
+ *   ws: adaln_workspace_bytes(ADALN_OP_RESIDUAL_BWD, B, S, D) bytes (either form).
+ * The plain site gives the same bytes as adaln_norm_mod_fwd / _bwd with emb =
+ * (scale | shift).  In a block: site 1 takes shift1, scale1 (and, fused with
+ * the previous block's residual add, that block's gate2); site 2 takes gate1,
+ * shift2, scale2. */
+int adaln_site_fwd(const adaln_bf16* x, const adaln_bf16* residual, const adaln_bf16* shift, const adaln_bf16* scale,
+                   const adaln_bf16* gate, int64_t mod_ld, adaln_bf16* h, adaln_bf16* out, float* mean, float* rstd,
+                   int64_t B, int64_t S, int64_t D, float eps, void* stream);
+int adaln_site_bwd(const adaln_bf16* g_out, const adaln_bf16* g_h, const adaln_bf16* x, const adaln_bf16* h,
+                   const float* mean, const float* rstd, const adaln_bf16* scale, const adaln_bf16* gate,
+                   int64_t mod_ld, adaln_bf16* d_residual, adaln_bf16* dx, float* d_shift, float* d_scale,
+                   float* d_gate, int64_t dmod_ld, void* ws, size_t ws_bytes, int64_t B, int64_t S, int64_t D,
+                   void* stream);
 
 /* proj_out, the 3072 -> 64 projection after the final modulation (pull
  * request 538, "What" and "Scope / Known limitations": a separate GEMM that
@@ -277,7 +309,7 @@ int adaln_proj_out_bwd(const adaln_bf16* d_lat, const adaln_bf16* out, const ada
 /* Benchmarking aid: per-launch durations of the main kernel of the backward
  * (adaln_bwd, adaln_bwd_f32 and adaln_norm_mod_bwd: the fused dx + level-0 kernel;
  * adaln_norm_mod_bwd_dx: the dx kernel; adaln_residual_bwd: the dh / dx +
- * level-0 kernel; adaln_proj_bwd with B <= 4: its one kernel;
+ * level-0 kernel, and adaln_site_bwd; adaln_proj_bwd with B <= 4: its one kernel;
  * adaln_proj_out_bwd: the d_out kernel), timed with HIP
  * events carried by the kernel dispatch itself (no extra packets).
  * A timed dispatch leaves the stream idle for a few microseconds around it, so

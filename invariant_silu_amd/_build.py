@@ -21,8 +21,8 @@ LIB_NAME = "libadaln.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "fwd.hip", "norm_bwd.hip", "proj_bwd.hip", "proj_out.hip", "token_tree.hip", "fp32.hip",
-           "selftest.hip"]
+SOURCES = ["api.cpp", "fwd.hip", "norm_bwd.hip", "site.hip", "proj_bwd.hip", "proj_out.hip", "token_tree.hip",
+           "fp32.hip", "selftest.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fno-gpu-rdc",

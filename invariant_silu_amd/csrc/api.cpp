@@ -88,6 +88,23 @@ int check_overlap(const std::vector<Range>& outs, const std::vector<Range>& ins)
   return ADALN_OK;
 }
 
+// Two [B rows x row_bytes] views with one row stride (ld_bytes): do any two
+// of their rows share a byte?  (Views of one tensor's column chunks do not.)
+bool views_overlap(const void* a, const void* b, int64_t row_bytes, int64_t ld_bytes, int64_t B) {
+  const int64_t delta = static_cast<int64_t>(reinterpret_cast<uintptr_t>(b)) -
+                        static_cast<int64_t>(reinterpret_cast<uintptr_t>(a));
+  // rows i of a and j of b overlap iff |delta + (j - i) ld| < row_bytes, |j - i| < B
+  const int64_t k0 = -delta / ld_bytes;
+  for (int64_t k = k0 - 1; k <= k0 + 1; ++k) {
+    if (k <= -B || k >= B) continue;
+    const int64_t d = delta + k * ld_bytes;
+    if (d > -row_bytes && d < row_bytes) return true;
+  }
+  return false;
+}
+// bytes a [B, D] view with row stride ld (elements of el bytes) spans
+size_t view_span(int64_t B, int64_t ld, size_t el) { return static_cast<size_t>((B - 1) * ld + kD) * el; }
+
 int check_device() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
@@ -566,22 +583,95 @@ int adaln_bwd_f32(const float* gout, const float* x, const float* mean, const fl
   return launched(adaln::launch_proj_bwd_f32(d_emb, temb, W, a, dW, db, dtemb, B, s));
 }
 
+int adaln_site_fwd(const adaln_bf16* x, const adaln_bf16* residual, const adaln_bf16* shift, const adaln_bf16* scale,
+                   const adaln_bf16* gate, int64_t mod_ld, adaln_bf16* h, adaln_bf16* out, float* mean, float* rstd,
+                   int64_t B, int64_t S, int64_t D, float eps, void* stream) {
+  const bool res = residual != nullptr;
+  if (!x || !shift || !scale || !out || !mean || !rstd || (res && (!gate || !h))) return ADALN_ERR_NULL;
+  if (!batch_ok(B) || !seq_ok(S) || D != kD || mod_ld < kD || mod_ld % 8 != 0) return ADALN_ERR_SHAPE;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return ADALN_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(shift) || !aligned16(scale) || !aligned16(out) || !aligned16(mean) ||
+      !aligned16(rstd) || (res && (!aligned16(residual) || !aligned16(gate) || !aligned16(h))))
+    return ADALN_ERR_ALIGN;
+  const size_t rows = static_cast<size_t>(B * S);
+  const size_t vspan = view_span(B, mod_ld, 2);
+  std::vector<Range> outs = {{out, rows * kD * 2}, {mean, rows * 4}, {rstd, rows * 4}};
+  std::vector<Range> ins = {{x, rows * kD * 2}, {shift, vspan}, {scale, vspan}};
+  if (res) {
+    outs.push_back({h, rows * kD * 2});
+    ins.push_back({residual, rows * kD * 2});
+    ins.push_back({gate, vspan});
+  }
+  if (int rc = check_overlap(outs, ins)) return rc;
+  if (int rc = check_device()) return rc;
+  (void)hipGetLastError();
+  const adaln::ModView mv{shift, scale, res ? gate : nullptr, mod_ld};
+  return launched(adaln::launch_site_fwd(x, residual, mv, res ? h : nullptr, out, mean, rstd, B, S, eps,
+                                         as_stream(stream)));
+}
+
 int adaln_residual_fwd(const adaln_bf16* x, const adaln_bf16* residual, const adaln_bf16* mod, adaln_bf16* h,
                        adaln_bf16* out, float* mean, float* rstd, int64_t B, int64_t S, int64_t D, float eps,
                        void* stream) {
   if (!x || !residual || !mod || !h || !out || !mean || !rstd) return ADALN_ERR_NULL;
-  if (!batch_ok(B) || !seq_ok(S) || D != kD) return ADALN_ERR_SHAPE;
-  if (!(eps >= 0.0f) || !std::isfinite(eps)) return ADALN_ERR_SHAPE;
-  if (!aligned16(x) || !aligned16(residual) || !aligned16(mod) || !aligned16(h) || !aligned16(out) ||
-      !aligned16(mean) || !aligned16(rstd))
+  if (D != kD) return ADALN_ERR_SHAPE;
+  return adaln_site_fwd(x, residual, mod, mod + kD, mod + 2 * kD, 3 * kD, h, out, mean, rstd, B, S, D, eps, stream);
+}
+
+int adaln_site_bwd(const adaln_bf16* g_out, const adaln_bf16* g_h, const adaln_bf16* x, const adaln_bf16* h,
+                   const float* mean, const float* rstd, const adaln_bf16* scale, const adaln_bf16* gate,
+                   int64_t mod_ld, adaln_bf16* d_residual, adaln_bf16* dx, float* d_shift, float* d_scale,
+                   float* d_gate, int64_t dmod_ld, void* ws, size_t ws_bytes, int64_t B, int64_t S, int64_t D,
+                   void* stream) {
+  const bool res = g_h != nullptr;
+  if (!g_out || !x || !mean || !rstd || !scale || !dx || !d_shift || !d_scale || !ws ||
+      (res && (!h || !gate || !d_residual || !d_gate)))
+    return ADALN_ERR_NULL;
+  if (!batch_ok(B) || !seq_ok(S) || D != kD || mod_ld < kD || mod_ld % 8 != 0 || dmod_ld < kD || dmod_ld % 8 != 0)
+    return ADALN_ERR_SHAPE;
+  if (!aligned16(g_out) || !aligned16(x) || !aligned16(mean) || !aligned16(rstd) || !aligned16(scale) ||
+      !aligned16(dx) || !aligned16(d_shift) || !aligned16(d_scale) || !aligned16(ws) ||
+      (res && (!aligned16(g_h) || !aligned16(h) || !aligned16(gate) || !aligned16(d_residual) || !aligned16(d_gate))))
     return ADALN_ERR_ALIGN;
+  const int64_t nseg = res ? 3 : 2;
+  const size_t need = ws_pairs(B, S, nseg * kD);
+  if (ws_bytes < need) return ADALN_ERR_WORKSPACE;
   const size_t rows = static_cast<size_t>(B * S);
-  if (int rc = check_overlap({{h, rows * kD * 2}, {out, rows * kD * 2}, {mean, rows * 4}, {rstd, rows * 4}},
-                             {{x, rows * kD * 2}, {residual, rows * kD * 2}, {mod, static_cast<size_t>(B * 3 * kD * 2)}}))
-    return rc;
+  const size_t vspan = view_span(B, mod_ld, 2), dspan = view_span(B, dmod_ld, 4);
+  std::vector<Range> outs = {{dx, rows * kD * 2}, {ws, need}};
+  std::vector<Range> ins = {{g_out, rows * kD * 2}, {x, rows * kD * 2}, {mean, rows * 4}, {rstd, rows * 4},
+                            {scale, vspan}};
+  std::vector<float*> dviews = {d_shift, d_scale};
+  if (res) {
+    outs.push_back({d_residual, rows * kD * 2});
+    ins.push_back({g_h, rows * kD * 2});
+    ins.push_back({h, rows * kD * 2});
+    ins.push_back({gate, vspan});
+    dviews.push_back(d_gate);
+  }
+  if (int rc = check_overlap(outs, ins)) return rc;
+  // the gradient views: against every dense range as spans, against each other row by row
+  for (size_t i = 0; i < dviews.size(); ++i) {
+    const Range vi{dviews[i], dspan};
+    for (const Range& r : outs)
+      if (overlaps(vi, r)) return ADALN_ERR_OVERLAP;
+    for (const Range& r : ins)
+      if (overlaps(vi, r)) return ADALN_ERR_OVERLAP;
+    for (size_t j = i + 1; j < dviews.size(); ++j)
+      if (views_overlap(dviews[i], dviews[j], kD * 4, dmod_ld * 4, B)) return ADALN_ERR_OVERLAP;
+  }
   if (int rc = check_device()) return rc;
   (void)hipGetLastError();
-  return launched(adaln::launch_residual_fwd(x, residual, mod, h, out, mean, rstd, B, S, eps, as_stream(stream)));
+  const hipStream_t s = as_stream(stream);
+  float* part = static_cast<float*>(ws);
+  hipEvent_t e0, e1;
+  timing_events(&e0, &e1);
+  const adaln::ModView mv{nullptr, scale, res ? gate : nullptr, mod_ld};
+  if (int rc = launched(adaln::launch_site_bwd(g_out, g_h, x, res ? h : x, mean, rstd, mv, res ? d_residual : nullptr,
+                                               dx, part, B, S, s, e0, e1)))
+    return rc;
+  return launched(adaln::launch_tree_fold_views(part, d_shift, d_scale, res ? d_gate : nullptr, dmod_ld, B,
+                                                ceil_div(S, kTile), nseg, s));
 }
 
 int adaln_residual_bwd(const adaln_bf16* g_out, const adaln_bf16* g_h, const adaln_bf16* x, const adaln_bf16* h,
@@ -590,30 +680,9 @@ int adaln_residual_bwd(const adaln_bf16* g_out, const adaln_bf16* g_h, const ada
                        void* stream) {
   if (!g_out || !g_h || !x || !h || !mean || !rstd || !mod || !d_residual || !dx || !d_mod || !ws)
     return ADALN_ERR_NULL;
-  if (!batch_ok(B) || !seq_ok(S) || D != kD) return ADALN_ERR_SHAPE;
-  if (!aligned16(g_out) || !aligned16(g_h) || !aligned16(x) || !aligned16(h) || !aligned16(mean) ||
-      !aligned16(rstd) || !aligned16(mod) || !aligned16(d_residual) || !aligned16(dx) || !aligned16(d_mod) ||
-      !aligned16(ws))
-    return ADALN_ERR_ALIGN;
-  const size_t need = ws_pairs(B, S, 3 * kD);
-  if (ws_bytes < need) return ADALN_ERR_WORKSPACE;
-  const size_t rows = static_cast<size_t>(B * S);
-  if (int rc = check_overlap(
-          {{d_residual, rows * kD * 2}, {dx, rows * kD * 2}, {d_mod, static_cast<size_t>(B * 3 * kD * 4)},
-           {ws, need}},
-          {{g_out, rows * kD * 2}, {g_h, rows * kD * 2}, {x, rows * kD * 2}, {h, rows * kD * 2}, {mean, rows * 4},
-           {rstd, rows * 4}, {mod, static_cast<size_t>(B * 3 * kD * 2)}}))
-    return rc;
-  if (int rc = check_device()) return rc;
-  (void)hipGetLastError();
-  const hipStream_t s = as_stream(stream);
-  float* part = static_cast<float*>(ws);
-  hipEvent_t e0, e1;
-  timing_events(&e0, &e1);
-  if (int rc = launched(
-          adaln::launch_residual_bwd(g_out, g_h, x, h, mean, rstd, mod, d_residual, dx, part, B, S, s, e0, e1)))
-    return rc;
-  return launched(adaln::launch_tree_fold(part, d_mod, B, ceil_div(S, kTile), 3 * kD, s));
+  if (D != kD) return ADALN_ERR_SHAPE;
+  return adaln_site_bwd(g_out, g_h, x, h, mean, rstd, mod + kD, mod + 2 * kD, 3 * kD, d_residual, dx, d_mod,
+                        d_mod + kD, d_mod + 2 * kD, 3 * kD, ws, ws_bytes, B, S, D, stream);
 }
 
 int adaln_proj_out_fwd(const adaln_bf16* out, const adaln_bf16* W, const adaln_bf16* bias, adaln_bf16* latent,

@@ -461,29 +461,35 @@ __global__ __launch_bounds__(kThreads) void norm_modulate_kernel(
   modulate(xv, mu, rs, m_lds, sh_lds, out + row * kD, lane);
 }
 
-// ------------------------------------------------- residual norm site ----
-// ScaleResidualLayerNormScaleShift at a block's norm site (reading of
-// miles_diffusion pull request 108, "Fused-norm rounding points"):
-//   h   = bf16(residual + bf16(gate * x))      eager bf16 multiply and add
-//   out = bf16((LayerNorm(h) * bf16(1 + scale)) + shift)
-// mod [B, 3D] = (shift | scale | gate).  One wave per row: the row's h is
-// formed in registers, stored, and goes through row_stats and modulate as the
-// final modulation's x does.
-__device__ __forceinline__ void load_mod3(const uint16_t* __restrict__ mod, int64_t b, ModRegs& r,
-                                          uint2 (&gt)[3]) {
-  const uint2* shift = reinterpret_cast<const uint2*>(mod + b * 3 * kD);
-  const uint2* scale = reinterpret_cast<const uint2*>(mod + b * 3 * kD + kD);
-  const uint2* gate = reinterpret_cast<const uint2*>(mod + b * 3 * kD + 2 * kD);
+// ----------------------------------------------------- a block's norm site ----
+// The norm sites of a block (reading of miles_diffusion pull request 108,
+// "Fused-norm rounding points"), kRes selects the form:
+//   ScaleResidualLayerNormScaleShift (kRes):
+//     h   = bf16(residual + bf16(gate * x))      eager bf16 multiply and add
+//     out = bf16((LayerNorm(h) * bf16(1 + scale)) + shift)
+//   LayerNormScaleShift: out = bf16((LayerNorm(x) * bf16(1 + scale)) + shift)
+// shift, scale, gate: rows of sample b at view + b * ld.  One wave per row: the
+// row's h is formed in registers, stored, and goes through row_stats and
+// modulate as the final modulation's x does.
+template <bool kRes>
+__device__ __forceinline__ void load_view(const ModView& mv, int64_t b, ModRegs& r, uint2 (&gt)[3]) {
+  const uint2* shift = reinterpret_cast<const uint2*>(mv.shift + b * mv.ld);
+  const uint2* scale = reinterpret_cast<const uint2*>(mv.scale + b * mv.ld);
 #pragma unroll
   for (int k = 0; k < 3; ++k) {
     r.sc[k] = scale[threadIdx.x + kThreads * k];
     r.sh[k] = shift[threadIdx.x + kThreads * k];
-    gt[k] = gate[threadIdx.x + kThreads * k];
+  }
+  if (kRes) {
+    const uint2* gate = reinterpret_cast<const uint2*>(mv.gate + b * mv.ld);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) gt[k] = gate[threadIdx.x + kThreads * k];
   }
 }
 
-__global__ __launch_bounds__(kThreads) void residual_fwd_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ residual, const uint16_t* __restrict__ mod,
+template <bool kRes>
+__global__ __launch_bounds__(kThreads) void site_fwd_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ residual, const ModView mv,
     uint16_t* __restrict__ h, uint16_t* __restrict__ out, float* __restrict__ mean, float* __restrict__ rstd,
     int64_t S, float eps) {
   __shared__ float4 m_lds[kD / 4];
@@ -496,19 +502,24 @@ __global__ __launch_bounds__(kThreads) void residual_fwd_kernel(
   const int64_t row = b * S + (s < S ? s : S - 1);
   ModRegs mr;
   uint2 gt[3];
-  load_mod3(mod, b, mr, gt);
+  load_view<kRes>(mv, b, mr, gt);
   uint4 xv[kLaneChunks], rv[kLaneChunks];
   load_row(x, row, lane, xv);
-  load_row(residual, row, lane, rv);
+  if (kRes) load_row(residual, row, lane, rv);
   store_mod(mr, m_lds, sh_lds);
+  if (kRes)
 #pragma unroll
-  for (int k = 0; k < 3; ++k)
-    gate_lds[threadIdx.x + kThreads * k] =
-        make_float4(bf_lo(gt[k].x), bf_hi(gt[k].x), bf_lo(gt[k].y), bf_hi(gt[k].y));
+    for (int k = 0; k < 3; ++k)
+      gate_lds[threadIdx.x + kThreads * k] =
+          make_float4(bf_lo(gt[k].x), bf_hi(gt[k].x), bf_lo(gt[k].y), bf_hi(gt[k].y));
   __syncthreads();
   uint4 hv[kLaneChunks];
 #pragma unroll
   for (int i = 0; i < kLaneChunks; ++i) {
+    if (!kRes) {
+      hv[i] = xv[i];
+      continue;
+    }
     const int c = lane + 64 * i;
     float xf[8], rf[8], hf[8];
     unpack8(xv[i], xf);
@@ -621,12 +632,15 @@ hipError_t launch_proj_fwd_f32(const float* temb, float* a, const float* W, cons
   return launch_mfma_from_a(a, W, bias, emb, B, s);
 }
 
-hipError_t launch_residual_fwd(const uint16_t* x, const uint16_t* residual, const uint16_t* mod, uint16_t* h,
-                               uint16_t* out, float* mean, float* rstd, int64_t B, int64_t S, float eps,
-                               hipStream_t s) {
-  const int64_t gx = (S + kWaves - 1) / kWaves;
-  hipLaunchKernelGGL(residual_fwd_kernel, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(B)), dim3(kThreads),
-                     0, s, x, residual, mod, h, out, mean, rstd, S, eps);
+hipError_t launch_site_fwd(const uint16_t* x, const uint16_t* residual, ModView mv, uint16_t* h, uint16_t* out,
+                           float* mean, float* rstd, int64_t B, int64_t S, float eps, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((S + kWaves - 1) / kWaves), static_cast<unsigned>(B));
+  if (residual)
+    hipLaunchKernelGGL(site_fwd_kernel<true>, grid, dim3(kThreads), 0, s, x, residual, mv, h, out, mean, rstd, S,
+                       eps);
+  else
+    hipLaunchKernelGGL(site_fwd_kernel<false>, grid, dim3(kThreads), 0, s, x, residual, mv, h, out, mean, rstd, S,
+                       eps);
   return hipGetLastError();
 }
 

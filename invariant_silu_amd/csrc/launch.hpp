@@ -32,6 +32,9 @@ hipError_t launch_token_level0(const float* x, float* part, int64_t B,
                                int64_t S, int64_t H, hipStream_t s);
 hipError_t launch_tree_fold(const float* part, float* out, int64_t B,
                             int64_t T0, int64_t H, hipStream_t s);
+// the same fold, roots of columns [k D, (k + 1) D) to view k (row stride ld), nseg views
+hipError_t launch_tree_fold_views(const float* part, float* d0, float* d1, float* d2, int64_t ld, int64_t B,
+                                  int64_t T0, int64_t nseg, hipStream_t s);
 int proj_bwd_fused_max_batch();
 hipError_t launch_proj_bwd_fused(const float* d_emb, const uint16_t* temb, const uint16_t* W,
                                  uint16_t* dW, uint16_t* db, uint16_t* dtemb, int64_t B, int64_t N,
@@ -40,14 +43,26 @@ hipError_t launch_proj_bwd_dw(const float* d_emb, const uint16_t* a, uint16_t* d
                               int64_t B, int64_t N, hipStream_t s);
 hipError_t launch_proj_bwd_da(const float* d_emb, const uint16_t* W, const uint16_t* temb,
                               uint16_t* dtemb, int64_t B, int64_t N, hipStream_t s);
-// residual norm site (mod = shift | scale | gate); part: pairs of 3D columns
-hipError_t launch_residual_fwd(const uint16_t* x, const uint16_t* residual, const uint16_t* mod, uint16_t* h,
-                               uint16_t* out, float* mean, float* rstd, int64_t B, int64_t S, float eps,
-                               hipStream_t s);
-hipError_t launch_residual_bwd(const uint16_t* g_out, const uint16_t* g_h, const uint16_t* x, const uint16_t* h,
-                               const float* mean, const float* rstd, const uint16_t* mod, uint16_t* d_residual,
-                               uint16_t* dx, float* part, int64_t B, int64_t S, hipStream_t s,
-                               hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+// A block's norm site.  Its modulation as three [B, D] bf16 views with one
+// row stride ld (elements, a multiple of 8); gate is used only with the
+// residual add.
+struct ModView {
+  const uint16_t* shift;
+  const uint16_t* scale;
+  const uint16_t* gate;
+  int64_t ld;
+};
+// residual != nullptr: h = bf16(residual + bf16(gate * x)) is stored and
+// normalized; else x is normalized (h unused)
+hipError_t launch_site_fwd(const uint16_t* x, const uint16_t* residual, ModView mv, uint16_t* h, uint16_t* out,
+                           float* mean, float* rstd, int64_t B, int64_t S, float eps, hipStream_t s);
+// g_h != nullptr: the residual form (d_residual, dx, pairs of 3D columns:
+// shift | scale | gate); else the plain form (dx, pairs of 2D columns: shift |
+// scale; the LayerNorm input is x, h and d_residual unused)
+hipError_t launch_site_bwd(const uint16_t* g_out, const uint16_t* g_h, const uint16_t* x, const uint16_t* h,
+                           const float* mean, const float* rstd, ModView mv, uint16_t* d_residual, uint16_t* dx,
+                           float* part, int64_t B, int64_t S, hipStream_t s, hipEvent_t ev_start = nullptr,
+                           hipEvent_t ev_stop = nullptr);
 // proj_out (3072 -> 64 per token).  Forward part: 4 x T x 64 fp32 (the K
 // quarters' partial sums); backward part: proj_out_chunks(T) x 64 x 3072 fp32,
 // part_db: proj_out_chunks(T) x 64 fp64

@@ -46,8 +46,25 @@ __global__ __launch_bounds__(256) void token_level0_kernel(const float* __restri
   part[i + kPairGroup] = c;
 }
 
+// Where the roots go: a dense [B, H] array, or up to three [B, D] views with
+// one row stride (columns [0, D) to the first, [D, 2D) to the second, ...).
+struct DenseOut {
+  float* out;
+  int64_t H;
+  __device__ __forceinline__ float* at(int64_t b, int64_t col) const { return out + b * H + col; }
+};
+struct ViewOut {
+  float* seg[3];
+  int64_t ld;
+  __device__ __forceinline__ float* at(int64_t b, int64_t col) const {
+    const int64_t k = col / kD;
+    return (k == 0 ? seg[0] : k == 1 ? seg[1] : seg[2]) + b * ld + (col - k * kD);
+  }
+};
+
+template <typename Out>
 __global__ __launch_bounds__(kFoldCols * kFoldLanes) void tree_fold_kernel(
-    const float* __restrict__ part, float* __restrict__ out, int64_t T0, int64_t H, int levels) {
+    const float* __restrict__ part, Out out, int64_t T0, int64_t H, int levels) {
   __shared__ float lds_s[kFoldLanes][kFoldCols];
   __shared__ float lds_c[kFoldLanes][kFoldCols];
   // node lane = wave index; readfirstlane tells the compiler it is uniform,
@@ -61,7 +78,7 @@ __global__ __launch_bounds__(kFoldCols * kFoldLanes) void tree_fold_kernel(
   const float* ps = part + pair_index(b, gridDim.x, T0, 0, col);
 
   if (levels == 0) {                                // one tile: s + c
-    if (q == 0 && ok) out[b * H + col] = ps[0] + ps[kPairGroup];
+    if (q == 0 && ok) *out.at(b, col) = ps[0] + ps[kPairGroup];
     return;
   }
   const int64_t T1 = (T0 + kTile - 1) / kTile;
@@ -150,7 +167,18 @@ __global__ __launch_bounds__(kFoldCols * kFoldLanes) void tree_fold_kernel(
     for (int l = 0; l < kMaxFoldLevels - 1; ++l)
       if (l == top) { root_s = rs[l]; root_c = rc[l]; }
   }
-  out[b * H + col] = root_s + root_c;
+  *out.at(b, col) = root_s + root_c;
+}
+
+template <typename Out>
+hipError_t fold(const float* part, Out out, int64_t B, int64_t T0, int64_t H, hipStream_t s) {
+  int levels = 0;
+  for (int64_t n = T0; n > 1; n = (n + kTile - 1) / kTile) ++levels;
+  if (levels > kMaxFoldLevels) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(tree_fold_kernel<Out>,
+                     dim3(static_cast<unsigned>((H + kFoldCols - 1) / kFoldCols), static_cast<unsigned>(B)),
+                     dim3(kFoldCols * kFoldLanes), 0, s, part, out, T0, H, levels);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -167,13 +195,12 @@ hipError_t launch_token_level0(const float* x, float* part, int64_t B, int64_t S
 
 hipError_t launch_tree_fold(const float* part, float* out, int64_t B, int64_t T0, int64_t H,
                             hipStream_t s) {
-  int levels = 0;
-  for (int64_t n = T0; n > 1; n = (n + kTile - 1) / kTile) ++levels;
-  if (levels > kMaxFoldLevels) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(tree_fold_kernel,
-                     dim3(static_cast<unsigned>((H + kFoldCols - 1) / kFoldCols), static_cast<unsigned>(B)),
-                     dim3(kFoldCols * kFoldLanes), 0, s, part, out, T0, H, levels);
-  return hipGetLastError();
+  return fold(part, DenseOut{out, H}, B, T0, H, s);
+}
+
+hipError_t launch_tree_fold_views(const float* part, float* d0, float* d1, float* d2, int64_t ld, int64_t B,
+                                  int64_t T0, int64_t nseg, hipStream_t s) {
+  return fold(part, ViewOut{{d0, d1, d2}, ld}, B, T0, nseg * kD, s);
 }
 
 }  // namespace adaln

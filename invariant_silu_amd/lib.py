@@ -20,6 +20,7 @@ ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DEVICE, ERR_WORKSPACE, ERR_OVERLAP, ERR_LAUN
  OP_PROJ_OUT_BWD, OP_PROJ_OUT_FWD) = range(1, 10)
 
 EXPORTS = ("adaln_fwd", "adaln_bwd", "adaln_fwd_f32", "adaln_bwd_f32", "adaln_residual_fwd", "adaln_residual_bwd",
+           "adaln_site_fwd", "adaln_site_bwd",
            "adaln_proj_out_fwd", "adaln_proj_out_bwd", "adaln_proj_fwd", "adaln_norm_mod_fwd", "adaln_norm_mod_bwd", "adaln_proj_bwd",
            "token_tree_sum", "adaln_norm_mod_bwd_dx", "adaln_norm_mod_bwd_tiles", "token_tree_fold",
            "adaln_workspace_bytes", "adaln_selftest", "adaln_strerror", "adaln_timing_begin",
@@ -36,6 +37,8 @@ _SIGS = {
     "adaln_residual_fwd": ([_P] * 7 + [_I64, _I64, _I64, ctypes.c_float, _P], ctypes.c_int),
     "adaln_residual_bwd": ([_P] * 11 + [_SZ, _I64, _I64, _I64, _P], ctypes.c_int),
     "adaln_proj_out_fwd": ([_P] * 5 + [_SZ, _I64, _I64, _I64, _P], ctypes.c_int),
+    "adaln_site_fwd": ([_P] * 5 + [_I64] + [_P] * 4 + [_I64, _I64, _I64, ctypes.c_float, _P], ctypes.c_int),
+    "adaln_site_bwd": ([_P] * 8 + [_I64] + [_P] * 5 + [_I64, _P, _SZ, _I64, _I64, _I64, _P], ctypes.c_int),
     "adaln_proj_out_bwd": ([_P] * 7 + [_SZ, _I64, _I64, _I64, _P], ctypes.c_int),
     "adaln_fwd_f32": ([_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_float, _P], ctypes.c_int),
     "adaln_bwd_f32": ([_P] * 13 + [_SZ, _I64, _I64, _I64, _P], ctypes.c_int),

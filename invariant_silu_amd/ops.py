@@ -212,6 +212,85 @@ def residual_bwd(g_out: torch.Tensor, g_h: torch.Tensor, x: torch.Tensor, h: tor
     return d_residual, dx, d_mod
 
 
+def _mod_views(views, dtype, name):
+    """Three (or two) [B, D] views sharing one row stride, 16-byte aligned rows:
+    (list of tensors, stride).  Otherwise copies them into one [B, n, D] buffer."""
+    for v, n in zip(views, name):
+        _check(v, dtype, n)
+    el = views[0].element_size()
+    ld = views[0].stride(0)
+    ok = all(v.dim() == 2 and v.stride(1) == 1 and v.stride(0) == ld and v.data_ptr() % 16 == 0 for v in views)
+    if ok and ld % 8 == 0 and (ld * el) % 16 == 0:
+        return list(views), ld
+    packed = torch.stack([v.contiguous() for v in views], dim=1)      # [B, n, D]
+    return [packed[:, i] for i in range(len(views))], packed.stride(0)
+
+
+def site_fwd(x: torch.Tensor, shift: torch.Tensor, scale: torch.Tensor, residual: torch.Tensor = None,
+             gate: torch.Tensor = None, eps: float = EPS):
+    """A block's norm site (adaln_site_fwd) with its modulation as [B, D] views,
+    e.g. chunks of the 6-way projection's output.  residual None: the plain
+    site, returns (out, mean, rstd); else the residual site h = bf16(residual +
+    bf16(gate * x)), returns (out, h, mean, rstd)."""
+    _check(x, torch.bfloat16, "x")
+    x = aligned(x)
+    res = residual is not None
+    views, ld = _mod_views([shift, scale] + ([gate] if res else []), torch.bfloat16, ("shift", "scale", "gate"))
+    B, S, Dx = x.shape
+    out = torch.empty_like(x)
+    h = torch.empty_like(x) if res else None
+    mean = torch.empty((B, S), dtype=torch.float32, device=x.device)
+    rstd = torch.empty((B, S), dtype=torch.float32, device=x.device)
+    if res:
+        _check(residual, torch.bfloat16, "residual")
+        residual = aligned(residual)
+    _lib.call("adaln_site_fwd", x.data_ptr(), residual.data_ptr() if res else None, views[0].data_ptr(),
+              views[1].data_ptr(), views[2].data_ptr() if res else None, ld, h.data_ptr() if res else None,
+              out.data_ptr(), mean.data_ptr(), rstd.data_ptr(), B, S, Dx, float(eps), _stream(x.device))
+    return (out, h, mean, rstd) if res else (out, mean, rstd)
+
+
+def site_bwd(g_out: torch.Tensor, x: torch.Tensor, mean: torch.Tensor, rstd: torch.Tensor, scale: torch.Tensor,
+             g_h: torch.Tensor = None, h: torch.Tensor = None, gate: torch.Tensor = None, d_views=None):
+    """Backward of a norm site (adaln_site_bwd).  g_h None: the plain site,
+    returns (dx, d_shift, d_scale); else the residual site, returns
+    (d_residual, dx, d_shift, d_scale, d_gate).  d_views: optional fp32 [B, D]
+    output views (d_shift, d_scale[, d_gate]) with one row stride, e.g. chunks
+    of a 6-way gradient; fresh tensors otherwise."""
+    res = g_h is not None
+    for t, n, dt in ((g_out, "g_out", torch.bfloat16), (x, "x", torch.bfloat16), (mean, "mean", torch.float32),
+                     (rstd, "rstd", torch.float32)):
+        _check(t, dt, n)
+    g_out, x, mean, rstd = (aligned(t) for t in (g_out, x, mean, rstd))
+    views, ld = _mod_views([scale] + ([gate] if res else []), torch.bfloat16, ("scale", "gate"))
+    B, S, Dx = x.shape
+    nseg = 3 if res else 2
+    if d_views is None:
+        dm = torch.empty((B, nseg, Dx), dtype=torch.float32, device=x.device)
+        d_views = [dm[:, i] for i in range(nseg)]
+    for v in d_views:
+        _check(v, torch.float32, "d_views")
+    dld = d_views[0].stride(0)
+    if not all(v.stride(0) == dld and v.stride(1) == 1 and v.data_ptr() % 16 == 0 for v in d_views):
+        raise ValueError("d_views must share one row stride and have 16-byte aligned rows")
+    dx = torch.empty_like(x)
+    d_res = None
+    if res:
+        _check(g_h, torch.bfloat16, "g_h")
+        _check(h, torch.bfloat16, "h")
+        g_h, h = aligned(g_h), aligned(h)
+        d_res = torch.empty_like(x)
+    ws = _ws(_lib.OP_RESIDUAL_BWD, B, S, Dx, x.device)
+    _lib.call("adaln_site_bwd", g_out.data_ptr(), g_h.data_ptr() if res else None, x.data_ptr(),
+              h.data_ptr() if res else None, mean.data_ptr(), rstd.data_ptr(), views[0].data_ptr(),
+              views[1].data_ptr() if res else None, ld, d_res.data_ptr() if res else None, dx.data_ptr(),
+              d_views[0].data_ptr(), d_views[1].data_ptr(), d_views[2].data_ptr() if res else None, dld,
+              ws.data_ptr(), ws.numel(), B, S, Dx, _stream(x.device))
+    if res:
+        return d_res, dx, d_views[0], d_views[1], d_views[2]
+    return dx, d_views[0], d_views[1]
+
+
 def proj_out_fwd(out: torch.Tensor, W: torch.Tensor, bias: torch.Tensor) -> torch.Tensor:
     """proj_out (adaln_proj_out_fwd): latent [..., 64] bf16 = bf16(out W^T + b) per
     token; out [..., 3072], W [64, 3072], bias [64], all bf16."""

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_strerror(L):
-    assert L.adaln_abi_version() == 6
+    assert L.adaln_abi_version() == 7
     for code in range(-7, 1):
         assert len(lib.strerror(code)) >= 2
 
@@ -149,3 +149,39 @@ def test_bf16_accumulation_gate():
     assert r["n_outside_ulp_gates"] == 1 and r["n_fail"] == 0
     far = f32_to_bf16_bits(np.array([1e-4 + 64 * 2.0 ** -24, 1.0 + 4 * bf16_ulp_at(1.0)], np.float32))
     assert bf16_accum_gate(far, o, o, e, A, kappa=20)["n_fail"] == 2
+
+
+def test_site_views_validation(L):
+    """adaln_site_fwd / _bwd: NULL rules of the two forms, view strides, and the
+    row-by-row overlap check of interleaved gradient views (chunks of one
+    6-way gradient pass; views whose rows share bytes do not)."""
+    p = 4096
+    M = 1 << 28
+    B, S, D = 4, 64, 3072
+    # forward: plain form needs no gate / h; the residual form needs both
+    assert L.adaln_site_fwd(p, None, p + M, p + 2 * M, None, 6 * D, None, p + 3 * M, p + 4 * M, p + 5 * M,
+                            B, S, D, 1e-6, None) not in (lib.ERR_NULL, lib.ERR_SHAPE, lib.ERR_ALIGN, lib.ERR_OVERLAP)
+    assert L.adaln_site_fwd(p, p + 6 * M, p + M, p + 2 * M, None, 6 * D, p + 7 * M, p + 3 * M, p + 4 * M, p + 5 * M,
+                            B, S, D, 1e-6, None) == lib.ERR_NULL
+    for ld in (D - 8, 6 * D + 4):
+        assert L.adaln_site_fwd(p, None, p + M, p + 2 * M, None, ld, None, p + 3 * M, p + 4 * M, p + 5 * M,
+                                B, S, D, 1e-6, None) == lib.ERR_SHAPE
+    # backward, residual form: gradient views into one [B, 6D] fp32 tensor
+    ws = lib.workspace_bytes(lib.OP_RESIDUAL_BWD, B, S, D)
+    dm = p + 9 * M
+
+    def bwd(d_shift, d_scale, d_gate, dld):
+        return L.adaln_site_bwd(p, p + M, p + 2 * M, p + 3 * M, p + 4 * M, p + 5 * M, p + 6 * M, p + 6 * M + 2 * D,
+                                6 * D, p + 7 * M, p + 8 * M, d_shift, d_scale, d_gate, dld, p + 10 * M, ws, B, S, D,
+                                None)
+
+    ok = bwd(dm + 4 * 3 * D, dm + 4 * 4 * D, dm + 4 * 2 * D, 6 * D)      # chunks 3, 4, 2
+    assert ok not in (lib.ERR_NULL, lib.ERR_SHAPE, lib.ERR_ALIGN, lib.ERR_OVERLAP, lib.ERR_WORKSPACE)
+    assert bwd(dm, dm + 4 * (D // 2), dm + 4 * 2 * D, 6 * D) == lib.ERR_OVERLAP   # rows share bytes
+    assert bwd(dm, dm + 4 * 6 * D, dm + 4 * 2 * D, 6 * D) == lib.ERR_OVERLAP      # row b of one = row b+1 of the other
+    assert bwd(dm, dm + 4 * D, dm + 4 * 2 * D, D) == lib.ERR_OVERLAP               # stride D: rows run into each other
+    assert bwd(dm, dm + 4 * D, None, 6 * D) == lib.ERR_NULL                        # residual form needs d_gate
+    # plain form: no g_h, h, gate, d_residual, d_gate
+    assert L.adaln_site_bwd(p, None, p + 2 * M, None, p + 4 * M, p + 5 * M, p + 6 * M, None, 6 * D, None, p + 8 * M,
+                            dm, dm + 4 * D, None, 6 * D, p + 10 * M, ws, B, S, D, None) not in (
+        lib.ERR_NULL, lib.ERR_SHAPE, lib.ERR_ALIGN, lib.ERR_OVERLAP, lib.ERR_WORKSPACE)
