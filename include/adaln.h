@@ -84,7 +84,8 @@ enum adaln_op {
  *   BWD:            H = D (3072).  NORM_MOD_BWD + PROJ_BWD, in that order.
  *   BWD_F32:        H = D (3072).  NORM_MOD_BWD + B*K*4 (fp32 activations).
  *   RESIDUAL_BWD:   H = D (3072).  B * ceil(S/32) * 3D * 8 bytes (level-0 pairs).
- *   PROJ_OUT_BWD:   H = K (3072), T = B * S tokens (T <= 65535 * 512).
+ *   PROJ_OUT_BWD:   H = K (3072), T = B * S tokens (T <= 65535 * 512; only the
+ *                   product is checked, so B = 1, S = T is fine).
  *                   C * 64 * K * 4 bytes (dWp partials) + C * 64 * 8 (dbp
  *                   partials), C = ceil(T / 512).
  *   PROJ_OUT_FWD:   H = K (3072), T = B * S tokens.  4 * T * 64 * 4 bytes (the

@@ -258,10 +258,12 @@ size_t adaln_workspace_bytes(int op, int64_t B, int64_t S, int64_t H) {
     case ADALN_OP_BWD: return (H == kD && seq_ok(S)) ? ws_norm_bwd(B, S) + ws_proj_bwd(B) : 0;
     case ADALN_OP_BWD_F32: return (H == kD && seq_ok(S)) ? ws_norm_bwd(B, S) + ws_proj_bwd_f32(B) : 0;
     case ADALN_OP_RESIDUAL_BWD: return (H == kD && seq_ok(S)) ? ws_pairs(B, S, 3 * kD) : 0;
+    // proj_out: only the token count T = B * S matters (S may exceed the
+    // modulation's sequence limit, e.g. B = 1, S = T)
     case ADALN_OP_PROJ_OUT_BWD:
-      return (H == kD && seq_ok(S) && tokens_ok(B * S)) ? ws_proj_out(B * S) : 0;
+      return (H == kD && S >= 1 && S <= kMaxTokens && tokens_ok(B * S)) ? ws_proj_out(B * S) : 0;
     case ADALN_OP_PROJ_OUT_FWD:
-      return (H == kD && seq_ok(S) && tokens_ok(B * S)) ? ws_proj_out_fwd(B * S) : 0;
+      return (H == kD && S >= 1 && S <= kMaxTokens && tokens_ok(B * S)) ? ws_proj_out_fwd(B * S) : 0;
     case ADALN_OP_TOKEN_TREE_SUM:
       return (seq_ok(S) && H >= 1 && H <= (int64_t{1} << 24)) ? ws_tree(B, S, H) : 0;
     default: return 0;

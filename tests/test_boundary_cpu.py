@@ -64,6 +64,11 @@ def test_workspace_sizes(L):
         C = math.ceil(B * S / 512)
         assert lib.workspace_bytes(lib.OP_PROJ_OUT_BWD, B, S, 3072) == pad(C * 64 * 3072 * 4) + pad(C * 64 * 8)
         assert lib.workspace_bytes(lib.OP_PROJ_OUT_FWD, B, S, 3072) == pad(4 * B * S * 64 * 4)
+    # proj_out: a flat token count beyond the modulation's sequence limit
+    T = 1 << 22
+    assert lib.workspace_bytes(lib.OP_PROJ_OUT_FWD, 1, T, 3072) == pad(4 * T * 64 * 4)
+    assert lib.workspace_bytes(lib.OP_PROJ_OUT_BWD, 1, T, 3072) == pad((T // 512) * 64 * 3072 * 4) + pad((T // 512) * 64 * 8)
+    assert lib.workspace_bytes(lib.OP_PROJ_OUT_FWD, 1, 65535 * 512 + 1, 3072) == 0
     assert lib.workspace_bytes(lib.OP_NORM_MOD_BWD, 1, 10, 1024) == 0
     assert lib.workspace_bytes(99, 1, 10, 3072) == 0
     assert lib.workspace_bytes(lib.OP_PROJ_BWD, 0, 1, 3072) == 0
