@@ -8,7 +8,8 @@
 //   gy   = g * m,  dx = rstd * ((gy - alpha) - n * beta)
 //   d_scale, d_shift, dW, db, da, dtemb: the same sums as with bf16 storage.
 //
-// Kernels here: silu_f32_kernel; norm_mod_fwd_f32_kernel (statistics and
+// Kernels here: silu_f32_kernel; proj_f32_small_kernel<NB> (the projection
+// for B = NB <= 4 on the vector units); norm_mod_fwd_f32_kernel (statistics and
 // modulation, one wave per row); norm_mod_bwd_f32_kernel (dx rows and the
 // level-0 token tiles, the same 14 blocks per 32-token tile on one XCD as
 // the bf16 kernel).  The projections run in the storage-templated matrix-core
@@ -74,6 +75,83 @@ __global__ __launch_bounds__(256) void silu_f32_kernel(const float* __restrict__
                                                        int64_t n) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < n) a[i] = silu_f32(temb[i]);
+}
+
+// Projection for B = NB <= 4, fp32 storage: the sum for one (sample, row of
+// W) is the matrix-core kernel's: 64 leaves, leaf l over k in [48 l, 48 l +
+// 48) as k = 48 l + 12 g + s (s = 0..11 outer, g = 0..3 inner), each term an
+// fp64 fused multiply-add of the fp32 operands (exact product) from +0, the
+// leaves then added pairwise in index order (wave_sum_f64); emb = fl32(sum) +
+// bias.  Lane l holds leaf l of two rows of W (48 floats each, 16-byte
+// loads); a (from silu_f32_kernel) is staged in LDS as [s][l][g] so a step
+// reads the four terms of a leaf with one conflict-free 16-byte load.  Block:
+// 4 waves x 2 rows.
+constexpr int kF32Rows = 2;
+constexpr int kF32LeafK = kD / 64;          // 48
+constexpr int kF32Steps = kF32LeafK / 4;    // 12
+
+template <int NB>
+__global__ __launch_bounds__(kThreads) void proj_f32_small_kernel(const float* __restrict__ a,
+                                                                  const float* __restrict__ W,
+                                                                  const float* __restrict__ bias,
+                                                                  float* __restrict__ emb) {
+  __shared__ float4 a_lds[NB][kF32Steps * 64];      // NB x 12 KB
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int row0 = (blockIdx.x * (kThreads / 64) + wave) * kF32Rows;
+  // W first: the long stream, in flight while a is staged
+  float4 w[kF32Rows][kF32LeafK / 4];
+#pragma unroll
+  for (int r = 0; r < kF32Rows; ++r)
+#pragma unroll
+    for (int q = 0; q < kF32LeafK / 4; ++q)
+      w[r][q] = *reinterpret_cast<const float4*>(W + static_cast<int64_t>(row0 + r) * kD + lane * kF32LeafK + 4 * q);
+  float* al = reinterpret_cast<float*>(a_lds);
+#pragma unroll
+  for (int it = 0; it < NB * kD / kThreads; ++it) {
+    const int i = threadIdx.x + kThreads * it;
+    const int bb = i / kD, k = i % kD;
+    const int l = k / kF32LeafK, rem = k % kF32LeafK;
+    al[(bb * kF32Steps * 64 + (rem % kF32Steps) * 64 + l) * 4 + rem / kF32Steps] = a[i];
+  }
+  __syncthreads();
+  const float* wf = reinterpret_cast<const float*>(w);
+  double acc[kF32Rows][NB];
+#pragma unroll
+  for (int r = 0; r < kF32Rows; ++r)
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) acc[r][bb] = 0.0;
+#pragma unroll
+  for (int st = 0; st < kF32Steps; ++st) {
+    float4 av[NB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) av[bb] = a_lds[bb][st * 64 + lane];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+      for (int r = 0; r < kF32Rows; ++r) {
+        const double wv = static_cast<double>(wf[r * kF32LeafK + 12 * g + st]);
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+          const float ag = g == 0 ? av[bb].x : g == 1 ? av[bb].y : g == 2 ? av[bb].z : av[bb].w;
+          acc[r][bb] = __builtin_fma(static_cast<double>(ag), wv, acc[r][bb]);
+        }
+      }
+    }
+    // the accumulators are materialised after every step, so the step's
+    // LDS reads and fp64 conversions stay next to their uses
+#pragma unroll
+    for (int r = 0; r < kF32Rows; ++r)
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) asm volatile("" : "+v"(acc[r][bb]));
+  }
+#pragma unroll
+  for (int r = 0; r < kF32Rows; ++r)
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      const double tot = wave_sum_f64(acc[r][bb]);
+      if (lane == r * NB + bb) emb[bb * kN + row0 + r] = static_cast<float>(tot) + bias[row0 + r];
+    }
 }
 
 // 4 rows of one sample per block (one per wave): statistics and modulation
@@ -267,6 +345,19 @@ __global__ __launch_bounds__(kThreads) void norm_mod_bwd_f32_kernel(
 }
 
 }  // namespace
+
+hipError_t launch_proj_f32_small(const float* a, const float* W, const float* bias, float* emb, int64_t B,
+                                 hipStream_t s) {
+  const dim3 grid(kN / ((kThreads / 64) * kF32Rows)), block(kThreads);
+  switch (B) {
+    case 1: hipLaunchKernelGGL(proj_f32_small_kernel<1>, grid, block, 0, s, a, W, bias, emb); break;
+    case 2: hipLaunchKernelGGL(proj_f32_small_kernel<2>, grid, block, 0, s, a, W, bias, emb); break;
+    case 3: hipLaunchKernelGGL(proj_f32_small_kernel<3>, grid, block, 0, s, a, W, bias, emb); break;
+    case 4: hipLaunchKernelGGL(proj_f32_small_kernel<4>, grid, block, 0, s, a, W, bias, emb); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_silu_f32(const float* temb, float* a, int64_t n, hipStream_t s) {
   const int64_t blocks = (n + 255) / 256;

@@ -629,6 +629,7 @@ hipError_t launch_fwd(const uint16_t* temb, const uint16_t* W, const uint16_t* b
 hipError_t launch_proj_fwd_f32(const float* temb, float* a, const float* W, const float* bias, float* emb,
                                int64_t B, hipStream_t s) {
   if (hipError_t e = launch_silu_f32(temb, a, B * kD, s); e != hipSuccess) return e;
+  if (B <= kMaxNarrowBatch) return launch_proj_f32_small(a, W, bias, emb, B, s);   // the same sums, vector units
   return launch_mfma_from_a(a, W, bias, emb, B, s);
 }
 

@@ -74,6 +74,9 @@ hipError_t launch_proj_out_bwd(const uint16_t* d_lat, const uint16_t* out, const
                                hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 // fp32 storage
 hipError_t launch_silu_f32(const float* temb, float* a, int64_t n, hipStream_t s);
+// B <= 4: the fp32-storage projection on the vector units (same bits as the matrix-core kernel)
+hipError_t launch_proj_f32_small(const float* a, const float* W, const float* bias, float* emb, int64_t B,
+                                 hipStream_t s);
 hipError_t launch_proj_fwd_f32(const float* temb, float* a, const float* W, const float* bias, float* emb,
                                int64_t B, hipStream_t s);
 hipError_t launch_norm_mod_fwd_f32(const float* x, const float* emb, float* out, float* mean, float* rstd,
