@@ -351,3 +351,22 @@ class AdaLNFinal(torch.autograd.Function):
 
 def adaln_final(x, temb, W, b, eps=EPS):
     return AdaLNFinal.apply(x, temb, W, b, eps)
+
+
+class ProjOut(torch.autograd.Function):
+    """latent = out Wp^T + bp per token (proj_out, 3072 -> 64), bf16; saves out and Wp."""
+
+    @staticmethod
+    def forward(ctx, out, Wp, bp):
+        ctx.save_for_backward(out, Wp)
+        return proj_out_fwd(out, Wp, bp)
+
+    @staticmethod
+    def backward(ctx, g):
+        out, Wp = ctx.saved_tensors
+        d_out, dW, db = proj_out_bwd(g.to(torch.bfloat16).contiguous(), out, Wp)
+        return d_out, dW, db
+
+
+def proj_out(out, Wp, bp):
+    return ProjOut.apply(out, Wp, bp)

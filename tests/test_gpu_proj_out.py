@@ -121,3 +121,30 @@ def test_proj_out_shapes_through_ops(gpu_lib):
     assert lat3.shape == (2, 300, O) and same_bytes(lat3.reshape(600, O), flat["latent"])
     assert same_bytes(d3.reshape(600, K), flat["d_out"])
     assert same_bytes(dW3, flat["dW"]) and same_bytes(db3, flat["db"])
+
+
+def test_proj_out_autograd_composes_with_final_modulation(gpu_lib):
+    """The final layer as autograd ops (adaln_final, then proj_out): the
+    gradients equal the entry points called by hand, byte for byte."""
+    print("[proj_out] autograd", flush=True)
+    from invariant_silu_amd import ops
+    from synthetic_inputs import make_inputs
+    inp = make_inputs(2, 40, seed=123)
+    d = {k: to_dev(inp[k]) for k in ("x", "temb", "W", "bias")}
+    po_in = _inputs(80, seed=124)
+    Wp, bp = to_dev(po_in["W"]), to_dev(po_in["bias"])
+    d_lat = to_dev(po_in["d_lat"]).view(2, 40, O)
+    leaves = {k: v.clone().requires_grad_(True) for k, v in d.items()}
+    Wp_l, bp_l = Wp.clone().requires_grad_(True), bp.clone().requires_grad_(True)
+    out = ops.adaln_final(leaves["x"], leaves["temb"], leaves["W"], leaves["bias"])
+    latent = ops.proj_out(out, Wp_l, bp_l)
+    latent.backward(d_lat)
+    # by hand
+    out2, emb, mean, rstd = ops.fwd(d["x"], d["temb"], d["W"], d["bias"])
+    lat2 = ops.proj_out_fwd(out2, Wp, bp)
+    d_out, dWp, dbp = ops.proj_out_bwd(d_lat, out2, Wp)
+    dx, d_emb, dW, db, dtemb = ops.bwd(d_out, d["x"], mean, rstd, emb, d["temb"], d["W"])
+    assert same_bytes(latent.detach(), lat2)
+    assert same_bytes(Wp_l.grad, dWp) and same_bytes(bp_l.grad, dbp)
+    assert same_bytes(leaves["x"].grad, dx) and same_bytes(leaves["temb"].grad, dtemb)
+    assert same_bytes(leaves["W"].grad, dW) and same_bytes(leaves["bias"].grad, db)
