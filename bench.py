@@ -147,6 +147,16 @@ def parse():
     return ap.parse_args()
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp: dict, reps: int = 8, site: str = "final") -> dict:
     """The oracle (NumPy, single-threaded element-wise loops) on the same batch."""
     from oracle import adaln, modulation, proj_out, residual
@@ -415,12 +425,16 @@ def main() -> int:
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None if (f32 or args.site != "final") else pmc_traffic(),
                      "bytes_per_launch": k_bytes, "avg_launch_ms": round(k_mean_ms, 5),
                      "timed_launches": n_timed, "timed_every": SAMPLE,
-                     "median_launch_ms": round(k_ms[len(k_ms) // 2], 5)},
+                     "median_launch_ms": round(k_ms[len(k_ms) // 2], 5),
+                     "p10_launch_ms": round(k_ms[len(k_ms) // 10], 5),
+                     "p90_launch_ms": round(k_ms[(9 * len(k_ms)) // 10], 5)},
     }
     if not args.no_cpu_baseline:
         if po_site:   # a bounded sample: the oracle on 256 of the tokens
             inp = make_proj_out_inputs(256, seed=0)
         result["cpu_baseline"] = cpu_baseline(inp, reps=1 if (mod6_site or po_site) else 8, site=args.site)
+        result["cpu_baseline"]["cpu_model"] = cpu_model()
+        result["cpu_baseline"]["host_cores_available"] = len(os.sched_getaffinity(0))
     print(json.dumps(result), flush=True)
     return 0
 
