@@ -15,7 +15,9 @@ fold) at the same B and S, bf16 storage.  --site mod6 times a block's 6-way
 modulation projection (adaln_proj_fwd and adaln_proj_bwd at N = 18432) at the
 workload's B.  --site proj_out times the 3072 -> 64 projection after the final
 modulation (adaln_proj_out_fwd and adaln_proj_out_bwd) over the workload's B * S
-tokens.
+tokens.  --site serve times the final layer's serving forward
+(adaln_fwd_proj_out: the final modulation's projection and statistics, then
+proj_out with the modulated output computed on chip) on the final workload.
 
 Inputs are resident in HBM before the timed region.  The step rotates over
 several independent copies of every buffer (parameters included), so no step
@@ -54,6 +56,7 @@ METRIC_MOD6 = "6-way modulation projection fwd+bwd samples/sec at 3072->18432 bf
 N6 = 6 * D
 PO = 64           # proj_out channels
 METRIC_PROJ_OUT = "proj_out fwd+bwd tokens/sec at 3072->64 bf16 (batch-invariant)"
+METRIC_SERVE = "final layer serving fwd (modulation + proj_out) tokens/sec at D=3072->64 bf16 (batch-invariant)"
 
 
 def algorithmic_bytes(B: int, S: int, el: int = 2) -> int:
@@ -113,6 +116,21 @@ def proj_out_dominant_kernel_bytes(T: int) -> int:
     return 2 * T * D + 2 * T * PO + 2 * PO * D
 
 
+def serve_algorithmic_bytes(B: int, S: int) -> int:
+    """Serving forward, bf16: x read once, mean and rstd written (fp32), latent
+    written; temb, W, bias, Wp, bp read, emb written."""
+    T = B * S
+    return 2 * T * D + 8 * T + 2 * T * PO + 2 * B * D + 2 * N * D + 2 * N + 2 * B * N + 2 * PO * D + 2 * PO
+
+
+def serve_dominant_kernel_bytes(B: int, S: int) -> int:
+    """The modulate-and-multiply kernel: x, mean, rstd, emb and Wp read; its
+    result counted as latent (the fp32 partials it hands to the final add are
+    this design's, not the method's)."""
+    T = B * S
+    return 2 * T * D + 8 * T + 2 * B * N + 2 * PO * D + 2 * T * PO
+
+
 def pmc_traffic():
     """HBM bytes per launch of the dominant kernel from the committed PMC record,
     or None when the kernel's sources changed since the counters were taken."""
@@ -138,9 +156,10 @@ def parse():
     ap.add_argument("--workload", default="img1024_b1_s4096")
     ap.add_argument("--storage", choices=("bf16", "fp32"), default="bf16",
                     help="tensor storage type (fp32: the fp32-storage entry points)")
-    ap.add_argument("--site", choices=("final", "residual", "mod6", "proj_out"), default="final",
+    ap.add_argument("--site", choices=("final", "residual", "mod6", "proj_out", "serve"), default="final",
                     help="final: the final modulation (norm_out); residual: a block's residual norm site; "
-                         "mod6: a block's 6-way modulation projection; proj_out: the 3072 -> 64 projection")
+                         "mod6: a block's 6-way modulation projection; proj_out: the 3072 -> 64 projection; "
+                         "serve: the final layer's serving forward (modulation + proj_out, forward only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true",
                     help="after the steps, run a plain 512 MiB device copy (PMC byte-counter calibration)")
@@ -163,7 +182,10 @@ def cpu_baseline(inp: dict, reps: int = 8, site: str = "final") -> dict:
     fwd, bwd = {"final": (adaln.forward, adaln.backward),
                 "residual": (residual.residual_forward, residual.residual_backward),
                 "mod6": (modulation.mod6_forward, modulation.mod6_backward),
-                "proj_out": (proj_out.proj_out_forward, lambda i, f: proj_out.proj_out_backward(i))}[site]
+                "proj_out": (proj_out.proj_out_forward, lambda i, f: proj_out.proj_out_backward(i)),
+                "serve": (adaln.forward,
+                          lambda i, f: proj_out.proj_out_forward(dict(out=f["out_bits"], W=i["Wp"], bias=i["bp"])))
+                }[site]
     t0 = time.perf_counter()
     for _ in range(reps):
         f = fwd(inp)
@@ -172,6 +194,11 @@ def cpu_baseline(inp: dict, reps: int = 8, site: str = "final") -> dict:
     if site == "mod6":
         return {"value": inp["B"] / dt, "unit": "samples/s", "cores": 1, "kind": "oracle",
                 "sample": f"the whole batch (B={inp['B']}), fwd+bwd, {reps} passes, {dt:.2f} s per pass"}
+    if site == "serve":
+        return {"value": inp["x"].shape[0] * inp["x"].shape[1] / dt, "unit": "tokens/s", "cores": 1,
+                "kind": "oracle",
+                "sample": f"the whole workload batch (B={inp['x'].shape[0]}, S={inp['x'].shape[1]}), forward only "
+                          f"(final modulation, then proj_out on its bf16 output), {reps} passes, {dt:.2f} s per pass"}
     if site == "proj_out":
         return {"value": inp["T"] / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
                 "sample": f"{inp['T']} of the workload's tokens, fwd+bwd, {reps} passes, {dt:.2f} s per pass"}
@@ -210,6 +237,7 @@ def main() -> int:
     residual_site = args.site == "residual"
     mod6_site = args.site == "mod6"
     po_site = args.site == "proj_out"
+    serve_site = args.site == "serve"
     if args.site != "final" and args.storage != "bf16":
         print(f"--site {args.site} runs with bf16 storage only", file=sys.stderr)
         return 2
@@ -227,6 +255,10 @@ def main() -> int:
     else:
         inp = make_workload(args.workload, seed=0, io=args.storage)
         keys = ("x", "temb", "W", "bias", "g")
+        if serve_site:
+            po = make_proj_out_inputs(1, seed=1)
+            inp = dict(inp, Wp=po["W"], bp=po["bias"])
+            keys = ("x", "temb", "W", "bias", "Wp", "bp")
     sdt = torch.float32 if f32 else torch.bfloat16
 
     def to_dev(a):
@@ -245,6 +277,9 @@ def main() -> int:
     elif po_site:
         ws_fw = lib.workspace_bytes(lib.OP_PROJ_OUT_FWD, B, S, D)
         ws_bw = lib.workspace_bytes(lib.OP_PROJ_OUT_BWD, B, S, D)
+    elif serve_site:
+        ws_fw = lib.workspace_bytes(lib.OP_FWD_PROJ_OUT, B, S, D)
+        ws_bw = 0
     else:
         ws_bw = lib.workspace_bytes(lib.OP_BWD_F32 if f32 else lib.OP_BWD, B, S, D)
 
@@ -258,6 +293,15 @@ def main() -> int:
                 dtemb=torch.empty((B, D), dtype=sdt, device=dev),
                 ws_fw=torch.empty(ws_fw, dtype=torch.uint8, device=dev),
                 ws_bw=torch.empty(ws_bw, dtype=torch.uint8, device=dev),
+            )
+            return s
+        if serve_site:
+            s.update(
+                emb=torch.empty((B, N), dtype=sdt, device=dev),
+                latent=torch.empty((B, S, PO), dtype=sdt, device=dev),
+                mean=torch.empty((B, S), dtype=torch.float32, device=dev),
+                rstd=torch.empty((B, S), dtype=torch.float32, device=dev),
+                ws_fw=torch.empty(ws_fw, dtype=torch.uint8, device=dev),
             )
             return s
         if po_site:
@@ -293,7 +337,12 @@ def main() -> int:
             )
         return s
 
-    if po_site:
+    if serve_site:
+        step_bytes = serve_algorithmic_bytes(B, S)
+        k_bytes = serve_dominant_kernel_bytes(B, S)
+        fwd_name = bwd_name = "adaln_fwd_proj_out"
+        k_name = "proj_out_fused_part_kernel (modulation into LDS, then the Wp chains)"
+    elif po_site:
         step_bytes = proj_out_algorithmic_bytes(B * S)
         k_bytes = proj_out_dominant_kernel_bytes(B * S)
         fwd_name, bwd_name = "adaln_proj_out_fwd", "adaln_proj_out_bwd"
@@ -324,6 +373,10 @@ def main() -> int:
 
     def step(s):
         p = lambda k: s[k].data_ptr()   # noqa: E731
+        if serve_site:
+            lib.check(fwd_name, fwd_fn(p("temb"), p("W"), p("bias"), p("x"), p("Wp"), p("bp"), p("emb"), p("latent"),
+                                       p("mean"), p("rstd"), p("ws_fw"), ws_fw, B, S, D, PO, 1e-6, st))
+            return
         if po_site:
             T = B * S
             lib.check(fwd_name, fwd_fn(p("out"), p("W"), p("bias"), p("latent"), p("ws_fw"), ws_fw, T, D, PO, st))
@@ -397,7 +450,7 @@ def main() -> int:
 
     result = {
         "metric": {"final": METRIC, "residual": METRIC_RESIDUAL, "mod6": METRIC_MOD6,
-                   "proj_out": METRIC_PROJ_OUT}[args.site],
+                   "proj_out": METRIC_PROJ_OUT, "serve": METRIC_SERVE}[args.site],
         "value": round(tokens_per_s, 1),
         "unit": "samples/s" if mod6_site else "tokens/s",
         "n_gpus": 1,
@@ -411,8 +464,10 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "S": None if mod6_site else S, "D": D,
                    "N": {"mod6": N6, "proj_out": PO}.get(args.site, N), "site": args.site,
-                   "storage": args.storage, "accumulate": "fp32" if po_site else "fp64",
-                   "outlier_rows": w["outlier_frac"] if args.site == "final" else 0.0,
+                   "storage": args.storage,
+                   "accumulate": {"proj_out": "fp32", "serve": "fp64 (projection), fp32 (proj_out)"}.get(
+                       args.site, "fp64"),
+                   "outlier_rows": w["outlier_frac"] if args.site in ("final", "serve") else 0.0,
                    "buffer_sets": nsets, "step_algorithmic_bytes": step_bytes,
                    "host_enqueue_ms_per_step": round((t_enq - t0) * 1e3 / args.steps, 5),
                    "step_gbps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
@@ -432,7 +487,8 @@ def main() -> int:
     if not args.no_cpu_baseline:
         if po_site:   # a bounded sample: the oracle on 256 of the tokens
             inp = make_proj_out_inputs(256, seed=0)
-        result["cpu_baseline"] = cpu_baseline(inp, reps=1 if (mod6_site or po_site) else 8, site=args.site)
+        result["cpu_baseline"] = cpu_baseline(inp, reps=1 if (mod6_site or po_site or serve_site) else 8,
+                                              site=args.site)
         result["cpu_baseline"]["cpu_model"] = cpu_model()
         result["cpu_baseline"]["host_cores_available"] = len(os.sched_getaffinity(0))
     print(json.dumps(result), flush=True)

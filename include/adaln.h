@@ -49,7 +49,7 @@ extern "C" {
 
 typedef uint16_t adaln_bf16;
 
-#define ADALN_ABI_VERSION 7
+#define ADALN_ABI_VERSION 8
 
 enum adaln_status {
   ADALN_OK = 0,
@@ -71,7 +71,8 @@ enum adaln_op {
   ADALN_OP_BWD_F32 = 6,
   ADALN_OP_RESIDUAL_BWD = 7,
   ADALN_OP_PROJ_OUT_BWD = 8,
-  ADALN_OP_PROJ_OUT_FWD = 9
+  ADALN_OP_PROJ_OUT_FWD = 9,
+  ADALN_OP_FWD_PROJ_OUT = 10
 };
 
 /* Workspace bytes an entry point needs (0 for an unknown op or bad sizes).
@@ -90,6 +91,8 @@ enum adaln_op {
  *                   partials), C = ceil(T / 512).
  *   PROJ_OUT_FWD:   H = K (3072), T = B * S tokens.  4 * T * 64 * 4 bytes (the
  *                   K quarters' partial sums).
+ *   FWD_PROJ_OUT:   H = D (3072), B and S within the modulation's limits.
+ *                   PROJ_FWD + PROJ_OUT_FWD (T = B * S), in that order.
  * Each region is padded to 256 bytes. */
 size_t adaln_workspace_bytes(int op, int64_t B, int64_t S, int64_t H);
 
@@ -307,11 +310,32 @@ int adaln_proj_out_bwd(const adaln_bf16* d_lat, const adaln_bf16* out, const ada
                        adaln_bf16* dW, adaln_bf16* db, void* ws, size_t ws_bytes, int64_t T, int64_t K, int64_t O,
                        void* stream);
 
+/* Serving forward of the final layer: the final modulation followed by
+ * proj_out (pull request 538, "What" and "Scope / Known limitations"; pull
+ * request 108, "Fused-norm rounding points": the modulated output is rounded to
+ * bf16 once, as the projection's input) without the modulated output in
+ * memory.  latent, emb, mean and rstd are bit for bit those of adaln_fwd
+ * followed by adaln_proj_out_fwd on its `out`: emb, mean and rstd come from the
+ * same kernels as adaln_fwd's, and proj_out's blocks compute their slice of
+ * out from x, mean, rstd and emb with the final modulation's expression
+ * straight into on-chip memory, then run adaln_proj_out_fwd's matrix-core
+ * chains on it.
+ *   temb [B, D], W [2D, D], bias [2D], x [B, S, D], Wp [O, D], bp [O] bf16 (in);
+ *   emb [B, 2D] bf16, latent [B, S, O] bf16, mean, rstd [B, S] fp32 (out);
+ *   D = 3072, O = 64, B and S within adaln_fwd's limits, eps >= 0 finite.
+ *   ws: adaln_workspace_bytes(ADALN_OP_FWD_PROJ_OUT, B, S, D) bytes, 16-byte
+ *   aligned, contents on entry ignored. */
+int adaln_fwd_proj_out(const adaln_bf16* temb, const adaln_bf16* W, const adaln_bf16* bias, const adaln_bf16* x,
+                       const adaln_bf16* Wp, const adaln_bf16* bp, adaln_bf16* emb, adaln_bf16* latent, float* mean,
+                       float* rstd, void* ws, size_t ws_bytes, int64_t B, int64_t S, int64_t D, int64_t O, float eps,
+                       void* stream);
+
 /* Benchmarking aid: per-launch durations of the main kernel of the backward
  * (adaln_bwd, adaln_bwd_f32 and adaln_norm_mod_bwd: the fused dx + level-0 kernel;
  * adaln_norm_mod_bwd_dx: the dx kernel; adaln_residual_bwd: the dh / dx +
  * level-0 kernel, and adaln_site_bwd; adaln_proj_bwd with B <= 4: its one kernel;
- * adaln_proj_out_bwd: the d_out kernel), timed with HIP
+ * adaln_proj_out_bwd: the d_out kernel; adaln_fwd_proj_out: the kernel that
+ * modulates and multiplies), timed with HIP
  * events carried by the kernel dispatch itself (no extra packets).
  * A timed dispatch leaves the stream idle for a few microseconds around it, so
  * timing can be sampled: adaln_timing_begin(n, stride) creates n event pairs;

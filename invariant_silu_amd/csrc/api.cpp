@@ -150,6 +150,7 @@ size_t ws_proj_out_fwd(int64_t T) { return pad256(static_cast<size_t>(4 * T * kP
 size_t ws_proj_out(int64_t T) {
   return ws_proj_out_db_offset(T) + pad256(static_cast<size_t>(adaln::proj_out_chunks(T) * kProjOutO * 8));
 }
+size_t ws_fwd_proj_out(int64_t B, int64_t S) { return ws_proj_fwd(B) + ws_proj_out_fwd(B * S); }
 size_t ws_proj_bwd_f32(int64_t B) {
   return pad256(static_cast<size_t>(B * kD * 4));   // SiLU activations (fp32 storage)
 }
@@ -264,6 +265,7 @@ size_t adaln_workspace_bytes(int op, int64_t B, int64_t S, int64_t H) {
       return (H == kD && S >= 1 && S <= kMaxTokens && tokens_ok(B * S)) ? ws_proj_out(B * S) : 0;
     case ADALN_OP_PROJ_OUT_FWD:
       return (H == kD && S >= 1 && S <= kMaxTokens && tokens_ok(B * S)) ? ws_proj_out_fwd(B * S) : 0;
+    case ADALN_OP_FWD_PROJ_OUT: return (H == kD && seq_ok(S)) ? ws_fwd_proj_out(B, S) : 0;
     case ADALN_OP_TOKEN_TREE_SUM:
       return (seq_ok(S) && H >= 1 && H <= (int64_t{1} << 24)) ? ws_tree(B, S, H) : 0;
     default: return 0;
@@ -728,6 +730,36 @@ int adaln_proj_out_bwd(const adaln_bf16* d_lat, const adaln_bf16* out, const ada
   timing_events(&e0, &e1);
   return launched(adaln::launch_proj_out_bwd(d_lat, out, W, d_out, dW, db, part, part_db, T, as_stream(stream), e0,
                                              e1));
+}
+
+int adaln_fwd_proj_out(const adaln_bf16* temb, const adaln_bf16* W, const adaln_bf16* bias, const adaln_bf16* x,
+                       const adaln_bf16* Wp, const adaln_bf16* bp, adaln_bf16* emb, adaln_bf16* latent, float* mean,
+                       float* rstd, void* ws, size_t ws_bytes, int64_t B, int64_t S, int64_t D, int64_t O, float eps,
+                       void* stream) {
+  if (!temb || !W || !bias || !x || !Wp || !bp || !emb || !latent || !mean || !rstd || !ws) return ADALN_ERR_NULL;
+  if (!batch_ok(B) || !seq_ok(S) || !tokens_ok(B * S) || D != kD || O != kProjOutO) return ADALN_ERR_SHAPE;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return ADALN_ERR_SHAPE;
+  if (!aligned16(temb) || !aligned16(W) || !aligned16(bias) || !aligned16(x) || !aligned16(Wp) || !aligned16(bp) ||
+      !aligned16(emb) || !aligned16(latent) || !aligned16(mean) || !aligned16(rstd) || !aligned16(ws))
+    return ADALN_ERR_ALIGN;
+  const size_t need = ws_fwd_proj_out(B, S);
+  if (ws_bytes < need) return ADALN_ERR_WORKSPACE;
+  const size_t rows = static_cast<size_t>(B * S);
+  if (int rc = check_overlap({{emb, static_cast<size_t>(B * kN * 2)}, {latent, rows * kProjOutO * 2},
+                              {mean, rows * 4}, {rstd, rows * 4}, {ws, need}},
+                             {{temb, static_cast<size_t>(B * kD * 2)}, {W, static_cast<size_t>(kN * kD * 2)},
+                              {bias, static_cast<size_t>(kN * 2)}, {x, rows * kD * 2},
+                              {Wp, static_cast<size_t>(kProjOutO * kD * 2)}, {bp, static_cast<size_t>(kProjOutO * 2)}}))
+    return rc;
+  if (int rc = check_device()) return rc;
+  (void)hipGetLastError();
+  const hipStream_t s = as_stream(stream);
+  uint16_t* a = static_cast<uint16_t*>(ws);
+  float* part = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + ws_proj_fwd(B));
+  if (int rc = launched(adaln::launch_fwd_stats(temb, W, bias, x, emb, mean, rstd, a, B, S, eps, s))) return rc;
+  hipEvent_t e0, e1;
+  timing_events(&e0, &e1);
+  return launched(adaln::launch_proj_out_fwd_fused(x, emb, mean, rstd, Wp, bp, latent, part, B, S, s, e0, e1));
 }
 
 int adaln_selftest(void) {

@@ -57,17 +57,24 @@ __device__ __forceinline__ void unpack4(const float4& v, float (&f)[4]) {
   f[3] = v.w;
 }
 
-// m = 1 + scale and shift of sample b into LDS (768 float4 each)
+// m = 1 + scale (and, with kShift, shift) of sample b into LDS (768 float4
+// each); all loads are issued before the first LDS write
+template <bool kShift>
 __device__ __forceinline__ void stage_mod_f32(const float* __restrict__ emb, int64_t b, float4* m_lds,
                                               float4* sh_lds) {
   const float4* scale = reinterpret_cast<const float4*>(emb + b * kN);
   const float4* shift = reinterpret_cast<const float4*>(emb + b * kN + kD);
+  float4 sc[3], sh[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    sc[k] = scale[threadIdx.x + kThreads * k];
+    if constexpr (kShift) sh[k] = shift[threadIdx.x + kThreads * k];
+  }
 #pragma unroll
   for (int k = 0; k < 3; ++k) {
     const int c = threadIdx.x + kThreads * k;
-    const float4 sc = scale[c];
-    m_lds[c] = make_float4(1.0f + sc.x, 1.0f + sc.y, 1.0f + sc.z, 1.0f + sc.w);
-    if (sh_lds != nullptr) sh_lds[c] = shift[c];
+    m_lds[c] = make_float4(1.0f + sc[k].x, 1.0f + sc[k].y, 1.0f + sc[k].z, 1.0f + sc[k].w);
+    if constexpr (kShift) sh_lds[c] = sh[k];
   }
 }
 
@@ -168,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void norm_mod_fwd_f32_kernel(
   const int64_t row = b * S + (s < S ? s : S - 1);
   float4 xv[kRowChunks];
   load_row_f32(x, row, lane, xv);
-  stage_mod_f32(emb, b, m_lds, sh_lds);
+  stage_mod_f32<true>(emb, b, m_lds, sh_lds);
   __syncthreads();
   double acc = 0.0;
 #pragma unroll
@@ -225,7 +232,7 @@ __device__ __forceinline__ void row_pass_f32(const float* __restrict__ g, const 
   float4 gv[kRowChunks], xv[kRowChunks];
   load_row_f32(g, row, lane, gv);
   load_row_f32(x, row, lane, xv);
-  stage_mod_f32(emb, b, m_lds, nullptr);
+  stage_mod_f32<false>(emb, b, m_lds, nullptr);
   __syncthreads();
   double q1 = 0.0, q2 = 0.0;
 #pragma unroll

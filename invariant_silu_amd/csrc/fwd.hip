@@ -540,6 +540,24 @@ __global__ __launch_bounds__(kThreads) void site_fwd_kernel(
   }
 }
 
+// LayerNorm statistics only (mean, rstd), one wave per row: the statistics
+// blocks of fwd_stage1_kernel as a kernel of their own
+__global__ __launch_bounds__(kThreads) void row_stats_kernel(const uint16_t* __restrict__ x,
+                                                             float* __restrict__ mean, float* __restrict__ rstd,
+                                                             int64_t rows, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  uint4 xv[kLaneChunks];
+  load_row(x, r, lane, xv);
+  float mu, rs;
+  row_stats(xv, eps, mu, rs);
+  if (lane == 0) {
+    mean[r] = mu;
+    rstd[r] = rs;
+  }
+}
+
 // B <= 4: proj_block with NB = B; larger batches: proj_mfma_kernel
 template <typename F>
 hipError_t by_batch(int64_t B, F&& f) {
@@ -624,6 +642,27 @@ hipError_t launch_fwd(const uint16_t* temb, const uint16_t* W, const uint16_t* b
   hipLaunchKernelGGL(norm_modulate_kernel, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(B)),
                      dim3(kThreads), 0, s, x, emb, mean, rstd, out, S);
   return hipGetLastError();
+}
+
+// emb, mean and rstd of the one-call forward without the modulation: B <= 4
+// fwd_stage1_kernel (the same launch as adaln_fwd's first); B > 4 the SiLU into
+// a, the matrix-core projection and row_stats_kernel
+hipError_t launch_fwd_stats(const uint16_t* temb, const uint16_t* W, const uint16_t* bias, const uint16_t* x,
+                            uint16_t* emb, float* mean, float* rstd, uint16_t* a, int64_t B, int64_t S, float eps,
+                            hipStream_t s) {
+  if (B > kMaxNarrowBatch) {
+    if (hipError_t e = launch_mfma(temb, a, W, bias, emb, B, s); e != hipSuccess) return e;
+    hipLaunchKernelGGL(row_stats_kernel, dim3(static_cast<unsigned>((B * S + kWaves - 1) / kWaves)), dim3(kThreads),
+                       0, s, x, mean, rstd, B * S, eps);
+    return hipGetLastError();
+  }
+  const int64_t stat_blocks = (B * S + kWaves - 1) / kWaves;
+  return by_batch(B, [&](auto nb) {
+    hipLaunchKernelGGL(fwd_stage1_kernel<decltype(nb)::value>,
+                       dim3(static_cast<unsigned>(kProjBlocks + stat_blocks)), dim3(kThreads), 0, s,
+                       temb, W, bias, emb, x, mean, rstd, S, eps);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_proj_fwd_f32(const float* temb, float* a, const float* W, const float* bias, float* emb,

@@ -11,6 +11,11 @@ hipError_t launch_silu(const uint16_t* temb, uint16_t* a, int64_t n, hipStream_t
 hipError_t launch_fwd(const uint16_t* temb, const uint16_t* W, const uint16_t* bias,
                       const uint16_t* x, uint16_t* emb, uint16_t* out, float* mean, float* rstd,
                       int64_t B, int64_t S, float eps, hipStream_t s);
+// the one-call forward's emb, mean, rstd without the modulation (a: B * D
+// bf16, used when B > 4)
+hipError_t launch_fwd_stats(const uint16_t* temb, const uint16_t* W, const uint16_t* bias, const uint16_t* x,
+                            uint16_t* emb, float* mean, float* rstd, uint16_t* a, int64_t B, int64_t S, float eps,
+                            hipStream_t s);
 // projections: N = kN (final modulation) or kN6 (a block's 6-way modulation)
 hipError_t launch_proj_fwd(const uint16_t* temb, const uint16_t* W, const uint16_t* bias,
                            uint16_t* emb, uint16_t* a, int64_t B, int64_t N, hipStream_t s);
@@ -67,6 +72,11 @@ hipError_t launch_site_bwd(const uint16_t* g_out, const uint16_t* g_h, const uin
 // quarters' partial sums); backward part: proj_out_chunks(T) x 64 x 3072 fp32,
 // part_db: proj_out_chunks(T) x 64 fp64
 int64_t proj_out_chunks(int64_t T);
+// latent from x with the final modulation computed on the fly (out is never
+// stored): the same bytes as launch_proj_out_fwd on the modulated output
+hipError_t launch_proj_out_fwd_fused(const uint16_t* x, const uint16_t* emb, const float* mean, const float* rstd,
+                                     const uint16_t* W, const uint16_t* bias, uint16_t* latent, float* part,
+                                     int64_t B, int64_t S, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 hipError_t launch_proj_out_fwd(const uint16_t* out, const uint16_t* W, const uint16_t* bias, uint16_t* latent,
                                float* part, int64_t T, hipStream_t s);
 hipError_t launch_proj_out_bwd(const uint16_t* d_lat, const uint16_t* out, const uint16_t* W, uint16_t* d_out,

@@ -45,6 +45,9 @@ constexpr int kRound = 64;             // tokens staged in LDS at a time
 constexpr int kLdsStride = 72;         // bf16 elements per transposed LDS row (64 + pad; 144 bytes)
 constexpr int kLdsStride2 = kLdsStride / 2;
 
+// the last valid row for t >= T (T >= 1)
+__device__ __forceinline__ int64_t clamp_row(int64_t t, int64_t T) { return t < T ? t : T - 1; }
+
 __device__ __forceinline__ uint32_t lo16(uint32_t w) { return w & 0xffffu; }
 __device__ __forceinline__ uint32_t hi16(uint32_t w) { return w >> 16; }
 
@@ -73,6 +76,19 @@ constexpr int kQSteps = kQK / 32;              // 24
 constexpr int kFwdTokens = 64;
 constexpr int kARow32 = (kQK * 2 + 16) / 4;    // 388 dwords per staged row
 
+// Zero the staged rows of tokens t >= T (the last block only), after the
+// block's own writes of those rows.
+template <int kRows>
+__device__ __forceinline__ void zero_tail_rows(uint32_t* as, int64_t t0, int64_t T) {
+  if (t0 + kRows <= T) return;
+  constexpr int kChunksPerRow = kQK / 8;
+  for (int q = threadIdx.x; q < kRows * kChunksPerRow; q += 256) {   // the staging loops' thread mapping
+    const int row = q / kChunksPerRow;
+    if (t0 + row >= T)
+      *reinterpret_cast<uint4*>(as + row * kARow32 + 4 * (q % kChunksPerRow)) = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
 __global__ __launch_bounds__(256) void proj_out_fwd_part_kernel(const uint16_t* __restrict__ out,
                                                                 const uint16_t* __restrict__ W,
                                                                 float* __restrict__ part, int64_t T) {
@@ -91,8 +107,10 @@ __global__ __launch_bounds__(256) void proj_out_fwd_part_kernel(const uint16_t* 
   for (int it = 0; it < kIt; ++it) {
     const int q = threadIdx.x + 256 * it;
     const int row = q / kChunksPerRow, c = q % kChunksPerRow;
-    const int64_t t = t0 + row;
-    av[it] = t < T ? ld16(abase + t * kD + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
+    // rows past T load row T - 1 (in bounds) and are zeroed after the LDS
+    // writes: a load under a branch, or a select on its value (which the
+    // compiler turns into one), makes it wait for every load issued before
+    av[it] = ld16(abase + clamp_row(t0 + row, T) * kD + 8 * c);
   }
   // all 24 loads stay in flight before the first LDS write (one block per CU:
   // the slice's bytes in flight are what keeps HBM busy)
@@ -103,6 +121,7 @@ __global__ __launch_bounds__(256) void proj_out_fwd_part_kernel(const uint16_t* 
     const int row = q / kChunksPerRow, c = q % kChunksPerRow;
     *reinterpret_cast<uint4*>(as + row * kARow32 + 4 * c) = av[it];
   }
+  zero_tail_rows<kFwdTokens>(as, t0, T);
   uint4 wv[kQSteps];
   const uint16_t* wrow = W + static_cast<int64_t>(16 * wave + r) * kD + kq * kQK + 8 * g;
 #pragma unroll
@@ -121,6 +140,127 @@ __global__ __launch_bounds__(256) void proj_out_fwd_part_kernel(const uint16_t* 
   float* pq = part + static_cast<int64_t>(kq) * T * kO;
 #pragma unroll
   for (int tt = 0; tt < kFwdTokens / 16; ++tt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t t = t0 + 16 * tt + 4 * g + v;
+      if (t < T) pq[t * kO + 16 * wave + r] = acc[tt][v];
+    }
+}
+
+// The same partials with the final modulation computed on the fly: the
+// block's slice of out, out[t][k] = bf16(((x - mean) * rstd) * bf16(1 + scale)
+// + shift) with t's sample's (scale | shift) from emb -- the final
+// modulation's expression, operation for operation -- goes straight into
+// LDS, so out never reaches HBM.  32 tokens per block.
+// kOneSample (S a multiple of 32: a block's tokens share one sample): the
+// sample's slice of scale and shift is staged once in LDS, which frees the
+// registers to issue Wp's quarter (from L2) ahead of x, so it has arrived by
+// the time the chains start.  Otherwise each row looks its sample up.
+constexpr int kFuseTokens = 32;
+
+template <bool kOneSample>
+__global__ __launch_bounds__(256) void proj_out_fused_part_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ emb, const float* __restrict__ mean,
+    const float* __restrict__ rstd, const uint16_t* __restrict__ W, float* __restrict__ part, int64_t T,
+    int64_t S) {
+  __shared__ __align__(16) uint32_t as[kFuseTokens * kARow32];   // 48.5 KB
+  const int kq = blockIdx.y;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kFuseTokens;
+  constexpr int kChunksPerRow = kQK / 8;                          // 96
+  constexpr int kIt = kFuseTokens * kChunksPerRow / 256;          // 12
+  const int kbase = kq * kQK;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const uint16_t* wrow = W + static_cast<int64_t>(16 * wave + r) * kD + kbase + 8 * g;
+  uint4 wv[kQSteps];
+  uint4 xv[kIt];
+  float mu[kIt], rs[kIt];
+  if constexpr (kOneSample) {
+    // the sample's scale then shift slice (bf16), in entries [0, 192); every
+    // thread loads and stores one entry (threads past 191 repeat chunk 191
+    // into spare entries): no branch around the load
+    __shared__ uint4 e_lds[256];
+    const int64_t b = static_cast<uint32_t>(t0) / static_cast<uint32_t>(S);
+    const int et = min(static_cast<int>(threadIdx.x), 2 * kChunksPerRow - 1);
+    const uint4 ev = ld16(emb + b * kN + (et < kChunksPerRow ? 0 : kD) + kbase + 8 * (et % kChunksPerRow));
+#pragma unroll
+    for (int st = 0; st < kQSteps; ++st) wv[st] = ld16(wrow + 32 * st);
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int q = threadIdx.x + 256 * it;
+      const int64_t t = clamp_row(t0 + q / kChunksPerRow, T);
+      xv[it] = ld16(x + t * kD + kbase + 8 * (q % kChunksPerRow));
+      mu[it] = mean[t];
+      rs[it] = rstd[t];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    e_lds[threadIdx.x] = ev;
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int q = threadIdx.x + 256 * it;
+      const int row = q / kChunksPerRow, c = q % kChunksPerRow;
+      float xf[8], sf[8], hf[8], o[8];
+      unpack8(xv[it], xf);
+      unpack8(e_lds[c], sf);
+      unpack8(e_lds[kChunksPerRow + c], hf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float n = (xf[e] - mu[it]) * rs[it];
+        o[e] = n * round_bf16(1.0f + sf[e]) + hf[e];
+      }
+      *reinterpret_cast<uint4*>(as + row * kARow32 + 4 * c) = pack8(o);
+    }
+    zero_tail_rows<kFuseTokens>(as, t0, T);
+  } else {
+    uint4 sc[kIt], sh[kIt];
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int q = threadIdx.x + 256 * it;
+      const int row = q / kChunksPerRow, c = q % kChunksPerRow;
+      const int64_t t = clamp_row(t0 + row, T);
+      // token index and sample fit 32 bits (T <= 65535 * 512)
+      const int64_t b = static_cast<uint32_t>(t) / static_cast<uint32_t>(S);
+      xv[it] = ld16(x + t * kD + kbase + 8 * c);
+      sc[it] = ld16(emb + b * kN + kbase + 8 * c);
+      sh[it] = ld16(emb + b * kN + kD + kbase + 8 * c);
+      mu[it] = mean[t];
+      rs[it] = rstd[t];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int q = threadIdx.x + 256 * it;
+      const int row = q / kChunksPerRow, c = q % kChunksPerRow;
+      float xf[8], sf[8], hf[8], o[8];
+      unpack8(xv[it], xf);
+      unpack8(sc[it], sf);
+      unpack8(sh[it], hf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float n = (xf[e] - mu[it]) * rs[it];
+        o[e] = n * round_bf16(1.0f + sf[e]) + hf[e];
+      }
+      *reinterpret_cast<uint4*>(as + row * kARow32 + 4 * c) = pack8(o);
+    }
+    zero_tail_rows<kFuseTokens>(as, t0, T);
+#pragma unroll
+    for (int st = 0; st < kQSteps; ++st) wv[st] = ld16(wrow + 32 * st);
+  }
+  __syncthreads();
+  f32x4_t acc[kFuseTokens / 16];
+#pragma unroll
+  for (int tt = 0; tt < kFuseTokens / 16; ++tt) {
+    acc[tt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    const uint32_t* arow = as + (16 * tt + r) * kARow32 + 4 * g;
+#pragma unroll
+    for (int st = 0; st < kQSteps; ++st)
+      acc[tt] = mfma_bf16(*reinterpret_cast<const uint4*>(arow + 16 * st), wv[st], acc[tt]);
+  }
+  float* pq = part + static_cast<int64_t>(kq) * T * kO;
+#pragma unroll
+  for (int tt = 0; tt < kFuseTokens / 16; ++tt)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int64_t t = t0 + 16 * tt + 4 * g + v;
@@ -298,6 +438,23 @@ hipError_t launch_proj_out_fwd(const uint16_t* out, const uint16_t* W, const uin
                                float* part, int64_t T, hipStream_t s) {
   hipLaunchKernelGGL(proj_out_fwd_part_kernel, dim3(static_cast<unsigned>((T + kFwdTokens - 1) / kFwdTokens), kQuarters),
                      dim3(256), 0, s, out, W, part, T);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  hipLaunchKernelGGL(proj_out_fwd_combine_kernel, dim3(static_cast<unsigned>((T * kO + 255) / 256)), dim3(256), 0, s,
+                     part, bias, latent, T);
+  return hipGetLastError();
+}
+
+hipError_t launch_proj_out_fwd_fused(const uint16_t* x, const uint16_t* emb, const float* mean, const float* rstd,
+                                     const uint16_t* W, const uint16_t* bias, uint16_t* latent, float* part,
+                                     int64_t B, int64_t S, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  const int64_t T = B * S;
+  const dim3 grid(static_cast<unsigned>((T + kFuseTokens - 1) / kFuseTokens), kQuarters);
+  // S a multiple of 32: every block's tokens belong to one sample
+  auto k = S % kFuseTokens == 0 ? proj_out_fused_part_kernel<true> : proj_out_fused_part_kernel<false>;
+  if (e0 && e1)
+    hipExtLaunchKernelGGL(k, grid, dim3(256), 0, s, e0, e1, 0, x, emb, mean, rstd, W, part, T, S);
+  else
+    hipLaunchKernelGGL(k, grid, dim3(256), 0, s, x, emb, mean, rstd, W, part, T, S);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   hipLaunchKernelGGL(proj_out_fwd_combine_kernel, dim3(static_cast<unsigned>((T * kO + 255) / 256)), dim3(256), 0, s,
                      part, bias, latent, T);

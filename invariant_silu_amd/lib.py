@@ -17,11 +17,11 @@ LIB_PATH = os.path.join(_PKG, "libadaln.so")
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DEVICE, ERR_WORKSPACE, ERR_OVERLAP, ERR_LAUNCH = range(-1, -8, -1)
 (OP_PROJ_FWD, OP_NORM_MOD_BWD, OP_PROJ_BWD, OP_TOKEN_TREE_SUM, OP_BWD, OP_BWD_F32, OP_RESIDUAL_BWD,
- OP_PROJ_OUT_BWD, OP_PROJ_OUT_FWD) = range(1, 10)
+ OP_PROJ_OUT_BWD, OP_PROJ_OUT_FWD, OP_FWD_PROJ_OUT) = range(1, 11)
 
 EXPORTS = ("adaln_fwd", "adaln_bwd", "adaln_fwd_f32", "adaln_bwd_f32", "adaln_residual_fwd", "adaln_residual_bwd",
            "adaln_site_fwd", "adaln_site_bwd",
-           "adaln_proj_out_fwd", "adaln_proj_out_bwd", "adaln_proj_fwd", "adaln_norm_mod_fwd", "adaln_norm_mod_bwd", "adaln_proj_bwd",
+           "adaln_proj_out_fwd", "adaln_proj_out_bwd", "adaln_fwd_proj_out", "adaln_proj_fwd", "adaln_norm_mod_fwd", "adaln_norm_mod_bwd", "adaln_proj_bwd",
            "token_tree_sum", "adaln_norm_mod_bwd_dx", "adaln_norm_mod_bwd_tiles", "token_tree_fold",
            "adaln_workspace_bytes", "adaln_selftest", "adaln_strerror", "adaln_timing_begin",
            "adaln_timing_end",
@@ -40,6 +40,7 @@ _SIGS = {
     "adaln_site_fwd": ([_P] * 5 + [_I64] + [_P] * 4 + [_I64, _I64, _I64, ctypes.c_float, _P], ctypes.c_int),
     "adaln_site_bwd": ([_P] * 8 + [_I64] + [_P] * 5 + [_I64, _P, _SZ, _I64, _I64, _I64, _P], ctypes.c_int),
     "adaln_proj_out_bwd": ([_P] * 7 + [_SZ, _I64, _I64, _I64, _P], ctypes.c_int),
+    "adaln_fwd_proj_out": ([_P] * 11 + [_SZ, _I64, _I64, _I64, _I64, ctypes.c_float, _P], ctypes.c_int),
     "adaln_fwd_f32": ([_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_float, _P], ctypes.c_int),
     "adaln_bwd_f32": ([_P] * 13 + [_SZ, _I64, _I64, _I64, _P], ctypes.c_int),
     "adaln_norm_mod_fwd": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_float, _P], ctypes.c_int),

@@ -306,6 +306,27 @@ def proj_out_fwd(out: torch.Tensor, W: torch.Tensor, bias: torch.Tensor) -> torc
     return latent
 
 
+def fwd_proj_out(x: torch.Tensor, temb: torch.Tensor, W: torch.Tensor, bias: torch.Tensor, Wp: torch.Tensor,
+                 bp: torch.Tensor, eps: float = EPS):
+    """Serving forward of the final layer (adaln_fwd_proj_out): the final
+    modulation then proj_out without the modulated output in memory.  Returns
+    (latent [B, S, 64], emb, mean, rstd), the same bits as fwd followed by
+    proj_out_fwd on its out.  All tensors bf16."""
+    for t, n in ((x, "x"), (temb, "temb"), (W, "W"), (bias, "bias"), (Wp, "Wp"), (bp, "bp")):
+        _check(t, torch.bfloat16, n)
+    x, temb, W, bias, Wp, bp = (aligned(t) for t in (x, temb, W, bias, Wp, bp))
+    B, S, Dx = x.shape
+    emb = torch.empty((B, N), dtype=torch.bfloat16, device=x.device)
+    latent = torch.empty((B, S, Wp.shape[0]), dtype=torch.bfloat16, device=x.device)
+    mean = torch.empty((B, S), dtype=torch.float32, device=x.device)
+    rstd = torch.empty((B, S), dtype=torch.float32, device=x.device)
+    ws = _ws(_lib.OP_FWD_PROJ_OUT, B, S, Dx, x.device)
+    _lib.call("adaln_fwd_proj_out", temb.data_ptr(), W.data_ptr(), bias.data_ptr(), x.data_ptr(), Wp.data_ptr(),
+              bp.data_ptr(), emb.data_ptr(), latent.data_ptr(), mean.data_ptr(), rstd.data_ptr(), ws.data_ptr(),
+              ws.numel(), B, S, Dx, Wp.shape[0], float(eps), _stream(x.device))
+    return latent, emb, mean, rstd
+
+
 def proj_out_bwd(d_lat: torch.Tensor, out: torch.Tensor, W: torch.Tensor):
     """Backward of proj_out (adaln_proj_out_bwd): (d_out bf16 like out, dW bf16
     [64, 3072], db bf16 [64])."""

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_strerror(L):
-    assert L.adaln_abi_version() == 7
+    assert L.adaln_abi_version() == 8
     for code in range(-7, 1):
         assert len(lib.strerror(code)) >= 2
 
@@ -64,6 +64,7 @@ def test_workspace_sizes(L):
         C = math.ceil(B * S / 512)
         assert lib.workspace_bytes(lib.OP_PROJ_OUT_BWD, B, S, 3072) == pad(C * 64 * 3072 * 4) + pad(C * 64 * 8)
         assert lib.workspace_bytes(lib.OP_PROJ_OUT_FWD, B, S, 3072) == pad(4 * B * S * 64 * 4)
+        assert lib.workspace_bytes(lib.OP_FWD_PROJ_OUT, B, S, 3072) == pad(B * 3072 * 2) + pad(4 * B * S * 64 * 4)
     # proj_out: a flat token count beyond the modulation's sequence limit
     T = 1 << 22
     assert lib.workspace_bytes(lib.OP_PROJ_OUT_FWD, 1, T, 3072) == pad(4 * T * 64 * 4)
@@ -122,6 +123,23 @@ def test_validation_before_device_work(L):
     # latent overlapping out is caught before the device check
     assert L.adaln_proj_out_fwd(p, p + (1 << 20), p + (2 << 20), p + 6144 * 3, p + (3 << 20), 1 << 20, 8, 3072, 64,
                                 None) == lib.ERR_OVERLAP
+    # serving forward of the final layer: the modulation's limits on B and S
+    fb = [p + (k << 28) for k in range(11)]
+    assert L.adaln_fwd_proj_out(*fb[:10], None, 1 << 30, 1, 64, 3072, 64, 1e-6, None) == lib.ERR_NULL
+    for B, S, D, O, eps in ((0, 4, 3072, 64, 1e-6), (1, 0, 3072, 64, 1e-6), (1, 4, 1024, 64, 1e-6),
+                            (1, 4, 3072, 32, 1e-6), (1, 4, 3072, 64, -1.0), (1, 4, 3072, 64, float("inf"))):
+        assert L.adaln_fwd_proj_out(*fb, 1 << 30, B, S, D, O, eps, None) == lib.ERR_SHAPE
+    assert lib.workspace_bytes(lib.OP_FWD_PROJ_OUT, 1, 1 << 22, 3072) == 0    # beyond the sequence limit
+    assert L.adaln_fwd_proj_out(*fb[:10], p + 8, 1 << 30, 1, 64, 3072, 64, 1e-6, None) == lib.ERR_ALIGN
+    need = lib.workspace_bytes(lib.OP_FWD_PROJ_OUT, 6, 64, 3072)
+    assert L.adaln_fwd_proj_out(*fb, need - 1, 6, 64, 3072, 64, 1e-6, None) == lib.ERR_WORKSPACE
+    # latent over x, and the workspace over mean, are refused before the device check
+    over = list(fb)
+    over[7] = fb[3] + 4096
+    assert L.adaln_fwd_proj_out(*over, need, 6, 64, 3072, 64, 1e-6, None) == lib.ERR_OVERLAP
+    over = list(fb)
+    over[10] = fb[8]
+    assert L.adaln_fwd_proj_out(*over, need, 6, 64, 3072, 64, 1e-6, None) == lib.ERR_OVERLAP
     assert L.adaln_norm_mod_fwd(p, p, p, p, p, 1, 0, 3072, 1e-6, None) == lib.ERR_SHAPE
     assert L.token_tree_sum(p, p, p, 1 << 20, 1, 1, 0, None) == lib.ERR_SHAPE
     assert L.adaln_norm_mod_fwd(p + 2, p, p, p, p, 1, 1, 3072, 1e-6, None) == lib.ERR_ALIGN
