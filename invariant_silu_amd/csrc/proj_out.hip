@@ -177,13 +177,14 @@ __global__ __launch_bounds__(256) void proj_out_fused_part_kernel(
   uint4 xv[kIt];
   float mu[kIt], rs[kIt];
   if constexpr (kOneSample) {
-    // the sample's scale then shift slice (bf16), in entries [0, 192); every
-    // thread loads and stores one entry (threads past 191 repeat chunk 191
-    // into spare entries): no branch around the load
-    __shared__ uint4 e_lds[256];
+    // the sample's bf16(1 + scale) and shift slices as fp32, 8 columns per
+    // 16-byte chunk pair: threads [0, 128) take chunk tid of scale, threads
+    // [128, 256) chunk tid - 128 of shift; chunks past 95 reload chunk 95 into
+    // spare entries (every thread loads and stores: no branch around a load)
+    __shared__ float4 m_lds[2 * 2 * 128];
     const int64_t b = static_cast<uint32_t>(t0) / static_cast<uint32_t>(S);
-    const int et = min(static_cast<int>(threadIdx.x), 2 * kChunksPerRow - 1);
-    const uint4 ev = ld16(emb + b * kN + (et < kChunksPerRow ? 0 : kD) + kbase + 8 * (et % kChunksPerRow));
+    const int half = threadIdx.x >> 7, ec = threadIdx.x & 127;
+    const uint4 ev = ld16(emb + b * kN + half * kD + kbase + 8 * min(ec, kChunksPerRow - 1));
 #pragma unroll
     for (int st = 0; st < kQSteps; ++st) wv[st] = ld16(wrow + 32 * st);
 #pragma unroll
@@ -195,20 +196,29 @@ __global__ __launch_bounds__(256) void proj_out_fused_part_kernel(
       rs[it] = rstd[t];
     }
     __builtin_amdgcn_sched_barrier(0);
-    e_lds[threadIdx.x] = ev;
+    {
+      float f[8];
+      unpack8(ev, f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = half ? f[e] : round_bf16(1.0f + f[e]);
+      m_lds[2 * threadIdx.x] = make_float4(f[0], f[1], f[2], f[3]);
+      m_lds[2 * threadIdx.x + 1] = make_float4(f[4], f[5], f[6], f[7]);
+    }
     __syncthreads();
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
       const int q = threadIdx.x + 256 * it;
       const int row = q / kChunksPerRow, c = q % kChunksPerRow;
-      float xf[8], sf[8], hf[8], o[8];
+      float xf[8], o[8];
       unpack8(xv[it], xf);
-      unpack8(e_lds[c], sf);
-      unpack8(e_lds[kChunksPerRow + c], hf);
+      const float4 m0 = m_lds[2 * c], m1 = m_lds[2 * c + 1];
+      const float4 h0 = m_lds[256 + 2 * c], h1 = m_lds[256 + 2 * c + 1];
+      const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+      const float hh[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float n = (xf[e] - mu[it]) * rs[it];
-        o[e] = n * round_bf16(1.0f + sf[e]) + hf[e];
+        o[e] = n * mm[e] + hh[e];
       }
       *reinterpret_cast<uint4*>(as + row * kARow32 + 4 * c) = pack8(o);
     }
