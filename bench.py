@@ -112,8 +112,10 @@ def proj_out_algorithmic_bytes(T: int) -> int:
 
 
 def proj_out_dominant_kernel_bytes(T: int) -> int:
-    """The d_out kernel: d_lat and W read, d_out written."""
-    return 2 * T * D + 2 * T * PO + 2 * PO * D
+    """The backward's main launch (d_out and the dWp partial sums): d_lat, out
+    and Wp read, d_out written (the fp32 partials it hands to the chunk sum
+    are this design's, not the method's)."""
+    return 4 * T * D + 2 * T * PO + 2 * PO * D
 
 
 def serve_algorithmic_bytes(B: int, S: int) -> int:
@@ -346,7 +348,7 @@ def main() -> int:
         step_bytes = proj_out_algorithmic_bytes(B * S)
         k_bytes = proj_out_dominant_kernel_bytes(B * S)
         fwd_name, bwd_name = "adaln_proj_out_fwd", "adaln_proj_out_bwd"
-        k_name = "proj_out_dx_kernel (d_out = d_lat Wp)"
+        k_name = "proj_out_bwd_kernel (d_out = d_lat Wp and the dWp chunk partials in one launch)"
     elif mod6_site:
         if B > 4:
             print("--site mod6 times the B <= 4 backward kernel; use a workload with B <= 4", file=sys.stderr)

@@ -334,7 +334,8 @@ int adaln_fwd_proj_out(const adaln_bf16* temb, const adaln_bf16* W, const adaln_
  * (adaln_bwd, adaln_bwd_f32 and adaln_norm_mod_bwd: the fused dx + level-0 kernel;
  * adaln_norm_mod_bwd_dx: the dx kernel; adaln_residual_bwd: the dh / dx +
  * level-0 kernel, and adaln_site_bwd; adaln_proj_bwd with B <= 4: its one kernel;
- * adaln_proj_out_bwd: the d_out kernel; adaln_fwd_proj_out: the kernel that
+ * adaln_proj_out_bwd: the kernel computing d_out and the dWp partial sums;
+ * adaln_fwd_proj_out: the kernel that
  * modulates and multiplies), timed with HIP
  * events carried by the kernel dispatch itself (no extra packets).
  * A timed dispatch leaves the stream idle for a few microseconds around it, so

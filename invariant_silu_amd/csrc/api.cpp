@@ -140,7 +140,7 @@ size_t ws_proj_bwd(int64_t B) {
   return pad256(static_cast<size_t>(B * kD * 2));   // SiLU activations (B > 4)
 }
 size_t ws_tree(int64_t B, int64_t S, int64_t H) { return ws_pairs(B, S, H); }
-constexpr int64_t kMaxTokens = int64_t{65535} * 512;   // proj_out: its dW launch has one grid row per 512 tokens
+constexpr int64_t kMaxTokens = int64_t{65535} * 512;   // proj_out: token indices (and a token's sample) fit 32 bits
 constexpr int64_t kProjOutO = 64;
 bool tokens_ok(int64_t T) { return T >= 1 && T <= kMaxTokens; }
 size_t ws_proj_out_db_offset(int64_t T) {

@@ -282,11 +282,20 @@ __global__ __launch_bounds__(256) void proj_out_fused_part_kernel(
 __global__ __launch_bounds__(256) void proj_out_fwd_combine_kernel(const float* __restrict__ part,
                                                                    const uint16_t* __restrict__ bias,
                                                                    uint16_t* __restrict__ latent, int64_t T) {
+  // 4 consecutive outputs of one token per thread (64 outputs per token)
   const int64_t n = T * kO;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t i = 4 * (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x);
   if (i >= n) return;
-  const float s = (part[i] + part[n + i]) + (part[2 * n + i] + part[3 * n + i]);
-  latent[i] = f32_to_bf16(s + bf16_to_f32(bias[i % kO]));
+  const float4 q0 = *reinterpret_cast<const float4*>(part + i);
+  const float4 q1 = *reinterpret_cast<const float4*>(part + n + i);
+  const float4 q2 = *reinterpret_cast<const float4*>(part + 2 * n + i);
+  const float4 q3 = *reinterpret_cast<const float4*>(part + 3 * n + i);
+  const uint2 bw = *reinterpret_cast<const uint2*>(bias + i % kO);
+  const float l0 = ((q0.x + q1.x) + (q2.x + q3.x)) + bf_lo(bw.x);
+  const float l1 = ((q0.y + q1.y) + (q2.y + q3.y)) + bf_hi(bw.x);
+  const float l2 = ((q0.z + q1.z) + (q2.z + q3.z)) + bf_lo(bw.y);
+  const float l3 = ((q0.w + q1.w) + (q2.w + q3.w)) + bf_hi(bw.y);
+  *reinterpret_cast<uint2*>(latent + i) = make_uint2(pack_bf16x2(l0, l1), pack_bf16x2(l2, l3));
 }
 
 // ---- backward: d_out ---------------------------------------------------------
@@ -299,11 +308,11 @@ __global__ __launch_bounds__(256) void proj_out_fwd_combine_kernel(const float* 
 // after the pair: one 16-byte store.
 constexpr int kDxCols = 256;
 
-__global__ __launch_bounds__(256) void proj_out_dx_kernel(const uint16_t* __restrict__ d_lat,
-                                                          const uint16_t* __restrict__ W,
-                                                          uint16_t* __restrict__ d_out, int64_t T) {
-  __shared__ __align__(16) uint32_t wt[kDxCols * kLdsStride2];   // 36 KB
-  const int k0 = static_cast<int>(blockIdx.y) * kDxCols;
+// d_out for 64 tokens (token block bx) x 256 columns (column block by)
+__device__ __forceinline__ void dx_block(const uint16_t* __restrict__ d_lat, const uint16_t* __restrict__ W,
+                                         uint16_t* __restrict__ d_out, int64_t T, int64_t bx, int by,
+                                         uint32_t* wt) {
+  const int k0 = by * kDxCols;
   // stage: row pair p (outputs 2p, 2p + 1) x column octet c8: 32 x 32 items
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
@@ -319,7 +328,7 @@ __global__ __launch_bounds__(256) void proj_out_dx_kernel(const uint16_t* __rest
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
-  const int64_t tw = static_cast<int64_t>(blockIdx.x) * 64 + 16 * wave;
+  const int64_t tw = bx * 64 + 16 * wave;
   const int64_t tr = tw + r < T ? tw + r : T - 1;
   const uint4 b0 = ld16(d_lat + tr * kO + 8 * g);
   const uint4 b1 = ld16(d_lat + tr * kO + 32 + 8 * g);
@@ -358,14 +367,15 @@ __global__ __launch_bounds__(256) void proj_out_dx_kernel(const uint16_t* __rest
 // outputs 16 w .. (A = d_lat rows), 4 column tiles n (B = out rows k0 + 16 n +
 // r); each instruction adds 32 tokens.  Blocks of column block 0 also sum
 // d_lat per output (wave 0, fp64, tokens ascending).
-__global__ __launch_bounds__(256) void proj_out_dw_kernel(const uint16_t* __restrict__ d_lat,
-                                                          const uint16_t* __restrict__ out,
-                                                          float* __restrict__ part, double* __restrict__ part_db,
-                                                          int64_t T) {
-  __shared__ __align__(16) uint32_t xs[64 * kLdsStride2];   // [k][token]
-  __shared__ __align__(16) uint32_t ds[64 * kLdsStride2];   // [o][token]
-  const int k0 = static_cast<int>(blockIdx.x) * 64;
-  const int64_t c = blockIdx.y;
+// One block: 64 columns of out x one 512-token chunk.  A full chunk (all
+// tokens < T) loads unconditionally, two rounds ahead of the one being
+// added; the last, partial chunk takes the guarded loads (zeros past T).
+template <bool kFull>
+__device__ __forceinline__ void dw_chunk(const uint16_t* __restrict__ d_lat, const uint16_t* __restrict__ out,
+                                         float* __restrict__ part, double* __restrict__ part_db, int64_t T,
+                                         int bx, int64_t c, uint32_t* xs, uint32_t* ds) {
+  constexpr int kRounds = kChunk / kRound;   // 8
+  const int k0 = bx * 64;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
@@ -374,23 +384,31 @@ __global__ __launch_bounds__(256) void proj_out_dw_kernel(const uint16_t* __rest
 #pragma unroll
   for (int n = 0; n < 4; ++n) acc[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   double sdb = 0.0;
-  // the round's four rows: out and d_lat of tokens tb, tb + 1 (zeros past T);
-  // the next round's are loaded while this one is added
-  uint4 x0, x1, d0, d1;
+  // a round's four rows per thread: out and d_lat of tokens tb, tb + 1
+  uint4 buf[kRounds][4];
   auto load = [&](int rd) {
     const int64_t tb = c * kChunk + rd * kRound + 2 * p;
-    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-    x0 = tb < T ? ld16(out + tb * kD + k0 + 8 * c8) : z;
-    x1 = tb + 1 < T ? ld16(out + (tb + 1) * kD + k0 + 8 * c8) : z;
-    d0 = tb < T ? ld16(d_lat + tb * kO + 8 * c8) : z;
-    d1 = tb + 1 < T ? ld16(d_lat + (tb + 1) * kO + 8 * c8) : z;
+    if constexpr (kFull) {
+      buf[rd][0] = ld16(out + tb * kD + k0 + 8 * c8);
+      buf[rd][1] = ld16(out + (tb + 1) * kD + k0 + 8 * c8);
+      buf[rd][2] = ld16(d_lat + tb * kO + 8 * c8);
+      buf[rd][3] = ld16(d_lat + (tb + 1) * kO + 8 * c8);
+    } else {
+      const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+      buf[rd][0] = tb < T ? ld16(out + tb * kD + k0 + 8 * c8) : z;
+      buf[rd][1] = tb + 1 < T ? ld16(out + (tb + 1) * kD + k0 + 8 * c8) : z;
+      buf[rd][2] = tb < T ? ld16(d_lat + tb * kO + 8 * c8) : z;
+      buf[rd][3] = tb + 1 < T ? ld16(d_lat + (tb + 1) * kO + 8 * c8) : z;
+    }
   };
   load(0);
-  for (int rd = 0; rd < kChunk / kRound; ++rd) {
+  load(1);
+#pragma unroll
+  for (int rd = 0; rd < kRounds; ++rd) {
     uint32_t ox[8], od[8];
-    interleave8(x0, x1, ox);
-    interleave8(d0, d1, od);
-    if (rd + 1 < kChunk / kRound) load(rd + 1);
+    interleave8(buf[rd][0], buf[rd][1], ox);
+    interleave8(buf[rd][2], buf[rd][3], od);
+    if (rd + 2 < kRounds) load(rd + 2);
     __syncthreads();   // the previous round's reads are done
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -407,7 +425,7 @@ __global__ __launch_bounds__(256) void proj_out_dw_kernel(const uint16_t* __rest
         acc[n] = mfma_bf16(a, b, acc[n]);
       }
     }
-    if (blockIdx.x == 0 && wave == 0) {
+    if (bx == 0 && wave == 0) {
       const uint32_t* row = ds + lane * kLdsStride2;
       for (int q = 0; q < kRound / 2; ++q) {
         sdb += static_cast<double>(bf_lo(row[q]));
@@ -421,18 +439,67 @@ __global__ __launch_bounds__(256) void proj_out_dw_kernel(const uint16_t* __rest
   for (int n = 0; n < 4; ++n)
 #pragma unroll
     for (int v = 0; v < 4; ++v) pc[static_cast<int64_t>(16 * wave + 4 * g + v) * kD + k0 + 16 * n + r] = acc[n][v];
-  if (blockIdx.x == 0 && wave == 0) part_db[c * kO + lane] = sdb;
+  if (bx == 0 && wave == 0) part_db[c * kO + lane] = sdb;
+}
+
+// The backward's two independent products in one launch: blocks [0, 48 C)
+// take a 64-column x 512-token chunk of the dWp partial sums (chunk-major, so
+// the longer blocks start first), the rest take 64 tokens x 256 columns of
+// d_out.
+constexpr int kDwColBlocks = kD / 64;   // 48
+
+__global__ __launch_bounds__(256) void proj_out_bwd_kernel(const uint16_t* __restrict__ d_lat,
+                                                           const uint16_t* __restrict__ out,
+                                                           const uint16_t* __restrict__ W,
+                                                           uint16_t* __restrict__ d_out, float* __restrict__ part,
+                                                           double* __restrict__ part_db, int64_t T,
+                                                           int64_t dw_blocks) {
+  __shared__ __align__(16) uint32_t lds[kDxCols * kLdsStride2];   // 36 KB: dx's Wp slab, or dw's two tiles
+  static_assert(2 * 64 * kLdsStride2 <= kDxCols * kLdsStride2, "dw tiles must fit the shared buffer");
+  const int64_t blk = blockIdx.x;
+  if (blk < dw_blocks) {
+    const int bx = static_cast<int>(blk % kDwColBlocks);
+    const int64_t c = blk / kDwColBlocks;
+    if ((c + 1) * kChunk <= T)
+      dw_chunk<true>(d_lat, out, part, part_db, T, bx, c, lds, lds + 64 * kLdsStride2);
+    else
+      dw_chunk<false>(d_lat, out, part, part_db, T, bx, c, lds, lds + 64 * kLdsStride2);
+  } else {
+    constexpr int kDxColBlocks = kD / kDxCols;
+    const int64_t q = blk - dw_blocks;
+    dx_block(d_lat, W, d_out, T, q / kDxColBlocks, static_cast<int>(q % kDxColBlocks), lds);
+  }
 }
 
 // dWp and dbp: the chunks' partials added in ascending order in fp64
+// 4 consecutive elements of dWp per thread; the chunks' partials are loaded
+// 8 at a time (indices clamped to the last chunk, so every load is in
+// bounds and none sits under a branch) and added in ascending chunk order
 __global__ __launch_bounds__(256) void proj_out_dw_combine_kernel(const float* __restrict__ part,
                                                                   const double* __restrict__ part_db,
                                                                   uint16_t* __restrict__ dW, uint16_t* __restrict__ db,
                                                                   int64_t chunks) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // < 64 * 3072 by the grid
-  double s = 0.0;
-  for (int64_t c = 0; c < chunks; ++c) s += static_cast<double>(part[c * kO * kD + i]);
-  dW[i] = f32_to_bf16(static_cast<float>(s));
+  const int64_t i = 4 * (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x);   // < 64 * 3072 by the grid
+  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+  for (int64_t c0 = 0; c0 < chunks; c0 += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t c = c0 + j < chunks ? c0 + j : chunks - 1;
+      v[j] = *reinterpret_cast<const float4*>(part + c * kO * kD + i);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool in = c0 + j < chunks;
+      s0 = in ? s0 + static_cast<double>(v[j].x) : s0;
+      s1 = in ? s1 + static_cast<double>(v[j].y) : s1;
+      s2 = in ? s2 + static_cast<double>(v[j].z) : s2;
+      s3 = in ? s3 + static_cast<double>(v[j].w) : s3;
+    }
+  }
+  const uint2 w = make_uint2(pack_bf16x2(static_cast<float>(s0), static_cast<float>(s1)),
+                             pack_bf16x2(static_cast<float>(s2), static_cast<float>(s3)));
+  *reinterpret_cast<uint2*>(dW + i) = w;
   if (blockIdx.x == 0 && threadIdx.x < kO) {
     double t = 0.0;
     for (int64_t c = 0; c < chunks; ++c) t += part_db[c * kO + threadIdx.x];
@@ -449,7 +516,7 @@ hipError_t launch_proj_out_fwd(const uint16_t* out, const uint16_t* W, const uin
   hipLaunchKernelGGL(proj_out_fwd_part_kernel, dim3(static_cast<unsigned>((T + kFwdTokens - 1) / kFwdTokens), kQuarters),
                      dim3(256), 0, s, out, W, part, T);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  hipLaunchKernelGGL(proj_out_fwd_combine_kernel, dim3(static_cast<unsigned>((T * kO + 255) / 256)), dim3(256), 0, s,
+  hipLaunchKernelGGL(proj_out_fwd_combine_kernel, dim3(static_cast<unsigned>((T * kO / 4 + 255) / 256)), dim3(256), 0, s,
                      part, bias, latent, T);
   return hipGetLastError();
 }
@@ -466,7 +533,7 @@ hipError_t launch_proj_out_fwd_fused(const uint16_t* x, const uint16_t* emb, con
   else
     hipLaunchKernelGGL(k, grid, dim3(256), 0, s, x, emb, mean, rstd, W, part, T, S);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  hipLaunchKernelGGL(proj_out_fwd_combine_kernel, dim3(static_cast<unsigned>((T * kO + 255) / 256)), dim3(256), 0, s,
+  hipLaunchKernelGGL(proj_out_fwd_combine_kernel, dim3(static_cast<unsigned>((T * kO / 4 + 255) / 256)), dim3(256), 0, s,
                      part, bias, latent, T);
   return hipGetLastError();
 }
@@ -475,16 +542,16 @@ hipError_t launch_proj_out_bwd(const uint16_t* d_lat, const uint16_t* out, const
                                uint16_t* dW, uint16_t* db, float* part, double* part_db, int64_t T, hipStream_t s,
                                hipEvent_t e0, hipEvent_t e1) {
   const int64_t chunks = proj_out_chunks(T);
-  const dim3 gdx(static_cast<unsigned>((T + 63) / 64), kD / kDxCols);
+  const int64_t dw_blocks = kDwColBlocks * chunks;
+  const int64_t dx_blocks = (T + 63) / 64 * (kD / kDxCols);
+  const dim3 grid(static_cast<unsigned>(dw_blocks + dx_blocks));
   if (e0 && e1)
-    hipExtLaunchKernelGGL(proj_out_dx_kernel, gdx, dim3(256), 0, s, e0, e1, 0, d_lat, W, d_out, T);
+    hipExtLaunchKernelGGL(proj_out_bwd_kernel, grid, dim3(256), 0, s, e0, e1, 0, d_lat, out, W, d_out, part, part_db,
+                          T, dw_blocks);
   else
-    hipLaunchKernelGGL(proj_out_dx_kernel, gdx, dim3(256), 0, s, d_lat, W, d_out, T);
+    hipLaunchKernelGGL(proj_out_bwd_kernel, grid, dim3(256), 0, s, d_lat, out, W, d_out, part, part_db, T, dw_blocks);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  hipLaunchKernelGGL(proj_out_dw_kernel, dim3(kD / 64, static_cast<unsigned>(chunks)), dim3(256), 0, s, d_lat, out,
-                     part, part_db, T);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  hipLaunchKernelGGL(proj_out_dw_combine_kernel, dim3(kO * kD / 256), dim3(256), 0, s, part, part_db, dW, db,
+  hipLaunchKernelGGL(proj_out_dw_combine_kernel, dim3(kO * kD / 4 / 256), dim3(256), 0, s, part, part_db, dW, db,
                      chunks);
   return hipGetLastError();
 }
