@@ -356,7 +356,7 @@ def main() -> int:
         step_bytes = mod6_algorithmic_bytes(B)
         k_bytes = mod6_dominant_kernel_bytes(B)
         fwd_name, bwd_name = "adaln_proj_fwd", "adaln_proj_bwd"
-        k_name = f"proj_bwd_small_kernel<{B}, 18432> (dW tiles + da column blocks)"
+        k_name = f"proj_bwd_small_kernel<{B}, 18432> (dW tiles + da leaf-group blocks)"
     elif residual_site:
         step_bytes = residual_algorithmic_bytes(B, S)
         k_bytes = residual_dominant_kernel_bytes(B, S)

@@ -49,7 +49,7 @@ extern "C" {
 
 typedef uint16_t adaln_bf16;
 
-#define ADALN_ABI_VERSION 8
+#define ADALN_ABI_VERSION 9
 
 enum adaln_status {
   ADALN_OK = 0,
@@ -79,8 +79,9 @@ enum adaln_op {
  *   PROJ_FWD:       H = K (3072), S ignored.  B*K*2 (SiLU activations, used when
  *                   B > 4).
  *   NORM_MOD_BWD:   H = D (3072).  B * ceil(S/32) * 2D * 8 bytes (level-0 pairs).
- *   PROJ_BWD:       H = K (3072), S ignored.  B*K*2 (SiLU activations, used when
- *                   B > 4).
+ *   PROJ_BWD:       H = K (3072), S ignored.  B <= 4: 8*B*K*8 (the fp64 da
+ *                   subtrees, 8 per sample and column); B > 4: B*K*2 (SiLU
+ *                   activations).
  *   TOKEN_TREE_SUM: B * ceil(S/32) * ceil(H/64) * 64 * 8 bytes (level-0 pairs).
  *   BWD:            H = D (3072).  NORM_MOD_BWD + PROJ_BWD, in that order.
  *   BWD_F32:        H = D (3072).  NORM_MOD_BWD + B*K*4 (fp32 activations).
@@ -171,8 +172,9 @@ int token_tree_fold(const void* part, float* out, int64_t B, int64_t T0, int64_t
  *   leaves (leaf t: rows t, t + 128, ..., ascending, from +0; N / 128 rows
  *   each) added pairwise in leaf order.  B <= 4 runs on the vector units, B > 4 on the fp64 matrix
  *   cores: the same bits either way.
- *   ws: adaln_workspace_bytes(ADALN_OP_PROJ_BWD, B, 1, K) bytes (holds a when
- *   B > 4). */
+ *   ws: adaln_workspace_bytes(ADALN_OP_PROJ_BWD, B, 1, K) bytes (B <= 4: the
+ *   sums of leaves 16g .. 16g + 15 for g = 0 .. 7, added pairwise by a second
+ *   launch; B > 4: a). */
 int adaln_proj_bwd(const float* d_emb, const adaln_bf16* temb, const adaln_bf16* W,
                    adaln_bf16* dW, adaln_bf16* db, adaln_bf16* dtemb, void* ws, size_t ws_bytes,
                    int64_t B, int64_t K, int64_t N, void* stream);

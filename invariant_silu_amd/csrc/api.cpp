@@ -137,7 +137,10 @@ size_t ws_proj_fwd(int64_t B) {
   return pad256(static_cast<size_t>(B * kD * 2));   // SiLU activations (B > 4)
 }
 size_t ws_proj_bwd(int64_t B) {
-  return pad256(static_cast<size_t>(B * kD * 2));   // SiLU activations (B > 4)
+  // B <= 4: the fp64 da subtrees (8 per sample and column) between the two
+  // launches; B > 4: the SiLU activations
+  return pad256(B <= adaln::proj_bwd_fused_max_batch() ? adaln::proj_bwd_fused_sub_bytes(B)
+                                                       : static_cast<size_t>(B * kD * 2));
 }
 size_t ws_tree(int64_t B, int64_t S, int64_t H) { return ws_pairs(B, S, H); }
 constexpr int64_t kMaxTokens = int64_t{65535} * 512;   // proj_out: token indices (and a token's sample) fit 32 bits
@@ -405,7 +408,8 @@ int adaln_proj_bwd(const float* d_emb, const adaln_bf16* temb, const adaln_bf16*
   if (B <= adaln::proj_bwd_fused_max_batch()) {
     hipEvent_t e0, e1;
     timing_events(&e0, &e1);
-    return launched(adaln::launch_proj_bwd_fused(d_emb, temb, W, dW, db, dtemb, B, N, s, e0, e1));
+    return launched(adaln::launch_proj_bwd_fused(d_emb, temb, W, dW, db, dtemb, static_cast<double*>(ws), B, N, s,
+                                                 e0, e1));
   }
   if (int rc = launched(adaln::launch_silu(temb, a, B * kD, s))) return rc;
   if (int rc = launched(adaln::launch_proj_bwd_dw(d_emb, a, dW, db, B, N, s))) return rc;
@@ -523,7 +527,8 @@ int adaln_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float* mean, co
     return rc;
   if (int rc = launched(adaln::launch_tree_fold(part, d_emb, B, T0, kN, s))) return rc;
   if (B <= adaln::proj_bwd_fused_max_batch())
-    return launched(adaln::launch_proj_bwd_fused(d_emb, temb, W, dW, db, dtemb, B, kN, s));
+    return launched(adaln::launch_proj_bwd_fused(d_emb, temb, W, dW, db, dtemb, reinterpret_cast<double*>(a), B, kN,
+                                                 s));
   if (int rc = launched(adaln::launch_silu(temb, a, B * kD, s))) return rc;
   if (int rc = launched(adaln::launch_proj_bwd_dw(d_emb, a, dW, db, B, kN, s))) return rc;
   return launched(adaln::launch_proj_bwd_da(d_emb, W, temb, dtemb, B, kN, s));

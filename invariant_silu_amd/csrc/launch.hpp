@@ -41,8 +41,10 @@ hipError_t launch_tree_fold(const float* part, float* out, int64_t B,
 hipError_t launch_tree_fold_views(const float* part, float* d0, float* d1, float* d2, int64_t ld, int64_t B,
                                   int64_t T0, int64_t nseg, hipStream_t s);
 int proj_bwd_fused_max_batch();
+// bytes of fp64 da subtrees the B <= 4 path keeps between its two launches
+size_t proj_bwd_fused_sub_bytes(int64_t B);
 hipError_t launch_proj_bwd_fused(const float* d_emb, const uint16_t* temb, const uint16_t* W,
-                                 uint16_t* dW, uint16_t* db, uint16_t* dtemb, int64_t B, int64_t N,
+                                 uint16_t* dW, uint16_t* db, uint16_t* dtemb, double* sub, int64_t B, int64_t N,
                                  hipStream_t s, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 hipError_t launch_proj_bwd_dw(const float* d_emb, const uint16_t* a, uint16_t* dW, uint16_t* db,
                               int64_t B, int64_t N, hipStream_t s);

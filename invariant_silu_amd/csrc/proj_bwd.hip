@@ -18,8 +18,10 @@
 // these orders exactly, so no result depends on the batch size or the grid.
 //
 // Kernels:
-//   proj_bwd_small_kernel<NB>  B <= 4: da column blocks (-> dtemb) and dW
-//                              tiles (-> dW, db) in one grid
+//   proj_bwd_small_kernel<NB>  B <= 4: da leaf-group blocks (-> the eight
+//                              16-leaf subtrees of every column) and dW tiles
+//                              (-> dW, db) in one grid
+//   da_finish_kernel<NB>       B <= 4: the subtrees added pairwise (-> dtemb)
 //   silu_kernel, dw_mfma_kernel, da_mfma_kernel   B > 4
 #include <hip/hip_ext.h>
 
@@ -230,6 +232,130 @@ __device__ __forceinline__ void da_block(const float* __restrict__ d_emb, const 
   }
 }
 
+// da for B <= 4 in two steps.  A leaf-group block (gq, cg) runs the 16
+// leaves 16 gq .. 16 gq + 15 over the 64 columns 64 cg .. 64 cg + 63 of W;
+// thread (leaf 16 gq + tid / 16, column quad tid % 16) holds 4 columns, so
+// one wave load covers 4 rows x 128 contiguous bytes: whole cache lines, and
+// the W stream is spread over 384 blocks.  The block then adds its 16 leaves
+// pairwise in leaf order -- the subtree those leaves form in the 128-leaf
+// pairwise tree -- and writes one fp64 value per (sample, column) to
+// sub[gq][b][col].  da_finish_kernel adds the 8 subtrees pairwise in order
+// (the tree's top three levels), so every sum is the one da_block computes.
+constexpr int kDaGroupLeaves = 16;
+constexpr int kDaGroups = kDaSlots / kDaGroupLeaves;            // 8
+constexpr int kDaQuadCols = 64;                                 // columns per leaf-group block
+constexpr int kDaQuads = kDaQuadCols / 4;                       // 16 column quads
+constexpr int kDaLeafBlocks = kDaGroups * (kD / kDaQuadCols);   // 384
+static_assert(kDaGroupLeaves * kDaQuads == kThreads, "leaf-group block shape");
+static_assert(kD % kDaQuadCols == 0, "leaf-group columns");
+
+template <int NB, int N = kN>
+__device__ __forceinline__ void da_leaf_group(const float* __restrict__ d_emb, const uint16_t* __restrict__ W,
+                                              double* __restrict__ sub, int L, double* red) {
+  // rows per batch (two batches in flight); N / 128 rows per leaf (48 or 144)
+  constexpr int U = NB == 1 ? 12 : (NB == 2 ? 8 : 6);
+  constexpr int kLeafRows = kDaSteps<N>;
+  static_assert(kLeafRows % (2 * U) == 0, "batch pairs");
+  const int gq = L % kDaGroups, cg = L / kDaGroups;
+  const int l = threadIdx.x / kDaQuads, cq = threadIdx.x % kDaQuads;
+  const int leaf = gq * kDaGroupLeaves + l;
+  const int col0 = cg * kDaQuadCols;
+  const Buffer wb(W, static_cast<uint32_t>(N) * kD * 2);
+  const Buffer eb(d_emb, static_cast<uint32_t>(NB) * N * 4);
+  const uint32_t w_lane = (static_cast<uint32_t>(leaf) * kD + col0 + cq * 4) * 2;
+  const uint32_t e_lane = static_cast<uint32_t>(leaf) * 4;
+  constexpr uint32_t kWStep = kDaSlots * kD * 2;   // bytes between a leaf's rows
+  constexpr uint32_t kEStep = kDaSlots * 4;
+
+  auto load = [&](int i0, uint2 (&w)[U], float (&d)[U][NB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(wb.rsrc, w_lane, (i0 + u) * kWStep, 0);
+      w[u] = make_uint2(v[0], v[1]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) d[u][b] = eb.f32(e_lane, b * N * 4 + (i0 + u) * kEStep);
+  };
+  double acc[NB][4];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[b][e] = 0.0;
+  auto accumulate = [&](const uint2 (&w)[U], const float (&d)[U][NB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float wf[4] = {bf_lo(w[u].x), bf_hi(w[u].x), bf_lo(w[u].y), bf_hi(w[u].y)};
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const double dd = static_cast<double>(d[u][b]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[b][e] = __builtin_fma(dd, static_cast<double>(wf[e]), acc[b][e]);
+      }
+    }
+  };
+
+  // two register batches: the next one is in flight while one is added
+  uint2 wa[U], wbt[U];
+  float da_[U][NB], db_[U][NB];
+  load(0, wa, da_);
+#pragma unroll 1
+  for (int i0 = 0; i0 < kLeafRows - 2 * U; i0 += 2 * U) {
+    load(i0 + U, wbt, db_);
+    __builtin_amdgcn_sched_barrier(0);
+    accumulate(wa, da_);
+    __builtin_amdgcn_sched_barrier(0);
+    load(i0 + 2 * U, wa, da_);
+    __builtin_amdgcn_sched_barrier(0);
+    accumulate(wbt, db_);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  load(kLeafRows - U, wbt, db_);
+  __builtin_amdgcn_sched_barrier(0);
+  accumulate(wa, da_);
+  accumulate(wbt, db_);
+
+  // the block's 16 leaves, pairwise in leaf order: ((l0 + l1) + (l2 + l3)) + ...
+  constexpr int kRow = NB * kDaQuadCols;   // doubles per leaf
+  static_assert(kRow <= kThreads, "one subtree value per thread");
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[l * kRow + b * kDaQuadCols + cq * 4 + e] = acc[b][e];
+  __syncthreads();
+#pragma unroll
+  for (int w = 1; w < kDaGroupLeaves; w <<= 1) {
+    for (int i = threadIdx.x; i < (kDaGroupLeaves / (2 * w)) * kRow; i += kThreads) {
+      const int s = (i / kRow) * 2 * w, r = i % kRow;
+      red[s * kRow + r] += red[(s + w) * kRow + r];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x < kRow) {
+    const int b = threadIdx.x / kDaQuadCols, c = threadIdx.x % kDaQuadCols;
+    sub[(static_cast<int64_t>(gq) * NB + b) * kD + col0 + c] = red[threadIdx.x];
+  }
+}
+
+// da = the 8 subtrees of a (sample, column) added pairwise in order, then
+// dtemb = bf16(da * silu'(temb)); one thread per (sample, column)
+template <int NB>
+__global__ __launch_bounds__(256) void da_finish_kernel(const double* __restrict__ sub,
+                                                        const uint16_t* __restrict__ temb,
+                                                        uint16_t* __restrict__ dtemb) {
+  const int i = blockIdx.x * 256 + threadIdx.x;   // b * D + column
+  if (i >= NB * kD) return;
+  double v[kDaGroups];
+#pragma unroll
+  for (int g = 0; g < kDaGroups; ++g) v[g] = sub[static_cast<int64_t>(g) * NB * kD + i];
+#pragma unroll
+  for (int w = 1; w < kDaGroups; w <<= 1)
+#pragma unroll
+    for (int s = 0; s < kDaGroups; s += 2 * w) v[s] += v[s + w];
+  dtemb[i] = f32_to_bf16(static_cast<float>(v[0]) * dsilu_f32(bf16_to_f32(temb[i])));
+}
+
 // dW tile (192 rows x 256 columns of part p, column block kb): a write
 // stream; a = bf16(SiLU(temb)) per thread for its 8 columns.  Tiles of column
 // block 0 also write db for their rows: samples in order from +0.
@@ -303,25 +429,25 @@ __device__ __forceinline__ void dw_tile(const float* __restrict__ d_emb,
 // LDS of a projection-backward block, laid out per role.
 template <int NB>
 struct ProjBwdShared {
-  static constexpr size_t kRed = sizeof(double) * kDaSlots * NB * kDaCols;
+  static constexpr size_t kRed = sizeof(double) * kDaGroupLeaves * NB * kDaQuadCols;
   static constexpr size_t kDe = sizeof(float) * NB * kRowsPerPart;
   static constexpr size_t kBytes = kRed > kDe ? kRed : kDe;
 };
 
-// Small batches (B <= 4, a template parameter): one grid, blocks [0, 192)
-// are the da column blocks (they read W and write dtemb), the rest the dW
-// tiles (they write dW and db): [192, 576) at N = 6144; the two streams run
-// side by side.
+// Small batches (B <= 4, a template parameter): one grid, blocks [0, 384)
+// are the da leaf-group blocks (they read W and write the subtrees), the
+// rest the dW tiles (they write dW and db): [384, 768) at N = 6144; the two
+// streams run side by side.  da_finish_kernel follows.
 template <int NB, int N = kN>
 __global__ __launch_bounds__(kThreads) void proj_bwd_small_kernel(
     const float* __restrict__ d_emb, const uint16_t* __restrict__ temb, const uint16_t* __restrict__ W,
-    uint16_t* __restrict__ dW, uint16_t* __restrict__ db, uint16_t* __restrict__ dtemb) {
+    uint16_t* __restrict__ dW, uint16_t* __restrict__ db, double* __restrict__ sub) {
   __shared__ __align__(16) unsigned char smem[ProjBwdShared<NB>::kBytes];
   const int blk = blockIdx.x;
-  if (blk < kDaBlocks) {
-    da_block<NB, uint16_t, N>(d_emb, W, temb, dtemb, blk, 0, NB, reinterpret_cast<double*>(smem));
+  if (blk < kDaLeafBlocks) {
+    da_leaf_group<NB, N>(d_emb, W, sub, blk, reinterpret_cast<double*>(smem));
   } else {
-    const int t = blk - kDaBlocks;
+    const int t = blk - kDaLeafBlocks;
     dw_tile<NB, N>(d_emb, temb, dW, db, t % kDwParts<N>, t / kDwParts<N>,
                    reinterpret_cast<float (*)[kRowsPerPart]>(smem));
   }
@@ -542,28 +668,30 @@ int proj_bwd_fused_max_batch() { return kBatchChunk; }
 namespace {
 
 template <int NB, int N>
-void launch_small(const float* d_emb, const uint16_t* temb, const uint16_t* W, uint16_t* dW, uint16_t* db,
-                  uint16_t* dtemb, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  const dim3 grid(kDaBlocks + kDwTiles<N>), block(kThreads);
+hipError_t launch_small(const float* d_emb, const uint16_t* temb, const uint16_t* W, uint16_t* dW, uint16_t* db,
+                        uint16_t* dtemb, double* sub, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  const dim3 grid(kDaLeafBlocks + kDwTiles<N>), block(kThreads);
   if (e0 && e1)
     hipExtLaunchKernelGGL((proj_bwd_small_kernel<NB, N>), grid, block, 0, s, e0, e1, 0, d_emb, temb, W, dW, db,
-                          dtemb);
+                          sub);
   else
-    hipLaunchKernelGGL((proj_bwd_small_kernel<NB, N>), grid, block, 0, s, d_emb, temb, W, dW, db, dtemb);
+    hipLaunchKernelGGL((proj_bwd_small_kernel<NB, N>), grid, block, 0, s, d_emb, temb, W, dW, db, sub);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  hipLaunchKernelGGL(da_finish_kernel<NB>, dim3((NB * kD + 255) / 256), dim3(256), 0, s, sub, temb, dtemb);
+  return hipGetLastError();
 }
 
 template <int N>
 hipError_t proj_bwd_fused_rows(const float* d_emb, const uint16_t* temb, const uint16_t* W, uint16_t* dW,
-                               uint16_t* db, uint16_t* dtemb, int64_t B, hipStream_t s, hipEvent_t e0,
-                               hipEvent_t e1) {
+                               uint16_t* db, uint16_t* dtemb, double* sub, int64_t B, hipStream_t s,
+                               hipEvent_t e0, hipEvent_t e1) {
   switch (B) {
-    case 1: launch_small<1, N>(d_emb, temb, W, dW, db, dtemb, s, e0, e1); break;
-    case 2: launch_small<2, N>(d_emb, temb, W, dW, db, dtemb, s, e0, e1); break;
-    case 3: launch_small<3, N>(d_emb, temb, W, dW, db, dtemb, s, e0, e1); break;
-    case 4: launch_small<4, N>(d_emb, temb, W, dW, db, dtemb, s, e0, e1); break;
+    case 1: return launch_small<1, N>(d_emb, temb, W, dW, db, dtemb, sub, s, e0, e1);
+    case 2: return launch_small<2, N>(d_emb, temb, W, dW, db, dtemb, sub, s, e0, e1);
+    case 3: return launch_small<3, N>(d_emb, temb, W, dW, db, dtemb, sub, s, e0, e1);
+    case 4: return launch_small<4, N>(d_emb, temb, W, dW, db, dtemb, sub, s, e0, e1);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 template <int N>
@@ -585,11 +713,13 @@ hipError_t proj_bwd_da_rows(const float* d_emb, const uint16_t* W, const uint16_
 
 }  // namespace
 
+size_t proj_bwd_fused_sub_bytes(int64_t B) { return static_cast<size_t>(kDaGroups * B * kD * 8); }
+
 hipError_t launch_proj_bwd_fused(const float* d_emb, const uint16_t* temb, const uint16_t* W,
-                                 uint16_t* dW, uint16_t* db, uint16_t* dtemb, int64_t B, int64_t N, hipStream_t s,
-                                 hipEvent_t e0, hipEvent_t e1) {
-  if (N == kN) return proj_bwd_fused_rows<kN>(d_emb, temb, W, dW, db, dtemb, B, s, e0, e1);
-  if (N == kN6) return proj_bwd_fused_rows<kN6>(d_emb, temb, W, dW, db, dtemb, B, s, e0, e1);
+                                 uint16_t* dW, uint16_t* db, uint16_t* dtemb, double* sub, int64_t B, int64_t N,
+                                 hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (N == kN) return proj_bwd_fused_rows<kN>(d_emb, temb, W, dW, db, dtemb, sub, B, s, e0, e1);
+  if (N == kN6) return proj_bwd_fused_rows<kN6>(d_emb, temb, W, dW, db, dtemb, sub, B, s, e0, e1);
   return hipErrorInvalidValue;
 }
 

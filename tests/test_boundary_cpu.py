@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_strerror(L):
-    assert L.adaln_abi_version() == 8
+    assert L.adaln_abi_version() == 9
     for code in range(-7, 1):
         assert len(lib.strerror(code)) >= 2
 
@@ -57,7 +57,9 @@ def test_workspace_sizes(L):
         T0 = math.ceil(S / 32)
         assert lib.workspace_bytes(lib.OP_NORM_MOD_BWD, B, S, 3072) == pad(B * T0 * 6144 * 8)
         assert lib.workspace_bytes(lib.OP_TOKEN_TREE_SUM, B, S, 100) == pad(B * T0 * 128 * 8)
-        assert lib.workspace_bytes(lib.OP_PROJ_BWD, B, S, 3072) == pad(B * 3072 * 2)
+        # B <= 4: 8 fp64 da subtrees per sample and column; B > 4: the SiLU activations
+        proj_bwd = pad(8 * B * 3072 * 8) if B <= 4 else pad(B * 3072 * 2)
+        assert lib.workspace_bytes(lib.OP_PROJ_BWD, B, S, 3072) == proj_bwd
         assert lib.workspace_bytes(lib.OP_PROJ_FWD, B, S, 3072) == pad(B * 3072 * 2)
         assert lib.workspace_bytes(lib.OP_BWD_F32, B, S, 3072) == pad(B * T0 * 6144 * 8) + pad(B * 3072 * 4)
         assert lib.workspace_bytes(lib.OP_RESIDUAL_BWD, B, S, 3072) == pad(B * T0 * 9216 * 8)
