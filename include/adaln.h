@@ -84,7 +84,8 @@ enum adaln_op {
  *                   activations).
  *   TOKEN_TREE_SUM: B * ceil(S/32) * ceil(H/64) * 64 * 8 bytes (level-0 pairs).
  *   BWD:            H = D (3072).  NORM_MOD_BWD + PROJ_BWD, in that order.
- *   BWD_F32:        H = D (3072).  NORM_MOD_BWD + B*K*4 (fp32 activations).
+ *   BWD_F32:        H = D (3072).  NORM_MOD_BWD + B*K*4 (fp32 activations),
+ *                   then for B <= 4 8*B*K*8 (the fp64 da subtrees).
  *   RESIDUAL_BWD:   H = D (3072).  B * ceil(S/32) * 3D * 8 bytes (level-0 pairs).
  *   PROJ_OUT_BWD:   H = K (3072), T = B * S tokens (T <= 65535 * 512; only the
  *                   product is checked, so B = 1, S = T is fine).

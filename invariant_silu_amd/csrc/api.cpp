@@ -155,7 +155,9 @@ size_t ws_proj_out(int64_t T) {
 }
 size_t ws_fwd_proj_out(int64_t B, int64_t S) { return ws_proj_fwd(B) + ws_proj_out_fwd(B * S); }
 size_t ws_proj_bwd_f32(int64_t B) {
-  return pad256(static_cast<size_t>(B * kD * 4));   // SiLU activations (fp32 storage)
+  // SiLU activations (fp32 storage); B <= 4: then the fp64 da subtrees
+  return pad256(static_cast<size_t>(B * kD * 4)) +
+         (B <= adaln::proj_bwd_fused_max_batch() ? pad256(adaln::proj_bwd_fused_sub_bytes(B)) : 0);
 }
 bool batch_ok(int64_t B) { return B >= 1 && B <= kMaxB; }
 bool seq_ok(int64_t S) { return S >= 1 && S <= kMaxS; }
@@ -589,7 +591,8 @@ int adaln_bwd_f32(const float* gout, const float* x, const float* mean, const fl
   if (int rc = launched(adaln::launch_norm_mod_bwd_f32(gout, x, mean, rstd, emb, dx, part, B, S, s, e0, e1)))
     return rc;
   if (int rc = launched(adaln::launch_tree_fold(part, d_emb, B, T0, kN, s))) return rc;
-  return launched(adaln::launch_proj_bwd_f32(d_emb, temb, W, a, dW, db, dtemb, B, s));
+  double* sub = reinterpret_cast<double*>(reinterpret_cast<char*>(a) + pad256(static_cast<size_t>(B * kD * 4)));
+  return launched(adaln::launch_proj_bwd_f32(d_emb, temb, W, a, dW, db, dtemb, sub, B, s));
 }
 
 int adaln_site_fwd(const adaln_bf16* x, const adaln_bf16* residual, const adaln_bf16* shift, const adaln_bf16* scale,

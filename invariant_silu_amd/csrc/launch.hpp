@@ -97,7 +97,7 @@ hipError_t launch_norm_mod_bwd_f32(const float* g, const float* x, const float* 
                                    const float* emb, float* dx, float* part, int64_t B, int64_t S,
                                    hipStream_t s, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 hipError_t launch_proj_bwd_f32(const float* d_emb, const float* temb, const float* W, float* a, float* dW,
-                               float* db, float* dtemb, int64_t B, hipStream_t s);
+                               float* db, float* dtemb, double* sub, int64_t B, hipStream_t s);   // sub: B <= 4
 hipError_t launch_selftest_probe(const float* in, float* out, uint32_t* bits, int n,
                                  hipStream_t s);
 

@@ -54,46 +54,13 @@ static_assert(kN % kRowsPerPart == 0 && kN6 % kRowsPerPart == 0 && kRowsPerPart 
 static_assert(kD % kTileCols == 0, "column blocks");
 static_assert(kBlockThreads == kThreads, "one block size for every role");
 
-// da blocks: 16 columns of W over all N rows, so each block finishes the
-// sum and writes dtemb itself.  128 row slots, slot t = leaf t: rows t,
-// t + 128, ... in order; the 128 slots are then added as a pairwise tree.  The four 32-byte quarters of a 128-byte row
-// segment go to blocks L, L + 8, L + 16 and L + 24, which the dispatcher
-// places on the same XCD (one L2 serves all four).
-constexpr int kDaCols = 16;
-constexpr int kDaColThreads = kDaCols / 8;            // 2
-constexpr int kDaSlots = kThreads / kDaColThreads;    // 128
-constexpr int kDaBlocks = kD / kDaCols;               // 192
+// da: 128 leaves per column, leaf t = rows t, t + 128, ... in that order
+// from +0 (N / 128 rows each); the leaves are then added pairwise in index
+// order.
+constexpr int kDaSlots = 128;
 template <int N>
-constexpr int kDaSteps = N / kDaSlots;                // rows per thread: 48 at N = 6144
-constexpr int kDaShare = 128 / (kDaCols * 2);         // blocks sharing a 128-byte segment: 4
-
-static_assert(kDaBlocks % (8 * kDaShare) == 0, "da block to column mapping");
-static_assert(kDaSteps<kN> == 48, "a slot is one leaf of 48 rows");
-
-// 8 consecutive elements of one row: one 16-byte load (bf16) or two (fp32)
-template <typename T>
-struct Row8;
-template <>
-struct Row8<uint16_t> {
-  uint4 v;
-  __device__ __forceinline__ void load(const Buffer& b, uint32_t lane_off, uint32_t off) {
-    v = b.u128(lane_off, off);
-  }
-  __device__ __forceinline__ void unpack(float (&f)[8]) const { unpack8(v, f); }
-};
-template <>
-struct Row8<float> {
-  uint4 v[2];
-  __device__ __forceinline__ void load(const Buffer& b, uint32_t lane_off, uint32_t off) {
-    v[0] = b.u128(lane_off, off);
-    v[1] = b.u128(lane_off, off + 16);
-  }
-  __device__ __forceinline__ void unpack(float (&f)[8]) const {
-    const uint32_t u[8] = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = __uint_as_float(u[e]);
-  }
-};
+constexpr int kDaSteps = N / kDaSlots;                // rows per leaf: 48 at N = 6144
+static_assert(kDaSteps<kN> == 48 && kN6 % kDaSlots == 0, "leaf rows");
 
 // 2 consecutive elements of one row
 template <typename T>
@@ -129,109 +96,6 @@ struct Pair<float> {
   }
 };
 
-__device__ __forceinline__ int da_first_col(int L) {
-  const int g = L / (8 * kDaShare), q = (L / 8) % kDaShare, xcd = L % 8;
-  return ((g * 8 + xcd) * kDaShare + q) * kDaCols;
-}
-
-// da and dtemb for samples b0 .. b0 + nb - 1 (nb <= NB) and the 16 columns of
-// block L; T is the storage type of W, temb and dtemb.  red: LDS,
-// kDaSlots * NB * kDaCols doubles.
-template <int NB, typename T, int N = kN>
-__device__ __forceinline__ void da_block(const float* __restrict__ d_emb, const T* __restrict__ W,
-                                         const T* __restrict__ temb, T* __restrict__ dtemb,
-                                         int L, int64_t b0, int nb, double* red) {
-  // rows per batch (two batches in flight), sized to keep registers <= ~128
-  constexpr int U = sizeof(T) == 4 ? 4 : (NB == 1 ? 8 : (NB == 2 ? 6 : (NB == 3 ? 6 : 4)));
-  constexpr int kLeafRows = kDaSteps<N>;
-  static_assert(kLeafRows % (2 * U) == 0, "batch pairs");
-  static_assert(kLeafRows % U == 0, "batches");
-  const int ct = threadIdx.x % kDaColThreads;
-  const int slot = threadIdx.x / kDaColThreads;
-  const int col0 = da_first_col(L);
-  const Buffer wb(W, static_cast<uint32_t>(N) * kD * sizeof(T));
-  const Buffer eb(d_emb + b0 * N, static_cast<uint32_t>(nb) * N * 4);
-  const uint32_t w_lane = (static_cast<uint32_t>(slot) * kD + col0 + ct * 8) * sizeof(T);
-  const uint32_t e_lane = static_cast<uint32_t>(slot) * 4;
-  constexpr uint32_t kWStep = kDaSlots * kD * sizeof(T);   // bytes between a slot's rows
-  constexpr uint32_t kEStep = kDaSlots * 4;
-
-  auto load = [&](int i0, Row8<T> (&w)[U], float (&d)[U][NB]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) w[u].load(wb, w_lane, (i0 + u) * kWStep);
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int bl = b < nb ? b : nb - 1;   // samples past nb: any in-range value, never stored
-        d[u][b] = eb.f32(e_lane, bl * N * 4 + (i0 + u) * kEStep);
-      }
-  };
-  double acc[NB][8];
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[b][e] = 0.0;
-  auto accumulate = [&](const Row8<T> (&w)[U], const float (&d)[U][NB]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float wf[8];
-      w[u].unpack(wf);
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const double dd = static_cast<double>(d[u][b]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[b][e] = __builtin_fma(dd, static_cast<double>(wf[e]), acc[b][e]);
-      }
-    }
-  };
-
-  // two register batches: the next one is in flight while one is added
-  Row8<T> wa[U], wbt[U];
-  float da_[U][NB], db_[U][NB];
-  load(0, wa, da_);
-  // (scheduling barriers keep the compiler from hoisting a batch's loads
-  // above the adds of the batch whose registers they reuse)
-#pragma unroll 1
-  for (int i0 = 0; i0 < kLeafRows - 2 * U; i0 += 2 * U) {
-    load(i0 + U, wbt, db_);
-    __builtin_amdgcn_sched_barrier(0);
-    accumulate(wa, da_);
-    __builtin_amdgcn_sched_barrier(0);
-    load(i0 + 2 * U, wa, da_);
-    __builtin_amdgcn_sched_barrier(0);
-    accumulate(wbt, db_);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  load(kLeafRows - U, wbt, db_);
-  __builtin_amdgcn_sched_barrier(0);
-  accumulate(wa, da_);
-  accumulate(wbt, db_);
-
-  constexpr int kRow = NB * kDaCols;   // doubles per slot
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) red[slot * kRow + b * kDaCols + ct * 8 + e] = acc[b][e];
-  __syncthreads();
-  // pairwise tree over the slots: ((s0 + s1) + (s2 + s3)) + ...
-#pragma unroll
-  for (int w = 1; w < kDaSlots; w <<= 1) {
-    for (int i = threadIdx.x; i < (kDaSlots / (2 * w)) * kRow; i += kThreads) {
-      const int s = (i / kRow) * 2 * w, r = i % kRow;
-      red[s * kRow + r] += red[(s + w) * kRow + r];
-    }
-    __syncthreads();
-  }
-  if (threadIdx.x < kRow) {
-    const int b = threadIdx.x / kDaCols, c = threadIdx.x % kDaCols;
-    if (b < nb) {
-      const int64_t i = (b0 + b) * kD + col0 + c;
-      dtemb[i] = Storage<T>::store1(static_cast<float>(red[threadIdx.x]) * dsilu_f32(Storage<T>::load1(temb[i])));
-    }
-  }
-}
-
 // da for B <= 4 in two steps.  A leaf-group block (gq, cg) runs the 16
 // leaves 16 gq .. 16 gq + 15 over the 64 columns 64 cg .. 64 cg + 63 of W;
 // thread (leaf 16 gq + tid / 16, column quad tid % 16) holds 4 columns, so
@@ -240,7 +104,7 @@ __device__ __forceinline__ void da_block(const float* __restrict__ d_emb, const 
 // pairwise in leaf order -- the subtree those leaves form in the 128-leaf
 // pairwise tree -- and writes one fp64 value per (sample, column) to
 // sub[gq][b][col].  da_finish_kernel adds the 8 subtrees pairwise in order
-// (the tree's top three levels), so every sum is the one da_block computes.
+// (the tree's top three levels): the 128-leaf pairwise tree exactly.
 constexpr int kDaGroupLeaves = 16;
 constexpr int kDaGroups = kDaSlots / kDaGroupLeaves;            // 8
 constexpr int kDaQuadCols = 64;                                 // columns per leaf-group block
@@ -249,30 +113,57 @@ constexpr int kDaLeafBlocks = kDaGroups * (kD / kDaQuadCols);   // 384
 static_assert(kDaGroupLeaves * kDaQuads == kThreads, "leaf-group block shape");
 static_assert(kD % kDaQuadCols == 0, "leaf-group columns");
 
-template <int NB, int N = kN>
-__device__ __forceinline__ void da_leaf_group(const float* __restrict__ d_emb, const uint16_t* __restrict__ W,
+// 4 consecutive elements of one row of W: one 8-byte load (bf16) or one
+// 16-byte load (fp32)
+template <typename T>
+struct Quad;
+template <>
+struct Quad<uint16_t> {
+  uint32_t v[2];
+  __device__ __forceinline__ void load(const Buffer& b, uint32_t lane_off, uint32_t off) {
+    const auto t = __builtin_amdgcn_raw_buffer_load_b64(b.rsrc, lane_off, off, 0);
+    v[0] = t[0];
+    v[1] = t[1];
+  }
+  __device__ __forceinline__ void unpack(float (&f)[4]) const {
+    f[0] = bf_lo(v[0]); f[1] = bf_hi(v[0]); f[2] = bf_lo(v[1]); f[3] = bf_hi(v[1]);
+  }
+};
+template <>
+struct Quad<float> {
+  uint32_t v[4];
+  __device__ __forceinline__ void load(const Buffer& b, uint32_t lane_off, uint32_t off) {
+    const uint4 t = b.u128(lane_off, off);
+    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+  }
+  __device__ __forceinline__ void unpack(float (&f)[4]) const {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(v[e]);
+  }
+};
+
+template <int NB, typename T, int N = kN>
+__device__ __forceinline__ void da_leaf_group(const float* __restrict__ d_emb, const T* __restrict__ W,
                                               double* __restrict__ sub, int L, double* red) {
-  // rows per batch (two batches in flight); N / 128 rows per leaf (48 or 144)
-  constexpr int U = NB == 1 ? 12 : (NB == 2 ? 8 : 6);
+  // rows per batch (two batches in flight, registers <= ~128); N / 128 rows
+  // per leaf (48 or 144)
+  constexpr int U = sizeof(T) == 4 ? (NB == 1 ? 8 : (NB == 2 ? 6 : 4)) : (NB == 1 ? 12 : (NB == 2 ? 8 : 6));
   constexpr int kLeafRows = kDaSteps<N>;
   static_assert(kLeafRows % (2 * U) == 0, "batch pairs");
   const int gq = L % kDaGroups, cg = L / kDaGroups;
   const int l = threadIdx.x / kDaQuads, cq = threadIdx.x % kDaQuads;
   const int leaf = gq * kDaGroupLeaves + l;
   const int col0 = cg * kDaQuadCols;
-  const Buffer wb(W, static_cast<uint32_t>(N) * kD * 2);
+  const Buffer wb(W, static_cast<uint32_t>(N) * kD * sizeof(T));
   const Buffer eb(d_emb, static_cast<uint32_t>(NB) * N * 4);
-  const uint32_t w_lane = (static_cast<uint32_t>(leaf) * kD + col0 + cq * 4) * 2;
+  const uint32_t w_lane = (static_cast<uint32_t>(leaf) * kD + col0 + cq * 4) * sizeof(T);
   const uint32_t e_lane = static_cast<uint32_t>(leaf) * 4;
-  constexpr uint32_t kWStep = kDaSlots * kD * 2;   // bytes between a leaf's rows
+  constexpr uint32_t kWStep = kDaSlots * kD * sizeof(T);   // bytes between a leaf's rows
   constexpr uint32_t kEStep = kDaSlots * 4;
 
-  auto load = [&](int i0, uint2 (&w)[U], float (&d)[U][NB]) __attribute__((always_inline)) {
+  auto load = [&](int i0, Quad<T> (&w)[U], float (&d)[U][NB]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b64(wb.rsrc, w_lane, (i0 + u) * kWStep, 0);
-      w[u] = make_uint2(v[0], v[1]);
-    }
+    for (int u = 0; u < U; ++u) w[u].load(wb, w_lane, (i0 + u) * kWStep);
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -283,10 +174,11 @@ __device__ __forceinline__ void da_leaf_group(const float* __restrict__ d_emb, c
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[b][e] = 0.0;
-  auto accumulate = [&](const uint2 (&w)[U], const float (&d)[U][NB]) __attribute__((always_inline)) {
+  auto accumulate = [&](const Quad<T> (&w)[U], const float (&d)[U][NB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float wf[4] = {bf_lo(w[u].x), bf_hi(w[u].x), bf_lo(w[u].y), bf_hi(w[u].y)};
+      float wf[4];
+      w[u].unpack(wf);
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const double dd = static_cast<double>(d[u][b]);
@@ -297,7 +189,7 @@ __device__ __forceinline__ void da_leaf_group(const float* __restrict__ d_emb, c
   };
 
   // two register batches: the next one is in flight while one is added
-  uint2 wa[U], wbt[U];
+  Quad<T> wa[U], wbt[U];
   float da_[U][NB], db_[U][NB];
   load(0, wa, da_);
 #pragma unroll 1
@@ -339,11 +231,12 @@ __device__ __forceinline__ void da_leaf_group(const float* __restrict__ d_emb, c
 }
 
 // da = the 8 subtrees of a (sample, column) added pairwise in order, then
-// dtemb = bf16(da * silu'(temb)); one thread per (sample, column)
-template <int NB>
+// dtemb = da * silu'(temb) in the storage type (bf16: one rounding); one
+// thread per (sample, column)
+template <int NB, typename T = uint16_t>
 __global__ __launch_bounds__(256) void da_finish_kernel(const double* __restrict__ sub,
-                                                        const uint16_t* __restrict__ temb,
-                                                        uint16_t* __restrict__ dtemb) {
+                                                        const T* __restrict__ temb,
+                                                        T* __restrict__ dtemb) {
   const int i = blockIdx.x * 256 + threadIdx.x;   // b * D + column
   if (i >= NB * kD) return;
   double v[kDaGroups];
@@ -353,7 +246,7 @@ __global__ __launch_bounds__(256) void da_finish_kernel(const double* __restrict
   for (int w = 1; w < kDaGroups; w <<= 1)
 #pragma unroll
     for (int s = 0; s < kDaGroups; s += 2 * w) v[s] += v[s + w];
-  dtemb[i] = f32_to_bf16(static_cast<float>(v[0]) * dsilu_f32(bf16_to_f32(temb[i])));
+  dtemb[i] = Storage<T>::store1(static_cast<float>(v[0]) * dsilu_f32(Storage<T>::load1(temb[i])));
 }
 
 // dW tile (192 rows x 256 columns of part p, column block kb): a write
@@ -445,7 +338,7 @@ __global__ __launch_bounds__(kThreads) void proj_bwd_small_kernel(
   __shared__ __align__(16) unsigned char smem[ProjBwdShared<NB>::kBytes];
   const int blk = blockIdx.x;
   if (blk < kDaLeafBlocks) {
-    da_leaf_group<NB, N>(d_emb, W, sub, blk, reinterpret_cast<double*>(smem));
+    da_leaf_group<NB, uint16_t, N>(d_emb, W, sub, blk, reinterpret_cast<double*>(smem));
   } else {
     const int t = blk - kDaLeafBlocks;
     dw_tile<NB, N>(d_emb, temb, dW, db, t % kDwParts<N>, t / kDwParts<N>,
@@ -652,13 +545,14 @@ __global__ __launch_bounds__(64 * kDaMWaves) void da_mfma_kernel(const float* __
 }
 
 // da and dtemb for fp32 storage and B = NB <= 4 (the vector da blocks)
+// fp32 storage, B <= 4: the da leaf-group blocks alone (dW and db run on the
+// matrix cores for every B); da_finish_kernel<NB, float> follows
 template <int NB>
-__global__ __launch_bounds__(kThreads) void da_small_f32_kernel(const float* __restrict__ d_emb,
-                                                                const float* __restrict__ W,
-                                                                const float* __restrict__ temb,
-                                                                float* __restrict__ dtemb) {
-  __shared__ __align__(16) double red[kDaSlots * NB * kDaCols];
-  da_block<NB, float>(d_emb, W, temb, dtemb, blockIdx.x, 0, NB, red);
+__global__ __launch_bounds__(kThreads) void da_leaf_f32_kernel(const float* __restrict__ d_emb,
+                                                               const float* __restrict__ W,
+                                                               double* __restrict__ sub) {
+  __shared__ __align__(16) double red[kDaGroupLeaves * NB * kDaQuadCols];
+  da_leaf_group<NB, float>(d_emb, W, sub, blockIdx.x, red);
 }
 
 }  // namespace
@@ -744,20 +638,33 @@ hipError_t launch_silu(const uint16_t* temb, uint16_t* a, int64_t n, hipStream_t
 }
 
 
+namespace {
+
+template <int NB>
+hipError_t da_f32_small(const float* d_emb, const float* W, const float* temb, float* dtemb, double* sub,
+                        hipStream_t s) {
+  hipLaunchKernelGGL(da_leaf_f32_kernel<NB>, dim3(kDaLeafBlocks), dim3(kThreads), 0, s, d_emb, W, sub);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  hipLaunchKernelGGL((da_finish_kernel<NB, float>), dim3((NB * kD + 255) / 256), dim3(256), 0, s, sub, temb, dtemb);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 // fp32 storage: a = SiLU(temb) into `a`, dW and db on the matrix cores for
 // every B, da and dtemb on the vector units for B <= 4 and the matrix cores
 // beyond (the same leaves and order either way)
 hipError_t launch_proj_bwd_f32(const float* d_emb, const float* temb, const float* W, float* a, float* dW,
-                               float* db, float* dtemb, int64_t B, hipStream_t s) {
+                               float* db, float* dtemb, double* sub, int64_t B, hipStream_t s) {
   if (hipError_t e = launch_silu_f32(temb, a, B * kD, s); e != hipSuccess) return e;
   hipLaunchKernelGGL(dw_mfma_kernel<float>, dim3(kN / kDwMRows, kD / (kDwMCols * kDwMWaves)),
                      dim3(64 * kDwMWaves), 0, s, d_emb, a, dW, db, B);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   switch (B) {
-    case 1: hipLaunchKernelGGL(da_small_f32_kernel<1>, dim3(kDaBlocks), dim3(kThreads), 0, s, d_emb, W, temb, dtemb); break;
-    case 2: hipLaunchKernelGGL(da_small_f32_kernel<2>, dim3(kDaBlocks), dim3(kThreads), 0, s, d_emb, W, temb, dtemb); break;
-    case 3: hipLaunchKernelGGL(da_small_f32_kernel<3>, dim3(kDaBlocks), dim3(kThreads), 0, s, d_emb, W, temb, dtemb); break;
-    case 4: hipLaunchKernelGGL(da_small_f32_kernel<4>, dim3(kDaBlocks), dim3(kThreads), 0, s, d_emb, W, temb, dtemb); break;
+    case 1: return da_f32_small<1>(d_emb, W, temb, dtemb, sub, s);
+    case 2: return da_f32_small<2>(d_emb, W, temb, dtemb, sub, s);
+    case 3: return da_f32_small<3>(d_emb, W, temb, dtemb, sub, s);
+    case 4: return da_f32_small<4>(d_emb, W, temb, dtemb, sub, s);
     default: {
       const int64_t by = (B + 15) / 16;
       hipLaunchKernelGGL(da_mfma_kernel<float>, dim3(kD / kDaMCols, static_cast<unsigned>(by)),

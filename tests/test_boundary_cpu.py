@@ -61,7 +61,9 @@ def test_workspace_sizes(L):
         proj_bwd = pad(8 * B * 3072 * 8) if B <= 4 else pad(B * 3072 * 2)
         assert lib.workspace_bytes(lib.OP_PROJ_BWD, B, S, 3072) == proj_bwd
         assert lib.workspace_bytes(lib.OP_PROJ_FWD, B, S, 3072) == pad(B * 3072 * 2)
-        assert lib.workspace_bytes(lib.OP_BWD_F32, B, S, 3072) == pad(B * T0 * 6144 * 8) + pad(B * 3072 * 4)
+        # fp32: the activations, then for B <= 4 the fp64 da subtrees
+        sub = pad(8 * B * 3072 * 8) if B <= 4 else 0
+        assert lib.workspace_bytes(lib.OP_BWD_F32, B, S, 3072) == pad(B * T0 * 6144 * 8) + pad(B * 3072 * 4) + sub
         assert lib.workspace_bytes(lib.OP_RESIDUAL_BWD, B, S, 3072) == pad(B * T0 * 9216 * 8)
         C = math.ceil(B * S / 512)
         assert lib.workspace_bytes(lib.OP_PROJ_OUT_BWD, B, S, 3072) == pad(C * 64 * 3072 * 4) + pad(C * 64 * 8)
