@@ -22,6 +22,8 @@
 //                              16-leaf subtrees of every column) and dW tiles
 //                              (-> dW, db) in one grid
 //   da_finish_kernel<NB>       B <= 4: the subtrees added pairwise (-> dtemb)
+//   da_leaf_f32_kernel<NB>     fp32 storage, B <= 4: the leaf-group blocks alone
+//                              (then da_finish_kernel<NB, float>)
 //   silu_kernel, dw_mfma_kernel, da_mfma_kernel   B > 4
 #include <hip/hip_ext.h>
 
