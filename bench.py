@@ -99,9 +99,9 @@ def mod6_algorithmic_bytes(B: int) -> int:
 
 
 def mod6_dominant_kernel_bytes(B: int) -> int:
-    """The backward's one kernel at B <= 4: W read, dW and db written, d_emb,
-    temb read, dtemb written."""
-    return 2 * 2 * N6 * D + 2 * N6 + (4 * N6 + 2 * 2 * D) * B
+    """The backward's main kernel at B <= 4 (its second launch only finishes
+    dtemb): W read, dW and db written, d_emb and temb read."""
+    return 2 * 2 * N6 * D + 2 * N6 + (4 * N6 + 2 * D) * B
 
 
 def proj_out_algorithmic_bytes(T: int) -> int:

@@ -336,7 +336,8 @@ int adaln_fwd_proj_out(const adaln_bf16* temb, const adaln_bf16* W, const adaln_
 /* Benchmarking aid: per-launch durations of the main kernel of the backward
  * (adaln_bwd, adaln_bwd_f32 and adaln_norm_mod_bwd: the fused dx + level-0 kernel;
  * adaln_norm_mod_bwd_dx: the dx kernel; adaln_residual_bwd: the dh / dx +
- * level-0 kernel, and adaln_site_bwd; adaln_proj_bwd with B <= 4: its one kernel;
+ * level-0 kernel, and adaln_site_bwd; adaln_proj_bwd with B <= 4: its first
+ * kernel (da leaf groups and dW tiles);
  * adaln_proj_out_bwd: the kernel computing d_out and the dWp partial sums;
  * adaln_fwd_proj_out: the kernel that
  * modulates and multiplies), timed with HIP
