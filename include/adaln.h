@@ -49,7 +49,7 @@ extern "C" {
 
 typedef uint16_t adaln_bf16;
 
-#define ADALN_ABI_VERSION 9
+#define ADALN_ABI_VERSION 10
 
 enum adaln_status {
   ADALN_OK = 0,
@@ -152,14 +152,18 @@ int adaln_norm_mod_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float*
  *   adaln_workspace_bytes(ADALN_OP_NORM_MOD_BWD, B, S, D).
  * token_tree_fold: levels >= 1 of the tree from such pairs: `part` as written by
  *   adaln_norm_mod_bwd_tiles (H = 2D) or by level 0 of token_tree_sum (any H, in
- *   the same layout), T0 tiles per sample; out [B, H] fp32. */
+ *   the same layout), T0 tiles per sample; out [B, H] fp32.  part_bytes is the
+ *   size of the caller's pair buffer: it must hold B * ceil(H/64) * T0 * 128
+ *   floats (rounded up to 256 bytes), else ADALN_ERR_WORKSPACE and nothing is
+ *   read. */
 int adaln_norm_mod_bwd_dx(const adaln_bf16* gout, const adaln_bf16* x, const float* mean,
                           const float* rstd, const adaln_bf16* emb, adaln_bf16* dx, int64_t B,
                           int64_t S, int64_t D, void* stream);
 int adaln_norm_mod_bwd_tiles(const adaln_bf16* gout, const adaln_bf16* x, const float* mean,
                              const float* rstd, void* part, size_t part_bytes, int64_t B, int64_t S,
                              int64_t D, void* stream);
-int token_tree_fold(const void* part, float* out, int64_t B, int64_t T0, int64_t H, void* stream);
+int token_tree_fold(const void* part, size_t part_bytes, float* out, int64_t B, int64_t T0, int64_t H,
+                    void* stream);
 
 /* Projection backward (pull request 538, "What": projection backward; review
  * thread: silu'(z) = sigmoid(z) * (1 + z * (1 - sigmoid(z)))).

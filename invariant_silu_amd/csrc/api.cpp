@@ -351,12 +351,14 @@ int adaln_norm_mod_bwd_tiles(const adaln_bf16* gout, const adaln_bf16* x, const 
                                                    as_stream(stream)));
 }
 
-int token_tree_fold(const void* part, float* out, int64_t B, int64_t T0, int64_t H, void* stream) {
+int token_tree_fold(const void* part, size_t part_bytes, float* out, int64_t B, int64_t T0, int64_t H,
+                    void* stream) {
   if (!part || !out) return ADALN_ERR_NULL;
   if (!batch_ok(B) || T0 < 1 || T0 > kMaxS / kTile || H < 1 || H > (int64_t{1} << 24))
     return ADALN_ERR_SHAPE;
   if (!aligned16(part) || !aligned16(out)) return ADALN_ERR_ALIGN;
   const size_t bytes = ws_pairs(B, T0 * kTile, H);
+  if (part_bytes < bytes) return ADALN_ERR_WORKSPACE;
   if (int rc = check_overlap({{out, static_cast<size_t>(B * H * 4)}}, {{part, bytes}})) return rc;
   if (int rc = check_device()) return rc;
   (void)hipGetLastError();
@@ -385,7 +387,7 @@ int adaln_norm_mod_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float*
   if (int rc = launched(adaln::launch_norm_mod_bwd(gout, x, mean, rstd, emb, dx, static_cast<float*>(ws), B, S,
                                                    as_stream(stream), e0, e1)))
     return rc;
-  return token_tree_fold(ws, d_emb, B, ceil_div(S, kTile), kN, stream);
+  return token_tree_fold(ws, need, d_emb, B, ceil_div(S, kTile), kN, stream);
 }
 
 int adaln_proj_bwd(const float* d_emb, const adaln_bf16* temb, const adaln_bf16* W,

@@ -49,7 +49,7 @@ _SIGS = {
     "token_tree_sum": ([_P, _P, _P, _SZ, _I64, _I64, _I64, _P], ctypes.c_int),
     "adaln_norm_mod_bwd_dx": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "adaln_norm_mod_bwd_tiles": ([_P, _P, _P, _P, _P, _SZ, _I64, _I64, _I64, _P], ctypes.c_int),
-    "token_tree_fold": ([_P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "token_tree_fold": ([_P, _SZ, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "adaln_workspace_bytes": ([ctypes.c_int, _I64, _I64, _I64], _SZ),
     "adaln_selftest": ([], ctypes.c_int),
     "adaln_timing_begin": ([ctypes.c_int, ctypes.c_int], ctypes.c_int),

@@ -32,6 +32,33 @@ def _stream(dev: torch.device) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
 
 
+def _shape(t: torch.Tensor, shape, name: str) -> None:
+    """The C ABI sees pointers only, so every extent it assumes is checked here,
+    before anything reaches it."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _rank(t: torch.Tensor, n: int, name: str) -> None:
+    if t.dim() != n:
+        raise ValueError(f"{name} must have {n} dimensions, got shape {tuple(t.shape)}")
+
+
+def _proj_width(W: torch.Tensor, widths=(N, 6 * D)) -> int:
+    _rank(W, 2, "W")
+    if W.shape[0] not in widths or W.shape[1] != D:
+        raise ValueError(f"W must have shape (N, {D}) with N in {widths}, got {tuple(W.shape)}")
+    return W.shape[0]
+
+
+def _rows(x: torch.Tensor, name: str = "x"):
+    """(B, S) of a [B, S, 3072] activation."""
+    _rank(x, 3, name)
+    if x.shape[2] != D:
+        raise ValueError(f"{name} must have shape (B, S, {D}), got {tuple(x.shape)}")
+    return x.shape[0], x.shape[1]
+
+
 def _check(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor (the HIP library has no CPU path)")
@@ -50,6 +77,10 @@ def proj_fwd(temb: torch.Tensor, W: torch.Tensor, bias: torch.Tensor) -> torch.T
     """emb [B, N] bf16 = bf16(SiLU(temb) W^T + b), N = W.shape[0]: 6144 for the
     final modulation (scale | shift), 18432 for a block's 6-way modulation
     (shift1 | scale1 | gate1 | shift2 | scale2 | gate2)."""
+    Nw = _proj_width(W)
+    _rank(temb, 2, "temb")
+    _shape(temb, (temb.shape[0], D), "temb")
+    _shape(bias, (Nw,), "bias")
     for t, n in ((temb, "temb"), (W, "W"), (bias, "bias")):
         _check(t, torch.bfloat16, n)
     temb, W, bias = aligned(temb), aligned(W), aligned(bias)
@@ -63,6 +94,8 @@ def proj_fwd(temb: torch.Tensor, W: torch.Tensor, bias: torch.Tensor) -> torch.T
 
 def norm_mod_fwd(x: torch.Tensor, emb: torch.Tensor, eps: float = EPS):
     """(out bf16 [B,S,D], mean fp32 [B,S], rstd fp32 [B,S])."""
+    B, S = _rows(x)
+    _shape(emb, (B, N), "emb")
     _check(x, torch.bfloat16, "x")
     _check(emb, torch.bfloat16, "emb")
     x, emb = aligned(x), aligned(emb)
@@ -78,6 +111,11 @@ def norm_mod_fwd(x: torch.Tensor, emb: torch.Tensor, eps: float = EPS):
 def norm_mod_bwd(g: torch.Tensor, x: torch.Tensor, mean: torch.Tensor, rstd: torch.Tensor,
                  emb: torch.Tensor):
     """(dx bf16 [B,S,D], d_emb fp32 [B, 2D] = (d_scale | d_shift))."""
+    B, S = _rows(x)
+    _shape(g, x.shape, "g")
+    _shape(mean, (B, S), "mean")
+    _shape(rstd, (B, S), "rstd")
+    _shape(emb, (B, N), "emb")
     _check(g, torch.bfloat16, "g")
     _check(x, torch.bfloat16, "x")
     _check(mean, torch.float32, "mean")
@@ -97,6 +135,10 @@ def norm_mod_bwd(g: torch.Tensor, x: torch.Tensor, mean: torch.Tensor, rstd: tor
 def proj_bwd(d_emb: torch.Tensor, temb: torch.Tensor, W: torch.Tensor):
     """(dW bf16 [N, 3072], db bf16 [N], dtemb bf16 [B, 3072]); N = W.shape[0]
     (6144 or 18432, as for proj_fwd)."""
+    Nw = _proj_width(W)
+    _rank(temb, 2, "temb")
+    _shape(temb, (temb.shape[0], D), "temb")
+    _shape(d_emb, (temb.shape[0], Nw), "d_emb")
     _check(d_emb, torch.float32, "d_emb")
     _check(temb, torch.bfloat16, "temb")
     _check(W, torch.bfloat16, "W")
@@ -114,6 +156,7 @@ def proj_bwd(d_emb: torch.Tensor, temb: torch.Tensor, W: torch.Tensor):
 
 def token_tree_sum(x: torch.Tensor) -> torch.Tensor:
     """Compensated 32-token tree sum over dim 1 of an fp32 [B, S, H] tensor."""
+    _rank(x, 3, "x")
     _check(x, torch.float32, "x")
     x = aligned(x)
     B, S, H = x.shape
@@ -131,6 +174,10 @@ def fwd(x: torch.Tensor, temb: torch.Tensor, W: torch.Tensor, bias: torch.Tensor
     """One-call forward (adaln_fwd, or adaln_fwd_f32 for fp32 tensors):
     (out, emb, mean, rstd); with bf16 tensors the same bits as proj_fwd
     followed by norm_mod_fwd."""
+    B, S = _rows(x)
+    _shape(temb, (B, D), "temb")
+    _proj_width(W, (N,))
+    _shape(bias, (N,), "bias")
     dt = x.dtype
     if dt not in _STORAGE:
         raise TypeError(f"x must be bfloat16 or float32, got {dt}")
@@ -153,6 +200,13 @@ def bwd(g: torch.Tensor, x: torch.Tensor, mean: torch.Tensor, rstd: torch.Tensor
     """One-call backward (adaln_bwd, or adaln_bwd_f32 for fp32 tensors):
     (dx, d_emb, dW, db, dtemb); with bf16 tensors the same bits as
     norm_mod_bwd followed by proj_bwd."""
+    B, S = _rows(x)
+    _shape(g, x.shape, "g")
+    _shape(mean, (B, S), "mean")
+    _shape(rstd, (B, S), "rstd")
+    _shape(emb, (B, N), "emb")
+    _shape(temb, (B, D), "temb")
+    _proj_width(W, (N,))
     dt = x.dtype
     if dt not in _STORAGE:
         raise TypeError(f"x must be bfloat16 or float32, got {dt}")
@@ -179,6 +233,9 @@ def residual_fwd(x: torch.Tensor, residual: torch.Tensor, mod: torch.Tensor, eps
     """Residual norm site (adaln_residual_fwd): (out, h, mean, rstd) with
     h = bf16(residual + bf16(gate * x)), out = bf16(LN(h) * bf16(1 + scale) + shift),
     mod [B, 3 * 3072] = (shift | scale | gate); bf16 tensors."""
+    B, S = _rows(x)
+    _shape(residual, x.shape, "residual")
+    _shape(mod, (B, 3 * D), "mod")
     for t, n in ((x, "x"), (residual, "residual"), (mod, "mod")):
         _check(t, torch.bfloat16, n)
     x, residual, mod = aligned(x), aligned(residual), aligned(mod)
@@ -196,6 +253,12 @@ def residual_bwd(g_out: torch.Tensor, g_h: torch.Tensor, x: torch.Tensor, h: tor
                  rstd: torch.Tensor, mod: torch.Tensor):
     """Backward of the residual norm site (adaln_residual_bwd):
     (d_residual bf16, dx bf16, d_mod fp32 [B, 3 * 3072] = (d_shift | d_scale | d_gate))."""
+    B, S = _rows(x)
+    for t, n in ((g_out, "g_out"), (g_h, "g_h"), (h, "h")):
+        _shape(t, x.shape, n)
+    _shape(mean, (B, S), "mean")
+    _shape(rstd, (B, S), "rstd")
+    _shape(mod, (B, 3 * D), "mod")
     for t, n, dt in ((g_out, "g_out", torch.bfloat16), (g_h, "g_h", torch.bfloat16), (x, "x", torch.bfloat16),
                      (h, "h", torch.bfloat16), (mean, "mean", torch.float32), (rstd, "rstd", torch.float32),
                      (mod, "mod", torch.bfloat16)):
@@ -232,6 +295,14 @@ def site_fwd(x: torch.Tensor, shift: torch.Tensor, scale: torch.Tensor, residual
     e.g. chunks of the 6-way projection's output.  residual None: the plain
     site, returns (out, mean, rstd); else the residual site h = bf16(residual +
     bf16(gate * x)), returns (out, h, mean, rstd)."""
+    B, S = _rows(x)
+    for v, n in ((shift, "shift"), (scale, "scale"), (gate, "gate")):
+        if v is not None:
+            _shape(v, (B, D), n)
+    if residual is not None:
+        _shape(residual, x.shape, "residual")
+        if gate is None:
+            raise ValueError("the residual form needs gate")
     _check(x, torch.bfloat16, "x")
     x = aligned(x)
     res = residual is not None
@@ -257,6 +328,22 @@ def site_bwd(g_out: torch.Tensor, x: torch.Tensor, mean: torch.Tensor, rstd: tor
     (d_residual, dx, d_shift, d_scale, d_gate).  d_views: optional fp32 [B, D]
     output views (d_shift, d_scale[, d_gate]) with one row stride, e.g. chunks
     of a 6-way gradient; fresh tensors otherwise."""
+    B, S = _rows(x)
+    _shape(g_out, x.shape, "g_out")
+    _shape(mean, (B, S), "mean")
+    _shape(rstd, (B, S), "rstd")
+    _shape(scale, (B, D), "scale")
+    if g_h is not None:
+        if h is None or gate is None:
+            raise ValueError("the residual form needs h and gate")
+        _shape(g_h, x.shape, "g_h")
+        _shape(h, x.shape, "h")
+        _shape(gate, (B, D), "gate")
+    if d_views is not None:
+        if len(d_views) != (3 if g_h is not None else 2):
+            raise ValueError("d_views must hold one view per gradient (d_shift, d_scale[, d_gate])")
+        for v in d_views:
+            _shape(v, (B, D), "d_views")
     res = g_h is not None
     for t, n, dt in ((g_out, "g_out", torch.bfloat16), (x, "x", torch.bfloat16), (mean, "mean", torch.float32),
                      (rstd, "rstd", torch.float32)):
@@ -294,6 +381,10 @@ def site_bwd(g_out: torch.Tensor, x: torch.Tensor, mean: torch.Tensor, rstd: tor
 def proj_out_fwd(out: torch.Tensor, W: torch.Tensor, bias: torch.Tensor) -> torch.Tensor:
     """proj_out (adaln_proj_out_fwd): latent [..., 64] bf16 = bf16(out W^T + b) per
     token; out [..., 3072], W [64, 3072], bias [64], all bf16."""
+    if out.dim() < 1 or out.shape[-1] != D:
+        raise ValueError(f"out must have shape (..., {D}), got {tuple(out.shape)}")
+    _shape(W, (64, D), "W")
+    _shape(bias, (64,), "bias")
     for t, n in ((out, "out"), (W, "W"), (bias, "bias")):
         _check(t, torch.bfloat16, n)
     out, W, bias = aligned(out), aligned(W), aligned(bias)
@@ -312,6 +403,12 @@ def fwd_proj_out(x: torch.Tensor, temb: torch.Tensor, W: torch.Tensor, bias: tor
     modulation then proj_out without the modulated output in memory.  Returns
     (latent [B, S, 64], emb, mean, rstd), the same bits as fwd followed by
     proj_out_fwd on its out.  All tensors bf16."""
+    B, S = _rows(x)
+    _shape(temb, (B, D), "temb")
+    _proj_width(W, (N,))
+    _shape(bias, (N,), "bias")
+    _shape(Wp, (64, D), "Wp")
+    _shape(bp, (64,), "bp")
     for t, n in ((x, "x"), (temb, "temb"), (W, "W"), (bias, "bias"), (Wp, "Wp"), (bp, "bp")):
         _check(t, torch.bfloat16, n)
     x, temb, W, bias, Wp, bp = (aligned(t) for t in (x, temb, W, bias, Wp, bp))
@@ -330,6 +427,10 @@ def fwd_proj_out(x: torch.Tensor, temb: torch.Tensor, W: torch.Tensor, bias: tor
 def proj_out_bwd(d_lat: torch.Tensor, out: torch.Tensor, W: torch.Tensor):
     """Backward of proj_out (adaln_proj_out_bwd): (d_out bf16 like out, dW bf16
     [64, 3072], db bf16 [64])."""
+    if out.dim() < 1 or out.shape[-1] != D:
+        raise ValueError(f"out must have shape (..., {D}), got {tuple(out.shape)}")
+    _shape(W, (64, D), "W")
+    _shape(d_lat, tuple(out.shape[:-1]) + (64,), "d_lat")
     for t, n in ((d_lat, "d_lat"), (out, "out"), (W, "W")):
         _check(t, torch.bfloat16, n)
     d_lat, out, W = aligned(d_lat), aligned(out), aligned(W)
@@ -365,7 +466,8 @@ class AdaLNFinal(torch.autograd.Function):
     @staticmethod
     def backward(ctx, g):
         x, temb, W, emb, mean, rstd = ctx.saved_tensors
-        g = g.to(x.dtype)
+        if g.dtype != x.dtype:
+            raise TypeError(f"the upstream gradient must be {x.dtype} (the output's dtype), got {g.dtype}")
         dx, d_emb, dW, db, dtemb = bwd(g, x, mean, rstd, emb, temb, W)
         return dx, dtemb, dW, db, None
 
@@ -385,7 +487,9 @@ class ProjOut(torch.autograd.Function):
     @staticmethod
     def backward(ctx, g):
         out, Wp = ctx.saved_tensors
-        d_out, dW, db = proj_out_bwd(g.to(torch.bfloat16).contiguous(), out, Wp)
+        if g.dtype != torch.bfloat16:
+            raise TypeError(f"the upstream gradient must be torch.bfloat16 (latent's dtype), got {g.dtype}")
+        d_out, dW, db = proj_out_bwd(g, out, Wp)
         return d_out, dW, db
 
 

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_strerror(L):
-    assert L.adaln_abi_version() == 9
+    assert L.adaln_abi_version() == 10
     for code in range(-7, 1):
         assert len(lib.strerror(code)) >= 2
 
@@ -146,6 +146,12 @@ def test_validation_before_device_work(L):
     assert L.adaln_fwd_proj_out(*over, need, 6, 64, 3072, 64, 1e-6, None) == lib.ERR_OVERLAP
     assert L.adaln_norm_mod_fwd(p, p, p, p, p, 1, 0, 3072, 1e-6, None) == lib.ERR_SHAPE
     assert L.token_tree_sum(p, p, p, 1 << 20, 1, 1, 0, None) == lib.ERR_SHAPE
+    # token_tree_fold sizes the caller's pair buffer before reading it
+    pairs = lib.workspace_bytes(lib.OP_NORM_MOD_BWD, 2, 4096, 3072)
+    assert L.token_tree_fold(p, pairs - 1, p + (1 << 28), 2, 128, 6144, None) == lib.ERR_WORKSPACE
+    assert L.token_tree_fold(p, pairs, p + (1 << 28), 2, 128, 6144, None) not in (
+        lib.ERR_NULL, lib.ERR_SHAPE, lib.ERR_ALIGN, lib.ERR_WORKSPACE, lib.ERR_OVERLAP)
+    assert L.token_tree_fold(p, 1 << 30, p + (1 << 28), 2, 0, 6144, None) == lib.ERR_SHAPE
     assert L.adaln_norm_mod_fwd(p + 2, p, p, p, p, 1, 1, 3072, 1e-6, None) == lib.ERR_ALIGN
     # overlapping output and input is caught before the device check
     assert L.adaln_norm_mod_fwd(p, p + (1 << 20), p, p + (2 << 20), p + (3 << 20), 1, 4, 3072, 1e-6,
