@@ -89,6 +89,36 @@ def test_parity_full(gpu_lib, name):
     assert sum(stats_equal) >= 1, "LayerNorm statistics differ from the oracle in every sample"
 
 
+# The pages' long-sequence gradient shapes over their three seeds (RL-Kernel
+# pull request 538, "Tests": S = 4096 / 6889 / 6032, seeds 0, 127, 2026), one
+# and two samples, through the one-call entry points the bench times.
+LONG_CASES = [(S, B, seed) for S in (6032, 6889) for B in (1, 2) for seed in (0, 127, 2026)]
+
+
+@pytest.mark.parametrize("S,B,seed", LONG_CASES)
+def test_parity_long_sequences_onecall(gpu_lib, S, B, seed):
+    _print_case(f"long_onecall_s{S}", B, S, seed)
+    inp = make_inputs(B, S, seed=seed)
+    d = dev_inputs(inp)
+    from tests.gpu_helpers import to_host
+    gpu = to_host(run_onecall_dev(d))
+    fwd = adaln.forward(inp, want_abs=True)
+    bwd = adaln.backward(inp, fwd, want_abs=True)
+    rep = _gates(inp, gpu, fwd, bwd, {})
+    for k, r in rep.items():
+        print(f"  {k}: {r}")
+    assert all(r["n_fail"] == 0 for r in rep.values()), rep
+    g = bits_to_f32(inp["g"])
+    tree = np.concatenate([token_tree.tree_sum(g * fwd["n"]), token_tree.tree_sum(g)], axis=1)
+    matched = 0
+    for b in range(B):
+        if (gpu["mean"][b].tobytes() == fwd["mean"][b].tobytes() and
+                gpu["rstd"][b].tobytes() == fwd["rstd"][b].tobytes()):
+            assert gpu["d_emb"][b].tobytes() == tree[b].tobytes(), f"sample {b}"
+            matched += 1
+    assert matched >= 1, "LayerNorm statistics differ from the oracle in every sample"
+
+
 def test_parity_large_batch_sampled(gpu_lib):
     """B = 64, S = 1024 (65,536 rows), in the same launch configuration as the
     bench: per-sample outputs of samples 0, 31, 63 against the oracle run on
