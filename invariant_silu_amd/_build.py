@@ -21,6 +21,11 @@ LIB_NAME = "libadaln.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
+# measurement helpers for bench.py (cache flush, streaming copy): a library of
+# their own, not part of the operator's
+BENCH_SOURCE = "bench_util.hip"
+BENCH_LIB_PATH = os.path.join(PKG, "libadaln_bench.so")
+
 SOURCES = ["api.cpp", "fwd.hip", "norm_bwd.hip", "site.hip", "proj_bwd.hip", "proj_out.hip", "token_tree.hip",
            "fp32.hip", "selftest.hip"]
 
@@ -61,16 +66,18 @@ def build(verbose: bool = True) -> str:
     objdir = os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        list(ex.map(_compile, SOURCES, objs))
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-fno-gpu-rdc", *objs, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
-    if verbose:
-        print(f"built {LIB_PATH}")
+    bench_obj = os.path.join(objdir, os.path.splitext(BENCH_SOURCE)[0] + ".o")
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + 1)) as ex:
+        list(ex.map(_compile, SOURCES + [BENCH_SOURCE], objs + [bench_obj]))
+    for out, ins in ((LIB_PATH, objs), (BENCH_LIB_PATH, [bench_obj])):
+        tmp = out + ".tmp"
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-fno-gpu-rdc", *ins, "-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stderr}")
+        os.replace(tmp, out)
+        if verbose:
+            print(f"built {out}")
     return LIB_PATH
 
 
