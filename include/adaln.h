@@ -49,7 +49,7 @@ extern "C" {
 
 typedef uint16_t adaln_bf16;
 
-#define ADALN_ABI_VERSION 10
+#define ADALN_ABI_VERSION 11
 
 enum adaln_status {
   ADALN_OK = 0,
@@ -59,8 +59,12 @@ enum adaln_status {
   ADALN_ERR_DEVICE = -4,     /* current device is not gfx950 / no HIP device       */
   ADALN_ERR_WORKSPACE = -5,  /* ws_bytes < adaln_workspace_bytes(...)             */
   ADALN_ERR_OVERLAP = -6,    /* an output overlaps an input, output or workspace  */
-  ADALN_ERR_LAUNCH = -7      /* a kernel launch failed (hipGetLastError)          */
+  ADALN_ERR_LAUNCH = -7,     /* a kernel launch failed (hipGetLastError)          */
+  ADALN_ERR_SCRATCH = -8     /* the problem needs more than the no-alloc scratch   */
 };
+
+/* Size of the fixed device array behind adaln_norm_mod_bwd_noalloc (per GPU). */
+#define ADALN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 enum adaln_op {
   ADALN_OP_PROJ_FWD = 1,
@@ -355,6 +359,25 @@ int adaln_fwd_proj_out(const adaln_bf16* temb, const adaln_bf16* W, const adaln_
  * objects; no device memory. */
 int adaln_timing_begin(int n, int stride);
 int adaln_timing_end(float* ms, int n);
+
+/* adaln_norm_mod_bwd for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Arguments, results and kernels are adaln_norm_mod_bwd's (the same
+ * bytes); there is no workspace argument: the level-0 pairs of the token tree
+ * live in a fixed file-scope device array of ADALN_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) that every GPU the library runs on holds until the process ends.
+ * The call allocates nothing; its first call on a device looks up that
+ * device's copy of the array (hipGetSymbolAddress) and keeps the address.
+ * Limit: adaln_workspace_bytes(ADALN_OP_NORM_MOD_BWD, B, S, D) <= 64 MiB, i.e.
+ * B * ceil(S / 32) <= 1365 tiles (B = 1: S <= 43680; B = 4: S <= 10912);
+ * larger problems return ADALN_ERR_SCRATCH before anything is launched.
+ * Nothing in the array needs to start at zero (every byte read is written
+ * earlier in the same call).  All calls on one GPU share its array: calls
+ * that overlap in time on one GPU (two streams, or two host threads) race on
+ * it and must be ordered by the caller. */
+int adaln_norm_mod_bwd_noalloc(const adaln_bf16* gout, const adaln_bf16* x, const float* mean,
+                               const float* rstd, const adaln_bf16* emb, adaln_bf16* dx, float* d_emb,
+                               int64_t B, int64_t S, int64_t D, void* stream);
 
 /* Static description of a status code. */
 const char* adaln_strerror(int status);

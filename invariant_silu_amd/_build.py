@@ -27,7 +27,7 @@ BENCH_SOURCE = "bench_util.hip"
 BENCH_LIB_PATH = os.path.join(PKG, "libadaln_bench.so")
 
 SOURCES = ["api.cpp", "fwd.hip", "norm_bwd.hip", "site.hip", "proj_bwd.hip", "proj_out.hip", "token_tree.hip",
-           "fp32.hip", "selftest.hip"]
+           "fp32.hip", "selftest.hip", "noalloc.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fno-gpu-rdc",

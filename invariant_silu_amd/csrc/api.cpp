@@ -251,6 +251,7 @@ const char* adaln_strerror(int status) {
     case ADALN_ERR_WORKSPACE: return "workspace too small";
     case ADALN_ERR_OVERLAP: return "an output overlaps an input, another output or the workspace";
     case ADALN_ERR_LAUNCH: return "kernel launch failed";
+    case ADALN_ERR_SCRATCH: return "problem too large for the fixed scratch array of the no-alloc entry point";
     default: return status > 0 ? "strict-math probe mismatches" : "unknown status";
   }
 }

@@ -15,7 +15,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libadaln.so")
 
 OK = 0
-ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DEVICE, ERR_WORKSPACE, ERR_OVERLAP, ERR_LAUNCH = range(-1, -8, -1)
+ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DEVICE, ERR_WORKSPACE, ERR_OVERLAP, ERR_LAUNCH, ERR_SCRATCH = range(-1, -9, -1)
 (OP_PROJ_FWD, OP_NORM_MOD_BWD, OP_PROJ_BWD, OP_TOKEN_TREE_SUM, OP_BWD, OP_BWD_F32, OP_RESIDUAL_BWD,
  OP_PROJ_OUT_BWD, OP_PROJ_OUT_FWD, OP_FWD_PROJ_OUT) = range(1, 11)
 
@@ -23,6 +23,7 @@ EXPORTS = ("adaln_fwd", "adaln_bwd", "adaln_fwd_f32", "adaln_bwd_f32", "adaln_re
            "adaln_site_fwd", "adaln_site_bwd",
            "adaln_proj_out_fwd", "adaln_proj_out_bwd", "adaln_fwd_proj_out", "adaln_proj_fwd", "adaln_norm_mod_fwd", "adaln_norm_mod_bwd", "adaln_proj_bwd",
            "token_tree_sum", "adaln_norm_mod_bwd_dx", "adaln_norm_mod_bwd_tiles", "token_tree_fold",
+           "adaln_norm_mod_bwd_noalloc",
            "adaln_workspace_bytes", "adaln_selftest", "adaln_strerror", "adaln_timing_begin",
            "adaln_timing_end",
            "adaln_abi_version")
@@ -50,6 +51,7 @@ _SIGS = {
     "adaln_norm_mod_bwd_dx": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "adaln_norm_mod_bwd_tiles": ([_P, _P, _P, _P, _P, _SZ, _I64, _I64, _I64, _P], ctypes.c_int),
     "token_tree_fold": ([_P, _SZ, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "adaln_norm_mod_bwd_noalloc": ([_P] * 7 + [_I64, _I64, _I64, _P], ctypes.c_int),
     "adaln_workspace_bytes": ([ctypes.c_int, _I64, _I64, _I64], _SZ),
     "adaln_selftest": ([], ctypes.c_int),
     "adaln_timing_begin": ([ctypes.c_int, ctypes.c_int], ctypes.c_int),
