@@ -49,7 +49,7 @@ extern "C" {
 
 typedef uint16_t adaln_bf16;
 
-#define ADALN_ABI_VERSION 11
+#define ADALN_ABI_VERSION 12
 
 enum adaln_status {
   ADALN_OK = 0,
@@ -83,20 +83,20 @@ enum adaln_op {
  *   PROJ_FWD:       H = K (3072), S ignored.  B*K*2 (SiLU activations, used when
  *                   B > 4).
  *   NORM_MOD_BWD:   H = D (3072).  B * ceil(S/32) * 2D * 8 bytes (level-0 pairs).
- *   PROJ_BWD:       H = K (3072), S ignored.  B <= 4: 8*B*K*8 (the fp64 da
- *                   subtrees, 8 per sample and column); B > 4: B*K*2 (SiLU
+ *   PROJ_BWD:       H = K (3072), S ignored.  B <= 4: 32*B*K*8 (the fp64 da
+ *                   subtrees, 32 per sample and column); B > 4: B*K*2 (SiLU
  *                   activations).
  *   TOKEN_TREE_SUM: B * ceil(S/32) * ceil(H/64) * 64 * 8 bytes (level-0 pairs).
  *   BWD:            H = D (3072).  NORM_MOD_BWD + PROJ_BWD, in that order.
  *   BWD_F32:        H = D (3072).  NORM_MOD_BWD + B*K*4 (fp32 activations),
- *                   then for B <= 4 8*B*K*8 (the fp64 da subtrees).
+ *                   then for B <= 4 32*B*K*8 (the fp64 da subtrees).
  *   RESIDUAL_BWD:   H = D (3072).  B * ceil(S/32) * 3D * 8 bytes (level-0 pairs).
  *   PROJ_OUT_BWD:   H = K (3072), T = B * S tokens (T <= 65535 * 512; only the
  *                   product is checked, so B = 1, S = T is fine).
- *                   C * 64 * K * 4 bytes (dWp partials) + C * 64 * 8 (dbp
- *                   partials), C = ceil(T / 512).
- *   PROJ_OUT_FWD:   H = K (3072), T = B * S tokens.  4 * T * 64 * 4 bytes (the
- *                   K quarters' partial sums).
+ *                   C * 64 * K * 8 bytes (fp64 dWp partials) + C * 64 * 8
+ *                   (dbp partials), C = ceil(T / 512).
+ *   PROJ_OUT_FWD:   H = K (3072), T = B * S tokens.  256 bytes (nothing is
+ *                   kept there; the parts of each sum meet on chip).
  *   FWD_PROJ_OUT:   H = D (3072), B and S within the modulation's limits.
  *                   PROJ_FWD + PROJ_OUT_FWD (T = B * S), in that order.
  * Each region is padded to 256 bytes. */
@@ -182,7 +182,7 @@ int token_tree_fold(const void* part, size_t part_bytes, float* out, int64_t B, 
  *   each) added pairwise in leaf order.  B <= 4 runs on the vector units, B > 4 on the fp64 matrix
  *   cores: the same bits either way.
  *   ws: adaln_workspace_bytes(ADALN_OP_PROJ_BWD, B, 1, K) bytes (B <= 4: the
- *   sums of leaves 16g .. 16g + 15 for g = 0 .. 7, added pairwise by a second
+ *   sums of leaves 4g .. 4g + 3 for g = 0 .. 31, added pairwise by a second
  *   launch; B > 4: a). */
 int adaln_proj_bwd(const float* d_emb, const adaln_bf16* temb, const adaln_bf16* W,
                    adaln_bf16* dW, adaln_bf16* db, adaln_bf16* dtemb, void* ws, size_t ws_bytes,
@@ -307,14 +307,15 @@ int adaln_site_bwd(const adaln_bf16* g_out, const adaln_bf16* g_h, const adaln_b
  *   [T, K] bf16 (out) = bf16(sum_o d_lat_to W_ok), dW [O, K] bf16 (out) =
  *   bf16(sum_t d_lat_to out_tk), db [O] bf16 (out) = bf16(sum_t d_lat_to);
  *   ws: adaln_workspace_bytes(ADALN_OP_PROJ_OUT_BWD, 1, T, K) bytes.
- * Products run on the bf16 matrix cores (exact products, fp32 accumulation):
- * latent is four fixed chains per output (one per quarter of K) added as
- * ((q0 + q1) + (q2 + q3)) + bias, d_out one chain per output, the same for a
- * token wherever it sits, so per-token outputs do not depend on T; dW and db sum
- * fixed 512-token chunks, then the chunks in ascending order in fp64, so
- * trailing tokens with d_lat = 0 leave them unchanged.  Results agree with the
- * exact sums to within the fp32 accumulation (within 1 bf16 ulp of the
- * correctly rounded result in all but near-tie cases). */
+ * Products run on the fp64 matrix cores: every product of two bf16 numbers is
+ * exact and the sums accumulate in fp64 in fixed orders -- latent as eight
+ * chains over 384 consecutive k each, added ((p0 + p1) + (p2 + p3)) + ((p4 +
+ * p5) + (p6 + p7)), rounded to fp32, plus the bias in fp32; d_out one chain
+ * over the 64 outputs; dW and db over fixed 512-token chunks, the chunks then
+ * added in ascending order -- so every result is the correctly rounded sum
+ * except where the exact sum lies within about 2^-40 of its magnitude from an
+ * fp32 rounding boundary.  A token's results do not depend on T or on where
+ * the token sits; trailing tokens with d_lat = 0 leave dW and db unchanged. */
 int adaln_proj_out_fwd(const adaln_bf16* out, const adaln_bf16* W, const adaln_bf16* bias, adaln_bf16* latent,
                        void* ws, size_t ws_bytes, int64_t T, int64_t K, int64_t O, void* stream);
 int adaln_proj_out_bwd(const adaln_bf16* d_lat, const adaln_bf16* out, const adaln_bf16* W, adaln_bf16* d_out,

@@ -147,9 +147,11 @@ constexpr int64_t kMaxTokens = int64_t{65535} * 512;   // proj_out: token indice
 constexpr int64_t kProjOutO = 64;
 bool tokens_ok(int64_t T) { return T >= 1 && T <= kMaxTokens; }
 size_t ws_proj_out_db_offset(int64_t T) {
-  return pad256(static_cast<size_t>(adaln::proj_out_chunks(T) * kProjOutO * kD * 4));
+  return pad256(static_cast<size_t>(adaln::proj_out_chunks(T) * kProjOutO * kD * 8));
 }
-size_t ws_proj_out_fwd(int64_t T) { return pad256(static_cast<size_t>(4 * T * kProjOutO * 4)); }
+// the forward keeps its partial sums on chip: a nominal 256 bytes (the
+// argument stays, so a later design can use it without an ABI change)
+size_t ws_proj_out_fwd(int64_t) { return 256; }
 size_t ws_proj_out(int64_t T) {
   return ws_proj_out_db_offset(T) + pad256(static_cast<size_t>(adaln::proj_out_chunks(T) * kProjOutO * 8));
 }
@@ -714,7 +716,7 @@ int adaln_proj_out_fwd(const adaln_bf16* out, const adaln_bf16* W, const adaln_b
     return rc;
   if (int rc = check_device()) return rc;
   (void)hipGetLastError();
-  return launched(adaln::launch_proj_out_fwd(out, W, bias, latent, static_cast<float*>(ws), T, as_stream(stream)));
+  return launched(adaln::launch_proj_out_fwd(out, W, bias, latent, T, as_stream(stream)));
 }
 
 int adaln_proj_out_bwd(const adaln_bf16* d_lat, const adaln_bf16* out, const adaln_bf16* W, adaln_bf16* d_out,
@@ -735,7 +737,7 @@ int adaln_proj_out_bwd(const adaln_bf16* d_lat, const adaln_bf16* out, const ada
     return rc;
   if (int rc = check_device()) return rc;
   (void)hipGetLastError();
-  float* part = static_cast<float*>(ws);
+  double* part = static_cast<double*>(ws);
   double* part_db = reinterpret_cast<double*>(static_cast<unsigned char*>(ws) + ws_proj_out_db_offset(T));
   hipEvent_t e0, e1;
   timing_events(&e0, &e1);
@@ -766,11 +768,10 @@ int adaln_fwd_proj_out(const adaln_bf16* temb, const adaln_bf16* W, const adaln_
   (void)hipGetLastError();
   const hipStream_t s = as_stream(stream);
   uint16_t* a = static_cast<uint16_t*>(ws);
-  float* part = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + ws_proj_fwd(B));
   if (int rc = launched(adaln::launch_fwd_stats(temb, W, bias, x, emb, mean, rstd, a, B, S, eps, s))) return rc;
   hipEvent_t e0, e1;
   timing_events(&e0, &e1);
-  return launched(adaln::launch_proj_out_fwd_fused(x, emb, mean, rstd, Wp, bp, latent, part, B, S, s, e0, e1));
+  return launched(adaln::launch_proj_out_fwd_fused(x, emb, mean, rstd, Wp, bp, latent, B, S, s, e0, e1));
 }
 
 int adaln_selftest(void) {

@@ -70,19 +70,19 @@ hipError_t launch_site_bwd(const uint16_t* g_out, const uint16_t* g_h, const uin
                            const float* mean, const float* rstd, ModView mv, uint16_t* d_residual, uint16_t* dx,
                            float* part, int64_t B, int64_t S, hipStream_t s, hipEvent_t ev_start = nullptr,
                            hipEvent_t ev_stop = nullptr);
-// proj_out (3072 -> 64 per token).  Forward part: 4 x T x 64 fp32 (the K
-// quarters' partial sums); backward part: proj_out_chunks(T) x 64 x 3072 fp32,
-// part_db: proj_out_chunks(T) x 64 fp64
+// proj_out (3072 -> 64 per token) on the fp64 matrix cores.  Backward part:
+// proj_out_chunks(T) x 64 x 3072 fp64 (the dWp chunk partials), part_db:
+// proj_out_chunks(T) x 64 fp64
 int64_t proj_out_chunks(int64_t T);
 // latent from x with the final modulation computed on the fly (out is never
 // stored): the same bytes as launch_proj_out_fwd on the modulated output
 hipError_t launch_proj_out_fwd_fused(const uint16_t* x, const uint16_t* emb, const float* mean, const float* rstd,
-                                     const uint16_t* W, const uint16_t* bias, uint16_t* latent, float* part,
-                                     int64_t B, int64_t S, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
+                                     const uint16_t* W, const uint16_t* bias, uint16_t* latent, int64_t B, int64_t S,
+                                     hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 hipError_t launch_proj_out_fwd(const uint16_t* out, const uint16_t* W, const uint16_t* bias, uint16_t* latent,
-                               float* part, int64_t T, hipStream_t s);
+                               int64_t T, hipStream_t s);
 hipError_t launch_proj_out_bwd(const uint16_t* d_lat, const uint16_t* out, const uint16_t* W, uint16_t* d_out,
-                               uint16_t* dW, uint16_t* db, float* part, double* part_db, int64_t T, hipStream_t s,
+                               uint16_t* dW, uint16_t* db, double* part, double* part_db, int64_t T, hipStream_t s,
                                hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 // fp32 storage
 hipError_t launch_silu_f32(const float* temb, float* a, int64_t n, hipStream_t s);

@@ -18,8 +18,8 @@
 // these orders exactly, so no result depends on the batch size or the grid.
 //
 // Kernels:
-//   proj_bwd_small_kernel<NB>  B <= 4: da leaf-group blocks (-> the eight
-//                              16-leaf subtrees of every column) and dW tiles
+//   proj_bwd_small_kernel<NB>  B <= 4: da leaf-group blocks (-> the 32
+//                              4-leaf subtrees of every column) and dW tiles
 //                              (-> dW, db) in one grid
 //   da_finish_kernel<NB>       B <= 4: the subtrees added pairwise (-> dtemb)
 //   da_leaf_f32_kernel<NB>     fp32 storage, B <= 4: the leaf-group blocks alone
@@ -98,19 +98,20 @@ struct Pair<float> {
   }
 };
 
-// da for B <= 4 in two steps.  A leaf-group block (gq, cg) runs the 16
-// leaves 16 gq .. 16 gq + 15 over the 64 columns 64 cg .. 64 cg + 63 of W;
-// thread (leaf 16 gq + tid / 16, column quad tid % 16) holds 4 columns, so
-// one wave load covers 4 rows x 128 contiguous bytes: whole cache lines, and
-// the W stream is spread over 384 blocks.  The block then adds its 16 leaves
-// pairwise in leaf order -- the subtree those leaves form in the 128-leaf
-// pairwise tree -- and writes one fp64 value per (sample, column) to
-// sub[gq][b][col].  da_finish_kernel adds the 8 subtrees pairwise in order
-// (the tree's top three levels): the 128-leaf pairwise tree exactly.
-constexpr int kDaGroupLeaves = 16;
-constexpr int kDaGroups = kDaSlots / kDaGroupLeaves;            // 8
-constexpr int kDaQuadCols = 64;                                 // columns per leaf-group block
-constexpr int kDaQuads = kDaQuadCols / 4;                       // 16 column quads
+// da for B <= 4 in two steps.  A leaf-group block (gq, cg) runs the 4
+// leaves 4 gq .. 4 gq + 3 over the 256 columns 256 cg .. 256 cg + 255 of W;
+// wave w is leaf 4 gq + w and its lane holds column quad lane (4 columns), so
+// one wave load is 512 contiguous bytes of one row of W (a 16-leaf block of 64
+// columns, each wave load 4 rows x 128 bytes, took 2 us longer with W cold in
+// HBM).  The W stream is spread over 384 blocks.  The block then adds its 4
+// leaves pairwise in leaf order -- the subtree those leaves form in the
+// 128-leaf pairwise tree -- and writes one fp64 value per (sample, column) to
+// sub[gq][b][col].  da_finish_kernel adds the 32 subtrees pairwise in order
+// (the tree's top five levels): the 128-leaf pairwise tree exactly.
+constexpr int kDaGroupLeaves = 4;
+constexpr int kDaGroups = kDaSlots / kDaGroupLeaves;            // 32
+constexpr int kDaQuadCols = 256;                                // columns per leaf-group block
+constexpr int kDaQuads = kDaQuadCols / 4;                       // 64 column quads
 constexpr int kDaLeafBlocks = kDaGroups * (kD / kDaQuadCols);   // 384
 static_assert(kDaGroupLeaves * kDaQuads == kThreads, "leaf-group block shape");
 static_assert(kD % kDaQuadCols == 0, "leaf-group columns");
@@ -210,9 +211,8 @@ __device__ __forceinline__ void da_leaf_group(const float* __restrict__ d_emb, c
   accumulate(wa, da_);
   accumulate(wbt, db_);
 
-  // the block's 16 leaves, pairwise in leaf order: ((l0 + l1) + (l2 + l3)) + ...
+  // the block's 4 leaves, pairwise in leaf order: (l0 + l1) + (l2 + l3)
   constexpr int kRow = NB * kDaQuadCols;   // doubles per leaf
-  static_assert(kRow <= kThreads, "one subtree value per thread");
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -226,13 +226,13 @@ __device__ __forceinline__ void da_leaf_group(const float* __restrict__ d_emb, c
     }
     __syncthreads();
   }
-  if (threadIdx.x < kRow) {
-    const int b = threadIdx.x / kDaQuadCols, c = threadIdx.x % kDaQuadCols;
-    sub[(static_cast<int64_t>(gq) * NB + b) * kD + col0 + c] = red[threadIdx.x];
+  for (int i = threadIdx.x; i < kRow; i += kThreads) {
+    const int b = i / kDaQuadCols, c = i % kDaQuadCols;
+    sub[(static_cast<int64_t>(gq) * NB + b) * kD + col0 + c] = red[i];
   }
 }
 
-// da = the 8 subtrees of a (sample, column) added pairwise in order, then
+// da = the 32 subtrees of a (sample, column) added pairwise in order, then
 // dtemb = da * silu'(temb) in the storage type (bf16: one rounding); one
 // thread per (sample, column)
 template <int NB, typename T = uint16_t>

@@ -7,499 +7,403 @@
 //   d_out[t, k]  = bf16(sum_o d_lat[t, o] Wp[o, k])
 //   dWp[o, k]    = bf16(sum_t d_lat[t, o] out[t, k]),  dbp[o] = bf16(sum_t d_lat[t, o])
 //
-// A dense contraction with bf16 operands: every product runs on the bf16
-// matrix cores (v_mfma_f32_16x16x32_bf16: products exact, fp32 accumulation
-// inside the instruction, fp32 accumulator).  A token's results come from the
-// same instruction sequence wherever the token sits in a tile (the unit gives
-// every output position the same arithmetic), so per-token outputs do not
-// depend on the batch.  Sums:
-//   latent: four chains per output, one per quarter of K, each 24
-//           instructions of 32 consecutive k from +0; then ((q0 + q1) +
-//           (q2 + q3)) + bias in fp32 (a second launch) and one bf16 rounding;
-//   d_out:  one chain per output over o in 2 instructions of 32;
-//   dWp:    per fixed chunk of 512 tokens a chain over 16 instructions of 32
-//           tokens, from +0; the chunks added in fp64 in ascending order
-//           (a second launch), then rounded to fp32 and to bf16; dbp the
-//           same with fp64 sums of the chunk's tokens.  Trailing tokens whose
-//           d_lat is zero add exact zeros.
+// A dense contraction, so it runs on the matrix cores -- the fp64 ones
+// (v_mfma_f64_16x16x4f64, a chain of fused multiply-adds): every product of
+// two bf16 numbers is exact in fp64 and the sums accumulate in fp64 in fixed
+// orders, so each result, rounded once to fp32 (then to bf16), is the
+// correctly rounded sum unless the sum sits within about 2^-40 of its size
+// from a rounding boundary.  The bf16 matrix cores were the first design
+// here; their fp32 accumulation inside the instruction left cancelling sums
+// several bf16 ulps from the correctly rounded result.
+//
+// Orders (the same for a token wherever it sits, so per-token results do not
+// depend on T):
+//   latent: eight parts of K (384 consecutive k each), one chain per part,
+//           step s of part p taking k = 384 p + 32 (s / 8) + 8 g + s % 8 for
+//           slots g = 0 .. 3 in order; the parts added as ((p0 + p1) +
+//           (p2 + p3)) + ((p4 + p5) + (p6 + p7)) in fp64, rounded to fp32,
+//           bias added in fp32, one bf16 rounding;
+//   d_out:  one chain per output over o, step s taking o = 16 g + s;
+//   dWp:    per fixed chunk of 512 tokens one chain over the chunk's tokens
+//           in ascending order (4 per step), from +0; the chunks added in
+//           fp64 in ascending order (a second launch), then rounded to fp32
+//           and to bf16; dbp the same with fp64 sums of the chunk's tokens.
+//           Trailing tokens whose d_lat is zero add exact zeros.
 #include <hip/hip_ext.h>
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "mfma.hpp"
 
 namespace adaln {
 
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
-                                                 0, 0, 0);
-}
-
 constexpr int kO = 64;                 // latent channels
 constexpr int kChunk = 512;            // tokens per dWp partial
-constexpr int kRound = 64;             // tokens staged in LDS at a time
-constexpr int kLdsStride = 72;         // bf16 elements per transposed LDS row (64 + pad; 144 bytes)
-constexpr int kLdsStride2 = kLdsStride / 2;
 
 // the last valid row for t >= T (T >= 1)
 __device__ __forceinline__ int64_t clamp_row(int64_t t, int64_t T) { return t < T ? t : T - 1; }
 
-__device__ __forceinline__ uint32_t lo16(uint32_t w) { return w & 0xffffu; }
-__device__ __forceinline__ uint32_t hi16(uint32_t w) { return w >> 16; }
+// element e (0 .. 7) of 8 consecutive bf16 in a 16-byte word, widened to fp64
+__device__ __forceinline__ double el8(const uint4& v, int e) {
+  const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+  return bf_half64(w, e & 1);
+}
+
+// ---- forward ---------------------------------------------------------------
+// Block: 16 tokens (t0 ..) x all 64 outputs, 8 waves; wave p runs part p of K
+// for the four 16-output tiles.  The block's 16 rows of out sit in LDS (rows
+// padded by 16 bytes); lane (r, g) takes A = out[t0 + r][k] from there and
+// B = Wp[16 j + r][k] from memory (Wp is 384 KB: it stays in L2), 16 bytes
+// per 8 steps each, one group of 8 steps ahead.  The parts then meet in LDS.
+// Tokens past T use row T - 1 and are never stored.
+constexpr int kFT = 16;                      // tokens per block
+constexpr int kParts = 8;                    // parts of K, one per wave
+constexpr int kPK = kD / kParts;             // 384
+constexpr int kPGroups = kPK / 32;           // 12 groups of 8 steps
+constexpr int kARowDw = kD / 2 + 4;          // LDS dwords per staged row (1540)
+constexpr int kFwdThreads = 64 * kParts;     // 512
+constexpr size_t kFwdLds = sizeof(uint32_t) * kFT * kARowDw;   // 98.6 KB
+static_assert(sizeof(double) * kParts * kFT * kO <= kFwdLds, "the parts' results reuse the staged rows");
+
+// The chains of part p over the staged rows; acc[j] = output tile j.
+__device__ __forceinline__ void fwd_chains(const uint32_t* __restrict__ a_lds, const uint16_t* __restrict__ W,
+                                           int p, f64x4_t (&acc)[4]) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const uint16_t* wrow = W + static_cast<int64_t>(r) * kD + kPK * p + 8 * g;
+  const uint32_t* arow = a_lds + r * kARowDw + (kPK * p + 8 * g) / 2;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+  uint4 wb[2][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) wb[0][j] = ld16(wrow + static_cast<int64_t>(16 * j) * kD);
+#pragma unroll
+  for (int q = 0; q < kPGroups; ++q) {
+    if (q + 1 < kPGroups) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wb[(q + 1) & 1][j] = ld16(wrow + static_cast<int64_t>(16 * j) * kD + 32 * (q + 1));
+    }
+    const uint4 av = *reinterpret_cast<const uint4*>(arow + 16 * q);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double a = el8(av, e);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = mfma_f64(a, el8(wb[q & 1][j], e), acc[j]);
+    }
+  }
+}
+
+// The parts' results into LDS (the staged rows are dead by then), then
+// latent for the block's tokens: 2 consecutive outputs per thread.
+__device__ __forceinline__ void fwd_combine(uint32_t* lds, const f64x4_t (&acc)[4], const uint16_t* __restrict__ bias,
+                                            uint16_t* __restrict__ latent, int64_t t0, int64_t T) {
+  const int p = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  double* cmb = reinterpret_cast<double*>(lds);   // [part][token][output]
+  __syncthreads();   // every wave is done reading the staged rows
+  // lane holds token g + 4 v, output 16 j + r of tile j
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) cmb[(p * kFT + g + 4 * v) * kO + 16 * j + r] = acc[j][v];
+  __syncthreads();
+  const int i = threadIdx.x >> 5, o = 2 * (threadIdx.x & 31);   // token i, outputs o, o + 1
+  float res[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    double c[kParts];
+#pragma unroll
+    for (int q = 0; q < kParts; ++q) c[q] = cmb[(q * kFT + i) * kO + o + h];
+    const double s = ((c[0] + c[1]) + (c[2] + c[3])) + ((c[4] + c[5]) + (c[6] + c[7]));
+    res[h] = static_cast<float>(s) + bf16_to_f32(bias[o + h]);
+  }
+  if (t0 + i < T) *reinterpret_cast<uint32_t*>(latent + (t0 + i) * kO + o) = pack_bf16x2(res[0], res[1]);
+}
+
+__global__ __launch_bounds__(kFwdThreads) void proj_out_fwd_kernel(const uint16_t* __restrict__ out,
+                                                                  const uint16_t* __restrict__ W,
+                                                                  const uint16_t* __restrict__ bias,
+                                                                  uint16_t* __restrict__ latent, int64_t T) {
+  __shared__ __align__(16) uint32_t lds[kFwdLds / 4];
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kFT;
+  // stage the 16 rows: 16 x 384 chunks of 16 bytes, 12 per thread, all in
+  // flight before the first LDS write
+  constexpr int kChunksPerRow = kD / 8;
+  constexpr int kIt = kFT * kChunksPerRow / kFwdThreads;
+  uint4 v[kIt];
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    const int q = threadIdx.x + kFwdThreads * it;
+    v[it] = ld16(out + clamp_row(t0 + q / kChunksPerRow, T) * kD + 8 * (q % kChunksPerRow));
+  }
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    const int q = threadIdx.x + kFwdThreads * it;
+    *reinterpret_cast<uint4*>(lds + (q / kChunksPerRow) * kARowDw + 4 * (q % kChunksPerRow)) = v[it];
+  }
+  __syncthreads();
+  f64x4_t acc[4];
+  fwd_chains(lds, W, threadIdx.x >> 6, acc);
+  fwd_combine(lds, acc, bias, latent, t0, T);
+}
+
+// The same with the final modulation computed on the fly: the block's rows
+// of out, out[t][k] = bf16(((x - mean) * rstd) * bf16(1 + scale) + shift)
+// with t's sample's (scale | shift) from emb -- the final modulation's
+// expression, operation for operation -- go straight into LDS, so out never
+// reaches HBM.
+__global__ __launch_bounds__(kFwdThreads) void proj_out_fused_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ emb, const float* __restrict__ mean,
+    const float* __restrict__ rstd, const uint16_t* __restrict__ W, const uint16_t* __restrict__ bias,
+    uint16_t* __restrict__ latent, int64_t T, int64_t S) {
+  __shared__ __align__(16) uint32_t lds[kFwdLds / 4];
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kFT;
+  constexpr int kChunksPerRow = kD / 8;
+  constexpr int kIt = kFT * kChunksPerRow / kFwdThreads;
+#pragma unroll 4
+  for (int it = 0; it < kIt; ++it) {
+    const int q = threadIdx.x + kFwdThreads * it;
+    const int row = q / kChunksPerRow, c = q % kChunksPerRow;
+    const int64_t t = clamp_row(t0 + row, T);
+    // token index and sample fit 32 bits (T <= 65535 * 512)
+    const int64_t b = static_cast<uint32_t>(t) / static_cast<uint32_t>(S);
+    const uint4 xv = ld16(x + t * kD + 8 * c);
+    const uint4 sc = ld16(emb + b * kN + 8 * c);
+    const uint4 sh = ld16(emb + b * kN + kD + 8 * c);
+    const float mu = mean[t], rs = rstd[t];
+    float xf[8], sf[8], hf[8], o[8];
+    unpack8(xv, xf);
+    unpack8(sc, sf);
+    unpack8(sh, hf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float n = (xf[e] - mu) * rs;
+      o[e] = n * round_bf16(1.0f + sf[e]) + hf[e];
+    }
+    *reinterpret_cast<uint4*>(lds + row * kARowDw + 4 * c) = pack8(o);
+  }
+  __syncthreads();
+  f64x4_t acc[4];
+  fwd_chains(lds, W, threadIdx.x >> 6, acc);
+  fwd_combine(lds, acc, bias, latent, t0, T);
+}
+
+// ---- backward ------------------------------------------------------------------
+// One launch, two roles of 512 threads: blocks [0, dw_blocks) the dWp chunk
+// partials, the rest d_out.
+constexpr int kBwdThreads = 512;
+constexpr int kWtStride2 = 36;               // dwords per LDS row of the transposed Wp slab (64 + 8 bf16)
+constexpr int kDxCols = 256;                 // d_out columns per block
+constexpr int kDxTokens = 64;                // d_out tokens per block
+constexpr int kDwCols = 128;                 // dWp columns per block
+constexpr int kDwColBlocks = kD / kDwCols;   // 24
+constexpr int kRound = 64;                   // tokens staged per round
+constexpr int kStRow2 = kDwCols / 2 + 4;     // dwords per staged token row of out (128 + 8 bf16)
+constexpr int kDlRow2 = kO / 2 + 4;          // dwords per staged token row of d_lat (64 + 8 bf16)
+constexpr size_t kBwdLds = sizeof(uint32_t) * kDxCols * kWtStride2;   // 36 KB
+static_assert(sizeof(uint32_t) * kRound * (kStRow2 + kDlRow2) <= kBwdLds, "dWp rounds fit the shared buffer");
+static_assert(sizeof(uint16_t) * 8 * 16 * 128 <= kBwdLds, "d_out staging fits the shared buffer");
 
 // two rows' 8 consecutive elements -> 8 dwords (element e of row 0 | of row 1 << 16)
 __device__ __forceinline__ void interleave8(const uint4& r0, const uint4& r1, uint32_t (&o)[8]) {
   const uint32_t a[4] = {r0.x, r0.y, r0.z, r0.w}, b[4] = {r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    o[2 * i] = lo16(a[i]) | (lo16(b[i]) << 16);
-    o[2 * i + 1] = hi16(a[i]) | (hi16(b[i]) << 16);
+    o[2 * i] = (a[i] & 0xffffu) | (b[i] << 16);
+    o[2 * i + 1] = (a[i] >> 16) | (b[i] & 0xffff0000u);
   }
 }
 
-// ---- forward ---------------------------------------------------------------
-// Partials: block = 64 tokens (t0 ..) x one quarter of K (kq: k in [768 kq,
-// 768 kq + 768)), 4 waves; wave w owns outputs 16 w .. + 15 and holds its B
-// operand, Wp[16 w + r][768 kq + 32 s + 8 g .. + 7] for the 24 steps s, in
-// registers.  The block stages its 64 x 768 slice of out in LDS once (rows
-// padded to 1552 bytes: 16 lanes reading 16 rows hit distinct banks); token
-// tile tt's A operand is out[t0 + 16 tt + r][same k].  Each partial is one
-// chain of 24 instructions from +0.  Tokens past T are staged as zeros and
-// never stored.  The quarters' partials go to part[kq][t][o].
-constexpr int kQuarters = 4;
-constexpr int kQK = kD / kQuarters;            // 768
-constexpr int kQSteps = kQK / 32;              // 24
-constexpr int kFwdTokens = 64;
-constexpr int kARow32 = (kQK * 2 + 16) / 4;    // 388 dwords per staged row
-
-// Zero the staged rows of tokens t >= T (the last block only), after the
-// block's own writes of those rows.
-template <int kRows>
-__device__ __forceinline__ void zero_tail_rows(uint32_t* as, int64_t t0, int64_t T) {
-  if (t0 + kRows <= T) return;
-  constexpr int kChunksPerRow = kQK / 8;
-  for (int q = threadIdx.x; q < kRows * kChunksPerRow; q += 256) {   // the staging loops' thread mapping
-    const int row = q / kChunksPerRow;
-    if (t0 + row >= T)
-      *reinterpret_cast<uint4*>(as + row * kARow32 + 4 * (q % kChunksPerRow)) = make_uint4(0u, 0u, 0u, 0u);
-  }
-}
-
-__global__ __launch_bounds__(256) void proj_out_fwd_part_kernel(const uint16_t* __restrict__ out,
-                                                                const uint16_t* __restrict__ W,
-                                                                float* __restrict__ part, int64_t T) {
-  __shared__ __align__(16) uint32_t as[kFwdTokens * kARow32];   // 97 KB
-  const int kq = blockIdx.y;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kFwdTokens;
-  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  const int lane = threadIdx.x & 63;
-  const int r = lane & 15, g = lane >> 4;
-  // stage: 64 rows x 96 chunks of 16 bytes, consecutive threads on consecutive chunks
-  const uint16_t* abase = out + kq * kQK;
-  constexpr int kChunksPerRow = kQK / 8;   // 96
-  constexpr int kIt = kFwdTokens * kChunksPerRow / 256;
-  uint4 av[kIt];
-#pragma unroll
-  for (int it = 0; it < kIt; ++it) {
-    const int q = threadIdx.x + 256 * it;
-    const int row = q / kChunksPerRow, c = q % kChunksPerRow;
-    // rows past T load row T - 1 (in bounds) and are zeroed after the LDS
-    // writes: a load under a branch, or a select on its value (which the
-    // compiler turns into one), makes it wait for every load issued before
-    av[it] = ld16(abase + clamp_row(t0 + row, T) * kD + 8 * c);
-  }
-  // all 24 loads stay in flight before the first LDS write (one block per CU:
-  // the slice's bytes in flight are what keeps HBM busy)
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int it = 0; it < kIt; ++it) {
-    const int q = threadIdx.x + 256 * it;
-    const int row = q / kChunksPerRow, c = q % kChunksPerRow;
-    *reinterpret_cast<uint4*>(as + row * kARow32 + 4 * c) = av[it];
-  }
-  zero_tail_rows<kFwdTokens>(as, t0, T);
-  uint4 wv[kQSteps];
-  const uint16_t* wrow = W + static_cast<int64_t>(16 * wave + r) * kD + kq * kQK + 8 * g;
-#pragma unroll
-  for (int st = 0; st < kQSteps; ++st) wv[st] = ld16(wrow + 32 * st);
-  __syncthreads();
-  f32x4_t acc[kFwdTokens / 16];
-#pragma unroll
-  for (int tt = 0; tt < kFwdTokens / 16; ++tt) {
-    acc[tt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    const uint32_t* arow = as + (16 * tt + r) * kARow32 + 4 * g;
-#pragma unroll
-    for (int st = 0; st < kQSteps; ++st)
-      acc[tt] = mfma_bf16(*reinterpret_cast<const uint4*>(arow + 16 * st), wv[st], acc[tt]);
-  }
-  // lane holds tokens t0 + 16 tt + 4 g + v, output 16 w + r
-  float* pq = part + static_cast<int64_t>(kq) * T * kO;
-#pragma unroll
-  for (int tt = 0; tt < kFwdTokens / 16; ++tt)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t t = t0 + 16 * tt + 4 * g + v;
-      if (t < T) pq[t * kO + 16 * wave + r] = acc[tt][v];
-    }
-}
-
-// The same partials with the final modulation computed on the fly: the
-// block's slice of out, out[t][k] = bf16(((x - mean) * rstd) * bf16(1 + scale)
-// + shift) with t's sample's (scale | shift) from emb -- the final
-// modulation's expression, operation for operation -- goes straight into
-// LDS, so out never reaches HBM.  32 tokens per block.
-// kOneSample (S a multiple of 32: a block's tokens share one sample): the
-// sample's slice of scale and shift is staged once in LDS, which frees the
-// registers to issue Wp's quarter (from L2) ahead of x, so it has arrived by
-// the time the chains start.  Otherwise each row looks its sample up.
-constexpr int kFuseTokens = 32;
-
-template <bool kOneSample>
-__global__ __launch_bounds__(256) void proj_out_fused_part_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ emb, const float* __restrict__ mean,
-    const float* __restrict__ rstd, const uint16_t* __restrict__ W, float* __restrict__ part, int64_t T,
-    int64_t S) {
-  __shared__ __align__(16) uint32_t as[kFuseTokens * kARow32];   // 48.5 KB
-  const int kq = blockIdx.y;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kFuseTokens;
-  constexpr int kChunksPerRow = kQK / 8;                          // 96
-  constexpr int kIt = kFuseTokens * kChunksPerRow / 256;          // 12
-  const int kbase = kq * kQK;
-  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  const int lane = threadIdx.x & 63;
-  const int r = lane & 15, g = lane >> 4;
-  const uint16_t* wrow = W + static_cast<int64_t>(16 * wave + r) * kD + kbase + 8 * g;
-  uint4 wv[kQSteps];
-  uint4 xv[kIt];
-  float mu[kIt], rs[kIt];
-  if constexpr (kOneSample) {
-    // the sample's bf16(1 + scale) and shift slices as fp32, 8 columns per
-    // 16-byte chunk pair: threads [0, 128) take chunk tid of scale, threads
-    // [128, 256) chunk tid - 128 of shift; chunks past 95 reload chunk 95 into
-    // spare entries (every thread loads and stores: no branch around a load)
-    __shared__ float4 m_lds[2 * 2 * 128];
-    const int64_t b = static_cast<uint32_t>(t0) / static_cast<uint32_t>(S);
-    const int half = threadIdx.x >> 7, ec = threadIdx.x & 127;
-    const uint4 ev = ld16(emb + b * kN + half * kD + kbase + 8 * min(ec, kChunksPerRow - 1));
-#pragma unroll
-    for (int st = 0; st < kQSteps; ++st) wv[st] = ld16(wrow + 32 * st);
-#pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      const int q = threadIdx.x + 256 * it;
-      const int64_t t = clamp_row(t0 + q / kChunksPerRow, T);
-      xv[it] = ld16(x + t * kD + kbase + 8 * (q % kChunksPerRow));
-      mu[it] = mean[t];
-      rs[it] = rstd[t];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    {
-      float f[8];
-      unpack8(ev, f);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = half ? f[e] : round_bf16(1.0f + f[e]);
-      m_lds[2 * threadIdx.x] = make_float4(f[0], f[1], f[2], f[3]);
-      m_lds[2 * threadIdx.x + 1] = make_float4(f[4], f[5], f[6], f[7]);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      const int q = threadIdx.x + 256 * it;
-      const int row = q / kChunksPerRow, c = q % kChunksPerRow;
-      float xf[8], o[8];
-      unpack8(xv[it], xf);
-      const float4 m0 = m_lds[2 * c], m1 = m_lds[2 * c + 1];
-      const float4 h0 = m_lds[256 + 2 * c], h1 = m_lds[256 + 2 * c + 1];
-      const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-      const float hh[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float n = (xf[e] - mu[it]) * rs[it];
-        o[e] = n * mm[e] + hh[e];
-      }
-      *reinterpret_cast<uint4*>(as + row * kARow32 + 4 * c) = pack8(o);
-    }
-    zero_tail_rows<kFuseTokens>(as, t0, T);
-  } else {
-    uint4 sc[kIt], sh[kIt];
-#pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      const int q = threadIdx.x + 256 * it;
-      const int row = q / kChunksPerRow, c = q % kChunksPerRow;
-      const int64_t t = clamp_row(t0 + row, T);
-      // token index and sample fit 32 bits (T <= 65535 * 512)
-      const int64_t b = static_cast<uint32_t>(t) / static_cast<uint32_t>(S);
-      xv[it] = ld16(x + t * kD + kbase + 8 * c);
-      sc[it] = ld16(emb + b * kN + kbase + 8 * c);
-      sh[it] = ld16(emb + b * kN + kD + kbase + 8 * c);
-      mu[it] = mean[t];
-      rs[it] = rstd[t];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      const int q = threadIdx.x + 256 * it;
-      const int row = q / kChunksPerRow, c = q % kChunksPerRow;
-      float xf[8], sf[8], hf[8], o[8];
-      unpack8(xv[it], xf);
-      unpack8(sc[it], sf);
-      unpack8(sh[it], hf);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float n = (xf[e] - mu[it]) * rs[it];
-        o[e] = n * round_bf16(1.0f + sf[e]) + hf[e];
-      }
-      *reinterpret_cast<uint4*>(as + row * kARow32 + 4 * c) = pack8(o);
-    }
-    zero_tail_rows<kFuseTokens>(as, t0, T);
-#pragma unroll
-    for (int st = 0; st < kQSteps; ++st) wv[st] = ld16(wrow + 32 * st);
-  }
-  __syncthreads();
-  f32x4_t acc[kFuseTokens / 16];
-#pragma unroll
-  for (int tt = 0; tt < kFuseTokens / 16; ++tt) {
-    acc[tt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    const uint32_t* arow = as + (16 * tt + r) * kARow32 + 4 * g;
-#pragma unroll
-    for (int st = 0; st < kQSteps; ++st)
-      acc[tt] = mfma_bf16(*reinterpret_cast<const uint4*>(arow + 16 * st), wv[st], acc[tt]);
-  }
-  float* pq = part + static_cast<int64_t>(kq) * T * kO;
-#pragma unroll
-  for (int tt = 0; tt < kFuseTokens / 16; ++tt)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t t = t0 + 16 * tt + 4 * g + v;
-      if (t < T) pq[t * kO + 16 * wave + r] = acc[tt][v];
-    }
-}
-
-// latent = bf16(((q0 + q1) + (q2 + q3)) + bias) per element, in fp32
-__global__ __launch_bounds__(256) void proj_out_fwd_combine_kernel(const float* __restrict__ part,
-                                                                   const uint16_t* __restrict__ bias,
-                                                                   uint16_t* __restrict__ latent, int64_t T) {
-  // 4 consecutive outputs of one token per thread (64 outputs per token)
-  const int64_t n = T * kO;
-  const int64_t i = 4 * (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x);
-  if (i >= n) return;
-  const float4 q0 = *reinterpret_cast<const float4*>(part + i);
-  const float4 q1 = *reinterpret_cast<const float4*>(part + n + i);
-  const float4 q2 = *reinterpret_cast<const float4*>(part + 2 * n + i);
-  const float4 q3 = *reinterpret_cast<const float4*>(part + 3 * n + i);
-  const uint2 bw = *reinterpret_cast<const uint2*>(bias + i % kO);
-  const float l0 = ((q0.x + q1.x) + (q2.x + q3.x)) + bf_lo(bw.x);
-  const float l1 = ((q0.y + q1.y) + (q2.y + q3.y)) + bf_hi(bw.x);
-  const float l2 = ((q0.z + q1.z) + (q2.z + q3.z)) + bf_lo(bw.y);
-  const float l3 = ((q0.w + q1.w) + (q2.w + q3.w)) + bf_hi(bw.y);
-  *reinterpret_cast<uint2*>(latent + i) = make_uint2(pack_bf16x2(l0, l1), pack_bf16x2(l2, l3));
-}
-
-// ---- backward: d_out ---------------------------------------------------------
-// Block: 64 tokens (wave w: tokens t0 + 16 w ..) x 256 columns (k0 ..).  Wp's
-// 64 x 256 slab is staged in LDS transposed (row k holds the 64 outputs'
-// weights).  Output tiles come in pairs (m, h = 0, 1) over 32 columns: tile
-// row i = 4 q + v is column 32 m + 8 q + 4 h + v, so A = the slab's rows for
-// those columns (outputs 8 g .. + 7, then 32 + 8 g ..), B = d_lat[t][8 g ..]
-// (the same outputs), and a lane holds 8 consecutive columns of one token
-// after the pair: one 16-byte store.
-constexpr int kDxCols = 256;
-
-// d_out for 64 tokens (token block bx) x 256 columns (column block by)
+// d_out for 64 tokens (tb ..) x 256 columns (k0 ..).  Wp's 64 x 256 slab is
+// staged transposed (row k holds the 64 outputs' weights).  Wave w: token
+// tile w % 4, columns 128 (w / 4) .. + 127 as 8 column tiles run side by
+// side.  Lane (r, g): A = d_lat[t][16 g + s] (its 16 values loaded once), B =
+// the slab's row of column 16 kt + r at outputs 16 g .. + 15 (32 bytes per
+// tile).  The results go through LDS so each lane stores 16 contiguous bytes.
 __device__ __forceinline__ void dx_block(const uint16_t* __restrict__ d_lat, const uint16_t* __restrict__ W,
-                                         uint16_t* __restrict__ d_out, int64_t T, int64_t bx, int by,
-                                         uint32_t* wt) {
-  const int k0 = by * kDxCols;
-  // stage: row pair p (outputs 2p, 2p + 1) x column octet c8: 32 x 32 items
+                                         uint16_t* __restrict__ d_out, int64_t T, int64_t tb, int k0,
+                                         uint32_t* lds) {
+  // stage: row pair p (outputs 2 p, 2 p + 1) x column octet c8: 32 x 32 items, 2 per thread
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int item = threadIdx.x + 256 * it;
+  for (int it = 0; it < 2; ++it) {
+    const int item = threadIdx.x + kBwdThreads * it;
     const int p = item % 32, c8 = item / 32;
     const uint4 r0 = ld16(W + static_cast<int64_t>(2 * p) * kD + k0 + 8 * c8);
     const uint4 r1 = ld16(W + static_cast<int64_t>(2 * p + 1) * kD + k0 + 8 * c8);
     uint32_t o[8];
     interleave8(r0, r1, o);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) wt[(8 * c8 + e) * kLdsStride2 + p] = o[e];
+    for (int e = 0; e < 8; ++e) lds[(8 * c8 + e) * kWtStride2 + p] = o[e];
   }
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
-  const int64_t tw = bx * 64 + 16 * wave;
-  const int64_t tr = tw + r < T ? tw + r : T - 1;
-  const uint4 b0 = ld16(d_lat + tr * kO + 8 * g);
-  const uint4 b1 = ld16(d_lat + tr * kO + 32 + 8 * g);
+  const int tt = wave & 3, half = wave >> 2;
+  const int64_t tw = tb + 16 * tt;
+  const int64_t tr = clamp_row(tw + r, T);
+  const uint4 a0 = ld16(d_lat + tr * kO + 16 * g);
+  const uint4 a1 = ld16(d_lat + tr * kO + 16 * g + 8);
   __syncthreads();
-  const bool store = tw + r < T;
-  uint16_t* orow = d_out + tr * kD + k0 + 8 * g;   // stored only when tw + r < T
-#pragma unroll 2
-  for (int m = 0; m < kDxCols / 32; ++m) {
-    f32x4_t acc[2];
+  f64x4_t acc[8];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      // A row r of tile (m, h): column 32 m + 8 (r / 4) + 4 h + r % 4
-      const uint32_t* wr = wt + (32 * m + 8 * (r / 4) + 4 * h + r % 4) * kLdsStride2;
-      const uint4 a0 = *reinterpret_cast<const uint4*>(wr + 4 * g);
-      const uint4 a1 = *reinterpret_cast<const uint4*>(wr + 16 + 4 * g);
-      acc[h] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-      acc[h] = mfma_bf16(a0, b0, acc[h]);
-      acc[h] = mfma_bf16(a1, b1, acc[h]);
-    }
-    // lane holds columns k0 + 32 m + 8 g + 4 h + v of token tw + r
-    if (store) {
-      uint4 v;
-      v.x = pack_bf16x2(acc[0][0], acc[0][1]);
-      v.y = pack_bf16x2(acc[0][2], acc[0][3]);
-      v.z = pack_bf16x2(acc[1][0], acc[1][1]);
-      v.w = pack_bf16x2(acc[1][2], acc[1][3]);
-      st16_nt(orow + 32 * m, v);
-    }
+  for (int kt = 0; kt < 8; ++kt) acc[kt] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+  uint4 b[8][2];
+#pragma unroll
+  for (int kt = 0; kt < 8; ++kt) {
+    const uint32_t* row = lds + (128 * half + 16 * kt + r) * kWtStride2 + 8 * g;
+    b[kt][0] = *reinterpret_cast<const uint4*>(row);
+    b[kt][1] = *reinterpret_cast<const uint4*>(row + 4);
+  }
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    const double a = el8(s < 8 ? a0 : a1, s & 7);
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt) acc[kt] = mfma_f64(a, el8(b[kt][s >> 3], s & 7), acc[kt]);
+  }
+  __syncthreads();   // the slab is read; its space now stages the results
+  // lane holds token tw + g + 4 v, column k0 + 128 half + 16 kt + r
+  uint16_t* st = reinterpret_cast<uint16_t*>(lds) + wave * (16 * 128);
+#pragma unroll
+  for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) st[(g + 4 * v) * 128 + 16 * kt + r] = f32_to_bf16(static_cast<float>(acc[kt][v]));
+  __syncthreads();
+  // 16 tokens x 16 chunks of 16 bytes per wave, 4 per lane
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int q = lane + 64 * it;
+    const int row = q / 16, c = q % 16;
+    if (tw + row < T)
+      st16_nt(d_out + (tw + row) * kD + k0 + 128 * half + 8 * c, *reinterpret_cast<const uint4*>(st + row * 128 + 8 * c));
   }
 }
 
-// ---- backward: dWp and dbp partials ------------------------------------------
-// Block: 64 columns (k0 ..) x one chunk of 512 tokens, in 8 rounds of 64
-// tokens staged in LDS transposed (out: row k holds the round's 64 tokens;
-// d_lat: row o likewise); tokens past T are staged as zeros.  Wave w owns
-// outputs 16 w .. (A = d_lat rows), 4 column tiles n (B = out rows k0 + 16 n +
-// r); each instruction adds 32 tokens.  Blocks of column block 0 also sum
-// d_lat per output (wave 0, fp64, tokens ascending).
-// One block: 64 columns of out x one 512-token chunk.  A full chunk (all
-// tokens < T) loads unconditionally, two rounds ahead of the one being
-// added; the last, partial chunk takes the guarded loads (zeros past T).
+// dWp and dbp partials of one 512-token chunk (c) for 128 columns (k0 ..): 8
+// rounds of 64 tokens staged in LDS as they are (token rows of out and
+// d_lat; tokens past T staged as zeros).  Wave w: output tile w % 4, column
+// tiles 4 (w / 4) .. + 3.  Lane (r, g) at step s of a round: A = d_lat[4 s +
+// g][16 (w % 4) + r], B = out[4 s + g][16 n + r]: the chunk's tokens in
+// ascending order.  Wave 0 of column block 0 also adds d_lat per output (lane
+// o, fp64, tokens ascending) for dbp.
 template <bool kFull>
 __device__ __forceinline__ void dw_chunk(const uint16_t* __restrict__ d_lat, const uint16_t* __restrict__ out,
-                                         float* __restrict__ part, double* __restrict__ part_db, int64_t T,
-                                         int bx, int64_t c, uint32_t* xs, uint32_t* ds) {
+                                         double* __restrict__ part, double* __restrict__ part_db, int64_t T,
+                                         int bx, int64_t c, uint32_t* lds) {
   constexpr int kRounds = kChunk / kRound;   // 8
-  const int k0 = bx * 64;
+  const int k0 = bx * kDwCols;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
-  const int p = threadIdx.x % 32, c8 = threadIdx.x / 32;   // staging: token pair p, octet c8
-  f32x4_t acc[4];
+  const int ot = wave & 3, n0 = 4 * (wave >> 2);
+  uint32_t* xs = lds;                        // [64 tokens][kStRow2]
+  uint32_t* ds = lds + kRound * kStRow2;     // [64 tokens][kDlRow2]
+  // staging items: out 64 tokens x 16 chunks (2 per thread), d_lat 64 x 8 (1 per thread)
+  const int xt = threadIdx.x / 16, xc = threadIdx.x % 16;     // + 32 tokens for the second
+  const int dt = threadIdx.x / 8, dc = threadIdx.x % 8;
+  f64x4_t acc[4];
 #pragma unroll
-  for (int n = 0; n < 4; ++n) acc[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int n = 0; n < 4; ++n) acc[n] = f64x4_t{0.0, 0.0, 0.0, 0.0};
   double sdb = 0.0;
-  // a round's four rows per thread: out and d_lat of tokens tb, tb + 1
-  uint4 buf[kRounds][4];
-  auto load = [&](int rd) {
-    const int64_t tb = c * kChunk + rd * kRound + 2 * p;
+  uint4 bx0[2], bx1[2], bd[2];
+  auto load = [&](int rd, int slot) {
+    const int64_t tbase = c * kChunk + rd * kRound;
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    const int64_t ta = tbase + xt, tb2 = tbase + xt + 32, td = tbase + dt;
     if constexpr (kFull) {
-      buf[rd][0] = ld16(out + tb * kD + k0 + 8 * c8);
-      buf[rd][1] = ld16(out + (tb + 1) * kD + k0 + 8 * c8);
-      buf[rd][2] = ld16(d_lat + tb * kO + 8 * c8);
-      buf[rd][3] = ld16(d_lat + (tb + 1) * kO + 8 * c8);
+      bx0[slot] = ld16(out + ta * kD + k0 + 8 * xc);
+      bx1[slot] = ld16(out + tb2 * kD + k0 + 8 * xc);
+      bd[slot] = ld16(d_lat + td * kO + 8 * dc);
     } else {
-      const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-      buf[rd][0] = tb < T ? ld16(out + tb * kD + k0 + 8 * c8) : z;
-      buf[rd][1] = tb + 1 < T ? ld16(out + (tb + 1) * kD + k0 + 8 * c8) : z;
-      buf[rd][2] = tb < T ? ld16(d_lat + tb * kO + 8 * c8) : z;
-      buf[rd][3] = tb + 1 < T ? ld16(d_lat + (tb + 1) * kO + 8 * c8) : z;
+      bx0[slot] = ta < T ? ld16(out + ta * kD + k0 + 8 * xc) : z;
+      bx1[slot] = tb2 < T ? ld16(out + tb2 * kD + k0 + 8 * xc) : z;
+      bd[slot] = td < T ? ld16(d_lat + td * kO + 8 * dc) : z;
     }
   };
-  load(0);
-  load(1);
+  load(0, 0);
 #pragma unroll
   for (int rd = 0; rd < kRounds; ++rd) {
-    uint32_t ox[8], od[8];
-    interleave8(buf[rd][0], buf[rd][1], ox);
-    interleave8(buf[rd][2], buf[rd][3], od);
-    if (rd + 2 < kRounds) load(rd + 2);
+    const int cur = rd & 1;
+    if (rd + 1 < kRounds) load(rd + 1, cur ^ 1);
     __syncthreads();   // the previous round's reads are done
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      xs[(8 * c8 + e) * kLdsStride2 + p] = ox[e];
-      ds[(8 * c8 + e) * kLdsStride2 + p] = od[e];
-    }
+    *reinterpret_cast<uint4*>(xs + xt * kStRow2 + 4 * xc) = bx0[cur];
+    *reinterpret_cast<uint4*>(xs + (xt + 32) * kStRow2 + 4 * xc) = bx1[cur];
+    *reinterpret_cast<uint4*>(ds + dt * kDlRow2 + 4 * dc) = bd[cur];
     __syncthreads();
+    const uint16_t* xh = reinterpret_cast<const uint16_t*>(xs);
+    const uint16_t* dh = reinterpret_cast<const uint16_t*>(ds);
 #pragma unroll
-    for (int sub = 0; sub < kRound / 32; ++sub) {
-      const uint4 a = *reinterpret_cast<const uint4*>(ds + (16 * wave + r) * kLdsStride2 + 16 * sub + 4 * g);
+    for (int s = 0; s < kRound / 4; ++s) {
+      const int t = 4 * s + g;
+      const double a = static_cast<double>(bf16_to_f32(dh[t * (2 * kDlRow2) + 16 * ot + r]));
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const uint4 b = *reinterpret_cast<const uint4*>(xs + (16 * n + r) * kLdsStride2 + 16 * sub + 4 * g);
-        acc[n] = mfma_bf16(a, b, acc[n]);
-      }
+      for (int n = 0; n < 4; ++n)
+        acc[n] = mfma_f64(a, static_cast<double>(bf16_to_f32(xh[t * (2 * kStRow2) + 16 * (n0 + n) + r])), acc[n]);
     }
     if (bx == 0 && wave == 0) {
-      const uint32_t* row = ds + lane * kLdsStride2;
-      for (int q = 0; q < kRound / 2; ++q) {
-        sdb += static_cast<double>(bf_lo(row[q]));
-        sdb += static_cast<double>(bf_hi(row[q]));
-      }
+      for (int t = 0; t < kRound; ++t) sdb += static_cast<double>(bf16_to_f32(dh[t * (2 * kDlRow2) + lane]));
     }
   }
-  // lane holds outputs 16 w + 4 g + v, columns k0 + 16 n + r
-  float* pc = part + c * kO * kD;
+  // lane holds outputs 16 ot + g + 4 v, columns k0 + 16 (n0 + n) + r
+  double* pc = part + c * kO * kD;
 #pragma unroll
   for (int n = 0; n < 4; ++n)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) pc[static_cast<int64_t>(16 * wave + 4 * g + v) * kD + k0 + 16 * n + r] = acc[n][v];
+    for (int v = 0; v < 4; ++v)
+      pc[static_cast<int64_t>(16 * ot + g + 4 * v) * kD + k0 + 16 * (n0 + n) + r] = acc[n][v];
   if (bx == 0 && wave == 0) part_db[c * kO + lane] = sdb;
 }
 
-// The backward's two independent products in one launch: blocks [0, 48 C)
-// take a 64-column x 512-token chunk of the dWp partial sums (chunk-major, so
-// the longer blocks start first), the rest take 64 tokens x 256 columns of
-// d_out.
-constexpr int kDwColBlocks = kD / 64;   // 48
-
-__global__ __launch_bounds__(256) void proj_out_bwd_kernel(const uint16_t* __restrict__ d_lat,
-                                                           const uint16_t* __restrict__ out,
-                                                           const uint16_t* __restrict__ W,
-                                                           uint16_t* __restrict__ d_out, float* __restrict__ part,
-                                                           double* __restrict__ part_db, int64_t T,
-                                                           int64_t dw_blocks) {
-  __shared__ __align__(16) uint32_t lds[kDxCols * kLdsStride2];   // 36 KB: dx's Wp slab, or dw's two tiles
-  static_assert(2 * 64 * kLdsStride2 <= kDxCols * kLdsStride2, "dw tiles must fit the shared buffer");
+__global__ __launch_bounds__(kBwdThreads) void proj_out_bwd_kernel(const uint16_t* __restrict__ d_lat,
+                                                                  const uint16_t* __restrict__ out,
+                                                                  const uint16_t* __restrict__ W,
+                                                                  uint16_t* __restrict__ d_out,
+                                                                  double* __restrict__ part,
+                                                                  double* __restrict__ part_db, int64_t T,
+                                                                  int64_t dw_blocks) {
+  __shared__ __align__(16) uint32_t lds[kBwdLds / 4];
   const int64_t blk = blockIdx.x;
   if (blk < dw_blocks) {
     const int bx = static_cast<int>(blk % kDwColBlocks);
     const int64_t c = blk / kDwColBlocks;
     if ((c + 1) * kChunk <= T)
-      dw_chunk<true>(d_lat, out, part, part_db, T, bx, c, lds, lds + 64 * kLdsStride2);
+      dw_chunk<true>(d_lat, out, part, part_db, T, bx, c, lds);
     else
-      dw_chunk<false>(d_lat, out, part, part_db, T, bx, c, lds, lds + 64 * kLdsStride2);
+      dw_chunk<false>(d_lat, out, part, part_db, T, bx, c, lds);
   } else {
     constexpr int kDxColBlocks = kD / kDxCols;
     const int64_t q = blk - dw_blocks;
-    dx_block(d_lat, W, d_out, T, q / kDxColBlocks, static_cast<int>(q % kDxColBlocks), lds);
+    dx_block(d_lat, W, d_out, T, (q / kDxColBlocks) * kDxTokens, static_cast<int>(q % kDxColBlocks) * kDxCols, lds);
   }
 }
 
-// dWp and dbp: the chunks' partials added in ascending order in fp64
-// 4 consecutive elements of dWp per thread; the chunks' partials are loaded
-// 8 at a time (indices clamped to the last chunk, so every load is in
-// bounds and none sits under a branch) and added in ascending chunk order
-__global__ __launch_bounds__(256) void proj_out_dw_combine_kernel(const float* __restrict__ part,
+// dWp and dbp: the chunks' partials added in ascending order in fp64, then
+// rounded to fp32 and to bf16.  2 consecutive elements of dWp per thread;
+// the partials are loaded 8 chunks at a time (indices clamped to the last
+// chunk, so every load is in bounds and none sits under a branch).
+__global__ __launch_bounds__(256) void proj_out_dw_combine_kernel(const double* __restrict__ part,
                                                                   const double* __restrict__ part_db,
                                                                   uint16_t* __restrict__ dW, uint16_t* __restrict__ db,
                                                                   int64_t chunks) {
-  const int64_t i = 4 * (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x);   // < 64 * 3072 by the grid
-  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+  const int64_t i = 2 * (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x);   // < 64 * 3072 by the grid
+  double s0 = 0.0, s1 = 0.0;
   for (int64_t c0 = 0; c0 < chunks; c0 += 8) {
-    float4 v[8];
+    double2 v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int64_t c = c0 + j < chunks ? c0 + j : chunks - 1;
-      v[j] = *reinterpret_cast<const float4*>(part + c * kO * kD + i);
+      v[j] = *reinterpret_cast<const double2*>(part + c * kO * kD + i);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const bool in = c0 + j < chunks;
-      s0 = in ? s0 + static_cast<double>(v[j].x) : s0;
-      s1 = in ? s1 + static_cast<double>(v[j].y) : s1;
-      s2 = in ? s2 + static_cast<double>(v[j].z) : s2;
-      s3 = in ? s3 + static_cast<double>(v[j].w) : s3;
+      s0 = in ? s0 + v[j].x : s0;
+      s1 = in ? s1 + v[j].y : s1;
     }
   }
-  const uint2 w = make_uint2(pack_bf16x2(static_cast<float>(s0), static_cast<float>(s1)),
-                             pack_bf16x2(static_cast<float>(s2), static_cast<float>(s3)));
-  *reinterpret_cast<uint2*>(dW + i) = w;
+  *reinterpret_cast<uint32_t*>(dW + i) = pack_bf16x2(static_cast<float>(s0), static_cast<float>(s1));
   if (blockIdx.x == 0 && threadIdx.x < kO) {
     double t = 0.0;
     for (int64_t c = 0; c < chunks; ++c) t += part_db[c * kO + threadIdx.x];
@@ -512,46 +416,41 @@ __global__ __launch_bounds__(256) void proj_out_dw_combine_kernel(const float* _
 int64_t proj_out_chunks(int64_t T) { return (T + kChunk - 1) / kChunk; }
 
 hipError_t launch_proj_out_fwd(const uint16_t* out, const uint16_t* W, const uint16_t* bias, uint16_t* latent,
-                               float* part, int64_t T, hipStream_t s) {
-  hipLaunchKernelGGL(proj_out_fwd_part_kernel, dim3(static_cast<unsigned>((T + kFwdTokens - 1) / kFwdTokens), kQuarters),
-                     dim3(256), 0, s, out, W, part, T);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  hipLaunchKernelGGL(proj_out_fwd_combine_kernel, dim3(static_cast<unsigned>((T * kO / 4 + 255) / 256)), dim3(256), 0, s,
-                     part, bias, latent, T);
+                               int64_t T, hipStream_t s) {
+  hipLaunchKernelGGL(proj_out_fwd_kernel, dim3(static_cast<unsigned>((T + kFT - 1) / kFT)), dim3(kFwdThreads), 0, s,
+                     out, W, bias, latent, T);
   return hipGetLastError();
 }
 
 hipError_t launch_proj_out_fwd_fused(const uint16_t* x, const uint16_t* emb, const float* mean, const float* rstd,
-                                     const uint16_t* W, const uint16_t* bias, uint16_t* latent, float* part,
-                                     int64_t B, int64_t S, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+                                     const uint16_t* W, const uint16_t* bias, uint16_t* latent, int64_t B, int64_t S,
+                                     hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int64_t T = B * S;
-  const dim3 grid(static_cast<unsigned>((T + kFuseTokens - 1) / kFuseTokens), kQuarters);
-  // S a multiple of 32: every block's tokens belong to one sample
-  auto k = S % kFuseTokens == 0 ? proj_out_fused_part_kernel<true> : proj_out_fused_part_kernel<false>;
+  const dim3 grid(static_cast<unsigned>((T + kFT - 1) / kFT));
   if (e0 && e1)
-    hipExtLaunchKernelGGL(k, grid, dim3(256), 0, s, e0, e1, 0, x, emb, mean, rstd, W, part, T, S);
+    hipExtLaunchKernelGGL(proj_out_fused_kernel, grid, dim3(kFwdThreads), 0, s, e0, e1, 0, x, emb, mean, rstd,
+                          W, bias, latent, T, S);
   else
-    hipLaunchKernelGGL(k, grid, dim3(256), 0, s, x, emb, mean, rstd, W, part, T, S);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  hipLaunchKernelGGL(proj_out_fwd_combine_kernel, dim3(static_cast<unsigned>((T * kO / 4 + 255) / 256)), dim3(256), 0, s,
-                     part, bias, latent, T);
+    hipLaunchKernelGGL(proj_out_fused_kernel, grid, dim3(kFwdThreads), 0, s, x, emb, mean, rstd, W, bias,
+                       latent, T, S);
   return hipGetLastError();
 }
 
 hipError_t launch_proj_out_bwd(const uint16_t* d_lat, const uint16_t* out, const uint16_t* W, uint16_t* d_out,
-                               uint16_t* dW, uint16_t* db, float* part, double* part_db, int64_t T, hipStream_t s,
+                               uint16_t* dW, uint16_t* db, double* part, double* part_db, int64_t T, hipStream_t s,
                                hipEvent_t e0, hipEvent_t e1) {
   const int64_t chunks = proj_out_chunks(T);
   const int64_t dw_blocks = kDwColBlocks * chunks;
-  const int64_t dx_blocks = (T + 63) / 64 * (kD / kDxCols);
+  const int64_t dx_blocks = (T + kDxTokens - 1) / kDxTokens * (kD / kDxCols);
   const dim3 grid(static_cast<unsigned>(dw_blocks + dx_blocks));
   if (e0 && e1)
-    hipExtLaunchKernelGGL(proj_out_bwd_kernel, grid, dim3(256), 0, s, e0, e1, 0, d_lat, out, W, d_out, part, part_db,
-                          T, dw_blocks);
+    hipExtLaunchKernelGGL(proj_out_bwd_kernel, grid, dim3(kBwdThreads), 0, s, e0, e1, 0, d_lat, out, W, d_out, part,
+                          part_db, T, dw_blocks);
   else
-    hipLaunchKernelGGL(proj_out_bwd_kernel, grid, dim3(256), 0, s, d_lat, out, W, d_out, part, part_db, T, dw_blocks);
+    hipLaunchKernelGGL(proj_out_bwd_kernel, grid, dim3(kBwdThreads), 0, s, d_lat, out, W, d_out, part, part_db, T,
+                       dw_blocks);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  hipLaunchKernelGGL(proj_out_dw_combine_kernel, dim3(kO * kD / 4 / 256), dim3(256), 0, s, part, part_db, dW, db,
+  hipLaunchKernelGGL(proj_out_dw_combine_kernel, dim3(kO * kD / 2 / 256), dim3(256), 0, s, part, part_db, dW, db,
                      chunks);
   return hipGetLastError();
 }

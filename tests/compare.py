@@ -5,14 +5,6 @@ mapping of bf16 bit patterns (+0 and -0 equal) must be <= 1 against the fp32
 oracle; an element further off passes only if it is within 1 ulp of the fp64
 twin (the arbiter).
 
-bf16 outputs of an fp32-accumulating matrix-core contraction (proj_out): an
-element outside both 1-ulp gates still passes when |gpu - e| <= ulp(e) +
-kappa 2^-24 A, e the exact sum (the oracle in exact mode), A the sum of the
-absolute values of its terms and kappa the number of fp32 roundings along the
-longest accumulation path -- the classical bound for recursive summation in
-fp32 (Higham, Accuracy and Stability of Numerical Algorithms, ch. 4), plus one
-bf16 ulp for the final rounding.  It matters only where the sum cancels.
-
 fp32 outputs (d_scale / d_shift, LayerNorm statistics): |gpu - o| must be at
 most 1e-5 |o| + 2^-24 A, where A is the sum of the absolute values of the
 reduced terms (the scale of the rounding error any fp32 summation order can
@@ -42,29 +34,6 @@ def bf16_gate(gpu_bits, oracle_bits, twin_bits=None, max_ulp: int = 1) -> dict:
         "n_fail": int(bad.sum()),
         "worst_index": (np.unravel_index(int(np.argmax(d)), d.shape) if d.size else None),
     }
-
-
-def bf16_ulp_at(v) -> np.ndarray:
-    """Spacing of bf16 numbers at |v| (the subnormal spacing below 2^-126)."""
-    a = np.abs(np.asarray(v, np.float64))
-    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
-    return np.where(a >= 2.0 ** -126, 2.0 ** (np.maximum(e, -126) - 7), 2.0 ** -133)
-
-
-def bf16_accum_gate(gpu_bits, oracle_bits, twin_bits, exact, A, kappa: int) -> dict:
-    """bf16_gate, then the fp32 accumulation bound for the elements it rejects."""
-    r = bf16_gate(gpu_bits, oracle_bits, twin_bits)
-    gpu_bits = np.asarray(gpu_bits, np.uint16)
-    d1 = bf16_ulp_diff(gpu_bits, oracle_bits)
-    bad = (d1 > 1) & (bf16_ulp_diff(gpu_bits, twin_bits) > 1)
-    g = (gpu_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    e = np.asarray(exact, np.float64)
-    tol = bf16_ulp_at(e) + kappa * U24 * np.asarray(A, np.float64)
-    within = np.abs(g - e) <= tol
-    r["n_outside_ulp_gates"] = int(bad.sum())
-    r["n_fail"] = int((bad & ~within).sum())
-    r["max_err_over_bound"] = float((np.abs(g - e) / tol).max()) if g.size else 0.0
-    return r
 
 
 def f32_gate(gpu, oracle, A, twin=None, rel: float = REL_F32) -> dict:

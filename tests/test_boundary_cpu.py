@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_strerror(L):
-    assert L.adaln_abi_version() == 11
+    assert L.adaln_abi_version() == 12
     for code in range(-8, 1):
         assert len(lib.strerror(code)) >= 2
 
@@ -57,22 +57,23 @@ def test_workspace_sizes(L):
         T0 = math.ceil(S / 32)
         assert lib.workspace_bytes(lib.OP_NORM_MOD_BWD, B, S, 3072) == pad(B * T0 * 6144 * 8)
         assert lib.workspace_bytes(lib.OP_TOKEN_TREE_SUM, B, S, 100) == pad(B * T0 * 128 * 8)
-        # B <= 4: 8 fp64 da subtrees per sample and column; B > 4: the SiLU activations
-        proj_bwd = pad(8 * B * 3072 * 8) if B <= 4 else pad(B * 3072 * 2)
+        # B <= 4: 32 fp64 da subtrees per sample and column; B > 4: the SiLU activations
+        proj_bwd = pad(32 * B * 3072 * 8) if B <= 4 else pad(B * 3072 * 2)
         assert lib.workspace_bytes(lib.OP_PROJ_BWD, B, S, 3072) == proj_bwd
         assert lib.workspace_bytes(lib.OP_PROJ_FWD, B, S, 3072) == pad(B * 3072 * 2)
         # fp32: the activations, then for B <= 4 the fp64 da subtrees
-        sub = pad(8 * B * 3072 * 8) if B <= 4 else 0
+        sub = pad(32 * B * 3072 * 8) if B <= 4 else 0
         assert lib.workspace_bytes(lib.OP_BWD_F32, B, S, 3072) == pad(B * T0 * 6144 * 8) + pad(B * 3072 * 4) + sub
         assert lib.workspace_bytes(lib.OP_RESIDUAL_BWD, B, S, 3072) == pad(B * T0 * 9216 * 8)
         C = math.ceil(B * S / 512)
-        assert lib.workspace_bytes(lib.OP_PROJ_OUT_BWD, B, S, 3072) == pad(C * 64 * 3072 * 4) + pad(C * 64 * 8)
-        assert lib.workspace_bytes(lib.OP_PROJ_OUT_FWD, B, S, 3072) == pad(4 * B * S * 64 * 4)
-        assert lib.workspace_bytes(lib.OP_FWD_PROJ_OUT, B, S, 3072) == pad(B * 3072 * 2) + pad(4 * B * S * 64 * 4)
+        # proj_out: fp64 dWp / dbp partial sums of 512-token chunks; the forward keeps its partials on chip
+        assert lib.workspace_bytes(lib.OP_PROJ_OUT_BWD, B, S, 3072) == pad(C * 64 * 3072 * 8) + pad(C * 64 * 8)
+        assert lib.workspace_bytes(lib.OP_PROJ_OUT_FWD, B, S, 3072) == 256
+        assert lib.workspace_bytes(lib.OP_FWD_PROJ_OUT, B, S, 3072) == pad(B * 3072 * 2) + 256
     # proj_out: a flat token count beyond the modulation's sequence limit
     T = 1 << 22
-    assert lib.workspace_bytes(lib.OP_PROJ_OUT_FWD, 1, T, 3072) == pad(4 * T * 64 * 4)
-    assert lib.workspace_bytes(lib.OP_PROJ_OUT_BWD, 1, T, 3072) == pad((T // 512) * 64 * 3072 * 4) + pad((T // 512) * 64 * 8)
+    assert lib.workspace_bytes(lib.OP_PROJ_OUT_FWD, 1, T, 3072) == 256
+    assert lib.workspace_bytes(lib.OP_PROJ_OUT_BWD, 1, T, 3072) == pad((T // 512) * 64 * 3072 * 8) + pad((T // 512) * 64 * 8)
     assert lib.workspace_bytes(lib.OP_PROJ_OUT_FWD, 1, 65535 * 512 + 1, 3072) == 0
     assert lib.workspace_bytes(lib.OP_NORM_MOD_BWD, 1, 10, 1024) == 0
     assert lib.workspace_bytes(99, 1, 10, 3072) == 0
@@ -121,7 +122,7 @@ def test_validation_before_device_work(L):
         assert L.adaln_proj_out_bwd(p, p, p, p, p, p, p, 1 << 30, T, K, O, None) == lib.ERR_SHAPE
     assert L.adaln_proj_out_fwd(p + 4, p, p, p, p, 1 << 20, 4, 3072, 64, None) == lib.ERR_ALIGN
     po = [p + (k << 28) for k in range(7)]
-    assert L.adaln_proj_out_fwd(*po[:5], 4 * 1000 * 64 * 4 - 1, 1000, 3072, 64, None) == lib.ERR_WORKSPACE
+    assert L.adaln_proj_out_fwd(*po[:5], 255, 1000, 3072, 64, None) == lib.ERR_WORKSPACE
     need = lib.workspace_bytes(lib.OP_PROJ_OUT_BWD, 1, 1000, 3072)
     assert L.adaln_proj_out_bwd(*po, need - 1, 1000, 3072, 64, None) == lib.ERR_WORKSPACE
     # latent overlapping out is caught before the device check
@@ -166,22 +167,6 @@ def test_missing_library_fails_loudly(tmp_path):
             lib.load(str(tmp_path / "missing.so"))
     finally:
         lib._lib = saved
-
-
-def test_bf16_accumulation_gate():
-    """The accumulation-bound gate passes a cancelling sum's fp32-accumulation
-    error and rejects an error beyond the bound."""
-    import numpy as np
-    from oracle.fpmath import f32_to_bf16_bits
-    from tests.compare import bf16_accum_gate, bf16_ulp_at
-    e = np.array([1e-4, 1.0])              # exact sums
-    A = np.array([1.0, 1.0])               # sums of |terms|: the first cancels
-    o = f32_to_bf16_bits(e.astype(np.float32))
-    near = f32_to_bf16_bits(np.array([1e-4 + 16 * 2.0 ** -24, 1.0], np.float32))   # 2 bf16 ulps, 16 u24 A
-    r = bf16_accum_gate(near, o, o, e, A, kappa=20)
-    assert r["n_outside_ulp_gates"] == 1 and r["n_fail"] == 0
-    far = f32_to_bf16_bits(np.array([1e-4 + 64 * 2.0 ** -24, 1.0 + 4 * bf16_ulp_at(1.0)], np.float32))
-    assert bf16_accum_gate(far, o, o, e, A, kappa=20)["n_fail"] == 2
 
 
 def test_site_views_validation(L):

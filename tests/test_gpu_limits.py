@@ -136,7 +136,7 @@ def test_proj_out_large_token_count(gpu_lib):
     oracle (a token's outputs depend only on its own row); dWp, dbp finite."""
     from invariant_silu_amd import ops
     from oracle import proj_out as po
-    from tests.compare import bf16_accum_gate
+    from tests.compare import bf16_gate
     from tests.gpu_helpers import bf16_bits
     T = 1 << 22
     print(f"[limits] proj_out T={T}", flush=True)
@@ -150,12 +150,11 @@ def test_proj_out_large_token_count(gpu_lib):
     torch.cuda.synchronize()
     rows = torch.tensor([0, 1, 511, 512, 1 << 20, T - 2, T - 1], device="cuda")
     sub = {"out": bf16_bits(out[rows]), "W": bf16_bits(W), "bias": bf16_bits(bias), "d_lat": bf16_bits(d_lat[rows])}
-    f, f6, fe = (po.proj_out_forward(sub, m, want_abs=(m == "fp32")) for m in ("fp32", "fp64", "exact"))
-    b, b6, be = (po.proj_out_backward(sub, m, want_abs=(m == "fp32"), outputs=("d_out",))
-                 for m in ("fp32", "fp64", "exact"))
-    r = bf16_accum_gate(bf16_bits(latent[rows]), f["latent_bits"], f6["latent_bits"], fe["latent"], f["A_latent"], 35)
+    f, f6 = (po.proj_out_forward(sub, m) for m in ("fp32", "fp64"))
+    b, b6 = (po.proj_out_backward(sub, m, outputs=("d_out",)) for m in ("fp32", "fp64"))
+    r = bf16_gate(bf16_bits(latent[rows]), f["latent_bits"], f6["latent_bits"])
     assert r["n_fail"] == 0, r
-    r = bf16_accum_gate(bf16_bits(d_out[rows]), b["d_out_bits"], b6["d_out_bits"], be["d_out"], b["A_d_out"], 10)
+    r = bf16_gate(bf16_bits(d_out[rows]), b["d_out_bits"], b6["d_out_bits"])
     assert r["n_fail"] == 0, r
     assert torch.isfinite(dW.float()).all() and torch.isfinite(db.float()).all()
     del out, d_out

@@ -2,16 +2,12 @@
 adaln_proj_out_bwd: parity with oracle/proj_out.py, per-token invariance and
 zero-gradient padding of dWp, dbp.
 
-Gates (tests/compare.py, bf16_accum_gate): every bf16 output within 1 ulp of
-the fp32 oracle, else within 1 ulp of its fp64 twin, else within the fp32
-accumulation bound ulp(e) + kappa 2^-24 A of the exact sum e.  The matrix
-cores accumulate in fp32 (the reading: an fp32-accumulating GEMM whose order
-the pages do not fix), so where a sum cancels the result can sit several bf16
-ulps from the correctly rounded one; the oracle, compensated, lands on it.
-kappa counts the fp32 roundings along the longest path: latent 24 chained
-instructions per quarter of K and 3 adds of the quarters, d_out 2, dWp 16
-per chunk, each + 8 for the adds inside an instruction and the final
-rounding; dbp sums in fp64.
+Gate (tests/compare.py, bf16_gate): every bf16 output within 1 ulp of the
+fp32 oracle, else within 1 ulp of its fp64 twin -- the same bar as every other
+bf16 output.  The kernels multiply exactly and accumulate in fp64 on the
+matrix cores, so they land on the correctly rounded sums; the cases at T = 600
+and T = 4096 are where the earlier fp32-accumulating bf16 kernels left
+cancelling sums several ulps off.
 """
 
 from __future__ import annotations
@@ -22,13 +18,12 @@ import torch
 
 from oracle import proj_out as po
 from synthetic_inputs import make_proj_out_inputs
-from tests.compare import bf16_accum_gate
+from tests.compare import bf16_gate
 from tests.gpu_helpers import bf16_bits, same_bytes, to_dev
 
 pytestmark = pytest.mark.gpu
 
 K, O = 3072, 64
-KAPPA = {"latent": 35, "d_out": 10, "dW": 26, "db": 2}
 
 
 KEYS = ("out", "W", "bias", "d_lat")
@@ -52,10 +47,10 @@ def test_proj_out_parity(gpu_lib, T):
     inp = _inputs(T, seed=100 + T)
     gpu = _run({k: to_dev(v) for k, v in inp.items()})
     torch.cuda.synchronize()
-    f, f6, fe = (po.proj_out_forward(inp, m, want_abs=(m == "fp32")) for m in ("fp32", "fp64", "exact"))
-    b, b6, be = (po.proj_out_backward(inp, m, want_abs=(m == "fp32")) for m in ("fp32", "fp64", "exact"))
-    for k, o, t, e in (("latent", f, f6, fe), ("d_out", b, b6, be), ("dW", b, b6, be), ("db", b, b6, be)):
-        r = bf16_accum_gate(bf16_bits(gpu[k]), o[k + "_bits"], t[k + "_bits"], e[k], o["A_" + k], KAPPA[k])
+    f, f6 = (po.proj_out_forward(inp, m) for m in ("fp32", "fp64"))
+    b, b6 = (po.proj_out_backward(inp, m) for m in ("fp32", "fp64"))
+    for k, o, t in (("latent", f, f6), ("d_out", b, b6), ("dW", b, b6), ("db", b, b6)):
+        r = bf16_gate(bf16_bits(gpu[k]), o[k + "_bits"], t[k + "_bits"])
         print(f"  {k}: {r}")
         assert r["n_fail"] == 0, k
 
@@ -70,17 +65,15 @@ def test_proj_out_large_sampled(gpu_lib):
     torch.cuda.synchronize()
     rows = np.array([0, 1, 15, 16, 63, 64, 511, 512, 2047, 4031, 4094, 4095])
     sub = dict(inp, out=inp["out"][rows], d_lat=inp["d_lat"][rows])
-    f, f6, fe = (po.proj_out_forward(sub, m, want_abs=(m == "fp32")) for m in ("fp32", "fp64", "exact"))
-    bs, bs6, bse = (po.proj_out_backward(sub, m, want_abs=(m == "fp32"), outputs=("d_out",))
-                    for m in ("fp32", "fp64", "exact"))
-    for k, got, o, t, e in (("latent", gpu["latent"][rows], f, f6, fe), ("d_out", gpu["d_out"][rows], bs, bs6, bse)):
-        r = bf16_accum_gate(bf16_bits(got), o[k + "_bits"], t[k + "_bits"], e[k], o["A_" + k], KAPPA[k])
+    f, f6 = (po.proj_out_forward(sub, m) for m in ("fp32", "fp64"))
+    bs, bs6 = (po.proj_out_backward(sub, m, outputs=("d_out",)) for m in ("fp32", "fp64"))
+    for k, got, o, t in (("latent", gpu["latent"][rows], f, f6), ("d_out", gpu["d_out"][rows], bs, bs6)):
+        r = bf16_gate(bf16_bits(got), o[k + "_bits"], t[k + "_bits"])
         print(f"  {k} (sampled): {r}")
         assert r["n_fail"] == 0, k
-    b, b6, be = (po.proj_out_backward(inp, m, want_abs=(m == "fp32"), outputs=("dW", "db"))
-                 for m in ("fp32", "fp64", "exact"))
+    b, b6 = (po.proj_out_backward(inp, m, outputs=("dW", "db")) for m in ("fp32", "fp64"))
     for k in ("dW", "db"):
-        r = bf16_accum_gate(bf16_bits(gpu[k]), b[k + "_bits"], b6[k + "_bits"], be[k], b["A_" + k], KAPPA[k])
+        r = bf16_gate(bf16_bits(gpu[k]), b[k + "_bits"], b6[k + "_bits"])
         print(f"  {k}: {r}")
         assert r["n_fail"] == 0, k
 
