@@ -19,17 +19,26 @@ tokens.  --site serve times the final layer's serving forward
 (adaln_fwd_proj_out: the final modulation's projection and statistics, then
 proj_out with the modulated output computed on chip) on the final workload.
 
-Inputs are resident in HBM before the timed region.  The step rotates over
-several independent copies of every buffer (parameters included), so no step
-finds the previous step's data in the 256 MB MALL; reuse inside one step (x
-read by the forward and the backward, W by both projections) is left as is.
+Measurement (inputs resident in HBM before anything is timed):
+  * cold caches, the headline: before the forward and before the backward a
+    flush writes and then reads back 768 MiB (three times the 256 MB
+    memory-side cache), and HIP events on the step's stream bracket each phase
+    (the flushes are outside them); ms_per_step is the mean over the timed
+    steps of forward + backward, and at least 100 cold steps give the median,
+    p10 and p90;
+  * warm, beside it: back-to-back steps over several independent copies of
+    every buffer, so no step finds the previous step's data in the cache, but
+    the backward finds what the forward of the same step read;
+  * the ceiling: a hand-written 16-byte-per-lane streaming copy of the step's
+    bytes, after the same flush (libadaln_bench.so, not part of the operator's
+    library).
 
-Prints ONE JSON line.  `roofline` covers the dominant kernel (the backward's
-main launch: g and x in, dx out, level-0 token tiles out), timed on every 8th
-timed step with HIP events that
-its own dispatch carries on the stream it runs on (adaln_timing_begin/end: a
-timed dispatch leaves the stream idle for a few us, so timing is sampled);
-`cpu_baseline` is the NumPy oracle timed on this host on the same workload.
+Prints ONE JSON line.  `roofline` covers the dominant kernel, the backward's
+first launch (g and x in, dx and the level-0 token tiles out), timed on its
+own through adaln_norm_mod_bwd_level0 with events around each launch, after
+the same flush as in the step; `cpu_baseline` is the NumPy oracle timed on
+this host on the same workload (one thread, and every core on independent
+copies), in child processes started before this process touches the GPU.
 """
 
 from __future__ import annotations
@@ -49,8 +58,8 @@ D = 3072
 N = 2 * D
 HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 << 20
-SAMPLE = 4        # the dominant kernel is timed on every SAMPLE-th timed step
 MIN_STAT_STEPS = 100   # cold steps behind the median / p10 / p90 (at least)
+MIN_KERNEL_LAUNCHES = 20   # timed launches of the dominant kernel (at least)
 FLUSH_BYTES = 768 << 20   # written, then read back, before each timed phase (3x the MALL)
 METRIC = "fwd+bwd tokens/sec + achieved HBM GB/s at S=4096 D=3072 bf16 (batch-invariant)"
 METRIC_RESIDUAL = "residual norm site fwd+bwd tokens/sec at D=3072 bf16 (batch-invariant)"
@@ -309,8 +318,12 @@ def main() -> int:
         print(f"{_build.BENCH_LIB_PATH} is missing: run __graft_entry__.build()", file=sys.stderr)
         return 2
     BL = ctypes.CDLL(_build.BENCH_LIB_PATH)
-    for fn, argt in (("bench_flush", [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
-                     ("bench_stream_copy", [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p])):
+    for fn, argt in (("bench_flush", [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p]),
+                     ("bench_stream_copy", [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+                     ("bench_event_create", [ctypes.POINTER(ctypes.c_void_p)]),
+                     ("bench_event_elapsed", [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]),
+                     ("bench_event_destroy", [ctypes.c_void_p])):
         getattr(BL, fn).argtypes = argt
         getattr(BL, fn).restype = ctypes.c_int
     dev = torch.device("cuda:0")
@@ -418,6 +431,10 @@ def main() -> int:
         step_bytes, k_bytes = algorithmic_bytes(B, S, el), dominant_kernel_bytes(B, S, el)
         fwd_name, bwd_name = ("adaln_fwd_f32", "adaln_bwd_f32") if f32 else ("adaln_fwd", "adaln_bwd")
         k_name = ("norm_mod_bwd_f32_kernel" if f32 else "norm_mod_bwd_kernel<0>") + " (dx rows + level-0 token tiles)"
+    kernel_timed = site == "final" and not f32
+    if not kernel_timed:
+        k_name = f"whole step ({fwd_name})" if serve_site else f"whole step ({fwd_name} + {bwd_name})"
+        k_bytes = step_bytes
     nsets = max(2, math.ceil(3 * MALL_BYTES / step_bytes))
     sets = [new_set() for _ in range(nsets)]
     stream = torch.cuda.current_stream(dev)
@@ -460,37 +477,76 @@ def main() -> int:
 
     flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
 
-    def flush():
-        if BL.bench_flush(flush_buf.data_ptr(), FLUSH_BYTES, st) != 0:
+    class Events:
+        """Timing events of the bench library: recorded by kernel dispatches
+        themselves (no event packet of their own in the stream)."""
+
+        def __init__(self, n):
+            self.h = []
+            for _ in range(n):
+                e = ctypes.c_void_p()
+                if BL.bench_event_create(ctypes.byref(e)) != 0:
+                    raise RuntimeError("bench_event_create failed")
+                self.h.append(e.value)
+
+        def ms(self, a, b):
+            out = ctypes.c_float()
+            if BL.bench_event_elapsed(self.h[a], self.h[b], ctypes.byref(out)) != 0:
+                raise RuntimeError("bench_event_elapsed failed")
+            return out.value
+
+        def close(self):
+            for e in self.h:
+                BL.bench_event_destroy(e)
+
+    def flush(ev_start=None, ev_end=None):
+        if BL.bench_flush(flush_buf.data_ptr(), FLUSH_BYTES, ev_start, ev_end, st) != 0:
             raise RuntimeError("bench_flush failed")
 
-    Ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
-
-    # ---- cold caches (the headline): flush before each phase, events bracket the phases only
+    # ---- cold caches (the headline): a flush before each phase; a phase runs
+    # from the end of the flush before it to the start of the flush after it,
+    # both recorded by the flush kernels' own dispatches
     for i in range(args.warmup):
         flush(); fwd(sets[i % nsets]); flush(); bwd(sets[i % nsets])   # noqa: E702
     torch.cuda.synchronize()
     n_cold = max(args.steps, MIN_STAT_STEPS)
-    n_sampled = (n_cold + SAMPLE - 1) // SAMPLE
-    lib.check("adaln_timing_begin", L.adaln_timing_begin(n_sampled, SAMPLE))
-    evs = [[Ev() for _ in range(4)] for _ in range(n_cold)]
+    ev = Events(4 * n_cold + 1)   # per step: flush A start, end; flush B start, end; then a closing flush start
     t0 = time.perf_counter()
     for i in range(n_cold):
         s = sets[i % nsets]
-        flush(); evs[i][0].record(stream); fwd(s); evs[i][1].record(stream)   # noqa: E702
-        flush(); evs[i][2].record(stream); bwd(s); evs[i][3].record(stream)   # noqa: E702
+        flush(ev.h[4 * i], ev.h[4 * i + 1]); fwd(s)         # noqa: E702
+        flush(ev.h[4 * i + 2], ev.h[4 * i + 3]); bwd(s)     # noqa: E702
+    flush(ev.h[4 * n_cold], None)
     torch.cuda.synchronize()
     t_cold = time.perf_counter() - t0
-    ms_buf = (ctypes.c_float * n_sampled)()
-    n_timed = L.adaln_timing_end(ms_buf, n_sampled)
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    bwd_ms = [e[2].elapsed_time(e[3]) for e in evs] if not serve_site else [0.0] * n_cold
+    fwd_ms = [ev.ms(4 * i + 1, 4 * i + 2) for i in range(n_cold)]
+    bwd_ms = [ev.ms(4 * i + 3, 4 * i + 4) for i in range(n_cold)] if not serve_site else [0.0] * n_cold
+    ev.close()
     step_ms = [a + b for a, b in zip(fwd_ms, bwd_ms)]
     timed = step_ms[:args.steps]
     ms_per_step = sum(timed) / len(timed)
     units = B if mod6_site else B * S
     value = units / (ms_per_step / 1e3)
-    k_ms = sorted(ms_buf[i] for i in range(n_timed))
+
+    # ---- the dominant kernel on its own: the backward's first launch (dx and
+    # the level-0 token tiles, adaln_norm_mod_bwd_level0), each launch after
+    # the same flush as in the step, timed by events its own dispatch records
+    n_k = max(MIN_KERNEL_LAUNCHES, args.steps)
+    if kernel_timed:
+        s0 = sets[0]
+        kev = Events(2 * n_k)
+        for i in range(n_k):
+            flush()
+            lib.check("adaln_norm_mod_bwd_level0", L.adaln_norm_mod_bwd_level0(
+                s0["g"].data_ptr(), s0["x"].data_ptr(), s0["mean"].data_ptr(), s0["rstd"].data_ptr(),
+                s0["emb"].data_ptr(), s0["dx"].data_ptr(), s0["ws_bw"].data_ptr(), ws_bw, B, S, D,
+                kev.h[2 * i], kev.h[2 * i + 1], st))
+        torch.cuda.synchronize()
+        k_ms = sorted(kev.ms(2 * i, 2 * i + 1) for i in range(n_k))
+        kev.close()
+    else:   # the whole step: fwd + bwd phases
+        k_ms = sorted(step_ms)
+        n_k = len(k_ms)
     k_mean_ms = sum(k_ms) / len(k_ms)
     achieved = k_bytes / (k_mean_ms / 1e3) / 1e9
 
@@ -509,17 +565,15 @@ def main() -> int:
     cn = (step_bytes // 2 + 255) // 256 * 256
     src = torch.empty(cn, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty(cn, dtype=torch.uint8, device=dev)
-    cps = []
-    for i in range(22):
-        flush()
-        e0, e1 = Ev(), Ev()
-        e0.record(stream)
+    cev = Events(2 * 22 + 1)
+    for i in range(22):   # timed as the phases are: flush end to next flush start
+        flush(cev.h[2 * i], cev.h[2 * i + 1])
         if BL.bench_stream_copy(src.data_ptr(), dst.data_ptr(), cn, st) != 0:
             raise RuntimeError("bench_stream_copy failed")
-        e1.record(stream)
-        cps.append((e0, e1))
+    flush(cev.h[44], None)
     torch.cuda.synchronize()
-    copy_ms = sorted(a.elapsed_time(b) for a, b in cps[2:])
+    copy_ms = sorted(cev.ms(2 * i + 1, 2 * i + 2) for i in range(2, 22))
+    cev.close()
     copy_gbps = 2 * cn / (copy_ms[len(copy_ms) // 2] / 1e3) / 1e9
     del src, dst
 
@@ -553,9 +607,10 @@ def main() -> int:
                        site, "fp64"),
                    "outlier_rows": w["outlier_frac"] if site in ("final", "serve") else 0.0,
                    "timing": ("cold caches: before each phase a flush writes and reads back "
-                              f"{FLUSH_BYTES >> 20} MiB; HIP events on the step's stream bracket the forward "
-                              "and the backward phase (flush excluded); ms_per_step = mean over the timed "
-                              "steps of (forward + backward)"),
+                              f"{FLUSH_BYTES >> 20} MiB; a phase runs from the end of the flush before it to the "
+                              "start of the flush after it (HIP events recorded by the flush kernels' own "
+                              "dispatches, so launch gaps inside the phase count and no event packet does); "
+                              "ms_per_step = mean over the timed steps of (forward + backward)"),
                    "step_algorithmic_bytes": step_bytes,
                    "step_gbps": round(gbps(ms_per_step), 1),
                    "step_frac_of_peak": round(gbps(ms_per_step) / HBM_PEAK_GBPS, 4),
@@ -574,7 +629,8 @@ def main() -> int:
                                  "x and W that the forward read there"),
                    "buffer_sets": nsets,
                    "copy_ceiling_gbps": round(copy_gbps, 1),
-                   "copy_ceiling_kernel": "bench_stream_copy: hand-written, 16 B per lane, cold, median of 20",
+                   "copy_ceiling_kernel": ("bench_stream_copy: hand-written, 16 B per lane, after the same flush, "
+                                           "timed as a phase, median of 20"),
                    "step_frac_of_copy_ceiling": round(gbps(ms_per_step) / copy_gbps, 4)},
         "roofline": {"bound": "hbm",
                      "kernel": k_name,
@@ -582,7 +638,12 @@ def main() -> int:
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None if (f32 or site != "final") else pmc_traffic(),
                      "bytes_per_launch": k_bytes, "avg_launch_ms": round(k_mean_ms, 5),
-                     "timed_launches": n_timed, "timed_every": SAMPLE,
+                     "timed_launches": n_k,
+                     "timing": ("HIP events recorded by the dispatch of adaln_norm_mod_bwd_level0 (this kernel "
+                                "alone) on the step's stream, each launch after the same flush as in the step"
+                                if kernel_timed else
+                                "the step's forward + backward phase events (this site has no single dominant "
+                                "kernel timed on its own)"),
                      "median_launch_ms": round(_pct(k_ms, 0.5), 5),
                      "p10_launch_ms": round(_pct(k_ms, 0.1), 5),
                      "p90_launch_ms": round(_pct(k_ms, 0.9), 5)},

@@ -49,7 +49,7 @@ extern "C" {
 
 typedef uint16_t adaln_bf16;
 
-#define ADALN_ABI_VERSION 12
+#define ADALN_ABI_VERSION 13
 
 enum adaln_status {
   ADALN_OK = 0,
@@ -168,6 +168,19 @@ int adaln_norm_mod_bwd_tiles(const adaln_bf16* gout, const adaln_bf16* x, const 
                              int64_t D, void* stream);
 int token_tree_fold(const void* part, size_t part_bytes, float* out, int64_t B, int64_t T0, int64_t H,
                     void* stream);
+
+/* adaln_norm_mod_bwd_level0: the first launch of adaln_norm_mod_bwd alone --
+ * dx and the level-0 pairs of the token tree in one pass over g and x (the
+ * same kernel, the same bytes as adaln_norm_mod_bwd_dx and
+ * adaln_norm_mod_bwd_tiles together); token_tree_fold on `part` then gives
+ * d_emb.  Arguments as in adaln_norm_mod_bwd_dx and _tiles.  ev_start /
+ * ev_stop: optional caller-owned hipEvent_t handles (NULL for none) that the
+ * kernel's dispatch records when it starts and ends -- a timing of this
+ * kernel alone with no event packet in the stream.  The library keeps no
+ * state for them. */
+int adaln_norm_mod_bwd_level0(const adaln_bf16* gout, const adaln_bf16* x, const float* mean, const float* rstd,
+                              const adaln_bf16* emb, adaln_bf16* dx, void* part, size_t part_bytes, int64_t B,
+                              int64_t S, int64_t D, void* ev_start, void* ev_stop, void* stream);
 
 /* Projection backward (pull request 538, "What": projection backward; review
  * thread: silu'(z) = sigmoid(z) * (1 + z * (1 - sigmoid(z)))).
@@ -341,25 +354,6 @@ int adaln_fwd_proj_out(const adaln_bf16* temb, const adaln_bf16* W, const adaln_
                        const adaln_bf16* Wp, const adaln_bf16* bp, adaln_bf16* emb, adaln_bf16* latent, float* mean,
                        float* rstd, void* ws, size_t ws_bytes, int64_t B, int64_t S, int64_t D, int64_t O, float eps,
                        void* stream);
-
-/* Benchmarking aid: per-launch durations of the main kernel of the backward
- * (adaln_bwd, adaln_bwd_f32 and adaln_norm_mod_bwd: the fused dx + level-0 kernel;
- * adaln_norm_mod_bwd_dx: the dx kernel; adaln_residual_bwd: the dh / dx +
- * level-0 kernel, and adaln_site_bwd; adaln_proj_bwd with B <= 4: its first
- * kernel (da leaf groups and dW tiles);
- * adaln_proj_out_bwd: the kernel computing d_out and the dWp partial sums;
- * adaln_fwd_proj_out: the kernel that
- * modulates and multiplies), timed with HIP
- * events carried by the kernel dispatch itself (no extra packets).
- * A timed dispatch leaves the stream idle for a few microseconds around it, so
- * timing can be sampled: adaln_timing_begin(n, stride) creates n event pairs;
- * launches number 0, stride, 2*stride, ... (counted from this call, on any
- * stream) record into them until n are used.  adaln_timing_end(ms, n) waits
- * for the recorded launches, writes up to n durations in milliseconds, frees
- * the events and returns the number written.  Events are host-side HIP
- * objects; no device memory. */
-int adaln_timing_begin(int n, int stride);
-int adaln_timing_end(float* ms, int n);
 
 /* adaln_norm_mod_bwd for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid

@@ -8,7 +8,6 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
-#include <mutex>
 #include <vector>
 
 #include "../../include/adaln.h"
@@ -28,41 +27,6 @@ constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_verdict[kMaxDevices];    // 0 unknown, 1 gfx950, 2 other
 std::atomic<int> g_probe_verdict[kMaxDevices];   // 0 unknown, 1 pass, 2 fail
 std::atomic<int> g_probe_failures[kMaxDevices];
-
-// Dispatch-attached timing of the norm backward's row pass (a benchmarking
-// aid): while armed, each launch records into the next free event pair.
-struct Timing {
-  std::mutex mu;
-  std::vector<hipEvent_t> start, stop;
-  size_t next = 0;     // next free event pair
-  int64_t seen = 0;    // launches since adaln_timing_begin
-  int64_t stride = 1;  // record every stride-th launch
-};
-Timing g_timing;
-
-void timing_events(hipEvent_t* a, hipEvent_t* b) {
-  std::lock_guard<std::mutex> lock(g_timing.mu);
-  const bool pick = g_timing.next < g_timing.start.size() && g_timing.seen % g_timing.stride == 0;
-  if (!g_timing.start.empty()) ++g_timing.seen;
-  if (pick) {
-    *a = g_timing.start[g_timing.next];
-    *b = g_timing.stop[g_timing.next];
-    ++g_timing.next;
-  } else {
-    *a = nullptr;
-    *b = nullptr;
-  }
-}
-
-void timing_free_locked() {
-  for (hipEvent_t e : g_timing.start) (void)hipEventDestroy(e);
-  for (hipEvent_t e : g_timing.stop) (void)hipEventDestroy(e);
-  g_timing.start.clear();
-  g_timing.stop.clear();
-  g_timing.next = 0;
-  g_timing.seen = 0;
-  g_timing.stride = 1;
-}
 
 inline size_t pad256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -330,9 +294,7 @@ int adaln_norm_mod_bwd_dx(const adaln_bf16* gout, const adaln_bf16* x, const flo
     return rc;
   if (int rc = check_device()) return rc;
   (void)hipGetLastError();
-  hipEvent_t e0, e1;
-  timing_events(&e0, &e1);
-  return launched(adaln::launch_norm_mod_bwd_dx(gout, x, mean, rstd, emb, dx, B, S, as_stream(stream), e0, e1));
+  return launched(adaln::launch_norm_mod_bwd_dx(gout, x, mean, rstd, emb, dx, B, S, as_stream(stream)));
 }
 
 int adaln_norm_mod_bwd_tiles(const adaln_bf16* gout, const adaln_bf16* x, const float* mean,
@@ -352,6 +314,28 @@ int adaln_norm_mod_bwd_tiles(const adaln_bf16* gout, const adaln_bf16* x, const 
   (void)hipGetLastError();
   return launched(adaln::launch_norm_mod_bwd_tiles(gout, x, mean, rstd, static_cast<float*>(part), B, S,
                                                    as_stream(stream)));
+}
+
+int adaln_norm_mod_bwd_level0(const adaln_bf16* gout, const adaln_bf16* x, const float* mean, const float* rstd,
+                              const adaln_bf16* emb, adaln_bf16* dx, void* part, size_t part_bytes, int64_t B,
+                              int64_t S, int64_t D, void* ev_start, void* ev_stop, void* stream) {
+  if (!gout || !x || !mean || !rstd || !emb || !dx || !part) return ADALN_ERR_NULL;
+  if (!batch_ok(B) || !seq_ok(S) || D != kD) return ADALN_ERR_SHAPE;
+  if (!aligned16(gout) || !aligned16(x) || !aligned16(mean) || !aligned16(rstd) || !aligned16(emb) ||
+      !aligned16(dx) || !aligned16(part))
+    return ADALN_ERR_ALIGN;
+  const size_t need = ws_norm_bwd(B, S);
+  if (part_bytes < need) return ADALN_ERR_WORKSPACE;
+  const size_t rows = static_cast<size_t>(B * S);
+  if (int rc = check_overlap({{dx, rows * kD * 2}, {part, need}},
+                             {{gout, rows * kD * 2}, {x, rows * kD * 2}, {mean, rows * 4}, {rstd, rows * 4},
+                              {emb, static_cast<size_t>(B * kN * 2)}}))
+    return rc;
+  if (int rc = check_device()) return rc;
+  (void)hipGetLastError();
+  return launched(adaln::launch_norm_mod_bwd(gout, x, mean, rstd, emb, dx, static_cast<float*>(part), B, S,
+                                             as_stream(stream), static_cast<hipEvent_t>(ev_start),
+                                             static_cast<hipEvent_t>(ev_stop)));
 }
 
 int token_tree_fold(const void* part, size_t part_bytes, float* out, int64_t B, int64_t T0, int64_t H,
@@ -385,10 +369,8 @@ int adaln_norm_mod_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float*
     return rc;
   if (int rc = check_device()) return rc;
   (void)hipGetLastError();
-  hipEvent_t e0, e1;
-  timing_events(&e0, &e1);
   if (int rc = launched(adaln::launch_norm_mod_bwd(gout, x, mean, rstd, emb, dx, static_cast<float*>(ws), B, S,
-                                                   as_stream(stream), e0, e1)))
+                                                   as_stream(stream))))
     return rc;
   return token_tree_fold(ws, need, d_emb, B, ceil_div(S, kTile), kN, stream);
 }
@@ -413,10 +395,7 @@ int adaln_proj_bwd(const float* d_emb, const adaln_bf16* temb, const adaln_bf16*
   uint16_t* a = static_cast<uint16_t*>(ws);
   const hipStream_t s = as_stream(stream);
   if (B <= adaln::proj_bwd_fused_max_batch()) {
-    hipEvent_t e0, e1;
-    timing_events(&e0, &e1);
-    return launched(adaln::launch_proj_bwd_fused(d_emb, temb, W, dW, db, dtemb, static_cast<double*>(ws), B, N, s,
-                                                 e0, e1));
+    return launched(adaln::launch_proj_bwd_fused(d_emb, temb, W, dW, db, dtemb, static_cast<double*>(ws), B, N, s));
   }
   if (int rc = launched(adaln::launch_silu(temb, a, B * kD, s))) return rc;
   if (int rc = launched(adaln::launch_proj_bwd_dw(d_emb, a, dW, db, B, N, s))) return rc;
@@ -440,42 +419,6 @@ int token_tree_sum(const float* x, float* out, void* ws, size_t ws_bytes, int64_
   const hipStream_t s = as_stream(stream);
   if (int rc = launched(adaln::launch_token_level0(x, part, B, S, H, s))) return rc;
   return launched(adaln::launch_tree_fold(part, out, B, T0, H, s));
-}
-
-int adaln_timing_begin(int n, int stride) {
-  if (n < 1 || n > (1 << 20) || stride < 1) return ADALN_ERR_SHAPE;
-  if (int rc = check_device()) return rc;
-  std::lock_guard<std::mutex> lock(g_timing.mu);
-  timing_free_locked();
-  g_timing.stride = stride;
-  for (int i = 0; i < n; ++i) {
-    hipEvent_t a = nullptr, b = nullptr;
-    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
-      if (a) (void)hipEventDestroy(a);
-      if (b) (void)hipEventDestroy(b);
-      timing_free_locked();
-      (void)hipGetLastError();
-      return ADALN_ERR_LAUNCH;
-    }
-    g_timing.start.push_back(a);
-    g_timing.stop.push_back(b);
-  }
-  return ADALN_OK;
-}
-
-int adaln_timing_end(float* ms, int n) {
-  std::lock_guard<std::mutex> lock(g_timing.mu);
-  const int used = static_cast<int>(g_timing.next);
-  int k = 0;
-  for (; ms && k < used && k < n; ++k) {
-    if (hipEventSynchronize(g_timing.stop[k]) != hipSuccess ||
-        hipEventElapsedTime(&ms[k], g_timing.start[k], g_timing.stop[k]) != hipSuccess) {
-      (void)hipGetLastError();
-      break;
-    }
-  }
-  timing_free_locked();
-  return k;
 }
 
 int adaln_fwd(const adaln_bf16* temb, const adaln_bf16* W, const adaln_bf16* bias, const adaln_bf16* x,
@@ -526,11 +469,9 @@ int adaln_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float* mean, co
   const int64_t T0 = ceil_div(S, kTile);
   float* part = static_cast<float*>(ws);
   uint16_t* a = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + n_norm);
-  hipEvent_t e0, e1;
-  timing_events(&e0, &e1);
   // dx rows and level-0 tiles in one launch (g and x read once), the fold,
   // then the projection backward: adaln_norm_mod_bwd then adaln_proj_bwd
-  if (int rc = launched(adaln::launch_norm_mod_bwd(gout, x, mean, rstd, emb, dx, part, B, S, s, e0, e1)))
+  if (int rc = launched(adaln::launch_norm_mod_bwd(gout, x, mean, rstd, emb, dx, part, B, S, s)))
     return rc;
   if (int rc = launched(adaln::launch_tree_fold(part, d_emb, B, T0, kN, s))) return rc;
   if (B <= adaln::proj_bwd_fused_max_batch())
@@ -591,9 +532,7 @@ int adaln_bwd_f32(const float* gout, const float* x, const float* mean, const fl
   const int64_t T0 = ceil_div(S, kTile);
   float* part = static_cast<float*>(ws);
   float* a = reinterpret_cast<float*>(static_cast<char*>(ws) + n_norm);
-  hipEvent_t e0, e1;
-  timing_events(&e0, &e1);
-  if (int rc = launched(adaln::launch_norm_mod_bwd_f32(gout, x, mean, rstd, emb, dx, part, B, S, s, e0, e1)))
+  if (int rc = launched(adaln::launch_norm_mod_bwd_f32(gout, x, mean, rstd, emb, dx, part, B, S, s)))
     return rc;
   if (int rc = launched(adaln::launch_tree_fold(part, d_emb, B, T0, kN, s))) return rc;
   double* sub = reinterpret_cast<double*>(reinterpret_cast<char*>(a) + pad256(static_cast<size_t>(B * kD * 4)));
@@ -681,11 +620,9 @@ int adaln_site_bwd(const adaln_bf16* g_out, const adaln_bf16* g_h, const adaln_b
   (void)hipGetLastError();
   const hipStream_t s = as_stream(stream);
   float* part = static_cast<float*>(ws);
-  hipEvent_t e0, e1;
-  timing_events(&e0, &e1);
   const adaln::ModView mv{nullptr, scale, res ? gate : nullptr, mod_ld};
   if (int rc = launched(adaln::launch_site_bwd(g_out, g_h, x, res ? h : x, mean, rstd, mv, res ? d_residual : nullptr,
-                                               dx, part, B, S, s, e0, e1)))
+                                               dx, part, B, S, s)))
     return rc;
   return launched(adaln::launch_tree_fold_views(part, d_shift, d_scale, res ? d_gate : nullptr, dmod_ld, B,
                                                 ceil_div(S, kTile), nseg, s));
@@ -739,10 +676,7 @@ int adaln_proj_out_bwd(const adaln_bf16* d_lat, const adaln_bf16* out, const ada
   (void)hipGetLastError();
   double* part = static_cast<double*>(ws);
   double* part_db = reinterpret_cast<double*>(static_cast<unsigned char*>(ws) + ws_proj_out_db_offset(T));
-  hipEvent_t e0, e1;
-  timing_events(&e0, &e1);
-  return launched(adaln::launch_proj_out_bwd(d_lat, out, W, d_out, dW, db, part, part_db, T, as_stream(stream), e0,
-                                             e1));
+  return launched(adaln::launch_proj_out_bwd(d_lat, out, W, d_out, dW, db, part, part_db, T, as_stream(stream)));
 }
 
 int adaln_fwd_proj_out(const adaln_bf16* temb, const adaln_bf16* W, const adaln_bf16* bias, const adaln_bf16* x,
@@ -769,9 +703,7 @@ int adaln_fwd_proj_out(const adaln_bf16* temb, const adaln_bf16* W, const adaln_
   const hipStream_t s = as_stream(stream);
   uint16_t* a = static_cast<uint16_t*>(ws);
   if (int rc = launched(adaln::launch_fwd_stats(temb, W, bias, x, emb, mean, rstd, a, B, S, eps, s))) return rc;
-  hipEvent_t e0, e1;
-  timing_events(&e0, &e1);
-  return launched(adaln::launch_proj_out_fwd_fused(x, emb, mean, rstd, Wp, bp, latent, B, S, s, e0, e1));
+  return launched(adaln::launch_proj_out_fwd_fused(x, emb, mean, rstd, Wp, bp, latent, B, S, s));
 }
 
 int adaln_selftest(void) {

@@ -6,10 +6,13 @@
 //   the 256 MB memory-side cache held before is gone and the dirty lines the
 //   write left behind are written back during the flush, not during the
 //   phase that follows.  Pass a buffer of at least twice the memory-side
-//   cache.
+//   cache.  Optional caller events are recorded by the flush's own dispatches
+//   (the start of its first kernel, the end of its last), so a phase between
+//   two flushes is timed with no event packet inside it.
 // bench_stream_copy: a plain device copy, 16 bytes per lane, four loads in
 //   flight per lane before the four stores: the bandwidth a stream of equal
 //   bytes reaches on this part, the ceiling the step is set against.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -64,15 +67,16 @@ extern "C" {
 
 // 0 on success, -1 for a bad argument (NULL, size not a positive multiple of
 // 16 bytes, pointer not 16-byte aligned), -7 for a launch error.
-int bench_flush(void* buf, size_t bytes, void* stream) {
+int bench_flush(void* buf, size_t bytes, void* ev_start, void* ev_end, void* stream) {
   if (!buf || bytes == 0 || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(buf) % 16 != 0) return -1;
   const int64_t n16 = static_cast<int64_t>(bytes / 16);
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  static uint32_t round = 0;
-  hipLaunchKernelGGL(fill_kernel, dim3(grid_for(n16)), dim3(kThreads), 0, s, static_cast<uint4*>(buf), n16,
-                     0x01010101u * (++round & 0x7fu));
-  hipLaunchKernelGGL(read_kernel, dim3(grid_for(n16)), dim3(kThreads), 0, s, static_cast<const uint4*>(buf), n16,
-                     static_cast<uint32_t*>(buf));
+  const uint32_t v = 0x5a5a5a5au;
+  hipExtLaunchKernelGGL(fill_kernel, dim3(grid_for(n16)), dim3(kThreads), 0, s,
+                        reinterpret_cast<hipEvent_t>(ev_start), nullptr, 0, static_cast<uint4*>(buf), n16, v);
+  hipExtLaunchKernelGGL(read_kernel, dim3(grid_for(n16)), dim3(kThreads), 0, s, nullptr,
+                        reinterpret_cast<hipEvent_t>(ev_end), 0, static_cast<const uint4*>(buf), n16,
+                        static_cast<uint32_t*>(buf));
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 
@@ -85,5 +89,21 @@ int bench_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
                      static_cast<const uint4*>(src), static_cast<uint4*>(dst), n16);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
+
+// Timing events for the flushes and for adaln_norm_mod_bwd_level0 (created
+// with timing enabled; milliseconds between two recorded events after the
+// stream has reached both).
+int bench_event_create(void** ev) {
+  hipEvent_t e = nullptr;
+  if (!ev || hipEventCreate(&e) != hipSuccess) return -7;
+  *ev = e;
+  return 0;
+}
+int bench_event_elapsed(void* a, void* b, float* ms) {
+  if (hipEventSynchronize(reinterpret_cast<hipEvent_t>(b)) != hipSuccess) return -7;
+  return hipEventElapsedTime(ms, reinterpret_cast<hipEvent_t>(a), reinterpret_cast<hipEvent_t>(b)) == hipSuccess ? 0
+                                                                                                                   : -7;
+}
+int bench_event_destroy(void* ev) { return hipEventDestroy(reinterpret_cast<hipEvent_t>(ev)) == hipSuccess ? 0 : -7; }
 
 }  // extern "C"

@@ -20,7 +20,6 @@
 // (i = 0 .. 11) of its row; row sums run over them in that order in fp64,
 // then wave_sum_f64.  Level-0 tiles: Neumaier over the tile's tokens in
 // ascending order, per column.  No order depends on the batch size.
-#include <hip/hip_ext.h>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -382,19 +381,13 @@ hipError_t launch_norm_mod_fwd_f32(const float* x, const float* emb, float* out,
 
 hipError_t launch_norm_mod_bwd_f32(const float* g, const float* x, const float* mean, const float* rstd,
                                    const float* emb, float* dx, float* part, int64_t B, int64_t S,
-                                   hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+                                   hipStream_t s) {
   static_assert(kD % kColBlockCols == 0, "column blocks must tile D");
   const int64_t T0 = (S + kTile - 1) / kTile;
   const int64_t groups = (B * T0 + 7) / 8;
   const dim3 grid(static_cast<unsigned>(groups * 8 * kBlocksPerTile));
-  if (e0 != nullptr && e1 != nullptr) {
-    // events carried by the dispatch itself: no extra barrier in the stream
-    hipExtLaunchKernelGGL(norm_mod_bwd_f32_kernel, grid, dim3(kThreads), 0, s, e0, e1, 0, g, x, mean, rstd,
-                          emb, dx, part, B, S, T0);
-  } else {
-    hipLaunchKernelGGL(norm_mod_bwd_f32_kernel, grid, dim3(kThreads), 0, s, g, x, mean, rstd, emb, dx, part,
-                       B, S, T0);
-  }
+  hipLaunchKernelGGL(norm_mod_bwd_f32_kernel, grid, dim3(kThreads), 0, s, g, x, mean, rstd, emb, dx, part, B, S,
+                     T0);
   return hipGetLastError();
 }
 

@@ -24,12 +24,11 @@ hipError_t launch_norm_mod_fwd(const uint16_t* x, const uint16_t* emb, uint16_t*
                                hipStream_t s);
 hipError_t launch_norm_mod_bwd(const uint16_t* g, const uint16_t* x, const float* mean,
                                const float* rstd, const uint16_t* emb, uint16_t* dx, float* part,
-                               int64_t B, int64_t S, hipStream_t s,
-                               hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+                               int64_t B, int64_t S, hipStream_t s, hipEvent_t ev_start = nullptr,
+                               hipEvent_t ev_stop = nullptr);
 hipError_t launch_norm_mod_bwd_dx(const uint16_t* g, const uint16_t* x, const float* mean,
                                   const float* rstd, const uint16_t* emb, uint16_t* dx, int64_t B,
-                                  int64_t S, hipStream_t s, hipEvent_t ev_start = nullptr,
-                                  hipEvent_t ev_stop = nullptr);
+                                  int64_t S, hipStream_t s);
 hipError_t launch_norm_mod_bwd_tiles(const uint16_t* g, const uint16_t* x, const float* mean,
                                      const float* rstd, float* part, int64_t B,
                                      int64_t S, hipStream_t s);
@@ -45,7 +44,7 @@ int proj_bwd_fused_max_batch();
 size_t proj_bwd_fused_sub_bytes(int64_t B);
 hipError_t launch_proj_bwd_fused(const float* d_emb, const uint16_t* temb, const uint16_t* W,
                                  uint16_t* dW, uint16_t* db, uint16_t* dtemb, double* sub, int64_t B, int64_t N,
-                                 hipStream_t s, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+                                 hipStream_t s);
 hipError_t launch_proj_bwd_dw(const float* d_emb, const uint16_t* a, uint16_t* dW, uint16_t* db,
                               int64_t B, int64_t N, hipStream_t s);
 hipError_t launch_proj_bwd_da(const float* d_emb, const uint16_t* W, const uint16_t* temb,
@@ -68,8 +67,7 @@ hipError_t launch_site_fwd(const uint16_t* x, const uint16_t* residual, ModView 
 // scale; the LayerNorm input is x, h and d_residual unused)
 hipError_t launch_site_bwd(const uint16_t* g_out, const uint16_t* g_h, const uint16_t* x, const uint16_t* h,
                            const float* mean, const float* rstd, ModView mv, uint16_t* d_residual, uint16_t* dx,
-                           float* part, int64_t B, int64_t S, hipStream_t s, hipEvent_t ev_start = nullptr,
-                           hipEvent_t ev_stop = nullptr);
+                           float* part, int64_t B, int64_t S, hipStream_t s);
 // proj_out (3072 -> 64 per token) on the fp64 matrix cores.  Backward part:
 // proj_out_chunks(T) x 64 x 3072 fp64 (the dWp chunk partials), part_db:
 // proj_out_chunks(T) x 64 fp64
@@ -78,12 +76,11 @@ int64_t proj_out_chunks(int64_t T);
 // stored): the same bytes as launch_proj_out_fwd on the modulated output
 hipError_t launch_proj_out_fwd_fused(const uint16_t* x, const uint16_t* emb, const float* mean, const float* rstd,
                                      const uint16_t* W, const uint16_t* bias, uint16_t* latent, int64_t B, int64_t S,
-                                     hipStream_t s, hipEvent_t e0, hipEvent_t e1);
+                                     hipStream_t s);
 hipError_t launch_proj_out_fwd(const uint16_t* out, const uint16_t* W, const uint16_t* bias, uint16_t* latent,
                                int64_t T, hipStream_t s);
 hipError_t launch_proj_out_bwd(const uint16_t* d_lat, const uint16_t* out, const uint16_t* W, uint16_t* d_out,
-                               uint16_t* dW, uint16_t* db, double* part, double* part_db, int64_t T, hipStream_t s,
-                               hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+                               uint16_t* dW, uint16_t* db, double* part, double* part_db, int64_t T, hipStream_t s);
 // fp32 storage
 hipError_t launch_silu_f32(const float* temb, float* a, int64_t n, hipStream_t s);
 // B <= 4: the fp32-storage projection on the vector units (same bits as the matrix-core kernel)
@@ -95,7 +92,7 @@ hipError_t launch_norm_mod_fwd_f32(const float* x, const float* emb, float* out,
                                    int64_t B, int64_t S, float eps, hipStream_t s);
 hipError_t launch_norm_mod_bwd_f32(const float* g, const float* x, const float* mean, const float* rstd,
                                    const float* emb, float* dx, float* part, int64_t B, int64_t S,
-                                   hipStream_t s, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+                                   hipStream_t s);
 hipError_t launch_proj_bwd_f32(const float* d_emb, const float* temb, const float* W, float* a, float* dW,
                                float* db, float* dtemb, double* sub, int64_t B, hipStream_t s);   // sub: B <= 4
 hipError_t launch_selftest_probe(const float* in, float* out, uint32_t* bits, int n,

@@ -123,19 +123,15 @@ __global__ __launch_bounds__(kThreads) void norm_mod_bwd_kernel(
 template <int kRole>
 hipError_t launch_role(const uint16_t* g, const uint16_t* x, const float* mean, const float* rstd,
                        const uint16_t* emb, uint16_t* dx, float* part, int64_t B,
-                       int64_t S, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+                       int64_t S, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
   constexpr int bpt = kRole == kBoth ? kBlocksPerTile : (kRole == kRowsOnly ? kRowBlocks : kColBlocks);
   const int64_t T0 = (S + kTile - 1) / kTile;
   const int64_t groups = (B * T0 + 7) / 8;
   const dim3 grid(static_cast<unsigned>(groups * 8 * bpt));
-  if (e0 != nullptr && e1 != nullptr) {
-    // events carried by the dispatch itself: no extra barrier in the stream
-    hipExtLaunchKernelGGL(norm_mod_bwd_kernel<kRole>, grid, dim3(kThreads), 0, s, e0, e1, 0, g, x, mean,
-                          rstd, emb, dx, part, B, S, T0);
-  } else {
-    hipLaunchKernelGGL(norm_mod_bwd_kernel<kRole>, grid, dim3(kThreads), 0, s, g, x, mean, rstd, emb, dx,
-                       part, B, S, T0);
-  }
+  // events, when given, are recorded by the dispatch itself: no packet of
+  // their own in the stream
+  hipExtLaunchKernelGGL(norm_mod_bwd_kernel<kRole>, grid, dim3(kThreads), 0, s, e0, e1, 0, g, x, mean, rstd, emb, dx,
+                        part, B, S, T0);
   return hipGetLastError();
 }
 
@@ -144,23 +140,21 @@ hipError_t launch_role(const uint16_t* g, const uint16_t* x, const float* mean, 
 
 hipError_t launch_norm_mod_bwd(const uint16_t* g, const uint16_t* x, const float* mean,
                                const float* rstd, const uint16_t* emb, uint16_t* dx, float* part,
-                               int64_t B, int64_t S, hipStream_t s, hipEvent_t e0,
-                               hipEvent_t e1) {
+                               int64_t B, int64_t S, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   static_assert(kD % kColBlockCols == 0, "column blocks must tile D");
   return launch_role<kBoth>(g, x, mean, rstd, emb, dx, part, B, S, s, e0, e1);
 }
 
 hipError_t launch_norm_mod_bwd_dx(const uint16_t* g, const uint16_t* x, const float* mean,
                                   const float* rstd, const uint16_t* emb, uint16_t* dx, int64_t B,
-                                  int64_t S, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  return launch_role<kRowsOnly>(g, x, mean, rstd, emb, dx, nullptr, B, S, s, e0, e1);
+                                  int64_t S, hipStream_t s) {
+  return launch_role<kRowsOnly>(g, x, mean, rstd, emb, dx, nullptr, B, S, s);
 }
 
 hipError_t launch_norm_mod_bwd_tiles(const uint16_t* g, const uint16_t* x, const float* mean,
                                      const float* rstd, float* part, int64_t B,
                                      int64_t S, hipStream_t s) {
-  return launch_role<kColsOnly>(g, x, mean, rstd, nullptr, nullptr, part, B, S, s, nullptr,
-                                nullptr);
+  return launch_role<kColsOnly>(g, x, mean, rstd, nullptr, nullptr, part, B, S, s);
 }
 
 

@@ -25,7 +25,6 @@
 //   da_leaf_f32_kernel<NB>     fp32 storage, B <= 4: the leaf-group blocks alone
 //                              (then da_finish_kernel<NB, float>)
 //   silu_kernel, dw_mfma_kernel, da_mfma_kernel   B > 4
-#include <hip/hip_ext.h>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -565,13 +564,9 @@ namespace {
 
 template <int NB, int N>
 hipError_t launch_small(const float* d_emb, const uint16_t* temb, const uint16_t* W, uint16_t* dW, uint16_t* db,
-                        uint16_t* dtemb, double* sub, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+                        uint16_t* dtemb, double* sub, hipStream_t s) {
   const dim3 grid(kDaLeafBlocks + kDwTiles<N>), block(kThreads);
-  if (e0 && e1)
-    hipExtLaunchKernelGGL((proj_bwd_small_kernel<NB, N>), grid, block, 0, s, e0, e1, 0, d_emb, temb, W, dW, db,
-                          sub);
-  else
-    hipLaunchKernelGGL((proj_bwd_small_kernel<NB, N>), grid, block, 0, s, d_emb, temb, W, dW, db, sub);
+  hipLaunchKernelGGL((proj_bwd_small_kernel<NB, N>), grid, block, 0, s, d_emb, temb, W, dW, db, sub);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   hipLaunchKernelGGL(da_finish_kernel<NB>, dim3((NB * kD + 255) / 256), dim3(256), 0, s, sub, temb, dtemb);
   return hipGetLastError();
@@ -579,13 +574,12 @@ hipError_t launch_small(const float* d_emb, const uint16_t* temb, const uint16_t
 
 template <int N>
 hipError_t proj_bwd_fused_rows(const float* d_emb, const uint16_t* temb, const uint16_t* W, uint16_t* dW,
-                               uint16_t* db, uint16_t* dtemb, double* sub, int64_t B, hipStream_t s,
-                               hipEvent_t e0, hipEvent_t e1) {
+                               uint16_t* db, uint16_t* dtemb, double* sub, int64_t B, hipStream_t s) {
   switch (B) {
-    case 1: return launch_small<1, N>(d_emb, temb, W, dW, db, dtemb, sub, s, e0, e1);
-    case 2: return launch_small<2, N>(d_emb, temb, W, dW, db, dtemb, sub, s, e0, e1);
-    case 3: return launch_small<3, N>(d_emb, temb, W, dW, db, dtemb, sub, s, e0, e1);
-    case 4: return launch_small<4, N>(d_emb, temb, W, dW, db, dtemb, sub, s, e0, e1);
+    case 1: return launch_small<1, N>(d_emb, temb, W, dW, db, dtemb, sub, s);
+    case 2: return launch_small<2, N>(d_emb, temb, W, dW, db, dtemb, sub, s);
+    case 3: return launch_small<3, N>(d_emb, temb, W, dW, db, dtemb, sub, s);
+    case 4: return launch_small<4, N>(d_emb, temb, W, dW, db, dtemb, sub, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -613,9 +607,9 @@ size_t proj_bwd_fused_sub_bytes(int64_t B) { return static_cast<size_t>(kDaGroup
 
 hipError_t launch_proj_bwd_fused(const float* d_emb, const uint16_t* temb, const uint16_t* W,
                                  uint16_t* dW, uint16_t* db, uint16_t* dtemb, double* sub, int64_t B, int64_t N,
-                                 hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  if (N == kN) return proj_bwd_fused_rows<kN>(d_emb, temb, W, dW, db, dtemb, sub, B, s, e0, e1);
-  if (N == kN6) return proj_bwd_fused_rows<kN6>(d_emb, temb, W, dW, db, dtemb, sub, B, s, e0, e1);
+                                 hipStream_t s) {
+  if (N == kN) return proj_bwd_fused_rows<kN>(d_emb, temb, W, dW, db, dtemb, sub, B, s);
+  if (N == kN6) return proj_bwd_fused_rows<kN6>(d_emb, temb, W, dW, db, dtemb, sub, B, s);
   return hipErrorInvalidValue;
 }
 

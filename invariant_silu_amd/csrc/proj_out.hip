@@ -29,8 +29,6 @@
 //           fp64 in ascending order (a second launch), then rounded to fp32
 //           and to bf16; dbp the same with fp64 sums of the chunk's tokens.
 //           Trailing tokens whose d_lat is zero add exact zeros.
-#include <hip/hip_ext.h>
-
 #include "common.hpp"
 #include "launch.hpp"
 #include "mfma.hpp"
@@ -424,31 +422,21 @@ hipError_t launch_proj_out_fwd(const uint16_t* out, const uint16_t* W, const uin
 
 hipError_t launch_proj_out_fwd_fused(const uint16_t* x, const uint16_t* emb, const float* mean, const float* rstd,
                                      const uint16_t* W, const uint16_t* bias, uint16_t* latent, int64_t B, int64_t S,
-                                     hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+                                     hipStream_t s) {
   const int64_t T = B * S;
-  const dim3 grid(static_cast<unsigned>((T + kFT - 1) / kFT));
-  if (e0 && e1)
-    hipExtLaunchKernelGGL(proj_out_fused_kernel, grid, dim3(kFwdThreads), 0, s, e0, e1, 0, x, emb, mean, rstd,
-                          W, bias, latent, T, S);
-  else
-    hipLaunchKernelGGL(proj_out_fused_kernel, grid, dim3(kFwdThreads), 0, s, x, emb, mean, rstd, W, bias,
-                       latent, T, S);
+  hipLaunchKernelGGL(proj_out_fused_kernel, dim3(static_cast<unsigned>((T + kFT - 1) / kFT)), dim3(kFwdThreads), 0, s,
+                     x, emb, mean, rstd, W, bias, latent, T, S);
   return hipGetLastError();
 }
 
 hipError_t launch_proj_out_bwd(const uint16_t* d_lat, const uint16_t* out, const uint16_t* W, uint16_t* d_out,
-                               uint16_t* dW, uint16_t* db, double* part, double* part_db, int64_t T, hipStream_t s,
-                               hipEvent_t e0, hipEvent_t e1) {
+                               uint16_t* dW, uint16_t* db, double* part, double* part_db, int64_t T, hipStream_t s) {
   const int64_t chunks = proj_out_chunks(T);
   const int64_t dw_blocks = kDwColBlocks * chunks;
   const int64_t dx_blocks = (T + kDxTokens - 1) / kDxTokens * (kD / kDxCols);
   const dim3 grid(static_cast<unsigned>(dw_blocks + dx_blocks));
-  if (e0 && e1)
-    hipExtLaunchKernelGGL(proj_out_bwd_kernel, grid, dim3(kBwdThreads), 0, s, e0, e1, 0, d_lat, out, W, d_out, part,
-                          part_db, T, dw_blocks);
-  else
-    hipLaunchKernelGGL(proj_out_bwd_kernel, grid, dim3(kBwdThreads), 0, s, d_lat, out, W, d_out, part, part_db, T,
-                       dw_blocks);
+  hipLaunchKernelGGL(proj_out_bwd_kernel, grid, dim3(kBwdThreads), 0, s, d_lat, out, W, d_out, part, part_db, T,
+                     dw_blocks);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   hipLaunchKernelGGL(proj_out_dw_combine_kernel, dim3(kO * kD / 2 / 256), dim3(256), 0, s, part, part_db, dW, db,
                      chunks);

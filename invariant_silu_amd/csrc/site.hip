@@ -1,6 +1,5 @@
 // Backward of a block's norm sites (the forward is site_fwd_kernel in fwd.hip;
 // reading of miles_diffusion pull request 108, "Fused-norm rounding points").
-#include <hip/hip_ext.h>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -202,31 +201,27 @@ __global__ __launch_bounds__(kThreads) void gate_tile_kernel(const uint16_t* __r
 
 namespace {
 template <bool kRes>
-void launch_site_bwd_kernel(dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const uint16_t* g_out,
+void launch_site_bwd_kernel(dim3 grid, hipStream_t s, const uint16_t* g_out,
                             const uint16_t* g_h, const uint16_t* x, const uint16_t* h, const float* mean,
                             const float* rstd, const ModView& mv, uint16_t* d_residual, uint16_t* dx, float* part,
                             int64_t B, int64_t S, int64_t T0) {
-  if (e0 && e1)
-    hipExtLaunchKernelGGL(site_bwd_kernel<kRes>, grid, dim3(kThreads), 0, s, e0, e1, 0, g_out, g_h, x, h, mean,
-                          rstd, mv, d_residual, dx, part, B, S, T0);
-  else
-    hipLaunchKernelGGL(site_bwd_kernel<kRes>, grid, dim3(kThreads), 0, s, g_out, g_h, x, h, mean, rstd, mv,
-                       d_residual, dx, part, B, S, T0);
+  hipLaunchKernelGGL(site_bwd_kernel<kRes>, grid, dim3(kThreads), 0, s, g_out, g_h, x, h, mean, rstd, mv, d_residual,
+                     dx, part, B, S, T0);
 }
 }  // namespace
 
 hipError_t launch_site_bwd(const uint16_t* g_out, const uint16_t* g_h, const uint16_t* x, const uint16_t* h,
                            const float* mean, const float* rstd, ModView mv, uint16_t* d_residual, uint16_t* dx,
-                           float* part, int64_t B, int64_t S, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+                           float* part, int64_t B, int64_t S, hipStream_t s) {
   const int64_t T0 = (S + kTile - 1) / kTile;
   const int64_t groups = (B * T0 + 7) / 8;
   const dim3 grid(static_cast<unsigned>(groups * 8 * kBlocksPerTile));
   if (!g_h) {   // plain form: the LayerNorm input is x
-    launch_site_bwd_kernel<false>(grid, s, e0, e1, g_out, nullptr, nullptr, x, mean, rstd, mv, nullptr, dx, part,
+    launch_site_bwd_kernel<false>(grid, s, g_out, nullptr, nullptr, x, mean, rstd, mv, nullptr, dx, part,
                                   B, S, T0);
     return hipGetLastError();
   }
-  launch_site_bwd_kernel<true>(grid, s, e0, e1, g_out, g_h, x, h, mean, rstd, mv, d_residual, dx, part, B, S, T0);
+  launch_site_bwd_kernel<true>(grid, s, g_out, g_h, x, h, mean, rstd, mv, d_residual, dx, part, B, S, T0);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   hipLaunchKernelGGL(gate_tile_kernel, dim3(static_cast<unsigned>(B * T0 * kColBlocks)), dim3(kThreads), 0, s,
                      d_residual, x, part, S, T0);

@@ -24,8 +24,7 @@ EXPORTS = ("adaln_fwd", "adaln_bwd", "adaln_fwd_f32", "adaln_bwd_f32", "adaln_re
            "adaln_proj_out_fwd", "adaln_proj_out_bwd", "adaln_fwd_proj_out", "adaln_proj_fwd", "adaln_norm_mod_fwd", "adaln_norm_mod_bwd", "adaln_proj_bwd",
            "token_tree_sum", "adaln_norm_mod_bwd_dx", "adaln_norm_mod_bwd_tiles", "token_tree_fold",
            "adaln_norm_mod_bwd_noalloc",
-           "adaln_workspace_bytes", "adaln_selftest", "adaln_strerror", "adaln_timing_begin",
-           "adaln_timing_end",
+           "adaln_norm_mod_bwd_level0", "adaln_workspace_bytes", "adaln_selftest", "adaln_strerror",
            "adaln_abi_version")
 
 _P = ctypes.c_void_p
@@ -54,8 +53,7 @@ _SIGS = {
     "adaln_norm_mod_bwd_noalloc": ([_P] * 7 + [_I64, _I64, _I64, _P], ctypes.c_int),
     "adaln_workspace_bytes": ([ctypes.c_int, _I64, _I64, _I64], _SZ),
     "adaln_selftest": ([], ctypes.c_int),
-    "adaln_timing_begin": ([ctypes.c_int, ctypes.c_int], ctypes.c_int),
-    "adaln_timing_end": ([ctypes.POINTER(ctypes.c_float), ctypes.c_int], ctypes.c_int),
+    "adaln_norm_mod_bwd_level0": ([_P] * 7 + [_SZ, _I64, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "adaln_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "adaln_abi_version": ([], ctypes.c_int),
 }

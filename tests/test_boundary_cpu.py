@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_strerror(L):
-    assert L.adaln_abi_version() == 12
+    assert L.adaln_abi_version() == 13
     for code in range(-8, 1):
         assert len(lib.strerror(code)) >= 2
 
