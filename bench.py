@@ -522,6 +522,15 @@ def main() -> int:
     fwd_ms = [ev.ms(4 * i + 1, 4 * i + 2) for i in range(n_cold)]
     bwd_ms = [ev.ms(4 * i + 3, 4 * i + 4) for i in range(n_cold)] if not serve_site else [0.0] * n_cold
     ev.close()
+    # the same boundaries with nothing between them: what a phase measured this
+    # way costs when it does no work (reported beside the result, not subtracted)
+    eev = Events(2 * 20 + 1)
+    for i in range(20):
+        flush(eev.h[2 * i], eev.h[2 * i + 1])
+    flush(eev.h[40], None)
+    torch.cuda.synchronize()
+    empty_ms = sorted(eev.ms(2 * i + 1, 2 * i + 2) for i in range(20))
+    eev.close()
     step_ms = [a + b for a, b in zip(fwd_ms, bwd_ms)]
     timed = step_ms[:args.steps]
     ms_per_step = sum(timed) / len(timed)
@@ -621,6 +630,7 @@ def main() -> int:
                    "cold_fwd_median_ms": round(_pct(fwd_ms, 0.5), 5),
                    "cold_bwd_median_ms": round(_pct(bwd_ms, 0.5), 5),
                    "cold_wall_s_incl_flushes": round(t_cold, 3),
+                   "empty_phase_ms": round(empty_ms[len(empty_ms) // 2], 5),
                    "warm_ms_per_step": round(warm_ms, 5),
                    "warm_tokens_per_s": round(units / (warm_ms / 1e3), 1),
                    "warm_step_gbps": round(gbps(warm_ms), 1),
