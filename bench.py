@@ -57,6 +57,7 @@ if ROOT not in sys.path:
 D = 3072
 N = 2 * D
 HBM_PEAK_GBPS = 8000.0
+FP64_MFMA_PEAK_TFLOPS = 78.6   # MI355X dense fp64 matrix peak
 MALL_BYTES = 256 << 20
 MIN_STAT_STEPS = 100   # cold steps behind the median / p10 / p90 (at least)
 MIN_KERNEL_LAUNCHES = 20   # timed launches of the dominant kernel (at least)
@@ -180,13 +181,22 @@ def parse():
 
 
 def cpu_model() -> str:
+    """The host CPU's model name with its family / model / stepping numbers
+    (a virtualised host may report only a short model name)."""
+    info = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = (t.strip() for t in line.split(":", 1))
+                if k in ("model name", "cpu family", "model", "stepping", "vendor_id") and k not in info:
+                    info[k] = v
+            elif info:
+                break
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = info.get("model name", "unknown")
+    ids = ", ".join(f"{k} {info[k]}" for k in ("vendor_id", "cpu family", "model", "stepping") if k in info)
+    return f"{name} ({ids})" if ids else name
 
 
 def _oracle_fns(site: str):
@@ -411,7 +421,7 @@ def main() -> int:
     if serve_site:
         step_bytes, k_bytes = serve_algorithmic_bytes(B, S), serve_dominant_kernel_bytes(B, S)
         fwd_name = bwd_name = "adaln_fwd_proj_out"
-        k_name = "proj_out_fused_part_kernel (modulation into LDS, then the Wp chains)"
+        k_name = "proj_out_fused_kernel (modulation into LDS, then the fp64 Wp chains)"
     elif po_site:
         step_bytes, k_bytes = proj_out_algorithmic_bytes(B * S), proj_out_dominant_kernel_bytes(B * S)
         fwd_name, bwd_name = "adaln_proj_out_fwd", "adaln_proj_out_bwd"
@@ -435,6 +445,11 @@ def main() -> int:
     if not kernel_timed:
         k_name = f"whole step ({fwd_name})" if serve_site else f"whole step ({fwd_name} + {bwd_name})"
         k_bytes = step_bytes
+    # proj_out runs on the fp64 matrix cores and is bound by them, not by HBM:
+    # its roofline is fp64 FLOP/s (2 per multiply-add) of the matrix-core work,
+    # latent (T x 64 x 3072 multiply-adds) in the forward, d_out and dWp in the
+    # backward
+    mfma_flops = (2 * B * S * PO * D * (1 if serve_site else 3)) if (po_site or serve_site) else None
     nsets = max(2, math.ceil(3 * MALL_BYTES / step_bytes))
     sets = [new_set() for _ in range(nsets)]
     stream = torch.cuda.current_stream(dev)
@@ -557,7 +572,10 @@ def main() -> int:
         k_ms = sorted(step_ms)
         n_k = len(k_ms)
     k_mean_ms = sum(k_ms) / len(k_ms)
-    achieved = k_bytes / (k_mean_ms / 1e3) / 1e9
+    if mfma_flops is None:
+        achieved, peak, bound, r_unit = k_bytes / (k_mean_ms / 1e3) / 1e9, HBM_PEAK_GBPS, "hbm", "GB/s"
+    else:
+        achieved, peak, bound, r_unit = mfma_flops / (k_mean_ms / 1e3) / 1e12, FP64_MFMA_PEAK_TFLOPS, "mfma", "TFLOP/s"
 
     # ---- warm: back-to-back steps over the rotating buffer sets, no flush
     for i in range(args.warmup):
@@ -570,21 +588,26 @@ def main() -> int:
     warm_ms = (time.perf_counter() - t0) * 1e3 / args.steps
 
     # ---- ceiling: the hand-written streaming copy of the step's bytes (half
-    # read, half written), after the same flush
-    cn = (step_bytes // 2 + 255) // 256 * 256
-    src = torch.empty(cn, dtype=torch.uint8, device=dev).fill_(1)
-    dst = torch.empty(cn, dtype=torch.uint8, device=dev)
-    cev = Events(2 * 22 + 1)
-    for i in range(22):   # timed as the phases are: flush end to next flush start
-        flush(cev.h[2 * i], cev.h[2 * i + 1])
-        if BL.bench_stream_copy(src.data_ptr(), dst.data_ptr(), cn, st) != 0:
-            raise RuntimeError("bench_stream_copy failed")
-    flush(cev.h[44], None)
-    torch.cuda.synchronize()
-    copy_ms = sorted(cev.ms(2 * i + 1, 2 * i + 2) for i in range(2, 22))
-    cev.close()
-    copy_gbps = 2 * cn / (copy_ms[len(copy_ms) // 2] / 1e3) / 1e9
-    del src, dst
+    # read, half written), after the same flush; and the same copy of four
+    # times those bytes, for how the rate grows with size
+    def copy_rate(total_bytes):
+        cn = (total_bytes // 2 + 255) // 256 * 256
+        src = torch.empty(cn, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty(cn, dtype=torch.uint8, device=dev)
+        cev = Events(2 * 22 + 1)
+        for i in range(22):   # timed as the phases are: flush end to next flush start
+            flush(cev.h[2 * i], cev.h[2 * i + 1])
+            if BL.bench_stream_copy(src.data_ptr(), dst.data_ptr(), cn, st) != 0:
+                raise RuntimeError("bench_stream_copy failed")
+        flush(cev.h[44], None)
+        torch.cuda.synchronize()
+        copy_ms = sorted(cev.ms(2 * i + 1, 2 * i + 2) for i in range(2, 22))
+        cev.close()
+        del src, dst
+        return 2 * cn / (copy_ms[len(copy_ms) // 2] / 1e3) / 1e9
+
+    copy_gbps = copy_rate(step_bytes)
+    copy4_gbps = copy_rate(4 * step_bytes)
 
     if args.copy_calib:
         n = 512 << 20
@@ -612,8 +635,7 @@ def main() -> int:
         "config": {"workload": args.workload, "B": B, "S": None if mod6_site else S, "D": D,
                    "N": {"mod6": N6, "proj_out": PO}.get(site, N), "site": site,
                    "storage": args.storage,
-                   "accumulate": {"proj_out": "fp32", "serve": "fp64 (projection), fp32 (proj_out)"}.get(
-                       site, "fp64"),
+                   "accumulate": "fp64",
                    "outlier_rows": w["outlier_frac"] if site in ("final", "serve") else 0.0,
                    "timing": ("cold caches: before each phase a flush writes and reads back "
                               f"{FLUSH_BYTES >> 20} MiB; a phase runs from the end of the flush before it to the "
@@ -641,13 +663,16 @@ def main() -> int:
                    "copy_ceiling_gbps": round(copy_gbps, 1),
                    "copy_ceiling_kernel": ("bench_stream_copy: hand-written, 16 B per lane, after the same flush, "
                                            "timed as a phase, median of 20"),
+                   "copy_4x_step_bytes_gbps": round(copy4_gbps, 1),
                    "step_frac_of_copy_ceiling": round(gbps(ms_per_step) / copy_gbps, 4)},
-        "roofline": {"bound": "hbm",
+        "roofline": {"bound": bound,
                      "kernel": k_name,
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "achieved": round(achieved, 1 if mfma_flops is None else 2), "peak": peak, "unit": r_unit,
+                     "frac": round(achieved / peak, 4),
                      "traffic": None if (f32 or site != "final") else pmc_traffic(),
-                     "bytes_per_launch": k_bytes, "avg_launch_ms": round(k_mean_ms, 5),
+                     **({"bytes_per_launch": k_bytes} if mfma_flops is None else
+                        {"fp64_flops_per_step": mfma_flops, "step_bytes": k_bytes}),
+                     "avg_launch_ms": round(k_mean_ms, 5),
                      "timed_launches": n_k,
                      "timing": ("HIP events recorded by the dispatch of adaln_norm_mod_bwd_level0 (this kernel "
                                 "alone) on the step's stream, each launch after the same flush as in the step"

@@ -49,7 +49,7 @@ extern "C" {
 
 typedef uint16_t adaln_bf16;
 
-#define ADALN_ABI_VERSION 13
+#define ADALN_ABI_VERSION 14
 
 enum adaln_status {
   ADALN_OK = 0,
@@ -80,6 +80,10 @@ enum adaln_op {
 };
 
 /* Workspace bytes an entry point needs (0 for an unknown op or bad sizes).
+ * The pages' operator allocates its scratch itself (pull request 538, review
+ * thread on det_linear.cu: checks that run after its torch::empty
+ * allocations); this library leaves every allocation to the caller, who sizes
+ * each entry point's scratch with this call.
  *   PROJ_FWD:       H = K (3072), S ignored.  B*K*2 (SiLU activations, used when
  *                   B > 4).
  *   NORM_MOD_BWD:   H = D (3072).  B * ceil(S/32) * 2D * 8 bytes (level-0 pairs).
@@ -201,6 +205,21 @@ int adaln_proj_bwd(const float* d_emb, const adaln_bf16* temb, const adaln_bf16*
                    adaln_bf16* dW, adaln_bf16* db, adaln_bf16* dtemb, void* ws, size_t ws_bytes,
                    int64_t B, int64_t K, int64_t N, void* stream);
 
+/* adaln_proj_bwd that also returns the fp32 values its bf16 outputs are
+ * rounded from (pull request 538, "What": dW, db and dtemb accumulate in
+ * fp32 before their single bf16 rounding; these are those fp32 results):
+ *   dW_f32 [N, K] = fp32(sum_b d_emb_bj * a_bk), db_f32 [N] = fp32(sum_b d_emb_bj),
+ *   dtemb_f32 [B, K] = fp32(sum_j d_emb_bj * W_jk) * silu'(temb) (one fp32 product),
+ * all fp32, 16-byte aligned.  Each may be NULL (not written); with all three
+ * NULL this is adaln_proj_bwd.  The bf16 outputs are the same bytes as
+ * adaln_proj_bwd's and are bf16(the fp32 outputs) exactly.  The fp32 outputs
+ * must not overlap any input, output or the workspace (ADALN_ERR_OVERLAP).
+ * Same shapes, workspace and errors as adaln_proj_bwd. */
+int adaln_proj_bwd_acc(const float* d_emb, const adaln_bf16* temb, const adaln_bf16* W,
+                       adaln_bf16* dW, adaln_bf16* db, adaln_bf16* dtemb, float* dW_f32, float* db_f32,
+                       float* dtemb_f32, void* ws, size_t ws_bytes, int64_t B, int64_t K, int64_t N,
+                       void* stream);
+
 /* Token-sum tree (pull request 538: fixed 32-way tree that depends only on S;
  * review thread: 32-token Neumaier tiles folded level by level, one final add).
  *   x [B, S, H] fp32 (in), out [B, H] fp32 (out).  Any H >= 1.  S = 1 still
@@ -208,9 +227,12 @@ int adaln_proj_bwd(const float* d_emb, const adaln_bf16* temb, const adaln_bf16*
 int token_tree_sum(const float* x, float* out, void* ws, size_t ws_bytes, int64_t B, int64_t S,
                    int64_t H, void* stream);
 
-/* Device check plus strict-math probe (correctly rounded sqrt and divide, no
- * contraction into fused multiply-add, bf16 round-to-nearest-even), run
- * synchronously on the current device.  It is the one entry point that
+/* Device check plus strict-math probe (pull request 538, "Results (H100
+ * sm90 ...)": the build's strict-math probe must report true; its review
+ * thread asks that the probe's verdict be cached on failure as well as on
+ * success, so a refused device is not probed again on every call):
+ * correctly rounded sqrt and divide, no contraction into fused multiply-add,
+ * bf16 round-to-nearest-even, run synchronously on the current device.  It is the one entry point that
  * allocates: 80 KB of device memory for the probe, freed before it returns.
  * The verdict is cached per device, both ways.  Returns ADALN_OK,
  * ADALN_ERR_DEVICE, or a positive count of failed probe values. */
@@ -374,7 +396,9 @@ int adaln_norm_mod_bwd_noalloc(const adaln_bf16* gout, const adaln_bf16* x, cons
                                const float* rstd, const adaln_bf16* emb, adaln_bf16* dx, float* d_emb,
                                int64_t B, int64_t S, int64_t D, void* stream);
 
-/* Static description of a status code. */
+/* Static description of a status code (pull request 538, "What": the
+ * operator has no fallback and other platforms fail closed, so every refusal
+ * reaches the caller; this names its reason). */
 const char* adaln_strerror(int status);
 
 /* ADALN_ABI_VERSION of the loaded library. */

@@ -375,31 +375,49 @@ int adaln_norm_mod_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float*
   return token_tree_fold(ws, need, d_emb, B, ceil_div(S, kTile), kN, stream);
 }
 
-int adaln_proj_bwd(const float* d_emb, const adaln_bf16* temb, const adaln_bf16* W,
-                   adaln_bf16* dW, adaln_bf16* db, adaln_bf16* dtemb, void* ws, size_t ws_bytes,
-                   int64_t B, int64_t K, int64_t N, void* stream) {
+int adaln_proj_bwd_acc(const float* d_emb, const adaln_bf16* temb, const adaln_bf16* W,
+                       adaln_bf16* dW, adaln_bf16* db, adaln_bf16* dtemb, float* dW_f32, float* db_f32,
+                       float* dtemb_f32, void* ws, size_t ws_bytes, int64_t B, int64_t K, int64_t N,
+                       void* stream) {
   if (!d_emb || !temb || !W || !dW || !db || !dtemb || !ws) return ADALN_ERR_NULL;
   if (!batch_ok(B) || K != kD || !proj_width_ok(N)) return ADALN_ERR_SHAPE;
   if (!aligned16(d_emb) || !aligned16(temb) || !aligned16(W) || !aligned16(dW) || !aligned16(db) ||
-      !aligned16(dtemb) || !aligned16(ws))
+      !aligned16(dtemb) || !aligned16(ws) || (dW_f32 && !aligned16(dW_f32)) || (db_f32 && !aligned16(db_f32)) ||
+      (dtemb_f32 && !aligned16(dtemb_f32)))
     return ADALN_ERR_ALIGN;
   const size_t need = ws_proj_bwd(B);
   if (ws_bytes < need) return ADALN_ERR_WORKSPACE;
-  if (int rc = check_overlap({{dW, static_cast<size_t>(N * kD * 2)}, {db, static_cast<size_t>(N * 2)},
-                              {dtemb, static_cast<size_t>(B * kD * 2)}, {ws, need}},
-                             {{d_emb, static_cast<size_t>(B * N * 4)}, {temb, static_cast<size_t>(B * kD * 2)},
-                              {W, static_cast<size_t>(N * kD * 2)}}))
+  std::vector<Range> outs = {{dW, static_cast<size_t>(N * kD * 2)}, {db, static_cast<size_t>(N * 2)},
+                             {dtemb, static_cast<size_t>(B * kD * 2)}, {ws, need}};
+  if (dW_f32) outs.push_back({dW_f32, static_cast<size_t>(N * kD * 4)});
+  if (db_f32) outs.push_back({db_f32, static_cast<size_t>(N * 4)});
+  if (dtemb_f32) outs.push_back({dtemb_f32, static_cast<size_t>(B * kD * 4)});
+  if (int rc = check_overlap(outs, {{d_emb, static_cast<size_t>(B * N * 4)},
+                                    {temb, static_cast<size_t>(B * kD * 2)},
+                                    {W, static_cast<size_t>(N * kD * 2)}}))
     return rc;
   if (int rc = check_device()) return rc;
   (void)hipGetLastError();
+  adaln::AccOut acc;
+  acc.dW = dW_f32;
+  acc.db = db_f32;
+  acc.dtemb = dtemb_f32;
   uint16_t* a = static_cast<uint16_t*>(ws);
   const hipStream_t s = as_stream(stream);
   if (B <= adaln::proj_bwd_fused_max_batch()) {
-    return launched(adaln::launch_proj_bwd_fused(d_emb, temb, W, dW, db, dtemb, static_cast<double*>(ws), B, N, s));
+    return launched(
+        adaln::launch_proj_bwd_fused(d_emb, temb, W, dW, db, dtemb, static_cast<double*>(ws), B, N, s, acc));
   }
   if (int rc = launched(adaln::launch_silu(temb, a, B * kD, s))) return rc;
-  if (int rc = launched(adaln::launch_proj_bwd_dw(d_emb, a, dW, db, B, N, s))) return rc;
-  return launched(adaln::launch_proj_bwd_da(d_emb, W, temb, dtemb, B, N, s));
+  if (int rc = launched(adaln::launch_proj_bwd_dw(d_emb, a, dW, db, B, N, s, acc))) return rc;
+  return launched(adaln::launch_proj_bwd_da(d_emb, W, temb, dtemb, B, N, s, acc));
+}
+
+int adaln_proj_bwd(const float* d_emb, const adaln_bf16* temb, const adaln_bf16* W,
+                   adaln_bf16* dW, adaln_bf16* db, adaln_bf16* dtemb, void* ws, size_t ws_bytes,
+                   int64_t B, int64_t K, int64_t N, void* stream) {
+  return adaln_proj_bwd_acc(d_emb, temb, W, dW, db, dtemb, nullptr, nullptr, nullptr, ws, ws_bytes, B, K, N,
+                            stream);
 }
 
 int token_tree_sum(const float* x, float* out, void* ws, size_t ws_bytes, int64_t B, int64_t S,

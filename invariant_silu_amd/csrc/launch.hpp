@@ -42,13 +42,20 @@ hipError_t launch_tree_fold_views(const float* part, float* d0, float* d1, float
 int proj_bwd_fused_max_batch();
 // bytes of fp64 da subtrees the B <= 4 path keeps between its two launches
 size_t proj_bwd_fused_sub_bytes(int64_t B);
+// Optional fp32 copies of the projection backward's bf16 outputs (the values
+// rounded to bf16); any member may be NULL.
+struct AccOut {
+  float* dW = nullptr;
+  float* db = nullptr;
+  float* dtemb = nullptr;
+};
 hipError_t launch_proj_bwd_fused(const float* d_emb, const uint16_t* temb, const uint16_t* W,
                                  uint16_t* dW, uint16_t* db, uint16_t* dtemb, double* sub, int64_t B, int64_t N,
-                                 hipStream_t s);
+                                 hipStream_t s, const AccOut& acc = AccOut{});
 hipError_t launch_proj_bwd_dw(const float* d_emb, const uint16_t* a, uint16_t* dW, uint16_t* db,
-                              int64_t B, int64_t N, hipStream_t s);
+                              int64_t B, int64_t N, hipStream_t s, const AccOut& acc = AccOut{});
 hipError_t launch_proj_bwd_da(const float* d_emb, const uint16_t* W, const uint16_t* temb,
-                              uint16_t* dtemb, int64_t B, int64_t N, hipStream_t s);
+                              uint16_t* dtemb, int64_t B, int64_t N, hipStream_t s, const AccOut& acc = AccOut{});
 // A block's norm site.  Its modulation as three [B, D] bf16 views with one
 // row stride ld (elements, a multiple of 8); gate is used only with the
 // residual add.

@@ -25,6 +25,10 @@
 //   da_leaf_f32_kernel<NB>     fp32 storage, B <= 4: the leaf-group blocks alone
 //                              (then da_finish_kernel<NB, float>)
 //   silu_kernel, dw_mfma_kernel, da_mfma_kernel   B > 4
+// With kAcc (adaln_proj_bwd_acc) the bf16 kernels also store the fp32 values
+// they round to bf16 -- fl32 of the dW and db sums, and da * silu'(temb) in
+// fp32 -- into whichever of the caller's fp32 arrays are not NULL; the
+// arithmetic is the same instructions either way.
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -234,10 +238,10 @@ __device__ __forceinline__ void da_leaf_group(const float* __restrict__ d_emb, c
 // da = the 32 subtrees of a (sample, column) added pairwise in order, then
 // dtemb = da * silu'(temb) in the storage type (bf16: one rounding); one
 // thread per (sample, column)
-template <int NB, typename T = uint16_t>
+template <int NB, typename T = uint16_t, bool kAcc = false>
 __global__ __launch_bounds__(256) void da_finish_kernel(const double* __restrict__ sub,
                                                         const T* __restrict__ temb,
-                                                        T* __restrict__ dtemb) {
+                                                        T* __restrict__ dtemb, float* __restrict__ dtemb32) {
   const int i = blockIdx.x * 256 + threadIdx.x;   // b * D + column
   if (i >= NB * kD) return;
   double v[kDaGroups];
@@ -247,16 +251,29 @@ __global__ __launch_bounds__(256) void da_finish_kernel(const double* __restrict
   for (int w = 1; w < kDaGroups; w <<= 1)
 #pragma unroll
     for (int s = 0; s < kDaGroups; s += 2 * w) v[s] += v[s + w];
-  dtemb[i] = Storage<T>::store1(static_cast<float>(v[0]) * dsilu_f32(Storage<T>::load1(temb[i])));
+  const float d = static_cast<float>(v[0]) * dsilu_f32(Storage<T>::load1(temb[i]));
+  dtemb[i] = Storage<T>::store1(d);
+  if constexpr (kAcc) {
+    if (dtemb32) dtemb32[i] = d;
+  }
+}
+
+// 8 consecutive fp32 values, two streaming 16-byte stores
+__device__ __forceinline__ void st32f_nt(float* p, const float (&f)[8]) {
+  const u32x4_t a = {__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
+  const u32x4_t b = {__float_as_uint(f[4]), __float_as_uint(f[5]), __float_as_uint(f[6]), __float_as_uint(f[7])};
+  __builtin_nontemporal_store(a, reinterpret_cast<u32x4_t*>(p));
+  __builtin_nontemporal_store(b, reinterpret_cast<u32x4_t*>(p + 4));
 }
 
 // dW tile (192 rows x 256 columns of part p, column block kb): a write
 // stream; a = bf16(SiLU(temb)) per thread for its 8 columns.  Tiles of column
 // block 0 also write db for their rows: samples in order from +0.
-template <int NB, int N = kN>
+template <int NB, int N = kN, bool kAcc = false>
 __device__ __forceinline__ void dw_tile(const float* __restrict__ d_emb,
                                         const uint16_t* __restrict__ temb, uint16_t* __restrict__ dW,
-                                        uint16_t* __restrict__ db, int p, int kb,
+                                        uint16_t* __restrict__ db, float* __restrict__ dW32,
+                                        float* __restrict__ db32, int p, int kb,
                                         float (*de_lds)[kRowsPerPart]) {
   const int ct = threadIdx.x % kColThreads;
   const int slot = threadIdx.x / kColThreads;
@@ -302,7 +319,11 @@ __device__ __forceinline__ void dw_tile(const float* __restrict__ d_emb,
     double s = 0.0;
 #pragma unroll
     for (int b = 0; b < NB; ++b) s += static_cast<double>(de_lds[b][threadIdx.x]);
-    db[jbase + threadIdx.x] = f32_to_bf16(static_cast<float>(s));
+    const float v = static_cast<float>(s);
+    db[jbase + threadIdx.x] = f32_to_bf16(v);
+    if constexpr (kAcc) {
+      if (db32) db32[jbase + threadIdx.x] = v;
+    }
   }
 #pragma unroll 4
   for (int i = 0; i < kSteps; ++i) {
@@ -317,6 +338,9 @@ __device__ __forceinline__ void dw_tile(const float* __restrict__ d_emb,
       o[e] = static_cast<float>(s);
     }
     st16_nt(dW + static_cast<int64_t>(jbase + jl) * kD + col, pack8(o));
+    if constexpr (kAcc) {
+      if (dW32) st32f_nt(dW32 + static_cast<int64_t>(jbase + jl) * kD + col, o);
+    }
   }
 }
 
@@ -332,18 +356,19 @@ struct ProjBwdShared {
 // are the da leaf-group blocks (they read W and write the subtrees), the
 // rest the dW tiles (they write dW and db): [384, 768) at N = 6144; the two
 // streams run side by side.  da_finish_kernel follows.
-template <int NB, int N = kN>
+template <int NB, int N = kN, bool kAcc = false>
 __global__ __launch_bounds__(kThreads) void proj_bwd_small_kernel(
     const float* __restrict__ d_emb, const uint16_t* __restrict__ temb, const uint16_t* __restrict__ W,
-    uint16_t* __restrict__ dW, uint16_t* __restrict__ db, double* __restrict__ sub) {
+    uint16_t* __restrict__ dW, uint16_t* __restrict__ db, double* __restrict__ sub, float* __restrict__ dW32,
+    float* __restrict__ db32) {
   __shared__ __align__(16) unsigned char smem[ProjBwdShared<NB>::kBytes];
   const int blk = blockIdx.x;
   if (blk < kDaLeafBlocks) {
     da_leaf_group<NB, uint16_t, N>(d_emb, W, sub, blk, reinterpret_cast<double*>(smem));
   } else {
     const int t = blk - kDaLeafBlocks;
-    dw_tile<NB, N>(d_emb, temb, dW, db, t % kDwParts<N>, t / kDwParts<N>,
-                   reinterpret_cast<float (*)[kRowsPerPart]>(smem));
+    dw_tile<NB, N, kAcc>(d_emb, temb, dW, db, dW32, db32, t % kDwParts<N>, t / kDwParts<N>,
+                         reinterpret_cast<float (*)[kRowsPerPart]>(smem));
   }
 }
 
@@ -371,11 +396,13 @@ constexpr int kDwMRows = 64;
 constexpr int kDwMCols = 32;
 constexpr int kDwMWaves = 4;
 
-template <typename T, int N = kN>
+template <typename T, int N = kN, bool kAcc = false>
 __global__ __launch_bounds__(64 * kDwMWaves) void dw_mfma_kernel(const float* __restrict__ d_emb,
                                                                  const T* __restrict__ a,
                                                                  T* __restrict__ dW,
-                                                                 T* __restrict__ db, int64_t B) {
+                                                                 T* __restrict__ db, int64_t B,
+                                                                 float* __restrict__ dW32,
+                                                                 float* __restrict__ db32) {
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
@@ -423,13 +450,22 @@ __global__ __launch_bounds__(64 * kDwMWaves) void dw_mfma_kernel(const float* __
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-      Pair<T>::store(dW + static_cast<int64_t>(j0 + 4 * (g + 4 * v) + m) * kD + k0 + 2 * r,
-                     static_cast<float>(acc[m][0][v]), static_cast<float>(acc[m][1][v]));
+    for (int v = 0; v < 4; ++v) {
+      const int64_t i = static_cast<int64_t>(j0 + 4 * (g + 4 * v) + m) * kD + k0 + 2 * r;
+      const float f0 = static_cast<float>(acc[m][0][v]), f1 = static_cast<float>(acc[m][1][v]);
+      Pair<T>::store(dW + i, f0, f1);
+      if constexpr (kAcc) {
+        if (dW32) *reinterpret_cast<float2*>(dW32 + i) = make_float2(f0, f1);
+      }
+    }
   if (blockIdx.y == 0 && wave == 0) {
     double sdb = 0.0;
     for (int64_t b = 0; b < B; ++b) sdb += static_cast<double>(d_emb[b * N + j0 + lane]);
-    db[j0 + lane] = Storage<T>::store1(static_cast<float>(sdb));
+    const float v = static_cast<float>(sdb);
+    db[j0 + lane] = Storage<T>::store1(v);
+    if constexpr (kAcc) {
+      if (db32) db32[j0 + lane] = v;
+    }
   }
 }
 
@@ -460,11 +496,12 @@ struct DaStep {
 };
 
 // T: storage type of W, temb and dtemb; N rows of W
-template <typename T, int N = kN>
+template <typename T, int N = kN, bool kAcc = false>
 __global__ __launch_bounds__(64 * kDaMWaves) void da_mfma_kernel(const float* __restrict__ d_emb,
                                                                  const T* __restrict__ W,
                                                                  const T* __restrict__ temb,
-                                                                 T* __restrict__ dtemb, int64_t B) {
+                                                                 T* __restrict__ dtemb, int64_t B,
+                                                                 float* __restrict__ dtemb32) {
   __shared__ f64x4_t sub[kDaMWaves - 1][2][64];   // 28 KB
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
@@ -539,8 +576,12 @@ __global__ __launch_bounds__(64 * kDaMWaves) void da_mfma_kernel(const float* __
       const int64_t i = (b0 + sr) * kD + k0 + 2 * r;
       Pair<T> z;
       z.load(temb + i);
-      Pair<T>::store(dtemb + i, static_cast<float>(tot[0][v]) * dsilu_f32(z.lo()),
-                     static_cast<float>(tot[1][v]) * dsilu_f32(z.hi()));
+      const float d0 = static_cast<float>(tot[0][v]) * dsilu_f32(z.lo());
+      const float d1 = static_cast<float>(tot[1][v]) * dsilu_f32(z.hi());
+      Pair<T>::store(dtemb + i, d0, d1);
+      if constexpr (kAcc) {
+        if (dtemb32) *reinterpret_cast<float2*>(dtemb32 + i) = make_float2(d0, d1);
+      }
     }
   }
 }
@@ -562,44 +603,49 @@ int proj_bwd_fused_max_batch() { return kBatchChunk; }
 
 namespace {
 
-template <int NB, int N>
+template <int NB, int N, bool kAcc>
 hipError_t launch_small(const float* d_emb, const uint16_t* temb, const uint16_t* W, uint16_t* dW, uint16_t* db,
-                        uint16_t* dtemb, double* sub, hipStream_t s) {
+                        uint16_t* dtemb, double* sub, const AccOut& acc, hipStream_t s) {
   const dim3 grid(kDaLeafBlocks + kDwTiles<N>), block(kThreads);
-  hipLaunchKernelGGL((proj_bwd_small_kernel<NB, N>), grid, block, 0, s, d_emb, temb, W, dW, db, sub);
+  hipLaunchKernelGGL((proj_bwd_small_kernel<NB, N, kAcc>), grid, block, 0, s, d_emb, temb, W, dW, db, sub, acc.dW,
+                     acc.db);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  hipLaunchKernelGGL(da_finish_kernel<NB>, dim3((NB * kD + 255) / 256), dim3(256), 0, s, sub, temb, dtemb);
+  hipLaunchKernelGGL((da_finish_kernel<NB, uint16_t, kAcc>), dim3((NB * kD + 255) / 256), dim3(256), 0, s, sub,
+                     temb, dtemb, acc.dtemb);
   return hipGetLastError();
 }
 
-template <int N>
+template <int N, bool kAcc>
 hipError_t proj_bwd_fused_rows(const float* d_emb, const uint16_t* temb, const uint16_t* W, uint16_t* dW,
-                               uint16_t* db, uint16_t* dtemb, double* sub, int64_t B, hipStream_t s) {
+                               uint16_t* db, uint16_t* dtemb, double* sub, int64_t B, const AccOut& acc,
+                               hipStream_t s) {
   switch (B) {
-    case 1: return launch_small<1, N>(d_emb, temb, W, dW, db, dtemb, sub, s);
-    case 2: return launch_small<2, N>(d_emb, temb, W, dW, db, dtemb, sub, s);
-    case 3: return launch_small<3, N>(d_emb, temb, W, dW, db, dtemb, sub, s);
-    case 4: return launch_small<4, N>(d_emb, temb, W, dW, db, dtemb, sub, s);
+    case 1: return launch_small<1, N, kAcc>(d_emb, temb, W, dW, db, dtemb, sub, acc, s);
+    case 2: return launch_small<2, N, kAcc>(d_emb, temb, W, dW, db, dtemb, sub, acc, s);
+    case 3: return launch_small<3, N, kAcc>(d_emb, temb, W, dW, db, dtemb, sub, acc, s);
+    case 4: return launch_small<4, N, kAcc>(d_emb, temb, W, dW, db, dtemb, sub, acc, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int N>
+template <int N, bool kAcc>
 hipError_t proj_bwd_dw_rows(const float* d_emb, const uint16_t* a, uint16_t* dW, uint16_t* db, int64_t B,
-                            hipStream_t s) {
-  hipLaunchKernelGGL((dw_mfma_kernel<uint16_t, N>), dim3(N / kDwMRows, kD / (kDwMCols * kDwMWaves)),
-                     dim3(64 * kDwMWaves), 0, s, d_emb, a, dW, db, B);
+                            const AccOut& acc, hipStream_t s) {
+  hipLaunchKernelGGL((dw_mfma_kernel<uint16_t, N, kAcc>), dim3(N / kDwMRows, kD / (kDwMCols * kDwMWaves)),
+                     dim3(64 * kDwMWaves), 0, s, d_emb, a, dW, db, B, acc.dW, acc.db);
   return hipGetLastError();
 }
 
-template <int N>
+template <int N, bool kAcc>
 hipError_t proj_bwd_da_rows(const float* d_emb, const uint16_t* W, const uint16_t* temb, uint16_t* dtemb,
-                            int64_t B, hipStream_t s) {
+                            int64_t B, const AccOut& acc, hipStream_t s) {
   const int64_t by = (B + 15) / 16;
-  hipLaunchKernelGGL((da_mfma_kernel<uint16_t, N>), dim3(kD / kDaMCols, static_cast<unsigned>(by)),
-                     dim3(64 * kDaMWaves), 0, s, d_emb, W, temb, dtemb, B);
+  hipLaunchKernelGGL((da_mfma_kernel<uint16_t, N, kAcc>), dim3(kD / kDaMCols, static_cast<unsigned>(by)),
+                     dim3(64 * kDaMWaves), 0, s, d_emb, W, temb, dtemb, B, acc.dtemb);
   return hipGetLastError();
 }
+
+bool any(const AccOut& acc) { return acc.dW || acc.db || acc.dtemb; }
 
 }  // namespace
 
@@ -607,23 +653,38 @@ size_t proj_bwd_fused_sub_bytes(int64_t B) { return static_cast<size_t>(kDaGroup
 
 hipError_t launch_proj_bwd_fused(const float* d_emb, const uint16_t* temb, const uint16_t* W,
                                  uint16_t* dW, uint16_t* db, uint16_t* dtemb, double* sub, int64_t B, int64_t N,
-                                 hipStream_t s) {
-  if (N == kN) return proj_bwd_fused_rows<kN>(d_emb, temb, W, dW, db, dtemb, sub, B, s);
-  if (N == kN6) return proj_bwd_fused_rows<kN6>(d_emb, temb, W, dW, db, dtemb, sub, B, s);
+                                 hipStream_t s, const AccOut& acc) {
+  const bool a = any(acc);
+  if (N == kN)
+    return a ? proj_bwd_fused_rows<kN, true>(d_emb, temb, W, dW, db, dtemb, sub, B, acc, s)
+             : proj_bwd_fused_rows<kN, false>(d_emb, temb, W, dW, db, dtemb, sub, B, acc, s);
+  if (N == kN6)
+    return a ? proj_bwd_fused_rows<kN6, true>(d_emb, temb, W, dW, db, dtemb, sub, B, acc, s)
+             : proj_bwd_fused_rows<kN6, false>(d_emb, temb, W, dW, db, dtemb, sub, B, acc, s);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_proj_bwd_dw(const float* d_emb, const uint16_t* a, uint16_t* dW, uint16_t* db, int64_t B,
-                              int64_t N, hipStream_t s) {
-  if (N == kN) return proj_bwd_dw_rows<kN>(d_emb, a, dW, db, B, s);
-  if (N == kN6) return proj_bwd_dw_rows<kN6>(d_emb, a, dW, db, B, s);
+                              int64_t N, hipStream_t s, const AccOut& acc) {
+  const bool f = any(acc);
+  if (N == kN)
+    return f ? proj_bwd_dw_rows<kN, true>(d_emb, a, dW, db, B, acc, s)
+             : proj_bwd_dw_rows<kN, false>(d_emb, a, dW, db, B, acc, s);
+  if (N == kN6)
+    return f ? proj_bwd_dw_rows<kN6, true>(d_emb, a, dW, db, B, acc, s)
+             : proj_bwd_dw_rows<kN6, false>(d_emb, a, dW, db, B, acc, s);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_proj_bwd_da(const float* d_emb, const uint16_t* W, const uint16_t* temb, uint16_t* dtemb,
-                              int64_t B, int64_t N, hipStream_t s) {
-  if (N == kN) return proj_bwd_da_rows<kN>(d_emb, W, temb, dtemb, B, s);
-  if (N == kN6) return proj_bwd_da_rows<kN6>(d_emb, W, temb, dtemb, B, s);
+                              int64_t B, int64_t N, hipStream_t s, const AccOut& acc) {
+  const bool f = any(acc);
+  if (N == kN)
+    return f ? proj_bwd_da_rows<kN, true>(d_emb, W, temb, dtemb, B, acc, s)
+             : proj_bwd_da_rows<kN, false>(d_emb, W, temb, dtemb, B, acc, s);
+  if (N == kN6)
+    return f ? proj_bwd_da_rows<kN6, true>(d_emb, W, temb, dtemb, B, acc, s)
+             : proj_bwd_da_rows<kN6, false>(d_emb, W, temb, dtemb, B, acc, s);
   return hipErrorInvalidValue;
 }
 
@@ -641,7 +702,8 @@ hipError_t da_f32_small(const float* d_emb, const float* W, const float* temb, f
                         hipStream_t s) {
   hipLaunchKernelGGL(da_leaf_f32_kernel<NB>, dim3(kDaLeafBlocks), dim3(kThreads), 0, s, d_emb, W, sub);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  hipLaunchKernelGGL((da_finish_kernel<NB, float>), dim3((NB * kD + 255) / 256), dim3(256), 0, s, sub, temb, dtemb);
+  hipLaunchKernelGGL((da_finish_kernel<NB, float>), dim3((NB * kD + 255) / 256), dim3(256), 0, s, sub, temb, dtemb,
+                     nullptr);
   return hipGetLastError();
 }
 
@@ -654,7 +716,7 @@ hipError_t launch_proj_bwd_f32(const float* d_emb, const float* temb, const floa
                                float* db, float* dtemb, double* sub, int64_t B, hipStream_t s) {
   if (hipError_t e = launch_silu_f32(temb, a, B * kD, s); e != hipSuccess) return e;
   hipLaunchKernelGGL(dw_mfma_kernel<float>, dim3(kN / kDwMRows, kD / (kDwMCols * kDwMWaves)),
-                     dim3(64 * kDwMWaves), 0, s, d_emb, a, dW, db, B);
+                     dim3(64 * kDwMWaves), 0, s, d_emb, a, dW, db, B, nullptr, nullptr);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   switch (B) {
     case 1: return da_f32_small<1>(d_emb, W, temb, dtemb, sub, s);
@@ -664,7 +726,7 @@ hipError_t launch_proj_bwd_f32(const float* d_emb, const float* temb, const floa
     default: {
       const int64_t by = (B + 15) / 16;
       hipLaunchKernelGGL(da_mfma_kernel<float>, dim3(kD / kDaMCols, static_cast<unsigned>(by)),
-                         dim3(64 * kDaMWaves), 0, s, d_emb, W, temb, dtemb, B);
+                         dim3(64 * kDaMWaves), 0, s, d_emb, W, temb, dtemb, B, nullptr);
     }
   }
   return hipGetLastError();

@@ -22,6 +22,7 @@ ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DEVICE, ERR_WORKSPACE, ERR_OVERLAP, ERR_LAUN
 EXPORTS = ("adaln_fwd", "adaln_bwd", "adaln_fwd_f32", "adaln_bwd_f32", "adaln_residual_fwd", "adaln_residual_bwd",
            "adaln_site_fwd", "adaln_site_bwd",
            "adaln_proj_out_fwd", "adaln_proj_out_bwd", "adaln_fwd_proj_out", "adaln_proj_fwd", "adaln_norm_mod_fwd", "adaln_norm_mod_bwd", "adaln_proj_bwd",
+           "adaln_proj_bwd_acc",
            "token_tree_sum", "adaln_norm_mod_bwd_dx", "adaln_norm_mod_bwd_tiles", "token_tree_fold",
            "adaln_norm_mod_bwd_noalloc",
            "adaln_norm_mod_bwd_level0", "adaln_workspace_bytes", "adaln_selftest", "adaln_strerror",
@@ -46,6 +47,7 @@ _SIGS = {
     "adaln_norm_mod_fwd": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_float, _P], ctypes.c_int),
     "adaln_norm_mod_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I64, _I64, _I64, _P], ctypes.c_int),
     "adaln_proj_bwd": ([_P, _P, _P, _P, _P, _P, _P, _SZ, _I64, _I64, _I64, _P], ctypes.c_int),
+    "adaln_proj_bwd_acc": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I64, _I64, _I64, _P], ctypes.c_int),
     "token_tree_sum": ([_P, _P, _P, _SZ, _I64, _I64, _I64, _P], ctypes.c_int),
     "adaln_norm_mod_bwd_dx": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "adaln_norm_mod_bwd_tiles": ([_P, _P, _P, _P, _P, _SZ, _I64, _I64, _I64, _P], ctypes.c_int),

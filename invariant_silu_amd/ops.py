@@ -132,9 +132,11 @@ def norm_mod_bwd(g: torch.Tensor, x: torch.Tensor, mean: torch.Tensor, rstd: tor
     return dx, d_emb
 
 
-def proj_bwd(d_emb: torch.Tensor, temb: torch.Tensor, W: torch.Tensor):
+def proj_bwd(d_emb: torch.Tensor, temb: torch.Tensor, W: torch.Tensor, want_f32: bool = False):
     """(dW bf16 [N, 3072], db bf16 [N], dtemb bf16 [B, 3072]); N = W.shape[0]
-    (6144 or 18432, as for proj_fwd)."""
+    (6144 or 18432, as for proj_fwd).  want_f32: also the fp32 values those
+    are rounded from, (dW, db, dtemb, dW_f32, db_f32, dtemb_f32)
+    (adaln_proj_bwd_acc)."""
     Nw = _proj_width(W)
     _rank(temb, 2, "temb")
     _shape(temb, (temb.shape[0], D), "temb")
@@ -148,10 +150,18 @@ def proj_bwd(d_emb: torch.Tensor, temb: torch.Tensor, W: torch.Tensor):
     db = torch.empty((W.shape[0],), dtype=torch.bfloat16, device=W.device)
     dtemb = torch.empty_like(temb)
     ws = _ws(_lib.OP_PROJ_BWD, B, 1, D, W.device)
-    _lib.call("adaln_proj_bwd", d_emb.data_ptr(), temb.data_ptr(), W.data_ptr(), dW.data_ptr(),
-              db.data_ptr(), dtemb.data_ptr(), ws.data_ptr(), ws.numel(), B, temb.shape[1],
-              W.shape[0], _stream(W.device))
-    return dW, db, dtemb
+    if not want_f32:
+        _lib.call("adaln_proj_bwd", d_emb.data_ptr(), temb.data_ptr(), W.data_ptr(), dW.data_ptr(),
+                  db.data_ptr(), dtemb.data_ptr(), ws.data_ptr(), ws.numel(), B, temb.shape[1],
+                  W.shape[0], _stream(W.device))
+        return dW, db, dtemb
+    dW32 = torch.empty(W.shape, dtype=torch.float32, device=W.device)
+    db32 = torch.empty((W.shape[0],), dtype=torch.float32, device=W.device)
+    dtemb32 = torch.empty(temb.shape, dtype=torch.float32, device=W.device)
+    _lib.call("adaln_proj_bwd_acc", d_emb.data_ptr(), temb.data_ptr(), W.data_ptr(), dW.data_ptr(),
+              db.data_ptr(), dtemb.data_ptr(), dW32.data_ptr(), db32.data_ptr(), dtemb32.data_ptr(),
+              ws.data_ptr(), ws.numel(), B, temb.shape[1], W.shape[0], _stream(W.device))
+    return dW, db, dtemb, dW32, db32, dtemb32
 
 
 def token_tree_sum(x: torch.Tensor) -> torch.Tensor:

@@ -274,18 +274,22 @@ def backward(inp: dict, fwd: dict, mode: str = "fp32", want_abs: bool = False,
 def proj_backward(d_emb, a, W, temb, ar: Arith, want_abs: bool = False) -> dict:
     """Projection backward from d_emb [B, N] (fp32 values), a [B, K] (bf16
     values), W [N, K] and temb [B, K]: da, dtemb = bf16(da * silu'(temb)),
-    dW = bf16(sum_b d_emb_b x a_b), db = bf16(sum_b d_emb_b), every product exact."""
+    dW = bf16(sum_b d_emb_b x a_b), db = bf16(sum_b d_emb_b), every product exact.
+    dtemb_acc, dW_acc, db_acc are the values before their single storage
+    rounding."""
     d_emb, a, W = ar.c(d_emb), ar.c(a), ar.c(W)
     B, N = d_emb.shape
     K = W.shape[1]
     r3 = ar.sum((t for j in range(N) for t in ar.prod(d_emb[:, j:j + 1], W[j][None, :])), (B, K), want_abs)
     da, A_da = r3 if want_abs else (r3, None)
-    dtemb = ar.store(da * dsilu(temb, ar))
+    dtemb_acc = da * dsilu(temb, ar)          # the value dtemb rounds once to storage
+    dtemb = ar.store(dtemb_acc)
     r4 = ar.sum((t for b in range(B) for t in ar.prod(d_emb[b][:, None], a[b][None, :])), (N, K), want_abs)
     dW_acc, A_dW = r4 if want_abs else (r4, None)
     r5 = ar.sum((d_emb[b] for b in range(B)), (N,), want_abs)
     db_acc, A_db = r5 if want_abs else (r5, None)
-    res = dict(da=da, dtemb=dtemb, dW_acc=dW_acc, dW=ar.store(dW_acc), db_acc=db_acc, db=ar.store(db_acc))
+    res = dict(da=da, dtemb=dtemb, dtemb_acc=dtemb_acc, dW_acc=dW_acc, dW=ar.store(dW_acc), db_acc=db_acc,
+               db=ar.store(db_acc))
     if want_abs:
         res.update(A_da=A_da, A_dW=A_dW, A_db=A_db)
     return res

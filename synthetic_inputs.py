@@ -110,21 +110,26 @@ def make_residual_inputs(B: int, S: int, seed: int = 0, D: int = HIDDEN) -> dict
             "seed": seed}
 
 
-def make_mod6_inputs(B: int, seed: int = 0, K: int = HIDDEN, d_sigma: float = 8.0) -> dict:
-    """One batch for a block's 6-way modulation projection: temb [B, K], W
-    [6K, K], bias [6K] as bf16 bits; d_emb [B, 6K] fp32 (the gradients of both
-    norm sites' shift | scale | gate: token sums, so several times larger
-    than a token's gradient).
+def make_proj_inputs(B: int, N: int, seed: int = 0, K: int = HIDDEN, d_sigma: float = 8.0) -> dict:
+    """One batch for a modulation projection K -> N and its backward: temb
+    [B, K], W [N, K], bias [N] as bf16 bits; d_emb [B, N] fp32 (token sums of
+    per-token gradients, so several times larger than a token's gradient).
 
     Draw order temb, W, bias, d_emb; standard normals scaled by 1, 0.02, 0.01
     and d_sigma; the first three rounded to bfloat16."""
     rng = np.random.default_rng(seed)
     temb = rng.standard_normal((B, K), dtype=np.float32)
-    W = rng.standard_normal((6 * K, K), dtype=np.float32) * np.float32(0.02)
-    bias = rng.standard_normal(6 * K, dtype=np.float32) * np.float32(0.01)
-    d_emb = rng.standard_normal((B, 6 * K), dtype=np.float32) * np.float32(d_sigma)
+    W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    bias = rng.standard_normal(N, dtype=np.float32) * np.float32(0.01)
+    d_emb = rng.standard_normal((B, N), dtype=np.float32) * np.float32(d_sigma)
     return {"temb": f32_to_bf16_bits(temb), "W": f32_to_bf16_bits(W), "bias": f32_to_bf16_bits(bias),
-            "d_emb": d_emb, "B": B, "K": K, "N": 6 * K, "seed": seed}
+            "d_emb": d_emb, "B": B, "K": K, "N": N, "seed": seed}
+
+
+def make_mod6_inputs(B: int, seed: int = 0, K: int = HIDDEN, d_sigma: float = 8.0) -> dict:
+    """One batch for a block's 6-way modulation projection (N = 6K): d_emb
+    holds the gradients of both norm sites' shift | scale | gate."""
+    return make_proj_inputs(B, 6 * K, seed=seed, K=K, d_sigma=d_sigma)
 
 
 def make_proj_out_inputs(T: int, seed: int = 0, K: int = HIDDEN, O: int = 64) -> dict:

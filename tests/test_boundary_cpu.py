@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_strerror(L):
-    assert L.adaln_abi_version() == 13
+    assert L.adaln_abi_version() == 14
     for code in range(-8, 1):
         assert len(lib.strerror(code)) >= 2
 
@@ -110,6 +110,22 @@ def test_validation_before_device_work(L):
                             8, 3072, 18432, None) == lib.ERR_WORKSPACE
     pb = [p + (k << 28) for k in range(7)]
     assert L.adaln_proj_bwd(*pb, 16, 8, 3072, 18432, None) == lib.ERR_WORKSPACE
+    # adaln_proj_bwd_acc: the fp32 outputs are optional (NULL accepted), checked
+    # for alignment and for overlap with every input, output and the workspace
+    pa = [p + (k << 28) for k in range(10)]   # d_emb temb W dW db dtemb dW32 db32 dtemb32 ws
+    assert L.adaln_proj_bwd_acc(*pa[:6], None, None, None, pa[9], 16, 8, 3072, 6144, None) == lib.ERR_WORKSPACE
+    assert L.adaln_proj_bwd_acc(*pa[:6], pa[6] + 4, None, None, pa[9], 1 << 30, 8, 3072, 6144,
+                                None) == lib.ERR_ALIGN
+    assert L.adaln_proj_bwd_acc(*pa[:6], None, None, pa[8] + 8, pa[9], 1 << 30, 8, 3072, 6144,
+                                None) == lib.ERR_ALIGN
+    assert L.adaln_proj_bwd_acc(*pa[:6], pa[2] + (16 << 20), None, None, pa[9], 1 << 30, 8, 3072, 6144,
+                                None) == lib.ERR_OVERLAP            # dW_f32 inside W
+    assert L.adaln_proj_bwd_acc(*pa[:6], None, pa[3], None, pa[9], 1 << 30, 8, 3072, 6144,
+                                None) == lib.ERR_OVERLAP            # db_f32 on dW
+    assert L.adaln_proj_bwd_acc(*pa[:6], None, None, pa[9], pa[9], 1 << 30, 8, 3072, 6144,
+                                None) == lib.ERR_OVERLAP            # dtemb_f32 on the workspace
+    assert L.adaln_proj_bwd_acc(*pa[:9], pa[9], 1 << 30, 8, 3072, 12288, None) == lib.ERR_SHAPE
+    assert L.adaln_proj_bwd_acc(*pa[:5], None, *pa[6:], 1 << 30, 8, 3072, 6144, None) == lib.ERR_NULL
     # the overlap check spans N rows of W: emb 100 MB past W's start lies inside
     # a 6-way W (113 MB) but not inside a final-modulation W (37.7 MB)
     args = (p, p + (1 << 20), p + (200 << 20), p + (101 << 20), p + (300 << 20), 1 << 20, 1, 3072)

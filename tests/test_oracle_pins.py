@@ -359,6 +359,13 @@ def test_projection_backward_tiny_exact_rationals():
     assert np.array_equal(f32_to_bf16_bits(r["dW"]), f32_to_bf16_bits(dW_ex))
     assert np.array_equal(r["dW_acc"].view(np.uint32), dW_ex.view(np.uint32))
     assert np.array_equal(r["da"].view(np.uint32), da_ex.view(np.uint32))
+    # dtemb before its bf16 rounding: the exact-rational da times silu'(z)
+    # (sigma(z) (1 + z (1 - sigma(z))) in float64, rounded to fp32), one fp32 product
+    z = temb.astype(np.float64)
+    sg = 1.0 / (1.0 + np.exp(-z))
+    ds = (sg * (1.0 + z * (1.0 - sg))).astype(np.float32)
+    assert np.array_equal(r["dtemb_acc"].view(np.uint32), (da_ex * ds).view(np.uint32))
+    assert np.array_equal(f32_to_bf16_bits(r["dtemb_acc"]), f32_to_bf16_bits(r["dtemb"]))
 
 
 def test_teeth_rounded_products_caught(monkeypatch):
