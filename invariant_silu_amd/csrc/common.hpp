@@ -102,9 +102,10 @@ __device__ __forceinline__ int64_t pair_index(int64_t b, int64_t groups, int64_t
   return ((b * groups + col / kPairGroup) * T0 + tile) * (2 * kPairGroup) + col % kPairGroup;
 }
 
-__device__ __forceinline__ void st8_nt(float* p, float a, float b) {
-  f32x2_t w = {a, b};
-  __builtin_nontemporal_store(w, reinterpret_cast<f32x2_t*>(p));
+// Level-0 token-tree pairs: plain stores, so the fold that reads them next
+// finds them in the caches.
+__device__ __forceinline__ void st8(float* p, float a, float b) {
+  *reinterpret_cast<f32x2_t*>(p) = f32x2_t{a, b};
 }
 
 // Sum over the 64 lanes of a wave as a pairwise tree over lane index

@@ -317,10 +317,10 @@ __device__ __forceinline__ void col_tile_f32(const float* __restrict__ g, const 
   constexpr int64_t kGroups = kN / kPairGroup;
   const int64_t i_scale = pair_index(b, kGroups, T0, tile, col);
   const int64_t i_shift = pair_index(b, kGroups, T0, tile, col + kD);
-  st8_nt(part + i_scale, sn0, sn1);
-  st8_nt(part + i_scale + kPairGroup, cn0, cn1);
-  st8_nt(part + i_shift, sg0, sg1);
-  st8_nt(part + i_shift + kPairGroup, cg0, cg1);
+  st8(part + i_scale, sn0, sn1);
+  st8(part + i_scale + kPairGroup, cn0, cn1);
+  st8(part + i_shift, sg0, sg1);
+  st8(part + i_shift + kPairGroup, cg0, cg1);
 }
 
 // grid: 1-D, ceil(B*T0 / 8) * 8 * 14 blocks.  Block L runs on XCD L % 8; on

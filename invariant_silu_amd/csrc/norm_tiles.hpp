@@ -73,10 +73,10 @@ __device__ __forceinline__ void col_tile(const uint16_t* __restrict__ g, const u
   }
   const int64_t i_scale = pair_index(b, groups, T0, tile, scale_col0 + col);
   const int64_t i_shift = pair_index(b, groups, T0, tile, shift_col0 + col);
-  st8_nt(part + i_scale, sn0, sn1);
-  st8_nt(part + i_scale + kPairGroup, cn0, cn1);
-  st8_nt(part + i_shift, sg0, sg1);
-  st8_nt(part + i_shift + kPairGroup, cg0, cg1);
+  st8(part + i_scale, sn0, sn1);
+  st8(part + i_scale + kPairGroup, cn0, cn1);
+  st8(part + i_shift, sg0, sg1);
+  st8(part + i_shift + kPairGroup, cg0, cg1);
 }
 
 // columns [0, D) of d_emb: d_scale (g * n); [D, 2D): d_shift (g)

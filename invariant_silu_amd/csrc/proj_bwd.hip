@@ -258,12 +258,10 @@ __global__ __launch_bounds__(256) void da_finish_kernel(const double* __restrict
   }
 }
 
-// 8 consecutive fp32 values, two streaming 16-byte stores
-__device__ __forceinline__ void st32f_nt(float* p, const float (&f)[8]) {
-  const u32x4_t a = {__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
-  const u32x4_t b = {__float_as_uint(f[4]), __float_as_uint(f[5]), __float_as_uint(f[6]), __float_as_uint(f[7])};
-  __builtin_nontemporal_store(a, reinterpret_cast<u32x4_t*>(p));
-  __builtin_nontemporal_store(b, reinterpret_cast<u32x4_t*>(p + 4));
+// 8 consecutive fp32 values, two 16-byte stores
+__device__ __forceinline__ void st32f(float* p, const float (&f)[8]) {
+  *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
 }
 
 // dW tile (192 rows x 256 columns of part p, column block kb): a write
@@ -337,9 +335,9 @@ __device__ __forceinline__ void dw_tile(const float* __restrict__ d_emb,
         s = __builtin_fma(static_cast<double>(de_lds[b][jl]), static_cast<double>(av[b][e]), s);
       o[e] = static_cast<float>(s);
     }
-    st16_nt(dW + static_cast<int64_t>(jbase + jl) * kD + col, pack8(o));
+    st16(dW + static_cast<int64_t>(jbase + jl) * kD + col, pack8(o));
     if constexpr (kAcc) {
-      if (dW32) st32f_nt(dW32 + static_cast<int64_t>(jbase + jl) * kD + col, o);
+      if (dW32) st32f(dW32 + static_cast<int64_t>(jbase + jl) * kD + col, o);
     }
   }
 }
@@ -355,12 +353,15 @@ struct ProjBwdShared {
 // Small batches (B <= 4, a template parameter): one grid, blocks [0, 384)
 // are the da leaf-group blocks (they read W and write the subtrees), the
 // rest the dW tiles (they write dW and db): [384, 768) at N = 6144; the two
-// streams run side by side.  da_finish_kernel follows.
-template <int NB, int N = kN, bool kAcc = false>
-__global__ __launch_bounds__(kThreads) void proj_bwd_small_kernel(
-    const float* __restrict__ d_emb, const uint16_t* __restrict__ temb, const uint16_t* __restrict__ W,
-    uint16_t* __restrict__ dW, uint16_t* __restrict__ db, double* __restrict__ sub, float* __restrict__ dW32,
-    float* __restrict__ db32) {
+// streams run side by side.  da_finish_kernel follows.  The kAcc form (its
+// own kernel, so the plain one keeps its argument list) also stores the fp32
+// dW and db.
+template <int NB, int N, bool kAcc>
+__device__ __forceinline__ void proj_bwd_small_body(const float* __restrict__ d_emb,
+                                                    const uint16_t* __restrict__ temb,
+                                                    const uint16_t* __restrict__ W, uint16_t* __restrict__ dW,
+                                                    uint16_t* __restrict__ db, double* __restrict__ sub,
+                                                    float* __restrict__ dW32, float* __restrict__ db32) {
   __shared__ __align__(16) unsigned char smem[ProjBwdShared<NB>::kBytes];
   const int blk = blockIdx.x;
   if (blk < kDaLeafBlocks) {
@@ -370,6 +371,21 @@ __global__ __launch_bounds__(kThreads) void proj_bwd_small_kernel(
     dw_tile<NB, N, kAcc>(d_emb, temb, dW, db, dW32, db32, t % kDwParts<N>, t / kDwParts<N>,
                          reinterpret_cast<float (*)[kRowsPerPart]>(smem));
   }
+}
+
+template <int NB, int N = kN>
+__global__ __launch_bounds__(kThreads) void proj_bwd_small_kernel(
+    const float* __restrict__ d_emb, const uint16_t* __restrict__ temb, const uint16_t* __restrict__ W,
+    uint16_t* __restrict__ dW, uint16_t* __restrict__ db, double* __restrict__ sub) {
+  proj_bwd_small_body<NB, N, false>(d_emb, temb, W, dW, db, sub, nullptr, nullptr);
+}
+
+template <int NB, int N = kN>
+__global__ __launch_bounds__(kThreads) void proj_bwd_small_acc_kernel(
+    const float* __restrict__ d_emb, const uint16_t* __restrict__ temb, const uint16_t* __restrict__ W,
+    uint16_t* __restrict__ dW, uint16_t* __restrict__ db, double* __restrict__ sub, float* __restrict__ dW32,
+    float* __restrict__ db32) {
+  proj_bwd_small_body<NB, N, true>(d_emb, temb, W, dW, db, sub, dW32, db32);
 }
 
 __global__ __launch_bounds__(256) void silu_kernel(const uint16_t* __restrict__ temb,
@@ -607,8 +623,11 @@ template <int NB, int N, bool kAcc>
 hipError_t launch_small(const float* d_emb, const uint16_t* temb, const uint16_t* W, uint16_t* dW, uint16_t* db,
                         uint16_t* dtemb, double* sub, const AccOut& acc, hipStream_t s) {
   const dim3 grid(kDaLeafBlocks + kDwTiles<N>), block(kThreads);
-  hipLaunchKernelGGL((proj_bwd_small_kernel<NB, N, kAcc>), grid, block, 0, s, d_emb, temb, W, dW, db, sub, acc.dW,
-                     acc.db);
+  if constexpr (kAcc)
+    hipLaunchKernelGGL((proj_bwd_small_acc_kernel<NB, N>), grid, block, 0, s, d_emb, temb, W, dW, db, sub, acc.dW,
+                       acc.db);
+  else
+    hipLaunchKernelGGL((proj_bwd_small_kernel<NB, N>), grid, block, 0, s, d_emb, temb, W, dW, db, sub);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   hipLaunchKernelGGL((da_finish_kernel<NB, uint16_t, kAcc>), dim3((NB * kD + 255) / 256), dim3(256), 0, s, sub,
                      temb, dtemb, acc.dtemb);

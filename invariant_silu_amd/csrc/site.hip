@@ -180,8 +180,8 @@ __device__ __forceinline__ void gate_tile(const uint16_t* __restrict__ dh, const
     }
   }
   const int64_t i = pair_index(b, kModGroups, T0, tile, 2 * kD + col);
-  st8_nt(part + i, s0, s1);
-  st8_nt(part + i + kPairGroup, c0, c1);
+  st8(part + i, s0, s1);
+  st8(part + i + kPairGroup, c0, c1);
 }
 
 // grid: B * T0 * 6 blocks; block (G, cb) = tile G, 512-column block cb
