@@ -330,7 +330,8 @@ def main() -> int:
     BL = ctypes.CDLL(_build.BENCH_LIB_PATH)
     for fn, argt in (("bench_flush", [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p]),
-                     ("bench_stream_copy", [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+                     ("bench_stream_copy", [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p]),
                      ("bench_event_create", [ctypes.POINTER(ctypes.c_void_p)]),
                      ("bench_event_elapsed", [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]),
                      ("bench_event_destroy", [ctypes.c_void_p])):
@@ -597,7 +598,7 @@ def main() -> int:
         cev = Events(2 * 22 + 1)
         for i in range(22):   # timed as the phases are: flush end to next flush start
             flush(cev.h[2 * i], cev.h[2 * i + 1])
-            if BL.bench_stream_copy(src.data_ptr(), dst.data_ptr(), cn, st) != 0:
+            if BL.bench_stream_copy(src.data_ptr(), dst.data_ptr(), cn, None, None, st) != 0:
                 raise RuntimeError("bench_stream_copy failed")
         flush(cev.h[44], None)
         torch.cuda.synchronize()
@@ -606,8 +607,26 @@ def main() -> int:
         del src, dst
         return 2 * cn / (copy_ms[len(copy_ms) // 2] / 1e3) / 1e9
 
+    def kernel_copy_rate(total_bytes):
+        """The same copy timed as the dominant kernel is: events recorded by
+        its own dispatch, after the same flush; mean of 20."""
+        cn = (total_bytes // 2 + 255) // 256 * 256
+        src = torch.empty(cn, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty(cn, dtype=torch.uint8, device=dev)
+        cev = Events(2 * 22)
+        for i in range(22):
+            flush()
+            if BL.bench_stream_copy(src.data_ptr(), dst.data_ptr(), cn, cev.h[2 * i], cev.h[2 * i + 1], st) != 0:
+                raise RuntimeError("bench_stream_copy failed")
+        torch.cuda.synchronize()
+        copy_ms = [cev.ms(2 * i, 2 * i + 1) for i in range(2, 22)]
+        cev.close()
+        del src, dst
+        return 2 * cn / (sum(copy_ms) / len(copy_ms) / 1e3) / 1e9
+
     copy_gbps = copy_rate(step_bytes)
     copy4_gbps = copy_rate(4 * step_bytes)
+    k_copy_gbps = kernel_copy_rate(k_bytes) if (kernel_timed and mfma_flops is None) else None
 
     if args.copy_calib:
         n = 512 << 20
@@ -673,6 +692,11 @@ def main() -> int:
                      **({"bytes_per_launch": k_bytes} if mfma_flops is None else
                         {"fp64_flops_per_step": mfma_flops, "step_bytes": k_bytes}),
                      "avg_launch_ms": round(k_mean_ms, 5),
+                     **({"copy_same_bytes_gbps": round(k_copy_gbps, 1),
+                         "frac_of_copy_same_bytes": round(achieved / k_copy_gbps, 4),
+                         "copy_note": ("bench_stream_copy of the kernel's algorithmic bytes (half read, half "
+                                       "written) after the same flush, timed by its own dispatch events")}
+                        if k_copy_gbps else {}),
                      "timed_launches": n_k,
                      "timing": ("HIP events recorded by the dispatch of adaln_norm_mod_bwd_level0 (this kernel "
                                 "alone) on the step's stream, each launch after the same flush as in the step"

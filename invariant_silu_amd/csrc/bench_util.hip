@@ -80,13 +80,16 @@ int bench_flush(void* buf, size_t bytes, void* ev_start, void* ev_end, void* str
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 
-int bench_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
+// Optional caller events are recorded by the copy's own dispatch (the start
+// and the end of the kernel), as for the kernel they are compared with.
+int bench_stream_copy(const void* src, void* dst, size_t bytes, void* ev_start, void* ev_end, void* stream) {
   if (!src || !dst || bytes == 0 || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(src) % 16 != 0 ||
       reinterpret_cast<uintptr_t>(dst) % 16 != 0)
     return -1;
   const int64_t n16 = static_cast<int64_t>(bytes / 16);
-  hipLaunchKernelGGL(copy_kernel, dim3(grid_for(n16)), dim3(kThreads), 0, reinterpret_cast<hipStream_t>(stream),
-                     static_cast<const uint4*>(src), static_cast<uint4*>(dst), n16);
+  hipExtLaunchKernelGGL(copy_kernel, dim3(grid_for(n16)), dim3(kThreads), 0, reinterpret_cast<hipStream_t>(stream),
+                        reinterpret_cast<hipEvent_t>(ev_start), reinterpret_cast<hipEvent_t>(ev_end), 0,
+                        static_cast<const uint4*>(src), static_cast<uint4*>(dst), n16);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 

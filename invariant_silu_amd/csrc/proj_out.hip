@@ -51,11 +51,12 @@ __device__ __forceinline__ double el8(const uint4& v, int e) {
 
 // ---- forward ---------------------------------------------------------------
 // Block: 16 tokens (t0 ..) x all 64 outputs, 8 waves; wave p runs part p of K
-// for the four 16-output tiles.  The block's 16 rows of out sit in LDS (rows
-// padded by 16 bytes); lane (r, g) takes A = out[t0 + r][k] from there and
-// B = Wp[16 j + r][k] from memory (Wp is 384 KB: it stays in L2), 16 bytes
-// per 8 steps each, one group of 8 steps ahead.  The parts then meet in LDS.
-// Tokens past T use row T - 1 and are never stored.
+// for the four 16-output tiles.  Lane (r, g) takes A = out[t0 + r][k] and B =
+// Wp[16 j + r][k] (Wp is 384 KB: it stays in L2), 16 bytes per 8 steps each,
+// one group of 8 steps ahead: from memory in proj_out_fwd_kernel (no staging,
+// so two blocks share a CU), from the rows the block computed into LDS in
+// proj_out_fused_kernel (rows padded by 16 bytes).  The parts then meet in
+// LDS.  Tokens past T use row T - 1 and are never stored.
 constexpr int kFT = 16;                      // tokens per block
 constexpr int kParts = 8;                    // parts of K, one per wave
 constexpr int kPK = kD / kParts;             // 384
@@ -121,30 +122,47 @@ __device__ __forceinline__ void fwd_combine(uint32_t* lds, const f64x4_t (&acc)[
   if (t0 + i < T) *reinterpret_cast<uint32_t*>(latent + (t0 + i) * kO + o) = pack_bf16x2(res[0], res[1]);
 }
 
+// The same chains with A from memory: lane (r, g) reads out[t0 + r][384 p +
+// 32 q + 8 g ..] (16 bytes per 8 steps, one group ahead), as it reads Wp.
+__device__ __forceinline__ void fwd_chains_direct(const uint16_t* __restrict__ out, const uint16_t* __restrict__ W,
+                                                  int64_t t0, int64_t T, int p, f64x4_t (&acc)[4]) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const uint16_t* wrow = W + static_cast<int64_t>(r) * kD + kPK * p + 8 * g;
+  const uint16_t* arow = out + clamp_row(t0 + r, T) * kD + kPK * p + 8 * g;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+  uint4 wb[2][4], ab[2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) wb[0][j] = ld16(wrow + static_cast<int64_t>(16 * j) * kD);
+  ab[0] = ld16(arow);
+#pragma unroll
+  for (int q = 0; q < kPGroups; ++q) {
+    if (q + 1 < kPGroups) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wb[(q + 1) & 1][j] = ld16(wrow + static_cast<int64_t>(16 * j) * kD + 32 * (q + 1));
+      ab[(q + 1) & 1] = ld16(arow + 32 * (q + 1));
+    }
+    const uint4 av = ab[q & 1];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double a = el8(av, e);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = mfma_f64(a, el8(wb[q & 1][j], e), acc[j]);
+    }
+  }
+}
+
+constexpr size_t kCmbLds = sizeof(double) * kParts * kFT * kO;   // 64 KB
+
 __global__ __launch_bounds__(kFwdThreads) void proj_out_fwd_kernel(const uint16_t* __restrict__ out,
                                                                   const uint16_t* __restrict__ W,
                                                                   const uint16_t* __restrict__ bias,
                                                                   uint16_t* __restrict__ latent, int64_t T) {
-  __shared__ __align__(16) uint32_t lds[kFwdLds / 4];
+  __shared__ __align__(16) uint32_t lds[kCmbLds / 4];
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kFT;
-  // stage the 16 rows: 16 x 384 chunks of 16 bytes, 12 per thread, all in
-  // flight before the first LDS write
-  constexpr int kChunksPerRow = kD / 8;
-  constexpr int kIt = kFT * kChunksPerRow / kFwdThreads;
-  uint4 v[kIt];
-#pragma unroll
-  for (int it = 0; it < kIt; ++it) {
-    const int q = threadIdx.x + kFwdThreads * it;
-    v[it] = ld16(out + clamp_row(t0 + q / kChunksPerRow, T) * kD + 8 * (q % kChunksPerRow));
-  }
-#pragma unroll
-  for (int it = 0; it < kIt; ++it) {
-    const int q = threadIdx.x + kFwdThreads * it;
-    *reinterpret_cast<uint4*>(lds + (q / kChunksPerRow) * kARowDw + 4 * (q % kChunksPerRow)) = v[it];
-  }
-  __syncthreads();
   f64x4_t acc[4];
-  fwd_chains(lds, W, threadIdx.x >> 6, acc);
+  fwd_chains_direct(out, W, t0, T, threadIdx.x >> 6, acc);
   fwd_combine(lds, acc, bias, latent, t0, T);
 }
 
@@ -248,18 +266,19 @@ __device__ __forceinline__ void dx_block(const uint16_t* __restrict__ d_lat, con
   f64x4_t acc[8];
 #pragma unroll
   for (int kt = 0; kt < 8; ++kt) acc[kt] = f64x4_t{0.0, 0.0, 0.0, 0.0};
-  uint4 b[8][2];
+  // outputs 16 g + s for s = 0 .. 7, then 8 .. 15: half of the slab's row in registers at a time
 #pragma unroll
-  for (int kt = 0; kt < 8; ++kt) {
-    const uint32_t* row = lds + (128 * half + 16 * kt + r) * kWtStride2 + 8 * g;
-    b[kt][0] = *reinterpret_cast<const uint4*>(row);
-    b[kt][1] = *reinterpret_cast<const uint4*>(row + 4);
-  }
+  for (int h = 0; h < 2; ++h) {
+    uint4 b[8];
 #pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    const double a = el8(s < 8 ? a0 : a1, s & 7);
+    for (int kt = 0; kt < 8; ++kt)
+      b[kt] = *reinterpret_cast<const uint4*>(lds + (128 * half + 16 * kt + r) * kWtStride2 + 8 * g + 4 * h);
 #pragma unroll
-    for (int kt = 0; kt < 8; ++kt) acc[kt] = mfma_f64(a, el8(b[kt][s >> 3], s & 7), acc[kt]);
+    for (int s = 0; s < 8; ++s) {
+      const double a = el8(h == 0 ? a0 : a1, s);
+#pragma unroll
+      for (int kt = 0; kt < 8; ++kt) acc[kt] = mfma_f64(a, el8(b[kt], s), acc[kt]);
+    }
   }
   __syncthreads();   // the slab is read; its space now stages the results
   // lane holds token tw + g + 4 v, column k0 + 128 half + 16 kt + r
@@ -320,10 +339,8 @@ __device__ __forceinline__ void dw_chunk(const uint16_t* __restrict__ d_lat, con
       bd[slot] = td < T ? ld16(d_lat + td * kO + 8 * dc) : z;
     }
   };
-  load(0, 0);
-#pragma unroll
-  for (int rd = 0; rd < kRounds; ++rd) {
-    const int cur = rd & 1;
+  auto round = [&](int rd, auto slot_c) __attribute__((always_inline)) {
+    constexpr int cur = decltype(slot_c)::value;
     if (rd + 1 < kRounds) load(rd + 1, cur ^ 1);
     __syncthreads();   // the previous round's reads are done
     *reinterpret_cast<uint4*>(xs + xt * kStRow2 + 4 * xc) = bx0[cur];
@@ -343,6 +360,12 @@ __device__ __forceinline__ void dw_chunk(const uint16_t* __restrict__ d_lat, con
     if (bx == 0 && wave == 0) {
       for (int t = 0; t < kRound; ++t) sdb += static_cast<double>(bf16_to_f32(dh[t * (2 * kDlRow2) + lane]));
     }
+  };
+  load(0, 0);
+#pragma unroll 1
+  for (int rp = 0; rp < kRounds / 2; ++rp) {
+    round(2 * rp, std::integral_constant<int, 0>{});
+    round(2 * rp + 1, std::integral_constant<int, 1>{});
   }
   // lane holds outputs 16 ot + g + 4 v, columns k0 + 16 (n0 + n) + r
   double* pc = part + c * kO * kD;
