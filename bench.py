@@ -175,6 +175,9 @@ def parse():
                          "mod6: a block's 6-way modulation projection; proj_out: the 3072 -> 64 projection; "
                          "serve: the final layer's serving forward (modulation + proj_out, forward only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--roles", action="store_true",
+                    help="also time the dominant kernel's two roles alone (adaln_norm_mod_bwd_dx and "
+                         "adaln_norm_mod_bwd_tiles, each after a flush, 20 launches each; the final site, bf16)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="after the steps, run a plain 512 MiB device copy (PMC byte-counter calibration)")
     return ap.parse_args()
@@ -628,6 +631,29 @@ def main() -> int:
     copy4_gbps = copy_rate(4 * step_bytes)
     k_copy_gbps = kernel_copy_rate(k_bytes) if (kernel_timed and mfma_flops is None) else None
 
+    roles = None
+    if args.roles and kernel_timed:
+        # each role of the dominant kernel alone, timed as a phase (flush end to
+        # next flush start): the dx rows, then the level-0 tiles
+        s0 = sets[0]
+        rev = Events(2 * 40 + 1)
+        for i in range(40):
+            flush(rev.h[2 * i], rev.h[2 * i + 1])
+            if i % 2 == 0:
+                lib.check("adaln_norm_mod_bwd_dx", L.adaln_norm_mod_bwd_dx(
+                    s0["g"].data_ptr(), s0["x"].data_ptr(), s0["mean"].data_ptr(), s0["rstd"].data_ptr(),
+                    s0["emb"].data_ptr(), s0["dx"].data_ptr(), B, S, D, st))
+            else:
+                lib.check("adaln_norm_mod_bwd_tiles", L.adaln_norm_mod_bwd_tiles(
+                    s0["g"].data_ptr(), s0["x"].data_ptr(), s0["mean"].data_ptr(), s0["rstd"].data_ptr(),
+                    s0["ws_bw"].data_ptr(), ws_bw, B, S, D, st))
+        flush(rev.h[80], None)
+        torch.cuda.synchronize()
+        ph = [rev.ms(2 * i + 1, 2 * i + 2) for i in range(40)]
+        rev.close()
+        roles = {"dx_rows_phase_ms": round(_pct(ph[0::2], 0.5), 5), "tiles_phase_ms": round(_pct(ph[1::2], 0.5), 5),
+                 "note": "each role alone after the same flush, timed as a phase, medians of 20"}
+
     if args.copy_calib:
         n = 512 << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -672,6 +698,7 @@ def main() -> int:
                    "cold_bwd_median_ms": round(_pct(bwd_ms, 0.5), 5),
                    "cold_wall_s_incl_flushes": round(t_cold, 3),
                    "empty_phase_ms": round(empty_ms[len(empty_ms) // 2], 5),
+                   **({"roles": roles} if roles else {}),
                    "warm_ms_per_step": round(warm_ms, 5),
                    "warm_tokens_per_s": round(units / (warm_ms / 1e3), 1),
                    "warm_step_gbps": round(gbps(warm_ms), 1),
