@@ -33,6 +33,8 @@ WORKLOADS = {
     "img512_b2_s1024": dict(B=2, S=1024, outlier_frac=0.0),
     "img1024_b1_s4096": dict(B=1, S=4096, outlier_frac=0.01),
     "batch64_s1024": dict(B=64, S=1024, outlier_frac=0.0),
+    # one GPU's share of batch64_s1024 split over eight GPUs by samples
+    "batch8_s1024": dict(B=8, S=1024, outlier_frac=0.0),
     # the pages' large conditioning batch: 2048 samples of 3 tokens
     "batch2048_s3": dict(B=2048, S=3, outlier_frac=0.0),
 }
