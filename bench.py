@@ -111,7 +111,7 @@ def mod6_algorithmic_bytes(B: int) -> int:
 
 
 def mod6_dominant_kernel_bytes(B: int) -> int:
-    """The backward's main kernel at B <= 4 (its second launch only finishes
+    """The backward's main kernel at B <= 8 (its second launch only finishes
     dtemb): W read, dW and db written, d_emb and temb read."""
     return 2 * 2 * N6 * D + 2 * N6 + (4 * N6 + 2 * D) * B
 
@@ -431,8 +431,8 @@ def main() -> int:
         fwd_name, bwd_name = "adaln_proj_out_fwd", "adaln_proj_out_bwd"
         k_name = "proj_out_bwd_kernel (d_out = d_lat Wp and the dWp chunk partials in one launch)"
     elif mod6_site:
-        if B > 4:
-            print("--site mod6 times the B <= 4 backward kernel; use a workload with B <= 4", file=sys.stderr)
+        if B > 8:
+            print("--site mod6 times the B <= 8 backward kernel; use a workload with B <= 8", file=sys.stderr)
             return 2
         step_bytes, k_bytes = mod6_algorithmic_bytes(B), mod6_dominant_kernel_bytes(B)
         fwd_name, bwd_name = "adaln_proj_fwd", "adaln_proj_bwd"

@@ -49,7 +49,7 @@ extern "C" {
 
 typedef uint16_t adaln_bf16;
 
-#define ADALN_ABI_VERSION 14
+#define ADALN_ABI_VERSION 15
 
 enum adaln_status {
   ADALN_OK = 0,
@@ -87,8 +87,8 @@ enum adaln_op {
  *   PROJ_FWD:       H = K (3072), S ignored.  B*K*2 (SiLU activations, used when
  *                   B > 4).
  *   NORM_MOD_BWD:   H = D (3072).  B * ceil(S/32) * 2D * 8 bytes (level-0 pairs).
- *   PROJ_BWD:       H = K (3072), S ignored.  B <= 4: 32*B*K*8 (the fp64 da
- *                   subtrees, 32 per sample and column); B > 4: B*K*2 (SiLU
+ *   PROJ_BWD:       H = K (3072), S ignored.  B <= 8: 32*B*K*8 (the fp64 da
+ *                   subtrees, 32 per sample and column); B > 8: B*K*2 (SiLU
  *                   activations).
  *   TOKEN_TREE_SUM: B * ceil(S/32) * ceil(H/64) * 64 * 8 bytes (level-0 pairs).
  *   BWD:            H = D (3072).  NORM_MOD_BWD + PROJ_BWD, in that order.
@@ -196,11 +196,11 @@ int adaln_norm_mod_bwd_level0(const adaln_bf16* gout, const adaln_bf16* x, const
  *   exact (an fp64 fused multiply-add) and the sums run in fp64 in orders that
  *   do not depend on B: dW and db over samples ascending from +0; da as 128
  *   leaves (leaf t: rows t, t + 128, ..., ascending, from +0; N / 128 rows
- *   each) added pairwise in leaf order.  B <= 4 runs on the vector units, B > 4 on the fp64 matrix
+ *   each) added pairwise in leaf order.  B <= 8 runs on the vector units, B > 8 on the fp64 matrix
  *   cores: the same bits either way.
- *   ws: adaln_workspace_bytes(ADALN_OP_PROJ_BWD, B, 1, K) bytes (B <= 4: the
+ *   ws: adaln_workspace_bytes(ADALN_OP_PROJ_BWD, B, 1, K) bytes (B <= 8: the
  *   sums of leaves 4g .. 4g + 3 for g = 0 .. 31, added pairwise by a second
- *   launch; B > 4: a). */
+ *   launch; B > 8: a). */
 int adaln_proj_bwd(const float* d_emb, const adaln_bf16* temb, const adaln_bf16* W,
                    adaln_bf16* dW, adaln_bf16* db, adaln_bf16* dtemb, void* ws, size_t ws_bytes,
                    int64_t B, int64_t K, int64_t N, void* stream);

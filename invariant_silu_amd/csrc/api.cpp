@@ -101,8 +101,8 @@ size_t ws_proj_fwd(int64_t B) {
   return pad256(static_cast<size_t>(B * kD * 2));   // SiLU activations (B > 4)
 }
 size_t ws_proj_bwd(int64_t B) {
-  // B <= 4: the fp64 da subtrees (8 per sample and column) between the two
-  // launches; B > 4: the SiLU activations
+  // B <= 8: the fp64 da subtrees (32 per sample and column) between the two
+  // launches; B > 8: the SiLU activations
   return pad256(B <= adaln::proj_bwd_fused_max_batch() ? adaln::proj_bwd_fused_sub_bytes(B)
                                                        : static_cast<size_t>(B * kD * 2));
 }
@@ -123,7 +123,7 @@ size_t ws_fwd_proj_out(int64_t B, int64_t S) { return ws_proj_fwd(B) + ws_proj_o
 size_t ws_proj_bwd_f32(int64_t B) {
   // SiLU activations (fp32 storage); B <= 4: then the fp64 da subtrees
   return pad256(static_cast<size_t>(B * kD * 4)) +
-         (B <= adaln::proj_bwd_fused_max_batch() ? pad256(adaln::proj_bwd_fused_sub_bytes(B)) : 0);
+         (B <= adaln::proj_bwd_f32_max_batch() ? pad256(adaln::proj_bwd_fused_sub_bytes(B)) : 0);
 }
 bool batch_ok(int64_t B) { return B >= 1 && B <= kMaxB; }
 bool seq_ok(int64_t S) { return S >= 1 && S <= kMaxS; }

@@ -40,6 +40,8 @@ hipError_t launch_tree_fold(const float* part, float* out, int64_t B,
 hipError_t launch_tree_fold_views(const float* part, float* d0, float* d1, float* d2, int64_t ld, int64_t B,
                                   int64_t T0, int64_t nseg, hipStream_t s);
 int proj_bwd_fused_max_batch();
+// the same for the fp32-storage projection backward
+int proj_bwd_f32_max_batch();
 // bytes of fp64 da subtrees the B <= 4 path keeps between its two launches
 size_t proj_bwd_fused_sub_bytes(int64_t B);
 // Optional fp32 copies of the projection backward's bf16 outputs (the values

@@ -18,13 +18,13 @@
 // these orders exactly, so no result depends on the batch size or the grid.
 //
 // Kernels:
-//   proj_bwd_small_kernel<NB>  B <= 4: da leaf-group blocks (-> the 32
+//   proj_bwd_small_kernel<NB>  B <= 8: da leaf-group blocks (-> the 32
 //                              4-leaf subtrees of every column) and dW tiles
 //                              (-> dW, db) in one grid
-//   da_finish_kernel<NB>       B <= 4: the subtrees added pairwise (-> dtemb)
+//   da_finish_kernel<NB>       B <= 8: the subtrees added pairwise (-> dtemb)
 //   da_leaf_f32_kernel<NB>     fp32 storage, B <= 4: the leaf-group blocks alone
 //                              (then da_finish_kernel<NB, float>)
-//   silu_kernel, dw_mfma_kernel, da_mfma_kernel   B > 4
+//   silu_kernel, dw_mfma_kernel, da_mfma_kernel   B > 8 (fp32 storage: B > 4)
 // With kAcc (adaln_proj_bwd_acc) the bf16 kernels also store the fp32 values
 // they round to bf16 -- fl32 of the dW and db sums, and da * silu'(temb) in
 // fp32 -- into whichever of the caller's fp32 arrays are not NULL; the
@@ -33,6 +33,8 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "mfma.hpp"
+
+#include <type_traits>
 
 namespace adaln {
 
@@ -53,7 +55,7 @@ template <int N>
 constexpr int kDwParts = N / kRowsPerPart;           // 32 at N = 6144
 template <int N>
 constexpr int kDwTiles = kDwParts<N> * (kD / kTileCols);   // 384 at N = 6144
-constexpr int kBatchChunk = 4;
+constexpr int kBatchChunk = 8;
 
 static_assert(kN % kRowsPerPart == 0 && kN6 % kRowsPerPart == 0 && kRowsPerPart % kSlots == 0, "part layout");
 static_assert(kD % kTileCols == 0, "column blocks");
@@ -153,7 +155,7 @@ __device__ __forceinline__ void da_leaf_group(const float* __restrict__ d_emb, c
                                               double* __restrict__ sub, int L, double* red) {
   // rows per batch (two batches in flight, registers <= ~128); N / 128 rows
   // per leaf (48 or 144)
-  constexpr int U = sizeof(T) == 4 ? (NB == 1 ? 8 : (NB == 2 ? 6 : 4)) : (NB == 1 ? 12 : (NB == 2 ? 8 : 6));
+  constexpr int U = sizeof(T) == 4 ? (NB == 1 ? 8 : (NB == 2 ? 6 : 4)) : (NB == 1 ? 12 : (NB == 2 ? 8 : (NB <= 4 ? 6 : 4)));
   constexpr int kLeafRows = kDaSteps<N>;
   static_assert(kLeafRows % (2 * U) == 0, "batch pairs");
   const int gq = L % kDaGroups, cg = L / kDaGroups;
@@ -294,15 +296,18 @@ __device__ __forceinline__ void dw_tile(const float* __restrict__ d_emb,
     if (idx < NB * kRowsPerPart) de_lds[idx / kRowsPerPart][idx % kRowsPerPart] = de_r[k];
   }
   float av[NB][8];
-  uint32_t redo = 0;
+  // 8 flag bits per sample: the mask holds NB * 8 bits
+  using Mask = std::conditional_t<(NB > 4), uint64_t, uint32_t>;
+  static_assert(NB <= 8, "redo mask holds 8 samples of 8 elements");
+  Mask redo = 0;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     uint32_t m;
     unpack8(silu8_fast(tz[b], m), av[b]);
-    redo |= m << (8 * b);
+    redo |= static_cast<Mask>(m) << (8 * b);
   }
   while (redo != 0) {   // rarely taken: elements the fast SiLU cannot decide
-    const int bit = __builtin_ctz(redo);
+    const int bit = sizeof(Mask) == 8 ? __builtin_ctzll(redo) : __builtin_ctz(static_cast<uint32_t>(redo));
     redo &= redo - 1;
     const int b = bit / 8, e = bit % 8;
     const float v = bf16_to_f32(silu_bf16_exact(bf16_to_f32(temb[static_cast<int64_t>(b) * kD + col + e])));
@@ -616,6 +621,7 @@ __global__ __launch_bounds__(kThreads) void da_leaf_f32_kernel(const float* __re
 }  // namespace
 
 int proj_bwd_fused_max_batch() { return kBatchChunk; }
+int proj_bwd_f32_max_batch() { return 4; }
 
 namespace {
 
@@ -643,6 +649,10 @@ hipError_t proj_bwd_fused_rows(const float* d_emb, const uint16_t* temb, const u
     case 2: return launch_small<2, N, kAcc>(d_emb, temb, W, dW, db, dtemb, sub, acc, s);
     case 3: return launch_small<3, N, kAcc>(d_emb, temb, W, dW, db, dtemb, sub, acc, s);
     case 4: return launch_small<4, N, kAcc>(d_emb, temb, W, dW, db, dtemb, sub, acc, s);
+    case 5: return launch_small<5, N, kAcc>(d_emb, temb, W, dW, db, dtemb, sub, acc, s);
+    case 6: return launch_small<6, N, kAcc>(d_emb, temb, W, dW, db, dtemb, sub, acc, s);
+    case 7: return launch_small<7, N, kAcc>(d_emb, temb, W, dW, db, dtemb, sub, acc, s);
+    case 8: return launch_small<8, N, kAcc>(d_emb, temb, W, dW, db, dtemb, sub, acc, s);
     default: return hipErrorInvalidValue;
   }
 }

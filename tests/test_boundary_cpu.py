@@ -46,19 +46,19 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_strerror(L):
-    assert L.adaln_abi_version() == 14
+    assert L.adaln_abi_version() == 15
     for code in range(-8, 1):
         assert len(lib.strerror(code)) >= 2
 
 
 def test_workspace_sizes(L):
     pad = lambda n: (n + 255) // 256 * 256   # noqa: E731
-    for B, S in [(1, 31), (2, 1024), (1, 4096), (64, 1024), (3, 6889)]:
+    for B, S in [(1, 31), (2, 1024), (1, 4096), (64, 1024), (3, 6889), (5, 33), (8, 1024), (9, 3)]:
         T0 = math.ceil(S / 32)
         assert lib.workspace_bytes(lib.OP_NORM_MOD_BWD, B, S, 3072) == pad(B * T0 * 6144 * 8)
         assert lib.workspace_bytes(lib.OP_TOKEN_TREE_SUM, B, S, 100) == pad(B * T0 * 128 * 8)
-        # B <= 4: 32 fp64 da subtrees per sample and column; B > 4: the SiLU activations
-        proj_bwd = pad(32 * B * 3072 * 8) if B <= 4 else pad(B * 3072 * 2)
+        # B <= 8: 32 fp64 da subtrees per sample and column; B > 8: the SiLU activations
+        proj_bwd = pad(32 * B * 3072 * 8) if B <= 8 else pad(B * 3072 * 2)
         assert lib.workspace_bytes(lib.OP_PROJ_BWD, B, S, 3072) == proj_bwd
         assert lib.workspace_bytes(lib.OP_PROJ_FWD, B, S, 3072) == pad(B * 3072 * 2)
         # fp32: the activations, then for B <= 4 the fp64 da subtrees

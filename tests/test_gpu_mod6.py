@@ -1,7 +1,7 @@
 """A block's 6-way modulation projection (N = 6 x 3072 = 18432) on the GPU,
 through adaln_proj_fwd / adaln_proj_bwd: parity with oracle/modulation.py and
-bytewise batch invariance across the vector-unit (B <= 4) and matrix-core
-(B > 4) branches.  bf16 outputs are gated at 1 ulp from the fp32 oracle,
+bytewise batch invariance across the vector-unit (forward B <= 4, backward
+B <= 8) and matrix-core (beyond) branches.  bf16 outputs are gated at 1 ulp from the fp32 oracle,
 else 1 ulp from its fp64 twin (tests/compare.py).
 """
 
@@ -72,10 +72,10 @@ def test_mod6_singleton_vs_batch(gpu_lib, B):
 
 
 def test_mod6_param_grads_zero_padding(gpu_lib):
-    """dW and db of three samples (vector units) equal those of seven samples
-    whose last four have d_emb = 0 (matrix cores), byte for byte."""
+    """dW and db of three samples (vector units) equal those of eleven samples
+    whose last eight have d_emb = 0 (matrix cores), byte for byte."""
     print("[mod6] zero padding", flush=True)
-    d = _dev(make_mod6_inputs(7, seed=97))
+    d = _dev(make_mod6_inputs(11, seed=97))
     base = _run({k: (v[:3] if k in ("temb", "d_emb") else v) for k, v in d.items()})
     padded = dict(d)
     padded["d_emb"] = d["d_emb"].clone()
