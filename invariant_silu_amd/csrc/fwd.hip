@@ -26,9 +26,11 @@
 //
 // Kernels: proj_fwd_kernel / proj_mfma_kernel (adaln_proj_fwd),
 // norm_mod_fwd_kernel (statistics and modulation, adaln_norm_mod_fwd), and
-// for the one-call forward adaln_fwd with B <= 4: fwd_stage1_kernel
-// (projection blocks and statistics blocks in one grid: two independent HBM
-// streams, W and x) then norm_modulate_kernel; with B > 4, silu_kernel and
+// for the one-call forward adaln_fwd with B <= 4 and x within the L2s
+// (32 MiB): fwd_stage1_kernel (projection blocks and statistics blocks in one
+// grid: two independent HBM streams, W and x) then norm_modulate_kernel, which
+// finds x in L2; with B <= 4 and a larger x, proj_fwd_kernel then
+// norm_mod_fwd_kernel (x read once); with B > 4, silu_kernel and
 // proj_mfma_kernel, then norm_mod_fwd_kernel.
 #include "common.hpp"
 #include "launch.hpp"
@@ -45,6 +47,10 @@ constexpr int kRows = 2;                                   // rows of W per wave
 constexpr int kProjRowsPerBlock = kWaves * kRows;          // 8
 constexpr int kProjBlocks = kN / kProjRowsPerBlock;        // 768
 constexpr int kMaxNarrowBatch = 4;                         // proj_block up to here
+// x up to this size (bytes) is read twice by the B <= 4 forward, the second
+// time from the L2s (8 XCDs x 4 MB); beyond it one statistics-and-modulation
+// pass after the projection reads it once
+constexpr int64_t kStage1MaxXBytes = int64_t(32) << 20;
 static_assert(kN % kProjRowsPerBlock == 0 && kN6 % kProjRowsPerBlock == 0, "rows per block must divide N");
 
 // ----------------------------------------------------------- projection ----
@@ -628,6 +634,10 @@ hipError_t launch_fwd(const uint16_t* temb, const uint16_t* W, const uint16_t* b
     // modulation overwrites later), the matrix-core projection, then
     // statistics and modulation in one pass over x
     if (hipError_t e = launch_mfma(temb, out, W, bias, emb, B, s); e != hipSuccess) return e;
+    return launch_norm_mod_fwd(x, emb, out, mean, rstd, B, S, eps, s);
+  }
+  if (B * S * kD * 2 > kStage1MaxXBytes) {
+    if (hipError_t e = proj_fwd_rows<kN>(temb, W, bias, emb, nullptr, B, s); e != hipSuccess) return e;
     return launch_norm_mod_fwd(x, emb, out, mean, rstd, B, S, eps, s);
   }
   const int64_t stat_blocks = (B * S + kWaves - 1) / kWaves;

@@ -146,7 +146,7 @@ def test_projection_paths_agree_on_extreme_inputs(gpu_lib):
     an fp32 product of the operands would lose bits: SiLU of temb near -90 is a
     bf16 subnormal (or zero), and W spans 2^-40 .. 2^20, so some products lie
     far below fp32's normal range while others dominate the sums."""
-    print("[invariance] projection paths, extreme inputs, B=40 vs 1 and 4", flush=True)
+    print("[invariance] projection paths, extreme inputs, B=40 vs 1, 4 and 8", flush=True)
     from invariant_silu_amd import ops
     from synthetic_inputs import f32_to_bf16_bits
     from tests.gpu_helpers import to_dev
@@ -165,3 +165,5 @@ def test_projection_paths_agree_on_extreme_inputs(gpu_lib):
         assert same_bytes(emb[b:b + 1], ops.proj_fwd(t_d[b:b + 1], W_d, b_d)), f"sample {b} (B=1)"
     for lo in range(0, B, 4):
         assert same_bytes(emb[lo:lo + 4], ops.proj_fwd(t_d[lo:lo + 4], W_d, b_d)), f"samples {lo}.. (B=4)"
+    for lo in range(0, B, 8):
+        assert same_bytes(emb[lo:lo + 8], ops.proj_fwd(t_d[lo:lo + 8], W_d, b_d)), f"samples {lo}.. (B=8)"
