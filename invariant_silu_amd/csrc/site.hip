@@ -26,8 +26,8 @@ template <bool kRes>
 __device__ __forceinline__ void site_row_pass(
     const uint16_t* __restrict__ g, const uint16_t* __restrict__ h, const float* __restrict__ mean,
     const float* __restrict__ rstd, const ModView& mv, const uint16_t* __restrict__ gh,
-    const uint16_t* __restrict__ x, uint16_t* __restrict__ dres, uint16_t* __restrict__ dxo, int64_t b, int64_t s,
-    int64_t S, float4* m_lds, float4* gate_lds) {
+    uint16_t* __restrict__ dres, uint16_t* __restrict__ dxo, int64_t b, int64_t s, int64_t S, float4* m_lds,
+    float4* gate_lds) {
   const int lane = threadIdx.x & 63;
   const int64_t row = b * S + (s < S ? s : S - 1);   // as in row_pass
   const uint2* scale = reinterpret_cast<const uint2*>(mv.scale + b * mv.ld);
@@ -74,13 +74,10 @@ __device__ __forceinline__ void site_row_pass(
       q2 += static_cast<double>(gy * n);
     }
   }
-  uint4 ghv[kLaneChunks], xv[kLaneChunks];
+  uint4 ghv[kLaneChunks];
   if (kRes)
 #pragma unroll
-    for (int i = 0; i < kLaneChunks; ++i) {
-      ghv[i] = ld16(gh + row * kD + (lane + 64 * i) * 8);
-      xv[i] = ld16(x + row * kD + (lane + 64 * i) * 8);
-    }
+    for (int i = 0; i < kLaneChunks; ++i) ghv[i] = ld16(gh + row * kD + (lane + 64 * i) * 8);
   const float alpha = static_cast<float>(wave_sum_f64(q1)) / static_cast<float>(kD);
   const float beta = static_cast<float>(wave_sum_f64(q2)) / static_cast<float>(kD);
 #pragma unroll
@@ -100,9 +97,8 @@ __device__ __forceinline__ void site_row_pass(
       st16_nt(dxo + row * kD + c * 8, pack8(dxv));
       continue;
     }
-    float ghf[8], xf[8];
+    float ghf[8];
     unpack8(ghv[i], ghf);
-    unpack8(xv[i], xf);
     const float4 m0 = m_lds[2 * c], m1 = m_lds[2 * c + 1];
     const float4 g0 = gate_lds[2 * c], g1 = gate_lds[2 * c + 1];
     const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
@@ -124,10 +120,10 @@ __device__ __forceinline__ void site_row_pass(
 // (d_shift, d_scale pairs) of one 32-token tile on one XCD
 template <bool kRes>
 __global__ __launch_bounds__(kThreads) void site_bwd_kernel(
-    const uint16_t* __restrict__ g, const uint16_t* __restrict__ gh, const uint16_t* __restrict__ x,
-    const uint16_t* __restrict__ h, const float* __restrict__ mean, const float* __restrict__ rstd,
-    const ModView mv, uint16_t* __restrict__ dres, uint16_t* __restrict__ dxo,
-    float* __restrict__ part, int64_t B, int64_t S, int64_t T0) {
+    const uint16_t* __restrict__ g, const uint16_t* __restrict__ gh, const uint16_t* __restrict__ h,
+    const float* __restrict__ mean, const float* __restrict__ rstd, const ModView mv,
+    uint16_t* __restrict__ dres, uint16_t* __restrict__ dxo, float* __restrict__ part, int64_t B, int64_t S,
+    int64_t T0) {
   __shared__ float4 m_lds[kD / 4];
   __shared__ float4 gate_lds[kD / 4];
   const int64_t L = blockIdx.x;
@@ -139,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void site_bwd_kernel(
   const int64_t tile = G % T0;
   if (role < kRowBlocks) {
     const int64_t s = tile * kTile + role * 4 + (threadIdx.x >> 6);
-    site_row_pass<kRes>(g, h, mean, rstd, mv, gh, x, dres, dxo, b, s, S, m_lds, gate_lds);
+    site_row_pass<kRes>(g, h, mean, rstd, mv, gh, dres, dxo, b, s, S, m_lds, gate_lds);
   } else {
     col_pass(g, h, mean, rstd, part, b, tile, role - kRowBlocks, S, T0, kRes ? kModGroups : kSiteGroups, kD, 0);
   }
@@ -201,11 +197,10 @@ __global__ __launch_bounds__(kThreads) void gate_tile_kernel(const uint16_t* __r
 
 namespace {
 template <bool kRes>
-void launch_site_bwd_kernel(dim3 grid, hipStream_t s, const uint16_t* g_out,
-                            const uint16_t* g_h, const uint16_t* x, const uint16_t* h, const float* mean,
-                            const float* rstd, const ModView& mv, uint16_t* d_residual, uint16_t* dx, float* part,
-                            int64_t B, int64_t S, int64_t T0) {
-  hipLaunchKernelGGL(site_bwd_kernel<kRes>, grid, dim3(kThreads), 0, s, g_out, g_h, x, h, mean, rstd, mv, d_residual,
+void launch_site_bwd_kernel(dim3 grid, hipStream_t s, const uint16_t* g_out, const uint16_t* g_h,
+                            const uint16_t* h, const float* mean, const float* rstd, const ModView& mv,
+                            uint16_t* d_residual, uint16_t* dx, float* part, int64_t B, int64_t S, int64_t T0) {
+  hipLaunchKernelGGL(site_bwd_kernel<kRes>, grid, dim3(kThreads), 0, s, g_out, g_h, h, mean, rstd, mv, d_residual,
                      dx, part, B, S, T0);
 }
 }  // namespace
@@ -217,11 +212,10 @@ hipError_t launch_site_bwd(const uint16_t* g_out, const uint16_t* g_h, const uin
   const int64_t groups = (B * T0 + 7) / 8;
   const dim3 grid(static_cast<unsigned>(groups * 8 * kBlocksPerTile));
   if (!g_h) {   // plain form: the LayerNorm input is x
-    launch_site_bwd_kernel<false>(grid, s, g_out, nullptr, nullptr, x, mean, rstd, mv, nullptr, dx, part,
-                                  B, S, T0);
+    launch_site_bwd_kernel<false>(grid, s, g_out, nullptr, x, mean, rstd, mv, nullptr, dx, part, B, S, T0);
     return hipGetLastError();
   }
-  launch_site_bwd_kernel<true>(grid, s, g_out, g_h, x, h, mean, rstd, mv, d_residual, dx, part, B, S, T0);
+  launch_site_bwd_kernel<true>(grid, s, g_out, g_h, h, mean, rstd, mv, d_residual, dx, part, B, S, T0);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   hipLaunchKernelGGL(gate_tile_kernel, dim3(static_cast<unsigned>(B * T0 * kColBlocks)), dim3(kThreads), 0, s,
                      d_residual, x, part, S, T0);
