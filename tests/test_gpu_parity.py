@@ -30,6 +30,9 @@ CASES = {
     "b2_s33": (2, 33, 2026, 0.0),
     "img512_b2_s1024": (2, 1024, 0, 0.0),
     "img1024_b1_s4096": (1, 4096, 0, 0.01),
+    # eight samples: the matrix-core forward projection with the vector-unit
+    # projection backward at its widest (NB = 8)
+    "b8_s40": (8, 40, 7, 0.0),
 }
 
 
