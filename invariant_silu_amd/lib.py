@@ -60,6 +60,9 @@ _SIGS = {
     "adaln_abi_version": ([], ctypes.c_int),
 }
 
+# ADALN_ABI_VERSION of include/adaln.h that the signatures above describe
+ABI_VERSION = 15
+
 _lock = threading.Lock()
 _lib = None
 
@@ -89,6 +92,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.argtypes = args
             fn.restype = res
+        found = lib.adaln_abi_version()
+        if found != ABI_VERSION:
+            raise ImportError(f"{path} has ABI version {found}, this binding expects {ABI_VERSION}: "
+                              "rebuild it with __graft_entry__.build()")
         _lib = lib
         return lib
 

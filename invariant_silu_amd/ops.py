@@ -66,6 +66,17 @@ def _check(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _call(tensors, name: str, *args) -> None:
+    """Call entry point `name` with every tensor it receives on one device, that
+    device current (the library launches on the current device and checks its
+    architecture there)."""
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) != 1:
+        raise ValueError(f"{name}: all tensors must be on one GPU, got {sorted(str(d) for d in devs)}")
+    with torch.cuda.device(devs.pop()):
+        _lib.call(name, *args)
+
+
 def _ws(op: int, B: int, S: int, H: int, device) -> torch.Tensor:
     n = _lib.workspace_bytes(op, B, S, H)
     if n == 0:
@@ -87,8 +98,8 @@ def proj_fwd(temb: torch.Tensor, W: torch.Tensor, bias: torch.Tensor) -> torch.T
     B = temb.shape[0]
     emb = torch.empty((B, W.shape[0]), dtype=torch.bfloat16, device=temb.device)
     ws = _ws(_lib.OP_PROJ_FWD, B, 1, temb.shape[1], temb.device)
-    _lib.call("adaln_proj_fwd", temb.data_ptr(), W.data_ptr(), bias.data_ptr(), emb.data_ptr(),
-              ws.data_ptr(), ws.numel(), B, temb.shape[1], W.shape[0], _stream(temb.device))
+    _call((temb, W, bias, emb, ws), "adaln_proj_fwd", temb.data_ptr(), W.data_ptr(), bias.data_ptr(), emb.data_ptr(),
+          ws.data_ptr(), ws.numel(), B, temb.shape[1], W.shape[0], _stream(temb.device))
     return emb
 
 
@@ -103,8 +114,8 @@ def norm_mod_fwd(x: torch.Tensor, emb: torch.Tensor, eps: float = EPS):
     out = torch.empty_like(x)
     mean = torch.empty((B, S), dtype=torch.float32, device=x.device)
     rstd = torch.empty((B, S), dtype=torch.float32, device=x.device)
-    _lib.call("adaln_norm_mod_fwd", x.data_ptr(), emb.data_ptr(), out.data_ptr(), mean.data_ptr(),
-              rstd.data_ptr(), B, S, Dx, float(eps), _stream(x.device))
+    _call((x, emb, out, mean, rstd), "adaln_norm_mod_fwd", x.data_ptr(), emb.data_ptr(), out.data_ptr(),
+          mean.data_ptr(), rstd.data_ptr(), B, S, Dx, float(eps), _stream(x.device))
     return out, mean, rstd
 
 
@@ -126,9 +137,9 @@ def norm_mod_bwd(g: torch.Tensor, x: torch.Tensor, mean: torch.Tensor, rstd: tor
     dx = torch.empty_like(x)
     d_emb = torch.empty((B, N), dtype=torch.float32, device=x.device)
     ws = _ws(_lib.OP_NORM_MOD_BWD, B, S, Dx, x.device)
-    _lib.call("adaln_norm_mod_bwd", g.data_ptr(), x.data_ptr(), mean.data_ptr(), rstd.data_ptr(),
-              emb.data_ptr(), dx.data_ptr(), d_emb.data_ptr(), ws.data_ptr(), ws.numel(), B, S, Dx,
-              _stream(x.device))
+    _call((g, x, mean, rstd, emb, dx, d_emb, ws), "adaln_norm_mod_bwd", g.data_ptr(), x.data_ptr(), mean.data_ptr(),
+          rstd.data_ptr(), emb.data_ptr(), dx.data_ptr(), d_emb.data_ptr(), ws.data_ptr(), ws.numel(), B, S, Dx,
+          _stream(x.device))
     return dx, d_emb
 
 
@@ -151,16 +162,17 @@ def proj_bwd(d_emb: torch.Tensor, temb: torch.Tensor, W: torch.Tensor, want_f32:
     dtemb = torch.empty_like(temb)
     ws = _ws(_lib.OP_PROJ_BWD, B, 1, D, W.device)
     if not want_f32:
-        _lib.call("adaln_proj_bwd", d_emb.data_ptr(), temb.data_ptr(), W.data_ptr(), dW.data_ptr(),
-                  db.data_ptr(), dtemb.data_ptr(), ws.data_ptr(), ws.numel(), B, temb.shape[1],
-                  W.shape[0], _stream(W.device))
+        _call((d_emb, temb, W, dW, db, dtemb, ws), "adaln_proj_bwd", d_emb.data_ptr(), temb.data_ptr(), W.data_ptr(),
+              dW.data_ptr(), db.data_ptr(), dtemb.data_ptr(), ws.data_ptr(), ws.numel(), B, temb.shape[1], W.shape[0],
+              _stream(W.device))
         return dW, db, dtemb
     dW32 = torch.empty(W.shape, dtype=torch.float32, device=W.device)
     db32 = torch.empty((W.shape[0],), dtype=torch.float32, device=W.device)
     dtemb32 = torch.empty(temb.shape, dtype=torch.float32, device=W.device)
-    _lib.call("adaln_proj_bwd_acc", d_emb.data_ptr(), temb.data_ptr(), W.data_ptr(), dW.data_ptr(),
-              db.data_ptr(), dtemb.data_ptr(), dW32.data_ptr(), db32.data_ptr(), dtemb32.data_ptr(),
-              ws.data_ptr(), ws.numel(), B, temb.shape[1], W.shape[0], _stream(W.device))
+    _call((d_emb, temb, W, dW, db, dtemb, dW32, db32, dtemb32, ws), "adaln_proj_bwd_acc", d_emb.data_ptr(),
+          temb.data_ptr(), W.data_ptr(), dW.data_ptr(), db.data_ptr(), dtemb.data_ptr(), dW32.data_ptr(),
+          db32.data_ptr(), dtemb32.data_ptr(), ws.data_ptr(), ws.numel(), B, temb.shape[1], W.shape[0],
+          _stream(W.device))
     return dW, db, dtemb, dW32, db32, dtemb32
 
 
@@ -172,8 +184,8 @@ def token_tree_sum(x: torch.Tensor) -> torch.Tensor:
     B, S, H = x.shape
     out = torch.empty((B, H), dtype=torch.float32, device=x.device)
     ws = _ws(_lib.OP_TOKEN_TREE_SUM, B, S, H, x.device)
-    _lib.call("token_tree_sum", x.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel(), B, S, H,
-              _stream(x.device))
+    _call((x, out, ws), "token_tree_sum", x.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel(), B, S, H,
+          _stream(x.device))
     return out
 
 
@@ -199,9 +211,9 @@ def fwd(x: torch.Tensor, temb: torch.Tensor, W: torch.Tensor, bias: torch.Tensor
     out = torch.empty_like(x)
     mean = torch.empty((B, S), dtype=torch.float32, device=x.device)
     rstd = torch.empty((B, S), dtype=torch.float32, device=x.device)
-    _lib.call("adaln_fwd" if dt == torch.bfloat16 else "adaln_fwd_f32", temb.data_ptr(), W.data_ptr(),
-              bias.data_ptr(), x.data_ptr(), emb.data_ptr(), out.data_ptr(), mean.data_ptr(), rstd.data_ptr(),
-              B, S, Dx, float(eps), _stream(x.device))
+    _call((temb, W, bias, x, emb, out, mean, rstd), "adaln_fwd" if dt == torch.bfloat16 else "adaln_fwd_f32",
+          temb.data_ptr(), W.data_ptr(), bias.data_ptr(), x.data_ptr(), emb.data_ptr(), out.data_ptr(),
+          mean.data_ptr(), rstd.data_ptr(), B, S, Dx, float(eps), _stream(x.device))
     return out, emb, mean, rstd
 
 
@@ -232,10 +244,10 @@ def bwd(g: torch.Tensor, x: torch.Tensor, mean: torch.Tensor, rstd: torch.Tensor
     dtemb = torch.empty_like(temb)
     f32 = dt == torch.float32
     ws = _ws(_lib.OP_BWD_F32 if f32 else _lib.OP_BWD, B, S, Dx, x.device)
-    _lib.call("adaln_bwd_f32" if f32 else "adaln_bwd", g.data_ptr(), x.data_ptr(), mean.data_ptr(),
-              rstd.data_ptr(), emb.data_ptr(), temb.data_ptr(), W.data_ptr(), dx.data_ptr(), d_emb.data_ptr(),
-              dW.data_ptr(), db.data_ptr(), dtemb.data_ptr(), ws.data_ptr(), ws.numel(), B, S, Dx,
-              _stream(x.device))
+    _call((g, x, mean, rstd, emb, temb, W, dx, d_emb, dW, db, dtemb, ws), "adaln_bwd_f32" if f32 else "adaln_bwd",
+          g.data_ptr(), x.data_ptr(), mean.data_ptr(), rstd.data_ptr(), emb.data_ptr(), temb.data_ptr(), W.data_ptr(),
+          dx.data_ptr(), d_emb.data_ptr(), dW.data_ptr(), db.data_ptr(), dtemb.data_ptr(), ws.data_ptr(), ws.numel(),
+          B, S, Dx, _stream(x.device))
     return dx, d_emb, dW, db, dtemb
 
 
@@ -254,8 +266,9 @@ def residual_fwd(x: torch.Tensor, residual: torch.Tensor, mod: torch.Tensor, eps
     out = torch.empty_like(x)
     mean = torch.empty((B, S), dtype=torch.float32, device=x.device)
     rstd = torch.empty((B, S), dtype=torch.float32, device=x.device)
-    _lib.call("adaln_residual_fwd", x.data_ptr(), residual.data_ptr(), mod.data_ptr(), h.data_ptr(), out.data_ptr(),
-              mean.data_ptr(), rstd.data_ptr(), B, S, Dx, float(eps), _stream(x.device))
+    _call((x, residual, mod, h, out, mean, rstd), "adaln_residual_fwd", x.data_ptr(), residual.data_ptr(),
+          mod.data_ptr(), h.data_ptr(), out.data_ptr(), mean.data_ptr(), rstd.data_ptr(), B, S, Dx, float(eps),
+          _stream(x.device))
     return out, h, mean, rstd
 
 
@@ -279,9 +292,10 @@ def residual_bwd(g_out: torch.Tensor, g_h: torch.Tensor, x: torch.Tensor, h: tor
     dx = torch.empty_like(x)
     d_mod = torch.empty((B, 3 * Dx), dtype=torch.float32, device=x.device)
     ws = _ws(_lib.OP_RESIDUAL_BWD, B, S, Dx, x.device)
-    _lib.call("adaln_residual_bwd", g_out.data_ptr(), g_h.data_ptr(), x.data_ptr(), h.data_ptr(), mean.data_ptr(),
-              rstd.data_ptr(), mod.data_ptr(), d_residual.data_ptr(), dx.data_ptr(), d_mod.data_ptr(),
-              ws.data_ptr(), ws.numel(), B, S, Dx, _stream(x.device))
+    _call((g_out, g_h, x, h, mean, rstd, mod, d_residual, dx, d_mod, ws), "adaln_residual_bwd", g_out.data_ptr(),
+          g_h.data_ptr(), x.data_ptr(), h.data_ptr(), mean.data_ptr(), rstd.data_ptr(), mod.data_ptr(),
+          d_residual.data_ptr(), dx.data_ptr(), d_mod.data_ptr(), ws.data_ptr(), ws.numel(), B, S, Dx,
+          _stream(x.device))
     return d_residual, dx, d_mod
 
 
@@ -325,9 +339,10 @@ def site_fwd(x: torch.Tensor, shift: torch.Tensor, scale: torch.Tensor, residual
     if res:
         _check(residual, torch.bfloat16, "residual")
         residual = aligned(residual)
-    _lib.call("adaln_site_fwd", x.data_ptr(), residual.data_ptr() if res else None, views[0].data_ptr(),
-              views[1].data_ptr(), views[2].data_ptr() if res else None, ld, h.data_ptr() if res else None,
-              out.data_ptr(), mean.data_ptr(), rstd.data_ptr(), B, S, Dx, float(eps), _stream(x.device))
+    _call((x, residual, *views, h, out, mean, rstd), "adaln_site_fwd", x.data_ptr(),
+          residual.data_ptr() if res else None, views[0].data_ptr(), views[1].data_ptr(),
+          views[2].data_ptr() if res else None, ld, h.data_ptr() if res else None, out.data_ptr(), mean.data_ptr(),
+          rstd.data_ptr(), B, S, Dx, float(eps), _stream(x.device))
     return (out, h, mean, rstd) if res else (out, mean, rstd)
 
 
@@ -378,11 +393,11 @@ def site_bwd(g_out: torch.Tensor, x: torch.Tensor, mean: torch.Tensor, rstd: tor
         g_h, h = aligned(g_h), aligned(h)
         d_res = torch.empty_like(x)
     ws = _ws(_lib.OP_RESIDUAL_BWD, B, S, Dx, x.device)
-    _lib.call("adaln_site_bwd", g_out.data_ptr(), g_h.data_ptr() if res else None, x.data_ptr(),
-              h.data_ptr() if res else None, mean.data_ptr(), rstd.data_ptr(), views[0].data_ptr(),
-              views[1].data_ptr() if res else None, ld, d_res.data_ptr() if res else None, dx.data_ptr(),
-              d_views[0].data_ptr(), d_views[1].data_ptr(), d_views[2].data_ptr() if res else None, dld,
-              ws.data_ptr(), ws.numel(), B, S, Dx, _stream(x.device))
+    _call((g_out, g_h, x, h, mean, rstd, *views, d_res, dx, *d_views, ws), "adaln_site_bwd", g_out.data_ptr(),
+          g_h.data_ptr() if res else None, x.data_ptr(), h.data_ptr() if res else None, mean.data_ptr(),
+          rstd.data_ptr(), views[0].data_ptr(), views[1].data_ptr() if res else None, ld,
+          d_res.data_ptr() if res else None, dx.data_ptr(), d_views[0].data_ptr(), d_views[1].data_ptr(),
+          d_views[2].data_ptr() if res else None, dld, ws.data_ptr(), ws.numel(), B, S, Dx, _stream(x.device))
     if res:
         return d_res, dx, d_views[0], d_views[1], d_views[2]
     return dx, d_views[0], d_views[1]
@@ -402,8 +417,8 @@ def proj_out_fwd(out: torch.Tensor, W: torch.Tensor, bias: torch.Tensor) -> torc
     latent = torch.empty(out.shape[:-1] + (W.shape[0],), dtype=torch.bfloat16, device=out.device)
     B, S = (out.shape[0], out.shape[1]) if out.dim() == 3 else (1, T)   # the workspace depends on T = B * S
     ws = _ws(_lib.OP_PROJ_OUT_FWD, B, S, out.shape[-1], out.device)
-    _lib.call("adaln_proj_out_fwd", out.data_ptr(), W.data_ptr(), bias.data_ptr(), latent.data_ptr(), ws.data_ptr(),
-              ws.numel(), T, out.shape[-1], W.shape[0], _stream(out.device))
+    _call((out, W, bias, latent, ws), "adaln_proj_out_fwd", out.data_ptr(), W.data_ptr(), bias.data_ptr(),
+          latent.data_ptr(), ws.data_ptr(), ws.numel(), T, out.shape[-1], W.shape[0], _stream(out.device))
     return latent
 
 
@@ -428,9 +443,10 @@ def fwd_proj_out(x: torch.Tensor, temb: torch.Tensor, W: torch.Tensor, bias: tor
     mean = torch.empty((B, S), dtype=torch.float32, device=x.device)
     rstd = torch.empty((B, S), dtype=torch.float32, device=x.device)
     ws = _ws(_lib.OP_FWD_PROJ_OUT, B, S, Dx, x.device)
-    _lib.call("adaln_fwd_proj_out", temb.data_ptr(), W.data_ptr(), bias.data_ptr(), x.data_ptr(), Wp.data_ptr(),
-              bp.data_ptr(), emb.data_ptr(), latent.data_ptr(), mean.data_ptr(), rstd.data_ptr(), ws.data_ptr(),
-              ws.numel(), B, S, Dx, Wp.shape[0], float(eps), _stream(x.device))
+    _call((temb, W, bias, x, Wp, bp, emb, latent, mean, rstd, ws), "adaln_fwd_proj_out", temb.data_ptr(),
+          W.data_ptr(), bias.data_ptr(), x.data_ptr(), Wp.data_ptr(), bp.data_ptr(), emb.data_ptr(),
+          latent.data_ptr(), mean.data_ptr(), rstd.data_ptr(), ws.data_ptr(), ws.numel(), B, S, Dx, Wp.shape[0],
+          float(eps), _stream(x.device))
     return latent, emb, mean, rstd
 
 
@@ -450,8 +466,9 @@ def proj_out_bwd(d_lat: torch.Tensor, out: torch.Tensor, W: torch.Tensor):
     db = torch.empty((W.shape[0],), dtype=torch.bfloat16, device=W.device)
     B, S = (out.shape[0], out.shape[1]) if out.dim() == 3 else (1, T)   # the workspace depends on T = B * S
     ws = _ws(_lib.OP_PROJ_OUT_BWD, B, S, out.shape[-1], out.device)
-    _lib.call("adaln_proj_out_bwd", d_lat.data_ptr(), out.data_ptr(), W.data_ptr(), d_out.data_ptr(), dW.data_ptr(),
-              db.data_ptr(), ws.data_ptr(), ws.numel(), T, out.shape[-1], W.shape[0], _stream(out.device))
+    _call((d_lat, out, W, d_out, dW, db, ws), "adaln_proj_out_bwd", d_lat.data_ptr(), out.data_ptr(), W.data_ptr(),
+          d_out.data_ptr(), dW.data_ptr(), db.data_ptr(), ws.data_ptr(), ws.numel(), T, out.shape[-1], W.shape[0],
+          _stream(out.device))
     return d_out, dW, db
 
 

@@ -46,7 +46,9 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_strerror(L):
-    assert L.adaln_abi_version() == 15
+    assert L.adaln_abi_version() == 15 == lib.ABI_VERSION
+    header = open(HEADER).read()
+    assert re.search(r"#define ADALN_ABI_VERSION (\d+)", header).group(1) == "15"
     for code in range(-8, 1):
         assert len(lib.strerror(code)) >= 2
 

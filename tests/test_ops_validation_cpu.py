@@ -86,3 +86,15 @@ def test_proj_out_shapes():
     shape_error(ops.fwd_proj_out, t(2, 7, D), t(2, D), t(N, D), t(N), t(64, D), t(32))
     shape_error(ops.fwd_proj_out, t(2, 7, D), t(2, D), t(N, D), t(N), t(48, D), t(48))
     shape_error(ops.fwd_proj_out, t(2, 7, D), t(1, D), t(N, D), t(N), t(64, D), t(64))
+
+
+def test_call_refuses_tensors_on_two_devices():
+    """Every wrapper hands its tensors to one helper that refuses a call whose
+    tensors sit on different devices (the kernels would otherwise dereference
+    another GPU's addresses), before the library is reached."""
+    from types import SimpleNamespace
+
+    a = SimpleNamespace(device=torch.device("cuda", 0))
+    b = SimpleNamespace(device=torch.device("cuda", 1))
+    with pytest.raises(ValueError, match="one GPU"):
+        ops._call((a, None, b), "adaln_proj_fwd")
