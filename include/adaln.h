@@ -35,7 +35,8 @@
  *   db are batch sums in ascending sample order; trailing all-zero gradient
  *   samples leave them byte-identical.
  * - Unsupported devices (anything but gfx950) fail closed with
- *   ADALN_ERR_DEVICE (pull request 538: other platforms fail closed).
+ *   ADALN_ERR_DEVICE (pull request 538: other platforms fail closed); so does
+ *   a stream that belongs to another device than the current one.
  */
 #ifndef ADALN_H
 #define ADALN_H
@@ -56,7 +57,8 @@ enum adaln_status {
   ADALN_ERR_NULL = -1,       /* a required pointer is NULL                        */
   ADALN_ERR_SHAPE = -2,      /* B, S, H out of range or D/K/N not 3072/3072/6144  */
   ADALN_ERR_ALIGN = -3,      /* a pointer is not 16-byte aligned                  */
-  ADALN_ERR_DEVICE = -4,     /* current device is not gfx950 / no HIP device       */
+  ADALN_ERR_DEVICE = -4,     /* current device not gfx950, no HIP device, or the
+                                stream is on another device                       */
   ADALN_ERR_WORKSPACE = -5,  /* ws_bytes < adaln_workspace_bytes(...)             */
   ADALN_ERR_OVERLAP = -6,    /* an output overlaps an input, output or workspace  */
   ADALN_ERR_LAUNCH = -7,     /* a kernel launch failed (hipGetLastError)          */

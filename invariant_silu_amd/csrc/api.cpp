@@ -69,11 +69,22 @@ bool views_overlap(const void* a, const void* b, int64_t row_bytes, int64_t ld_b
 // bytes a [B, D] view with row stride ld (elements of el bytes) spans
 size_t view_span(int64_t B, int64_t ld, size_t el) { return static_cast<size_t>((B - 1) * ld + kD) * el; }
 
-int check_device() {
+// The current device must be a gfx950, and the caller's stream (when one is
+// given) must belong to it: the kernels run on the stream's device, while the
+// per-device state (the verdicts, the allocation-free entry point's array)
+// is looked up on the current one.
+int check_device(void* stream = nullptr) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
     (void)hipGetLastError();
     return ADALN_ERR_DEVICE;
+  }
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(reinterpret_cast<hipStream_t>(stream), &sdev) != hipSuccess || sdev != dev) {
+      (void)hipGetLastError();
+      return ADALN_ERR_DEVICE;
+    }
   }
   int v = g_arch_verdict[dev].load(std::memory_order_acquire);
   if (v == 0) {
@@ -213,7 +224,8 @@ const char* adaln_strerror(int status) {
     case ADALN_ERR_NULL: return "a required pointer is NULL";
     case ADALN_ERR_SHAPE: return "bad shape (need B, S >= 1 within limits and D = K = 3072, N = 6144)";
     case ADALN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
-    case ADALN_ERR_DEVICE: return "unsupported or missing device (gfx950 required)";
+    case ADALN_ERR_DEVICE:
+      return "unsupported or missing device (gfx950 required), or a stream of another device than the current one";
     case ADALN_ERR_WORKSPACE: return "workspace too small";
     case ADALN_ERR_OVERLAP: return "an output overlaps an input, another output or the workspace";
     case ADALN_ERR_LAUNCH: return "kernel launch failed";
@@ -257,7 +269,7 @@ int adaln_proj_fwd(const adaln_bf16* temb, const adaln_bf16* W, const adaln_bf16
                              {{temb, static_cast<size_t>(B * kD * 2)}, {W, static_cast<size_t>(N * kD * 2)},
                               {bias, static_cast<size_t>(N * 2)}}))
     return rc;
-  if (int rc = check_device()) return rc;
+  if (int rc = check_device(stream)) return rc;
   (void)hipGetLastError();
   return launched(adaln::launch_proj_fwd(temb, W, bias, emb, static_cast<uint16_t*>(ws), B, N,
                                          as_stream(stream)));
@@ -274,7 +286,7 @@ int adaln_norm_mod_fwd(const adaln_bf16* x, const adaln_bf16* emb, adaln_bf16* o
   if (int rc = check_overlap({{out, rows * kD * 2}, {mean, rows * 4}, {rstd, rows * 4}},
                              {{x, rows * kD * 2}, {emb, static_cast<size_t>(B * kN * 2)}}))
     return rc;
-  if (int rc = check_device()) return rc;
+  if (int rc = check_device(stream)) return rc;
   (void)hipGetLastError();
   return launched(adaln::launch_norm_mod_fwd(x, emb, out, mean, rstd, B, S, eps, as_stream(stream)));
 }
@@ -292,7 +304,7 @@ int adaln_norm_mod_bwd_dx(const adaln_bf16* gout, const adaln_bf16* x, const flo
                              {{gout, rows * kD * 2}, {x, rows * kD * 2}, {mean, rows * 4},
                               {rstd, rows * 4}, {emb, static_cast<size_t>(B * kN * 2)}}))
     return rc;
-  if (int rc = check_device()) return rc;
+  if (int rc = check_device(stream)) return rc;
   (void)hipGetLastError();
   return launched(adaln::launch_norm_mod_bwd_dx(gout, x, mean, rstd, emb, dx, B, S, as_stream(stream)));
 }
@@ -310,7 +322,7 @@ int adaln_norm_mod_bwd_tiles(const adaln_bf16* gout, const adaln_bf16* x, const 
   if (int rc = check_overlap({{part, need}}, {{gout, rows * kD * 2}, {x, rows * kD * 2},
                                               {mean, rows * 4}, {rstd, rows * 4}}))
     return rc;
-  if (int rc = check_device()) return rc;
+  if (int rc = check_device(stream)) return rc;
   (void)hipGetLastError();
   return launched(adaln::launch_norm_mod_bwd_tiles(gout, x, mean, rstd, static_cast<float*>(part), B, S,
                                                    as_stream(stream)));
@@ -331,7 +343,7 @@ int adaln_norm_mod_bwd_level0(const adaln_bf16* gout, const adaln_bf16* x, const
                              {{gout, rows * kD * 2}, {x, rows * kD * 2}, {mean, rows * 4}, {rstd, rows * 4},
                               {emb, static_cast<size_t>(B * kN * 2)}}))
     return rc;
-  if (int rc = check_device()) return rc;
+  if (int rc = check_device(stream)) return rc;
   (void)hipGetLastError();
   return launched(adaln::launch_norm_mod_bwd(gout, x, mean, rstd, emb, dx, static_cast<float*>(part), B, S,
                                              as_stream(stream), static_cast<hipEvent_t>(ev_start),
@@ -347,7 +359,7 @@ int token_tree_fold(const void* part, size_t part_bytes, float* out, int64_t B, 
   const size_t bytes = ws_pairs(B, T0 * kTile, H);
   if (part_bytes < bytes) return ADALN_ERR_WORKSPACE;
   if (int rc = check_overlap({{out, static_cast<size_t>(B * H * 4)}}, {{part, bytes}})) return rc;
-  if (int rc = check_device()) return rc;
+  if (int rc = check_device(stream)) return rc;
   (void)hipGetLastError();
   return launched(adaln::launch_tree_fold(static_cast<const float*>(part), out, B, T0, H, as_stream(stream)));
 }
@@ -367,7 +379,7 @@ int adaln_norm_mod_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float*
                              {{gout, rows * kD * 2}, {x, rows * kD * 2}, {mean, rows * 4},
                               {rstd, rows * 4}, {emb, static_cast<size_t>(B * kN * 2)}}))
     return rc;
-  if (int rc = check_device()) return rc;
+  if (int rc = check_device(stream)) return rc;
   (void)hipGetLastError();
   if (int rc = launched(adaln::launch_norm_mod_bwd(gout, x, mean, rstd, emb, dx, static_cast<float*>(ws), B, S,
                                                    as_stream(stream))))
@@ -396,7 +408,7 @@ int adaln_proj_bwd_acc(const float* d_emb, const adaln_bf16* temb, const adaln_b
                                     {temb, static_cast<size_t>(B * kD * 2)},
                                     {W, static_cast<size_t>(N * kD * 2)}}))
     return rc;
-  if (int rc = check_device()) return rc;
+  if (int rc = check_device(stream)) return rc;
   (void)hipGetLastError();
   adaln::AccOut acc;
   acc.dW = dW_f32;
@@ -430,7 +442,7 @@ int token_tree_sum(const float* x, float* out, void* ws, size_t ws_bytes, int64_
   if (int rc = check_overlap({{out, static_cast<size_t>(B * H * 4)}, {ws, need}},
                              {{x, static_cast<size_t>(B * S * H * 4)}}))
     return rc;
-  if (int rc = check_device()) return rc;
+  if (int rc = check_device(stream)) return rc;
   (void)hipGetLastError();
   const int64_t T0 = ceil_div(S, kTile);
   float* part = static_cast<float*>(ws);
@@ -454,7 +466,7 @@ int adaln_fwd(const adaln_bf16* temb, const adaln_bf16* W, const adaln_bf16* bia
                              {{temb, static_cast<size_t>(B * kD * 2)}, {W, static_cast<size_t>(kN * kD * 2)},
                               {bias, static_cast<size_t>(kN * 2)}, {x, rows * kD * 2}}))
     return rc;
-  if (int rc = check_device()) return rc;
+  if (int rc = check_device(stream)) return rc;
   (void)hipGetLastError();
   return launched(adaln::launch_fwd(temb, W, bias, x, emb, out, mean, rstd, B, S, eps, as_stream(stream)));
 }
@@ -481,7 +493,7 @@ int adaln_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float* mean, co
            {emb, static_cast<size_t>(B * kN * 2)}, {temb, static_cast<size_t>(B * kD * 2)},
            {W, static_cast<size_t>(kN * kD * 2)}}))
     return rc;
-  if (int rc = check_device()) return rc;
+  if (int rc = check_device(stream)) return rc;
   (void)hipGetLastError();
   const hipStream_t s = as_stream(stream);
   const int64_t T0 = ceil_div(S, kTile);
@@ -514,7 +526,7 @@ int adaln_fwd_f32(const float* temb, const float* W, const float* bias, const fl
                              {{temb, static_cast<size_t>(B * kD * 4)}, {W, static_cast<size_t>(kN * kD * 4)},
                               {bias, static_cast<size_t>(kN * 4)}, {x, rows * kD * 4}}))
     return rc;
-  if (int rc = check_device()) return rc;
+  if (int rc = check_device(stream)) return rc;
   (void)hipGetLastError();
   const hipStream_t s = as_stream(stream);
   // SiLU into the first B * 3072 elements of `out` (overwritten by the
@@ -544,7 +556,7 @@ int adaln_bwd_f32(const float* gout, const float* x, const float* mean, const fl
            {emb, static_cast<size_t>(B * kN * 4)}, {temb, static_cast<size_t>(B * kD * 4)},
            {W, static_cast<size_t>(kN * kD * 4)}}))
     return rc;
-  if (int rc = check_device()) return rc;
+  if (int rc = check_device(stream)) return rc;
   (void)hipGetLastError();
   const hipStream_t s = as_stream(stream);
   const int64_t T0 = ceil_div(S, kTile);
@@ -577,7 +589,7 @@ int adaln_site_fwd(const adaln_bf16* x, const adaln_bf16* residual, const adaln_
     ins.push_back({gate, vspan});
   }
   if (int rc = check_overlap(outs, ins)) return rc;
-  if (int rc = check_device()) return rc;
+  if (int rc = check_device(stream)) return rc;
   (void)hipGetLastError();
   const adaln::ModView mv{shift, scale, res ? gate : nullptr, mod_ld};
   return launched(adaln::launch_site_fwd(x, residual, mv, res ? h : nullptr, out, mean, rstd, B, S, eps,
@@ -634,7 +646,7 @@ int adaln_site_bwd(const adaln_bf16* g_out, const adaln_bf16* g_h, const adaln_b
     for (size_t j = i + 1; j < dviews.size(); ++j)
       if (views_overlap(dviews[i], dviews[j], kD * 4, dmod_ld * 4, B)) return ADALN_ERR_OVERLAP;
   }
-  if (int rc = check_device()) return rc;
+  if (int rc = check_device(stream)) return rc;
   (void)hipGetLastError();
   const hipStream_t s = as_stream(stream);
   float* part = static_cast<float*>(ws);
@@ -669,7 +681,7 @@ int adaln_proj_out_fwd(const adaln_bf16* out, const adaln_bf16* W, const adaln_b
                              {{out, static_cast<size_t>(T * kD * 2)}, {W, static_cast<size_t>(kProjOutO * kD * 2)},
                               {bias, static_cast<size_t>(kProjOutO * 2)}}))
     return rc;
-  if (int rc = check_device()) return rc;
+  if (int rc = check_device(stream)) return rc;
   (void)hipGetLastError();
   return launched(adaln::launch_proj_out_fwd(out, W, bias, latent, T, as_stream(stream)));
 }
@@ -690,7 +702,7 @@ int adaln_proj_out_bwd(const adaln_bf16* d_lat, const adaln_bf16* out, const ada
           {{d_lat, static_cast<size_t>(T * kProjOutO * 2)}, {out, static_cast<size_t>(T * kD * 2)},
            {W, static_cast<size_t>(kProjOutO * kD * 2)}}))
     return rc;
-  if (int rc = check_device()) return rc;
+  if (int rc = check_device(stream)) return rc;
   (void)hipGetLastError();
   double* part = static_cast<double*>(ws);
   double* part_db = reinterpret_cast<double*>(static_cast<unsigned char*>(ws) + ws_proj_out_db_offset(T));
@@ -716,7 +728,7 @@ int adaln_fwd_proj_out(const adaln_bf16* temb, const adaln_bf16* W, const adaln_
                               {bias, static_cast<size_t>(kN * 2)}, {x, rows * kD * 2},
                               {Wp, static_cast<size_t>(kProjOutO * kD * 2)}, {bp, static_cast<size_t>(kProjOutO * 2)}}))
     return rc;
-  if (int rc = check_device()) return rc;
+  if (int rc = check_device(stream)) return rc;
   (void)hipGetLastError();
   const hipStream_t s = as_stream(stream);
   uint16_t* a = static_cast<uint16_t*>(ws);
@@ -725,7 +737,7 @@ int adaln_fwd_proj_out(const adaln_bf16* temb, const adaln_bf16* W, const adaln_
 }
 
 int adaln_selftest(void) {
-  if (int rc = check_device()) return rc;
+  if (int rc = check_device(nullptr)) return rc;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return ADALN_ERR_DEVICE;
   int v = g_probe_verdict[dev].load(std::memory_order_acquire);
