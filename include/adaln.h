@@ -243,7 +243,7 @@ int adaln_selftest(void);
 /* One-call forward: adaln_proj_fwd then adaln_norm_mod_fwd, same results bit
  * for bit.  B <= 4 with x of at most 32 MiB: the projection's pass over W and
  * the LayerNorm statistics pass over x run side by side (one launch), then the
- * modulation, which finds x in the L2 caches; B <= 4 with a larger x: the
+ * modulation, which re-reads x from the caches; B <= 4 with a larger x: the
  * projection, then statistics and modulation in one pass over x.  B > 4: the
  * SiLU once (into the first B * 3072 elements of `out`, which the modulation
  * overwrites afterwards), the projection, then statistics and modulation in

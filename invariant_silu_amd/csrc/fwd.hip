@@ -26,10 +26,10 @@
 //
 // Kernels: proj_fwd_kernel / proj_mfma_kernel (adaln_proj_fwd),
 // norm_mod_fwd_kernel (statistics and modulation, adaln_norm_mod_fwd), and
-// for the one-call forward adaln_fwd with B <= 4 and x within the L2s
-// (32 MiB): fwd_stage1_kernel (projection blocks and statistics blocks in one
-// grid: two independent HBM streams, W and x) then norm_modulate_kernel, which
-// finds x in L2; with B <= 4 and a larger x, proj_fwd_kernel then
+// for the one-call forward adaln_fwd with B <= 4 and x of at most 32 MiB:
+// fwd_stage1_kernel (projection blocks and statistics blocks in one grid: two
+// independent HBM streams, W and x) then norm_modulate_kernel, which re-reads
+// x from the caches; with B <= 4 and a larger x, proj_fwd_kernel then
 // norm_mod_fwd_kernel (x read once); with B > 4, silu_kernel and
 // proj_mfma_kernel, then norm_mod_fwd_kernel.
 #include "common.hpp"
@@ -48,8 +48,9 @@ constexpr int kProjRowsPerBlock = kWaves * kRows;          // 8
 constexpr int kProjBlocks = kN / kProjRowsPerBlock;        // 768
 constexpr int kMaxNarrowBatch = 4;                         // proj_block up to here
 // x up to this size (bytes) is read twice by the B <= 4 forward, the second
-// time from the L2s (8 XCDs x 4 MB); beyond it one statistics-and-modulation
-// pass after the projection reads it once
+// read served by the caches right after the first; beyond it one
+// statistics-and-modulation pass after the projection reads it once (the
+// faster of the two there, measured)
 constexpr int64_t kStage1MaxXBytes = int64_t(32) << 20;
 static_assert(kN % kProjRowsPerBlock == 0 && kN6 % kProjRowsPerBlock == 0, "rows per block must divide N");
 
@@ -419,8 +420,9 @@ __global__ __launch_bounds__(kThreads) void norm_mod_fwd_kernel(
 // B = NB <= 4: projection blocks [0, 768), then statistics blocks (4 rows
 // each, rows of all samples in order).  The statistics run last on purpose: the block for
 // rows 4i..4i+3 runs on XCD i % 8, and (S a multiple of 4) so does the
-// modulation block for the same rows right after, which then finds x in that
-// XCD's L2 (3.1 MB of x per XCD at S = 4096 against a 4 MB L2).
+// modulation block for the same rows right after, so the second read of x
+// follows the first closely (the byte counters show it served beyond L2, by
+// the memory-side cache).
 template <int NB>
 __global__ __launch_bounds__(kThreads) void fwd_stage1_kernel(
     const uint16_t* __restrict__ temb, const uint16_t* __restrict__ W,
