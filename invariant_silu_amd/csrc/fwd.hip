@@ -578,20 +578,28 @@ hipError_t by_batch(int64_t B, F&& f) {
   }
 }
 
-// a = SiLU(temb) computed once into `a`, then the matrix-core projection:
-// one sample tile per wave up to 16 samples, two beyond
-constexpr int kMfmaSplit = 4;
-template <int kTiles, typename T, int N>
+// a = SiLU(temb) computed once into `a`, then the matrix-core projection.
+// Sample tiles per wave and waves per block by batch (cold timings of the
+// bf16 projection): one tile and 4 waves up to 16 samples; two tiles below
+// 128 (fewer blocks would idle CUs); four tiles from 128 (a converted W
+// operand feeds four chains: B = 256 221 -> 202 us, B = 2048 1572 -> 1475),
+// with 2 waves per block from 1024 samples (B = 2048: 1435 us).  fp32 storage
+// keeps two tiles (its operands take twice the registers).
+template <int kTiles, int kSplit, typename T, int N>
 hipError_t launch_mfma_tiles(const T* a, const T* W, const T* bias, T* emb, int64_t B, hipStream_t s) {
   const int64_t by = (B + 16 * kTiles - 1) / (16 * kTiles);
-  hipLaunchKernelGGL((proj_mfma_kernel<kTiles, kMfmaSplit, T, N>), dim3(N / kMfmaRows, static_cast<unsigned>(by)),
-                     dim3(64 * kMfmaSplit), 0, s, a, W, bias, emb, B);
+  hipLaunchKernelGGL((proj_mfma_kernel<kTiles, kSplit, T, N>), dim3(N / kMfmaRows, static_cast<unsigned>(by)),
+                     dim3(64 * kSplit), 0, s, a, W, bias, emb, B);
   return hipGetLastError();
 }
 template <typename T, int N = kN>
 hipError_t launch_mfma_from_a(const T* a, const T* W, const T* bias, T* emb, int64_t B, hipStream_t s) {
-  return B <= 16 ? launch_mfma_tiles<1, T, N>(a, W, bias, emb, B, s)
-                 : launch_mfma_tiles<2, T, N>(a, W, bias, emb, B, s);
+  if (B <= 16) return launch_mfma_tiles<1, 4, T, N>(a, W, bias, emb, B, s);
+  if constexpr (sizeof(T) == 2) {
+    if (B >= 1024) return launch_mfma_tiles<4, 2, T, N>(a, W, bias, emb, B, s);
+    if (B >= 128) return launch_mfma_tiles<4, 4, T, N>(a, W, bias, emb, B, s);
+  }
+  return launch_mfma_tiles<2, 4, T, N>(a, W, bias, emb, B, s);
 }
 template <int N = kN>
 hipError_t launch_mfma(const uint16_t* temb, uint16_t* a, const uint16_t* W, const uint16_t* bias,
