@@ -381,9 +381,13 @@ int adaln_norm_mod_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float*
     return rc;
   if (int rc = check_device(stream)) return rc;
   (void)hipGetLastError();
+  // one tile per sample: the LayerNorm backward writes the roots itself
+  const bool one_tile = S <= kTile;
   if (int rc = launched(adaln::launch_norm_mod_bwd(gout, x, mean, rstd, emb, dx, static_cast<float*>(ws), B, S,
-                                                   as_stream(stream))))
+                                                   as_stream(stream), nullptr, nullptr,
+                                                   one_tile ? d_emb : nullptr)))
     return rc;
+  if (one_tile) return ADALN_OK;
   return token_tree_fold(ws, need, d_emb, B, ceil_div(S, kTile), kN, stream);
 }
 
@@ -501,9 +505,12 @@ int adaln_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float* mean, co
   uint16_t* a = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + n_norm);
   // dx rows and level-0 tiles in one launch (g and x read once), the fold,
   // then the projection backward: adaln_norm_mod_bwd then adaln_proj_bwd
-  if (int rc = launched(adaln::launch_norm_mod_bwd(gout, x, mean, rstd, emb, dx, part, B, S, s)))
+  // one tile per sample (S <= 32): the LayerNorm backward writes d_emb's roots itself
+  if (int rc = launched(adaln::launch_norm_mod_bwd(gout, x, mean, rstd, emb, dx, part, B, S, s, nullptr, nullptr,
+                                                   T0 == 1 ? d_emb : nullptr)))
     return rc;
-  if (int rc = launched(adaln::launch_tree_fold(part, d_emb, B, T0, kN, s))) return rc;
+  if (T0 > 1)
+    if (int rc = launched(adaln::launch_tree_fold(part, d_emb, B, T0, kN, s))) return rc;
   if (B <= adaln::proj_bwd_fused_max_batch())
     return launched(adaln::launch_proj_bwd_fused(d_emb, temb, W, dW, db, dtemb, reinterpret_cast<double*>(a), B, kN,
                                                  s));
@@ -562,9 +569,12 @@ int adaln_bwd_f32(const float* gout, const float* x, const float* mean, const fl
   const int64_t T0 = ceil_div(S, kTile);
   float* part = static_cast<float*>(ws);
   float* a = reinterpret_cast<float*>(static_cast<char*>(ws) + n_norm);
-  if (int rc = launched(adaln::launch_norm_mod_bwd_f32(gout, x, mean, rstd, emb, dx, part, B, S, s)))
+  // one tile per sample (S <= 32): the LayerNorm backward writes d_emb's roots itself
+  if (int rc = launched(adaln::launch_norm_mod_bwd_f32(gout, x, mean, rstd, emb, dx, part, B, S, s,
+                                                       T0 == 1 ? d_emb : nullptr)))
     return rc;
-  if (int rc = launched(adaln::launch_tree_fold(part, d_emb, B, T0, kN, s))) return rc;
+  if (T0 > 1)
+    if (int rc = launched(adaln::launch_tree_fold(part, d_emb, B, T0, kN, s))) return rc;
   double* sub = reinterpret_cast<double*>(reinterpret_cast<char*>(a) + pad256(static_cast<size_t>(B * kD * 4)));
   return launched(adaln::launch_proj_bwd_f32(d_emb, temb, W, a, dW, db, dtemb, sub, B, s));
 }

@@ -270,12 +270,14 @@ __device__ __forceinline__ void row_pass_f32(const float* __restrict__ g, const 
 
 // Level-0 pairs of one 32-token tile for 512 columns (2 per thread); a full
 // tile uses buffer loads (column in a VGPR, row in an SGPR), the last ragged
-// tile of a sample a guarded loop.
+// tile of a sample a guarded loop.  With one tile per sample (S <= 32) and
+// `root` given, s + c (the fold's one add at that size) goes straight to
+// root = d_emb [B, 2D] instead of the pair.
 template <bool kFull>
 __device__ __forceinline__ void col_tile_f32(const float* __restrict__ g, const float* __restrict__ x,
                                              const float* __restrict__ mean, const float* __restrict__ rstd,
                                              float* __restrict__ part, int64_t b, int64_t tile, int cb,
-                                             int64_t S, int64_t T0, int rows) {
+                                             int64_t S, int64_t T0, int rows, float* __restrict__ root) {
   const int col = cb * kColBlockCols + 2 * threadIdx.x;
   const int64_t row0 = b * S + tile * kTile;
   float2 gw[kTile], xw[kTile];
@@ -314,6 +316,11 @@ __device__ __forceinline__ void col_tile_f32(const float* __restrict__ g, const 
       neumaier_add(sn1, cn1, g1 * n1);
     }
   }
+  if (root != nullptr) {
+    st8(root + b * kN + col, sn0 + cn0, sn1 + cn1);
+    st8(root + b * kN + kD + col, sg0 + cg0, sg1 + cg1);
+    return;
+  }
   constexpr int64_t kGroups = kN / kPairGroup;
   const int64_t i_scale = pair_index(b, kGroups, T0, tile, col);
   const int64_t i_shift = pair_index(b, kGroups, T0, tile, col + kD);
@@ -330,7 +337,7 @@ __device__ __forceinline__ void col_tile_f32(const float* __restrict__ g, const 
 __global__ __launch_bounds__(kThreads) void norm_mod_bwd_f32_kernel(
     const float* __restrict__ g, const float* __restrict__ x, const float* __restrict__ mean,
     const float* __restrict__ rstd, const float* __restrict__ emb, float* __restrict__ dx,
-    float* __restrict__ part, int64_t B, int64_t S, int64_t T0) {
+    float* __restrict__ part, int64_t B, int64_t S, int64_t T0, float* __restrict__ root) {
   __shared__ float4 m_lds[kD / 4];
   const int64_t L = blockIdx.x;
   const int64_t j = L >> 3;
@@ -345,8 +352,8 @@ __global__ __launch_bounds__(kThreads) void norm_mod_bwd_f32_kernel(
   } else {
     const int cb = role - kRowBlocks;
     const int64_t left = S - tile * kTile;
-    if (left >= kTile) col_tile_f32<true>(g, x, mean, rstd, part, b, tile, cb, S, T0, kTile);
-    else col_tile_f32<false>(g, x, mean, rstd, part, b, tile, cb, S, T0, static_cast<int>(left));
+    if (left >= kTile) col_tile_f32<true>(g, x, mean, rstd, part, b, tile, cb, S, T0, kTile, root);
+    else col_tile_f32<false>(g, x, mean, rstd, part, b, tile, cb, S, T0, static_cast<int>(left), root);
   }
 }
 
@@ -381,13 +388,13 @@ hipError_t launch_norm_mod_fwd_f32(const float* x, const float* emb, float* out,
 
 hipError_t launch_norm_mod_bwd_f32(const float* g, const float* x, const float* mean, const float* rstd,
                                    const float* emb, float* dx, float* part, int64_t B, int64_t S,
-                                   hipStream_t s) {
+                                   hipStream_t s, float* root) {
   static_assert(kD % kColBlockCols == 0, "column blocks must tile D");
   const int64_t T0 = (S + kTile - 1) / kTile;
   const int64_t groups = (B * T0 + 7) / 8;
   const dim3 grid(static_cast<unsigned>(groups * 8 * kBlocksPerTile));
   hipLaunchKernelGGL(norm_mod_bwd_f32_kernel, grid, dim3(kThreads), 0, s, g, x, mean, rstd, emb, dx, part, B, S,
-                     T0);
+                     T0, root);
   return hipGetLastError();
 }
 

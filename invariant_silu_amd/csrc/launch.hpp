@@ -25,7 +25,7 @@ hipError_t launch_norm_mod_fwd(const uint16_t* x, const uint16_t* emb, uint16_t*
 hipError_t launch_norm_mod_bwd(const uint16_t* g, const uint16_t* x, const float* mean,
                                const float* rstd, const uint16_t* emb, uint16_t* dx, float* part,
                                int64_t B, int64_t S, hipStream_t s, hipEvent_t ev_start = nullptr,
-                               hipEvent_t ev_stop = nullptr);
+                               hipEvent_t ev_stop = nullptr, float* root = nullptr);
 hipError_t launch_norm_mod_bwd_dx(const uint16_t* g, const uint16_t* x, const float* mean,
                                   const float* rstd, const uint16_t* emb, uint16_t* dx, int64_t B,
                                   int64_t S, hipStream_t s);
@@ -101,7 +101,7 @@ hipError_t launch_norm_mod_fwd_f32(const float* x, const float* emb, float* out,
                                    int64_t B, int64_t S, float eps, hipStream_t s);
 hipError_t launch_norm_mod_bwd_f32(const float* g, const float* x, const float* mean, const float* rstd,
                                    const float* emb, float* dx, float* part, int64_t B, int64_t S,
-                                   hipStream_t s);
+                                   hipStream_t s, float* root = nullptr);
 hipError_t launch_proj_bwd_f32(const float* d_emb, const float* temb, const float* W, float* a, float* dW,
                                float* db, float* dtemb, double* sub, int64_t B, hipStream_t s);   // sub: B <= 4
 hipError_t launch_selftest_probe(const float* in, float* out, uint32_t* bits, int n,

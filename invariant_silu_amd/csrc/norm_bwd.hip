@@ -10,7 +10,8 @@
 //   (fp64 lane partials, chunks and columns in order, then wave_sum_f64)
 // and the level-0 pairs of the token tree, per (b, 32-token tile, column):
 // Neumaier (s, c) of g (-> d_shift) and of g * n (-> d_scale), tokens in
-// ascending order.  Levels >= 1 are folded by tree_fold_kernel.
+// ascending order.  Levels >= 1 are folded by tree_fold_kernel; with one tile
+// per sample (S <= 32) the kernel writes the roots, s + c, to d_emb itself.
 //
 // norm_mod_bwd_kernel<role>: dx rows and/or level-0 tiles of a 32-token tile;
 // the 14 blocks of a tile (8 row blocks, 6 tile blocks) run on one XCD, so
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void norm_mod_bwd_kernel(
     const uint16_t* __restrict__ g, const uint16_t* __restrict__ x,
     const float* __restrict__ mean, const float* __restrict__ rstd,
     const uint16_t* __restrict__ emb, uint16_t* __restrict__ dx,
-    float* __restrict__ part, int64_t B, int64_t S, int64_t T0) {
+    float* __restrict__ part, int64_t B, int64_t S, int64_t T0, float* __restrict__ root) {
   constexpr int bpt = kRole == kBoth ? kBlocksPerTile : (kRole == kRowsOnly ? kRowBlocks : kColBlocks);
   __shared__ float4 m_lds[kD / 4];   // row blocks: m = bf16(1 + scale)
   const int64_t L = blockIdx.x;
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void norm_mod_bwd_kernel(
     row_pass(g, x, mean, rstd, emb, dx, b, s, S, m_lds);
   } else {
     const int cb = kRole == kColsOnly ? role : role - kRowBlocks;
-    col_pass(g, x, mean, rstd, part, b, tile, cb, S, T0);
+    col_pass(g, x, mean, rstd, part, b, tile, cb, S, T0, kN / kPairGroup, 0, kD, root, kN);
   }
 }
 
@@ -123,7 +124,8 @@ __global__ __launch_bounds__(kThreads) void norm_mod_bwd_kernel(
 template <int kRole>
 hipError_t launch_role(const uint16_t* g, const uint16_t* x, const float* mean, const float* rstd,
                        const uint16_t* emb, uint16_t* dx, float* part, int64_t B,
-                       int64_t S, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
+                       int64_t S, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr,
+                       float* root = nullptr) {
   constexpr int bpt = kRole == kBoth ? kBlocksPerTile : (kRole == kRowsOnly ? kRowBlocks : kColBlocks);
   const int64_t T0 = (S + kTile - 1) / kTile;
   const int64_t groups = (B * T0 + 7) / 8;
@@ -131,7 +133,7 @@ hipError_t launch_role(const uint16_t* g, const uint16_t* x, const float* mean, 
   // events, when given, are recorded by the dispatch itself: no packet of
   // their own in the stream
   hipExtLaunchKernelGGL(norm_mod_bwd_kernel<kRole>, grid, dim3(kThreads), 0, s, e0, e1, 0, g, x, mean, rstd, emb, dx,
-                        part, B, S, T0);
+                        part, B, S, T0, root);
   return hipGetLastError();
 }
 
@@ -140,9 +142,10 @@ hipError_t launch_role(const uint16_t* g, const uint16_t* x, const float* mean, 
 
 hipError_t launch_norm_mod_bwd(const uint16_t* g, const uint16_t* x, const float* mean,
                                const float* rstd, const uint16_t* emb, uint16_t* dx, float* part,
-                               int64_t B, int64_t S, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+                               int64_t B, int64_t S, hipStream_t s, hipEvent_t e0, hipEvent_t e1,
+                               float* root) {
   static_assert(kD % kColBlockCols == 0, "column blocks must tile D");
-  return launch_role<kBoth>(g, x, mean, rstd, emb, dx, part, B, S, s, e0, e1);
+  return launch_role<kBoth>(g, x, mean, rstd, emb, dx, part, B, S, s, e0, e1, root);
 }
 
 hipError_t launch_norm_mod_bwd_dx(const uint16_t* g, const uint16_t* x, const float* mean,
