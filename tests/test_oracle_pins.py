@@ -242,6 +242,27 @@ def test_layernorm_closed_forms():
     assert np.max(np.abs(e1["n"] - e2["n"])) < 1e-5
 
 
+def test_constant_rows_closed_form():
+    """P-5b: a row of one repeated value v has mean v, variance 0, rstd =
+    fp32(1 / sqrt(fp32(1e-6))) and n = 0, so out is the shift bit for bit; and
+    its dx is rstd * (g m - mean(g m)) (beta drops out with n = 0), rounded
+    once."""
+    inp = _small_inputs(1, 5, seed=12)
+    vals = np.array([0.0, 0.75, -3.0, 1.0e4, 2.0 ** -20], np.float32)
+    inp["x"] = f32_to_bf16_bits(np.repeat(vals, D).reshape(1, 5, D))
+    f = adaln.forward(inp)
+    b = adaln.backward(inp, f)
+    v = bits_to_f32(inp["x"])[0, :, 0]
+    assert np.array_equal(f["mean"][0], v)
+    rs = np.float32(1.0) / np.sqrt(np.float32(1e-6), dtype=np.float32)
+    assert np.all(f["rstd"][0] == rs)
+    assert np.array_equal(f["out_bits"], np.broadcast_to(f["emb_bits"][:, D:][:, None, :], f["out_bits"].shape))
+    gm = bits_to_f32(inp["g"])[0].astype(np.float64) * f["m"][0].astype(np.float64)
+    want = rs.astype(np.float64) * (gm - gm.mean(-1, keepdims=True))
+    d = bf16_ulp_diff(b["dx_bits"][0], fpmath.f64_to_bf16_bits(want))
+    assert d.max() <= 1
+
+
 def test_identity_modulation_is_textbook_layernorm():
     """P-6: W = 0, b = 0 gives out = bf16(LayerNorm(x)); checked against a
     float64 two-pass LayerNorm; and scale = -1 gives out = shift exactly."""
