@@ -313,7 +313,7 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.site, args.workload,
-                           reps=1 if args.site in ("mod6", "proj_out", "serve") else 4)
+                           reps=1 if args.site in ("mod6", "proj_out", "serve") else 10)
 
     import ctypes
 
