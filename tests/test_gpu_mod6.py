@@ -55,10 +55,11 @@ def test_mod6_parity(gpu_lib, B):
         assert r["n_fail"] == 0, k
 
 
-@pytest.mark.parametrize("B", [9, 33])
+@pytest.mark.parametrize("B", [9, 33, 130])
 def test_mod6_singleton_vs_batch(gpu_lib, B):
     """emb and dtemb rows are the same bytes alone (vector units) and in the
-    batch (matrix cores, one or two sample tiles)."""
+    batch (matrix cores: one, two or four sample tiles per wave in the
+    projection)."""
     print(f"[mod6] invariance B={B}", flush=True)
     d = _dev(make_mod6_inputs(B, seed=95))
     full = _run(d)
