@@ -661,9 +661,14 @@ int adaln_site_bwd(const adaln_bf16* g_out, const adaln_bf16* g_h, const adaln_b
   const hipStream_t s = as_stream(stream);
   float* part = static_cast<float*>(ws);
   const adaln::ModView mv{nullptr, scale, res ? gate : nullptr, mod_ld};
+  // one tile per sample (S <= 32): the tile blocks write the roots into the views, no fold
+  const bool one_tile = S <= kTile;
   if (int rc = launched(adaln::launch_site_bwd(g_out, g_h, x, res ? h : x, mean, rstd, mv, res ? d_residual : nullptr,
-                                               dx, part, B, S, s)))
+                                               dx, part, B, S, s, one_tile ? d_shift : nullptr,
+                                               one_tile ? d_scale : nullptr, (one_tile && res) ? d_gate : nullptr,
+                                               dmod_ld)))
     return rc;
+  if (one_tile) return ADALN_OK;
   return launched(adaln::launch_tree_fold_views(part, d_shift, d_scale, res ? d_gate : nullptr, dmod_ld, B,
                                                 ceil_div(S, kTile), nseg, s));
 }

@@ -76,7 +76,8 @@ hipError_t launch_site_fwd(const uint16_t* x, const uint16_t* residual, ModView 
 // scale; the LayerNorm input is x, h and d_residual unused)
 hipError_t launch_site_bwd(const uint16_t* g_out, const uint16_t* g_h, const uint16_t* x, const uint16_t* h,
                            const float* mean, const float* rstd, ModView mv, uint16_t* d_residual, uint16_t* dx,
-                           float* part, int64_t B, int64_t S, hipStream_t s);
+                           float* part, int64_t B, int64_t S, hipStream_t s, float* r_shift = nullptr,
+                           float* r_scale = nullptr, float* r_gate = nullptr, int64_t r_ld = 0);
 // proj_out (3072 -> 64 per token) on the fp64 matrix cores.  Backward part:
 // proj_out_chunks(T) x 64 x 3072 fp64 (the dWp chunk partials), part_db:
 // proj_out_chunks(T) x 64 fp64

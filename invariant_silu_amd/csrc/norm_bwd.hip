@@ -116,7 +116,8 @@ __global__ __launch_bounds__(kThreads) void norm_mod_bwd_kernel(
     row_pass(g, x, mean, rstd, emb, dx, b, s, S, m_lds);
   } else {
     const int cb = kRole == kColsOnly ? role : role - kRowBlocks;
-    col_pass(g, x, mean, rstd, part, b, tile, cb, S, T0, kN / kPairGroup, 0, kD, root, kN);
+    col_pass(g, x, mean, rstd, part, b, tile, cb, S, T0, kN / kPairGroup, 0, kD, root, root ? root + kD : nullptr,
+             kN);
   }
 }
 

@@ -29,14 +29,16 @@ constexpr int kBlocksPerTile = kRowBlocks + kColBlocks;   // 14
 // guarded form.
 // Pairs go to columns scale_col0 + col (g * n) and shift_col0 + col (g) of a
 // pair buffer of `groups` 64-column groups.  A sample of one tile (S <= 32)
-// has its root here already: with `root` given, s + c (the fold's one add at
-// that size) goes to root[b * root_ld + column] instead of the pair.
+// has its roots here already: with root_scale / root_shift given, s + c (the
+// fold's one add at that size) goes to root_scale[b * root_ld + col] and
+// root_shift[b * root_ld + col] instead of the pairs.
 template <bool kFull>
 __device__ __forceinline__ void col_tile(const uint16_t* __restrict__ g, const uint16_t* __restrict__ x,
                                          const float* __restrict__ mean, const float* __restrict__ rstd,
                                          float* __restrict__ part, int64_t b, int64_t tile, int cb,
                                          int64_t S, int64_t T0, int rows, int64_t groups, int scale_col0,
-                                         int shift_col0, float* __restrict__ root, int64_t root_ld) {
+                                         int shift_col0, float* __restrict__ root_scale,
+                                         float* __restrict__ root_shift, int64_t root_ld) {
   const int col = cb * kColBlockCols + 2 * threadIdx.x;
   const int64_t row0 = b * S + tile * kTile;
   uint32_t gw[kTile], xw[kTile];
@@ -73,9 +75,9 @@ __device__ __forceinline__ void col_tile(const uint16_t* __restrict__ g, const u
       neumaier_add(sn1, cn1, g1 * n1);
     }
   }
-  if (root != nullptr) {
-    st8(root + b * root_ld + scale_col0 + col, sn0 + cn0, sn1 + cn1);
-    st8(root + b * root_ld + shift_col0 + col, sg0 + cg0, sg1 + cg1);
+  if (root_scale != nullptr) {
+    st8(root_scale + b * root_ld + col, sn0 + cn0, sn1 + cn1);
+    st8(root_shift + b * root_ld + col, sg0 + cg0, sg1 + cg1);
     return;
   }
   const int64_t i_scale = pair_index(b, groups, T0, tile, scale_col0 + col);
@@ -91,15 +93,15 @@ __device__ __forceinline__ void col_pass(const uint16_t* __restrict__ g, const u
                                          const float* __restrict__ mean, const float* __restrict__ rstd,
                                          float* __restrict__ part, int64_t b, int64_t tile, int cb,
                                          int64_t S, int64_t T0, int64_t groups = kN / kPairGroup,
-                                         int scale_col0 = 0, int shift_col0 = kD, float* root = nullptr,
-                                         int64_t root_ld = 0) {
+                                         int scale_col0 = 0, int shift_col0 = kD, float* root_scale = nullptr,
+                                         float* root_shift = nullptr, int64_t root_ld = 0) {
   const int64_t left = S - tile * kTile;
   if (left >= kTile)
-    col_tile<true>(g, x, mean, rstd, part, b, tile, cb, S, T0, kTile, groups, scale_col0, shift_col0, root,
-                   root_ld);
+    col_tile<true>(g, x, mean, rstd, part, b, tile, cb, S, T0, kTile, groups, scale_col0, shift_col0, root_scale,
+                   root_shift, root_ld);
   else
     col_tile<false>(g, x, mean, rstd, part, b, tile, cb, S, T0, static_cast<int>(left), groups, scale_col0,
-                    shift_col0, root, root_ld);
+                    shift_col0, root_scale, root_shift, root_ld);
 }
 
 }  // namespace

@@ -117,13 +117,15 @@ __device__ __forceinline__ void site_row_pass(
 }
 
 // grid as norm_mod_bwd_kernel<kBoth>: row blocks (dh, dx) and tile blocks
-// (d_shift, d_scale pairs) of one 32-token tile on one XCD
+// (d_shift, d_scale pairs) of one 32-token tile on one XCD; with one tile per
+// sample (S <= 32) the tile blocks write the roots into the gradient views
+// (r_shift, r_scale, row stride r_ld) instead of pairs
 template <bool kRes>
 __global__ __launch_bounds__(kThreads) void site_bwd_kernel(
     const uint16_t* __restrict__ g, const uint16_t* __restrict__ gh, const uint16_t* __restrict__ h,
     const float* __restrict__ mean, const float* __restrict__ rstd, const ModView mv,
     uint16_t* __restrict__ dres, uint16_t* __restrict__ dxo, float* __restrict__ part, int64_t B, int64_t S,
-    int64_t T0) {
+    int64_t T0, float* __restrict__ r_shift, float* __restrict__ r_scale, int64_t r_ld) {
   __shared__ float4 m_lds[kD / 4];
   __shared__ float4 gate_lds[kD / 4];
   const int64_t L = blockIdx.x;
@@ -137,15 +139,17 @@ __global__ __launch_bounds__(kThreads) void site_bwd_kernel(
     const int64_t s = tile * kTile + role * 4 + (threadIdx.x >> 6);
     site_row_pass<kRes>(g, h, mean, rstd, mv, gh, dres, dxo, b, s, S, m_lds, gate_lds);
   } else {
-    col_pass(g, h, mean, rstd, part, b, tile, role - kRowBlocks, S, T0, kRes ? kModGroups : kSiteGroups, kD, 0);
+    col_pass(g, h, mean, rstd, part, b, tile, role - kRowBlocks, S, T0, kRes ? kModGroups : kSiteGroups, kD, 0,
+             r_scale, r_shift, r_ld);
   }
 }
 
 // level-0 pairs of d_gate (dh * x) for one 32-token tile and 512 columns
+// (with r_gate given, one tile per sample: the roots into that view)
 template <bool kFull>
 __device__ __forceinline__ void gate_tile(const uint16_t* __restrict__ dh, const uint16_t* __restrict__ x,
                                           float* __restrict__ part, int64_t b, int64_t tile, int cb, int64_t S,
-                                          int64_t T0, int rows) {
+                                          int64_t T0, int rows, float* __restrict__ r_gate, int64_t r_ld) {
   const int col = cb * kColBlockCols + 2 * threadIdx.x;
   const int64_t row0 = b * S + tile * kTile;
   uint32_t dw[kTile], xw[kTile];
@@ -175,6 +179,10 @@ __device__ __forceinline__ void gate_tile(const uint16_t* __restrict__ dh, const
       neumaier_add(s1, c1, bf_hi(dw[r]) * bf_hi(xw[r]));
     }
   }
+  if (r_gate != nullptr) {
+    st8(r_gate + b * r_ld + col, s0 + c0, s1 + c1);
+    return;
+  }
   const int64_t i = pair_index(b, kModGroups, T0, tile, 2 * kD + col);
   st8(part + i, s0, s1);
   st8(part + i + kPairGroup, c0, c1);
@@ -183,14 +191,15 @@ __device__ __forceinline__ void gate_tile(const uint16_t* __restrict__ dh, const
 // grid: B * T0 * 6 blocks; block (G, cb) = tile G, 512-column block cb
 __global__ __launch_bounds__(kThreads) void gate_tile_kernel(const uint16_t* __restrict__ dh,
                                                              const uint16_t* __restrict__ x,
-                                                             float* __restrict__ part, int64_t S, int64_t T0) {
+                                                             float* __restrict__ part, int64_t S, int64_t T0,
+                                                             float* __restrict__ r_gate, int64_t r_ld) {
   const int64_t G = blockIdx.x / kColBlocks;
   const int cb = static_cast<int>(blockIdx.x % kColBlocks);
   const int64_t b = G / T0;
   const int64_t tile = G % T0;
   const int64_t left = S - tile * kTile;
-  if (left >= kTile) gate_tile<true>(dh, x, part, b, tile, cb, S, T0, kTile);
-  else gate_tile<false>(dh, x, part, b, tile, cb, S, T0, static_cast<int>(left));
+  if (left >= kTile) gate_tile<true>(dh, x, part, b, tile, cb, S, T0, kTile, r_gate, r_ld);
+  else gate_tile<false>(dh, x, part, b, tile, cb, S, T0, static_cast<int>(left), r_gate, r_ld);
 }
 
 }  // namespace
@@ -199,26 +208,30 @@ namespace {
 template <bool kRes>
 void launch_site_bwd_kernel(dim3 grid, hipStream_t s, const uint16_t* g_out, const uint16_t* g_h,
                             const uint16_t* h, const float* mean, const float* rstd, const ModView& mv,
-                            uint16_t* d_residual, uint16_t* dx, float* part, int64_t B, int64_t S, int64_t T0) {
+                            uint16_t* d_residual, uint16_t* dx, float* part, int64_t B, int64_t S, int64_t T0,
+                            float* r_shift, float* r_scale, int64_t r_ld) {
   hipLaunchKernelGGL(site_bwd_kernel<kRes>, grid, dim3(kThreads), 0, s, g_out, g_h, h, mean, rstd, mv, d_residual,
-                     dx, part, B, S, T0);
+                     dx, part, B, S, T0, r_shift, r_scale, r_ld);
 }
 }  // namespace
 
 hipError_t launch_site_bwd(const uint16_t* g_out, const uint16_t* g_h, const uint16_t* x, const uint16_t* h,
                            const float* mean, const float* rstd, ModView mv, uint16_t* d_residual, uint16_t* dx,
-                           float* part, int64_t B, int64_t S, hipStream_t s) {
+                           float* part, int64_t B, int64_t S, hipStream_t s, float* r_shift, float* r_scale,
+                           float* r_gate, int64_t r_ld) {
   const int64_t T0 = (S + kTile - 1) / kTile;
   const int64_t groups = (B * T0 + 7) / 8;
   const dim3 grid(static_cast<unsigned>(groups * 8 * kBlocksPerTile));
   if (!g_h) {   // plain form: the LayerNorm input is x
-    launch_site_bwd_kernel<false>(grid, s, g_out, nullptr, x, mean, rstd, mv, nullptr, dx, part, B, S, T0);
+    launch_site_bwd_kernel<false>(grid, s, g_out, nullptr, x, mean, rstd, mv, nullptr, dx, part, B, S, T0, r_shift,
+                                  r_scale, r_ld);
     return hipGetLastError();
   }
-  launch_site_bwd_kernel<true>(grid, s, g_out, g_h, h, mean, rstd, mv, d_residual, dx, part, B, S, T0);
+  launch_site_bwd_kernel<true>(grid, s, g_out, g_h, h, mean, rstd, mv, d_residual, dx, part, B, S, T0, r_shift,
+                               r_scale, r_ld);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   hipLaunchKernelGGL(gate_tile_kernel, dim3(static_cast<unsigned>(B * T0 * kColBlocks)), dim3(kThreads), 0, s,
-                     d_residual, x, part, S, T0);
+                     d_residual, x, part, S, T0, r_gate, r_ld);
   return hipGetLastError();
 }
 
