@@ -38,6 +38,9 @@ WORKLOADS = {
     # the pages' large conditioning batch: 2048 samples of 3 tokens
     "batch2048_s3": dict(B=2048, S=3, outlier_frac=0.0),
 }
+# one sample of the headline's distribution at other sequence lengths
+# (S = 1024 ... 65536: 512 x 512 to 4096 x 4096 images at 16 pixels per token)
+WORKLOADS.update({f"seq_b1_s{S}": dict(B=1, S=S, outlier_frac=0.01) for S in (1024, 2048, 8192, 16384, 32768, 65536)})
 SWEEP_S = (32, 33, 6032, 6889)
 SWEEP_B = (1, 2, 4)
 
