@@ -50,7 +50,7 @@ extern "C" {
 
 typedef uint16_t adaln_bf16;
 
-#define ADALN_ABI_VERSION 15
+#define ADALN_ABI_VERSION 16
 
 enum adaln_status {
   ADALN_OK = 0,
@@ -202,7 +202,9 @@ int adaln_norm_mod_bwd_level0(const adaln_bf16* gout, const adaln_bf16* x, const
  *   cores: the same bits either way.
  *   ws: adaln_workspace_bytes(ADALN_OP_PROJ_BWD, B, 1, K) bytes (B <= 8: the
  *   sums of leaves 4g .. 4g + 3 for g = 0 .. 31, added pairwise by a second
- *   launch; B > 8: a). */
+ *   launch; B > 8: a, then for B <= 64 the subtrees of aligned runs of the
+ *   128 leaves -- 8 runs of 16 for B <= 16, 4 runs of 32 up to 64 -- added
+ *   pairwise by a second launch: the same tree, spread over more blocks). */
 int adaln_proj_bwd(const float* d_emb, const adaln_bf16* temb, const adaln_bf16* W,
                    adaln_bf16* dW, adaln_bf16* db, adaln_bf16* dtemb, void* ws, size_t ws_bytes,
                    int64_t B, int64_t K, int64_t N, void* stream);

@@ -113,9 +113,14 @@ size_t ws_proj_fwd(int64_t B) {
 }
 size_t ws_proj_bwd(int64_t B) {
   // B <= 8: the fp64 da subtrees (32 per sample and column) between the two
-  // launches; B > 8: the SiLU activations
-  return pad256(B <= adaln::proj_bwd_fused_max_batch() ? adaln::proj_bwd_fused_sub_bytes(B)
-                                                       : static_cast<size_t>(B * kD * 2));
+  // launches; B > 8: the SiLU activations, then (B <= 64) the fp64 subtrees
+  // of the da leaf runs
+  if (B <= adaln::proj_bwd_fused_max_batch()) return pad256(adaln::proj_bwd_fused_sub_bytes(B));
+  return pad256(static_cast<size_t>(B * kD * 2)) + pad256(adaln::proj_bwd_da_parts_bytes(B));
+}
+// the da run subtrees: after the SiLU activations a (bf16, B > 8)
+double* da_parts(void* a, int64_t B) {
+  return reinterpret_cast<double*>(static_cast<char*>(a) + pad256(static_cast<size_t>(B * kD * 2)));
 }
 size_t ws_tree(int64_t B, int64_t S, int64_t H) { return ws_pairs(B, S, H); }
 constexpr int64_t kMaxTokens = int64_t{65535} * 512;   // proj_out: token indices (and a token's sample) fit 32 bits
@@ -132,9 +137,11 @@ size_t ws_proj_out(int64_t T) {
 }
 size_t ws_fwd_proj_out(int64_t B, int64_t S) { return ws_proj_fwd(B) + ws_proj_out_fwd(B * S); }
 size_t ws_proj_bwd_f32(int64_t B) {
-  // SiLU activations (fp32 storage); B <= 4: then the fp64 da subtrees
+  // SiLU activations (fp32 storage), then the fp64 da subtrees: B <= 4, the
+  // leaf groups'; B > 4, the leaf runs' (none beyond B = 64)
   return pad256(static_cast<size_t>(B * kD * 4)) +
-         (B <= adaln::proj_bwd_f32_max_batch() ? pad256(adaln::proj_bwd_fused_sub_bytes(B)) : 0);
+         pad256(B <= adaln::proj_bwd_f32_max_batch() ? adaln::proj_bwd_fused_sub_bytes(B)
+                                                      : adaln::proj_bwd_da_parts_bytes(B));
 }
 bool batch_ok(int64_t B) { return B >= 1 && B <= kMaxB; }
 bool seq_ok(int64_t S) { return S >= 1 && S <= kMaxS; }
@@ -426,7 +433,7 @@ int adaln_proj_bwd_acc(const float* d_emb, const adaln_bf16* temb, const adaln_b
   }
   if (int rc = launched(adaln::launch_silu(temb, a, B * kD, s))) return rc;
   if (int rc = launched(adaln::launch_proj_bwd_dw(d_emb, a, dW, db, B, N, s, acc))) return rc;
-  return launched(adaln::launch_proj_bwd_da(d_emb, W, temb, dtemb, B, N, s, acc));
+  return launched(adaln::launch_proj_bwd_da(d_emb, W, temb, dtemb, da_parts(a, B), B, N, s, acc));
 }
 
 int adaln_proj_bwd(const float* d_emb, const adaln_bf16* temb, const adaln_bf16* W,
@@ -516,7 +523,7 @@ int adaln_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float* mean, co
                                                  s));
   if (int rc = launched(adaln::launch_silu(temb, a, B * kD, s))) return rc;
   if (int rc = launched(adaln::launch_proj_bwd_dw(d_emb, a, dW, db, B, kN, s))) return rc;
-  return launched(adaln::launch_proj_bwd_da(d_emb, W, temb, dtemb, B, kN, s));
+  return launched(adaln::launch_proj_bwd_da(d_emb, W, temb, dtemb, da_parts(a, B), B, kN, s));
 }
 
 int adaln_fwd_f32(const float* temb, const float* W, const float* bias, const float* x, float* emb, float* out,

@@ -44,6 +44,8 @@ int proj_bwd_fused_max_batch();
 int proj_bwd_f32_max_batch();
 // bytes of fp64 da subtrees the B <= 4 path keeps between its two launches
 size_t proj_bwd_fused_sub_bytes(int64_t B);
+// B > 8 (bf16) or B > 4 (fp32 storage): the da run subtrees (0: none)
+size_t proj_bwd_da_parts_bytes(int64_t B);
 // Optional fp32 copies of the projection backward's bf16 outputs (the values
 // rounded to bf16); any member may be NULL.
 struct AccOut {
@@ -57,7 +59,8 @@ hipError_t launch_proj_bwd_fused(const float* d_emb, const uint16_t* temb, const
 hipError_t launch_proj_bwd_dw(const float* d_emb, const uint16_t* a, uint16_t* dW, uint16_t* db,
                               int64_t B, int64_t N, hipStream_t s, const AccOut& acc = AccOut{});
 hipError_t launch_proj_bwd_da(const float* d_emb, const uint16_t* W, const uint16_t* temb,
-                              uint16_t* dtemb, int64_t B, int64_t N, hipStream_t s, const AccOut& acc = AccOut{});
+                              uint16_t* dtemb, double* parts, int64_t B, int64_t N, hipStream_t s,
+                              const AccOut& acc = AccOut{});
 // A block's norm site.  Its modulation as three [B, D] bf16 views with one
 // row stride ld (elements, a multiple of 8); gate is used only with the
 // residual add.
@@ -104,7 +107,9 @@ hipError_t launch_norm_mod_bwd_f32(const float* g, const float* x, const float* 
                                    const float* emb, float* dx, float* part, int64_t B, int64_t S,
                                    hipStream_t s, float* root = nullptr);
 hipError_t launch_proj_bwd_f32(const float* d_emb, const float* temb, const float* W, float* a, float* dW,
-                               float* db, float* dtemb, double* sub, int64_t B, hipStream_t s);   // sub: B <= 4
+                               float* db, float* dtemb, double* sub, int64_t B, hipStream_t s);
+// sub: B <= 4, the da subtrees (proj_bwd_fused_sub_bytes); B > 4, the da run
+// subtrees (proj_bwd_da_parts_bytes)
 hipError_t launch_selftest_probe(const float* in, float* out, uint32_t* bits, int n,
                                  hipStream_t s);
 

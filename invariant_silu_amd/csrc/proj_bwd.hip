@@ -25,6 +25,8 @@
 //   da_leaf_f32_kernel<NB>     fp32 storage, B <= 4: the leaf-group blocks alone
 //                              (then da_finish_kernel<NB, float>)
 //   silu_kernel, dw_mfma_kernel, da_mfma_kernel   B > 8 (fp32 storage: B > 4)
+//   da_parts_kernel            B <= 64 of those: the leaf runs' subtrees
+//                              added pairwise (-> dtemb)
 // With kAcc (adaln_proj_bwd_acc) the bf16 kernels also store the fp32 values
 // they round to bf16 -- fl32 of the dW and db sums, and da * silu'(temb) in
 // fp32 -- into whichever of the caller's fp32 arrays are not NULL; the
@@ -502,10 +504,15 @@ __global__ __launch_bounds__(64 * kDwMWaves) void dw_mfma_kernel(const float* __
 // so two blocks fit a CU.  Blocks x and x + 8
 // (same XCD) take the two halves of one 128-byte row segment of W.  Rows
 // past B load sample B - 1 and are never stored.
+// Split form (kParts = 2, 4 or 8): the 128 leaves fall into kParts aligned
+// runs of 128 / kParts, one per blockIdx.z, each run on 4 waves; a block
+// stores its run's subtree (fp64, 2 tiles x 64 lanes) in `parts` and
+// da_parts_kernel adds the kParts subtrees pairwise in run order, which is
+// the tree the one-block form builds.  With 96 x ceil(B / 16) blocks the
+// one-block form leaves most CUs idle for B <= 64; the split fills them.
 template <int N>
 constexpr int kLeafSteps = N / (4 * kDaSlots);   // a leaf's rows, 4 per matrix-core step
 constexpr int kDaMWaves = 8;
-constexpr int kDaMLeaves = 128 / kDaMWaves;    // 16 per wave
 constexpr int kDaMGroup = 4;                   // leaves run side by side
 constexpr int kDaMCols = 32;
 constexpr int kDaMAhead = 1;                   // steps in flight
@@ -517,18 +524,51 @@ struct DaStep {
 };
 
 // T: storage type of W, temb and dtemb; N rows of W
-template <typename T, int N = kN, bool kAcc = false>
+// blocks for kParts runs: 4 waves; one run: kDaMWaves
+template <int kParts>
+constexpr int kDaWavesFor = kParts == 1 ? kDaMWaves : 4;
+
+// block x's first column and the block's samples b0 .. b0 + rows - 1
+__device__ __forceinline__ int da_col0(int x) { return ((x / 16) * 8 + x % 8) * 64 + ((x / 8) % 2) * kDaMCols; }
+
+// dtemb from the root tiles: lane (r, g) holds samples b0 + g + 4 v, columns
+// k0 + 2 r + n
+template <typename T, bool kAcc>
+__device__ __forceinline__ void da_store(const f64x4_t (&tot)[2], const T* __restrict__ temb,
+                                         T* __restrict__ dtemb, float* __restrict__ dtemb32, int64_t b0,
+                                         int rows_here, int k0, int r, int g) {
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int sr = g + 4 * v;
+    if (sr < rows_here) {
+      const int64_t i = (b0 + sr) * kD + k0 + 2 * r;
+      Pair<T> z;
+      z.load(temb + i);
+      const float d0 = static_cast<float>(tot[0][v]) * dsilu_f32(z.lo());
+      const float d1 = static_cast<float>(tot[1][v]) * dsilu_f32(z.hi());
+      Pair<T>::store(dtemb + i, d0, d1);
+      if constexpr (kAcc) {
+        if (dtemb32) *reinterpret_cast<float2*>(dtemb32 + i) = make_float2(d0, d1);
+      }
+    }
+  }
+}
+
+template <typename T, int N = kN, bool kAcc = false, int kParts = 1>
 __global__ __launch_bounds__(64 * kDaMWaves) void da_mfma_kernel(const float* __restrict__ d_emb,
                                                                  const T* __restrict__ W,
                                                                  const T* __restrict__ temb,
                                                                  T* __restrict__ dtemb, int64_t B,
-                                                                 float* __restrict__ dtemb32) {
-  __shared__ f64x4_t sub[kDaMWaves - 1][2][64];   // 28 KB
+                                                                 float* __restrict__ dtemb32,
+                                                                 f64x4_t* __restrict__ parts) {
+  constexpr int kWaves = kDaWavesFor<kParts>;
+  constexpr int kLeaves = 128 / (kParts * kWaves);   // per wave
+  static_assert(kLeaves >= kDaMGroup && kLeaves % kDaMGroup == 0, "a wave runs whole leaf groups");
+  __shared__ f64x4_t sub[kWaves - 1][2][64];   // 28 KB at 8 waves
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
-  const int x = blockIdx.x;
-  const int k0 = ((x / 16) * 8 + x % 8) * 64 + ((x / 8) % 2) * kDaMCols;
+  const int k0 = da_col0(blockIdx.x);
   const int64_t b0 = static_cast<int64_t>(blockIdx.y) * 16;
   const int rows_here = static_cast<int>((B - b0) < 16 ? (B - b0) : 16);
   const int br = r < rows_here ? r : rows_here - 1;
@@ -537,10 +577,10 @@ __global__ __launch_bounds__(64 * kDaMWaves) void da_mfma_kernel(const float* __
   const Buffer wbuf(W, static_cast<uint32_t>(N) * kD * sizeof(T));
   const uint32_t e_off = (static_cast<uint32_t>(br) * N + kDaSlots * g) * 4;
   const uint32_t w_off = (static_cast<uint32_t>(kDaSlots * g) * kD + k0 + 2 * r) * sizeof(T);
-  const int leaf0 = wave * kDaMLeaves;
+  const int leaf0 = (static_cast<int>(blockIdx.z) * kWaves + wave) * kLeaves;
 
-  PairTree<ilog2(kDaMLeaves), f64x4_t> tree[2];
-  static_for<0, kDaMLeaves / kDaMGroup>([&](auto qc) {
+  PairTree<ilog2(kLeaves), f64x4_t> tree[2];
+  static_for<0, kLeaves / kDaMGroup>([&](auto qc) {
     constexpr int q = decltype(qc)::value;
     const int t0 = leaf0 + kDaMGroup * q;
     auto load = [&](DaStep<T>& d, int st) {
@@ -573,7 +613,7 @@ __global__ __launch_bounds__(64 * kDaMWaves) void da_mfma_kernel(const float* __
       tree[1].template push<kDaMGroup * q + l>(acc[l][1]);
     });
   });
-  constexpr int kTop = ilog2(kDaMLeaves);
+  constexpr int kTop = ilog2(kLeaves);
   if (wave > 0) {
     sub[wave - 1][0][lane] = tree[0].node[kTop];
     sub[wave - 1][1][lane] = tree[1].node[kTop];
@@ -583,27 +623,76 @@ __global__ __launch_bounds__(64 * kDaMWaves) void da_mfma_kernel(const float* __
   f64x4_t tot[2];
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
-    f64x4_t v[kDaMWaves];
+    f64x4_t v[kWaves];
     v[0] = tree[n].node[kTop];
 #pragma unroll
-    for (int w = 1; w < kDaMWaves; ++w) v[w] = sub[w - 1][n][lane];
+    for (int w = 1; w < kWaves; ++w) v[w] = sub[w - 1][n][lane];
     tot[n] = pair_reduce(v);
   }
-  // lane holds samples b0 + g + 4 v, columns k0 + 2 r + n
+  if constexpr (kParts > 1) {
+    // run blockIdx.z of block (x, y): its two tiles, lane-major
+    const int64_t at = ((static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x) * kParts + blockIdx.z) * 2;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int sr = g + 4 * v;
-    if (sr < rows_here) {
-      const int64_t i = (b0 + sr) * kD + k0 + 2 * r;
-      Pair<T> z;
-      z.load(temb + i);
-      const float d0 = static_cast<float>(tot[0][v]) * dsilu_f32(z.lo());
-      const float d1 = static_cast<float>(tot[1][v]) * dsilu_f32(z.hi());
-      Pair<T>::store(dtemb + i, d0, d1);
-      if constexpr (kAcc) {
-        if (dtemb32) *reinterpret_cast<float2*>(dtemb32 + i) = make_float2(d0, d1);
-      }
-    }
+    for (int n = 0; n < 2; ++n) parts[(at + n) * 64 + lane] = tot[n];
+  } else {
+    da_store<T, kAcc>(tot, temb, dtemb, dtemb32, b0, rows_here, k0, r, g);
+  }
+}
+
+// the split form's second launch: block (x, y) of 64 lanes adds its kParts
+// run subtrees pairwise in run order and writes dtemb
+template <typename T, int kParts, bool kAcc>
+__global__ __launch_bounds__(64) void da_parts_kernel(const f64x4_t* __restrict__ parts,
+                                                      const T* __restrict__ temb, T* __restrict__ dtemb,
+                                                      int64_t B, float* __restrict__ dtemb32) {
+  const int lane = threadIdx.x;
+  const int r = lane & 15, g = lane >> 4;
+  const int k0 = da_col0(blockIdx.x);
+  const int64_t b0 = static_cast<int64_t>(blockIdx.y) * 16;
+  const int rows_here = static_cast<int>((B - b0) < 16 ? (B - b0) : 16);
+  const int64_t blk = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
+  f64x4_t tot[2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    f64x4_t v[kParts];
+#pragma unroll
+    for (int q = 0; q < kParts; ++q) v[q] = parts[((blk * kParts + q) * 2 + n) * 64 + lane];
+    tot[n] = pair_reduce(v);
+  }
+  da_store<T, kAcc>(tot, temb, dtemb, dtemb32, b0, rows_here, k0, r, g);
+}
+
+// runs per da block for B samples (1 = the one-block form): 8 for one row of
+// blocks (B <= 16), 4 up to four rows (B <= 64); measured at S = 1024
+int da_runs(int64_t B) {
+  const int64_t by = (B + 15) / 16;
+  return by == 1 ? 8 : by <= 4 ? 4 : 1;
+}
+
+// da on the matrix cores for B samples: the one-block form, or the split
+// form with its subtrees in `parts` (da_parts_bytes(B) bytes)
+template <typename T, int N, bool kAcc, int kParts>
+hipError_t da_launch(const float* d_emb, const T* W, const T* temb, T* dtemb, int64_t B, float* dtemb32,
+                     f64x4_t* parts, hipStream_t s) {
+  const dim3 grid(kD / kDaMCols, static_cast<unsigned>((B + 15) / 16), kParts);
+  hipLaunchKernelGGL((da_mfma_kernel<T, N, kAcc, kParts>), grid, dim3(64 * kDaWavesFor<kParts>), 0, s, d_emb, W,
+                     temb, dtemb, B, dtemb32, parts);
+  if constexpr (kParts > 1) {
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    hipLaunchKernelGGL((da_parts_kernel<T, kParts, kAcc>), dim3(grid.x, grid.y), dim3(64), 0, s, parts, temb,
+                       dtemb, B, dtemb32);
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int N, bool kAcc>
+hipError_t da_rows(const float* d_emb, const T* W, const T* temb, T* dtemb, int64_t B, float* dtemb32,
+                   double* parts, hipStream_t s) {
+  f64x4_t* p = reinterpret_cast<f64x4_t*>(parts);
+  switch (da_runs(B)) {
+    case 8: return da_launch<T, N, kAcc, 8>(d_emb, W, temb, dtemb, B, dtemb32, p, s);
+    case 4: return da_launch<T, N, kAcc, 4>(d_emb, W, temb, dtemb, B, dtemb32, p, s);
+    default: return da_launch<T, N, kAcc, 1>(d_emb, W, temb, dtemb, B, dtemb32, nullptr, s);
   }
 }
 
@@ -667,11 +756,8 @@ hipError_t proj_bwd_dw_rows(const float* d_emb, const uint16_t* a, uint16_t* dW,
 
 template <int N, bool kAcc>
 hipError_t proj_bwd_da_rows(const float* d_emb, const uint16_t* W, const uint16_t* temb, uint16_t* dtemb,
-                            int64_t B, const AccOut& acc, hipStream_t s) {
-  const int64_t by = (B + 15) / 16;
-  hipLaunchKernelGGL((da_mfma_kernel<uint16_t, N, kAcc>), dim3(kD / kDaMCols, static_cast<unsigned>(by)),
-                     dim3(64 * kDaMWaves), 0, s, d_emb, W, temb, dtemb, B, acc.dtemb);
-  return hipGetLastError();
+                            double* parts, int64_t B, const AccOut& acc, hipStream_t s) {
+  return da_rows<uint16_t, N, kAcc>(d_emb, W, temb, dtemb, B, acc.dtemb, parts, s);
 }
 
 bool any(const AccOut& acc) { return acc.dW || acc.db || acc.dtemb; }
@@ -679,6 +765,11 @@ bool any(const AccOut& acc) { return acc.dW || acc.db || acc.dtemb; }
 }  // namespace
 
 size_t proj_bwd_fused_sub_bytes(int64_t B) { return static_cast<size_t>(kDaGroups * B * kD * 8); }
+
+size_t proj_bwd_da_parts_bytes(int64_t B) {
+  const int runs = da_runs(B);
+  return runs == 1 ? 0 : static_cast<size_t>((B + 15) / 16) * (kD / kDaMCols) * runs * 2 * 64 * sizeof(f64x4_t);
+}
 
 hipError_t launch_proj_bwd_fused(const float* d_emb, const uint16_t* temb, const uint16_t* W,
                                  uint16_t* dW, uint16_t* db, uint16_t* dtemb, double* sub, int64_t B, int64_t N,
@@ -706,14 +797,14 @@ hipError_t launch_proj_bwd_dw(const float* d_emb, const uint16_t* a, uint16_t* d
 }
 
 hipError_t launch_proj_bwd_da(const float* d_emb, const uint16_t* W, const uint16_t* temb, uint16_t* dtemb,
-                              int64_t B, int64_t N, hipStream_t s, const AccOut& acc) {
+                              double* parts, int64_t B, int64_t N, hipStream_t s, const AccOut& acc) {
   const bool f = any(acc);
   if (N == kN)
-    return f ? proj_bwd_da_rows<kN, true>(d_emb, W, temb, dtemb, B, acc, s)
-             : proj_bwd_da_rows<kN, false>(d_emb, W, temb, dtemb, B, acc, s);
+    return f ? proj_bwd_da_rows<kN, true>(d_emb, W, temb, dtemb, parts, B, acc, s)
+             : proj_bwd_da_rows<kN, false>(d_emb, W, temb, dtemb, parts, B, acc, s);
   if (N == kN6)
-    return f ? proj_bwd_da_rows<kN6, true>(d_emb, W, temb, dtemb, B, acc, s)
-             : proj_bwd_da_rows<kN6, false>(d_emb, W, temb, dtemb, B, acc, s);
+    return f ? proj_bwd_da_rows<kN6, true>(d_emb, W, temb, dtemb, parts, B, acc, s)
+             : proj_bwd_da_rows<kN6, false>(d_emb, W, temb, dtemb, parts, B, acc, s);
   return hipErrorInvalidValue;
 }
 
@@ -752,13 +843,8 @@ hipError_t launch_proj_bwd_f32(const float* d_emb, const float* temb, const floa
     case 2: return da_f32_small<2>(d_emb, W, temb, dtemb, sub, s);
     case 3: return da_f32_small<3>(d_emb, W, temb, dtemb, sub, s);
     case 4: return da_f32_small<4>(d_emb, W, temb, dtemb, sub, s);
-    default: {
-      const int64_t by = (B + 15) / 16;
-      hipLaunchKernelGGL(da_mfma_kernel<float>, dim3(kD / kDaMCols, static_cast<unsigned>(by)),
-                         dim3(64 * kDaMWaves), 0, s, d_emb, W, temb, dtemb, B, nullptr);
-    }
+    default: return da_rows<float, kN, false>(d_emb, W, temb, dtemb, B, nullptr, sub, s);
   }
-  return hipGetLastError();
 }
 
 }  // namespace adaln

@@ -35,6 +35,8 @@ WORKLOADS = {
     "batch64_s1024": dict(B=64, S=1024, outlier_frac=0.0),
     # one GPU's share of batch64_s1024 split over eight GPUs by samples
     "batch8_s1024": dict(B=8, S=1024, outlier_frac=0.0),
+    # ... and over four GPUs
+    "batch16_s1024": dict(B=16, S=1024, outlier_frac=0.0),
     # the pages' large conditioning batch: 2048 samples of 3 tokens
     "batch2048_s3": dict(B=2048, S=3, outlier_frac=0.0),
 }

@@ -46,25 +46,33 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_strerror(L):
-    assert L.adaln_abi_version() == 15 == lib.ABI_VERSION
+    assert L.adaln_abi_version() == 16 == lib.ABI_VERSION
     header = open(HEADER).read()
-    assert re.search(r"#define ADALN_ABI_VERSION (\d+)", header).group(1) == "15"
+    assert re.search(r"#define ADALN_ABI_VERSION (\d+)", header).group(1) == "16"
     for code in range(-8, 1):
         assert len(lib.strerror(code)) >= 2
 
 
 def test_workspace_sizes(L):
     pad = lambda n: (n + 255) // 256 * 256   # noqa: E731
-    for B, S in [(1, 31), (2, 1024), (1, 4096), (64, 1024), (3, 6889), (5, 33), (8, 1024), (9, 3)]:
+    for B, S in [(1, 31), (2, 1024), (1, 4096), (64, 1024), (3, 6889), (5, 33), (8, 1024), (9, 3), (17, 2),
+                 (65, 2), (300, 1)]:
         T0 = math.ceil(S / 32)
         assert lib.workspace_bytes(lib.OP_NORM_MOD_BWD, B, S, 3072) == pad(B * T0 * 6144 * 8)
         assert lib.workspace_bytes(lib.OP_TOKEN_TREE_SUM, B, S, 100) == pad(B * T0 * 128 * 8)
-        # B <= 8: 32 fp64 da subtrees per sample and column; B > 8: the SiLU activations
-        proj_bwd = pad(32 * B * 3072 * 8) if B <= 8 else pad(B * 3072 * 2)
+        # da leaf runs on the matrix cores: 8 for one row of 16 samples, 4 up to
+        # four rows, one beyond; each run's subtree is 96 column blocks x 2 tiles
+        # x 64 lanes x 4 fp64 per row of samples
+        rows = math.ceil(B / 16)
+        runs = 8 if rows == 1 else 4 if rows <= 4 else 1
+        parts = 0 if runs == 1 else rows * 96 * runs * 2 * 64 * 32
+        # B <= 8: 32 fp64 da subtrees per sample and column; B > 8: the SiLU
+        # activations, then the run subtrees
+        proj_bwd = pad(32 * B * 3072 * 8) if B <= 8 else pad(B * 3072 * 2) + pad(parts)
         assert lib.workspace_bytes(lib.OP_PROJ_BWD, B, S, 3072) == proj_bwd
         assert lib.workspace_bytes(lib.OP_PROJ_FWD, B, S, 3072) == pad(B * 3072 * 2)
-        # fp32: the activations, then for B <= 4 the fp64 da subtrees
-        sub = pad(32 * B * 3072 * 8) if B <= 4 else 0
+        # fp32: the activations, then the fp64 da subtrees (B <= 4) or run subtrees
+        sub = pad(32 * B * 3072 * 8) if B <= 4 else pad(parts)
         assert lib.workspace_bytes(lib.OP_BWD_F32, B, S, 3072) == pad(B * T0 * 6144 * 8) + pad(B * 3072 * 4) + sub
         assert lib.workspace_bytes(lib.OP_RESIDUAL_BWD, B, S, 3072) == pad(B * T0 * 9216 * 8)
         C = math.ceil(B * S / 512)

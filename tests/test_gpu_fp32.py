@@ -78,7 +78,7 @@ def test_fp32_parity(gpu_lib, B, S):
         assert r["n_fail"] == 0, k
 
 
-@pytest.mark.parametrize("B,S", [(5, 33), (20, 3)])
+@pytest.mark.parametrize("B,S", [(5, 33), (20, 3), (70, 2)])
 def test_fp32_singleton_vs_batch(gpu_lib, B, S):
     """Per-sample outputs are the same bytes alone (B = 1: vector da) and in
     the batch (B > 4: matrix-core da)."""

@@ -7,7 +7,8 @@ its bf16 outputs are rounded from (dW_f32, db_f32, dtemb_f32).
   their storage rounding (dW_acc, db_acc, dtemb_acc), the fp64 twin
   arbitrating, on the vector-unit (B <= 8) and matrix-core (B > 8) paths and
   at both projection widths;
-* dtemb_f32 rows are bytewise batch-invariant across the two paths;
+* dtemb_f32 rows are bytewise batch-invariant across the vector-unit path
+  and the three matrix-core forms of da (8, 4 or 1 leaf runs per block);
 * a NULL fp32 pointer is accepted and changes none of the other outputs.
 """
 
@@ -48,7 +49,8 @@ def _f32(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy()
 
 
-@pytest.mark.parametrize("n,B", [(N, 1), (N, 3), (N, 6), (N, 17), (N6, 1), (N6, 6), (N6, 10)])
+@pytest.mark.parametrize("n,B", [(N, 1), (N, 3), (N, 6), (N, 16), (N, 17), (N, 70), (N6, 1), (N6, 6), (N6, 10),
+                                 (N6, 40)])
 def test_proj_bwd_acc_parity(gpu_lib, n, B):
     from invariant_silu_amd import ops
     print(f"[proj_bwd_acc] N={n} B={B}", flush=True)
@@ -76,15 +78,21 @@ def test_proj_bwd_acc_parity(gpu_lib, n, B):
         assert r["n_fail"] == 0, k
 
 
-def test_proj_bwd_acc_dtemb_batch_invariant(gpu_lib):
-    """dtemb_f32 rows: alone (vector units) and inside B = 9 (matrix cores)."""
+@pytest.mark.parametrize("n,B", [(N, 9), (N, 40), (N6, 70)])
+def test_proj_bwd_acc_dtemb_batch_invariant(gpu_lib, n, B):
+    """dtemb and dtemb_f32 rows are the same bytes alone (vector units), in a
+    batch of 9 .. 16 (8 leaf runs per matrix-core block), of 17 .. 64 (4 runs)
+    and beyond (one block over all 128 leaves)."""
     from invariant_silu_amd import ops
-    print("[proj_bwd_acc] invariance B=9", flush=True)
-    _, d = _case(9, N, seed=321)
+    print(f"[proj_bwd_acc] invariance N={n} B={B}", flush=True)
+    _, d = _case(B, n, seed=321 + B)
     full = ops.proj_bwd(d["d_emb"], d["temb"], d["W"], want_f32=True)
-    for b in (0, 4, 8):
+    for b in sorted({0, B // 2, B - 1}):
         one = ops.proj_bwd(d["d_emb"][b:b + 1], d["temb"][b:b + 1], d["W"], want_f32=True)
-        assert same_bytes(full[5][b:b + 1], one[5]), f"sample {b}"
+        assert same_bytes(full[2][b:b + 1], one[2]) and same_bytes(full[5][b:b + 1], one[5]), f"sample {b}"
+    for lo, hi in ((B - 9, B), (max(0, B - 16), B), (max(0, B - 40), B)):
+        sub = ops.proj_bwd(d["d_emb"][lo:hi], d["temb"][lo:hi], d["W"], want_f32=True)
+        assert same_bytes(full[2][lo:hi], sub[2]) and same_bytes(full[5][lo:hi], sub[5]), f"samples {lo}..{hi}"
 
 
 @pytest.mark.parametrize("B", [2, 7, 11])
