@@ -432,8 +432,7 @@ int adaln_proj_bwd_acc(const float* d_emb, const adaln_bf16* temb, const adaln_b
         adaln::launch_proj_bwd_fused(d_emb, temb, W, dW, db, dtemb, static_cast<double*>(ws), B, N, s, acc));
   }
   if (int rc = launched(adaln::launch_silu(temb, a, B * kD, s))) return rc;
-  if (int rc = launched(adaln::launch_proj_bwd_dw(d_emb, a, dW, db, B, N, s, acc))) return rc;
-  return launched(adaln::launch_proj_bwd_da(d_emb, W, temb, dtemb, da_parts(a, B), B, N, s, acc));
+  return launched(adaln::launch_proj_bwd_mfma(d_emb, a, W, temb, dW, db, dtemb, da_parts(a, B), B, N, s, acc));
 }
 
 int adaln_proj_bwd(const float* d_emb, const adaln_bf16* temb, const adaln_bf16* W,
@@ -522,8 +521,7 @@ int adaln_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float* mean, co
     return launched(adaln::launch_proj_bwd_fused(d_emb, temb, W, dW, db, dtemb, reinterpret_cast<double*>(a), B, kN,
                                                  s));
   if (int rc = launched(adaln::launch_silu(temb, a, B * kD, s))) return rc;
-  if (int rc = launched(adaln::launch_proj_bwd_dw(d_emb, a, dW, db, B, kN, s))) return rc;
-  return launched(adaln::launch_proj_bwd_da(d_emb, W, temb, dtemb, da_parts(a, B), B, kN, s));
+  return launched(adaln::launch_proj_bwd_mfma(d_emb, a, W, temb, dW, db, dtemb, da_parts(a, B), B, kN, s));
 }
 
 int adaln_fwd_f32(const float* temb, const float* W, const float* bias, const float* x, float* emb, float* out,

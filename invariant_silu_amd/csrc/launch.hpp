@@ -56,11 +56,11 @@ struct AccOut {
 hipError_t launch_proj_bwd_fused(const float* d_emb, const uint16_t* temb, const uint16_t* W,
                                  uint16_t* dW, uint16_t* db, uint16_t* dtemb, double* sub, int64_t B, int64_t N,
                                  hipStream_t s, const AccOut& acc = AccOut{});
-hipError_t launch_proj_bwd_dw(const float* d_emb, const uint16_t* a, uint16_t* dW, uint16_t* db,
-                              int64_t B, int64_t N, hipStream_t s, const AccOut& acc = AccOut{});
-hipError_t launch_proj_bwd_da(const float* d_emb, const uint16_t* W, const uint16_t* temb,
-                              uint16_t* dtemb, double* parts, int64_t B, int64_t N, hipStream_t s,
-                              const AccOut& acc = AccOut{});
+// B > 8: dW, db, da and dtemb on the matrix cores from a = SiLU(temb);
+// parts: proj_bwd_da_parts_bytes(B) bytes
+hipError_t launch_proj_bwd_mfma(const float* d_emb, const uint16_t* a, const uint16_t* W, const uint16_t* temb,
+                                uint16_t* dW, uint16_t* db, uint16_t* dtemb, double* parts, int64_t B, int64_t N,
+                                hipStream_t s, const AccOut& acc = AccOut{});
 // A block's norm site.  Its modulation as three [B, D] bf16 views with one
 // row stride ld (elements, a multiple of 8); gate is used only with the
 // residual add.

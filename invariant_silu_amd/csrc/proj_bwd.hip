@@ -25,8 +25,10 @@
 //   da_leaf_f32_kernel<NB>     fp32 storage, B <= 4: the leaf-group blocks alone
 //                              (then da_finish_kernel<NB, float>)
 //   silu_kernel, dw_mfma_kernel, da_mfma_kernel   B > 8 (fp32 storage: B > 4)
-//   da_parts_kernel            B <= 64 of those: the leaf runs' subtrees
-//                              added pairwise (-> dtemb)
+//   proj_bwd_mid_kernel        B <= 64 of those: da's leaf runs and the dW
+//                              tiles in one grid (fp32 storage: 17 <= B)
+//   da_parts_kernel            B <= 64: the leaf runs' subtrees added
+//                              pairwise (-> dtemb)
 // With kAcc (adaln_proj_bwd_acc) the bf16 kernels also store the fp32 values
 // they round to bf16 -- fl32 of the dW and db sums, and da * silu'(temb) in
 // fp32 -- into whichever of the caller's fp32 arrays are not NULL; the
@@ -419,18 +421,16 @@ constexpr int kDwMRows = 64;
 constexpr int kDwMCols = 32;
 constexpr int kDwMWaves = 4;
 
-template <typename T, int N = kN, bool kAcc = false>
-__global__ __launch_bounds__(64 * kDwMWaves) void dw_mfma_kernel(const float* __restrict__ d_emb,
-                                                                 const T* __restrict__ a,
-                                                                 T* __restrict__ dW,
-                                                                 T* __restrict__ db, int64_t B,
-                                                                 float* __restrict__ dW32,
-                                                                 float* __restrict__ db32) {
+// block (bx, by): rows bx * 64 .., columns by * 128 .. (32 per wave)
+template <typename T, int N, bool kAcc>
+__device__ __forceinline__ void dw_block(const float* __restrict__ d_emb, const T* __restrict__ a,
+                                         T* __restrict__ dW, T* __restrict__ db, int64_t B,
+                                         float* __restrict__ dW32, float* __restrict__ db32, int bx, int by) {
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
-  const int j0 = static_cast<int>(blockIdx.x) * kDwMRows;
-  const int k0 = (static_cast<int>(blockIdx.y) * kDwMWaves + wave) * kDwMCols;
+  const int j0 = bx * kDwMRows;
+  const int k0 = (by * kDwMWaves + wave) * kDwMCols;
   const int64_t steps = (B + 3) / 4;
 
   f64x4_t acc[4][2];
@@ -481,7 +481,7 @@ __global__ __launch_bounds__(64 * kDwMWaves) void dw_mfma_kernel(const float* __
         if (dW32) *reinterpret_cast<float2*>(dW32 + i) = make_float2(f0, f1);
       }
     }
-  if (blockIdx.y == 0 && wave == 0) {
+  if (by == 0 && wave == 0) {
     double sdb = 0.0;
     for (int64_t b = 0; b < B; ++b) sdb += static_cast<double>(d_emb[b * N + j0 + lane]);
     const float v = static_cast<float>(sdb);
@@ -490,6 +490,16 @@ __global__ __launch_bounds__(64 * kDwMWaves) void dw_mfma_kernel(const float* __
       if (db32) db32[j0 + lane] = v;
     }
   }
+}
+
+template <typename T, int N = kN, bool kAcc = false>
+__global__ __launch_bounds__(64 * kDwMWaves) void dw_mfma_kernel(const float* __restrict__ d_emb,
+                                                                 const T* __restrict__ a,
+                                                                 T* __restrict__ dW,
+                                                                 T* __restrict__ db, int64_t B,
+                                                                 float* __restrict__ dW32,
+                                                                 float* __restrict__ db32) {
+  dw_block<T, N, kAcc>(d_emb, a, dW, db, B, dW32, db32, blockIdx.x, blockIdx.y);
 }
 
 // da and dtemb: block of 16 samples (b0 ..) x 32 columns (k0 ..), 8 waves;
@@ -515,6 +525,7 @@ constexpr int kLeafSteps = N / (4 * kDaSlots);   // a leaf's rows, 4 per matrix-
 constexpr int kDaMWaves = 8;
 constexpr int kDaMGroup = 4;                   // leaves run side by side
 constexpr int kDaMCols = 32;
+constexpr int kDaBlocksX = kD / kDaMCols;        // column blocks
 constexpr int kDaMAhead = 1;                   // steps in flight
 
 template <typename T>
@@ -554,22 +565,24 @@ __device__ __forceinline__ void da_store(const f64x4_t (&tot)[2], const T* __res
   }
 }
 
-template <typename T, int N = kN, bool kAcc = false, int kParts = 1>
-__global__ __launch_bounds__(64 * kDaMWaves) void da_mfma_kernel(const float* __restrict__ d_emb,
-                                                                 const T* __restrict__ W,
-                                                                 const T* __restrict__ temb,
-                                                                 T* __restrict__ dtemb, int64_t B,
-                                                                 float* __restrict__ dtemb32,
-                                                                 f64x4_t* __restrict__ parts) {
+// da block (x, y) of run z (z = 0 with one run); sub: the block's LDS for
+// its waves' subtrees
+template <int kParts>
+using DaSub = f64x4_t[kDaWavesFor<kParts> - 1][2][64];   // 28 KB at 8 waves
+
+template <typename T, int N, bool kAcc, int kParts>
+__device__ __forceinline__ void da_block(const float* __restrict__ d_emb, const T* __restrict__ W,
+                                         const T* __restrict__ temb, T* __restrict__ dtemb, int64_t B,
+                                         float* __restrict__ dtemb32, f64x4_t* __restrict__ parts, int x, int y,
+                                         int z, DaSub<kParts>& sub) {
   constexpr int kWaves = kDaWavesFor<kParts>;
   constexpr int kLeaves = 128 / (kParts * kWaves);   // per wave
   static_assert(kLeaves >= kDaMGroup && kLeaves % kDaMGroup == 0, "a wave runs whole leaf groups");
-  __shared__ f64x4_t sub[kWaves - 1][2][64];   // 28 KB at 8 waves
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
-  const int k0 = da_col0(blockIdx.x);
-  const int64_t b0 = static_cast<int64_t>(blockIdx.y) * 16;
+  const int k0 = da_col0(x);
+  const int64_t b0 = static_cast<int64_t>(y) * 16;
   const int rows_here = static_cast<int>((B - b0) < 16 ? (B - b0) : 16);
   const int br = r < rows_here ? r : rows_here - 1;
 
@@ -577,7 +590,7 @@ __global__ __launch_bounds__(64 * kDaMWaves) void da_mfma_kernel(const float* __
   const Buffer wbuf(W, static_cast<uint32_t>(N) * kD * sizeof(T));
   const uint32_t e_off = (static_cast<uint32_t>(br) * N + kDaSlots * g) * 4;
   const uint32_t w_off = (static_cast<uint32_t>(kDaSlots * g) * kD + k0 + 2 * r) * sizeof(T);
-  const int leaf0 = (static_cast<int>(blockIdx.z) * kWaves + wave) * kLeaves;
+  const int leaf0 = (z * kWaves + wave) * kLeaves;
 
   PairTree<ilog2(kLeaves), f64x4_t> tree[2];
   static_for<0, kLeaves / kDaMGroup>([&](auto qc) {
@@ -630,12 +643,47 @@ __global__ __launch_bounds__(64 * kDaMWaves) void da_mfma_kernel(const float* __
     tot[n] = pair_reduce(v);
   }
   if constexpr (kParts > 1) {
-    // run blockIdx.z of block (x, y): its two tiles, lane-major
-    const int64_t at = ((static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x) * kParts + blockIdx.z) * 2;
+    // run z of block (x, y): its two tiles, lane-major
+    const int64_t at = ((static_cast<int64_t>(y) * kDaBlocksX + x) * kParts + z) * 2;
 #pragma unroll
     for (int n = 0; n < 2; ++n) parts[(at + n) * 64 + lane] = tot[n];
   } else {
     da_store<T, kAcc>(tot, temb, dtemb, dtemb32, b0, rows_here, k0, r, g);
+  }
+}
+
+template <typename T, int N = kN, bool kAcc = false, int kParts = 1>
+__global__ __launch_bounds__(64 * kDaMWaves) void da_mfma_kernel(const float* __restrict__ d_emb,
+                                                                 const T* __restrict__ W,
+                                                                 const T* __restrict__ temb,
+                                                                 T* __restrict__ dtemb, int64_t B,
+                                                                 float* __restrict__ dtemb32,
+                                                                 f64x4_t* __restrict__ parts) {
+  __shared__ DaSub<kParts> sub;
+  da_block<T, N, kAcc, kParts>(d_emb, W, temb, dtemb, B, dtemb32, parts, blockIdx.x, blockIdx.y, blockIdx.z, sub);
+}
+
+// B <= 64 (the split form): the da run blocks (ids [0, n_da), x fastest,
+// then the sample row, then the run) and the dW tiles (row block fastest) in
+// one grid of 4-wave blocks, so each fills the CUs the other leaves idle.
+// n_da is a multiple of 8, so both keep their XCD placement.
+template <typename T, int N, bool kAcc, int kParts>
+__global__ __launch_bounds__(256) void proj_bwd_mid_kernel(const float* __restrict__ d_emb,
+                                                           const T* __restrict__ a, const T* __restrict__ W,
+                                                           T* __restrict__ dW, T* __restrict__ db, int64_t B,
+                                                           f64x4_t* __restrict__ parts, float* __restrict__ dW32,
+                                                           float* __restrict__ db32) {
+  static_assert(kParts > 1 && kDaWavesFor<kParts> == 4 && kDwMWaves == 4, "both roles run 4-wave blocks");
+  __shared__ DaSub<kParts> sub;
+  const int rows = static_cast<int>((B + 15) / 16);
+  const int n_da = kDaBlocksX * rows * kParts;
+  const int id = blockIdx.x;
+  if (id < n_da) {
+    da_block<T, N, kAcc, kParts>(d_emb, W, nullptr, nullptr, B, nullptr, parts, id % kDaBlocksX,
+                                 (id / kDaBlocksX) % rows, id / (kDaBlocksX * rows), sub);
+  } else {
+    const int t = id - n_da;
+    dw_block<T, N, kAcc>(d_emb, a, dW, db, B, dW32, db32, t % (N / kDwMRows), t / (N / kDwMRows));
   }
 }
 
@@ -669,30 +717,45 @@ int da_runs(int64_t B) {
   return by == 1 ? 8 : by <= 4 ? 4 : 1;
 }
 
-// da on the matrix cores for B samples: the one-block form, or the split
-// form with its subtrees in `parts` (da_parts_bytes(B) bytes)
+// dW, db, da and dtemb on the matrix cores, a = SiLU(temb) already in `a`:
+// the dW tiles, then one block over all 128 leaves per tile (kParts = 1); or
+// the leaf runs and the dW tiles in one grid, then da_parts_kernel (parts:
+// proj_bwd_da_parts_bytes(B) bytes).  fp32 storage with 8 runs keeps the
+// two grids apart: its combined blocks hold more registers than the dW
+// tiles alone and measured slower (B = 8: 103.6 -> 106.0 us backward).
 template <typename T, int N, bool kAcc, int kParts>
-hipError_t da_launch(const float* d_emb, const T* W, const T* temb, T* dtemb, int64_t B, float* dtemb32,
-                     f64x4_t* parts, hipStream_t s) {
-  const dim3 grid(kD / kDaMCols, static_cast<unsigned>((B + 15) / 16), kParts);
-  hipLaunchKernelGGL((da_mfma_kernel<T, N, kAcc, kParts>), grid, dim3(64 * kDaWavesFor<kParts>), 0, s, d_emb, W,
-                     temb, dtemb, B, dtemb32, parts);
+hipError_t mfma_launch(const float* d_emb, const T* a, const T* W, const T* temb, T* dW, T* db, T* dtemb,
+                       int64_t B, const AccOut& acc, f64x4_t* parts, hipStream_t s) {
+  constexpr bool kCombined = kParts > 1 && !(sizeof(T) == 4 && kParts == 8);
+  const unsigned rows = static_cast<unsigned>((B + 15) / 16);
+  const dim3 dw_grid(N / kDwMRows, kD / (kDwMCols * kDwMWaves));
+  if constexpr (kCombined) {
+    const unsigned blocks = kDaBlocksX * rows * kParts + dw_grid.x * dw_grid.y;
+    hipLaunchKernelGGL((proj_bwd_mid_kernel<T, N, kAcc, kParts>), dim3(blocks), dim3(256), 0, s, d_emb, a, W, dW,
+                       db, B, parts, acc.dW, acc.db);
+  } else {
+    hipLaunchKernelGGL((dw_mfma_kernel<T, N, kAcc>), dw_grid, dim3(64 * kDwMWaves), 0, s, d_emb, a, dW, db, B,
+                       acc.dW, acc.db);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    hipLaunchKernelGGL((da_mfma_kernel<T, N, kAcc, kParts>), dim3(kDaBlocksX, rows, kParts),
+                       dim3(64 * kDaWavesFor<kParts>), 0, s, d_emb, W, temb, dtemb, B, acc.dtemb, parts);
+  }
   if constexpr (kParts > 1) {
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    hipLaunchKernelGGL((da_parts_kernel<T, kParts, kAcc>), dim3(grid.x, grid.y), dim3(64), 0, s, parts, temb,
-                       dtemb, B, dtemb32);
+    hipLaunchKernelGGL((da_parts_kernel<T, kParts, kAcc>), dim3(kDaBlocksX, rows), dim3(64), 0, s, parts, temb,
+                       dtemb, B, acc.dtemb);
   }
   return hipGetLastError();
 }
 
 template <typename T, int N, bool kAcc>
-hipError_t da_rows(const float* d_emb, const T* W, const T* temb, T* dtemb, int64_t B, float* dtemb32,
-                   double* parts, hipStream_t s) {
+hipError_t mfma_rows(const float* d_emb, const T* a, const T* W, const T* temb, T* dW, T* db, T* dtemb,
+                     double* parts, int64_t B, const AccOut& acc, hipStream_t s) {
   f64x4_t* p = reinterpret_cast<f64x4_t*>(parts);
   switch (da_runs(B)) {
-    case 8: return da_launch<T, N, kAcc, 8>(d_emb, W, temb, dtemb, B, dtemb32, p, s);
-    case 4: return da_launch<T, N, kAcc, 4>(d_emb, W, temb, dtemb, B, dtemb32, p, s);
-    default: return da_launch<T, N, kAcc, 1>(d_emb, W, temb, dtemb, B, dtemb32, nullptr, s);
+    case 8: return mfma_launch<T, N, kAcc, 8>(d_emb, a, W, temb, dW, db, dtemb, B, acc, p, s);
+    case 4: return mfma_launch<T, N, kAcc, 4>(d_emb, a, W, temb, dW, db, dtemb, B, acc, p, s);
+    default: return mfma_launch<T, N, kAcc, 1>(d_emb, a, W, temb, dW, db, dtemb, B, acc, nullptr, s);
   }
 }
 
@@ -746,20 +809,6 @@ hipError_t proj_bwd_fused_rows(const float* d_emb, const uint16_t* temb, const u
   }
 }
 
-template <int N, bool kAcc>
-hipError_t proj_bwd_dw_rows(const float* d_emb, const uint16_t* a, uint16_t* dW, uint16_t* db, int64_t B,
-                            const AccOut& acc, hipStream_t s) {
-  hipLaunchKernelGGL((dw_mfma_kernel<uint16_t, N, kAcc>), dim3(N / kDwMRows, kD / (kDwMCols * kDwMWaves)),
-                     dim3(64 * kDwMWaves), 0, s, d_emb, a, dW, db, B, acc.dW, acc.db);
-  return hipGetLastError();
-}
-
-template <int N, bool kAcc>
-hipError_t proj_bwd_da_rows(const float* d_emb, const uint16_t* W, const uint16_t* temb, uint16_t* dtemb,
-                            double* parts, int64_t B, const AccOut& acc, hipStream_t s) {
-  return da_rows<uint16_t, N, kAcc>(d_emb, W, temb, dtemb, B, acc.dtemb, parts, s);
-}
-
 bool any(const AccOut& acc) { return acc.dW || acc.db || acc.dtemb; }
 
 }  // namespace
@@ -784,27 +833,16 @@ hipError_t launch_proj_bwd_fused(const float* d_emb, const uint16_t* temb, const
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_proj_bwd_dw(const float* d_emb, const uint16_t* a, uint16_t* dW, uint16_t* db, int64_t B,
-                              int64_t N, hipStream_t s, const AccOut& acc) {
+hipError_t launch_proj_bwd_mfma(const float* d_emb, const uint16_t* a, const uint16_t* W, const uint16_t* temb,
+                                uint16_t* dW, uint16_t* db, uint16_t* dtemb, double* parts, int64_t B, int64_t N,
+                                hipStream_t s, const AccOut& acc) {
   const bool f = any(acc);
   if (N == kN)
-    return f ? proj_bwd_dw_rows<kN, true>(d_emb, a, dW, db, B, acc, s)
-             : proj_bwd_dw_rows<kN, false>(d_emb, a, dW, db, B, acc, s);
+    return f ? mfma_rows<uint16_t, kN, true>(d_emb, a, W, temb, dW, db, dtemb, parts, B, acc, s)
+             : mfma_rows<uint16_t, kN, false>(d_emb, a, W, temb, dW, db, dtemb, parts, B, acc, s);
   if (N == kN6)
-    return f ? proj_bwd_dw_rows<kN6, true>(d_emb, a, dW, db, B, acc, s)
-             : proj_bwd_dw_rows<kN6, false>(d_emb, a, dW, db, B, acc, s);
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_proj_bwd_da(const float* d_emb, const uint16_t* W, const uint16_t* temb, uint16_t* dtemb,
-                              double* parts, int64_t B, int64_t N, hipStream_t s, const AccOut& acc) {
-  const bool f = any(acc);
-  if (N == kN)
-    return f ? proj_bwd_da_rows<kN, true>(d_emb, W, temb, dtemb, parts, B, acc, s)
-             : proj_bwd_da_rows<kN, false>(d_emb, W, temb, dtemb, parts, B, acc, s);
-  if (N == kN6)
-    return f ? proj_bwd_da_rows<kN6, true>(d_emb, W, temb, dtemb, parts, B, acc, s)
-             : proj_bwd_da_rows<kN6, false>(d_emb, W, temb, dtemb, parts, B, acc, s);
+    return f ? mfma_rows<uint16_t, kN6, true>(d_emb, a, W, temb, dW, db, dtemb, parts, B, acc, s)
+             : mfma_rows<uint16_t, kN6, false>(d_emb, a, W, temb, dW, db, dtemb, parts, B, acc, s);
   return hipErrorInvalidValue;
 }
 
@@ -835,6 +873,8 @@ hipError_t da_f32_small(const float* d_emb, const float* W, const float* temb, f
 hipError_t launch_proj_bwd_f32(const float* d_emb, const float* temb, const float* W, float* a, float* dW,
                                float* db, float* dtemb, double* sub, int64_t B, hipStream_t s) {
   if (hipError_t e = launch_silu_f32(temb, a, B * kD, s); e != hipSuccess) return e;
+  if (B > proj_bwd_f32_max_batch()) return mfma_rows<float, kN, false>(d_emb, a, W, temb, dW, db, dtemb, sub, B,
+                                                                       AccOut{}, s);
   hipLaunchKernelGGL(dw_mfma_kernel<float>, dim3(kN / kDwMRows, kD / (kDwMCols * kDwMWaves)),
                      dim3(64 * kDwMWaves), 0, s, d_emb, a, dW, db, B, nullptr, nullptr);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
@@ -842,8 +882,7 @@ hipError_t launch_proj_bwd_f32(const float* d_emb, const float* temb, const floa
     case 1: return da_f32_small<1>(d_emb, W, temb, dtemb, sub, s);
     case 2: return da_f32_small<2>(d_emb, W, temb, dtemb, sub, s);
     case 3: return da_f32_small<3>(d_emb, W, temb, dtemb, sub, s);
-    case 4: return da_f32_small<4>(d_emb, W, temb, dtemb, sub, s);
-    default: return da_rows<float, kN, false>(d_emb, W, temb, dtemb, B, nullptr, sub, s);
+    default: return da_f32_small<4>(d_emb, W, temb, dtemb, sub, s);
   }
 }
 
