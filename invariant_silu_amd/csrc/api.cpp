@@ -515,12 +515,18 @@ int adaln_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float* mean, co
   if (int rc = launched(adaln::launch_norm_mod_bwd(gout, x, mean, rstd, emb, dx, part, B, S, s, nullptr, nullptr,
                                                    T0 == 1 ? d_emb : nullptr)))
     return rc;
+  // B > 8: the fold's launch also computes a = SiLU(temb) for the matrix cores
+  const bool vec = B <= adaln::proj_bwd_fused_max_batch();
+  bool act_done = false;
   if (T0 > 1)
-    if (int rc = launched(adaln::launch_tree_fold(part, d_emb, B, T0, kN, s))) return rc;
-  if (B <= adaln::proj_bwd_fused_max_batch())
+    if (int rc = launched(adaln::launch_tree_fold(part, d_emb, B, T0, kN, s, vec ? nullptr : temb, vec ? nullptr : a,
+                                                  &act_done)))
+      return rc;
+  if (vec)
     return launched(adaln::launch_proj_bwd_fused(d_emb, temb, W, dW, db, dtemb, reinterpret_cast<double*>(a), B, kN,
                                                  s));
-  if (int rc = launched(adaln::launch_silu(temb, a, B * kD, s))) return rc;
+  if (!act_done)
+    if (int rc = launched(adaln::launch_silu(temb, a, B * kD, s))) return rc;
   return launched(adaln::launch_proj_bwd_mfma(d_emb, a, W, temb, dW, db, dtemb, da_parts(a, B), B, kN, s));
 }
 

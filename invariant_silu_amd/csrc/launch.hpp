@@ -34,8 +34,11 @@ hipError_t launch_norm_mod_bwd_tiles(const uint16_t* g, const uint16_t* x, const
                                      int64_t S, hipStream_t s);
 hipError_t launch_token_level0(const float* x, float* part, int64_t B,
                                int64_t S, int64_t H, hipStream_t s);
+// with temb and act: the same launch also writes act = bf16(SiLU(temb))
+// ([B, D]; *act_done = false when it could not, B near the grid's limit)
 hipError_t launch_tree_fold(const float* part, float* out, int64_t B,
-                            int64_t T0, int64_t H, hipStream_t s);
+                            int64_t T0, int64_t H, hipStream_t s, const uint16_t* temb = nullptr,
+                            uint16_t* act = nullptr, bool* act_done = nullptr);
 // the same fold, roots of columns [k D, (k + 1) D) to view k (row stride ld), nseg views
 hipError_t launch_tree_fold_views(const float* part, float* d0, float* d1, float* d2, int64_t ld, int64_t B,
                                   int64_t T0, int64_t nseg, hipStream_t s);

@@ -19,6 +19,9 @@
 //   compute the level-1 nodes 4 at a time (one per wave); the first wave then
 //   streams them through levels 2.. with per-level running nodes kept in
 //   registers, which is the same arithmetic as building each level in turn.
+//   Rows of blocks past the last sample (blockIdx.y >= B), when asked for,
+//   compute a = bf16(SiLU(temb)) for the matrix-core projection backward that
+//   follows, so that pass needs no launch of its own.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -62,9 +65,29 @@ struct ViewOut {
   }
 };
 
+// a = bf16(SiLU(temb)) for the 8 elements of chunk i (n = B * D elements in
+// all, a multiple of 8): the same bits as silu_kernel
+__device__ __forceinline__ void silu_chunk(const uint16_t* __restrict__ temb, uint16_t* __restrict__ act,
+                                           int64_t i) {
+  uint32_t redo;
+  const uint4 v = silu8_fast(*reinterpret_cast<const uint4*>(temb + 8 * i), redo);
+  *reinterpret_cast<uint4*>(act + 8 * i) = v;
+  while (redo != 0) {
+    const int e = __builtin_ctz(redo);
+    redo &= redo - 1;
+    act[8 * i + e] = silu_bf16_exact(bf16_to_f32(temb[8 * i + e]));
+  }
+}
+
 template <typename Out>
 __global__ __launch_bounds__(kFoldCols * kFoldLanes) void tree_fold_kernel(
-    const float* __restrict__ part, Out out, int64_t T0, int64_t H, int levels) {
+    const float* __restrict__ part, Out out, int64_t T0, int64_t H, int levels, int64_t B,
+    const uint16_t* __restrict__ temb, uint16_t* __restrict__ act, int64_t n_chunks) {
+  if (blockIdx.y >= B) {   // SiLU rows: one 8-element chunk per thread
+    const int64_t i = (static_cast<int64_t>(blockIdx.y - B) * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n_chunks) silu_chunk(temb, act, i);
+    return;
+  }
   __shared__ float lds_s[kFoldLanes][kFoldCols];
   __shared__ float lds_c[kFoldLanes][kFoldCols];
   // node lane = wave index; readfirstlane tells the compiler it is uniform,
@@ -170,14 +193,26 @@ __global__ __launch_bounds__(kFoldCols * kFoldLanes) void tree_fold_kernel(
   *out.at(b, col) = root_s + root_c;
 }
 
+// with temb and act: also a = bf16(SiLU(temb)) over B * D elements in extra
+// rows of blocks, unless they would take the grid past 65535 rows (*act_done
+// says which)
 template <typename Out>
-hipError_t fold(const float* part, Out out, int64_t B, int64_t T0, int64_t H, hipStream_t s) {
+hipError_t fold(const float* part, Out out, int64_t B, int64_t T0, int64_t H, hipStream_t s,
+                const uint16_t* temb = nullptr, uint16_t* act = nullptr, bool* act_done = nullptr) {
   int levels = 0;
   for (int64_t n = T0; n > 1; n = (n + kTile - 1) / kTile) ++levels;
   if (levels > kMaxFoldLevels) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(tree_fold_kernel<Out>,
-                     dim3(static_cast<unsigned>((H + kFoldCols - 1) / kFoldCols), static_cast<unsigned>(B)),
-                     dim3(kFoldCols * kFoldLanes), 0, s, part, out, T0, H, levels);
+  const int64_t gx = (H + kFoldCols - 1) / kFoldCols;
+  constexpr int64_t kBlock = kFoldCols * kFoldLanes;
+  int64_t n_chunks = 0, rows = 0;
+  if (temb && act) {
+    n_chunks = B * kD / 8;
+    rows = (n_chunks + gx * kBlock - 1) / (gx * kBlock);
+    if (B + rows > 65535) n_chunks = rows = 0;
+  }
+  if (act_done) *act_done = rows > 0;
+  hipLaunchKernelGGL(tree_fold_kernel<Out>, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(B + rows)),
+                     dim3(kBlock), 0, s, part, out, T0, H, levels, B, temb, act, n_chunks);
   return hipGetLastError();
 }
 
@@ -194,8 +229,8 @@ hipError_t launch_token_level0(const float* x, float* part, int64_t B, int64_t S
 }
 
 hipError_t launch_tree_fold(const float* part, float* out, int64_t B, int64_t T0, int64_t H,
-                            hipStream_t s) {
-  return fold(part, DenseOut{out, H}, B, T0, H, s);
+                            hipStream_t s, const uint16_t* temb, uint16_t* act, bool* act_done) {
+  return fold(part, DenseOut{out, H}, B, T0, H, s, temb, act, act_done);
 }
 
 hipError_t launch_tree_fold_views(const float* part, float* d0, float* d1, float* d2, int64_t ld, int64_t B,

@@ -156,13 +156,14 @@ def test_parity_large_batch_sampled(gpu_lib):
 
 
 @pytest.mark.parametrize("B,S", [(1, 31), (1, 4096), (2, 1024), (3, 4096), (3, 97), (4, 33), (5, 40), (8, 36),
-                                 (9, 17), (16, 5), (64, 64)])
+                                 (9, 17), (16, 5), (12, 40), (64, 64), (70, 33)])
 def test_onecall_path_matches_separate_calls(gpu_lib, B, S):
     """adaln_fwd / adaln_bwd give the same bytes as the five separate entry
     points on every branch: the forward's projection on the vector units
     (B <= 4; x within 32 MiB read twice, B = 3, S = 4096 once) or the matrix
     cores (B > 4), the backward's on the vector units (B <= 8) or the matrix
-    cores (B > 8)."""
+    cores (B > 8; with more than one token tile the fold's launch computes
+    SiLU(temb) for them, which adaln_proj_bwd does in a launch of its own)."""
     print(f"[parity] one-call vs separate B={B} S={S}", flush=True)
     d = dev_inputs(make_inputs(B, S, seed=B * 1000 + S, outlier_frac=0.01))
     a = run_path_dev(d)
