@@ -584,10 +584,13 @@ int adaln_bwd_f32(const float* gout, const float* x, const float* mean, const fl
   if (int rc = launched(adaln::launch_norm_mod_bwd_f32(gout, x, mean, rstd, emb, dx, part, B, S, s,
                                                        T0 == 1 ? d_emb : nullptr)))
     return rc;
+  // the fold's launch also computes a = SiLU(temb) for the projection backward
+  bool act_done = false;
   if (T0 > 1)
-    if (int rc = launched(adaln::launch_tree_fold(part, d_emb, B, T0, kN, s))) return rc;
+    if (int rc = launched(adaln::launch_tree_fold(part, d_emb, B, T0, kN, s, nullptr, nullptr, &act_done, temb, a)))
+      return rc;
   double* sub = reinterpret_cast<double*>(reinterpret_cast<char*>(a) + pad256(static_cast<size_t>(B * kD * 4)));
-  return launched(adaln::launch_proj_bwd_f32(d_emb, temb, W, a, dW, db, dtemb, sub, B, s));
+  return launched(adaln::launch_proj_bwd_f32(d_emb, temb, W, a, dW, db, dtemb, sub, B, s, act_done));
 }
 
 int adaln_site_fwd(const adaln_bf16* x, const adaln_bf16* residual, const adaln_bf16* shift, const adaln_bf16* scale,

@@ -34,11 +34,13 @@ hipError_t launch_norm_mod_bwd_tiles(const uint16_t* g, const uint16_t* x, const
                                      int64_t S, hipStream_t s);
 hipError_t launch_token_level0(const float* x, float* part, int64_t B,
                                int64_t S, int64_t H, hipStream_t s);
-// with temb and act: the same launch also writes act = bf16(SiLU(temb))
-// ([B, D]; *act_done = false when it could not, B near the grid's limit)
+// with temb and act (bf16) or temb32 and act32 (fp32 storage): the same
+// launch also writes act = SiLU(temb) ([B, D]; *act_done = false when it
+// could not, B near the grid's limit)
 hipError_t launch_tree_fold(const float* part, float* out, int64_t B,
                             int64_t T0, int64_t H, hipStream_t s, const uint16_t* temb = nullptr,
-                            uint16_t* act = nullptr, bool* act_done = nullptr);
+                            uint16_t* act = nullptr, bool* act_done = nullptr, const float* temb32 = nullptr,
+                            float* act32 = nullptr);
 // the same fold, roots of columns [k D, (k + 1) D) to view k (row stride ld), nseg views
 hipError_t launch_tree_fold_views(const float* part, float* d0, float* d1, float* d2, int64_t ld, int64_t B,
                                   int64_t T0, int64_t nseg, hipStream_t s);
@@ -110,7 +112,8 @@ hipError_t launch_norm_mod_bwd_f32(const float* g, const float* x, const float* 
                                    const float* emb, float* dx, float* part, int64_t B, int64_t S,
                                    hipStream_t s, float* root = nullptr);
 hipError_t launch_proj_bwd_f32(const float* d_emb, const float* temb, const float* W, float* a, float* dW,
-                               float* db, float* dtemb, double* sub, int64_t B, hipStream_t s);
+                               float* db, float* dtemb, double* sub, int64_t B, hipStream_t s,
+                               bool a_ready = false);   // a_ready: a = SiLU(temb) already in `a`
 // sub: B <= 4, the da subtrees (proj_bwd_fused_sub_bytes); B > 4, the da run
 // subtrees (proj_bwd_da_parts_bytes)
 hipError_t launch_selftest_probe(const float* in, float* out, uint32_t* bits, int n,

@@ -22,8 +22,9 @@
 //                              4-leaf subtrees of every column) and dW tiles
 //                              (-> dW, db) in one grid
 //   da_finish_kernel<NB>       B <= 8: the subtrees added pairwise (-> dtemb)
-//   da_leaf_f32_kernel<NB>     fp32 storage, B <= 4: the leaf-group blocks alone
-//                              (then da_finish_kernel<NB, float>)
+//   proj_bwd_f32_small_kernel<NB>  fp32 storage, B <= 4: the leaf-group blocks
+//                              and the matrix-core dW tiles in one grid (then
+//                              da_finish_kernel<NB, float>)
 //   silu_kernel, dw_mfma_kernel, da_mfma_kernel   B > 8 (fp32 storage: B > 4)
 //   proj_bwd_mid_kernel        B <= 64 of those: da's leaf runs and the dW
 //                              tiles in one grid (fp32 storage: 17 <= B)
@@ -759,15 +760,23 @@ hipError_t mfma_rows(const float* d_emb, const T* a, const T* W, const T* temb, 
   }
 }
 
-// da and dtemb for fp32 storage and B = NB <= 4 (the vector da blocks)
-// fp32 storage, B <= 4: the da leaf-group blocks alone (dW and db run on the
-// matrix cores for every B); da_finish_kernel<NB, float> follows
+// fp32 storage, B = NB <= 4: the da leaf-group blocks (blocks [0, 384))
+// beside the matrix-core dW tiles (the rest, row block fastest) in one grid,
+// as proj_bwd_small_kernel does for bf16; da_finish_kernel<NB, float> follows
 template <int NB>
-__global__ __launch_bounds__(kThreads) void da_leaf_f32_kernel(const float* __restrict__ d_emb,
-                                                               const float* __restrict__ W,
-                                                               double* __restrict__ sub) {
+__global__ __launch_bounds__(kThreads) void proj_bwd_f32_small_kernel(const float* __restrict__ d_emb,
+                                                                      const float* __restrict__ a,
+                                                                      const float* __restrict__ W,
+                                                                      float* __restrict__ dW, float* __restrict__ db,
+                                                                      double* __restrict__ sub) {
+  static_assert(kThreads == 64 * kDwMWaves && kDaLeafBlocks % 8 == 0, "one block shape; XCD placement kept");
   __shared__ __align__(16) double red[kDaGroupLeaves * NB * kDaQuadCols];
-  da_leaf_group<NB, float>(d_emb, W, sub, blockIdx.x, red);
+  if (blockIdx.x < kDaLeafBlocks) {
+    da_leaf_group<NB, float>(d_emb, W, sub, blockIdx.x, red);
+    return;
+  }
+  const int t = static_cast<int>(blockIdx.x) - kDaLeafBlocks;
+  dw_block<float, kN, false>(d_emb, a, dW, db, NB, nullptr, nullptr, t % (kN / kDwMRows), t / (kN / kDwMRows));
 }
 
 }  // namespace
@@ -856,9 +865,10 @@ hipError_t launch_silu(const uint16_t* temb, uint16_t* a, int64_t n, hipStream_t
 namespace {
 
 template <int NB>
-hipError_t da_f32_small(const float* d_emb, const float* W, const float* temb, float* dtemb, double* sub,
-                        hipStream_t s) {
-  hipLaunchKernelGGL(da_leaf_f32_kernel<NB>, dim3(kDaLeafBlocks), dim3(kThreads), 0, s, d_emb, W, sub);
+hipError_t proj_f32_small(const float* d_emb, const float* a, const float* W, const float* temb, float* dW,
+                          float* db, float* dtemb, double* sub, hipStream_t s) {
+  const unsigned blocks = kDaLeafBlocks + (kN / kDwMRows) * (kD / (kDwMCols * kDwMWaves));
+  hipLaunchKernelGGL(proj_bwd_f32_small_kernel<NB>, dim3(blocks), dim3(kThreads), 0, s, d_emb, a, W, dW, db, sub);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   hipLaunchKernelGGL((da_finish_kernel<NB, float>), dim3((NB * kD + 255) / 256), dim3(256), 0, s, sub, temb, dtemb,
                      nullptr);
@@ -867,22 +877,19 @@ hipError_t da_f32_small(const float* d_emb, const float* W, const float* temb, f
 
 }  // namespace
 
-// fp32 storage: a = SiLU(temb) into `a`, dW and db on the matrix cores for
-// every B, da and dtemb on the vector units for B <= 4 and the matrix cores
-// beyond (the same leaves and order either way)
+// fp32 storage: a = SiLU(temb) into `a` (unless a_ready), dW and db on the
+// matrix cores for every B, da and dtemb on the vector units for B <= 4 and
+// the matrix cores beyond (the same leaves and order either way)
 hipError_t launch_proj_bwd_f32(const float* d_emb, const float* temb, const float* W, float* a, float* dW,
-                               float* db, float* dtemb, double* sub, int64_t B, hipStream_t s) {
-  if (hipError_t e = launch_silu_f32(temb, a, B * kD, s); e != hipSuccess) return e;
-  if (B > proj_bwd_f32_max_batch()) return mfma_rows<float, kN, false>(d_emb, a, W, temb, dW, db, dtemb, sub, B,
-                                                                       AccOut{}, s);
-  hipLaunchKernelGGL(dw_mfma_kernel<float>, dim3(kN / kDwMRows, kD / (kDwMCols * kDwMWaves)),
-                     dim3(64 * kDwMWaves), 0, s, d_emb, a, dW, db, B, nullptr, nullptr);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+                               float* db, float* dtemb, double* sub, int64_t B, hipStream_t s, bool a_ready) {
+  if (!a_ready)
+    if (hipError_t e = launch_silu_f32(temb, a, B * kD, s); e != hipSuccess) return e;
   switch (B) {
-    case 1: return da_f32_small<1>(d_emb, W, temb, dtemb, sub, s);
-    case 2: return da_f32_small<2>(d_emb, W, temb, dtemb, sub, s);
-    case 3: return da_f32_small<3>(d_emb, W, temb, dtemb, sub, s);
-    default: return da_f32_small<4>(d_emb, W, temb, dtemb, sub, s);
+    case 1: return proj_f32_small<1>(d_emb, a, W, temb, dW, db, dtemb, sub, s);
+    case 2: return proj_f32_small<2>(d_emb, a, W, temb, dW, db, dtemb, sub, s);
+    case 3: return proj_f32_small<3>(d_emb, a, W, temb, dW, db, dtemb, sub, s);
+    case 4: return proj_f32_small<4>(d_emb, a, W, temb, dW, db, dtemb, sub, s);
+    default: return mfma_rows<float, kN, false>(d_emb, a, W, temb, dW, db, dtemb, sub, B, AccOut{}, s);
   }
 }
 

@@ -20,8 +20,8 @@
 //   streams them through levels 2.. with per-level running nodes kept in
 //   registers, which is the same arithmetic as building each level in turn.
 //   Rows of blocks past the last sample (blockIdx.y >= B), when asked for,
-//   compute a = bf16(SiLU(temb)) for the matrix-core projection backward that
-//   follows, so that pass needs no launch of its own.
+//   compute a = SiLU(temb) (bf16 or fp32 storage) for the projection backward
+//   that follows, so that pass needs no launch of its own.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -79,13 +79,23 @@ __device__ __forceinline__ void silu_chunk(const uint16_t* __restrict__ temb, ui
   }
 }
 
+// fp32 storage: a = silu_f32(temb) for the 4 elements of chunk i, as silu_f32_kernel
+__device__ __forceinline__ void silu_chunk_f32(const float* __restrict__ temb, float* __restrict__ act, int64_t i) {
+  const float4 t = *reinterpret_cast<const float4*>(temb + 4 * i);
+  *reinterpret_cast<float4*>(act + 4 * i) = make_float4(silu_f32(t.x), silu_f32(t.y), silu_f32(t.z), silu_f32(t.w));
+}
+
 template <typename Out>
 __global__ __launch_bounds__(kFoldCols * kFoldLanes) void tree_fold_kernel(
     const float* __restrict__ part, Out out, int64_t T0, int64_t H, int levels, int64_t B,
-    const uint16_t* __restrict__ temb, uint16_t* __restrict__ act, int64_t n_chunks) {
-  if (blockIdx.y >= B) {   // SiLU rows: one 8-element chunk per thread
+    const uint16_t* __restrict__ temb, uint16_t* __restrict__ act, const float* __restrict__ temb32,
+    float* __restrict__ act32, int64_t n_chunks) {
+  if (blockIdx.y >= B) {   // SiLU rows: one chunk (8 bf16 or 4 fp32 elements) per thread
     const int64_t i = (static_cast<int64_t>(blockIdx.y - B) * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i < n_chunks) silu_chunk(temb, act, i);
+    if (i < n_chunks) {
+      if (act32) silu_chunk_f32(temb32, act32, i);
+      else silu_chunk(temb, act, i);
+    }
     return;
   }
   __shared__ float lds_s[kFoldLanes][kFoldCols];
@@ -193,26 +203,27 @@ __global__ __launch_bounds__(kFoldCols * kFoldLanes) void tree_fold_kernel(
   *out.at(b, col) = root_s + root_c;
 }
 
-// with temb and act: also a = bf16(SiLU(temb)) over B * D elements in extra
-// rows of blocks, unless they would take the grid past 65535 rows (*act_done
-// says which)
+// with temb and act (or their fp32 forms): also a = SiLU(temb) over B * D
+// elements in extra rows of blocks, unless they would take the grid past
+// 65535 rows (*act_done says which)
 template <typename Out>
 hipError_t fold(const float* part, Out out, int64_t B, int64_t T0, int64_t H, hipStream_t s,
-                const uint16_t* temb = nullptr, uint16_t* act = nullptr, bool* act_done = nullptr) {
+                const uint16_t* temb = nullptr, uint16_t* act = nullptr, bool* act_done = nullptr,
+                const float* temb32 = nullptr, float* act32 = nullptr) {
   int levels = 0;
   for (int64_t n = T0; n > 1; n = (n + kTile - 1) / kTile) ++levels;
   if (levels > kMaxFoldLevels) return hipErrorInvalidValue;
   const int64_t gx = (H + kFoldCols - 1) / kFoldCols;
   constexpr int64_t kBlock = kFoldCols * kFoldLanes;
   int64_t n_chunks = 0, rows = 0;
-  if (temb && act) {
-    n_chunks = B * kD / 8;
+  if ((temb && act) || (temb32 && act32)) {
+    n_chunks = B * kD / (act32 ? 4 : 8);
     rows = (n_chunks + gx * kBlock - 1) / (gx * kBlock);
     if (B + rows > 65535) n_chunks = rows = 0;
   }
   if (act_done) *act_done = rows > 0;
   hipLaunchKernelGGL(tree_fold_kernel<Out>, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(B + rows)),
-                     dim3(kBlock), 0, s, part, out, T0, H, levels, B, temb, act, n_chunks);
+                     dim3(kBlock), 0, s, part, out, T0, H, levels, B, temb, act, temb32, act32, n_chunks);
   return hipGetLastError();
 }
 
@@ -229,8 +240,9 @@ hipError_t launch_token_level0(const float* x, float* part, int64_t B, int64_t S
 }
 
 hipError_t launch_tree_fold(const float* part, float* out, int64_t B, int64_t T0, int64_t H,
-                            hipStream_t s, const uint16_t* temb, uint16_t* act, bool* act_done) {
-  return fold(part, DenseOut{out, H}, B, T0, H, s, temb, act, act_done);
+                            hipStream_t s, const uint16_t* temb, uint16_t* act, bool* act_done,
+                            const float* temb32, float* act32) {
+  return fold(part, DenseOut{out, H}, B, T0, H, s, temb, act, act_done, temb32, act32);
 }
 
 hipError_t launch_tree_fold_views(const float* part, float* d0, float* d1, float* d2, int64_t ld, int64_t B,
