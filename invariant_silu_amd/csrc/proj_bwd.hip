@@ -515,7 +515,7 @@ __global__ __launch_bounds__(64 * kDwMWaves) void dw_mfma_kernel(const float* __
 // so two blocks fit a CU.  Blocks x and x + 8
 // (same XCD) take the two halves of one 128-byte row segment of W.  Rows
 // past B load sample B - 1 and are never stored.
-// Split form (kParts = 2, 4 or 8): the 128 leaves fall into kParts aligned
+// Split form (kParts = 8 or 4, by da_runs): the 128 leaves fall into kParts aligned
 // runs of 128 / kParts, one per blockIdx.z, each run on 4 waves; a block
 // stores its run's subtree (fp64, 2 tiles x 64 lanes) in `parts` and
 // da_parts_kernel adds the kParts subtrees pairwise in run order, which is
