@@ -44,7 +44,7 @@ def _same(a: torch.Tensor, b: torch.Tensor) -> bool:
     return a.shape == b.shape and bool(torch.equal(a.contiguous().view(torch.int32), b.contiguous().view(torch.int32)))
 
 
-@pytest.mark.parametrize("B,S", [(1, 31), (2, 64), (5, 17), (1, 6032), (2, 6889)])
+@pytest.mark.parametrize("B,S", [(1, 31), (2, 64), (5, 17), (6, 40), (1, 6032), (2, 6889)])
 def test_fp32_parity(gpu_lib, B, S):
     """Small shapes on both projection paths, and the pages' long-sequence
     shapes (S = 6032, 6889: several levels of the token tree)."""
