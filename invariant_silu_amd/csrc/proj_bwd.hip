@@ -688,27 +688,41 @@ __global__ __launch_bounds__(256) void proj_bwd_mid_kernel(const float* __restri
   }
 }
 
-// the split form's second launch: block (x, y) of 64 lanes adds its kParts
-// run subtrees pairwise in run order and writes dtemb
+// the split form's second launch: block (x, y) of 4 x 64 threads; thread
+// (v, lane) adds component v (sample g + 4 v of the lane's tiles) of its
+// kParts run subtrees pairwise in run order and writes that sample's dtemb
 template <typename T, int kParts, bool kAcc>
-__global__ __launch_bounds__(64) void da_parts_kernel(const f64x4_t* __restrict__ parts,
-                                                      const T* __restrict__ temb, T* __restrict__ dtemb,
-                                                      int64_t B, float* __restrict__ dtemb32) {
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(256) void da_parts_kernel(const f64x4_t* __restrict__ parts,
+                                                       const T* __restrict__ temb, T* __restrict__ dtemb,
+                                                       int64_t B, float* __restrict__ dtemb32) {
+  const int lane = threadIdx.x & 63;
+  const int v = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int k0 = da_col0(blockIdx.x);
   const int64_t b0 = static_cast<int64_t>(blockIdx.y) * 16;
   const int rows_here = static_cast<int>((B - b0) < 16 ? (B - b0) : 16);
   const int64_t blk = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
-  f64x4_t tot[2];
+  const double* pd = reinterpret_cast<const double*>(parts);
+  double tot[2];
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
-    f64x4_t v[kParts];
+    double w[kParts];
 #pragma unroll
-    for (int q = 0; q < kParts; ++q) v[q] = parts[((blk * kParts + q) * 2 + n) * 64 + lane];
-    tot[n] = pair_reduce(v);
+    for (int q = 0; q < kParts; ++q) w[q] = pd[(((blk * kParts + q) * 2 + n) * 64 + lane) * 4 + v];
+    tot[n] = pair_reduce(w);
   }
-  da_store<T, kAcc>(tot, temb, dtemb, dtemb32, b0, rows_here, k0, r, g);
+  const int sr = g + 4 * v;
+  if (sr < rows_here) {
+    const int64_t i = (b0 + sr) * kD + k0 + 2 * r;
+    Pair<T> z;
+    z.load(temb + i);
+    const float d0 = static_cast<float>(tot[0]) * dsilu_f32(z.lo());
+    const float d1 = static_cast<float>(tot[1]) * dsilu_f32(z.hi());
+    Pair<T>::store(dtemb + i, d0, d1);
+    if constexpr (kAcc) {
+      if (dtemb32) *reinterpret_cast<float2*>(dtemb32 + i) = make_float2(d0, d1);
+    }
+  }
 }
 
 // runs per da block for B samples (1 = the one-block form): 8 for one row of
@@ -743,7 +757,7 @@ hipError_t mfma_launch(const float* d_emb, const T* a, const T* W, const T* temb
   }
   if constexpr (kParts > 1) {
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    hipLaunchKernelGGL((da_parts_kernel<T, kParts, kAcc>), dim3(kDaBlocksX, rows), dim3(64), 0, s, parts, temb,
+    hipLaunchKernelGGL((da_parts_kernel<T, kParts, kAcc>), dim3(kDaBlocksX, rows), dim3(256), 0, s, parts, temb,
                        dtemb, B, acc.dtemb);
   }
   return hipGetLastError();
