@@ -245,20 +245,34 @@ __device__ __forceinline__ void da_leaf_group(const float* __restrict__ d_emb, c
 // da = the 32 subtrees of a (sample, column) added pairwise in order, then
 // dtemb = da * silu'(temb) in the storage type (bf16: one rounding); one
 // thread per (sample, column)
+// da_finish_kernel: block of 64 (sample, column) elements, 8 waves; wave w
+// adds subtrees 4 w .. 4 w + 3 pairwise (two levels of the 32-subtree top),
+// wave 0 then the 8 results pairwise through LDS (three more): the same tree
+// as one thread over all 32, with four loads per thread in flight instead of
+// one thread's 32
+constexpr int kFinishWaves = 8;
+
 template <int NB, typename T = uint16_t, bool kAcc = false>
-__global__ __launch_bounds__(256) void da_finish_kernel(const double* __restrict__ sub,
-                                                        const T* __restrict__ temb,
-                                                        T* __restrict__ dtemb, float* __restrict__ dtemb32) {
-  const int i = blockIdx.x * 256 + threadIdx.x;   // b * D + column
-  if (i >= NB * kD) return;
-  double v[kDaGroups];
+__global__ __launch_bounds__(64 * kFinishWaves) void da_finish_kernel(const double* __restrict__ sub,
+                                                                      const T* __restrict__ temb,
+                                                                      T* __restrict__ dtemb,
+                                                                      float* __restrict__ dtemb32) {
+  constexpr int kPer = kDaGroups / kFinishWaves;   // subtrees per wave
+  static_assert(kPer == 4 && kD % 64 == 0, "two levels per wave, whole 64-column blocks");
+  __shared__ double node[kFinishWaves][64];
+  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 64 + lane;   // b * D + column
+  double v[kPer];
 #pragma unroll
-  for (int g = 0; g < kDaGroups; ++g) v[g] = sub[static_cast<int64_t>(g) * NB * kD + i];
+  for (int q = 0; q < kPer; ++q) v[q] = sub[static_cast<int64_t>(w * kPer + q) * NB * kD + i];
+  node[w][lane] = (v[0] + v[1]) + (v[2] + v[3]);
+  __syncthreads();
+  if (w != 0) return;
+  double u[kFinishWaves];
 #pragma unroll
-  for (int w = 1; w < kDaGroups; w <<= 1)
-#pragma unroll
-    for (int s = 0; s < kDaGroups; s += 2 * w) v[s] += v[s + w];
-  const float d = static_cast<float>(v[0]) * dsilu_f32(Storage<T>::load1(temb[i]));
+  for (int j = 0; j < kFinishWaves; ++j) u[j] = node[j][lane];
+  const float d = static_cast<float>(pair_reduce(u)) * dsilu_f32(Storage<T>::load1(temb[i]));
   dtemb[i] = Storage<T>::store1(d);
   if constexpr (kAcc) {
     if (dtemb32) dtemb32[i] = d;
@@ -810,7 +824,7 @@ hipError_t launch_small(const float* d_emb, const uint16_t* temb, const uint16_t
   else
     hipLaunchKernelGGL((proj_bwd_small_kernel<NB, N>), grid, block, 0, s, d_emb, temb, W, dW, db, sub);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  hipLaunchKernelGGL((da_finish_kernel<NB, uint16_t, kAcc>), dim3((NB * kD + 255) / 256), dim3(256), 0, s, sub,
+  hipLaunchKernelGGL((da_finish_kernel<NB, uint16_t, kAcc>), dim3(NB * kD / 64), dim3(64 * kFinishWaves), 0, s, sub,
                      temb, dtemb, acc.dtemb);
   return hipGetLastError();
 }
@@ -884,7 +898,7 @@ hipError_t proj_f32_small(const float* d_emb, const float* a, const float* W, co
   const unsigned blocks = kDaLeafBlocks + (kN / kDwMRows) * (kD / (kDwMCols * kDwMWaves));
   hipLaunchKernelGGL(proj_bwd_f32_small_kernel<NB>, dim3(blocks), dim3(kThreads), 0, s, d_emb, a, W, dW, db, sub);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  hipLaunchKernelGGL((da_finish_kernel<NB, float>), dim3((NB * kD + 255) / 256), dim3(256), 0, s, sub, temb, dtemb,
+  hipLaunchKernelGGL((da_finish_kernel<NB, float>), dim3(NB * kD / 64), dim3(64 * kFinishWaves), 0, s, sub, temb, dtemb,
                      nullptr);
   return hipGetLastError();
 }
