@@ -50,7 +50,7 @@ extern "C" {
 
 typedef uint16_t adaln_bf16;
 
-#define ADALN_ABI_VERSION 16
+#define ADALN_ABI_VERSION 17
 
 enum adaln_status {
   ADALN_OK = 0,
@@ -89,13 +89,17 @@ enum adaln_op {
  *   PROJ_FWD:       H = K (3072), S ignored.  B*K*2 (SiLU activations, used when
  *                   B > 4).
  *   NORM_MOD_BWD:   H = D (3072).  B * ceil(S/32) * 2D * 8 bytes (level-0 pairs).
- *   PROJ_BWD:       H = K (3072), S ignored.  B <= 8: 32*B*K*8 (the fp64 da
- *                   subtrees, 32 per sample and column); B > 8: B*K*2 (SiLU
- *                   activations).
+ *   PROJ_BWD:       H = K (3072), S ignored.  B <= 6: 32*B*K*8 (the fp64 da
+ *                   subtrees, 32 per sample and column); B > 6: B*K*2 (SiLU
+ *                   activations), then for B <= 64 the fp64 subtrees of the
+ *                   da leaf runs, ceil(B/16) * 96 * R * 2 * 64 * 32 bytes with
+ *                   R = 8 runs for B <= 16 and 4 beyond.
  *   TOKEN_TREE_SUM: B * ceil(S/32) * ceil(H/64) * 64 * 8 bytes (level-0 pairs).
  *   BWD:            H = D (3072).  NORM_MOD_BWD + PROJ_BWD, in that order.
  *   BWD_F32:        H = D (3072).  NORM_MOD_BWD + B*K*4 (fp32 activations),
- *                   then for B <= 4 32*B*K*8 (the fp64 da subtrees).
+ *                   then for B <= 4 32*B*K*8 (the fp64 da subtrees), for
+ *                   4 < B <= 64 the da runs' subtrees as for PROJ_BWD.
+ *   (Every part is rounded up to a multiple of 256 bytes.)
  *   RESIDUAL_BWD:   H = D (3072).  B * ceil(S/32) * 3D * 8 bytes (level-0 pairs).
  *   PROJ_OUT_BWD:   H = K (3072), T = B * S tokens (T <= 65535 * 512; only the
  *                   product is checked, so B = 1, S = T is fine).
@@ -198,11 +202,11 @@ int adaln_norm_mod_bwd_level0(const adaln_bf16* gout, const adaln_bf16* x, const
  *   exact (an fp64 fused multiply-add) and the sums run in fp64 in orders that
  *   do not depend on B: dW and db over samples ascending from +0; da as 128
  *   leaves (leaf t: rows t, t + 128, ..., ascending, from +0; N / 128 rows
- *   each) added pairwise in leaf order.  B <= 8 runs on the vector units, B > 8 on the fp64 matrix
+ *   each) added pairwise in leaf order.  B <= 6 runs on the vector units, B > 6 on the fp64 matrix
  *   cores: the same bits either way.
- *   ws: adaln_workspace_bytes(ADALN_OP_PROJ_BWD, B, 1, K) bytes (B <= 8: the
+ *   ws: adaln_workspace_bytes(ADALN_OP_PROJ_BWD, B, 1, K) bytes (B <= 6: the
  *   sums of leaves 4g .. 4g + 3 for g = 0 .. 31, added pairwise by a second
- *   launch; B > 8: a, then for B <= 64 the subtrees of aligned runs of the
+ *   launch; B > 6: a, then for B <= 64 the subtrees of aligned runs of the
  *   128 leaves -- 8 runs of 16 for B <= 16, 4 runs of 32 up to 64 -- added
  *   pairwise by a second launch: the same tree, spread over more blocks). */
 int adaln_proj_bwd(const float* d_emb, const adaln_bf16* temb, const adaln_bf16* W,

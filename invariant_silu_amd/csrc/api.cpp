@@ -112,13 +112,13 @@ size_t ws_proj_fwd(int64_t B) {
   return pad256(static_cast<size_t>(B * kD * 2));   // SiLU activations (B > 4)
 }
 size_t ws_proj_bwd(int64_t B) {
-  // B <= 8: the fp64 da subtrees (32 per sample and column) between the two
-  // launches; B > 8: the SiLU activations, then (B <= 64) the fp64 subtrees
+  // B <= 6: the fp64 da subtrees (32 per sample and column) between the two
+  // launches; B > 6: the SiLU activations, then (B <= 64) the fp64 subtrees
   // of the da leaf runs
   if (B <= adaln::proj_bwd_fused_max_batch()) return pad256(adaln::proj_bwd_fused_sub_bytes(B));
   return pad256(static_cast<size_t>(B * kD * 2)) + pad256(adaln::proj_bwd_da_parts_bytes(B));
 }
-// the da run subtrees: after the SiLU activations a (bf16, B > 8)
+// the da run subtrees: after the SiLU activations a (bf16, B > 6)
 double* da_parts(void* a, int64_t B) {
   return reinterpret_cast<double*>(static_cast<char*>(a) + pad256(static_cast<size_t>(B * kD * 2)));
 }
@@ -515,7 +515,7 @@ int adaln_bwd(const adaln_bf16* gout, const adaln_bf16* x, const float* mean, co
   if (int rc = launched(adaln::launch_norm_mod_bwd(gout, x, mean, rstd, emb, dx, part, B, S, s, nullptr, nullptr,
                                                    T0 == 1 ? d_emb : nullptr)))
     return rc;
-  // B > 8: the fold's launch also computes a = SiLU(temb) for the matrix cores
+  // B > 6: the fold's launch also computes a = SiLU(temb) for the matrix cores
   const bool vec = B <= adaln::proj_bwd_fused_max_batch();
   bool act_done = false;
   if (T0 > 1)

@@ -18,14 +18,14 @@
 // these orders exactly, so no result depends on the batch size or the grid.
 //
 // Kernels:
-//   proj_bwd_small_kernel<NB>  B <= 8: da leaf-group blocks (-> the 32
+//   proj_bwd_small_kernel<NB>  B <= 6: da leaf-group blocks (-> the 32
 //                              4-leaf subtrees of every column) and dW tiles
 //                              (-> dW, db) in one grid
-//   da_finish_kernel<NB>       B <= 8: the subtrees added pairwise (-> dtemb)
+//   da_finish_kernel<NB>       B <= 6: the subtrees added pairwise (-> dtemb)
 //   proj_bwd_f32_small_kernel<NB>  fp32 storage, B <= 4: the leaf-group blocks
 //                              and the matrix-core dW tiles in one grid (then
 //                              da_finish_kernel<NB, float>)
-//   silu_kernel, dw_mfma_kernel, da_mfma_kernel   B > 8 (fp32 storage: B > 4)
+//   silu_kernel, dw_mfma_kernel, da_mfma_kernel   B > 6 (fp32 storage: B > 4)
 //   proj_bwd_mid_kernel        B <= 64 of those: da's leaf runs and the dW
 //                              tiles in one grid (fp32 storage: 17 <= B)
 //   da_parts_kernel            B <= 64: the leaf runs' subtrees added
@@ -60,7 +60,9 @@ template <int N>
 constexpr int kDwParts = N / kRowsPerPart;           // 32 at N = 6144
 template <int N>
 constexpr int kDwTiles = kDwParts<N> * (kD / kTileCols);   // 384 at N = 6144
-constexpr int kBatchChunk = 8;
+// largest B on the vector units (the matrix-core path from 7 samples: backward
+// -4 to -6 us at B = 7 and 8 for S = 3 ... 4096; at B = 6 it is no faster)
+constexpr int kBatchChunk = 6;
 
 static_assert(kN % kRowsPerPart == 0 && kN6 % kRowsPerPart == 0 && kRowsPerPart % kSlots == 0, "part layout");
 static_assert(kD % kTileCols == 0, "column blocks");
@@ -840,8 +842,6 @@ hipError_t proj_bwd_fused_rows(const float* d_emb, const uint16_t* temb, const u
     case 4: return launch_small<4, N, kAcc>(d_emb, temb, W, dW, db, dtemb, sub, acc, s);
     case 5: return launch_small<5, N, kAcc>(d_emb, temb, W, dW, db, dtemb, sub, acc, s);
     case 6: return launch_small<6, N, kAcc>(d_emb, temb, W, dW, db, dtemb, sub, acc, s);
-    case 7: return launch_small<7, N, kAcc>(d_emb, temb, W, dW, db, dtemb, sub, acc, s);
-    case 8: return launch_small<8, N, kAcc>(d_emb, temb, W, dW, db, dtemb, sub, acc, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -61,7 +61,7 @@ _SIGS = {
 }
 
 # ADALN_ABI_VERSION of include/adaln.h that the signatures above describe
-ABI_VERSION = 16
+ABI_VERSION = 17
 
 _lock = threading.Lock()
 _lib = None

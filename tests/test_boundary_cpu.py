@@ -46,9 +46,9 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_strerror(L):
-    assert L.adaln_abi_version() == 16 == lib.ABI_VERSION
+    assert L.adaln_abi_version() == 17 == lib.ABI_VERSION
     header = open(HEADER).read()
-    assert re.search(r"#define ADALN_ABI_VERSION (\d+)", header).group(1) == "16"
+    assert re.search(r"#define ADALN_ABI_VERSION (\d+)", header).group(1) == "17"
     for code in range(-8, 1):
         assert len(lib.strerror(code)) >= 2
 
@@ -66,9 +66,9 @@ def test_workspace_sizes(L):
         rows = math.ceil(B / 16)
         runs = 8 if rows == 1 else 4 if rows <= 4 else 1
         parts = 0 if runs == 1 else rows * 96 * runs * 2 * 64 * 32
-        # B <= 8: 32 fp64 da subtrees per sample and column; B > 8: the SiLU
+        # B <= 6: 32 fp64 da subtrees per sample and column; B > 6: the SiLU
         # activations, then the run subtrees
-        proj_bwd = pad(32 * B * 3072 * 8) if B <= 8 else pad(B * 3072 * 2) + pad(parts)
+        proj_bwd = pad(32 * B * 3072 * 8) if B <= 6 else pad(B * 3072 * 2) + pad(parts)
         assert lib.workspace_bytes(lib.OP_PROJ_BWD, B, S, 3072) == proj_bwd
         assert lib.workspace_bytes(lib.OP_PROJ_FWD, B, S, 3072) == pad(B * 3072 * 2)
         # fp32: the activations, then the fp64 da subtrees (B <= 4) or run subtrees

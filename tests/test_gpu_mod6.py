@@ -1,7 +1,7 @@
 """A block's 6-way modulation projection (N = 6 x 3072 = 18432) on the GPU,
 through adaln_proj_fwd / adaln_proj_bwd: parity with oracle/modulation.py and
 bytewise batch invariance across the vector-unit (forward B <= 4, backward
-B <= 8) and matrix-core (beyond) branches.  bf16 outputs are gated at 1 ulp from the fp32 oracle,
+B <= 6) and matrix-core (beyond) branches.  bf16 outputs are gated at 1 ulp from the fp32 oracle,
 else 1 ulp from its fp64 twin (tests/compare.py).
 """
 

@@ -30,8 +30,11 @@ CASES = {
     "b2_s33": (2, 33, 2026, 0.0),
     "img512_b2_s1024": (2, 1024, 0, 0.0),
     "img1024_b1_s4096": (1, 4096, 0, 0.01),
-    # eight samples: the matrix-core forward projection with the vector-unit
-    # projection backward at its widest (NB = 8)
+    # six samples: the matrix-core forward projection with the vector-unit
+    # projection backward at its widest (NB = 6)
+    "b6_s40": (6, 40, 7, 0.0),
+    # eight samples: both projections on the matrix cores (the leaf runs of
+    # da and the dW tiles in one grid)
     "b8_s40": (8, 40, 7, 0.0),
 }
 
@@ -161,8 +164,8 @@ def test_onecall_path_matches_separate_calls(gpu_lib, B, S):
     """adaln_fwd / adaln_bwd give the same bytes as the five separate entry
     points on every branch: the forward's projection on the vector units
     (B <= 4; x within 32 MiB read twice, B = 3, S = 4096 once) or the matrix
-    cores (B > 4), the backward's on the vector units (B <= 8) or the matrix
-    cores (B > 8; with more than one token tile the fold's launch computes
+    cores (B > 4), the backward's on the vector units (B <= 6) or the matrix
+    cores (B > 6; with more than one token tile the fold's launch computes
     SiLU(temb) for them, which adaln_proj_bwd does in a launch of its own)."""
     print(f"[parity] one-call vs separate B={B} S={S}", flush=True)
     d = dev_inputs(make_inputs(B, S, seed=B * 1000 + S, outlier_frac=0.01))

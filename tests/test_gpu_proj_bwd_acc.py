@@ -5,7 +5,7 @@ its bf16 outputs are rounded from (dW_f32, db_f32, dtemb_f32).
   bf16 rounding of its fp32 output;
 * the fp32 outputs pass the fp32 gate against the oracle's values before
   their storage rounding (dW_acc, db_acc, dtemb_acc), the fp64 twin
-  arbitrating, on the vector-unit (B <= 8) and matrix-core (B > 8) paths and
+  arbitrating, on the vector-unit (B <= 6) and matrix-core (B > 6) paths and
   at both projection widths;
 * dtemb_f32 rows are bytewise batch-invariant across the vector-unit path
   and the three matrix-core forms of da (8, 4 or 1 leaf runs per block);
