@@ -49,7 +49,7 @@ int proj_bwd_fused_max_batch();
 int proj_bwd_f32_max_batch();
 // bytes of fp64 da subtrees the B <= 4 path keeps between its two launches
 size_t proj_bwd_fused_sub_bytes(int64_t B);
-// B > 8 (bf16) or B > 4 (fp32 storage): the da run subtrees (0: none)
+// B > 6 (bf16) or B > 4 (fp32 storage): the da run subtrees (0: none)
 size_t proj_bwd_da_parts_bytes(int64_t B);
 // Optional fp32 copies of the projection backward's bf16 outputs (the values
 // rounded to bf16); any member may be NULL.
@@ -61,7 +61,7 @@ struct AccOut {
 hipError_t launch_proj_bwd_fused(const float* d_emb, const uint16_t* temb, const uint16_t* W,
                                  uint16_t* dW, uint16_t* db, uint16_t* dtemb, double* sub, int64_t B, int64_t N,
                                  hipStream_t s, const AccOut& acc = AccOut{});
-// B > 8: dW, db, da and dtemb on the matrix cores from a = SiLU(temb);
+// B > 6: dW, db, da and dtemb on the matrix cores from a = SiLU(temb);
 // parts: proj_bwd_da_parts_bytes(B) bytes
 hipError_t launch_proj_bwd_mfma(const float* d_emb, const uint16_t* a, const uint16_t* W, const uint16_t* temb,
                                 uint16_t* dW, uint16_t* db, uint16_t* dtemb, double* parts, int64_t B, int64_t N,
