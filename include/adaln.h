@@ -91,14 +91,14 @@ enum adaln_op {
  *   NORM_MOD_BWD:   H = D (3072).  B * ceil(S/32) * 2D * 8 bytes (level-0 pairs).
  *   PROJ_BWD:       H = K (3072), S ignored.  B <= 6: 32*B*K*8 (the fp64 da
  *                   subtrees, 32 per sample and column); B > 6: B*K*2 (SiLU
- *                   activations), then for B <= 128 the fp64 subtrees of the
- *                   da leaf runs, ceil(B/16) * 96 * R * 2 * 64 * 32 bytes with
- *                   R = 8 runs for B <= 16, 4 for B <= 64 and 2 beyond.
+ *                   activations), then the fp64 subtrees of the da leaf runs,
+ *                   ceil(B/16) * 96 * R * 2 * 64 * 32 bytes with R = 8 runs for
+ *                   B <= 16, 4 for B <= 64 and 2 beyond.
  *   TOKEN_TREE_SUM: B * ceil(S/32) * ceil(H/64) * 64 * 8 bytes (level-0 pairs).
  *   BWD:            H = D (3072).  NORM_MOD_BWD + PROJ_BWD, in that order.
  *   BWD_F32:        H = D (3072).  NORM_MOD_BWD + B*K*4 (fp32 activations),
  *                   then for B <= 4 32*B*K*8 (the fp64 da subtrees), for
- *                   4 < B <= 128 the da runs' subtrees as for PROJ_BWD.
+ *                   B > 4 the da runs' subtrees as for PROJ_BWD.
  *   (Every part is rounded up to a multiple of 256 bytes.)
  *   RESIDUAL_BWD:   H = D (3072).  B * ceil(S/32) * 3D * 8 bytes (level-0 pairs).
  *   PROJ_OUT_BWD:   H = K (3072), T = B * S tokens (T <= 65535 * 512; only the
@@ -206,9 +206,8 @@ int adaln_norm_mod_bwd_level0(const adaln_bf16* gout, const adaln_bf16* x, const
  *   cores: the same bits either way.
  *   ws: adaln_workspace_bytes(ADALN_OP_PROJ_BWD, B, 1, K) bytes (B <= 6: the
  *   sums of leaves 4g .. 4g + 3 for g = 0 .. 31, added pairwise by a second
- *   launch; B > 6: a, then for B <= 128 the subtrees of aligned runs of the
- *   128 leaves -- 8 runs of 16 for B <= 16, 4 runs of 32 up to 64, 2 of 64 up
- *   to 128 -- added
+ *   launch; B > 6: a, then the subtrees of aligned runs of the 128 leaves --
+ *   8 runs of 16 for B <= 16, 4 runs of 32 up to 64, 2 of 64 beyond -- added
  *   pairwise by a second launch: the same tree, spread over more blocks). */
 int adaln_proj_bwd(const float* d_emb, const adaln_bf16* temb, const adaln_bf16* W,
                    adaln_bf16* dW, adaln_bf16* db, adaln_bf16* dtemb, void* ws, size_t ws_bytes,

@@ -113,7 +113,7 @@ size_t ws_proj_fwd(int64_t B) {
 }
 size_t ws_proj_bwd(int64_t B) {
   // B <= 6: the fp64 da subtrees (32 per sample and column) between the two
-  // launches; B > 6: the SiLU activations, then (B <= 128) the fp64 subtrees
+  // launches; B > 6: the SiLU activations, then the fp64 subtrees
   // of the da leaf runs
   if (B <= adaln::proj_bwd_fused_max_batch()) return pad256(adaln::proj_bwd_fused_sub_bytes(B));
   return pad256(static_cast<size_t>(B * kD * 2)) + pad256(adaln::proj_bwd_da_parts_bytes(B));

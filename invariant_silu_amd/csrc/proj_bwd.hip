@@ -26,9 +26,9 @@
 //                              and the matrix-core dW tiles in one grid (then
 //                              da_finish_kernel<NB, float>)
 //   silu_kernel, dw_mfma_kernel, da_mfma_kernel   B > 6 (fp32 storage: B > 4)
-//   proj_bwd_mid_kernel        B <= 128 of those: da's leaf runs and the dW
+//   proj_bwd_mid_kernel        da's leaf runs and the dW
 //                              tiles in one grid (fp32 storage: 17 <= B)
-//   da_parts_kernel            B <= 128: the leaf runs' subtrees added
+//   da_parts_kernel            the leaf runs' subtrees added
 //                              pairwise (-> dtemb)
 // With kAcc (adaln_proj_bwd_acc) the bf16 kernels also store the fp32 values
 // they round to bf16 -- fl32 of the dW and db sums, and da * silu'(temb) in
@@ -536,7 +536,7 @@ __global__ __launch_bounds__(64 * kDwMWaves) void dw_mfma_kernel(const float* __
 // stores its run's subtree (fp64, 2 tiles x 64 lanes) in `parts` and
 // da_parts_kernel adds the kParts subtrees pairwise in run order, which is
 // the tree the one-block form builds.  With 96 x ceil(B / 16) blocks the
-// one-block form leaves CUs idle for B <= 128; the split fills them.
+// one-block form leaves CUs idle; the split fills them (at every B measured).
 template <int N>
 constexpr int kLeafSteps = N / (4 * kDaSlots);   // a leaf's rows, 4 per matrix-core step
 constexpr int kDaMWaves = 8;
@@ -680,7 +680,7 @@ __global__ __launch_bounds__(64 * kDaMWaves) void da_mfma_kernel(const float* __
   da_block<T, N, kAcc, kParts>(d_emb, W, temb, dtemb, B, dtemb32, parts, blockIdx.x, blockIdx.y, blockIdx.z, sub);
 }
 
-// B <= 128 (the split form): the da run blocks (ids [0, n_da), x fastest,
+// The split form: the da run blocks (ids [0, n_da), x fastest,
 // then the sample row, then the run) and the dW tiles (row block fastest) in
 // one grid of 4-wave blocks, so each fills the CUs the other leaves idle.
 // n_da is a multiple of 8, so both keep their XCD placement.
@@ -741,12 +741,14 @@ __global__ __launch_bounds__(256) void da_parts_kernel(const f64x4_t* __restrict
   }
 }
 
-// runs per da block for B samples (1 = the one-block form): 8 for one row of
-// blocks (B <= 16), 4 up to four rows (B <= 64), 2 up to eight (B <= 128:
-// with the dW tiles in the same grid, backward -8 to -25 us at S = 1024)
+// runs per da block for B samples: 8 for one row of blocks (B <= 16), 4 up
+// to four rows (B <= 64), 2 beyond (with the dW tiles in the same grid:
+// backward -8 to -25 us at B = 72 ... 256, S = 1024; -106 us at B = 2048,
+// S = 3) than one block over all 128 leaves (kParts = 1), the form those
+// figures compare against.
 int da_runs(int64_t B) {
   const int64_t by = (B + 15) / 16;
-  return by == 1 ? 8 : by <= 4 ? 4 : by <= 8 ? 2 : 1;
+  return by == 1 ? 8 : by <= 4 ? 4 : 2;
 }
 
 // dW, db, da and dtemb on the matrix cores, a = SiLU(temb) already in `a`:
@@ -787,8 +789,7 @@ hipError_t mfma_rows(const float* d_emb, const T* a, const T* W, const T* temb, 
   switch (da_runs(B)) {
     case 8: return mfma_launch<T, N, kAcc, 8>(d_emb, a, W, temb, dW, db, dtemb, B, acc, p, s);
     case 4: return mfma_launch<T, N, kAcc, 4>(d_emb, a, W, temb, dW, db, dtemb, B, acc, p, s);
-    case 2: return mfma_launch<T, N, kAcc, 2>(d_emb, a, W, temb, dW, db, dtemb, B, acc, p, s);
-    default: return mfma_launch<T, N, kAcc, 1>(d_emb, a, W, temb, dW, db, dtemb, B, acc, nullptr, s);
+    default: return mfma_launch<T, N, kAcc, 2>(d_emb, a, W, temb, dW, db, dtemb, B, acc, p, s);
   }
 }
 

@@ -61,11 +61,11 @@ def test_workspace_sizes(L):
         assert lib.workspace_bytes(lib.OP_NORM_MOD_BWD, B, S, 3072) == pad(B * T0 * 6144 * 8)
         assert lib.workspace_bytes(lib.OP_TOKEN_TREE_SUM, B, S, 100) == pad(B * T0 * 128 * 8)
         # da leaf runs on the matrix cores: 8 for one row of 16 samples, 4 up to
-        # four rows, 2 up to eight, one beyond; each run's subtree is 96 column blocks x 2 tiles
+        # four rows, 2 beyond; each run's subtree is 96 column blocks x 2 tiles
         # x 64 lanes x 4 fp64 per row of samples
         rows = math.ceil(B / 16)
-        runs = 8 if rows == 1 else 4 if rows <= 4 else 2 if rows <= 8 else 1
-        parts = 0 if runs == 1 else rows * 96 * runs * 2 * 64 * 32
+        runs = 8 if rows == 1 else 4 if rows <= 4 else 2
+        parts = rows * 96 * runs * 2 * 64 * 32
         # B <= 6: 32 fp64 da subtrees per sample and column; B > 6: the SiLU
         # activations, then the run subtrees
         proj_bwd = pad(32 * B * 3072 * 8) if B <= 6 else pad(B * 3072 * 2) + pad(parts)
